@@ -1,0 +1,315 @@
+"""CPU oracle for the block-quantized linear layer -- TEST INFRASTRUCTURE.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never does, and this package never imports the product.
+
+The arithmetic lives in ``oracle.c`` (plain scalar C, built with
+``-O2 -fno-fast-math -ffp-contract=off``); this module only marshals NumPy
+arrays.  Every function states the passage it follows in ``oracle.c``.
+
+Format names: ``"q8_0"``, ``"q4k"``, ``"q6k"`` (page "Quantization types",
+sections "Legacy GGML types" and "Q*K family").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+FORMATS = ("q8_0", "q4k", "q6k")
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc (plain C, OpenMP over
+    independent rows/blocks only)."""
+    if force or not os.path.exists(_LIB):
+        cmd = ["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp",
+               "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC", _SRC,
+               "-o", _LIB + ".tmp", "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _L():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I = ctypes.c_int64
+        lib.oracle_f16_from_f32.restype = ctypes.c_uint16
+        lib.oracle_f16_from_f32.argtypes = [ctypes.c_float]
+        lib.oracle_f32_from_f16.restype = ctypes.c_float
+        lib.oracle_f32_from_f16.argtypes = [ctypes.c_uint16]
+        lib.oracle_rha.restype = ctypes.c_float
+        lib.oracle_rha.argtypes = [ctypes.c_float]
+        sigs = {
+            "oracle_f16_from_f32_array": [P, I, P],
+            "oracle_f32_from_f16_array": [P, I, P],
+            "oracle_rha_array": [P, I, P],
+            "oracle_quantize_q8_0": [P, I, I, P, P],
+            "oracle_quantize_q4k": [P, I, I, P, P, P, P, P],
+            "oracle_quantize_q6k": [P, I, I, P, P, P],
+            "oracle_dequant_q8_0": [P, P, I, P],
+            "oracle_dequant_q4k": [P, P, P, P, P, I, P],
+            "oracle_dequant_q6k": [P, P, P, I, P],
+            "oracle_matmul_a16": [P, P, I, I, I, P, P],
+            "oracle_matmul_a16_pairs": [P, P, I, P, P, I, P, P],
+            "oracle_matmul_a8": [P, P, P, P, I, I, I, P, P, I, P, P],
+            "oracle_pack_q8_0": [P, P, I, I, P],
+            "oracle_unpack_q8_0": [P, I, I, P, P],
+            "oracle_pack_q4k": [P, P, P, P, P, I, I, P],
+            "oracle_unpack_q4k": [P, I, I, P, P, P, P, P],
+            "oracle_pack_q6k": [P, P, P, I, I, P],
+            "oracle_unpack_q6k": [P, I, I, P, P, P],
+        }
+        for name, args in sigs.items():
+            fn = getattr(lib, name)
+            fn.restype = None
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _p(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# ----------------------------------------------------------------------------
+# scalar conversions (vectorised by looping in Python over small arrays only;
+# bulk checks use f16_from_f32_array below)
+# ----------------------------------------------------------------------------
+
+def f16_from_f32(v: float) -> int:
+    """IEEE binary32 -> binary16 bits, RNE, gradual underflow, overflow to inf."""
+    return int(_L().oracle_f16_from_f32(float(v)))
+
+
+def f32_from_f16(h: int) -> float:
+    return float(_L().oracle_f32_from_f16(int(h)))
+
+
+def rha(v: float) -> float:
+    """Round half away from zero on a binary32 value."""
+    return float(_L().oracle_rha(float(v)))
+
+
+def f16_from_f32_array(a: np.ndarray) -> np.ndarray:
+    """Element-wise binary32 -> binary16 bits (oracle_f16_from_f32)."""
+    a = _c(a, np.float32)
+    out = np.empty(a.shape, np.uint16)
+    _L().oracle_f16_from_f32_array(_p(a), a.size, _p(out))
+    return out
+
+
+def f32_from_f16_array(h: np.ndarray) -> np.ndarray:
+    h = _c(h, np.uint16)
+    out = np.empty(h.shape, np.float32)
+    _L().oracle_f32_from_f16_array(_p(h), h.size, _p(out))
+    return out
+
+
+def rha_array(a: np.ndarray) -> np.ndarray:
+    a = _c(a, np.float32)
+    out = np.empty(a.shape, np.float32)
+    _L().oracle_rha_array(_p(a), a.size, _p(out))
+    return out
+
+
+# ----------------------------------------------------------------------------
+# quantizers -> logical fields
+# ----------------------------------------------------------------------------
+
+def quantize(fmt: str, w_bf16: np.ndarray) -> dict:
+    """Quantize a [rows][cols] bf16 tensor (given as uint16 bit patterns) to
+    the logical fields of ``fmt`` (oracle.c: q8_0_block / q4k_group /
+    q6k_group)."""
+    w = _c(w_bf16, np.uint16)
+    assert w.ndim == 2
+    rows, cols = w.shape
+    L = _L()
+    if fmt == "q8_0":
+        assert cols % 32 == 0
+        d16 = np.empty((rows, cols // 32), np.uint16)
+        q = np.empty((rows, cols), np.int8)
+        L.oracle_quantize_q8_0(_p(w), rows, cols, _p(d16), _p(q))
+        return {"d16": d16, "q": q}
+    assert cols % 256 == 0
+    G = rows * cols // 256
+    if fmt == "q4k":
+        d16 = np.empty(G, np.uint16)
+        dmin16 = np.empty(G, np.uint16)
+        sc = np.empty((G, 8), np.uint8)
+        mq = np.empty((G, 8), np.uint8)
+        q = np.empty((rows, cols), np.uint8)
+        L.oracle_quantize_q4k(_p(w), rows, cols, _p(d16), _p(dmin16), _p(sc), _p(mq), _p(q))
+        return {"d16": d16, "dmin16": dmin16, "sc": sc, "mq": mq, "q": q}
+    if fmt == "q6k":
+        d16 = np.empty(G, np.uint16)
+        sc = np.empty((G, 16), np.int8)
+        q = np.empty((rows, cols), np.int8)
+        L.oracle_quantize_q6k(_p(w), rows, cols, _p(d16), _p(sc), _p(q))
+        return {"d16": d16, "sc": sc, "q": q}
+    raise ValueError(fmt)
+
+
+def blocks_bytes(fmt: str, rows: int, cols: int) -> int:
+    """Bytes of the planar buffer: 34/32, 144/256, 210/256 bytes per element."""
+    n = rows * cols
+    return {"q8_0": n * 34 // 32, "q4k": n * 144 // 256, "q6k": n * 210 // 256}[fmt]
+
+
+def pack(fmt: str, f: dict, rows: int, cols: int) -> np.ndarray:
+    """Logical fields -> planar bytes (layout in oracle.c, 'Planar byte layout')."""
+    buf = np.zeros(blocks_bytes(fmt, rows, cols), np.uint8)
+    L = _L()
+    if fmt == "q8_0":
+        L.oracle_pack_q8_0(_p(_c(f["d16"], np.uint16)), _p(_c(f["q"], np.int8)), rows, cols, _p(buf))
+    elif fmt == "q4k":
+        L.oracle_pack_q4k(_p(_c(f["d16"], np.uint16)), _p(_c(f["dmin16"], np.uint16)),
+                          _p(_c(f["sc"], np.uint8)), _p(_c(f["mq"], np.uint8)),
+                          _p(_c(f["q"], np.uint8)), rows, cols, _p(buf))
+    elif fmt == "q6k":
+        L.oracle_pack_q6k(_p(_c(f["d16"], np.uint16)), _p(_c(f["sc"], np.int8)),
+                          _p(_c(f["q"], np.int8)), rows, cols, _p(buf))
+    else:
+        raise ValueError(fmt)
+    return buf
+
+
+def unpack(fmt: str, buf: np.ndarray, rows: int, cols: int) -> dict:
+    """Planar bytes -> logical fields (the oracle's own reader)."""
+    b = _c(buf, np.uint8)
+    assert b.size == blocks_bytes(fmt, rows, cols), (b.size, blocks_bytes(fmt, rows, cols))
+    L = _L()
+    G = rows * cols // 256
+    if fmt == "q8_0":
+        d16 = np.empty((rows, cols // 32), np.uint16)
+        q = np.empty((rows, cols), np.int8)
+        L.oracle_unpack_q8_0(_p(b), rows, cols, _p(d16), _p(q))
+        return {"d16": d16, "q": q}
+    if fmt == "q4k":
+        d16 = np.empty(G, np.uint16)
+        dmin16 = np.empty(G, np.uint16)
+        sc = np.empty((G, 8), np.uint8)
+        mq = np.empty((G, 8), np.uint8)
+        q = np.empty((rows, cols), np.uint8)
+        L.oracle_unpack_q4k(_p(b), rows, cols, _p(d16), _p(dmin16), _p(sc), _p(mq), _p(q))
+        return {"d16": d16, "dmin16": dmin16, "sc": sc, "mq": mq, "q": q}
+    if fmt == "q6k":
+        d16 = np.empty(G, np.uint16)
+        sc = np.empty((G, 16), np.int8)
+        q = np.empty((rows, cols), np.int8)
+        L.oracle_unpack_q6k(_p(b), rows, cols, _p(d16), _p(sc), _p(q))
+        return {"d16": d16, "sc": sc, "q": q}
+    raise ValueError(fmt)
+
+
+def dequant(fmt: str, f: dict, rows: int, cols: int) -> np.ndarray:
+    """Exact dequantized weights [rows][cols] in fp64."""
+    out = np.empty((rows, cols), np.float64)
+    n = rows * cols
+    L = _L()
+    if fmt == "q8_0":
+        L.oracle_dequant_q8_0(_p(_c(f["d16"], np.uint16)), _p(_c(f["q"], np.int8)), n, _p(out))
+    elif fmt == "q4k":
+        L.oracle_dequant_q4k(_p(_c(f["d16"], np.uint16)), _p(_c(f["dmin16"], np.uint16)),
+                             _p(_c(f["sc"], np.uint8)), _p(_c(f["mq"], np.uint8)),
+                             _p(_c(f["q"], np.uint8)), n, _p(out))
+    elif fmt == "q6k":
+        L.oracle_dequant_q6k(_p(_c(f["d16"], np.uint16)), _p(_c(f["sc"], np.int8)),
+                             _p(_c(f["q"], np.int8)), n, _p(out))
+    else:
+        raise ValueError(fmt)
+    return out
+
+
+def select_rows(fmt: str, f: dict, rows, cols: int) -> dict:
+    """Fields of the selected weight rows only (for sampled parity checks)."""
+    rows = np.asarray(rows, np.int64)
+    if fmt == "q8_0":
+        return {"d16": f["d16"][rows], "q": f["q"][rows]}
+    gpr = cols // 256
+    gsel = (rows[:, None] * gpr + np.arange(gpr)[None, :]).ravel()
+    out = {k: v[gsel] for k, v in f.items() if k != "q"}
+    out["q"] = f["q"][rows]
+    return out
+
+
+# ----------------------------------------------------------------------------
+# fp64 matmuls and the error metric
+# ----------------------------------------------------------------------------
+
+def matmul_a16(W: np.ndarray, x_bf16: np.ndarray):
+    """Y = x . W^T in fp64 with W the exact dequantized weight [N][K] and x
+    bf16 [M][K]; also returns the normaliser sum_k |w||x| per output."""
+    W = _c(W, np.float64)
+    x = _c(x_bf16, np.uint16)
+    N, K = W.shape
+    M = x.shape[0]
+    assert x.shape[1] == K
+    Y = np.empty((M, N), np.float64)
+    den = np.empty((M, N), np.float64)
+    _L().oracle_matmul_a16(_p(W), _p(x), M, N, K, _p(Y), _p(den))
+    return Y, den
+
+
+def matmul_a16_pairs(W_rows: np.ndarray, x_bf16: np.ndarray, mi, wrow):
+    """The same sums for selected outputs only: output i is row ``mi[i]`` of x
+    against row ``wrow[i]`` of ``W_rows``."""
+    W = _c(W_rows, np.float64)
+    x = _c(x_bf16, np.uint16)
+    mi = _c(mi, np.int64)
+    wrow = _c(wrow, np.int64)
+    K = W.shape[1]
+    Y = np.empty(mi.size, np.float64)
+    den = np.empty(mi.size, np.float64)
+    _L().oracle_matmul_a16_pairs(_p(W), _p(x), K, _p(mi), _p(wrow), mi.size, _p(Y), _p(den))
+    return Y, den
+
+
+def matmul_a8(fw: dict, fx: dict, M: int, N: int, K: int, mi=None, ni=None):
+    """A8 oracle: both operands Q8_0 (weights fw, activations fx, the logical
+    fields of ``quantize('q8_0', ...)``); integer block sums exact, the rest
+    fp64.  Returns (Y, den) for all outputs or for the pairs (mi, ni)."""
+    full = mi is None
+    if full:
+        mm, nn = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+        mi, ni = mm.ravel(), nn.ravel()
+    mi = _c(mi, np.int64)
+    ni = _c(ni, np.int64)
+    Y = np.empty(mi.size, np.float64)
+    den = np.empty(mi.size, np.float64)
+    _L().oracle_matmul_a8(_p(_c(fw["d16"], np.uint16)), _p(_c(fw["q"], np.int8)),
+                          _p(_c(fx["d16"], np.uint16)), _p(_c(fx["q"], np.int8)),
+                          M, N, K, _p(mi), _p(ni), mi.size, _p(Y), _p(den))
+    if full:
+        return Y.reshape(M, N), den.reshape(M, N)
+    return Y, den
+
+
+def normalized_error(y_gpu, y_ref, den) -> np.ndarray:
+    """e = |y_gpu - y_ref| / sum_k |w||x| per output; where the normaliser is
+    0 the output must be exactly 0, so e is 0 there if y_gpu == 0 else inf."""
+    y_gpu = np.asarray(y_gpu, np.float64)
+    diff = np.abs(y_gpu - np.asarray(y_ref, np.float64))
+    den = np.asarray(den, np.float64)
+    e = np.where(den > 0, diff / np.where(den > 0, den, 1.0), np.where(y_gpu == 0, 0.0, np.inf))
+    return e

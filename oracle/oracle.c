@@ -1,0 +1,640 @@
+/*
+ * oracle.c -- plain, slow, obviously correct CPU reference for the
+ * block-quantized linear layer (Q8_0, Q4K, Q6K).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file: only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no code, header, table or helper with
+ * the HIP library; the two meet only in the byte layout, which each side
+ * implements on its own.
+ *
+ * Source of the method:
+ *   - page "Quantization types" (mistral.rs reference), sections
+ *     "Q*K family" (q4k = 4 bits, q6k = 6 bits, GGML K-quant formats) and
+ *     "Legacy GGML types" (q8_0 = 8 bits).  The page names the formats and
+ *     their bit widths; it prints no block layout and no quantizer.
+ *   - the block definitions this library implements: Q8_0 = blocks of 32
+ *     elements, fp16 scale d = max|x|/127, int8 codes q = round(x/d) with
+ *     round-half-away-from-zero; Q4K = 256-element super-blocks of 8
+ *     sub-blocks of 32 with 6-bit scales and mins and fp16 d/dmin, 4-bit
+ *     codes; Q6K = 256-element super-blocks with 6-bit codes.
+ *   Every point those leave open is settled by a stated reading, listed in
+ *   the design notes and repeated at the function that applies it.
+ *
+ * Arithmetic rules (identical on both sides of the parity check):
+ *   - quantizer arithmetic is IEEE binary32, round-to-nearest-even, one
+ *     operation at a time: no contraction, no reciprocal-multiply, no
+ *     denormal flushing (build with -O2 -fno-fast-math -ffp-contract=off);
+ *   - fp32 -> fp16 conversion is written out from IEEE 754 below;
+ *   - RHA(v) = round half away from zero = C roundf;
+ *   - a -0.0 input element is read as +0.0, so no sign of zero can reach a
+ *     scale's bit pattern (it never changes a code);
+ *   - dequantized values and matmuls are exact / fp64.
+ *
+ * Parity status of each function is stated in its comment.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------ */
+/* Scalar conversions                                                  */
+/* ------------------------------------------------------------------ */
+
+/* bf16 bit pattern -> binary32 (exact: bf16 is the top half of binary32).
+ * -0.0 is returned as +0.0 (the reading above). */
+static float bf16_in(uint16_t h)
+{
+    uint32_t u = (h == 0x8000u) ? 0u : ((uint32_t)h << 16);
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* binary32 -> binary16 bits, round to nearest, ties to even, gradual
+ * underflow, overflow to infinity (IEEE 754-2008, section 4.3.1 / 7.4).
+ * Pinned exhaustively against NumPy's float16 cast. */
+uint16_t oracle_f16_from_f32(float v)
+{
+    uint32_t x;
+    memcpy(&x, &v, sizeof x);
+    uint32_t sign = (x >> 16) & 0x8000u;
+    uint32_t bexp = (x >> 23) & 0xffu;
+    uint32_t frac = x & 0x7fffffu;
+
+    if (bexp == 0xffu) /* inf or NaN */
+        return (uint16_t)(sign | 0x7c00u | (frac ? (0x200u | (frac >> 13)) : 0u));
+    if (bexp == 0u) /* zero or binary32 subnormal: |v| < 2^-126, rounds to 0 */
+        return (uint16_t)sign;
+
+    int e = (int)bexp - 127; /* v = 1.frac * 2^e */
+    if (e > 15)
+        return (uint16_t)(sign | 0x7c00u);
+    if (e >= -14) {
+        /* normal binary16: keep 10 of the 23 fraction bits */
+        uint32_t keep = frac >> 13;
+        uint32_t rest = frac & 0x1fffu;
+        uint32_t h = ((uint32_t)(e + 15) << 10) | keep;
+        if (rest > 0x1000u || (rest == 0x1000u && (keep & 1u)))
+            h += 1u; /* a carry may step the exponent, up to 0x7c00 = inf */
+        return (uint16_t)(sign | h);
+    }
+    /* subnormal binary16: units of 2^-24.  The 24-bit significand sig
+     * (with its leading 1) is worth sig * 2^(e-23) = sig * 2^(e+1) units,
+     * so drop -(e+1) >= 14 low bits. */
+    int drop = -(e + 1);
+    if (drop > 24)
+        return (uint16_t)sign; /* below half the smallest subnormal */
+    uint32_t sig = frac | 0x800000u;
+    uint32_t keep = sig >> drop;
+    uint32_t rest = sig & ((1u << drop) - 1u);
+    uint32_t half = 1u << (drop - 1);
+    if (rest > half || (rest == half && (keep & 1u)))
+        keep += 1u; /* may become 0x400 = smallest normal, which is right */
+    return (uint16_t)(sign | keep);
+}
+
+/* binary16 bits -> binary32 (exact). */
+float oracle_f32_from_f16(uint16_t h)
+{
+    uint32_t sign = ((uint32_t)h & 0x8000u) << 16;
+    uint32_t bexp = ((uint32_t)h >> 10) & 0x1fu;
+    uint32_t frac = (uint32_t)h & 0x3ffu;
+    uint32_t u;
+    float f;
+    if (bexp == 0u) {
+        f = (float)frac * 0x1p-24f; /* exact: frac < 2^10 */
+        return sign ? -f : f;
+    }
+    if (bexp == 0x1fu)
+        u = sign | 0x7f800000u | (frac << 13);
+    else
+        u = sign | ((bexp - 15u + 127u) << 23) | (frac << 13);
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* The scale conversion F16(v) for v >= 0: clamp to the largest finite
+ * binary16 (65504) first, then round to nearest even.  The clamp replaces
+ * overflow to infinity [reading: the pages give no overflow rule]. */
+static uint16_t scale_f16(float v)
+{
+    if (v > 65504.0f)
+        v = 65504.0f;
+    return oracle_f16_from_f32(v);
+}
+
+/* Round half away from zero.  Pinned against decimal ROUND_HALF_UP. */
+float oracle_rha(float v) { return roundf(v); }
+
+/* Array forms of the two scalar helpers, for the bulk pins. */
+void oracle_f16_from_f32_array(const float *in, int64_t n, uint16_t *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i++)
+        out[i] = oracle_f16_from_f32(in[i]);
+}
+
+void oracle_f32_from_f16_array(const uint16_t *in, int64_t n, float *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i++)
+        out[i] = oracle_f32_from_f16(in[i]);
+}
+
+void oracle_rha_array(const float *in, int64_t n, float *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i++)
+        out[i] = roundf(in[i]);
+}
+
+static int clamp_code(float r, int lo, int hi)
+{
+    if (r < (float)lo)
+        return lo;
+    if (r > (float)hi)
+        return hi;
+    return (int)r;
+}
+
+/* ------------------------------------------------------------------ */
+/* Q8_0: blocks of 32, fp16 d = max|x|/127, q = RHA(x / d)             */
+/* ------------------------------------------------------------------ */
+
+/* One block.  Steps:
+ *   a   = max |x_i|                     (exact)
+ *   d16 = F16(a / 127)                  (fp32 division, then F16)
+ *   q_i = clamp(RHA(x_i / F32(d16)), -127, 127), or 0 when d16 == 0.
+ * Readings: the code divides by the stored fp16 scale (so that the
+ * round-trip bound |x - q d| <= d/2 holds), codes are symmetric in
+ * [-127, 127], and an all-zero block stores d = 0 and zero codes. */
+static void q8_0_block(const uint16_t *x16, uint16_t *d16_out, int8_t *q)
+{
+    float x[32];
+    float a = 0.0f;
+    for (int i = 0; i < 32; i++) {
+        x[i] = bf16_in(x16[i]);
+        float ax = fabsf(x[i]);
+        if (ax > a)
+            a = ax;
+    }
+    float d32 = a / 127.0f;
+    uint16_t d16 = scale_f16(d32);
+    float df = oracle_f32_from_f16(d16);
+    for (int i = 0; i < 32; i++)
+        q[i] = (int8_t)(df == 0.0f ? 0 : clamp_code(roundf(x[i] / df), -127, 127));
+    *d16_out = d16;
+}
+
+/* Quantize rows*cols bf16 values (row-major, cols % 32 == 0) to Q8_0
+ * logical fields: d16[rows][cols/32], q[rows][cols]. */
+void oracle_quantize_q8_0(const uint16_t *w, int64_t rows, int64_t cols,
+                          uint16_t *d16, int8_t *q)
+{
+    int64_t nb = rows * (cols / 32);
+#pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < nb; b++)
+        q8_0_block(w + 32 * b, d16 + b, q + 32 * b);
+}
+
+/* ------------------------------------------------------------------ */
+/* Q4K: groups of 256 = 8 sub-blocks of 32; 6-bit sc/m; fp16 d, dmin   */
+/* ------------------------------------------------------------------ */
+
+/* One group, plain min/max affine rule [reading: the pages name the fields
+ * only].  Steps:
+ *   per sub-block j: lo_j = min(0, min x), hi_j = max x,
+ *                    s_j = (hi_j - lo_j) / 15,  m_j = 0 - lo_j
+ *   d16 = F16(max_j s_j / 63),  dmin16 = F16(max_j m_j / 63)
+ *   sc_j = clamp(RHA(s_j / d), 0, 63)   (0 when d == 0)
+ *   mq_j = clamp(RHA(m_j / dmin), 0, 63) (0 when dmin == 0)
+ *   S_j = d * sc_j,  M_j = dmin * mq_j   (both exact in binary32)
+ *   q_i = clamp(RHA((x_i + M_j) / S_j), 0, 15)  (0 when S_j == 0)
+ * so that the decoded value is S_j * q_i - M_j. */
+static void q4k_group(const uint16_t *x16, uint16_t *d16_out, uint16_t *dmin16_out,
+                      uint8_t *sc, uint8_t *mq, uint8_t *q)
+{
+    float x[256], s[8], m[8];
+    for (int i = 0; i < 256; i++)
+        x[i] = bf16_in(x16[i]);
+    for (int j = 0; j < 8; j++) {
+        float lo = 0.0f, hi = x[32 * j];
+        for (int i = 0; i < 32; i++) {
+            float v = x[32 * j + i];
+            if (v < lo)
+                lo = v;
+            if (v > hi)
+                hi = v;
+        }
+        s[j] = (hi - lo) / 15.0f;
+        m[j] = 0.0f - lo;
+    }
+    float smax = 0.0f, mmax = 0.0f;
+    for (int j = 0; j < 8; j++) {
+        if (s[j] > smax)
+            smax = s[j];
+        if (m[j] > mmax)
+            mmax = m[j];
+    }
+    uint16_t d16 = scale_f16(smax / 63.0f);
+    uint16_t dm16 = scale_f16(mmax / 63.0f);
+    float df = oracle_f32_from_f16(d16);
+    float dmf = oracle_f32_from_f16(dm16);
+    for (int j = 0; j < 8; j++) {
+        sc[j] = (uint8_t)(df > 0.0f ? clamp_code(roundf(s[j] / df), 0, 63) : 0);
+        mq[j] = (uint8_t)(dmf > 0.0f ? clamp_code(roundf(m[j] / dmf), 0, 63) : 0);
+        float S = df * (float)sc[j];
+        float M = dmf * (float)mq[j];
+        for (int i = 0; i < 32; i++) {
+            float t = x[32 * j + i] + M;
+            q[32 * j + i] = (uint8_t)(S > 0.0f ? clamp_code(roundf(t / S), 0, 15) : 0);
+        }
+    }
+    *d16_out = d16;
+    *dmin16_out = dm16;
+}
+
+/* rows*cols bf16 (cols % 256 == 0) -> Q4K logical fields per group g:
+ * d16[g], dmin16[g], sc[g][8], mq[g][8], q[g][256] (q is [rows][cols]). */
+void oracle_quantize_q4k(const uint16_t *w, int64_t rows, int64_t cols,
+                         uint16_t *d16, uint16_t *dmin16, uint8_t *sc,
+                         uint8_t *mq, uint8_t *q)
+{
+    int64_t ng = rows * (cols / 256);
+#pragma omp parallel for schedule(static)
+    for (int64_t g = 0; g < ng; g++)
+        q4k_group(w + 256 * g, d16 + g, dmin16 + g, sc + 8 * g, mq + 8 * g, q + 256 * g);
+}
+
+/* ------------------------------------------------------------------ */
+/* Q6K: groups of 256 = 16 sub-blocks of 16; int8 sc; one fp16 d       */
+/* ------------------------------------------------------------------ */
+
+/* One group, symmetric rule [reading: 6-bit symmetric codes, 16 sub-blocks
+ * of 16 with 8-bit sub-scales and one fp16 d, no mins -- the field set
+ * that gives 210 bytes per 256 elements].  Steps:
+ *   s_j = max_i |x_i| / 31 over sub-block j
+ *   d16 = F16(max_j s_j / 127)
+ *   sc_j = clamp(RHA(s_j / d), 0, 127)  (0 when d == 0)
+ *   S_j = d * sc_j                       (exact in binary32)
+ *   q_i = clamp(RHA(x_i / S_j), -32, 31) (0 when S_j == 0)
+ * decoded value S_j * q_i. */
+static void q6k_group(const uint16_t *x16, uint16_t *d16_out, int8_t *sc, int8_t *q)
+{
+    float x[256], s[16];
+    for (int i = 0; i < 256; i++)
+        x[i] = bf16_in(x16[i]);
+    float smax = 0.0f;
+    for (int j = 0; j < 16; j++) {
+        float a = 0.0f;
+        for (int i = 0; i < 16; i++) {
+            float ax = fabsf(x[16 * j + i]);
+            if (ax > a)
+                a = ax;
+        }
+        s[j] = a / 31.0f;
+        if (s[j] > smax)
+            smax = s[j];
+    }
+    uint16_t d16 = scale_f16(smax / 127.0f);
+    float df = oracle_f32_from_f16(d16);
+    for (int j = 0; j < 16; j++) {
+        sc[j] = (int8_t)(df > 0.0f ? clamp_code(roundf(s[j] / df), 0, 127) : 0);
+        float S = df * (float)sc[j];
+        for (int i = 0; i < 16; i++)
+            q[16 * j + i] = (int8_t)(S > 0.0f ? clamp_code(roundf(x[16 * j + i] / S), -32, 31) : 0);
+    }
+    *d16_out = d16;
+}
+
+/* rows*cols bf16 (cols % 256 == 0) -> Q6K fields per group g:
+ * d16[g], sc[g][16] (int8, never negative), q[g][256] signed in [-32, 31]. */
+void oracle_quantize_q6k(const uint16_t *w, int64_t rows, int64_t cols,
+                         uint16_t *d16, int8_t *sc, int8_t *q)
+{
+    int64_t ng = rows * (cols / 256);
+#pragma omp parallel for schedule(static)
+    for (int64_t g = 0; g < ng; g++)
+        q6k_group(w + 256 * g, d16 + g, sc + 16 * g, q + 256 * g);
+}
+
+/* ------------------------------------------------------------------ */
+/* Exact dequantization to fp64                                        */
+/* ------------------------------------------------------------------ */
+
+/* Q8_0: w = d * q (exact). */
+void oracle_dequant_q8_0(const uint16_t *d16, const int8_t *q, int64_t n_elems, double *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t e = 0; e < n_elems; e++)
+        out[e] = (double)oracle_f32_from_f16(d16[e / 32]) * (double)q[e];
+}
+
+/* Q4K: w = (d * sc_j) * q - (dmin * mq_j), evaluated exactly in fp64. */
+void oracle_dequant_q4k(const uint16_t *d16, const uint16_t *dmin16, const uint8_t *sc,
+                        const uint8_t *mq, const uint8_t *q, int64_t n_elems, double *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t e = 0; e < n_elems; e++) {
+        int64_t g = e / 256;
+        int j = (int)((e % 256) / 32);
+        double S = (double)oracle_f32_from_f16(d16[g]) * (double)sc[8 * g + j];
+        double M = (double)oracle_f32_from_f16(dmin16[g]) * (double)mq[8 * g + j];
+        out[e] = S * (double)q[e] - M;
+    }
+}
+
+/* Q6K: w = (d * sc_j) * q (exact). */
+void oracle_dequant_q6k(const uint16_t *d16, const int8_t *sc, const int8_t *q,
+                        int64_t n_elems, double *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t e = 0; e < n_elems; e++) {
+        int64_t g = e / 256;
+        int j = (int)((e % 256) / 16);
+        out[e] = (double)oracle_f32_from_f16(d16[g]) * (double)sc[16 * g + j] * (double)q[e];
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* fp64 matmuls and the error normaliser                               */
+/* ------------------------------------------------------------------ */
+
+/* A16 oracle: Y[m][n] = sum_k W[n][k] * x[m][k] in fp64, sequential k,
+ * and den[m][n] = sum_k |W[n][k]| * |x[m][k]|.  x is bf16 bits [M][K];
+ * W is the exact dequantized weight [N][K] in fp64. */
+void oracle_matmul_a16(const double *W, const uint16_t *x16, int64_t M, int64_t N,
+                       int64_t K, double *Y, double *den)
+{
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; m++)
+        for (int64_t n = 0; n < N; n++) {
+            double acc = 0.0, a = 0.0;
+            for (int64_t k = 0; k < K; k++) {
+                double x = (double)bf16_in(x16[m * K + k]);
+                double w = W[n * K + k];
+                acc += w * x;
+                a += fabs(w) * fabs(x);
+            }
+            Y[m * N + n] = acc;
+            den[m * N + n] = a;
+        }
+}
+
+/* The same sum for a list of (m, n) pairs only, for shapes too large to
+ * evaluate in full.  Wrow(n) is taken from W given as dequantized rows:
+ * W is [n_rows][K] and rowsel[i] is the row of W that output i uses. */
+void oracle_matmul_a16_pairs(const double *W, const uint16_t *x16, int64_t K,
+                             const int64_t *mi, const int64_t *wrow, int64_t npairs,
+                             double *Y, double *den)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < npairs; i++) {
+        double acc = 0.0, a = 0.0;
+        for (int64_t k = 0; k < K; k++) {
+            double x = (double)bf16_in(x16[mi[i] * K + k]);
+            double w = W[wrow[i] * K + k];
+            acc += w * x;
+            a += fabs(w) * fabs(x);
+        }
+        Y[i] = acc;
+        den[i] = a;
+    }
+}
+
+/* A8 oracle (activations quantized to Q8_0 as well):
+ *   Y[m][n] = sum_b dw[n][b] * dx[m][b] * (sum_{i in b} qw * qx)
+ * with the integer block sums exact in int64 and the rest in fp64.
+ * den[m][n] = sum_k |dw qw| * |dx qx| (the normaliser on the same values). */
+void oracle_matmul_a8(const uint16_t *dw16, const int8_t *qw, const uint16_t *dx16,
+                      const int8_t *qx, int64_t M, int64_t N, int64_t K,
+                      const int64_t *mi, const int64_t *ni, int64_t npairs,
+                      double *Y, double *den)
+{
+    int64_t nb = K / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < npairs; i++) {
+        int64_t m = mi[i], n = ni[i];
+        double acc = 0.0, a = 0.0;
+        for (int64_t b = 0; b < nb; b++) {
+            int64_t isum = 0, iabs = 0;
+            for (int64_t t = 0; t < 32; t++) {
+                int64_t pw = qw[n * K + 32 * b + t], px = qx[m * K + 32 * b + t];
+                isum += pw * px;
+                iabs += (pw < 0 ? -pw : pw) * (px < 0 ? -px : px);
+            }
+            double dw = (double)oracle_f32_from_f16(dw16[n * nb + b]);
+            double dx = (double)oracle_f32_from_f16(dx16[m * nb + b]);
+            acc += dw * dx * (double)isum;
+            a += fabs(dw) * fabs(dx) * (double)iabs;
+        }
+        Y[i] = acc;
+        den[i] = a;
+    }
+    (void)M;
+    (void)N;
+}
+
+/* ------------------------------------------------------------------ */
+/* Planar byte layout: logical fields <-> bytes                        */
+/* ------------------------------------------------------------------ */
+/*
+ * One buffer per tensor [rows][cols], cols % 256 == 0 (Q8_0: cols % 32),
+ * made of planes that each start 16-byte aligned.  G = rows*cols/256.
+ *
+ * Q8_0  [C: rows*cols int8, row-major]            code of element (n,k)
+ *       [S: rows*cols/32 fp16, row-major]          d of block (n, k/32)
+ * Q4K   [C: G*128 bytes] [S: G*16 bytes]
+ *       C: group g owns bytes 128g..128g+127; sub-block j owns the 16
+ *          bytes 16j..16j+15 of its group, read as 4 little-endian dwords;
+ *          dword w holds elements e = 8w..8w+7 of the sub-block: nibble p
+ *          (bits 4p..4p+3) holds e = 8w + 2p for p < 4 and
+ *          e = 8w + 2(p-4) + 1 for p >= 4 (even elements in the low half,
+ *          odd elements in the high half).
+ *       S: bytes 0-1 d (fp16), 2-3 dmin (fp16), bytes 4-7 a dword whose
+ *          nibble j is sc_j & 15, bytes 8-11 a dword whose nibble j is
+ *          mq_j & 15, bytes 12-15 a dword with bits 2j..2j+1 = sc_j >> 4
+ *          and bits 16+2j..17+2j = mq_j >> 4.
+ * Q6K   [C: G*192 bytes] [S: G*16 bytes] [D: G*2 bytes]
+ *       stored code u = q + 32 in [0, 63].
+ *       C: group g owns bytes 192g..192g+191 (layout at q6k_pack_group).
+ *       S: 16 int8 sub-scales sc_j per group.  D: fp16 d per group (the
+ *          plane starts at byte 208*G, a multiple of 16).
+ */
+
+/* Q8_0 pack/unpack: the planes are the fields themselves. */
+void oracle_pack_q8_0(const uint16_t *d16, const int8_t *q, int64_t rows, int64_t cols,
+                      uint8_t *buf)
+{
+    int64_t n = rows * cols;
+    memcpy(buf, q, (size_t)n);
+    memcpy(buf + n, d16, (size_t)(n / 32) * 2);
+}
+
+void oracle_unpack_q8_0(const uint8_t *buf, int64_t rows, int64_t cols, uint16_t *d16,
+                        int8_t *q)
+{
+    int64_t n = rows * cols;
+    memcpy(q, buf, (size_t)n);
+    memcpy(d16, buf + n, (size_t)(n / 32) * 2);
+}
+
+/* nibble position p (0..7) within a dword -> element offset 0..7 */
+static int nib_elem(int p) { return p < 4 ? 2 * p : 2 * (p - 4) + 1; }
+
+static void put_u32(uint8_t *p, uint32_t v)
+{
+    p[0] = (uint8_t)v;
+    p[1] = (uint8_t)(v >> 8);
+    p[2] = (uint8_t)(v >> 16);
+    p[3] = (uint8_t)(v >> 24);
+}
+
+static uint32_t get_u32(const uint8_t *p)
+{
+    return (uint32_t)p[0] | (uint32_t)p[1] << 8 | (uint32_t)p[2] << 16 | (uint32_t)p[3] << 24;
+}
+
+/* 32 four-bit values v[0..31] -> 16 bytes in the nibble order above. */
+static void pack_nibbles32(const uint8_t *v, uint8_t *out16)
+{
+    for (int w = 0; w < 4; w++) {
+        uint32_t d = 0;
+        for (int p = 0; p < 8; p++)
+            d |= (uint32_t)(v[8 * w + nib_elem(p)] & 15u) << (4 * p);
+        put_u32(out16 + 4 * w, d);
+    }
+}
+
+static void unpack_nibbles32(const uint8_t *in16, uint8_t *v)
+{
+    for (int w = 0; w < 4; w++) {
+        uint32_t d = get_u32(in16 + 4 * w);
+        for (int p = 0; p < 8; p++)
+            v[8 * w + nib_elem(p)] = (uint8_t)((d >> (4 * p)) & 15u);
+    }
+}
+
+void oracle_pack_q4k(const uint16_t *d16, const uint16_t *dmin16, const uint8_t *sc,
+                     const uint8_t *mq, const uint8_t *q, int64_t rows, int64_t cols,
+                     uint8_t *buf)
+{
+    int64_t G = rows * cols / 256;
+    uint8_t *C = buf, *S = buf + 128 * G;
+    for (int64_t g = 0; g < G; g++) {
+        for (int j = 0; j < 8; j++)
+            pack_nibbles32(q + 256 * g + 32 * j, C + 128 * g + 16 * j);
+        uint8_t *h = S + 16 * g;
+        h[0] = (uint8_t)d16[g];
+        h[1] = (uint8_t)(d16[g] >> 8);
+        h[2] = (uint8_t)dmin16[g];
+        h[3] = (uint8_t)(dmin16[g] >> 8);
+        uint32_t lo_s = 0, lo_m = 0, hi = 0;
+        for (int j = 0; j < 8; j++) {
+            lo_s |= (uint32_t)(sc[8 * g + j] & 15u) << (4 * j);
+            lo_m |= (uint32_t)(mq[8 * g + j] & 15u) << (4 * j);
+            hi |= (uint32_t)((sc[8 * g + j] >> 4) & 3u) << (2 * j);
+            hi |= (uint32_t)((mq[8 * g + j] >> 4) & 3u) << (16 + 2 * j);
+        }
+        put_u32(h + 4, lo_s);
+        put_u32(h + 8, lo_m);
+        put_u32(h + 12, hi);
+    }
+}
+
+void oracle_unpack_q4k(const uint8_t *buf, int64_t rows, int64_t cols, uint16_t *d16,
+                       uint16_t *dmin16, uint8_t *sc, uint8_t *mq, uint8_t *q)
+{
+    int64_t G = rows * cols / 256;
+    const uint8_t *C = buf, *S = buf + 128 * G;
+    for (int64_t g = 0; g < G; g++) {
+        for (int j = 0; j < 8; j++)
+            unpack_nibbles32(C + 128 * g + 16 * j, q + 256 * g + 32 * j);
+        const uint8_t *h = S + 16 * g;
+        d16[g] = (uint16_t)(h[0] | h[1] << 8);
+        dmin16[g] = (uint16_t)(h[2] | h[3] << 8);
+        uint32_t lo_s = get_u32(h + 4), lo_m = get_u32(h + 8), hi = get_u32(h + 12);
+        for (int j = 0; j < 8; j++) {
+            sc[8 * g + j] = (uint8_t)(((lo_s >> (4 * j)) & 15u) | ((hi >> (2 * j)) & 3u) << 4);
+            mq[8 * g + j] = (uint8_t)(((lo_m >> (4 * j)) & 15u) | ((hi >> (16 + 2 * j)) & 3u) << 4);
+        }
+    }
+}
+
+/* Q6K code plane of one group (192 bytes).  The group is 8 chunks of 32
+ * elements (chunk c = elements 32c..32c+31 = sub-blocks 2c and 2c+1).
+ *   bytes 0..127:   low 4 bits of u; chunk c in bytes 16c..16c+15, in the
+ *                   Q4K nibble order (dword w = elements 8w..8w+7).
+ *   bytes 128..191: high 2 bits of u; chunk c owns the two dwords at
+ *                   128+8c+4h (h = 0, 1).  Dword h covers the octets
+ *                   o = 0, 1 (elements 16h+8o .. 16h+8o+7); for the pair
+ *                   s = 0..3 of an octet, bits 8o+2s..8o+2s+1 hold the high
+ *                   bits of element 16h+8o+2s and bits 16+8o+2s..17+8o+2s
+ *                   those of element 16h+8o+2s+1.
+ */
+static void q6k_pack_group(const int8_t *qg, uint8_t *C)
+{
+    for (int c = 0; c < 8; c++) {
+        uint8_t lo[32];
+        for (int i = 0; i < 32; i++)
+            lo[i] = (uint8_t)((qg[32 * c + i] + 32) & 15);
+        pack_nibbles32(lo, C + 16 * c);
+        for (int h = 0; h < 2; h++) {
+            uint32_t d = 0;
+            for (int o = 0; o < 2; o++)
+                for (int s = 0; s < 4; s++) {
+                    int e = 32 * c + 16 * h + 8 * o + 2 * s;
+                    uint32_t u0 = (uint32_t)(qg[e] + 32) >> 4;
+                    uint32_t u1 = (uint32_t)(qg[e + 1] + 32) >> 4;
+                    d |= u0 << (2 * s + 8 * o);
+                    d |= u1 << (16 + 2 * s + 8 * o);
+                }
+            put_u32(C + 128 + 8 * c + 4 * h, d);
+        }
+    }
+}
+
+static void q6k_unpack_group(const uint8_t *C, int8_t *qg)
+{
+    for (int c = 0; c < 8; c++) {
+        uint8_t lo[32];
+        unpack_nibbles32(C + 16 * c, lo);
+        for (int h = 0; h < 2; h++) {
+            uint32_t d = get_u32(C + 128 + 8 * c + 4 * h);
+            for (int o = 0; o < 2; o++)
+                for (int s = 0; s < 4; s++) {
+                    int i0 = 16 * h + 8 * o + 2 * s;
+                    uint32_t u0 = lo[i0] | ((d >> (2 * s + 8 * o)) & 3u) << 4;
+                    uint32_t u1 = lo[i0 + 1] | ((d >> (16 + 2 * s + 8 * o)) & 3u) << 4;
+                    qg[32 * c + i0] = (int8_t)((int)u0 - 32);
+                    qg[32 * c + i0 + 1] = (int8_t)((int)u1 - 32);
+                }
+        }
+    }
+}
+
+void oracle_pack_q6k(const uint16_t *d16, const int8_t *sc, const int8_t *q, int64_t rows,
+                     int64_t cols, uint8_t *buf)
+{
+    int64_t G = rows * cols / 256;
+    uint8_t *C = buf, *S = buf + 192 * G, *D = buf + 208 * G;
+    for (int64_t g = 0; g < G; g++) {
+        q6k_pack_group(q + 256 * g, C + 192 * g);
+        memcpy(S + 16 * g, sc + 16 * g, 16);
+        D[2 * g] = (uint8_t)d16[g];
+        D[2 * g + 1] = (uint8_t)(d16[g] >> 8);
+    }
+}
+
+void oracle_unpack_q6k(const uint8_t *buf, int64_t rows, int64_t cols, uint16_t *d16,
+                       int8_t *sc, int8_t *q)
+{
+    int64_t G = rows * cols / 256;
+    const uint8_t *C = buf, *S = buf + 192 * G, *D = buf + 208 * G;
+    for (int64_t g = 0; g < G; g++) {
+        q6k_unpack_group(C + 192 * g, q + 256 * g);
+        memcpy(sc + 16 * g, S + 16 * g, 16);
+        d16[g] = (uint16_t)(D[2 * g] | D[2 * g + 1] << 8);
+    }
+}
