@@ -1,0 +1,380 @@
+"""Benchmark of the block-quantized linear layer on one MI355X.
+
+Headline step: one decode step of a quantized projection -- the fused
+dequant-GEMV of a Q4K weight at the FFN up-projection shape (N = 14336,
+K = 4096, M = 1 token), weights already quantized (ISQ) and resident in HBM.
+`value` is quantized-weight GB/s: weight bytes per step / time per step.
+Each step reads a different copy of the weights (enough copies to exceed
+twice the 256 MiB Infinity Cache), so the bytes come from HBM.  Launches are
+captured in a HIP graph (kernels are warmed before capture) so that host
+launch cost does not enter a 4-microsecond kernel's time.
+
+The same run also measures, as "parts": the Q8_0 variant of the headline
+GEMV, batched decode (M = 4/16/64, K = 14336, N = 4096, Q4K with outliers),
+prefill (M = 2048, K = 4096, N = 14336, Q8_0 weights) on the bf16 MFMA and
+the int8 MFMA paths, ISQ of a 32-layer decoder to Q4K plus its 131072 x 5120
+output head to Q6K, the output head GEMV at M = 1 and 8, and the equivalent
+decode tokens/s of that decoder (all 224 projection GEMVs plus the head).
+Parity with the CPU oracle is checked in the same run before timing.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0     # dense MFMA bf16, published
+INT8_PEAK_TOPS = 5000.0       # dense MFMA int8, published
+MALL_BYTES = 256 << 20        # Infinity Cache
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--quick", action="store_true", help="headline only (for profiling runs)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    return ap.parse_args()
+
+
+def copies_for(nbytes: int) -> int:
+    return max(2, math.ceil(2 * MALL_BYTES / nbytes))
+
+
+class Timer:
+    """HIP events on the current stream (the stream every launch uses)."""
+
+    def __init__(self, torch):
+        self.t = torch
+        self.a = torch.cuda.Event(enable_timing=True)
+        self.b = torch.cuda.Event(enable_timing=True)
+
+    def __enter__(self):
+        self.t.cuda.synchronize()
+        self.a.record()
+        return self
+
+    def __exit__(self, *exc):
+        self.b.record()
+        self.t.cuda.synchronize()
+        self.ms = self.a.elapsed_time(self.b)
+
+
+def graph_of(torch, launch, n):
+    """Capture n calls launch(i) in one HIP graph (after eager warm-up)."""
+    launch(0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(n):
+                launch(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(torch, g, reps, calls_per_replay):
+    g.replay()
+    torch.cuda.synchronize()
+    with Timer(torch) as t:
+        for _ in range(reps):
+            g.replay()
+    return t.ms / (reps * calls_per_replay)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this library has no multi-GPU path "
+              "(sharding is described in the design notes, not built). Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import ggml_block_quant_amd as ql
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    ql.lib()  # fail loudly if the HIP library is not built
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    result = {}
+
+    def bf16_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ------------------------------------------------------------------
+    # headline: Q4K GEMV, N=14336, K=4096, M=1, cold weights
+    # ------------------------------------------------------------------
+    N, K, M = 14336, 4096, 1
+    log("headline: generating 14336x4096 weights and quantizing")
+    w = synth.weights_bf16(synth.seed_for(2, 0), N, K)
+    x = synth.activations_bf16(synth.seed_for(2, 1), M, K)
+    W = bf16_dev(w)
+    X = bf16_dev(x)
+    parts = {}
+    head = {}
+    for fmt in ("q4k", "q8_0"):
+        blocks = ql.isq(fmt, W)
+        nb = blocks.numel()
+        R = copies_for(nb)
+        copies = [blocks] + [blocks.clone() for _ in range(R - 1)]
+        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        # parity on the live buffers (oracle on 256 sampled rows)
+        parity = check_gemv_parity(ql, fmt, w, x, blocks, Y, N)
+
+        def launch(i, fmt=fmt, copies=copies, Y=Y):
+            ql.qmatmul(fmt, copies[i % len(copies)], X, N, out=Y)
+
+        steps = args.steps
+        for i in range(args.warmup):
+            launch(i)
+        g = graph_of(torch, launch, steps)
+        torch.cuda.synchronize()
+        # the replay must reproduce the eager result (checked before timing)
+        y_eager = Y.clone()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(Y, y_eager), "graph replay differs from eager launch"
+        ms = time_graph(torch, g, 1, steps)   # exactly `steps` launches timed
+        ms_rep = time_graph(torch, g, 5, steps)
+        wbytes = nb
+        alg = nb + M * K * 2 + M * N * 4
+        head[fmt] = dict(ms=ms, ms_5reps=ms_rep, weight_bytes=wbytes, alg_bytes=alg, copies=R,
+                         weight_GBps=wbytes / (ms * 1e-3) / 1e9, alg_GBps=alg / (ms * 1e-3) / 1e9,
+                         parity_max_err=parity)
+        log(f"  {fmt} GEMV: {ms * 1e3:.2f} us/launch  {head[fmt]['weight_GBps']:.0f} GB/s weights  "
+            f"(max err {parity:.1e}, {R} copies)")
+        del copies, g, blocks
+        torch.cuda.empty_cache()
+
+    q4 = head["q4k"]
+    result.update({
+        "metric": "quantized GEMV weight GB/s (% HBM peak) + prefill qGEMM TOPS (% MFMA peak)",
+        "value": round(q4["weight_GBps"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": q4["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "q4k_decode_gemv", "N": N, "K": K, "M": M, "weights": "N(0,0.02) bf16 -> Q4K",
+                   "activations": "N(0,1) bf16", "weight_copies_rotated": q4["copies"],
+                   "launch": "HIP graph of `steps` launches"},
+        "roofline": {"bound": "hbm", "achieved": round(q4["alg_GBps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(q4["alg_GBps"] / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "gemv_kernel<Q4K, M=1>", "alg_bytes_per_launch": q4["alg_bytes"]},
+    })
+    parts["gemv_q8_0_14336x4096_m1"] = {
+        "us": round(head["q8_0"]["ms"] * 1e3, 3), "weight_GBps": round(head["q8_0"]["weight_GBps"], 1),
+        "hbm_frac": round(head["q8_0"]["alg_GBps"] / HBM_PEAK_GBPS, 4), "parity_max_err": head["q8_0"]["parity_max_err"]}
+    parts["gemv_q4k_14336x4096_m1"] = {
+        "us": round(q4["ms"] * 1e3, 3), "weight_GBps": round(q4["weight_GBps"], 1),
+        "hbm_frac": round(q4["alg_GBps"] / HBM_PEAK_GBPS, 4), "parity_max_err": q4["parity_max_err"]}
+    del W
+
+    if not args.quick:
+        parts.update(bench_parts(torch, ql, synth, dev, bf16_dev))
+    result["parts"] = parts
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(w, x)
+    print(json.dumps(result), flush=True)
+
+
+def check_gemv_parity(ql, fmt, w, x, blocks, Y, N):
+    import torch
+
+    import oracle
+
+    ql.qmatmul(fmt, blocks, torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(blocks.device), N, out=Y)
+    y = Y.cpu().numpy()
+    rng = np.random.Generator(np.random.PCG64(1))
+    rows = np.sort(rng.choice(N, 256, replace=False))
+    K = w.shape[1]
+    got = oracle.rows_of_buffer(fmt, blocks.cpu().numpy(), N, K, rows)
+    f = oracle.quantize(fmt, w[rows])
+    if not np.array_equal(got, oracle.pack(fmt, f, len(rows), K)):
+        raise SystemExit(f"parity failure: {fmt} ISQ bytes differ from the oracle")
+    Yr, den = oracle.matmul_a16(oracle.dequant(fmt, f, len(rows), K), x)
+    e = oracle.normalized_error(y[:, rows], Yr, den).max()
+    if e > 1e-3:
+        raise SystemExit(f"parity failure: {fmt} GEMV error {e:.3e}")
+    return float(e)
+
+
+def bench_parts(torch, ql, synth, dev, bf16_dev):
+    parts = {}
+
+    def timed_calls(launch, n_calls, reps=3):
+        for i in range(3):
+            launch(i)
+        g = graph_of(torch, launch, n_calls)
+        return time_graph(torch, g, reps, n_calls)
+
+    # batched decode: K=14336, N=4096, Q4K with outliers, M = 4, 16, 64
+    log("batched decode 4096x14336 q4k")
+    N, K = 4096, 14336
+    w = synth.weights_bf16(synth.seed_for(3, 0), N, K, outliers=True)
+    xs = synth.activations_bf16(synth.seed_for(3, 1), 64, K)
+    blocks = ql.isq("q4k", bf16_dev(w))
+    R = copies_for(blocks.numel())
+    copies = [blocks] + [blocks.clone() for _ in range(R - 1)]
+    for M in (4, 16, 64):
+        X = bf16_dev(xs[:M])
+        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        ms = timed_calls(lambda i: ql.qmatmul("q4k", copies[i % R], X, N, out=Y), 4 * R)
+        fl = 2.0 * M * N * K
+        parts[f"batched_q4k_m{M}"] = {
+            "us": round(ms * 1e3, 3), "path": "gemv" if M <= 8 else "mfma_bf16",
+            "weight_GBps": round(blocks.numel() / ms / 1e6, 1),
+            "hbm_frac": round((blocks.numel() + M * K * 2 + M * N * 4) / ms / 1e6 / HBM_PEAK_GBPS, 4),
+            "TFLOPs": round(fl / ms / 1e9, 2)}
+        log(f"  M={M}: {ms * 1e3:.2f} us")
+    del copies, blocks
+    torch.cuda.empty_cache()
+
+    # prefill: M=2048, K=4096, N=14336, Q8_0; bf16 MFMA path and int8 path
+    log("prefill 2048x4096x14336 q8_0")
+    M, N, K = 2048, 14336, 4096
+    w = synth.weights_bf16(synth.seed_for(4, 0), N, K)
+    X = bf16_dev(synth.activations_bf16(synth.seed_for(4, 1), M, K))
+    blocks = ql.isq("q8_0", bf16_dev(w))
+    copies = [blocks, blocks.clone()]
+    Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    ws = torch.empty(ql.workspace_bytes("q8_0", "mfma_i8", M, K), dtype=torch.uint8, device=dev)
+    fl = 2.0 * M * N * K
+    ms = timed_calls(lambda i: ql.qmatmul("q8_0", copies[i % 2], X, N, out=Y, path="mfma_bf16"), 10)
+    parts["prefill_q8_0_bf16_mfma"] = {"us": round(ms * 1e3, 2), "TFLOPs": round(fl / ms / 1e9, 1),
+                                       "mfma_frac": round(fl / ms / 1e9 / BF16_PEAK_TFLOPS, 4)}
+    log(f"  bf16 path: {ms * 1e3:.1f} us {fl / ms / 1e9:.0f} TFLOP/s")
+    ms = timed_calls(lambda i: ql.qmatmul("q8_0", copies[i % 2], X, N, out=Y, path="mfma_i8", workspace=ws), 10)
+    parts["prefill_q8_0_int8_mfma"] = {"us": round(ms * 1e3, 2), "TOPs": round(fl / ms / 1e9, 1),
+                                       "mfma_frac": round(fl / ms / 1e9 / INT8_PEAK_TOPS, 4),
+                                       "includes": "activation quantization"}
+    log(f"  int8 path: {ms * 1e3:.1f} us {fl / ms / 1e9:.0f} TOP/s")
+    del copies, blocks, ws, Y, X
+    torch.cuda.empty_cache()
+
+    # ISQ of the 32-layer decoder (Q4K) and the output head (Q6K)
+    log("decoder ISQ: 32 layers x 7 projections to q4k + 131072x5120 head to q6k")
+    shapes = [(4096, 4096), (1024, 4096), (1024, 4096), (4096, 4096), (14336, 4096), (14336, 4096),
+              (4096, 14336)]
+    Wl, Bl = [], []
+    read = write = 0
+    for layer in range(32):
+        for kind, (n, k) in enumerate(shapes):
+            Wt = synth.device_normal_bf16(synth.decoder_seed(layer, kind), (n, k), synth.W_SIGMA)
+            Wl.append(Wt)
+            Bl.append(torch.empty(ql.blocks_bytes("q4k", n, k), dtype=torch.uint8, device=dev))
+    Wh = synth.device_normal_bf16(synth.LM_HEAD_W_SEED, (131072, 5120), synth.W_SIGMA)
+    Bh = torch.empty(ql.blocks_bytes("q6k", 131072, 5120), dtype=torch.uint8, device=dev)
+    for Wt, Bt in zip(Wl, Bl):
+        read += Wt.numel() * 2
+        write += Bt.numel()
+    read += Wh.numel() * 2
+    write += Bh.numel()
+
+    def isq_all():
+        for Wt, Bt in zip(Wl, Bl):
+            ql.isq("q4k", Wt, out=Bt)
+        ql.isq("q6k", Wh, out=Bh)
+
+    isq_all()
+    torch.cuda.synchronize()
+    with Timer(torch) as t:
+        isq_all()
+    parts["isq_decoder_32l_q4k_plus_head_q6k"] = {
+        "ms": round(t.ms, 3), "read_bytes": read, "write_bytes": write,
+        "GBps": round((read + write) / t.ms / 1e6, 1),
+        "hbm_frac": round((read + write) / t.ms / 1e6 / HBM_PEAK_GBPS, 4)}
+    log(f"  ISQ all: {t.ms:.2f} ms ({(read + write) / t.ms / 1e6:.0f} GB/s)")
+    del Wl, Wh
+    torch.cuda.empty_cache()
+
+    # output head GEMV, M = 1 and M = 8 (Q6K)
+    xh = synth.activations_bf16(synth.LM_HEAD_X_SEED, 8, 5120)
+    Bh2 = [Bh, Bh.clone()]
+    for M in (1, 8):
+        X = bf16_dev(xh[:M])
+        Y = torch.empty((M, 131072), dtype=torch.float32, device=dev)
+        ms = timed_calls(lambda i: ql.qmatmul("q6k", Bh2[i % 2], X, 131072, out=Y), 8)
+        parts[f"lm_head_q6k_m{M}"] = {"us": round(ms * 1e3, 2), "weight_GBps": round(Bh.numel() / ms / 1e6, 1),
+                                      "hbm_frac": round((Bh.numel() + M * 5120 * 2 + M * 131072 * 4) / ms / 1e6 / HBM_PEAK_GBPS, 4)}
+        log(f"  lm_head M={M}: {ms * 1e3:.1f} us")
+    del Bh2
+
+    # equivalent decode tokens/s: every projection GEMV of the 32 layers + head
+    x1 = bf16_dev(synth.activations_bf16(9001, 1, 14336))
+    Ys = [torch.empty((1, n), dtype=torch.float32, device=dev) for (n, k) in shapes]
+    Yh = torch.empty((1, 131072), dtype=torch.float32, device=dev)
+
+    def token(_i):
+        for j, Bt in enumerate(Bl):
+            n, k = shapes[j % 7]
+            ql.qmatmul("q4k", Bt, x1[:, :k], n, out=Ys[j % 7])
+        ql.qmatmul("q6k", Bh, x1[:, :5120], 131072, out=Yh)
+
+    token(0)
+    g = graph_of(torch, token, 1)
+    ms = time_graph(torch, g, 10, 1)
+    total = sum(b.numel() for b in Bl) + Bh.numel()
+    parts["equiv_decode_tok_s"] = {"tok_s": round(1000.0 / ms, 1), "ms_per_token": round(ms, 4),
+                                   "weight_bytes_per_token": total,
+                                   "weight_GBps": round(total / ms / 1e6, 1),
+                                   "note": "225 quantized GEMVs per token (M=1); attention, norms, sampling excluded"}
+    log(f"  decode token: {ms:.3f} ms -> {1000 / ms:.0f} tok/s")
+    return parts
+
+
+def cpu_baseline(w, x):
+    """The oracle's quantized GEMV (unpack + exact dequant + fp64 matmul) on
+    the host cores, over whole 14336x4096 Q4K matrices, repeated for ~10 s."""
+    import oracle
+
+    N, K = w.shape
+    f = oracle.quantize("q4k", w)
+    buf = oracle.pack("q4k", f, N, K)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        g = oracle.unpack("q4k", buf, N, K)
+        Wd = oracle.dequant("q4k", g, N, K)
+        oracle.matmul_a16(Wd, x)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el > 10.0 or reps >= 50:
+            break
+    cores = len(os.sched_getaffinity(0))
+    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    return {"value": round(buf.size * reps / el / 1e9, 3), "unit": "GB/s", "cores": min(cores, threads),
+            "kind": "oracle",
+            "sample": f"{reps} full 14336x4096 Q4K GEMVs (M=1): unpack + fp64 dequant + fp64 matmul, {el:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

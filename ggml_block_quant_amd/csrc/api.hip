@@ -1,0 +1,262 @@
+// api.hip -- the C ABI declared in include/qlinear.h: argument checks, path
+// selection and launches.  Every check happens before any HIP call, so an
+// argument error never launches anything.
+#include "../../include/qlinear.h"
+#include "qlinear_internal.h"
+
+#include <stdint.h>
+
+namespace {
+
+bool implemented(int fmt) { return fmt == QFMT_Q8_0 || fmt == QFMT_Q4K || fmt == QFMT_Q6K; }
+bool known(int fmt) { return fmt >= QFMT_Q8_0 && fmt <= QFMT_Q8_1; }
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+// shape of a [rows][K] tensor in `fmt`: K % 256 (Q8_0: K % 32)
+int check_tensor(int fmt, int64_t rows, int64_t K, int64_t max_rows)
+{
+    if (rows < 1 || rows > max_rows || K < 1 || K > QLINEAR_MAX_K)
+        return Q_ESHAPE;
+    if (K % (fmt == QFMT_Q8_0 ? 32 : 256) != 0)
+        return Q_ESHAPE;
+    if (rows * K > kMaxElems)
+        return Q_ESHAPE;
+    return Q_OK;
+}
+
+int status_of(hipError_t e)
+{
+    if (e == hipSuccess)
+        return Q_OK;
+    if (e == hipErrorNotSupported)
+        return Q_ENOTSUP;
+    return Q_EHIP;
+}
+
+hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+int matmul_args(int fmt, const void *blocks, const void *X, const float *Y, int64_t M, int64_t N,
+                int64_t K)
+{
+    if (!known(fmt))
+        return Q_EINVAL;
+    if (!implemented(fmt))
+        return Q_ENOTSUP;
+    if (!blocks || !X || !Y)
+        return Q_EINVAL;
+    if (!aligned16(blocks) || !aligned16(X) || !aligned16(Y))
+        return Q_EALIGN;
+    if (M < 1 || M > QLINEAR_MAX_M || N < 1 || N > QLINEAR_MAX_N || K < 256 || K > QLINEAR_MAX_K ||
+        K % 256 != 0 || N * K > kMaxElems || M * K > kMaxElems || M * N > kMaxElems)
+        return Q_ESHAPE;
+    return Q_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t q_blocks_bytes(int fmt, int64_t N, int64_t K)
+{
+    if (!implemented(fmt) || check_tensor(fmt, N, K, QLINEAR_MAX_N) != Q_OK)
+        return 0;
+    return (size_t)ql::planes_of(fmt, N, K).total;
+}
+
+int isq_quantize(int fmt, const void *W_bf16, int64_t N, int64_t K, void *out_blocks, void *stream)
+{
+    if (!known(fmt))
+        return Q_EINVAL;
+    if (!implemented(fmt))
+        return Q_ENOTSUP;
+    if (!W_bf16 || !out_blocks)
+        return Q_EINVAL;
+    if (!aligned16(W_bf16) || !aligned16(out_blocks))
+        return Q_EALIGN;
+    const int st = check_tensor(fmt, N, K, QLINEAR_MAX_N);
+    if (st != Q_OK)
+        return st;
+    return status_of(ql::launch_isq(fmt, static_cast<const uint16_t *>(W_bf16), N, K,
+                                    static_cast<uint8_t *>(out_blocks), as_stream(stream)));
+}
+
+int q_act_quantize(const void *X_bf16, int64_t M, int64_t K, void *out_blocks, void *stream)
+{
+    if (!X_bf16 || !out_blocks)
+        return Q_EINVAL;
+    if (!aligned16(X_bf16) || !aligned16(out_blocks))
+        return Q_EALIGN;
+    const int st = check_tensor(QFMT_Q8_0, M, K, QLINEAR_MAX_M);
+    if (st != Q_OK)
+        return st;
+    return status_of(ql::launch_isq(ql::FMT_Q8_0, static_cast<const uint16_t *>(X_bf16), M, K,
+                                    static_cast<uint8_t *>(out_blocks), as_stream(stream)));
+}
+
+size_t qmatmul_workspace_bytes(int fmt, int path, int64_t M, int64_t K)
+{
+    if (path != QPATH_MFMA_I8 || fmt != QFMT_Q8_0)
+        return 0;
+    if (check_tensor(QFMT_Q8_0, M, K, QLINEAR_MAX_M) != Q_OK)
+        return 0;
+    return (size_t)ql::planes_of(ql::FMT_Q8_0, M, K).total;
+}
+
+int qmatmul_ex(int fmt, const void *blocks, const void *X_bf16, float *Y_fp32, int64_t M, int64_t N,
+               int64_t K, int path, void *workspace, size_t workspace_bytes, void *stream)
+{
+    int st = matmul_args(fmt, blocks, X_bf16, Y_fp32, M, N, K);
+    if (st != Q_OK)
+        return st;
+    const auto *B = static_cast<const uint8_t *>(blocks);
+    const auto *X = static_cast<const uint16_t *>(X_bf16);
+    const hipStream_t s = as_stream(stream);
+    switch (path) {
+    case QPATH_AUTO:
+        if (M <= 8) {
+            st = status_of(ql::launch_gemv(fmt, B, X, Y_fp32, (int)M, N, K, s));
+            if (st != Q_ENOTSUP)
+                return st;
+        }
+        return status_of(ql::launch_gemm_bf16(fmt, B, X, Y_fp32, M, N, K, s));
+    case QPATH_GEMV:
+        if (M > 8)
+            return Q_ESHAPE;
+        return status_of(ql::launch_gemv(fmt, B, X, Y_fp32, (int)M, N, K, s));
+    case QPATH_MFMA_BF16:
+        return status_of(ql::launch_gemm_bf16(fmt, B, X, Y_fp32, M, N, K, s));
+    case QPATH_MFMA_I8: {
+        if (fmt != QFMT_Q8_0)
+            return Q_ENOTSUP;
+        if (!workspace)
+            return Q_EINVAL;
+        if (!aligned16(workspace))
+            return Q_EALIGN;
+        if (workspace_bytes < qmatmul_workspace_bytes(fmt, path, M, K))
+            return Q_EINVAL;
+        auto *ws = static_cast<uint8_t *>(workspace);
+        st = status_of(ql::launch_isq(ql::FMT_Q8_0, X, M, K, ws, s));
+        if (st != Q_OK)
+            return st;
+        return status_of(ql::launch_gemm_i8(B, ws, Y_fp32, M, N, K, s));
+    }
+    default:
+        return Q_EINVAL;
+    }
+}
+
+int qmatmul(int fmt, const void *blocks, const void *X_bf16, float *Y_fp32, int64_t M, int64_t N, int64_t K,
+            void *stream)
+{
+    return qmatmul_ex(fmt, blocks, X_bf16, Y_fp32, M, N, K, QPATH_AUTO, nullptr, 0, stream);
+}
+
+int q_dequantize(int fmt, const void *blocks, int64_t N, int64_t K, float *W_fp32, void *stream)
+{
+    if (!known(fmt))
+        return Q_EINVAL;
+    if (!implemented(fmt))
+        return Q_ENOTSUP;
+    if (!blocks || !W_fp32)
+        return Q_EINVAL;
+    if (!aligned16(blocks) || !aligned16(W_fp32))
+        return Q_EALIGN;
+    const int st = check_tensor(fmt, N, K, QLINEAR_MAX_N);
+    if (st != Q_OK)
+        return st;
+    return status_of(ql::launch_dequant(fmt, static_cast<const uint8_t *>(blocks), N, K, W_fp32,
+                                        as_stream(stream)));
+}
+
+int isq_resolve_level(int level, int *out_fmt)
+{
+    if (!out_fmt)
+        return Q_EINVAL;
+    int f;
+    switch (level) {
+    case 2: f = QFMT_Q2K; break;
+    case 3: f = QFMT_Q3K; break;
+    case 4: f = QFMT_Q4K; break;
+    case 5: f = QFMT_Q5K; break;
+    case 6: f = QFMT_Q6K; break;
+    case 8: f = QFMT_Q8_0; break;
+    default: return Q_EINVAL;
+    }
+    *out_fmt = f;
+    return Q_OK;
+}
+
+int isq_sensitive_fmt(int model_default, int *out_fmt)
+{
+    if (!out_fmt)
+        return Q_EINVAL;
+    switch (model_default) {
+    case QFMT_Q2K:
+    case QFMT_Q3K:
+    case QFMT_Q4K:
+    case QFMT_Q4_0:
+    case QFMT_Q4_1:
+        *out_fmt = QFMT_Q6K;
+        return Q_OK;
+    case QFMT_Q5K:
+    case QFMT_Q6K:
+    case QFMT_Q8K:
+    case QFMT_Q5_0:
+    case QFMT_Q5_1:
+    case QFMT_Q8_0:
+    case QFMT_Q8_1:
+        *out_fmt = QFMT_Q8_0;
+        return Q_OK;
+    default:
+        return Q_EINVAL;
+    }
+}
+
+int isq_tensor_fmt(int level, int is_embedding_or_head, int explicit_fmt, int *out_fmt)
+{
+    if (!out_fmt)
+        return Q_EINVAL;
+    if (explicit_fmt >= 0) {
+        if (!known(explicit_fmt))
+            return Q_EINVAL;
+        *out_fmt = explicit_fmt;
+        return Q_OK;
+    }
+    int f;
+    int st = isq_resolve_level(level, &f);
+    if (st != Q_OK)
+        return st;
+    if (is_embedding_or_head) {
+        st = isq_sensitive_fmt(f, &f);
+        if (st != Q_OK)
+            return st;
+    }
+    *out_fmt = f;
+    return Q_OK;
+}
+
+int q_fmt_supported(int fmt) { return implemented(fmt) ? 1 : 0; }
+
+const char *q_fmt_name(int fmt)
+{
+    static const char *names[] = {"q8_0", "q4k", "q6k", "q2k", "q3k", "q5k",
+                                  "q8k", "q4_0", "q4_1", "q5_0", "q5_1", "q8_1"};
+    return known(fmt) ? names[fmt] : nullptr;
+}
+
+const char *q_strerror(int status)
+{
+    switch (status) {
+    case Q_OK: return "ok";
+    case Q_EINVAL: return "invalid argument (null pointer, unknown format or path, bad workspace)";
+    case Q_ESHAPE: return "shape out of range (M, N, K limits; K must be a multiple of 256)";
+    case Q_EALIGN: return "pointer not 16-byte aligned";
+    case Q_ENOTSUP: return "format or path not implemented for these arguments";
+    case Q_EHIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,423 @@
+// gemm.hip -- tiled quantized matmuls on the MFMA matrix cores for batched
+// decode and prefill (M > 8):
+//   * dequant-to-bf16 path: each 128 x 64 tile of W is decoded from its
+//     blocks in registers, rounded to bf16 and staged in LDS next to the
+//     bf16 X tile; v_mfma_f32_16x16x32_bf16 accumulates in fp32.
+//   * Q8_0 x Q8_0 int8 path: X is first quantized to Q8_0 blocks (the same
+//     rule as the weights); per 32-element block, v_mfma_i32_32x32x32_i8
+//     forms the exact integer dot products, which are scaled by
+//     d_w * d_x and accumulated in fp32.
+//
+// Page "Quantization types": section "NVFP4" (larger dense batches use
+// tiled matrix multiplication; activations are quantized once and reused
+// across output tiles) and section "FP8" (a weight tile is converted to
+// BF16 inside the GEMM; dynamic per-token activation quantizers feed the
+// quantized GEMM).
+//
+// Both kernels use 256 threads (4 wavefronts) per 128 (n) x BM (m) output
+// tile, K-steps of 64, and optionally split K over gridDim.z with fp32
+// atomics into a zeroed Y when the (n, m) tiles alone cannot fill 256 CUs.
+#include "qlinear_internal.h"
+
+namespace ql {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float h2f(uint32_t bits16)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits16 & 0xffffu));
+}
+
+// two fp32 -> one dword of two bf16 (round to nearest even, v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b)
+{
+    const f32x2_t f = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+// Decode the 32-element chunk c of row n into 16 bf16 pairs (elements
+// 2e, 2e+1 in dword e).
+template <int FMT>
+__device__ __forceinline__ void dequant_chunk(const uint8_t *__restrict__ B, int64_t sc_off,
+                                              int64_t d_off, int K, int64_t n, int c,
+                                              uint32_t out[16])
+{
+    if constexpr (FMT == FMT_Q8_0) {
+        const int64_t blk = n * (K / 32) + c;
+        const uint4 *p = reinterpret_cast<const uint4 *>(B + 32 * blk);
+        const uint4 c0 = p[0], c1 = p[1];
+        const float d = h2f(*reinterpret_cast<const uint16_t *>(B + sc_off + 2 * blk));
+        const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            out[2 * i] = pack_bf16(d * (float)(int8_t)(w[i]), d * (float)(int8_t)(w[i] >> 8));
+            out[2 * i + 1] = pack_bf16(d * (float)(int8_t)(w[i] >> 16), d * (float)(int8_t)(w[i] >> 24));
+        }
+    } else if constexpr (FMT == FMT_Q4K) {
+        const int64_t sub = n * (K / 32) + c;
+        const uint4 cw = *reinterpret_cast<const uint4 *>(B + 16 * sub);
+        const uint4 h = *reinterpret_cast<const uint4 *>(B + sc_off + 16 * (sub >> 3));
+        const int j = c & 7;
+        const uint32_t sc = __builtin_amdgcn_ubfe(h.y, 4 * j, 4) | (__builtin_amdgcn_ubfe(h.w, 2 * j, 2) << 4);
+        const uint32_t mq = __builtin_amdgcn_ubfe(h.z, 4 * j, 4) | (__builtin_amdgcn_ubfe(h.w, 16 + 2 * j, 2) << 4);
+        const float S = h2f(h.x) * (float)sc;
+        const float Mn = h2f(h.x >> 16) * (float)mq;
+        const uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+#pragma unroll
+            for (int p = 0; p < 4; p++)
+                out[4 * q + p] = pack_bf16(fmaf(S, (float)((w[q] >> (4 * p)) & 15u), -Mn),
+                                           fmaf(S, (float)((w[q] >> (16 + 4 * p)) & 15u), -Mn));
+    } else {
+        const int64_t grp = n * (K / 256) + (c >> 3);
+        const int cc = c & 7;
+        const uint8_t *Cg = B + 192 * grp;
+        const uint4 lw = *reinterpret_cast<const uint4 *>(Cg + 16 * cc);
+        const uint2 hw = *reinterpret_cast<const uint2 *>(Cg + 128 + 8 * cc);
+        const uint32_t sc2 = *reinterpret_cast<const uint16_t *>(B + sc_off + 16 * grp + 2 * cc);
+        const float d = h2f(*reinterpret_cast<const uint16_t *>(B + d_off + 2 * grp));
+        const float Sab[2] = {d * (float)(int8_t)(sc2 & 0xffu), d * (float)(int8_t)(sc2 >> 8)};
+        const uint32_t l4[4] = {lw.x, lw.y, lw.z, lw.w};
+        const uint32_t h2[2] = {hw.x, hw.y};
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const int o = q & 1;
+            const float S = Sab[q >> 1];
+#pragma unroll
+            for (int p = 0; p < 4; p++) {
+                const int sh = 8 * o + 2 * p;
+                const int u0 = (int)(((l4[q] >> (4 * p)) & 15u) | ((h2[q >> 1] >> sh) & 3u) << 4);
+                const int u1 = (int)(((l4[q] >> (16 + 4 * p)) & 15u) | ((h2[q >> 1] >> (16 + sh)) & 3u) << 4);
+                out[4 * q + p] = pack_bf16(S * (float)(u0 - 32), S * (float)(u1 - 32));
+            }
+        }
+    }
+}
+
+constexpr int BN = 128;
+constexpr int BK = 64;
+constexpr int PITCH = BK + 8;  // bf16 elements per LDS row (144 bytes: 16-byte aligned rows)
+
+template <int FMT, int BM>
+__global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint8_t *__restrict__ B, int64_t sc_off,
+                                                        int64_t d_off, const uint16_t *__restrict__ X,
+                                                        float *__restrict__ Y, int M, int N, int K,
+                                                        int kt_per_split)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t sW[BN * PITCH];
+    __shared__ __attribute__((aligned(16))) uint16_t sX[BM * PITCH];
+
+    constexpr int WN = BM >= 128 ? 2 : 4;  // waves along n
+    constexpr int WM = 4 / WN;             // waves along m
+    constexpr int TN = BN / WN / 16;       // 16-row MFMA tiles per wave along n
+    constexpr int TM = BM / WM / 16;       // along m
+    static_assert(TM >= 1 && TN >= 1, "tile shape");
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wn = wave % WN, wm = wave / WN;
+    const int64_t n0 = (int64_t)blockIdx.x * BN;
+    const int m0 = blockIdx.y * BM;
+    const int nkt = K / BK;
+    const int kt0 = blockIdx.z * kt_per_split;
+    const int kt1 = min(nkt, kt0 + kt_per_split);
+
+    f32x4_t acc[TN][TM];
+#pragma unroll
+    for (int i = 0; i < TN; i++)
+#pragma unroll
+        for (int j = 0; j < TM; j++)
+            acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    for (int kt = kt0; kt < kt1; kt++) {
+        const int k0 = kt * BK;
+        {  // W tile: thread -> (row tid/2, 32-element half tid%2)
+            const int r = tid >> 1, h = tid & 1;
+            uint32_t v[16];
+            if (n0 + r < N) {
+                dequant_chunk<FMT>(B, sc_off, d_off, K, n0 + r, (k0 >> 5) + h, v);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 16; e++)
+                    v[e] = 0u;
+            }
+            uint4 *dst = reinterpret_cast<uint4 *>(sW + r * PITCH + 32 * h);
+#pragma unroll
+            for (int q = 0; q < 4; q++)
+                dst[q] = make_uint4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+        }
+        for (int i = tid; i < BM * 8; i += 256) {  // X tile: BM rows x 8 uint4
+            const int r = i >> 3, q = i & 7;
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (m0 + r < M)
+                v = *reinterpret_cast<const uint4 *>(X + (int64_t)(m0 + r) * K + k0 + 8 * q);
+            *reinterpret_cast<uint4 *>(sX + r * PITCH + 8 * q) = v;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < BK; kk += 32) {
+            bf16x8_t a[TN], b[TM];
+#pragma unroll
+            for (int i = 0; i < TN; i++)
+                a[i] = *reinterpret_cast<const bf16x8_t *>(
+                    sW + (wn * TN * 16 + 16 * i + (lane & 15)) * PITCH + kk + 8 * (lane >> 4));
+#pragma unroll
+            for (int j = 0; j < TM; j++)
+                b[j] = *reinterpret_cast<const bf16x8_t *>(
+                    sX + (wm * TM * 16 + 16 * j + (lane & 15)) * PITCH + kk + 8 * (lane >> 4));
+#pragma unroll
+            for (int i = 0; i < TN; i++)
+#pragma unroll
+                for (int j = 0; j < TM; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+        __syncthreads();
+    }
+
+    // acc[i][j] element r = D[n = 4*(lane/16) + r][m = lane%16] of its tile
+    const bool atomic = gridDim.z > 1;
+    const bool vec4 = (N & 3) == 0;  // rows of Y 16-byte aligned
+#pragma unroll
+    for (int i = 0; i < TN; i++)
+#pragma unroll
+        for (int j = 0; j < TM; j++) {
+            const int64_t n = n0 + wn * TN * 16 + 16 * i + 4 * (lane >> 4);
+            const int m = m0 + wm * TM * 16 + 16 * j + (lane & 15);
+            if (m >= M)
+                continue;
+            float *y = Y + (int64_t)m * N + n;
+            if (!atomic && vec4 && n + 3 < N) {
+                *reinterpret_cast<f32x4_t *>(y) = acc[i][j];
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; r++)
+                    if (n + r < N) {
+                        if (atomic)
+                            atomicAdd(y + r, acc[i][j][r]);
+                        else
+                            y[r] = acc[i][j][r];
+                    }
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------
+// Q8_0 x Q8_0 int8 path
+// ---------------------------------------------------------------------------
+constexpr int IBM = 128;    // m tile
+constexpr int IPITCH = 80;  // bytes per LDS row of 64 codes (16-byte aligned, skewed banks)
+
+__global__ __launch_bounds__(256) void gemm_i8_kernel(const int8_t *__restrict__ Wq,
+                                                      const uint16_t *__restrict__ Wd,
+                                                      const int8_t *__restrict__ Xq,
+                                                      const uint16_t *__restrict__ Xd,
+                                                      float *__restrict__ Y, int M, int N, int K,
+                                                      int kt_per_split)
+{
+    __shared__ __attribute__((aligned(16))) int8_t sW[BN * IPITCH];
+    __shared__ __attribute__((aligned(16))) int8_t sX[IBM * IPITCH];
+    __shared__ __attribute__((aligned(16))) float sDw[2][BN];
+    __shared__ __attribute__((aligned(16))) float sDx[2][IBM];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wn = wave & 1, wm = wave >> 1;  // 2 x 2 waves, 64 x 64 each
+    const int64_t n0 = (int64_t)blockIdx.x * BN;
+    const int m0 = blockIdx.y * IBM;
+    const int nkt = K / BK;
+    const int kt0 = blockIdx.z * kt_per_split;
+    const int kt1 = min(nkt, kt0 + kt_per_split);
+    const int KB = K / 32;
+
+    float acc[2][2][16];
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+                acc[i][j][r] = 0.0f;
+    const i32x16_t zero = {};
+
+    for (int kt = kt0; kt < kt1; kt++) {
+        const int k0 = kt * BK;
+        {  // codes: 128 rows x 64 bytes per operand = 512 uint4; thread -> 2 of each
+#pragma unroll
+            for (int t = 0; t < 2; t++) {
+                const int i = tid + 256 * t, r = i >> 2, q = i & 3;
+                uint4 vw = make_uint4(0u, 0u, 0u, 0u), vx = make_uint4(0u, 0u, 0u, 0u);
+                if (n0 + r < N)
+                    vw = *reinterpret_cast<const uint4 *>(Wq + (n0 + r) * K + k0 + 16 * q);
+                if (m0 + r < M)
+                    vx = *reinterpret_cast<const uint4 *>(Xq + (int64_t)(m0 + r) * K + k0 + 16 * q);
+                *reinterpret_cast<uint4 *>(sW + r * IPITCH + 16 * q) = vw;
+                *reinterpret_cast<uint4 *>(sX + r * IPITCH + 16 * q) = vx;
+            }
+            const int r = tid >> 1, b = tid & 1;
+            sDw[b][r] = n0 + r < N ? h2f(Wd[(n0 + r) * KB + 2 * kt + b]) : 0.0f;
+            sDx[b][r] = m0 + r < M ? h2f(Xd[(int64_t)(m0 + r) * KB + 2 * kt + b]) : 0.0f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int blk = 0; blk < 2; blk++) {
+            i32x4_t a[2], bx[2];
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+                a[i] = *reinterpret_cast<const i32x4_t *>(sW + (wn * 64 + 32 * i + (lane & 31)) * IPITCH +
+                                                          32 * blk + 16 * (lane >> 5));
+#pragma unroll
+            for (int j = 0; j < 2; j++)
+                bx[j] = *reinterpret_cast<const i32x4_t *>(sX + (wm * 64 + 32 * j + (lane & 31)) * IPITCH +
+                                                           32 * blk + 16 * (lane >> 5));
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int j = 0; j < 2; j++) {
+                    const i32x16_t d = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], bx[j], zero, 0, 0, 0);
+                    const float dx = sDx[blk][wm * 64 + 32 * j + (lane & 31)];
+#pragma unroll
+                    for (int g = 0; g < 4; g++) {
+                        // rows 8g + 4*(lane/32) + 0..3 of the 32 x 32 tile
+                        const f32x4_t dw = *reinterpret_cast<const f32x4_t *>(
+                            &sDw[blk][wn * 64 + 32 * i + 8 * g + 4 * (lane >> 5)]);
+#pragma unroll
+                        for (int e = 0; e < 4; e++)
+                            acc[i][j][4 * g + e] = fmaf((float)d[4 * g + e], dw[e] * dx, acc[i][j][4 * g + e]);
+                    }
+                }
+        }
+        __syncthreads();
+    }
+
+    // acc[i][j][4g+e] = D[n = 8g + 4*(lane/32) + e][m = lane%32] of its 32 x 32 tile
+    const bool atomic = gridDim.z > 1;
+    const bool vec4 = (N & 3) == 0;
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const int m = m0 + wm * 64 + 32 * j + (lane & 31);
+            if (m >= M)
+                continue;
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+                const int64_t n = n0 + wn * 64 + 32 * i + 8 * g + 4 * (lane >> 5);
+                float *y = Y + (int64_t)m * N + n;
+                if (!atomic && vec4 && n + 3 < N) {
+                    *reinterpret_cast<f32x4_t *>(y) =
+                        f32x4_t{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; e++)
+                        if (n + e < N) {
+                            if (atomic)
+                                atomicAdd(y + e, acc[i][j][4 * g + e]);
+                            else
+                                y[e] = acc[i][j][4 * g + e];
+                        }
+                }
+            }
+        }
+}
+
+// Zero-fill of Y before a split-K accumulation (a kernel, not a memset, so
+// that the call can be captured in a HIP graph).
+__global__ void zero_kernel(float *__restrict__ p, int64_t n)
+{
+    const int64_t n4 = n / 4;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride)
+        reinterpret_cast<float4 *>(p)[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        for (int64_t i = 4 * n4; i < n; i++)
+            p[i] = 0.0f;
+}
+
+// Split K so that at least ~2 workgroups per CU exist.
+inline int splits_for(int64_t tiles, int nkt)
+{
+    int s = 1;
+    while (tiles * s < 512 && s < 16 && nkt / (2 * s) >= 2)
+        s *= 2;
+    return s;
+}
+
+hipError_t zero_y(float *Y, int64_t count, hipStream_t s)
+{
+    int64_t g = (count / 4 + 255) / 256;
+    g = g < 1 ? 1 : (g > 65536 ? 65536 : g);
+    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)g), dim3(256), 0, s, Y, count);
+    return hipGetLastError();
+}
+
+template <int FMT, int BM>
+hipError_t go_bf16(const uint8_t *blocks, const Planes &p, const uint16_t *X, float *Y, int64_t M,
+                   int64_t N, int64_t K, hipStream_t s)
+{
+    const int64_t gx = (N + BN - 1) / BN, gy = (M + BM - 1) / BM;
+    const int nkt = (int)(K / BK);
+    const int splits = splits_for(gx * gy, nkt);
+    const int per = (nkt + splits - 1) / splits;
+    if (splits > 1) {
+        const hipError_t e = zero_y(Y, M * N, s);
+        if (e != hipSuccess)
+            return e;
+    }
+    hipLaunchKernelGGL((gemm_bf16_kernel<FMT, BM>), dim3((unsigned)gx, (unsigned)gy, (unsigned)splits), dim3(256), 0, s,
+                       blocks, p.scales, p.d, X, Y, (int)M, (int)N, (int)K, per);
+    return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t bf16_by_m(const uint8_t *blocks, const Planes &p, const uint16_t *X, float *Y, int64_t M,
+                     int64_t N, int64_t K, hipStream_t s)
+{
+    if (M <= 16)
+        return go_bf16<FMT, 16>(blocks, p, X, Y, M, N, K, s);
+    if (M <= 32)
+        return go_bf16<FMT, 32>(blocks, p, X, Y, M, N, K, s);
+    if (M <= 64)
+        return go_bf16<FMT, 64>(blocks, p, X, Y, M, N, K, s);
+    return go_bf16<FMT, 128>(blocks, p, X, Y, M, N, K, s);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_bf16(int fmt, const uint8_t *blocks, const uint16_t *X, float *Y, int64_t M,
+                            int64_t N, int64_t K, hipStream_t s)
+{
+    const Planes p = planes_of(fmt, N, K);
+    if (fmt == FMT_Q4K)
+        return bf16_by_m<FMT_Q4K>(blocks, p, X, Y, M, N, K, s);
+    if (fmt == FMT_Q6K)
+        return bf16_by_m<FMT_Q6K>(blocks, p, X, Y, M, N, K, s);
+    return bf16_by_m<FMT_Q8_0>(blocks, p, X, Y, M, N, K, s);
+}
+
+hipError_t launch_gemm_i8(const uint8_t *wblocks, const uint8_t *xblocks, float *Y, int64_t M, int64_t N,
+                          int64_t K, hipStream_t s)
+{
+    const Planes pw = planes_of(FMT_Q8_0, N, K), px = planes_of(FMT_Q8_0, M, K);
+    const int64_t gx = (N + BN - 1) / BN, gy = (M + IBM - 1) / IBM;
+    const int nkt = (int)(K / BK);
+    const int splits = splits_for(gx * gy, nkt);
+    const int per = (nkt + splits - 1) / splits;
+    if (splits > 1) {
+        const hipError_t e = zero_y(Y, M * N, s);
+        if (e != hipSuccess)
+            return e;
+    }
+    hipLaunchKernelGGL(gemm_i8_kernel, dim3((unsigned)gx, (unsigned)gy, (unsigned)splits), dim3(256), 0, s,
+                       reinterpret_cast<const int8_t *>(wblocks),
+                       reinterpret_cast<const uint16_t *>(wblocks + pw.scales),
+                       reinterpret_cast<const int8_t *>(xblocks),
+                       reinterpret_cast<const uint16_t *>(xblocks + px.scales), Y, (int)M, (int)N, (int)K, per);
+    return hipGetLastError();
+}
+
+}  // namespace ql

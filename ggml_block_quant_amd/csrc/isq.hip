@@ -1,0 +1,312 @@
+// isq.hip -- block-parallel in-situ quantization (ISQ) of bf16 weights into
+// Q8_0, Q4K and Q6K blocks, and the exact dequantizer used as a test aid.
+//
+// Page "Quantization types" (mistral.rs reference): ISQ quantizes weights at
+// load time (introduction: "--isq N forces runtime ISQ"); the formats are
+// q8_0 ("Legacy GGML types"), q4k and q6k ("Q*K family").
+//
+// Work split: one lane owns 8 consecutive elements of the flattened [N][K]
+// tensor (one 16-byte load).  A Q8_0 block (32 elements) is 4 lanes; a Q4K
+// or Q6K group (256 elements) is 32 lanes, so every reduction runs inside a
+// wavefront with cross-lane shuffles and no LDS.  Codes leave as one dword
+// per lane, so stores are coalesced too.
+//
+// Arithmetic is binary32 IEEE, one rounding per operation, in exactly the
+// order of the reference definition, so that codes and scales are
+// bit-exact:  this file is compiled with -ffp-contract=off; x / y is the
+// correctly rounded division; max/min are exact; roundf rounds half away
+// from zero; fp16 scales are clamped to 65504 and converted with
+// v_cvt_f16_f32 (round to nearest even, subnormals kept).  A -0.0 input is
+// read as +0.0 (x + 0.0f), so the sign of a zero never reaches a scale.
+#include "qlinear_internal.h"
+
+namespace ql {
+namespace {
+
+__device__ __forceinline__ void load8(const uint4 v, float x[8])
+{
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        x[2 * i] = __uint_as_float(w[i] << 16) + 0.0f;
+        x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u) + 0.0f;
+    }
+}
+
+// F16 of a non-negative scale: clamp to the largest finite binary16, round
+// to nearest even.  Returns the bits; *back receives the fp16 value as fp32.
+__device__ __forceinline__ uint32_t scale_f16(float v, float *back)
+{
+    v = fminf(v, 65504.0f);
+    const _Float16 h = (_Float16)v;
+    *back = (float)h;
+    return (uint32_t)__builtin_bit_cast(uint16_t, h);
+}
+
+// Round half away from zero, then clamp to [lo, hi] (integer-valued bounds).
+__device__ __forceinline__ int code_of(float v, float lo, float hi)
+{
+    float r = roundf(v);
+    r = fminf(fmaxf(r, lo), hi);
+    return (int)r;
+}
+
+// Even elements of an octet in the low half of a dword, odd ones in the high
+// half: nibble p holds element 2p (p < 4) or 2(p-4)+1 (p >= 4).
+__device__ __forceinline__ uint32_t pack_nibbles(const int q[8])
+{
+    return (uint32_t)q[0] | (uint32_t)q[2] << 4 | (uint32_t)q[4] << 8 | (uint32_t)q[6] << 12 |
+           (uint32_t)q[1] << 16 | (uint32_t)q[3] << 20 | (uint32_t)q[5] << 24 |
+           (uint32_t)q[7] << 28;
+}
+
+// ---------------------------------------------------------------------------
+// Q8_0: d = F16(max|x| / 127), q = clamp(RHA(x / d), -127, 127); 4 lanes/block
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void isq_q8_0_kernel(const uint4 *__restrict__ W, int64_t tasks,
+                                                       uint2 *__restrict__ codes,
+                                                       uint16_t *__restrict__ scales)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < tasks; t += stride) {
+        float x[8];
+        load8(W[t], x);
+        float a = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+            a = fmaxf(a, fabsf(x[i]));
+        a = fmaxf(a, __shfl_xor(a, 1));
+        a = fmaxf(a, __shfl_xor(a, 2));
+        float df;
+        const uint32_t d16 = scale_f16(a / 127.0f, &df);
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int q0 = df == 0.0f ? 0 : code_of(x[i] / df, -127.0f, 127.0f);
+            const int q1 = df == 0.0f ? 0 : code_of(x[i + 4] / df, -127.0f, 127.0f);
+            lo |= ((uint32_t)q0 & 0xffu) << (8 * i);
+            hi |= ((uint32_t)q1 & 0xffu) << (8 * i);
+        }
+        codes[t] = make_uint2(lo, hi);
+        if ((t & 3) == 0)
+            scales[t >> 2] = (uint16_t)d16;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Q4K: plain min/max affine rule per sub-block of 32; 32 lanes per group
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void isq_q4k_kernel(const uint4 *__restrict__ W, int64_t tasks,
+                                                      uint32_t *__restrict__ codes,
+                                                      uint4 *__restrict__ headers)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < tasks; t += stride) {
+        float x[8];
+        load8(W[t], x);
+        float lo = 0.0f, hi = x[0];
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            lo = fminf(lo, x[i]);
+            hi = fmaxf(hi, x[i]);
+        }
+        lo = fminf(lo, __shfl_xor(lo, 1));
+        lo = fminf(lo, __shfl_xor(lo, 2));
+        hi = fmaxf(hi, __shfl_xor(hi, 1));
+        hi = fmaxf(hi, __shfl_xor(hi, 2));
+        const float s = (hi - lo) / 15.0f;
+        const float m = 0.0f - lo;
+        float smax = s, mmax = m;
+#pragma unroll
+        for (int k = 4; k <= 16; k <<= 1) {
+            smax = fmaxf(smax, __shfl_xor(smax, k));
+            mmax = fmaxf(mmax, __shfl_xor(mmax, k));
+        }
+        float df, dmf;
+        const uint32_t d16 = scale_f16(smax / 63.0f, &df);
+        const uint32_t dm16 = scale_f16(mmax / 63.0f, &dmf);
+        const int sc = df > 0.0f ? code_of(s / df, 0.0f, 63.0f) : 0;
+        const int mq = dmf > 0.0f ? code_of(m / dmf, 0.0f, 63.0f) : 0;
+        const float S = df * (float)sc;
+        const float M = dmf * (float)mq;
+        int q[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const float u = x[i] + M;
+            q[i] = S > 0.0f ? code_of(u / S, 0.0f, 15.0f) : 0;
+        }
+        codes[t] = pack_nibbles(q);
+
+        const int l = (int)(t & 31), j = l >> 2, w = l & 3;
+        uint32_t h0 = w == 0 ? ((uint32_t)sc & 15u) << (4 * j) : 0u;
+        uint32_t h1 = w == 0 ? ((uint32_t)mq & 15u) << (4 * j) : 0u;
+        uint32_t h2 = w == 0 ? (((uint32_t)sc >> 4) << (2 * j)) | (((uint32_t)mq >> 4) << (16 + 2 * j))
+                             : 0u;
+#pragma unroll
+        for (int k = 4; k <= 16; k <<= 1) {
+            h0 |= __shfl_xor(h0, k);
+            h1 |= __shfl_xor(h1, k);
+            h2 |= __shfl_xor(h2, k);
+        }
+        if (l == 0)
+            headers[t >> 5] = make_uint4(d16 | (dm16 << 16), h0, h1, h2);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Q6K: symmetric 6-bit codes, 16 sub-blocks of 16, int8 sub-scales, fp16 d
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void isq_q6k_kernel(const uint4 *__restrict__ W, int64_t tasks,
+                                                      uint8_t *__restrict__ C,
+                                                      int8_t *__restrict__ SC,
+                                                      uint16_t *__restrict__ D)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < tasks; t += stride) {
+        float x[8];
+        load8(W[t], x);
+        float a = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+            a = fmaxf(a, fabsf(x[i]));
+        a = fmaxf(a, __shfl_xor(a, 1));  // sub-block of 16 = 2 lanes
+        const float s = a / 31.0f;
+        float smax = s;
+#pragma unroll
+        for (int k = 2; k <= 16; k <<= 1)
+            smax = fmaxf(smax, __shfl_xor(smax, k));
+        float df;
+        const uint32_t d16 = scale_f16(smax / 127.0f, &df);
+        const int sc = df > 0.0f ? code_of(s / df, 0.0f, 127.0f) : 0;
+        const float S = df * (float)sc;
+        int u[8], lo4[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            u[i] = (S > 0.0f ? code_of(x[i] / S, -32.0f, 31.0f) : 0) + 32;
+            lo4[i] = u[i] & 15;
+        }
+        const int64_t g = t >> 5;
+        const int l = (int)(t & 31), c = l >> 2, w = l & 3, o = w & 1;
+        uint8_t *Cg = C + 192 * g;
+        *reinterpret_cast<uint32_t *>(Cg + 4 * l) = pack_nibbles(lo4);
+        uint32_t hb = 0;
+#pragma unroll
+        for (int p = 0; p < 4; p++) {
+            hb |= (uint32_t)(u[2 * p] >> 4) << (8 * o + 2 * p);
+            hb |= (uint32_t)(u[2 * p + 1] >> 4) << (16 + 8 * o + 2 * p);
+        }
+        hb |= __shfl_xor(hb, 1);
+        if (o == 0)
+            *reinterpret_cast<uint32_t *>(Cg + 128 + 8 * c + 4 * (w >> 1)) = hb;
+        if ((l & 1) == 0)
+            SC[16 * g + (l >> 1)] = (int8_t)sc;
+        if (l == 0)
+            D[g] = (uint16_t)d16;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Exact dequantization to fp32 (test aid), same lane split
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float h2f(uint32_t bits16) { return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16); }
+
+__device__ __forceinline__ void unpack_nibbles(uint32_t d, int q[8])
+{
+#pragma unroll
+    for (int p = 0; p < 4; p++) {
+        q[2 * p] = (d >> (4 * p)) & 15;
+        q[2 * p + 1] = (d >> (16 + 4 * p)) & 15;
+    }
+}
+
+__global__ __launch_bounds__(256) void dequant_kernel(int fmt, const uint8_t *__restrict__ B,
+                                                      int64_t tasks, int64_t scales_off,
+                                                      int64_t d_off, float4 *__restrict__ out)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < tasks; t += stride) {
+        float v[8];
+        if (fmt == FMT_Q8_0) {
+            const uint2 c = reinterpret_cast<const uint2 *>(B)[t];
+            const float d = h2f(reinterpret_cast<const uint16_t *>(B + scales_off)[t >> 2]);
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                v[i] = d * (float)(int8_t)(c.x >> (8 * i));
+                v[i + 4] = d * (float)(int8_t)(c.y >> (8 * i));
+            }
+        } else if (fmt == FMT_Q4K) {
+            const uint32_t c = reinterpret_cast<const uint32_t *>(B)[t];
+            const uint4 h = reinterpret_cast<const uint4 *>(B + scales_off)[t >> 5];
+            const int j = (int)((t & 31) >> 2);
+            const uint32_t sc = ((h.y >> (4 * j)) & 15u) | ((h.w >> (2 * j)) & 3u) << 4;
+            const uint32_t mq = ((h.z >> (4 * j)) & 15u) | ((h.w >> (16 + 2 * j)) & 3u) << 4;
+            const float S = h2f(h.x & 0xffffu) * (float)sc;
+            const float M = h2f(h.x >> 16) * (float)mq;
+            int q[8];
+            unpack_nibbles(c, q);
+#pragma unroll
+            for (int i = 0; i < 8; i++)
+                v[i] = fmaf(S, (float)q[i], -M);  // one rounding of the exact value
+        } else {
+            const int64_t g = t >> 5;
+            const int l = (int)(t & 31), c = l >> 2, w = l & 3, o = w & 1;
+            const uint8_t *Cg = B + 192 * g;
+            const uint32_t lo = *reinterpret_cast<const uint32_t *>(Cg + 4 * l);
+            const uint32_t hd = *reinterpret_cast<const uint32_t *>(Cg + 128 + 8 * c + 4 * (w >> 1));
+            const int sc = reinterpret_cast<const int8_t *>(B + scales_off)[16 * g + (l >> 1)];
+            const float S = h2f(reinterpret_cast<const uint16_t *>(B + d_off)[g]) * (float)sc;
+            int q[8];
+            unpack_nibbles(lo, q);
+#pragma unroll
+            for (int p = 0; p < 4; p++) {
+                q[2 * p] |= (int)((hd >> (8 * o + 2 * p)) & 3u) << 4;
+                q[2 * p + 1] |= (int)((hd >> (16 + 8 * o + 2 * p)) & 3u) << 4;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; i++)
+                v[i] = S * (float)(q[i] - 32);
+        }
+        out[2 * t] = make_float4(v[0], v[1], v[2], v[3]);
+        out[2 * t + 1] = make_float4(v[4], v[5], v[6], v[7]);
+    }
+}
+
+inline unsigned grid_for(int64_t tasks)
+{
+    int64_t b = (tasks + 255) / 256;
+    const int64_t cap = int64_t(1) << 22;
+    return (unsigned)(b < 1 ? 1 : (b > cap ? cap : b));
+}
+
+}  // namespace
+
+hipError_t launch_isq(int fmt, const uint16_t *W, int64_t N, int64_t K, uint8_t *out, hipStream_t s)
+{
+    const int64_t tasks = N * K / 8;
+    const Planes p = planes_of(fmt, N, K);
+    const uint4 *w = reinterpret_cast<const uint4 *>(W);
+    if (fmt == FMT_Q8_0)
+        hipLaunchKernelGGL(isq_q8_0_kernel, dim3(grid_for(tasks)), dim3(256), 0, s, w, tasks,
+                           reinterpret_cast<uint2 *>(out),
+                           reinterpret_cast<uint16_t *>(out + p.scales));
+    else if (fmt == FMT_Q4K)
+        hipLaunchKernelGGL(isq_q4k_kernel, dim3(grid_for(tasks)), dim3(256), 0, s, w, tasks,
+                           reinterpret_cast<uint32_t *>(out),
+                           reinterpret_cast<uint4 *>(out + p.scales));
+    else
+        hipLaunchKernelGGL(isq_q6k_kernel, dim3(grid_for(tasks)), dim3(256), 0, s, w, tasks, out,
+                           reinterpret_cast<int8_t *>(out + p.scales),
+                           reinterpret_cast<uint16_t *>(out + p.d));
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant(int fmt, const uint8_t *blocks, int64_t N, int64_t K, float *W, hipStream_t s)
+{
+    const int64_t tasks = N * K / 8;
+    const Planes p = planes_of(fmt, N, K);
+    hipLaunchKernelGGL(dequant_kernel, dim3(grid_for(tasks)), dim3(256), 0, s, fmt, blocks, tasks,
+                       p.scales, p.d, reinterpret_cast<float4 *>(W));
+    return hipGetLastError();
+}
+
+}  // namespace ql

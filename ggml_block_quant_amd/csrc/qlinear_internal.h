@@ -1,0 +1,53 @@
+// qlinear_internal.h -- shared declarations of the HIP implementation of the
+// block-quantized linear layer (gfx950).  Host launchers live next to their
+// kernels; api.hip validates arguments and dispatches to them.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ql {
+
+enum Fmt { FMT_Q8_0 = 0, FMT_Q4K = 1, FMT_Q6K = 2 };
+
+// Byte offsets of the planes of a [N][K] block buffer (see q_blocks_bytes in
+// the public header).  G = N*K/256 groups.
+struct Planes {
+    int64_t codes;   // always 0
+    int64_t scales;  // Q8_0: fp16 d per 32; Q4K: 16-byte headers; Q6K: int8 sub-scales
+    int64_t d;       // Q6K only: fp16 d per group
+    int64_t total;
+};
+
+inline Planes planes_of(int fmt, int64_t N, int64_t K)
+{
+    const int64_t E = N * K;
+    Planes p{0, 0, 0, 0};
+    if (fmt == FMT_Q8_0) {
+        p.scales = E;
+        p.total = E + E / 16;  // E/32 scales of 2 bytes
+    } else if (fmt == FMT_Q4K) {
+        const int64_t G = E / 256;
+        p.scales = 128 * G;
+        p.total = 144 * G;
+    } else {
+        const int64_t G = E / 256;
+        p.scales = 192 * G;
+        p.d = 208 * G;
+        p.total = 210 * G;
+    }
+    return p;
+}
+
+hipError_t launch_isq(int fmt, const uint16_t *W, int64_t N, int64_t K, uint8_t *out,
+                      hipStream_t s);
+hipError_t launch_dequant(int fmt, const uint8_t *blocks, int64_t N, int64_t K, float *W,
+                          hipStream_t s);
+hipError_t launch_gemv(int fmt, const uint8_t *blocks, const uint16_t *X, float *Y, int M,
+                       int64_t N, int64_t K, hipStream_t s);
+hipError_t launch_gemm_bf16(int fmt, const uint8_t *blocks, const uint16_t *X, float *Y,
+                            int64_t M, int64_t N, int64_t K, hipStream_t s);
+hipError_t launch_gemm_i8(const uint8_t *wblocks, const uint8_t *xblocks, float *Y, int64_t M,
+                          int64_t N, int64_t K, hipStream_t s);
+
+}  // namespace ql

@@ -1,0 +1,178 @@
+/*
+ * qlinear.h -- C ABI of the block-quantized linear layer for AMD MI355X
+ * (gfx950): in-situ quantization (ISQ) of bf16 weights into Q8_0, Q4K or
+ * Q6K blocks, and the fused dequantize-matmul that consumes them.
+ *
+ * The operations come from page "Quantization types" (mistral.rs
+ * reference): ISQ levels and their formats (section "Numeric shorthands",
+ * column "CUDA / CPU resolves to"), the higher-precision default for
+ * embeddings and output heads (section "Sensitive tensor precision"), and
+ * the formats themselves (sections "Q*K family": q4k 4 bits, q6k 6 bits;
+ * "Legacy GGML types": q8_0 8 bits).  The same page describes the kernel
+ * split this library follows: a matrix-vector kernel for small decode
+ * batches, a tiled matrix multiplication for larger batches, and
+ * activations quantized once and reused across output tiles (section
+ * "NVFP4").
+ *
+ * Conventions for every call:
+ *   - Tensors are row-major.  W is [N][K] (N = output features, K = input
+ *     features), X is [M][K] (M = tokens), Y is [M][N].
+ *     Y[m][n] = sum_k X[m][k] * deq(W)[n][k]   (Y = X . deq(W)^T).
+ *   - bf16 and fp16 values are passed as their 16-bit patterns.
+ *   - Device pointers must come from the same HIP device as the stream,
+ *     be non-NULL and 16-byte aligned.  Buffers are owned by the caller;
+ *     the library allocates nothing and keeps no state, so every call is
+ *     thread-safe and re-entrant.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls return
+ *     once the work is enqueued; a fault inside a kernel surfaces at the
+ *     caller's next synchronization.
+ *   - Status codes are below.  An argument error returns before anything
+ *     is launched.  Q_EHIP means the HIP runtime refused a launch.
+ *   - Inputs with Inf or NaN break a precondition: the results are then
+ *     unspecified (but the call still returns).
+ *
+ * Block formats (quantized along K, each row independently, in groups of
+ * 256 consecutive elements of a row; the byte layout is given at
+ * q_blocks_bytes below):
+ *   Q8_0: blocks of 32, fp16 scale d = max|x|/127, int8 codes
+ *         q = round-half-away-from-zero(x / d), 34 bytes per 32 elements.
+ *   Q4K:  super-blocks of 256 = 8 sub-blocks of 32, 6-bit scale and 6-bit
+ *         min per sub-block, fp16 d and dmin, 4-bit codes, w = d*sc*q -
+ *         dmin*m, 144 bytes per 256 elements.
+ *   Q6K:  super-blocks of 256 = 16 sub-blocks of 16, 8-bit sub-scales, one
+ *         fp16 d, 6-bit symmetric codes, w = d*sc*q, 210 bytes per 256.
+ */
+#ifndef QLINEAR_H
+#define QLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Quantization types.  The first three are implemented; the others are
+ * named by the pages' tables (so that the level and promotion helpers can
+ * answer for every row) and are rejected with Q_ENOTSUP by the compute
+ * calls. */
+typedef enum {
+    QFMT_Q8_0 = 0,
+    QFMT_Q4K = 1,
+    QFMT_Q6K = 2,
+    QFMT_Q2K = 3,
+    QFMT_Q3K = 4,
+    QFMT_Q5K = 5,
+    QFMT_Q8K = 6,
+    QFMT_Q4_0 = 7,
+    QFMT_Q4_1 = 8,
+    QFMT_Q5_0 = 9,
+    QFMT_Q5_1 = 10,
+    QFMT_Q8_1 = 11
+} qfmt;
+
+/* Matmul path.  AUTO: GEMV for M <= 8, bf16 MFMA GEMM above. */
+typedef enum {
+    QPATH_AUTO = 0,
+    QPATH_GEMV = 1,      /* fused dequant-GEMV, M <= 8 only */
+    QPATH_MFMA_BF16 = 2, /* weights dequantized to bf16 in LDS, MFMA bf16 */
+    QPATH_MFMA_I8 = 3    /* Q8_0 weights only: X quantized to Q8_0, int8 MFMA */
+} qpath;
+
+enum {
+    Q_OK = 0,
+    Q_EINVAL = -1,  /* NULL pointer, unknown format/path, bad workspace */
+    Q_ESHAPE = -2,  /* M, N, K out of range or K not a multiple of 256 */
+    Q_EALIGN = -3,  /* a pointer is not 16-byte aligned */
+    Q_ENOTSUP = -4, /* format or path not implemented for these arguments */
+    Q_EHIP = -5     /* the HIP runtime refused a launch or a query */
+};
+
+/* Largest accepted dimension values (element counts N*K and M*K must also
+ * stay below 2^40). */
+#define QLINEAR_MAX_M 65536
+#define QLINEAR_MAX_N (1 << 24)
+#define QLINEAR_MAX_K (1 << 20)
+
+/* Bytes of the block buffer of a [N][K] tensor in `fmt`: 34*N*K/32 (Q8_0),
+ * 144*N*K/256 (Q4K), 210*N*K/256 (Q6K).  Returns 0 for an unsupported format
+ * or an invalid shape.  The buffer is made of planes, each 16-byte aligned
+ * (G = N*K/256 groups, group g = row n, columns 256*kb .. 256*kb+255 with
+ * g = n*K/256 + kb):
+ *   Q8_0: [codes int8 N*K, row-major][d fp16 N*K/32, row-major]
+ *   Q4K:  [codes G*128][headers G*16: d, dmin, 12 bytes of 6-bit sc/m]
+ *   Q6K:  [codes G*192: 128 bytes low 4 bits + 64 bytes high 2 bits of
+ *          q+32][sub-scales G*16 int8][d G*2 fp16]                        */
+size_t q_blocks_bytes(int fmt, int64_t N, int64_t K);
+
+/* In-situ quantization (page "Quantization types": ISQ, --isq N).
+ * W_bf16: device [N][K] bf16.  out_blocks: device, q_blocks_bytes(fmt,N,K)
+ * bytes, fully overwritten.  Codes and scales are bit-exact with the
+ * library's reference definition (fp32 IEEE arithmetic, fp16 scales rounded
+ * to nearest even after clamping to 65504, round-half-away-from-zero codes).
+ * Requires K % 256 == 0 (Q8_0: K % 32 == 0), 1 <= N <= QLINEAR_MAX_N. */
+int isq_quantize(int fmt, const void *W_bf16, int64_t N, int64_t K, void *out_blocks,
+                 void *stream);
+
+/* Activation quantization to Q8_0 for the int8 path (page "Quantization
+ * types", section "NVFP4": activations quantized once and reused across
+ * output tiles; section "FP8": dynamic per-token activation quantizers).
+ * X_bf16 device [M][K]; out_blocks device, q_blocks_bytes(QFMT_Q8_0, M, K)
+ * bytes: codes [M][K] int8 then scales [M][K/32] fp16 -- the same rule and
+ * layout as isq_quantize(QFMT_Q8_0, ...). */
+int q_act_quantize(const void *X_bf16, int64_t M, int64_t K, void *out_blocks, void *stream);
+
+/* Quantized matmul Y = X . deq(W)^T on the AUTO path (no workspace).
+ * blocks: device, from isq_quantize(fmt, W, N, K).  X_bf16: device [M][K].
+ * Y_fp32: device [M][N], overwritten (not accumulated).
+ * 1 <= M <= QLINEAR_MAX_M, K % 256 == 0. */
+int qmatmul(int fmt, const void *blocks, const void *X_bf16, float *Y_fp32, int64_t M,
+            int64_t N, int64_t K, void *stream);
+
+/* Workspace bytes `qmatmul_ex` needs for (fmt, path, M, K): the Q8_0 blocks
+ * of X for QPATH_MFMA_I8 (q_blocks_bytes(QFMT_Q8_0, M, K)), 0 otherwise. */
+size_t qmatmul_workspace_bytes(int fmt, int path, int64_t M, int64_t K);
+
+/* Quantized matmul on an explicit path.  QPATH_GEMV needs M <= 8.
+ * QPATH_MFMA_I8 needs fmt == QFMT_Q8_0 and a device workspace of at least
+ * qmatmul_workspace_bytes() bytes (16-byte aligned); on return it holds
+ * the Q8_0 blocks of X (codes then scales).  Other paths ignore it. */
+int qmatmul_ex(int fmt, const void *blocks, const void *X_bf16, float *Y_fp32, int64_t M,
+               int64_t N, int64_t K, int path, void *workspace, size_t workspace_bytes,
+               void *stream);
+
+/* Test aid: exact dequantization of a block buffer to fp32 [N][K] (device). */
+int q_dequantize(int fmt, const void *blocks, int64_t N, int64_t K, float *W_fp32,
+                 void *stream);
+
+/* ISQ level -> format, page "Quantization types", section "Numeric
+ * shorthands", column "CUDA / CPU resolves to": 2 Q2K, 3 Q3K, 4 Q4K, 5 Q5K,
+ * 6 Q6K, 8 Q8_0.  Other levels: Q_EINVAL.  *out_fmt may name a format this
+ * library does not implement (q_fmt_supported tells). */
+int isq_resolve_level(int level, int *out_fmt);
+
+/* Effective type of token embeddings and output heads for a model whose
+ * default type is `model_default`, page "Quantization types", section
+ * "Sensitive tensor precision": Q2K, Q3K, Q4K, Q4_0, Q4_1 -> Q6K; Q5K, Q6K,
+ * Q8K, Q5_0, Q5_1, Q8_0, Q8_1 -> Q8_0. */
+int isq_sensitive_fmt(int model_default, int *out_fmt);
+
+/* The type one tensor gets: an explicit per-tensor type (explicit_fmt >= 0)
+ * takes precedence; otherwise the level's format, promoted by
+ * isq_sensitive_fmt when is_embedding_or_head is nonzero (same section). */
+int isq_tensor_fmt(int level, int is_embedding_or_head, int explicit_fmt, int *out_fmt);
+
+/* 1 if the compute calls implement `fmt`, else 0. */
+int q_fmt_supported(int fmt);
+
+/* Name of a format ("q8_0", "q4k", ...) or NULL. */
+const char *q_fmt_name(int fmt);
+
+/* Static description of a status code. */
+const char *q_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLINEAR_H */

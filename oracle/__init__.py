@@ -253,6 +253,29 @@ def select_rows(fmt: str, f: dict, rows, cols: int) -> dict:
     return out
 
 
+def rows_of_buffer(fmt: str, buf: np.ndarray, rows: int, cols: int, sel) -> np.ndarray:
+    """The planar buffer of the sub-tensor made of rows ``sel`` of a
+    [rows][cols] buffer (each plane sliced per row; layout in oracle.c)."""
+    sel = np.asarray(sel, np.int64)
+    b = np.asarray(buf, np.uint8)
+    E = rows * cols
+    if fmt == "q8_0":
+        planes = [(0, cols), (E, cols // 16)]
+    elif fmt == "q4k":
+        G = E // 256
+        planes = [(0, cols // 2), (128 * G, cols // 16)]
+    elif fmt == "q6k":
+        G = E // 256
+        planes = [(0, cols * 192 // 256), (192 * G, cols // 16), (208 * G, cols // 128)]
+    else:
+        raise ValueError(fmt)
+    parts = []
+    for off, per_row in planes:
+        idx = off + sel[:, None] * per_row + np.arange(per_row)[None, :]
+        parts.append(b[idx.ravel()])
+    return np.concatenate(parts)
+
+
 # ----------------------------------------------------------------------------
 # fp64 matmuls and the error metric
 # ----------------------------------------------------------------------------

@@ -1,0 +1,137 @@
+"""Host-side tests of the C ABI (no GPU needed): the library loads and
+exports every symbol the header declares, sizes and workspace sizes, the ISQ
+policy tables of page "Quantization types", and every argument error, which
+must be reported before anything is launched (the fake pointers below are
+never dereferenced)."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import ggml_block_quant_amd as ql
+from conftest import GOLDEN, ROOT
+
+HEADER = os.path.join(ROOT, "include", "qlinear.h")
+
+
+def test_library_exports_every_declared_symbol():
+    text = open(HEADER).read()
+    body = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", body)) - {"sizeof", "defined"}
+    assert names == set(ql.SIGNATURES), (names ^ set(ql.SIGNATURES))
+    L = ql.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_blocks_bytes():
+    assert ql.blocks_bytes("q8_0", 1024, 1024) == 1024 * 1024 * 34 // 32
+    assert ql.blocks_bytes("q4k", 14336, 4096) == 33_030_144
+    assert ql.blocks_bytes("q8_0", 14336, 4096) == 62_390_272
+    assert ql.blocks_bytes("q6k", 131072, 5120) == 550_502_400
+    assert ql.blocks_bytes("q8_0", 3, 32) == 3 * 34
+    assert ql.blocks_bytes("q4k", 3, 32) == 0          # K % 256
+    assert ql.blocks_bytes("q4k", 0, 256) == 0
+    assert ql.blocks_bytes("q2k", 4, 256) == 0         # named but not implemented
+    assert ql.blocks_bytes(99, 4, 256) == 0
+    # bits per weight: 8.5, 4.5, 6.5625 (nominal 8, 4, 6 on the page's tables)
+    assert ql.blocks_bytes("q8_0", 1, 256) * 8 / 256 == 8.5
+    assert ql.blocks_bytes("q4k", 1, 256) * 8 / 256 == 4.5
+    assert ql.blocks_bytes("q6k", 1, 256) * 8 / 256 == 6.5625
+
+
+def test_workspace_bytes():
+    assert ql.workspace_bytes("q8_0", "mfma_i8", 2048, 4096) == ql.blocks_bytes("q8_0", 2048, 4096)
+    assert ql.workspace_bytes("q8_0", "mfma_bf16", 2048, 4096) == 0
+    assert ql.workspace_bytes("q4k", "mfma_i8", 16, 4096) == 0
+
+
+def test_policy_tables_match_the_page():
+    g = json.load(open(os.path.join(GOLDEN, "isq_policy_tables.json")))
+    for level, fmt in g["shorthand_cuda_cpu"].items():
+        assert ql.resolve_level(int(level)) == fmt.lower(), level
+    for default, eff in g["sensitive_promotion"].items():
+        assert ql.sensitive_fmt(default.lower()) == eff.lower(), default
+    for bad in (0, 1, 7, 9, 16, -4):
+        with pytest.raises(ql.QLinearError) as e:
+            ql.resolve_level(bad)
+        assert e.value.status == ql.Q_EINVAL
+
+
+def test_tensor_fmt_precedence():
+    # level 4 -> Q4K; an embedding or output head is promoted to Q6K; an
+    # explicit per-tensor type wins over both
+    assert ql.tensor_fmt(4, False) == "q4k"
+    assert ql.tensor_fmt(4, True) == "q6k"
+    assert ql.tensor_fmt(8, True) == "q8_0"
+    assert ql.tensor_fmt(6, True) == "q8_0"
+    assert ql.tensor_fmt(4, True, explicit="q4k") == "q4k"
+    assert ql.tensor_fmt(99, True, explicit="q8_0") == "q8_0"
+    # the workload's 32-layer decoder at level 4: layers Q4K, lm_head Q6K
+    assert [ql.tensor_fmt(4, k == "lm_head") for k in ("q", "down", "lm_head")] == ["q4k", "q4k", "q6k"]
+
+
+def test_supported_formats():
+    assert [ql.fmt_supported(f) for f in ("q8_0", "q4k", "q6k")] == [True] * 3
+    assert not any(ql.fmt_supported(f) for f in ("q2k", "q3k", "q5k", "q8k", "q4_0", "q8_1"))
+    L = ql.lib()
+    assert L.q_fmt_name(1) == b"q4k" and L.q_fmt_name(42) is None
+    for s in range(-6, 1):
+        assert L.q_strerror(s)
+
+
+A = ctypes.c_void_p(0x10000)     # 16-byte aligned, never dereferenced
+A2 = ctypes.c_void_p(0x20000)
+A3 = ctypes.c_void_p(0x30000)
+MIS = ctypes.c_void_p(0x10004)   # misaligned
+NULL = ctypes.c_void_p(0)
+
+
+def test_isq_argument_errors():
+    L = ql.lib()
+    assert L.isq_quantize(0, NULL, 4, 256, A, NULL) == ql.Q_EINVAL
+    assert L.isq_quantize(0, A, 4, 256, NULL, NULL) == ql.Q_EINVAL
+    assert L.isq_quantize(17, A, 4, 256, A2, NULL) == ql.Q_EINVAL
+    assert L.isq_quantize(3, A, 4, 256, A2, NULL) == ql.Q_ENOTSUP   # Q2K
+    assert L.isq_quantize(1, MIS, 4, 256, A2, NULL) == ql.Q_EALIGN
+    assert L.isq_quantize(1, A, 4, 256, MIS, NULL) == ql.Q_EALIGN
+    assert L.isq_quantize(1, A, 4, 250, A2, NULL) == ql.Q_ESHAPE
+    assert L.isq_quantize(1, A, 4, 32, A2, NULL) == ql.Q_ESHAPE     # Q4K needs K % 256
+    assert L.isq_quantize(1, A, 0, 256, A2, NULL) == ql.Q_ESHAPE
+    assert L.isq_quantize(1, A, -1, 256, A2, NULL) == ql.Q_ESHAPE
+    assert L.isq_quantize(1, A, 1 << 25, 256, A2, NULL) == ql.Q_ESHAPE
+    assert L.isq_quantize(0, A, 4, 48, A2, NULL) == ql.Q_ESHAPE     # Q8_0 needs K % 32
+    assert L.q_act_quantize(NULL, 4, 256, A2, NULL) == ql.Q_EINVAL
+    assert L.q_act_quantize(A, 4, 100, A2, NULL) == ql.Q_ESHAPE
+    assert L.q_dequantize(1, A, 4, 100, A2, NULL) == ql.Q_ESHAPE
+    assert L.q_dequantize(1, MIS, 4, 256, A2, NULL) == ql.Q_EALIGN
+
+
+def test_qmatmul_argument_errors():
+    L = ql.lib()
+    ok = dict(M=4, N=64, K=256)
+
+    def call(fmt=1, b=A, x=A2, y=A3, M=4, N=64, K=256, path=0, ws=NULL, wsb=0):
+        return L.qmatmul_ex(fmt, b, x, y, M, N, K, path, ws, wsb, NULL)
+
+    assert call(b=NULL) == ql.Q_EINVAL
+    assert call(x=NULL) == ql.Q_EINVAL
+    assert call(y=NULL) == ql.Q_EINVAL
+    assert call(fmt=12) == ql.Q_EINVAL
+    assert call(fmt=5) == ql.Q_ENOTSUP
+    assert call(y=MIS) == ql.Q_EALIGN
+    assert call(K=128) == ql.Q_ESHAPE
+    assert call(K=384) == ql.Q_ESHAPE
+    assert call(M=0) == ql.Q_ESHAPE
+    assert call(M=70000) == ql.Q_ESHAPE
+    assert call(N=0) == ql.Q_ESHAPE
+    assert call(path=9) == ql.Q_EINVAL
+    assert call(path=1, M=9) == ql.Q_ESHAPE            # GEMV is for M <= 8
+    assert call(path=3) == ql.Q_ENOTSUP                # int8 path needs Q8_0 weights
+    assert call(fmt=0, path=3) == ql.Q_EINVAL          # ... and a workspace
+    assert call(fmt=0, path=3, ws=A, wsb=10) == ql.Q_EINVAL
+    assert call(fmt=0, path=3, ws=MIS, wsb=1 << 20) == ql.Q_EALIGN
+    assert L.qmatmul(1, A, A2, NULL, 4, 64, 256, NULL) == ql.Q_EINVAL
+    assert ok

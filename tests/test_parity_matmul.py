@@ -1,0 +1,244 @@
+"""GPU parity of the quantized matmuls against the fp64 oracle:
+  * GEMV (M <= 8) and the bf16 MFMA path against the A16 oracle
+    (exact dequantized weights times bf16 activations);
+  * the int8 MFMA path against the A8 oracle (activations quantized to
+    Q8_0 as well), and its activation blocks bit-exact;
+every output within 1e-3 of the oracle, normalised by sum |w||x|."""
+import numpy as np
+import pytest
+import torch
+
+import ggml_block_quant_amd as ql
+import oracle
+import synth
+from gpu_util import TOL, assert_blocks_equal, check_outputs, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+FMTS = ("q8_0", "q4k", "q6k")
+
+
+def run(fmt, path, w, x):
+    N, K = w.shape
+    blocks = ql.isq(fmt, to_dev_bf16(w))
+    Y = ql.qmatmul(fmt, blocks, to_dev_bf16(x), N, path=path)
+    return Y.cpu().numpy()
+
+
+def a16_ref(fmt, w, x):
+    N, K = w.shape
+    return oracle.matmul_a16(oracle.dequant(fmt, oracle.quantize(fmt, w), N, K), x)
+
+
+def a8_ref(w, x):
+    N, K = w.shape
+    M = x.shape[0]
+    return oracle.matmul_a8(oracle.quantize("q8_0", w), oracle.quantize("q8_0", x), M, N, K)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("K", [256, 1024, 4096, 5120, 14336])
+def test_gemv_shapes(fmt, K):
+    for M in (1, 2, 3, 4, 5, 8):
+        for N in (1, 7, 300):
+            w = synth.weights_bf16(1000 + K + N, N, K)
+            x = synth.activations_bf16(2000 + M, M, K)
+            y = run(fmt, "gemv", w, x)
+            Yr, den = a16_ref(fmt, w, x)
+            check_outputs(y, Yr, den, f"gemv {fmt} M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_long_rows(fmt):
+    """K = 20480 (two chunks per lane over 8 waves) and K = 32768 (M = 1,
+    four chunks per lane)."""
+    for M, K in ((1, 20480), (4, 20480), (1, 32768)):
+        if fmt == "q8_0" and M > 1:
+            continue  # Q8_0 keeps one chunk of X per lane for M > 1
+        w = synth.weights_bf16(3000 + K, 64, K)
+        x = synth.activations_bf16(3001, M, K)
+        Yr, den = a16_ref(fmt, w, x)
+        check_outputs(run(fmt, "gemv", w, x), Yr, den, f"gemv {fmt} M={M} K={K}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_one_hot_is_exact(fmt):
+    """X = e_k: the GEMV must return the fp32 value of the dequantized weight
+    bit for bit (products with 1 and sums of zeros are exact), for every
+    position k of a 256-element group -- this pins the decoding of every
+    nibble, high-bit field and 6-bit scale of the layout."""
+    N, K = 40, 512
+    w = synth.weights_bf16(4000, N, K, outliers=True)
+    blocks = ql.isq(fmt, to_dev_bf16(w))
+    Wref = oracle.dequant(fmt, oracle.quantize(fmt, w), N, K).astype(np.float32)
+    for k0 in range(0, 512, 8):
+        x = np.zeros((8, K), np.uint16)
+        for m in range(8):
+            x[m, k0 + m] = 0x3F80  # 1.0
+        Y = ql.qmatmul(fmt, blocks, to_dev_bf16(x), N, path="gemv").cpu().numpy()
+        assert np.array_equal(Y, Wref[:, k0:k0 + 8].T), f"{fmt} k0={k0}"
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_mfma_bf16_one_hot(fmt):
+    """Same pin for the bf16 MFMA path: one-hot rows give bf16(w) exactly."""
+    N, K = 130, 512
+    w = synth.weights_bf16(4100, N, K, outliers=True)
+    blocks = ql.isq(fmt, to_dev_bf16(w))
+    Wref = oracle.dequant(fmt, oracle.quantize(fmt, w), N, K).astype(np.float32)
+    Wbf = synth.bf16_bits_to_f32(synth.bf16_bits_from_f32(Wref))
+    x = np.zeros((K, K), np.uint16)
+    x[np.arange(K), np.arange(K)] = 0x3F80
+    Y = ql.qmatmul(fmt, blocks, to_dev_bf16(x), N, path="mfma_bf16").cpu().numpy()
+    assert np.array_equal(Y, Wbf.T)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_mfma_bf16_shapes(fmt):
+    for M in (9, 16, 17, 64, 100, 128, 200):
+        for N, K in ((7, 256), (64, 1024), (300, 4096), (129, 512)):
+            w = synth.weights_bf16(5000 + N, N, K)
+            x = synth.activations_bf16(5001 + M, M, K)
+            Yr, den = a16_ref(fmt, w, x)
+            check_outputs(run(fmt, "mfma_bf16", w, x), Yr, den, f"mfma_bf16 {fmt} M={M} N={N} K={K}")
+
+
+def test_mfma_i8_shapes_and_activation_blocks():
+    for M in (1, 9, 16, 64, 130, 256):
+        for N, K in ((7, 256), (64, 1024), (300, 4096), (129, 512)):
+            w = synth.weights_bf16(6000 + N, N, K)
+            x = synth.activations_bf16(6001 + M, M, K)
+            ws = torch.empty(ql.workspace_bytes("q8_0", "mfma_i8", M, K), dtype=torch.uint8, device="cuda")
+            blocks = ql.isq("q8_0", to_dev_bf16(w))
+            Y = ql.qmatmul("q8_0", blocks, to_dev_bf16(x), N, path="mfma_i8", workspace=ws).cpu().numpy()
+            # the activation blocks left in the workspace are X's Q8_0 blocks, bit for bit
+            assert_blocks_equal("q8_0", ws.cpu().numpy(), x, "activation quantization")
+            Yr, den = a8_ref(w, x)
+            check_outputs(Y, Yr, den, f"mfma_i8 M={M} N={N} K={K}")
+
+
+def test_act_quantize_entry_point():
+    x = synth.activations_bf16(6100, 37, 1024)
+    assert_blocks_equal("q8_0", ql.act_quantize(to_dev_bf16(x)).cpu().numpy(), x, "q_act_quantize")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_auto_path_dispatch(fmt):
+    """AUTO = GEMV for M <= 8 (bit for bit: the GEMV is deterministic) and
+    the bf16 MFMA GEMM above (equal up to the order of the fp32 split-K
+    atomics, so compared to 1e-6 of sum |w||x|)."""
+    N, K = 200, 1024
+    w = synth.weights_bf16(7000, N, K)
+    blocks = ql.isq(fmt, to_dev_bf16(w))
+    for M, path in ((1, "gemv"), (8, "gemv"), (9, "mfma_bf16"), (100, "mfma_bf16")):
+        x = synth.activations_bf16(7001, M, K)
+        X = to_dev_bf16(x)
+        a = ql.qmatmul(fmt, blocks, X, N, path="auto")
+        b = ql.qmatmul(fmt, blocks, X, N, path=path)
+        if path == "gemv":
+            assert torch.equal(a, b), (fmt, M)
+        else:
+            _, den = a16_ref(fmt, w, x)
+            e = oracle.normalized_error(a.cpu().numpy(), b.cpu().numpy(), den)
+            assert e.max() <= 1e-6, (fmt, M, e.max())
+
+
+@pytest.mark.parametrize("path", ["gemv", "mfma_bf16", "mfma_i8"])
+def test_zero_inputs_give_zero(path):
+    fmt = "q8_0" if path == "mfma_i8" else "q4k"
+    M = 4 if path == "gemv" else 32
+    N, K = 70, 512
+    w = synth.weights_bf16(7100, N, K)
+    w[5] = 0  # an all-zero weight row
+    x = synth.activations_bf16(7101, M, K)
+    x[1] = 0  # an all-zero activation row
+    y = run(fmt, path, w, x)
+    assert (y[1] == 0).all() and (y[:, 5] == 0).all()
+
+
+def test_gemv_is_deterministic():
+    w = synth.weights_bf16(7200, 512, 4096)
+    x = synth.activations_bf16(7201, 3, 4096)
+    blocks = ql.isq("q4k", to_dev_bf16(w))
+    X = to_dev_bf16(x)
+    a = ql.qmatmul("q4k", blocks, X, 512, path="gemv")
+    b = ql.qmatmul("q4k", blocks, X, 512, path="gemv")
+    assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads
+# ---------------------------------------------------------------------------
+
+def test_workload_gemv_1024_q8_0():
+    w = synth.weights_bf16(synth.seed_for(1, 0), 1024, 1024)
+    x = synth.activations_bf16(synth.seed_for(1, 1), 1, 1024)
+    Yr, den = a16_ref("q8_0", w, x)
+    check_outputs(run("q8_0", "auto", w, x), Yr, den, "1024x1024 q8_0")
+
+
+def test_workload_gemv_ffn_up_q4k_and_q8_0():
+    w = synth.weights_bf16(synth.seed_for(2, 0), 14336, 4096)
+    x = synth.activations_bf16(synth.seed_for(2, 1), 1, 4096)
+    for fmt in ("q4k", "q8_0"):
+        Yr, den = a16_ref(fmt, w, x)
+        check_outputs(run(fmt, "auto", w, x), Yr, den, f"14336x4096 {fmt} M=1")
+
+
+def test_workload_batched_decode_down_proj():
+    """M in {4, 16, 64} x K = 14336 x N = 4096, Q4K weights with 1 % outliers
+    at 10 sigma; M = 4 runs the GEMV, 16 and 64 the bf16 MFMA path."""
+    w = synth.weights_bf16(synth.seed_for(3, 0), 4096, 14336, outliers=True)
+    x = synth.activations_bf16(synth.seed_for(3, 1), 64, 14336)
+    W = oracle.dequant("q4k", oracle.quantize("q4k", w), 4096, 14336)
+    blocks = ql.isq("q4k", to_dev_bf16(w))
+    for M in (4, 16, 64):
+        Yr, den = oracle.matmul_a16(W, x[:M])
+        y = ql.qmatmul("q4k", blocks, to_dev_bf16(x[:M]), 4096).cpu().numpy()
+        check_outputs(y, Yr, den, f"down-proj M={M}")
+
+
+def _sampled(N, M, count, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return rng.integers(0, M, count), rng.integers(0, N, count)
+
+
+def test_workload_prefill_2048_both_paths():
+    """M = 2048 x K = 4096 x N = 14336, Q8_0 weights; the bf16 MFMA path and
+    the int8 path, checked on 4096 sampled outputs (rows of W quantized by
+    the oracle one by one)."""
+    M, N, K = 2048, 14336, 4096
+    w = synth.weights_bf16(synth.seed_for(4, 0), N, K)
+    x = synth.activations_bf16(synth.seed_for(4, 1), M, K)
+    blocks = ql.isq("q8_0", to_dev_bf16(w))
+    X = to_dev_bf16(x)
+    mi, ni = _sampled(N, M, 4096, 11)
+    rows, inv = np.unique(ni, return_inverse=True)
+    fw = oracle.quantize("q8_0", w[rows])
+    Wr = oracle.dequant("q8_0", fw, len(rows), K)
+    Yr, den = oracle.matmul_a16_pairs(Wr, x, mi, inv)
+    y = ql.qmatmul("q8_0", blocks, X, N, path="mfma_bf16").cpu().numpy()
+    check_outputs(y[mi, ni], Yr, den, "prefill bf16")
+    ws = torch.empty(ql.workspace_bytes("q8_0", "mfma_i8", M, K), dtype=torch.uint8, device="cuda")
+    y8 = ql.qmatmul("q8_0", blocks, X, N, path="mfma_i8", workspace=ws).cpu().numpy()
+    fx = oracle.quantize("q8_0", x)
+    assert_blocks_equal("q8_0", ws.cpu().numpy(), x, "prefill activations")
+    Y8, den8 = oracle.matmul_a8(fw, fx, M, len(rows), K, mi=mi, ni=inv)
+    check_outputs(y8[mi, ni], Y8, den8, "prefill int8")
+
+
+def test_workload_lm_head_q6k_m1_m8():
+    """131072 x 5120 output head in Q6K, M = 1 and M = 8, on 512 sampled rows."""
+    N, K = 131072, 5120
+    W = synth.device_normal_bf16(synth.LM_HEAD_W_SEED, (N, K), synth.W_SIGMA)
+    blocks = ql.isq("q6k", W)
+    x = synth.activations_bf16(synth.LM_HEAD_X_SEED, 8, K)
+    rng = np.random.Generator(np.random.PCG64(12))
+    rows = np.sort(rng.choice(N, 512, replace=False))
+    from gpu_util import from_dev_bf16
+    w_rows = from_dev_bf16(W[torch.from_numpy(rows).cuda()])
+    Wr = oracle.dequant("q6k", oracle.quantize("q6k", w_rows), len(rows), K)
+    for M in (1, 8):
+        y = ql.qmatmul("q6k", blocks, to_dev_bf16(x[:M]), N).cpu().numpy()
+        Yr, den = oracle.matmul_a16(Wr, x[:M])
+        check_outputs(y[:, rows], Yr, den, f"lm_head M={M}")
