@@ -14,9 +14,9 @@
 // BF16 inside the GEMM; dynamic per-token activation quantizers feed the
 // quantized GEMM).
 //
-// Both kernels use 256 threads (4 wavefronts) per 128 (n) x BM (m) output
-// tile, K-steps of 64, and optionally split K over gridDim.z with fp32
-// atomics into a zeroed Y when the (n, m) tiles alone cannot fill 256 CUs.
+// Both kernels use 256 threads (4 wavefronts) per output tile and optionally
+// split K over gridDim.z with fp32 atomics into a zeroed Y when the (n, m)
+// tiles alone cannot fill the 256 CUs.
 #include "qlinear_internal.h"
 
 namespace ql {
@@ -41,51 +41,96 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
-// Decode the 32-element chunk c of row n into 16 bf16 pairs (elements
-// 2e, 2e+1 in dword e).
+// ---------------------------------------------------------------------------
+// Dequant-to-bf16 path.  Output tile BN (n) x BM (m) per workgroup of 4
+// wavefronts; wave w owns rows n0 + w*16*NT .. +16*NT of W and all BM rows
+// of X.  K advances in slabs of 128 = 4 blocks of 32.
+//
+// W never goes through LDS: in a slab, lane l of a wave decodes the whole
+// 32-element block (4*s + l/16) of row l%16 of its n-tile -- one 16/32-byte
+// load, one scale decode -- straight into the four bf16 B-operand
+// fragments of the slab's four MFMAs.  MFMA t then pairs, for lane group
+// g = l/16, elements 8t..8t+7 of block 4s+g with the same elements of X:
+// the k order inside the slab is permuted, identically on both operands,
+// which leaves every dot product unchanged.  Only X is staged in LDS
+// (double-buffered, one barrier per slab), and the next slab's W bytes and
+// X are loaded while the current slab is computed.
+//
+// v_mfma_f32_16x16x32_bf16: A = X (16 m x 32 k), B = W^T (32 k x 16 n);
+// lane l holds D[m = 4*(l/16) + r][n = l%16], r = 0..3.
+// ---------------------------------------------------------------------------
+constexpr int SLAB = 128;            // k per slab
+constexpr int XPITCH = SLAB * 2 + 16; // bytes per LDS row of X (272: conflict-free 16-byte reads)
+
+template <int FMT> struct WBlk;  // raw bytes of one 32-element block + its scales
+template <> struct WBlk<FMT_Q8_0> { uint4 c0, c1; uint32_t d; };
+template <> struct WBlk<FMT_Q4K> { uint4 c; uint4 h; };
+template <> struct WBlk<FMT_Q6K> { uint4 lo; uint2 hi; uint32_t sc2, d; };
+
 template <int FMT>
-__device__ __forceinline__ void dequant_chunk(const uint8_t *__restrict__ B, int64_t sc_off,
-                                              int64_t d_off, int K, int64_t n, int c,
-                                              uint32_t out[16])
+__device__ __forceinline__ void load_wblk(const uint8_t *__restrict__ B, int64_t sc_off, int64_t d_off, int K,
+                                          int64_t n, int c, WBlk<FMT> &w)
 {
     if constexpr (FMT == FMT_Q8_0) {
         const int64_t blk = n * (K / 32) + c;
         const uint4 *p = reinterpret_cast<const uint4 *>(B + 32 * blk);
-        const uint4 c0 = p[0], c1 = p[1];
-        const float d = h2f(*reinterpret_cast<const uint16_t *>(B + sc_off + 2 * blk));
-        const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-#pragma unroll
-        for (int i = 0; i < 8; i++) {
-            out[2 * i] = pack_bf16(d * (float)(int8_t)(w[i]), d * (float)(int8_t)(w[i] >> 8));
-            out[2 * i + 1] = pack_bf16(d * (float)(int8_t)(w[i] >> 16), d * (float)(int8_t)(w[i] >> 24));
-        }
+        w.c0 = p[0];
+        w.c1 = p[1];
+        w.d = *reinterpret_cast<const uint16_t *>(B + sc_off + 2 * blk);
     } else if constexpr (FMT == FMT_Q4K) {
         const int64_t sub = n * (K / 32) + c;
-        const uint4 cw = *reinterpret_cast<const uint4 *>(B + 16 * sub);
-        const uint4 h = *reinterpret_cast<const uint4 *>(B + sc_off + 16 * (sub >> 3));
-        const int j = c & 7;
-        const uint32_t sc = __builtin_amdgcn_ubfe(h.y, 4 * j, 4) | (__builtin_amdgcn_ubfe(h.w, 2 * j, 2) << 4);
-        const uint32_t mq = __builtin_amdgcn_ubfe(h.z, 4 * j, 4) | (__builtin_amdgcn_ubfe(h.w, 16 + 2 * j, 2) << 4);
-        const float S = h2f(h.x) * (float)sc;
-        const float Mn = h2f(h.x >> 16) * (float)mq;
-        const uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
-#pragma unroll
-        for (int q = 0; q < 4; q++)
-#pragma unroll
-            for (int p = 0; p < 4; p++)
-                out[4 * q + p] = pack_bf16(fmaf(S, (float)((w[q] >> (4 * p)) & 15u), -Mn),
-                                           fmaf(S, (float)((w[q] >> (16 + 4 * p)) & 15u), -Mn));
+        w.c = *reinterpret_cast<const uint4 *>(B + 16 * sub);
+        w.h = *reinterpret_cast<const uint4 *>(B + sc_off + 16 * (sub >> 3));
     } else {
         const int64_t grp = n * (K / 256) + (c >> 3);
         const int cc = c & 7;
         const uint8_t *Cg = B + 192 * grp;
-        const uint4 lw = *reinterpret_cast<const uint4 *>(Cg + 16 * cc);
-        const uint2 hw = *reinterpret_cast<const uint2 *>(Cg + 128 + 8 * cc);
-        const uint32_t sc2 = *reinterpret_cast<const uint16_t *>(B + sc_off + 16 * grp + 2 * cc);
-        const float d = h2f(*reinterpret_cast<const uint16_t *>(B + d_off + 2 * grp));
-        const float Sab[2] = {d * (float)(int8_t)(sc2 & 0xffu), d * (float)(int8_t)(sc2 >> 8)};
-        const uint32_t l4[4] = {lw.x, lw.y, lw.z, lw.w};
-        const uint32_t h2[2] = {hw.x, hw.y};
+        w.lo = *reinterpret_cast<const uint4 *>(Cg + 16 * cc);
+        w.hi = *reinterpret_cast<const uint2 *>(Cg + 128 + 8 * cc);
+        w.sc2 = *reinterpret_cast<const uint16_t *>(B + sc_off + 16 * grp + 2 * cc);
+        w.d = *reinterpret_cast<const uint16_t *>(B + d_off + 2 * grp);
+    }
+}
+
+// 32 dequantized weights -> 16 dwords of bf16 pairs (element 2e, 2e+1 in dword e)
+template <int FMT>
+__device__ __forceinline__ void decode_wblk(const WBlk<FMT> &w, int c, uint32_t out[16])
+{
+    if constexpr (FMT == FMT_Q8_0) {
+        const float d = h2f(w.d);
+        const uint32_t v[8] = {w.c0.x, w.c0.y, w.c0.z, w.c0.w, w.c1.x, w.c1.y, w.c1.z, w.c1.w};
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            out[2 * i] = pack_bf16(d * (float)(int8_t)(v[i]), d * (float)(int8_t)(v[i] >> 8));
+            out[2 * i + 1] = pack_bf16(d * (float)(int8_t)(v[i] >> 16), d * (float)(int8_t)(v[i] >> 24));
+        }
+    } else if constexpr (FMT == FMT_Q4K) {
+        const int j = c & 7;
+        const uint32_t sc = __builtin_amdgcn_ubfe(w.h.y, 4 * j, 4) | (__builtin_amdgcn_ubfe(w.h.w, 2 * j, 2) << 4);
+        const uint32_t mq = __builtin_amdgcn_ubfe(w.h.z, 4 * j, 4) | (__builtin_amdgcn_ubfe(w.h.w, 16 + 2 * j, 2) << 4);
+        const float S = h2f(w.h.x) * (float)sc;
+        const float Mn = h2f(w.h.x >> 16) * (float)mq;
+        const uint32_t v[4] = {w.c.x, w.c.y, w.c.z, w.c.w};
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            // nibble p holds element 2p (p < 4) or 2(p-4)+1, so the bytes of
+            // lo = v & 0x0F0F0F0F are elements 0,4,1,5 and those of
+            // hi = (v >> 4) & 0x0F0F0F0F are elements 2,6,3,7
+            const uint32_t lo = v[q] & 0x0F0F0F0Fu, hi = (v[q] >> 4) & 0x0F0F0F0Fu;
+            const float e0 = (float)(lo & 0xffu), e4 = (float)((lo >> 8) & 0xffu);
+            const float e1 = (float)((lo >> 16) & 0xffu), e5 = (float)(lo >> 24);
+            const float e2 = (float)(hi & 0xffu), e6 = (float)((hi >> 8) & 0xffu);
+            const float e3 = (float)((hi >> 16) & 0xffu), e7 = (float)(hi >> 24);
+            out[4 * q + 0] = pack_bf16(fmaf(S, e0, -Mn), fmaf(S, e1, -Mn));
+            out[4 * q + 1] = pack_bf16(fmaf(S, e2, -Mn), fmaf(S, e3, -Mn));
+            out[4 * q + 2] = pack_bf16(fmaf(S, e4, -Mn), fmaf(S, e5, -Mn));
+            out[4 * q + 3] = pack_bf16(fmaf(S, e6, -Mn), fmaf(S, e7, -Mn));
+        }
+    } else {
+        const float d = h2f(w.d);
+        const float Sab[2] = {d * (float)(int8_t)(w.sc2 & 0xffu), d * (float)(int8_t)(w.sc2 >> 8)};
+        const uint32_t l4[4] = {w.lo.x, w.lo.y, w.lo.z, w.lo.w};
+        const uint32_t h2[2] = {w.hi.x, w.hi.y};
 #pragma unroll
         for (int q = 0; q < 4; q++) {
             const int o = q & 1;
@@ -101,115 +146,139 @@ __device__ __forceinline__ void dequant_chunk(const uint8_t *__restrict__ B, int
     }
 }
 
-constexpr int BN = 128;
-constexpr int BK = 64;
-constexpr int PITCH = BK + 8;  // bf16 elements per LDS row (144 bytes: 16-byte aligned rows)
-
-template <int FMT, int BM>
+template <int FMT, int TM, int NT>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint8_t *__restrict__ B, int64_t sc_off,
                                                         int64_t d_off, const uint16_t *__restrict__ X,
                                                         float *__restrict__ Y, int M, int N, int K,
-                                                        int kt_per_split)
+                                                        int slabs_per_split)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t sW[BN * PITCH];
-    __shared__ __attribute__((aligned(16))) uint16_t sX[BM * PITCH];
-
-    constexpr int WN = BM >= 128 ? 2 : 4;  // waves along n
-    constexpr int WM = 4 / WN;             // waves along m
-    constexpr int TN = BN / WN / 16;       // 16-row MFMA tiles per wave along n
-    constexpr int TM = BM / WM / 16;       // along m
-    static_assert(TM >= 1 && TN >= 1, "tile shape");
+    constexpr int BM = 16 * TM;
+    constexpr int XU4 = BM * SLAB * 2 / 16 / 256;  // uint4 of X per thread per slab
+    static_assert(XU4 >= 1 || BM * SLAB * 2 / 16 < 256, "X staging");
+    constexpr int XPER = BM * SLAB * 2 / 16;        // uint4 of X per slab
+    __shared__ __attribute__((aligned(16))) uint8_t sX[2][BM * XPITCH];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wn = wave % WN, wm = wave / WN;
-    const int64_t n0 = (int64_t)blockIdx.x * BN;
+    const int g = lane >> 4, r16 = lane & 15;
+    const int64_t n_wave = (int64_t)blockIdx.x * (64 * NT) + wave * 16 * NT;
     const int m0 = blockIdx.y * BM;
-    const int nkt = K / BK;
-    const int kt0 = blockIdx.z * kt_per_split;
-    const int kt1 = min(nkt, kt0 + kt_per_split);
+    const int nslab = K / SLAB;
+    const int s0 = blockIdx.z * slabs_per_split;
+    const int s1 = min(nslab, s0 + slabs_per_split);
+    if (s0 >= s1)
+        return;
 
-    f32x4_t acc[TN][TM];
+    // rows of W this lane decodes (clamped: rows past N are decoded but not stored)
+    int64_t wrow[NT];
 #pragma unroll
-    for (int i = 0; i < TN; i++)
+    for (int i = 0; i < NT; i++) {
+        const int64_t n = n_wave + 16 * i + r16;
+        wrow[i] = n < N ? n : N - 1;
+    }
+
+    auto load_x = [&](int s, uint4 (&xr)[XU4 > 0 ? XU4 : 1]) {
+#pragma unroll
+        for (int t = 0; t < (XU4 > 0 ? XU4 : 1); t++) {
+            const int i = tid + 256 * t;
+            const int row = i / (SLAB / 8), q = i % (SLAB / 8);
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (i < XPER && m0 + row < M)
+                v = *reinterpret_cast<const uint4 *>(X + (int64_t)(m0 + row) * K + s * SLAB + 8 * q);
+            xr[t] = v;
+        }
+    };
+    auto store_x = [&](int buf, const uint4 (&xr)[XU4 > 0 ? XU4 : 1]) {
+#pragma unroll
+        for (int t = 0; t < (XU4 > 0 ? XU4 : 1); t++) {
+            const int i = tid + 256 * t;
+            const int row = i / (SLAB / 8), q = i % (SLAB / 8);
+            if (i < XPER)
+                *reinterpret_cast<uint4 *>(&sX[buf][row * XPITCH + 16 * q]) = xr[t];
+        }
+    };
+
+    f32x4_t acc[NT][TM];
+#pragma unroll
+    for (int i = 0; i < NT; i++)
 #pragma unroll
         for (int j = 0; j < TM; j++)
             acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    for (int kt = kt0; kt < kt1; kt++) {
-        const int k0 = kt * BK;
-        {  // W tile: thread -> (row tid/2, 32-element half tid%2)
-            const int r = tid >> 1, h = tid & 1;
-            uint32_t v[16];
-            if (n0 + r < N) {
-                dequant_chunk<FMT>(B, sc_off, d_off, K, n0 + r, (k0 >> 5) + h, v);
-            } else {
+    uint4 xr[XU4 > 0 ? XU4 : 1];
+    WBlk<FMT> wb[NT];
+    load_x(s0, xr);
+    store_x(0, xr);
 #pragma unroll
-                for (int e = 0; e < 16; e++)
-                    v[e] = 0u;
-            }
-            uint4 *dst = reinterpret_cast<uint4 *>(sW + r * PITCH + 32 * h);
+    for (int i = 0; i < NT; i++)
+        load_wblk<FMT>(B, sc_off, d_off, K, wrow[i], 4 * s0 + g, wb[i]);
+    __syncthreads();
+
+    for (int s = s0; s < s1; s++) {
+        const int buf = (s - s0) & 1;
+        const bool more = s + 1 < s1;
+        WBlk<FMT> wn[NT];
+        if (more) {
+            load_x(s + 1, xr);
 #pragma unroll
-            for (int q = 0; q < 4; q++)
-                dst[q] = make_uint4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+            for (int i = 0; i < NT; i++)
+                load_wblk<FMT>(B, sc_off, d_off, K, wrow[i], 4 * (s + 1) + g, wn[i]);
         }
-        for (int i = tid; i < BM * 8; i += 256) {  // X tile: BM rows x 8 uint4
-            const int r = i >> 3, q = i & 7;
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (m0 + r < M)
-                v = *reinterpret_cast<const uint4 *>(X + (int64_t)(m0 + r) * K + k0 + 8 * q);
-            *reinterpret_cast<uint4 *>(sX + r * PITCH + 8 * q) = v;
-        }
-        __syncthreads();
+        // X fragments of this slab: 4 k-steps x TM m-tiles
+        bf16x8_t xa[4][TM];
 #pragma unroll
-        for (int kk = 0; kk < BK; kk += 32) {
-            bf16x8_t a[TN], b[TM];
-#pragma unroll
-            for (int i = 0; i < TN; i++)
-                a[i] = *reinterpret_cast<const bf16x8_t *>(
-                    sW + (wn * TN * 16 + 16 * i + (lane & 15)) * PITCH + kk + 8 * (lane >> 4));
+        for (int t = 0; t < 4; t++)
 #pragma unroll
             for (int j = 0; j < TM; j++)
-                b[j] = *reinterpret_cast<const bf16x8_t *>(
-                    sX + (wm * TM * 16 + 16 * j + (lane & 15)) * PITCH + kk + 8 * (lane >> 4));
+                xa[t][j] = *reinterpret_cast<const bf16x8_t *>(&sX[buf][(16 * j + r16) * XPITCH + 64 * g + 16 * t]);
 #pragma unroll
-            for (int i = 0; i < TN; i++)
+        for (int i = 0; i < NT; i++) {
+            uint32_t wv[16];
+            decode_wblk<FMT>(wb[i], 4 * s + g, wv);
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                const bf16x8_t bw = __builtin_bit_cast(bf16x8_t, make_uint4(wv[4 * t], wv[4 * t + 1], wv[4 * t + 2], wv[4 * t + 3]));
 #pragma unroll
                 for (int j = 0; j < TM; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[t][j], bw, acc[i][j], 0, 0, 0);
+            }
+        }
+        if (more) {
+            store_x(buf ^ 1, xr);
+#pragma unroll
+            for (int i = 0; i < NT; i++)
+                wb[i] = wn[i];
         }
         __syncthreads();
     }
 
-    // acc[i][j] element r = D[n = 4*(lane/16) + r][m = lane%16] of its tile
+    // lane holds D[m = 4*g + r][n = r16] of each 16 x 16 tile
     const bool atomic = gridDim.z > 1;
-    const bool vec4 = (N & 3) == 0;  // rows of Y 16-byte aligned
 #pragma unroll
-    for (int i = 0; i < TN; i++)
+    for (int i = 0; i < NT; i++) {
+        const int64_t n = n_wave + 16 * i + r16;
+        if (n >= N)
+            continue;
 #pragma unroll
-        for (int j = 0; j < TM; j++) {
-            const int64_t n = n0 + wn * TN * 16 + 16 * i + 4 * (lane >> 4);
-            const int m = m0 + wm * TM * 16 + 16 * j + (lane & 15);
-            if (m >= M)
-                continue;
-            float *y = Y + (int64_t)m * N + n;
-            if (!atomic && vec4 && n + 3 < N) {
-                *reinterpret_cast<f32x4_t *>(y) = acc[i][j];
-            } else {
+        for (int j = 0; j < TM; j++)
 #pragma unroll
-                for (int r = 0; r < 4; r++)
-                    if (n + r < N) {
-                        if (atomic)
-                            atomicAdd(y + r, acc[i][j][r]);
-                        else
-                            y[r] = acc[i][j][r];
-                    }
+            for (int r = 0; r < 4; r++) {
+                const int m = m0 + 16 * j + 4 * g + r;
+                if (m < M) {
+                    float *y = Y + (int64_t)m * N + n;
+                    if (atomic)
+                        atomicAdd(y, acc[i][j][r]);
+                    else
+                        *y = acc[i][j][r];
+                }
             }
-        }
+    }
 }
 
 // ---------------------------------------------------------------------------
 // Q8_0 x Q8_0 int8 path
 // ---------------------------------------------------------------------------
+constexpr int BN = 128;     // n tile
+constexpr int BK = 64;      // k per step (two Q8_0 blocks)
 constexpr int IBM = 128;    // m tile
 constexpr int IPITCH = 80;  // bytes per LDS row of 64 codes (16-byte aligned, skewed banks)
 
@@ -355,21 +424,23 @@ hipError_t zero_y(float *Y, int64_t count, hipStream_t s)
     return hipGetLastError();
 }
 
-template <int FMT, int BM>
+template <int FMT, int TM, int NT>
 hipError_t go_bf16(const uint8_t *blocks, const Planes &p, const uint16_t *X, float *Y, int64_t M,
                    int64_t N, int64_t K, hipStream_t s)
 {
-    const int64_t gx = (N + BN - 1) / BN, gy = (M + BM - 1) / BM;
-    const int nkt = (int)(K / BK);
-    const int splits = splits_for(gx * gy, nkt);
-    const int per = (nkt + splits - 1) / splits;
+    const int64_t gx = (N + 64 * NT - 1) / (64 * NT), gy = (M + 16 * TM - 1) / (16 * TM);
+    const int nslab = (int)(K / SLAB);
+    int splits = 1;
+    while (gx * gy * splits < 512 && splits < 32 && nslab / (2 * splits) >= 2)
+        splits *= 2;
+    const int per = (nslab + splits - 1) / splits;
     if (splits > 1) {
         const hipError_t e = zero_y(Y, M * N, s);
         if (e != hipSuccess)
             return e;
     }
-    hipLaunchKernelGGL((gemm_bf16_kernel<FMT, BM>), dim3((unsigned)gx, (unsigned)gy, (unsigned)splits), dim3(256), 0, s,
-                       blocks, p.scales, p.d, X, Y, (int)M, (int)N, (int)K, per);
+    hipLaunchKernelGGL((gemm_bf16_kernel<FMT, TM, NT>), dim3((unsigned)gx, (unsigned)gy, (unsigned)splits), dim3(256), 0,
+                       s, blocks, p.scales, p.d, X, Y, (int)M, (int)N, (int)K, per);
     return hipGetLastError();
 }
 
@@ -378,12 +449,12 @@ hipError_t bf16_by_m(const uint8_t *blocks, const Planes &p, const uint16_t *X, 
                      int64_t N, int64_t K, hipStream_t s)
 {
     if (M <= 16)
-        return go_bf16<FMT, 16>(blocks, p, X, Y, M, N, K, s);
+        return go_bf16<FMT, 1, 4>(blocks, p, X, Y, M, N, K, s);
     if (M <= 32)
-        return go_bf16<FMT, 32>(blocks, p, X, Y, M, N, K, s);
+        return go_bf16<FMT, 2, 4>(blocks, p, X, Y, M, N, K, s);
     if (M <= 64)
-        return go_bf16<FMT, 64>(blocks, p, X, Y, M, N, K, s);
-    return go_bf16<FMT, 128>(blocks, p, X, Y, M, N, K, s);
+        return go_bf16<FMT, 4, 4>(blocks, p, X, Y, M, N, K, s);
+    return go_bf16<FMT, 8, 4>(blocks, p, X, Y, M, N, K, s);
 }
 
 }  // namespace

@@ -17,14 +17,19 @@
 // wave with a halving butterfly (each step halves the values a lane keeps),
 // then across the KS waves through LDS.
 //
+// Workgroups are persistent: each walks batches b, b+G, b+2G, ... and the
+// loads of the next batch are issued before the current one is computed.
+// Rows and chunks past the end are clamped (they re-read valid bytes and
+// their contribution is dropped or multiplied by a zero X), so the load
+// path has no branches.
+//
 // Arithmetic.  Q4K / Q6K codes u (4 or 6 bits) become bf16 pairs with one
-// and/or: bits 0x4300 | u are exactly the bf16 value 128 + u, and the
+// v_and_or_b32: bits 0x4300 | u are exactly the bf16 value 128 + u, and the
 // nibble order of the layout puts two consecutive elements in the two
 // halves of a dword.  v_dot2_f32_bf16 multiplies them by the bf16 pair of
 // X directly (products exact in fp32), and the bias is removed once per
-// sub-block:  sum x*(128+u) - 128*sum x.  Q8_0 codes are turned to fp32
-// with v_cvt_f32_ubyte after an xor (offset-binary bytes) and FMA'd.  All
-// accumulation is fp32.
+// sub-block:  sum x*(128+u) - 128*sum x.  Q8_0 codes are sign-extended
+// bytes converted to fp32 and FMA'd.  All accumulation is fp32.
 #include "qlinear_internal.h"
 
 namespace ql {
@@ -93,17 +98,34 @@ __device__ __forceinline__ void load_chunk<FMT_Q8_0>(const Geo &g, int64_t n, in
     ck.d = *reinterpret_cast<const uint16_t *>(g.B + g.scales_off + 2 * blk);
 }
 
-// X of one chunk for M rows: 16 bf16 pairs per row, plus the sums the bias
-// correction needs (s0: whole chunk or first half, s1: second half).
+// X of one chunk for M rows: 16 bf16 pairs per row, plus the terms of the
+// bias correction (Q4K: s0 = 128 * sum, s1 = sum over the chunk; Q6K:
+// s0, s1 = 160 * sum over each 16-element half).
 template <int M> struct XChunk {
     uint32_t p[M][16];
     float s0[M], s1[M];
 };
 
-template <int M>
-__device__ __forceinline__ void q4k_dot(const Chunk<FMT_Q4K> &ck, const XChunk<M> &x, int c, float acc[M])
+// Loop-invariant constants held in VGPRs: a VOP3 and-or on gfx950 takes at
+// most one SGPR/constant operand, so the masks live in registers and the
+// bias in an SGPR, which gives one v_and_or_b32 per bf16 pair.
+struct Masks {
+    uint32_t nib;  // 0x000F000F
+    uint32_t hi2;  // 0x00300030
+};
+
+__device__ __forceinline__ Masks make_masks()
 {
-    const int j = c & 7;
+    Masks k;
+    asm volatile("v_mov_b32 %0, 0x000f000f" : "=v"(k.nib));
+    asm volatile("v_mov_b32 %0, 0x00300030" : "=v"(k.hi2));
+    return k;
+}
+
+template <int M>
+__device__ __forceinline__ void q4k_dot(const Chunk<FMT_Q4K> &ck, const XChunk<M> &x, int j, float acc[M],
+                                        const Masks &k)
+{
     const uint32_t sc = __builtin_amdgcn_ubfe(ck.h.y, 4 * j, 4) | (__builtin_amdgcn_ubfe(ck.h.w, 2 * j, 2) << 4);
     const uint32_t mq = __builtin_amdgcn_ubfe(ck.h.z, 4 * j, 4) | (__builtin_amdgcn_ubfe(ck.h.w, 16 + 2 * j, 2) << 4);
     const float S = h2f(ck.h.x) * (float)sc;
@@ -114,7 +136,7 @@ __device__ __forceinline__ void q4k_dot(const Chunk<FMT_Q4K> &ck, const XChunk<M
     for (int q = 0; q < 4; q++)
 #pragma unroll
         for (int s = 0; s < 4; s++)
-            pr[4 * q + s] = ((w[q] >> (4 * s)) & 0x000F000Fu) | 0x43004300u;
+            pr[4 * q + s] = ((w[q] >> (4 * s)) & k.nib) | 0x43004300u;
 #pragma unroll
     for (int m = 0; m < M; m++) {
         float d = 0.0f;
@@ -122,13 +144,14 @@ __device__ __forceinline__ void q4k_dot(const Chunk<FMT_Q4K> &ck, const XChunk<M
         for (int e = 0; e < 16; e++)
             d = dot2(pr[e], x.p[m][e], d);
         // S*(d - 128*sum x) - Mn*sum x
-        acc[m] = fmaf(S, d - 128.0f * x.s0[m], acc[m]);
-        acc[m] = fmaf(-Mn, x.s0[m], acc[m]);
+        acc[m] = fmaf(S, d - x.s0[m], acc[m]);
+        acc[m] = fmaf(-Mn, x.s1[m], acc[m]);
     }
 }
 
 template <int M>
-__device__ __forceinline__ void q6k_dot(const Chunk<FMT_Q6K> &ck, const XChunk<M> &x, float acc[M])
+__device__ __forceinline__ void q6k_dot(const Chunk<FMT_Q6K> &ck, const XChunk<M> &x, float acc[M],
+                                        const Masks &k)
 {
     const float d = h2f(ck.d);
     const float Sa = d * (float)(int8_t)(ck.sc2 & 0xffu);
@@ -141,10 +164,10 @@ __device__ __forceinline__ void q6k_dot(const Chunk<FMT_Q6K> &ck, const XChunk<M
         const int o = q & 1;
 #pragma unroll
         for (int s = 0; s < 4; s++) {
-            const uint32_t lo = (lw[q] >> (4 * s)) & 0x000F000Fu;
+            const uint32_t lo = ((lw[q] >> (4 * s)) & k.nib) | 0x43004300u;
             const int sh = 8 * o + 2 * s;  // high bits of this pair start at bit sh (and 16+sh)
-            const uint32_t hi = (sh >= 4 ? (hw[q >> 1] >> (sh - 4)) : (hw[q >> 1] << (4 - sh))) & 0x00300030u;
-            pr[4 * q + s] = lo | hi | 0x43004300u;
+            const uint32_t h = sh >= 4 ? (hw[q >> 1] >> (sh - 4)) : (hw[q >> 1] << (4 - sh));
+            pr[4 * q + s] = (h & k.hi2) | lo;
         }
     }
 #pragma unroll
@@ -156,11 +179,13 @@ __device__ __forceinline__ void q6k_dot(const Chunk<FMT_Q6K> &ck, const XChunk<M
             db = dot2(pr[8 + e], x.p[m][8 + e], db);
         }
         // stored u = q + 32, so 128 + u = 160 + q
-        acc[m] = fmaf(Sa, da - 160.0f * x.s0[m], acc[m]);
-        acc[m] = fmaf(Sb, db - 160.0f * x.s1[m], acc[m]);
+        acc[m] = fmaf(Sa, da - x.s0[m], acc[m]);
+        acc[m] = fmaf(Sb, db - x.s1[m], acc[m]);
     }
 }
 
+// Q8_0: signed codes converted with v_cvt_f32_i32 on a sign-extended byte
+// (SDWA), X either kept in fp32 (small M) or widened from bf16 on the fly.
 template <int M>
 __device__ __forceinline__ void q8_0_dot(const Chunk<FMT_Q8_0> &ck, const XChunk<M> &x, float acc[M])
 {
@@ -172,9 +197,8 @@ __device__ __forceinline__ void q8_0_dot(const Chunk<FMT_Q8_0> &ck, const XChunk
         d[m] = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-        const uint32_t u = w[i] ^ 0x80808080u;  // offset-binary bytes: u = q + 128
-        const float f0 = (float)(u & 0xffu), f1 = (float)((u >> 8) & 0xffu);
-        const float f2 = (float)((u >> 16) & 0xffu), f3 = (float)(u >> 24);
+        const float f0 = (float)(int8_t)(w[i]), f1 = (float)(int8_t)(w[i] >> 8);
+        const float f2 = (float)(int8_t)(w[i] >> 16), f3 = (float)(int8_t)(w[i] >> 24);
 #pragma unroll
         for (int m = 0; m < M; m++) {
             d[m] = fmaf(f0, lo_bf16(x.p[m][2 * i]), d[m]);
@@ -185,48 +209,69 @@ __device__ __forceinline__ void q8_0_dot(const Chunk<FMT_Q8_0> &ck, const XChunk
     }
 #pragma unroll
     for (int m = 0; m < M; m++)
-        acc[m] = fmaf(dw, d[m] - 128.0f * x.s0[m], acc[m]);
+        acc[m] = fmaf(dw, d[m], acc[m]);
 }
 
-template <int FMT, int M>
-__device__ __forceinline__ void dot_any(const Chunk<FMT> &ck, const XChunk<M> &x, int c, float acc[M])
+// ----------------------------------------------------------------------------
+// Halving butterfly over the 64 lanes.  V values per lane (V a power of two
+// <= 64).  Lane bits are taken in the order 0, 1, ..., 5.  While more than
+// one value is left, a step keeps half of them (the lane whose bit is set
+// keeps the upper half) and adds the partner's copy, so the partner must be
+// lane ^ (1 << bit) exactly: quad_perm DPP for bits 0 and 1, shuffles above.
+// Once one value is left, plain sums only need a partner with the same low
+// (already halved) bits: row_ror:4 and row_ror:8 DPP within a 16-lane row.
+// Afterwards lanes 0..V-1 hold the totals of distinct indices idx(lane).
+// ----------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v)
 {
-    if constexpr (FMT == FMT_Q4K)
-        q4k_dot<M>(ck, x, c, acc);
-    else if constexpr (FMT == FMT_Q6K)
-        q6k_dot<M>(ck, x, acc);
-    else
-        q8_0_dot<M>(ck, x, acc);
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 
-// ----------------------------------------------------------------------------
-// Halving butterfly: V values per lane (V a power of two <= 64) are summed
-// over the 64 lanes.  Afterwards lane l holds the total of value index
-// idx(l) = sum_t bit(5-t of l) * V/2^(t+1) over the log2(V) halving steps,
-// and every lane whose low 6-log2(V) bits are zero holds a distinct index.
-// ----------------------------------------------------------------------------
+template <int STEP, bool HALVING>
+__device__ __forceinline__ float partner(float v)
+{
+    if constexpr (STEP == 0)
+        return dpp_f<0xB1>(v);  // quad_perm [1,0,3,2]: lane ^ 1
+    else if constexpr (STEP == 1)
+        return dpp_f<0x4E>(v);  // quad_perm [2,3,0,1]: lane ^ 2
+    else if constexpr (STEP == 2)
+        return HALVING ? __shfl_xor(v, 4) : dpp_f<0x124>(v);  // row_ror:4
+    else if constexpr (STEP == 3)
+        return HALVING ? __shfl_xor(v, 8) : dpp_f<0x128>(v);  // row_ror:8
+    else if constexpr (STEP == 4)
+        return __shfl_xor(v, 16);
+    else
+        return __shfl_xor(v, 32);
+}
+
+template <int V, int STEP>
+__device__ __forceinline__ void bfly_step(float (&v)[V], int lane)
+{
+    constexpr int CNT = (V >> STEP) > 1 ? (V >> STEP) : 1;  // values left before this step
+    if constexpr (CNT > 1) {
+        constexpr int HALF = CNT / 2;
+        const bool up = (lane >> STEP) & 1;
+#pragma unroll
+        for (int i = 0; i < HALF; i++) {
+            const float keep = up ? v[i + HALF] : v[i];
+            const float send = up ? v[i] : v[i + HALF];
+            v[i] = keep + partner<STEP, true>(send);
+        }
+    } else {
+        v[0] += partner<STEP, false>(v[0]);
+    }
+}
+
 template <int V>
 __device__ __forceinline__ float butterfly_sum(float (&v)[V], int lane)
 {
-    int cnt = V;
-#pragma unroll
-    for (int k = 32; k >= 1; k >>= 1) {
-        if (cnt > 1) {
-            const int half = cnt / 2;
-            const bool up = (lane & k) != 0;
-#pragma unroll
-            for (int i = 0; i < V / 2; i++) {
-                if (i < half) {
-                    const float keep = up ? v[i + half] : v[i];
-                    const float send = up ? v[i] : v[i + half];
-                    v[i] = keep + __shfl_xor(send, k);
-                }
-            }
-            cnt = half;
-        } else {
-            v[0] += __shfl_xor(v[0], k);
-        }
-    }
+    bfly_step<V, 0>(v, lane);
+    bfly_step<V, 1>(v, lane);
+    bfly_step<V, 2>(v, lane);
+    bfly_step<V, 3>(v, lane);
+    bfly_step<V, 4>(v, lane);
+    bfly_step<V, 5>(v, lane);
     return v[0];
 }
 
@@ -235,9 +280,9 @@ __device__ __forceinline__ int butterfly_index(int lane)
 {
     int idx = 0, part = V;
 #pragma unroll
-    for (int k = 32; k >= 1 && part > 1; k >>= 1) {
+    for (int b = 0; b < 6 && part > 1; b++) {
         part >>= 1;
-        if (lane & k)
+        if ((lane >> b) & 1)
             idx += part;
     }
     return idx;
@@ -254,6 +299,80 @@ constexpr int pow2_at_least(int v)
 // ----------------------------------------------------------------------------
 // The kernel
 // ----------------------------------------------------------------------------
+template <int FMT, int M, int CPT, int R> struct Batch {
+    Chunk<FMT> ck[R][CPT];
+};
+
+template <int FMT, int M, int CPT, int R>
+__device__ __forceinline__ void load_batch(const Geo &g, int64_t b, int64_t N, const int (&cl)[CPT],
+                                           Batch<FMT, M, CPT, R> &bt)
+{
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+        // rows past the end re-read the last row; their results are dropped
+        const int64_t n = b * R + r < N ? b * R + r : N - 1;
+#pragma unroll
+        for (int i = 0; i < CPT; i++)
+            load_chunk<FMT>(g, n, cl[i], bt.ck[r][i]);
+    }
+}
+
+template <int FMT, int M, int CPT, int R>
+__device__ __forceinline__ void process_batch(const Batch<FMT, M, CPT, R> &bt, const XChunk<M> (&xr)[CPT],
+                                              const int (&cj)[CPT], const Masks &k, int64_t b, int64_t N,
+                                              float *__restrict__ Y, int lane, int wv, int KS,
+                                              float (*part)[pow2_at_least(R * M)])
+{
+    constexpr int V = pow2_at_least(R * M);
+    float v[V];
+#pragma unroll
+    for (int t = 0; t < V; t++)
+        v[t] = 0.0f;
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+        float acc[M];
+#pragma unroll
+        for (int m = 0; m < M; m++)
+            acc[m] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < CPT; i++) {
+            if constexpr (FMT == FMT_Q4K)
+                q4k_dot<M>(bt.ck[r][i], xr[i], cj[i], acc, k);
+            else if constexpr (FMT == FMT_Q6K)
+                q6k_dot<M>(bt.ck[r][i], xr[i], acc, k);
+            else
+                q8_0_dot<M>(bt.ck[r][i], xr[i], acc);
+        }
+#pragma unroll
+        for (int m = 0; m < M; m++)
+            v[r * M + m] = acc[m];
+    }
+    const float tot = butterfly_sum<V>(v, lane);
+    const int idx = butterfly_index<V>(lane);
+    const bool writer = lane < V && idx < R * M;
+    const int64_t n0 = b * R;
+    if (KS == 1) {
+        if (writer) {
+            const int r = idx / M, m = idx % M;
+            if (n0 + r < N)
+                Y[(int64_t)m * N + n0 + r] = tot;
+        }
+    } else {
+        if (writer)
+            part[wv][idx] = tot;
+        __syncthreads();
+        if (threadIdx.x < R * M) {
+            float s = 0.0f;
+            for (int w = 0; w < KS; w++)
+                s += part[w][threadIdx.x];
+            const int r = threadIdx.x / M, m = threadIdx.x % M;
+            if (n0 + r < N)
+                Y[(int64_t)m * N + n0 + r] = s;
+        }
+        __syncthreads();
+    }
+}
+
 template <int FMT, int M, int CPT, int R>
 __global__ __launch_bounds__(512) void gemv_kernel(Geo g, const uint16_t *__restrict__ X,
                                                    float *__restrict__ Y, int64_t N)
@@ -265,22 +384,27 @@ __global__ __launch_bounds__(512) void gemv_kernel(Geo g, const uint16_t *__rest
     const int wv = threadIdx.x >> 6;
     const int KS = blockDim.x >> 6;
     const int S = g.K / 32;
+    const Masks k = make_masks();
 
-    int cidx[CPT];
-    bool live[CPT];
+    // chunks of this lane; lanes past the row end read the last chunk with a
+    // zero X, so they add exactly nothing and need no branch
+    int cl[CPT], cj[CPT];
     XChunk<M> xr[CPT];
 #pragma unroll
     for (int i = 0; i < CPT; i++) {
-        cidx[i] = wv * 64 + lane + i * KS * 64;
-        live[i] = cidx[i] < S;
+        const int c = wv * 64 + lane + i * KS * 64;
+        const bool live = c < S;
+        cl[i] = live ? c : S - 1;
+        cj[i] = cl[i] & 7;
 #pragma unroll
         for (int m = 0; m < M; m++) {
-            uint4 q[4] = {};
-            if (live[i]) {
-                const uint4 *xp = reinterpret_cast<const uint4 *>(X + (int64_t)m * g.K + 32 * cidx[i]);
+            uint4 q[4];
+            const uint4 *xp = reinterpret_cast<const uint4 *>(X + (int64_t)m * g.K + 32 * cl[i]);
 #pragma unroll
-                for (int t = 0; t < 4; t++)
-                    q[t] = xp[t];
+            for (int t = 0; t < 4; t++) {
+                q[t] = xp[t];
+                if (!live)
+                    q[t] = make_uint4(0u, 0u, 0u, 0u);
             }
 #pragma unroll
             for (int t = 0; t < 4; t++) {
@@ -295,104 +419,73 @@ __global__ __launch_bounds__(512) void gemv_kernel(Geo g, const uint16_t *__rest
                 s0 = dot2(xr[i].p[m][e], 0x3F803F80u, s0);
                 s1 = dot2(xr[i].p[m][8 + e], 0x3F803F80u, s1);
             }
+            // bias corrections: Q4K s0 = 128*sum, s1 = sum (whole chunk);
+            // Q6K s0/s1 = 160*sum of each half; Q8_0 needs none
             if constexpr (FMT == FMT_Q6K) {
-                xr[i].s0[m] = s0;
-                xr[i].s1[m] = s1;
+                xr[i].s0[m] = 160.0f * s0;
+                xr[i].s1[m] = 160.0f * s1;
             } else {
-                xr[i].s0[m] = s0 + s1;
-                xr[i].s1[m] = 0.0f;
+                xr[i].s0[m] = 128.0f * (s0 + s1);
+                xr[i].s1[m] = s0 + s1;
             }
         }
     }
 
+    // persistent workgroups; the next batch's loads are in flight while the
+    // current one is computed
     const int64_t nbatch = (N + R - 1) / R;
-    for (int64_t b = blockIdx.x; b < nbatch; b += gridDim.x) {
-        const int64_t n0 = b * R;
-        Chunk<FMT> ck[R][CPT];
-#pragma unroll
-        for (int r = 0; r < R; r++)
-#pragma unroll
-            for (int i = 0; i < CPT; i++)
-                if (live[i] && n0 + r < N)
-                    load_chunk<FMT>(g, n0 + r, cidx[i], ck[r][i]);
-        float v[V];
-#pragma unroll
-        for (int t = 0; t < V; t++)
-            v[t] = 0.0f;
-#pragma unroll
-        for (int r = 0; r < R; r++) {
-            float acc[M];
-#pragma unroll
-            for (int m = 0; m < M; m++)
-                acc[m] = 0.0f;
-#pragma unroll
-            for (int i = 0; i < CPT; i++)
-                if (live[i] && n0 + r < N)
-                    dot_any<FMT, M>(ck[r][i], xr[i], cidx[i], acc);
-#pragma unroll
-            for (int m = 0; m < M; m++)
-                v[r * M + m] = acc[m];
-        }
-        const float tot = butterfly_sum<V>(v, lane);
-        const int idx = butterfly_index<V>(lane);
-        constexpr int low_mask = (64 / V) - 1;  // lanes sharing one index
-        const bool writer = (lane & low_mask) == 0 && idx < R * M;
-        if (KS == 1) {
-            if (writer) {
-                const int r = idx / M, m = idx % M;
-                if (n0 + r < N)
-                    Y[(int64_t)m * N + n0 + r] = tot;
-            }
-        } else {
-            if (writer)
-                part[wv][idx] = tot;
-            __syncthreads();
-            if (threadIdx.x < R * M) {
-                float s = 0.0f;
-                for (int w = 0; w < KS; w++)
-                    s += part[w][threadIdx.x];
-                const int r = threadIdx.x / M, m = threadIdx.x % M;
-                if (n0 + r < N)
-                    Y[(int64_t)m * N + n0 + r] = s;
-            }
-            __syncthreads();
-        }
+    const int64_t G = gridDim.x;
+    Batch<FMT, M, CPT, R> A, B;
+    int64_t b = blockIdx.x;
+    if (b < nbatch)
+        load_batch<FMT, M, CPT, R>(g, b, N, cl, A);
+    for (; b < nbatch; b += 2 * G) {
+        const bool hasB = b + G < nbatch;
+        if (hasB)
+            load_batch<FMT, M, CPT, R>(g, b + G, N, cl, B);
+        process_batch<FMT, M, CPT, R>(A, xr, cj, k, b, N, Y, lane, wv, KS, part);
+        if (b + 2 * G < nbatch)
+            load_batch<FMT, M, CPT, R>(g, b + 2 * G, N, cl, A);
+        if (hasB)
+            process_batch<FMT, M, CPT, R>(B, xr, cj, k, b + G, N, Y, lane, wv, KS, part);
     }
 }
 
 template <int FMT, int M, int CPT, int R>
-hipError_t go(const Geo &g, const uint16_t *X, float *Y, int64_t N, int KS, hipStream_t s)
+hipError_t go(const Geo &g, const uint16_t *X, float *Y, int64_t N, int KS, int wgs_per_cu, hipStream_t s)
 {
     const int64_t nbatch = (N + R - 1) / R;
-    // enough workgroups to keep every CU busy while each walks many rows
-    const int64_t target = (int64_t)256 * 16 / KS;
+    const int64_t target = (int64_t)256 * wgs_per_cu;
     const int64_t grid = nbatch < target ? nbatch : target;
     hipLaunchKernelGGL((gemv_kernel<FMT, M, CPT, R>), dim3((unsigned)grid), dim3(64 * KS), 0, s, g, X, Y, N);
     return hipGetLastError();
 }
 
+// Launch shape per (format, M, K), chosen from measured sweeps on MI355X at
+// the decode shapes (14336 x 4096, 4096 x 14336, 131072 x 5120).
 template <int FMT, int M>
 hipError_t pick(const Geo &g, const uint16_t *X, float *Y, int64_t N, hipStream_t s)
 {
     const int S = g.K / 32;  // chunks per row
-    constexpr int R = M <= 2 ? 4 : (M <= 4 ? 2 : 1);
-    // Two chunks of X per lane fit in registers only for small M.
-    constexpr bool wide = FMT == FMT_Q8_0 ? M <= 1 : M <= 4;
-    // One wave per row while a lane can hold the row's share of X, else
-    // split K over up to 8 waves, then give lanes more chunks.
+    constexpr int R = M <= 4 ? 2 : 1;
+    // Two chunks of X per lane fit in registers only for small M; Q8_0
+    // streams twice the bytes per chunk and prefers one chunk per lane.
+    constexpr bool wide = FMT == FMT_Q8_0 ? false : M <= 4;
     if (S <= 64)
-        return go<FMT, M, 1, R>(g, X, Y, N, 1, s);
+        return go<FMT, M, 1, R>(g, X, Y, N, 1, 16, s);
     if constexpr (wide)
         if (S <= 128)
-            return go<FMT, M, 2, R>(g, X, Y, N, 1, s);
-    if (S <= 512)
-        return go<FMT, M, 1, R>(g, X, Y, N, (S + 63) / 64, s);
+            return go<FMT, M, 2, R>(g, X, Y, N, 1, 8, s);
+    if (S <= 512) {
+        const int KS = (S + 63) / 64;
+        return go<FMT, M, 1, R>(g, X, Y, N, KS, 16 / KS > 1 ? 16 / KS : 1, s);
+    }
     if constexpr (wide)
         if (S <= 1024)
-            return go<FMT, M, 2, 1>(g, X, Y, N, 8, s);
+            return go<FMT, M, 2, 1>(g, X, Y, N, 8, 1, s);
     if constexpr (M == 1)
         if (S <= 2048)
-            return go<FMT, M, 4, 1>(g, X, Y, N, 8, s);
+            return go<FMT, M, 4, 1>(g, X, Y, N, 8, 1, s);
     return hipErrorNotSupported;  // the caller falls back to the MFMA path
 }
 
