@@ -34,6 +34,20 @@ __device__ __forceinline__ float h2f(uint32_t bits16)
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits16 & 0xffffu));
 }
 
+// Workgroup barrier for LDS hand-offs only.  __syncthreads() also fences
+// global memory, which makes the compiler drain every outstanding global
+// load (s_waitcnt vmcnt(0)) -- including prefetches meant to stay in flight
+// across the barrier.  Here only this wave's LDS accesses must be complete
+// (lgkmcnt(0)); the signal fences keep the compiler from moving memory
+// accesses across the barrier.
+__device__ __forceinline__ void lds_barrier()
+{
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63, expcnt 7, lgkmcnt 0
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // two fp32 -> one dword of two bf16 (round to nearest even, v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b)
 {
@@ -204,51 +218,57 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint8_t *__restric
         for (int j = 0; j < TM; j++)
             acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    uint4 xr[XU4 > 0 ? XU4 : 1];
-    WBlk<FMT> wb[NT];
-    load_x(s0, xr);
-    store_x(0, xr);
+    // Prefetch distance 2: while slab s is computed, X of slab s+1 waits in
+    // registers for its LDS stage and the bytes of slab s+2 are in flight.
+    uint4 x1[XU4 > 0 ? XU4 : 1], x2[XU4 > 0 ? XU4 : 1];
+    WBlk<FMT> wa[NT], wb[NT], wc[NT];
+    load_x(s0, x1);
 #pragma unroll
     for (int i = 0; i < NT; i++)
-        load_wblk<FMT>(B, sc_off, d_off, K, wrow[i], 4 * s0 + g, wb[i]);
+        load_wblk<FMT>(B, sc_off, d_off, K, wrow[i], 4 * s0 + g, wa[i]);
+    store_x(0, x1);
+    if (s0 + 1 < s1) {
+        load_x(s0 + 1, x1);
+#pragma unroll
+        for (int i = 0; i < NT; i++)
+            load_wblk<FMT>(B, sc_off, d_off, K, wrow[i], 4 * (s0 + 1) + g, wb[i]);
+    }
     __syncthreads();
 
     for (int s = s0; s < s1; s++) {
         const int buf = (s - s0) & 1;
-        const bool more = s + 1 < s1;
-        WBlk<FMT> wn[NT];
-        if (more) {
-            load_x(s + 1, xr);
+        if (s + 2 < s1) {
+            load_x(s + 2, x2);
 #pragma unroll
             for (int i = 0; i < NT; i++)
-                load_wblk<FMT>(B, sc_off, d_off, K, wrow[i], 4 * (s + 1) + g, wn[i]);
+                load_wblk<FMT>(B, sc_off, d_off, K, wrow[i], 4 * (s + 2) + g, wc[i]);
         }
-        // X fragments of this slab: 4 k-steps x TM m-tiles
-        bf16x8_t xa[4][TM];
-#pragma unroll
-        for (int t = 0; t < 4; t++)
-#pragma unroll
-            for (int j = 0; j < TM; j++)
-                xa[t][j] = *reinterpret_cast<const bf16x8_t *>(&sX[buf][(16 * j + r16) * XPITCH + 64 * g + 16 * t]);
 #pragma unroll
         for (int i = 0; i < NT; i++) {
             uint32_t wv[16];
-            decode_wblk<FMT>(wb[i], 4 * s + g, wv);
+            decode_wblk<FMT>(wa[i], 4 * s + g, wv);
 #pragma unroll
             for (int t = 0; t < 4; t++) {
                 const bf16x8_t bw = __builtin_bit_cast(bf16x8_t, make_uint4(wv[4 * t], wv[4 * t + 1], wv[4 * t + 2], wv[4 * t + 3]));
 #pragma unroll
-                for (int j = 0; j < TM; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[t][j], bw, acc[i][j], 0, 0, 0);
+                for (int j = 0; j < TM; j++) {
+                    const bf16x8_t xa = *reinterpret_cast<const bf16x8_t *>(
+                        &sX[buf][(16 * j + r16) * XPITCH + 64 * g + 16 * t]);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bw, acc[i][j], 0, 0, 0);
+                }
             }
         }
-        if (more) {
-            store_x(buf ^ 1, xr);
-#pragma unroll
-            for (int i = 0; i < NT; i++)
-                wb[i] = wn[i];
-        }
+        if (s + 1 < s1)
+            store_x(buf ^ 1, x1);
         __syncthreads();
+#pragma unroll
+        for (int i = 0; i < NT; i++) {
+            wa[i] = wb[i];
+            wb[i] = wc[i];
+        }
+#pragma unroll
+        for (int t = 0; t < (XU4 > 0 ? XU4 : 1); t++)
+            x1[t] = x2[t];
     }
 
     // lane holds D[m = 4*g + r][n = r16] of each 16 x 16 tile
@@ -271,6 +291,304 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint8_t *__restric
                         *y = acc[i][j][r];
                 }
             }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Prefill dequant-to-bf16 path (M > 64): v_mfma_f32_32x32x16_bf16, which
+// keeps the matrix cores full with four independent accumulators per wave
+// (16x16x32 needs sixteen).  Workgroup tile 256 (n) x 128 (m), four waves
+// along n, each 64 n x 128 m = 2 x 4 tiles of 32 x 32.  Per slab of 128 k a
+// lane decodes the blocks 2h and 2h+1 of the slab (h = lane/32) for its two
+// rows n = n_wave + 32 i + lane%32, i.e. 64 weights per row; MFMA step t
+// (0..7) takes elements 8t..8t+7 of those 64 from every lane, which is
+// X[m][128 s + 64 h + 8 t ..] on the A side -- contiguous 16-byte LDS reads.
+// A = X (32 m x 16 k), B = W^T (16 k x 32 n); lane l holds
+// D[m = 8*(r/4) + 4*(l/32) + r%4][n = l%32], r = 0..15.
+// ---------------------------------------------------------------------------
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+template <int U>
+__device__ __forceinline__ void prefill_load_x(u32x4_t (&xr)[U], const uint16_t *__restrict__ X, int K, int M,
+                                               int m0, int tid, int s)
+{
+#pragma unroll
+    for (int t = 0; t < U; t++) {
+        const int i = tid + 256 * t, row = i >> 4, q = i & 15;
+        const int m = m0 + row < M ? m0 + row : M - 1;
+        xr[t] = *reinterpret_cast<const u32x4_t *>(X + (int64_t)m * K + s * SLAB + 8 * q);
+    }
+}
+
+template <int U>
+__device__ __forceinline__ void prefill_store_x(const u32x4_t (&xr)[U], uint8_t *sx, int tid)
+{
+#pragma unroll
+    for (int t = 0; t < U; t++) {
+        const int i = tid + 256 * t;
+        *reinterpret_cast<u32x4_t *>(sx + (i >> 4) * XPITCH + 16 * (i & 15)) = xr[t];
+    }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256) void gemm_prefill_kernel(const uint8_t *__restrict__ B, int64_t sc_off,
+                                                           int64_t d_off, const uint16_t *__restrict__ X,
+                                                           float *__restrict__ Y, int M, int N, int K)
+{
+    constexpr int BMP = 128;                             // m per workgroup
+    constexpr int XU4P = BMP * SLAB * 2 / 16 / 256;      // 8 uint4 of X per thread per slab
+    __shared__ __attribute__((aligned(16))) uint8_t sX[2][BMP * XPITCH];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int h = lane >> 5, r32 = lane & 31;
+    const int64_t n_wave = (int64_t)blockIdx.x * 256 + wave * 64;
+    const int m0 = blockIdx.y * BMP;
+    const int nslab = K / SLAB;
+
+    int64_t wrow[2];
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const int64_t n = n_wave + 32 * i + r32;
+        wrow[i] = n < N ? n : N - 1;
+    }
+    f32x16_t acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+                acc[i][j][r] = 0.0f;
+
+    u32x4_t xr[XU4P];
+    // W bytes: slab s in wb, s+1 in wn, s+2 loading into wf (distance 2)
+    WBlk<FMT> wb[2][2], wn[2][2], wf[2][2];
+    // X staging: thread covers 16-byte units i = tid + 256 t of the 128 x 128
+    // tile (row i/16, unit i%16); rows past M re-read row M-1 and feed
+    // outputs that are never stored
+    prefill_load_x<XU4P>(xr, X, K, M, m0, tid, 0);
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int b = 0; b < 2; b++) {
+            load_wblk<FMT>(B, sc_off, d_off, K, wrow[i], 2 * h + b, wb[i][b]);
+            if (nslab > 1)
+                load_wblk<FMT>(B, sc_off, d_off, K, wrow[i], 4 + 2 * h + b, wn[i][b]);
+        }
+    prefill_store_x<XU4P>(xr, sX[0], tid);
+    lds_barrier();
+
+    for (int s = 0; s < nslab; s++) {
+        const int buf = s & 1;
+        const bool more = s + 1 < nslab;
+        if (more)
+            prefill_load_x<XU4P>(xr, X, K, M, m0, tid, s + 1);
+        if (s + 2 < nslab) {
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int b = 0; b < 2; b++)
+                    load_wblk<FMT>(B, sc_off, d_off, K, wrow[i], 4 * (s + 2) + 2 * h + b, wf[i][b]);
+        }
+        // wv[i][b*16 + e] = bf16 pair e of block b of row i.  Block 0 is
+        // decoded first; block 1 is decoded while the matrix cores run the
+        // four k-steps of block 0 (the scheduler interleaves them below).
+        uint32_t wv[2][32];
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            uint32_t tmp[16];
+            decode_wblk<FMT>(wb[i][0], 4 * s + 2 * h, tmp);
+#pragma unroll
+            for (int e = 0; e < 16; e++)
+                wv[i][e] = tmp[e];
+        }
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+            bf16x8_t xa[4];
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+                xa[j] = *reinterpret_cast<const bf16x8_t *>(&sX[buf][(32 * j + r32) * XPITCH + 128 * h + 16 * t]);
+#pragma unroll
+            for (int i = 0; i < 2; i++) {
+                const bf16x8_t bw = __builtin_bit_cast(
+                    bf16x8_t, make_uint4(wv[i][4 * t], wv[i][4 * t + 1], wv[i][4 * t + 2], wv[i][4 * t + 3]));
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[j], bw, acc[i][j], 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            uint32_t tmp[16];
+            decode_wblk<FMT>(wb[i][1], 4 * s + 2 * h + 1, tmp);
+#pragma unroll
+            for (int e = 0; e < 16; e++)
+                wv[i][16 + e] = tmp[e];
+        }
+        // interleave: one MFMA, then a few VALU of the block-1 decode
+#pragma unroll
+        for (int k = 0; k < 32; k++) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+        }
+#pragma unroll
+        for (int t = 4; t < 8; t++) {
+            bf16x8_t xa[4];
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+                xa[j] = *reinterpret_cast<const bf16x8_t *>(&sX[buf][(32 * j + r32) * XPITCH + 128 * h + 16 * t]);
+#pragma unroll
+            for (int i = 0; i < 2; i++) {
+                const bf16x8_t bw = __builtin_bit_cast(
+                    bf16x8_t, make_uint4(wv[i][4 * t], wv[i][4 * t + 1], wv[i][4 * t + 2], wv[i][4 * t + 3]));
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[j], bw, acc[i][j], 0, 0, 0);
+            }
+        }
+        if (more)
+            prefill_store_x<XU4P>(xr, sX[buf ^ 1], tid);
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+            for (int b = 0; b < 2; b++) {
+                wb[i][b] = wn[i][b];
+                wn[i][b] = wf[i][b];
+            }
+        lds_barrier();
+    }
+
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const int64_t n = n_wave + 32 * i + r32;
+        if (n >= N)
+            continue;
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int m = m0 + 32 * j + 8 * (r >> 2) + 4 * h + (r & 3);
+                if (m < M)
+                    Y[(int64_t)m * N + n] = acc[i][j][r];
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Skinny dequant-to-bf16 path for small M (M <= 16 * TM): a weight stream.
+// A workgroup of KS wavefronts owns 16*NT rows of W; wave w takes slabs
+// [w*per, (w+1)*per) of K.  Each wave is independent until the end: it
+// keeps a ring of PF slabs of W bytes in flight (PF * NT * 32 bytes per lane)
+// and reads its X fragments straight from L2 (X is small and shared by all
+// workgroups), decodes W into the MFMA B operand as in gemm_bf16_kernel,
+// and accumulates 16 x 16 tiles.  The KS partial tiles are summed once
+// through LDS, so Y is written with plain stores.
+// ---------------------------------------------------------------------------
+template <int FMT, int TM, int NT, int PF>
+__global__ __launch_bounds__(512) void gemm_skinny_kernel(const uint8_t *__restrict__ B, int64_t sc_off,
+                                                          int64_t d_off, const uint16_t *__restrict__ X,
+                                                          float *__restrict__ Y, int M, int N, int K, int per)
+{
+    extern __shared__ float red[];  // [KS][NT*TM*4][64]
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, KS = blockDim.x >> 6;
+    const int g = lane >> 4, r16 = lane & 15;
+    const int64_t n0 = (int64_t)blockIdx.x * 16 * NT;
+    const int nslab = K / SLAB;
+    const int sb = wv * per;
+    const int se = min(nslab, sb + per);
+
+    int64_t wrow[NT];
+#pragma unroll
+    for (int i = 0; i < NT; i++) {
+        const int64_t n = n0 + 16 * i + r16;
+        wrow[i] = n < N ? n : N - 1;
+    }
+    const uint16_t *xrow[TM];
+    bool xlive[TM];
+#pragma unroll
+    for (int j = 0; j < TM; j++) {
+        const int m = 16 * j + r16;
+        xlive[j] = m < M;
+        xrow[j] = X + (int64_t)(xlive[j] ? m : 0) * K + 32 * g;
+    }
+
+    f32x4_t acc[NT][TM];
+#pragma unroll
+    for (int i = 0; i < NT; i++)
+#pragma unroll
+        for (int j = 0; j < TM; j++)
+            acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // ring of PF slabs in flight: W bytes and X fragments
+    WBlk<FMT> ring[PF][NT];
+    uint4 xq[PF][TM][4];
+    auto load_slab = [&](int u, int su) {
+#pragma unroll
+        for (int i = 0; i < NT; i++)
+            load_wblk<FMT>(B, sc_off, d_off, K, wrow[i], 4 * su + g, ring[u][i]);
+#pragma unroll
+        for (int j = 0; j < TM; j++) {
+            const uint4 *xp = reinterpret_cast<const uint4 *>(xrow[j] + su * SLAB);
+#pragma unroll
+            for (int t = 0; t < 4; t++)
+                xq[u][j][t] = xp[t];
+        }
+    };
+#pragma unroll
+    for (int u = 0; u < PF; u++)
+        if (sb + u < se)
+            load_slab(u, sb + u);
+
+    for (int s = sb; s < se; s += PF) {
+#pragma unroll
+        for (int u = 0; u < PF; u++) {
+            const int su = s + u;
+            if (su < se) {
+#pragma unroll
+                for (int i = 0; i < NT; i++) {
+                    uint32_t wv16[16];
+                    decode_wblk<FMT>(ring[u][i], 4 * su + g, wv16);
+#pragma unroll
+                    for (int t = 0; t < 4; t++) {
+                        const bf16x8_t bw = __builtin_bit_cast(
+                            bf16x8_t, make_uint4(wv16[4 * t], wv16[4 * t + 1], wv16[4 * t + 2], wv16[4 * t + 3]));
+#pragma unroll
+                        for (int j = 0; j < TM; j++) {
+                            // rows of X past M read row 0 and are zeroed here
+                            const uint4 xv = xlive[j] ? xq[u][j][t] : make_uint4(0u, 0u, 0u, 0u);
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8_t, xv), bw, acc[i][j], 0, 0, 0);
+                        }
+                    }
+                }
+                if (su + PF < se)
+                    load_slab(u, su + PF);
+            }
+        }
+    }
+
+    // sum the KS partial tiles: red[w][e][lane], e = (i*TM + j)*4 + r
+    constexpr int E = NT * TM * 4;
+#pragma unroll
+    for (int i = 0; i < NT; i++)
+#pragma unroll
+        for (int j = 0; j < TM; j++)
+#pragma unroll
+            for (int r = 0; r < 4; r++)
+                red[(wv * E + (i * TM + j) * 4 + r) * 64 + lane] = acc[i][j][r];
+    __syncthreads();
+    for (int q = threadIdx.x; q < E * 64; q += blockDim.x) {
+        const int e = q >> 6, l = q & 63;
+        float sum = 0.0f;
+        for (int w = 0; w < KS; w++)
+            sum += red[(w * E + e) * 64 + l];
+        const int i = e / (TM * 4), j = (e / 4) % TM, r = e & 3;
+        const int64_t n = n0 + 16 * i + (l & 15);
+        const int m = 16 * j + 4 * (l >> 4) + r;
+        if (n < N && m < M)
+            Y[(int64_t)m * N + n] = sum;
     }
 }
 
@@ -444,17 +762,36 @@ hipError_t go_bf16(const uint8_t *blocks, const Planes &p, const uint16_t *X, fl
     return hipGetLastError();
 }
 
+template <int FMT, int TM, int NT, int PF>
+hipError_t go_skinny(const uint8_t *blocks, const Planes &p, const uint16_t *X, float *Y, int64_t M,
+                     int64_t N, int64_t K, hipStream_t s)
+{
+    const int64_t gx = (N + 16 * NT - 1) / (16 * NT);
+    const int nslab = (int)(K / SLAB);
+    // enough waves to keep ~8 per CU streaming: split K over up to 8 waves
+    int KS = 1;
+    while (gx * KS < 2048 && KS < 8 && nslab / (2 * KS) >= PF)
+        KS *= 2;
+    const int per = (nslab + KS - 1) / KS;
+    const size_t lds = (size_t)KS * NT * TM * 4 * 64 * sizeof(float);
+    hipLaunchKernelGGL((gemm_skinny_kernel<FMT, TM, NT, PF>), dim3((unsigned)gx), dim3(64 * KS), lds, s, blocks,
+                       p.scales, p.d, X, Y, (int)M, (int)N, (int)K, per);
+    return hipGetLastError();
+}
+
 template <int FMT>
 hipError_t bf16_by_m(const uint8_t *blocks, const Planes &p, const uint16_t *X, float *Y, int64_t M,
                      int64_t N, int64_t K, hipStream_t s)
 {
     if (M <= 16)
-        return go_bf16<FMT, 1, 4>(blocks, p, X, Y, M, N, K, s);
+        return go_skinny<FMT, 1, 1, 4>(blocks, p, X, Y, M, N, K, s);
     if (M <= 32)
-        return go_bf16<FMT, 2, 4>(blocks, p, X, Y, M, N, K, s);
+        return go_skinny<FMT, 2, 1, 4>(blocks, p, X, Y, M, N, K, s);
     if (M <= 64)
         return go_bf16<FMT, 4, 4>(blocks, p, X, Y, M, N, K, s);
-    return go_bf16<FMT, 8, 4>(blocks, p, X, Y, M, N, K, s);
+    hipLaunchKernelGGL(gemm_prefill_kernel<FMT>, dim3((unsigned)((N + 255) / 256), (unsigned)((M + 127) / 128)),
+                       dim3(256), 0, s, blocks, p.scales, p.d, X, Y, (int)M, (int)N, (int)K);
+    return hipGetLastError();
 }
 
 }  // namespace
