@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--quick", action="store_true", help="headline only (for profiling runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only copy a buffer of BYTES bytes 10 times (the reference kernel that scales "
+                         "the FETCH_SIZE / WRITE_SIZE counters), then exit")
     return ap.parse_args()
 
 
@@ -120,6 +123,14 @@ def main():
     ql.lib()  # fail loudly if the HIP library is not built
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_probe:
+        a = torch.ones(args.copy_probe // 4, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(10):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": args.copy_probe, "launches": 10}))
+        return
     result = {}
 
     def bf16_dev(a):
@@ -251,11 +262,23 @@ def bench_parts(torch, ql, synth, dev, bf16_dev):
         ms = timed_calls(lambda i: ql.qmatmul("q4k", copies[i % R], X, N, out=Y), 4 * R)
         fl = 2.0 * M * N * K
         parts[f"batched_q4k_m{M}"] = {
-            "us": round(ms * 1e3, 3), "path": "gemv" if M <= 8 else "mfma_bf16",
+            "us": round(ms * 1e3, 3), "path": "gemv" if M <= 2 else "mfma_bf16",
             "weight_GBps": round(blocks.numel() / ms / 1e6, 1),
             "hbm_frac": round((blocks.numel() + M * K * 2 + M * N * 4) / ms / 1e6 / HBM_PEAK_GBPS, 4),
             "TFLOPs": round(fl / ms / 1e9, 2)}
         log(f"  M={M}: {ms * 1e3:.2f} us")
+    # GEMV / MFMA crossover at this shape (sets the AUTO dispatch)
+    cross = {}
+    for M in range(1, 9):
+        X = bf16_dev(xs[:M])
+        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        row = {}
+        for path in ("gemv", "mfma_bf16"):
+            ms = timed_calls(lambda i: ql.qmatmul("q4k", copies[i % R], X, N, out=Y, path=path), 2 * R)
+            row[path] = round(ms * 1e3, 2)
+        cross[str(M)] = row
+    parts["crossover_q4k_4096x14336_us"] = cross
+    log(f"  crossover: {cross}")
     del copies, blocks
     torch.cuda.empty_cache()
 

@@ -115,7 +115,9 @@ int qmatmul_ex(int fmt, const void *blocks, const void *X_bf16, float *Y_fp32, i
     const hipStream_t s = as_stream(stream);
     switch (path) {
     case QPATH_AUTO:
-        if (M <= 8) {
+        // measured crossover on MI355X: the fused GEMV wins for one or two
+        // tokens; from three tokens the MFMA weight stream is faster
+        if (M <= 2) {
             st = status_of(ql::launch_gemv(fmt, B, X, Y_fp32, (int)M, N, K, s));
             if (st != Q_ENOTSUP)
                 return st;

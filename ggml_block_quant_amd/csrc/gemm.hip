@@ -233,7 +233,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint8_t *__restric
         for (int i = 0; i < NT; i++)
             load_wblk<FMT>(B, sc_off, d_off, K, wrow[i], 4 * (s0 + 1) + g, wb[i]);
     }
-    __syncthreads();
+    lds_barrier();
 
     for (int s = s0; s < s1; s++) {
         const int buf = (s - s0) & 1;
@@ -260,7 +260,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint8_t *__restric
         }
         if (s + 1 < s1)
             store_x(buf ^ 1, x1);
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int i = 0; i < NT; i++) {
             wa[i] = wb[i];
@@ -306,176 +306,6 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint8_t *__restric
 // A = X (32 m x 16 k), B = W^T (16 k x 32 n); lane l holds
 // D[m = 8*(r/4) + 4*(l/32) + r%4][n = l%32], r = 0..15.
 // ---------------------------------------------------------------------------
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
-template <int U>
-__device__ __forceinline__ void prefill_load_x(u32x4_t (&xr)[U], const uint16_t *__restrict__ X, int K, int M,
-                                               int m0, int tid, int s)
-{
-#pragma unroll
-    for (int t = 0; t < U; t++) {
-        const int i = tid + 256 * t, row = i >> 4, q = i & 15;
-        const int m = m0 + row < M ? m0 + row : M - 1;
-        xr[t] = *reinterpret_cast<const u32x4_t *>(X + (int64_t)m * K + s * SLAB + 8 * q);
-    }
-}
-
-template <int U>
-__device__ __forceinline__ void prefill_store_x(const u32x4_t (&xr)[U], uint8_t *sx, int tid)
-{
-#pragma unroll
-    for (int t = 0; t < U; t++) {
-        const int i = tid + 256 * t;
-        *reinterpret_cast<u32x4_t *>(sx + (i >> 4) * XPITCH + 16 * (i & 15)) = xr[t];
-    }
-}
-
-template <int FMT>
-__global__ __launch_bounds__(256) void gemm_prefill_kernel(const uint8_t *__restrict__ B, int64_t sc_off,
-                                                           int64_t d_off, const uint16_t *__restrict__ X,
-                                                           float *__restrict__ Y, int M, int N, int K)
-{
-    constexpr int BMP = 128;                             // m per workgroup
-    constexpr int XU4P = BMP * SLAB * 2 / 16 / 256;      // 8 uint4 of X per thread per slab
-    __shared__ __attribute__((aligned(16))) uint8_t sX[2][BMP * XPITCH];
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int h = lane >> 5, r32 = lane & 31;
-    const int64_t n_wave = (int64_t)blockIdx.x * 256 + wave * 64;
-    const int m0 = blockIdx.y * BMP;
-    const int nslab = K / SLAB;
-
-    int64_t wrow[2];
-#pragma unroll
-    for (int i = 0; i < 2; i++) {
-        const int64_t n = n_wave + 32 * i + r32;
-        wrow[i] = n < N ? n : N - 1;
-    }
-    f32x16_t acc[2][4];
-#pragma unroll
-    for (int i = 0; i < 2; i++)
-#pragma unroll
-        for (int j = 0; j < 4; j++)
-#pragma unroll
-            for (int r = 0; r < 16; r++)
-                acc[i][j][r] = 0.0f;
-
-    u32x4_t xr[XU4P];
-    // W bytes: slab s in wb, s+1 in wn, s+2 loading into wf (distance 2)
-    WBlk<FMT> wb[2][2], wn[2][2], wf[2][2];
-    // X staging: thread covers 16-byte units i = tid + 256 t of the 128 x 128
-    // tile (row i/16, unit i%16); rows past M re-read row M-1 and feed
-    // outputs that are never stored
-    prefill_load_x<XU4P>(xr, X, K, M, m0, tid, 0);
-#pragma unroll
-    for (int i = 0; i < 2; i++)
-#pragma unroll
-        for (int b = 0; b < 2; b++) {
-            load_wblk<FMT>(B, sc_off, d_off, K, wrow[i], 2 * h + b, wb[i][b]);
-            if (nslab > 1)
-                load_wblk<FMT>(B, sc_off, d_off, K, wrow[i], 4 + 2 * h + b, wn[i][b]);
-        }
-    prefill_store_x<XU4P>(xr, sX[0], tid);
-    lds_barrier();
-
-    for (int s = 0; s < nslab; s++) {
-        const int buf = s & 1;
-        const bool more = s + 1 < nslab;
-        if (more)
-            prefill_load_x<XU4P>(xr, X, K, M, m0, tid, s + 1);
-        if (s + 2 < nslab) {
-#pragma unroll
-            for (int i = 0; i < 2; i++)
-#pragma unroll
-                for (int b = 0; b < 2; b++)
-                    load_wblk<FMT>(B, sc_off, d_off, K, wrow[i], 4 * (s + 2) + 2 * h + b, wf[i][b]);
-        }
-        // wv[i][b*16 + e] = bf16 pair e of block b of row i.  Block 0 is
-        // decoded first; block 1 is decoded while the matrix cores run the
-        // four k-steps of block 0 (the scheduler interleaves them below).
-        uint32_t wv[2][32];
-#pragma unroll
-        for (int i = 0; i < 2; i++) {
-            uint32_t tmp[16];
-            decode_wblk<FMT>(wb[i][0], 4 * s + 2 * h, tmp);
-#pragma unroll
-            for (int e = 0; e < 16; e++)
-                wv[i][e] = tmp[e];
-        }
-#pragma unroll
-        for (int t = 0; t < 4; t++) {
-            bf16x8_t xa[4];
-#pragma unroll
-            for (int j = 0; j < 4; j++)
-                xa[j] = *reinterpret_cast<const bf16x8_t *>(&sX[buf][(32 * j + r32) * XPITCH + 128 * h + 16 * t]);
-#pragma unroll
-            for (int i = 0; i < 2; i++) {
-                const bf16x8_t bw = __builtin_bit_cast(
-                    bf16x8_t, make_uint4(wv[i][4 * t], wv[i][4 * t + 1], wv[i][4 * t + 2], wv[i][4 * t + 3]));
-#pragma unroll
-                for (int j = 0; j < 4; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[j], bw, acc[i][j], 0, 0, 0);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < 2; i++) {
-            uint32_t tmp[16];
-            decode_wblk<FMT>(wb[i][1], 4 * s + 2 * h + 1, tmp);
-#pragma unroll
-            for (int e = 0; e < 16; e++)
-                wv[i][16 + e] = tmp[e];
-        }
-        // interleave: one MFMA, then a few VALU of the block-1 decode
-#pragma unroll
-        for (int k = 0; k < 32; k++) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-        }
-#pragma unroll
-        for (int t = 4; t < 8; t++) {
-            bf16x8_t xa[4];
-#pragma unroll
-            for (int j = 0; j < 4; j++)
-                xa[j] = *reinterpret_cast<const bf16x8_t *>(&sX[buf][(32 * j + r32) * XPITCH + 128 * h + 16 * t]);
-#pragma unroll
-            for (int i = 0; i < 2; i++) {
-                const bf16x8_t bw = __builtin_bit_cast(
-                    bf16x8_t, make_uint4(wv[i][4 * t], wv[i][4 * t + 1], wv[i][4 * t + 2], wv[i][4 * t + 3]));
-#pragma unroll
-                for (int j = 0; j < 4; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[j], bw, acc[i][j], 0, 0, 0);
-            }
-        }
-        if (more)
-            prefill_store_x<XU4P>(xr, sX[buf ^ 1], tid);
-#pragma unroll
-        for (int i = 0; i < 2; i++)
-#pragma unroll
-            for (int b = 0; b < 2; b++) {
-                wb[i][b] = wn[i][b];
-                wn[i][b] = wf[i][b];
-            }
-        lds_barrier();
-    }
-
-#pragma unroll
-    for (int i = 0; i < 2; i++) {
-        const int64_t n = n_wave + 32 * i + r32;
-        if (n >= N)
-            continue;
-#pragma unroll
-        for (int j = 0; j < 4; j++)
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int m = m0 + 32 * j + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (m < M)
-                    Y[(int64_t)m * N + n] = acc[i][j][r];
-            }
-    }
-}
-
 // ---------------------------------------------------------------------------
 // Skinny dequant-to-bf16 path for small M (M <= 16 * TM): a weight stream.
 // A workgroup of KS wavefronts owns 16*NT rows of W; wave w takes slabs
@@ -531,9 +361,11 @@ __global__ __launch_bounds__(512) void gemm_skinny_kernel(const uint8_t *__restr
 #pragma unroll
         for (int j = 0; j < TM; j++) {
             const uint4 *xp = reinterpret_cast<const uint4 *>(xrow[j] + su * SLAB);
+            // rows of the 16-row tile past M are not read (they are zeroed at use)
+            if (xlive[j])
 #pragma unroll
-            for (int t = 0; t < 4; t++)
-                xq[u][j][t] = xp[t];
+                for (int t = 0; t < 4; t++)
+                    xq[u][j][t] = xp[t];
         }
     };
 #pragma unroll
@@ -783,15 +615,16 @@ template <int FMT>
 hipError_t bf16_by_m(const uint8_t *blocks, const Planes &p, const uint16_t *X, float *Y, int64_t M,
                      int64_t N, int64_t K, hipStream_t s)
 {
+    // tall matrices (many row tiles) stream two 16-row tiles per wave
+    const bool tall = N >= 32768;
     if (M <= 16)
-        return go_skinny<FMT, 1, 1, 4>(blocks, p, X, Y, M, N, K, s);
+        return tall ? go_skinny<FMT, 1, 2, 4>(blocks, p, X, Y, M, N, K, s)
+                    : go_skinny<FMT, 1, 1, 4>(blocks, p, X, Y, M, N, K, s);
     if (M <= 32)
         return go_skinny<FMT, 2, 1, 4>(blocks, p, X, Y, M, N, K, s);
     if (M <= 64)
         return go_bf16<FMT, 4, 4>(blocks, p, X, Y, M, N, K, s);
-    hipLaunchKernelGGL(gemm_prefill_kernel<FMT>, dim3((unsigned)((N + 255) / 256), (unsigned)((M + 127) / 128)),
-                       dim3(256), 0, s, blocks, p.scales, p.d, X, Y, (int)M, (int)N, (int)K);
-    return hipGetLastError();
+    return go_bf16<FMT, 8, 4>(blocks, p, X, Y, M, N, K, s);
 }
 
 }  // namespace

@@ -124,13 +124,14 @@ def test_act_quantize_entry_point():
 
 @pytest.mark.parametrize("fmt", FMTS)
 def test_auto_path_dispatch(fmt):
-    """AUTO = GEMV for M <= 8 (bit for bit: the GEMV is deterministic) and
-    the bf16 MFMA GEMM above (equal up to the order of the fp32 split-K
-    atomics, so compared to 1e-6 of sum |w||x|)."""
+    """AUTO = GEMV for M <= 2 (bit for bit: the GEMV is deterministic) and
+    the bf16 MFMA GEMM above (equal up to the order of fp32 sums, so
+    compared to 1e-6 of sum |w||x|)."""
     N, K = 200, 1024
     w = synth.weights_bf16(7000, N, K)
     blocks = ql.isq(fmt, to_dev_bf16(w))
-    for M, path in ((1, "gemv"), (8, "gemv"), (9, "mfma_bf16"), (100, "mfma_bf16")):
+    for M, path in ((1, "gemv"), (2, "gemv"), (3, "mfma_bf16"), (8, "mfma_bf16"), (9, "mfma_bf16"),
+                    (100, "mfma_bf16")):
         x = synth.activations_bf16(7001, M, K)
         X = to_dev_bf16(x)
         a = ql.qmatmul(fmt, blocks, X, N, path="auto")
@@ -187,7 +188,8 @@ def test_workload_gemv_ffn_up_q4k_and_q8_0():
 
 def test_workload_batched_decode_down_proj():
     """M in {4, 16, 64} x K = 14336 x N = 4096, Q4K weights with 1 % outliers
-    at 10 sigma; M = 4 runs the GEMV, 16 and 64 the bf16 MFMA path."""
+    at 10 sigma, on the AUTO path (bf16 MFMA for all three) and, for M = 4,
+    also on the GEMV."""
     w = synth.weights_bf16(synth.seed_for(3, 0), 4096, 14336, outliers=True)
     x = synth.activations_bf16(synth.seed_for(3, 1), 64, 14336)
     W = oracle.dequant("q4k", oracle.quantize("q4k", w), 4096, 14336)
@@ -196,6 +198,9 @@ def test_workload_batched_decode_down_proj():
         Yr, den = oracle.matmul_a16(W, x[:M])
         y = ql.qmatmul("q4k", blocks, to_dev_bf16(x[:M]), 4096).cpu().numpy()
         check_outputs(y, Yr, den, f"down-proj M={M}")
+        if M == 4:
+            y = ql.qmatmul("q4k", blocks, to_dev_bf16(x[:M]), 4096, path="gemv").cpu().numpy()
+            check_outputs(y, Yr, den, "down-proj M=4 gemv")
 
 
 def _sampled(N, M, count, seed):
@@ -238,7 +243,7 @@ def test_workload_lm_head_q6k_m1_m8():
     from gpu_util import from_dev_bf16
     w_rows = from_dev_bf16(W[torch.from_numpy(rows).cuda()])
     Wr = oracle.dequant("q6k", oracle.quantize("q6k", w_rows), len(rows), K)
-    for M in (1, 8):
-        y = ql.qmatmul("q6k", blocks, to_dev_bf16(x[:M]), N).cpu().numpy()
+    for M, path in ((1, "auto"), (8, "auto"), (8, "gemv")):
+        y = ql.qmatmul("q6k", blocks, to_dev_bf16(x[:M]), N, path=path).cpu().numpy()
         Yr, den = oracle.matmul_a16(Wr, x[:M])
-        check_outputs(y[:, rows], Yr, den, f"lm_head M={M}")
+        check_outputs(y[:, rows], Yr, den, f"lm_head M={M} {path}")
