@@ -56,6 +56,34 @@ def parse():
     return ap.parse_args()
 
 
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gemv_q4k_14336x4096_m1_traffic.md")
+TRAFFIC_SOURCES = [os.path.join(ROOT, "ggml_block_quant_amd", "csrc", f) for f in ("gemv.hip", "qlinear_internal.h")]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the headline GEMV from the committed FETCH_SIZE /
+    WRITE_SIZE counter record, scaled by the copy-probe factors it states; None
+    when there is no record or the kernel's sources changed since it was taken."""
+    import hashlib
+
+    try:
+        rec = {}
+        for line in open(TRAFFIC_RECORD):
+            if line.startswith("traffic_"):
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.strip()
+        h = hashlib.sha256()
+        for f in TRAFFIC_SOURCES:
+            h.update(open(f, "rb").read())
+        if h.hexdigest() != rec["traffic_source_sha256"]:
+            return None
+        kib = (float(rec["traffic_fetch_kib_per_dispatch"]) * float(rec["traffic_fetch_scale"])
+               + float(rec["traffic_write_kib_per_dispatch"]) * float(rec["traffic_write_scale"]))
+        return int(round(kib * 1024))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def copies_for(nbytes: int) -> int:
     return max(2, math.ceil(2 * MALL_BYTES / nbytes))
 
@@ -199,7 +227,8 @@ def main():
                    "activations": "N(0,1) bf16", "weight_copies_rotated": q4["copies"],
                    "launch": "HIP graph of `steps` launches"},
         "roofline": {"bound": "hbm", "achieved": round(q4["alg_GBps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(q4["alg_GBps"] / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(q4["alg_GBps"] / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(),
+                     "traffic_unit": "HBM bytes per launch (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0)",
                      "kernel": "gemv_kernel<Q4K, M=1>", "alg_bytes_per_launch": q4["alg_bytes"]},
     })
     parts["gemv_q8_0_14336x4096_m1"] = {
@@ -377,7 +406,7 @@ def bench_parts(torch, ql, synth, dev, bf16_dev):
 
 def cpu_baseline(w, x):
     """The oracle's quantized GEMV (unpack + exact dequant + fp64 matmul) on
-    the host cores, over whole 14336x4096 Q4K matrices, repeated for ~10 s."""
+    the host cores, over whole 14336x4096 Q4K matrices, repeated for ~12 s."""
     import oracle
 
     N, K = w.shape
@@ -390,7 +419,7 @@ def cpu_baseline(w, x):
         oracle.matmul_a16(Wd, x)
         reps += 1
         el = time.perf_counter() - t0
-        if el > 10.0 or reps >= 50:
+        if el > 12.0 or reps >= 1000:
             break
     cores = len(os.sched_getaffinity(0))
     threads = int(os.environ.get("OMP_NUM_THREADS", cores))
