@@ -34,20 +34,6 @@ __device__ __forceinline__ float h2f(uint32_t bits16)
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits16 & 0xffffu));
 }
 
-// Workgroup barrier for LDS hand-offs only.  __syncthreads() also fences
-// global memory, which makes the compiler drain every outstanding global
-// load (s_waitcnt vmcnt(0)) -- including prefetches meant to stay in flight
-// across the barrier.  Here only this wave's LDS accesses must be complete
-// (lgkmcnt(0)); the signal fences keep the compiler from moving memory
-// accesses across the barrier.
-__device__ __forceinline__ void lds_barrier()
-{
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63, expcnt 7, lgkmcnt 0
-    __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
 // two fp32 -> one dword of two bf16 (round to nearest even, v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b)
 {

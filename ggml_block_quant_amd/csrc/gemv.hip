@@ -451,6 +451,236 @@ __global__ __launch_bounds__(512) void gemv_kernel(Geo g, const uint16_t *__rest
     }
 }
 
+// ----------------------------------------------------------------------------
+// One-shot GEMV for one or two tokens.  Each wave owns R whole rows and
+// issues every weight load for them at once; the four waves of a workgroup
+// share one copy of X, staged in LDS (zero-padded to CPT*64 chunks) by the
+// workgroup before any weight is consumed.  The threads that stage X also
+// produce the per-chunk sums of the bias correction, so no wave recomputes
+// them.  There is no loop over rows: the grid covers N, and the weight bytes
+// of a wave are in flight from its first instructions.
+// ----------------------------------------------------------------------------
+constexpr int LW = 4;  // waves per workgroup of the one-shot kernel
+
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+
+// weight bytes are read once: non-temporal loads keep them from displacing X
+// and the scale planes in the caches
+__device__ __forceinline__ uint4 ld_stream16(const uint8_t *p)
+{
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld_stream8(const uint8_t *p)
+{
+    const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p));
+    return make_uint2(v.x, v.y);
+}
+
+// what a lane loads for one chunk of one row; Q4K takes one dword of the
+// 16-byte group header (dword lane%4) and the quad shares the four by DPP
+template <int FMT> struct WLoad;
+template <> struct WLoad<FMT_Q4K> { uint4 c; uint32_t h; };
+template <> struct WLoad<FMT_Q6K> { Chunk<FMT_Q6K> ck; };
+template <> struct WLoad<FMT_Q8_0> { Chunk<FMT_Q8_0> ck; };
+
+template <int FMT>
+__device__ __forceinline__ void load_w(const Geo &g, int64_t n, int c, int lane, WLoad<FMT> &w)
+{
+    if constexpr (FMT == FMT_Q4K) {
+        const int64_t sub = n * (g.K / 32) + c;
+        w.c = ld_stream16(g.B + 16 * sub);
+        w.h = *reinterpret_cast<const uint32_t *>(g.B + g.scales_off + 16 * (sub >> 3) + 4 * (lane & 3));
+    } else if constexpr (FMT == FMT_Q6K) {
+        const int64_t grp = n * (g.K / 256) + (c >> 3);
+        const int cc = c & 7;
+        const uint8_t *Cg = g.B + 192 * grp;
+        w.ck.lo = ld_stream16(Cg + 16 * cc);
+        w.ck.hi = ld_stream8(Cg + 128 + 8 * cc);
+        w.ck.sc2 = *reinterpret_cast<const uint16_t *>(g.B + g.scales_off + 16 * grp + 2 * cc);
+        w.ck.d = *reinterpret_cast<const uint16_t *>(g.B + g.d_off + 2 * grp);
+    } else {
+        const int64_t blk = n * (g.K / 32) + c;
+        w.ck.c0 = ld_stream16(g.B + 32 * blk);
+        w.ck.c1 = ld_stream16(g.B + 32 * blk + 16);
+        w.ck.d = *reinterpret_cast<const uint16_t *>(g.B + g.scales_off + 2 * blk);
+    }
+}
+
+template <int FMT>
+__device__ __forceinline__ Chunk<FMT> chunk_of(const WLoad<FMT> &w)
+{
+    if constexpr (FMT == FMT_Q4K) {
+        const int h = (int)w.h;
+        Chunk<FMT_Q4K> ck;
+        ck.c = w.c;
+        ck.h.x = __builtin_amdgcn_update_dpp(0, h, 0x00, 0xF, 0xF, false);  // quad_perm [0,0,0,0]
+        ck.h.y = __builtin_amdgcn_update_dpp(0, h, 0x55, 0xF, 0xF, false);  // quad_perm [1,1,1,1]
+        ck.h.z = __builtin_amdgcn_update_dpp(0, h, 0xAA, 0xF, 0xF, false);  // quad_perm [2,2,2,2]
+        ck.h.w = __builtin_amdgcn_update_dpp(0, h, 0xFF, 0xF, 0xF, false);  // quad_perm [3,3,3,3]
+        return ck;
+    } else {
+        return w.ck;
+    }
+}
+
+template <int FMT, int M, int CPT, int R>
+__global__ __launch_bounds__(64 * LW) void gemv_lds_kernel(Geo g, const uint16_t *__restrict__ X,
+                                                           float *__restrict__ Y, int64_t N)
+{
+    constexpr int SLOTS = 64 * CPT;           // chunk slots per row
+    constexpr bool SUMS = FMT != FMT_Q8_0;    // bias-correction sums (Q4K, Q6K)
+    constexpr int XU = M * CPT;               // uint4 of X staged per thread
+    __shared__ uint4 sx[M][4][SLOTS];         // quarter t of chunk c at sx[m][t][c]
+    __shared__ float2 ss[SUMS ? M : 1][SUMS ? SLOTS : 1];
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int S = g.K / 32;
+    const int64_t n0 = ((int64_t)blockIdx.x * LW + wv) * R;
+
+    // X first, so that waiting for it never waits for the weights
+    uint4 xs[XU];
+#pragma unroll
+    for (int j = 0; j < XU; j++) {
+        const int u = tid + 64 * LW * j;
+        const int m = u / (4 * SLOTS), c = (u >> 2) % SLOTS, t = u & 3;
+        const int cc = c < S ? c : S - 1;
+        xs[j] = *reinterpret_cast<const uint4 *>(X + (int64_t)m * g.K + 32 * cc + 8 * t);
+    }
+    // every weight load of the wave; rows past N re-read row N-1 and slots
+    // past the row end re-read its last chunk (their X is zero)
+    WLoad<FMT> w[R][CPT];
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+        const int64_t n = n0 + r < N ? n0 + r : N - 1;
+#pragma unroll
+        for (int i = 0; i < CPT; i++) {
+            const int c = lane + 64 * i;
+            load_w<FMT>(g, n, c < S ? c : S - 1, lane, w[r][i]);
+        }
+    }
+    // stage X and the chunk sums (four consecutive lanes hold one chunk)
+#pragma unroll
+    for (int j = 0; j < XU; j++) {
+        const int u = tid + 64 * LW * j;
+        const int m = u / (4 * SLOTS), c = (u >> 2) % SLOTS, t = u & 3;
+        const uint32_t keep = c < S ? ~0u : 0u;
+        const uint4 v = make_uint4(xs[j].x & keep, xs[j].y & keep, xs[j].z & keep, xs[j].w & keep);
+        sx[m][t][c] = v;
+        if constexpr (SUMS) {
+            float p = dot2(v.x, 0x3F803F80u, 0.0f);
+            p = dot2(v.y, 0x3F803F80u, p);
+            p = dot2(v.z, 0x3F803F80u, p);
+            p = dot2(v.w, 0x3F803F80u, p);
+            p += dpp_f<0xB1>(p);  // quarters t, t^1: one 16-element half
+            if constexpr (FMT == FMT_Q4K) {
+                p += dpp_f<0x4E>(p);  // both halves: the chunk
+                if (t == 0)
+                    ss[m][c].x = p;
+            } else {
+                if (t == 0)
+                    ss[m][c].x = p;
+                if (t == 2)
+                    ss[m][c].y = p;
+            }
+        }
+    }
+    lds_barrier();
+
+    const Masks k = make_masks();
+    constexpr int V = pow2_at_least(R * M);
+    float v[V];
+#pragma unroll
+    for (int t = 0; t < V; t++)
+        v[t] = 0.0f;
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+        float acc[M];
+#pragma unroll
+        for (int m = 0; m < M; m++)
+            acc[m] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < CPT; i++) {
+            const int c = lane + 64 * i;
+            XChunk<M> xc;
+#pragma unroll
+            for (int m = 0; m < M; m++) {
+#pragma unroll
+                for (int t = 0; t < 4; t++) {
+                    const uint4 q = sx[m][t][c];
+                    xc.p[m][4 * t + 0] = q.x;
+                    xc.p[m][4 * t + 1] = q.y;
+                    xc.p[m][4 * t + 2] = q.z;
+                    xc.p[m][4 * t + 3] = q.w;
+                }
+                if constexpr (FMT == FMT_Q4K) {
+                    const float tot = ss[m][c].x;
+                    xc.s0[m] = 128.0f * tot;
+                    xc.s1[m] = tot;
+                } else if constexpr (FMT == FMT_Q6K) {
+                    const float2 h = ss[m][c];
+                    xc.s0[m] = 160.0f * h.x;
+                    xc.s1[m] = 160.0f * h.y;
+                }
+            }
+            const Chunk<FMT> ck = chunk_of<FMT>(w[r][i]);
+            if constexpr (FMT == FMT_Q4K)
+                q4k_dot<M>(ck, xc, c & 7, acc, k);
+            else if constexpr (FMT == FMT_Q6K)
+                q6k_dot<M>(ck, xc, acc, k);
+            else
+                q8_0_dot<M>(ck, xc, acc);
+        }
+#pragma unroll
+        for (int m = 0; m < M; m++)
+            v[r * M + m] = acc[m];
+    }
+    const float tot = butterfly_sum<V>(v, lane);
+    const int idx = butterfly_index<V>(lane);
+    if (lane < V && idx < R * M) {
+        const int r = idx / M, m = idx % M;
+        if (n0 + r < N)
+            Y[(int64_t)m * N + n0 + r] = tot;
+    }
+}
+
+template <int FMT, int M, int CPT>
+hipError_t go_lds(const Geo &g, const uint16_t *X, float *Y, int64_t N, hipStream_t s)
+{
+    constexpr int R = (M == 1 && CPT <= 2) ? 2 : 1;
+    const int64_t grid = (N + LW * R - 1) / (LW * R);
+    hipLaunchKernelGGL((gemv_lds_kernel<FMT, M, CPT, R>), dim3((unsigned)grid), dim3(64 * LW), 0, s, g, X, Y, N);
+    return hipGetLastError();
+}
+
+// one-shot kernel for M <= 2 while X fits the workgroup's LDS budget
+// (M * CPT <= 14: at most 63 KiB); false when the shape needs the
+// persistent kernel
+template <int FMT, int M>
+bool pick_lds(const Geo &g, const uint16_t *X, float *Y, int64_t N, hipStream_t s, hipError_t &e)
+{
+    const int S = g.K / 32;
+    const int cpt = (S + 63) / 64;
+    if (M > 2 || cpt > 8 || M * cpt > 14)
+        return false;
+    switch (cpt) {
+    case 1: e = go_lds<FMT, M, 1>(g, X, Y, N, s); return true;
+    case 2: e = go_lds<FMT, M, 2>(g, X, Y, N, s); return true;
+    case 3: e = go_lds<FMT, M, 3>(g, X, Y, N, s); return true;
+    case 4: e = go_lds<FMT, M, 4>(g, X, Y, N, s); return true;
+    case 5: e = go_lds<FMT, M, 5>(g, X, Y, N, s); return true;
+    case 6: e = go_lds<FMT, M, 6>(g, X, Y, N, s); return true;
+    case 7: e = go_lds<FMT, M, 7>(g, X, Y, N, s); return true;
+    default:
+        if constexpr (M == 1) {
+            e = go_lds<FMT, M, 8>(g, X, Y, N, s);
+            return true;
+        }
+        return false;
+    }
+}
+
 template <int FMT, int M, int CPT, int R>
 hipError_t go(const Geo &g, const uint16_t *X, float *Y, int64_t N, int KS, int wgs_per_cu, hipStream_t s)
 {
@@ -467,6 +697,11 @@ template <int FMT, int M>
 hipError_t pick(const Geo &g, const uint16_t *X, float *Y, int64_t N, hipStream_t s)
 {
     const int S = g.K / 32;  // chunks per row
+    if constexpr (M <= 2) {
+        hipError_t e;
+        if (pick_lds<FMT, M>(g, X, Y, N, s, e))
+            return e;
+    }
     constexpr int R = M <= 4 ? 2 : 1;
     // Two chunks of X per lane fit in registers only for small M; Q8_0
     // streams twice the bytes per chunk and prefers one chunk per lane.

@@ -39,6 +39,20 @@ inline Planes planes_of(int fmt, int64_t N, int64_t K)
     return p;
 }
 
+// Workgroup barrier for LDS hand-offs only.  __syncthreads() also fences
+// global memory, which makes the compiler drain every outstanding global
+// load (s_waitcnt vmcnt(0)) -- including loads meant to stay in flight
+// across the barrier.  Here only this wave's LDS accesses must be complete
+// (lgkmcnt(0)); the signal fences keep the compiler from moving memory
+// accesses across the barrier.
+__device__ __forceinline__ void lds_barrier()
+{
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63, expcnt 7, lgkmcnt 0
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 hipError_t launch_isq(int fmt, const uint16_t *W, int64_t N, int64_t K, uint8_t *out,
                       hipStream_t s);
 hipError_t launch_dequant(int fmt, const uint8_t *blocks, int64_t N, int64_t K, float *W,

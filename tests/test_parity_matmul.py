@@ -80,6 +80,44 @@ def test_gemv_one_hot_is_exact(fmt):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_one_and_two_tokens_all_widths(fmt):
+    """One- and two-token GEMVs stage X in LDS with one to eight chunks of 32
+    per lane (K = 32*64*CPT at most); K = 8192 ... 16384 complete the widths
+    the shape test does not reach, with ragged N and rows past the last
+    full workgroup."""
+    for K in (8192, 10240, 12288, 16384):
+        for M in (1, 2):
+            for N in (1, 9, 300):
+                w = synth.weights_bf16(5000 + K + N, N, K, outliers=True)
+                x = synth.activations_bf16(5001 + M, M, K)
+                Yr, den = a16_ref(fmt, w, x)
+                check_outputs(run(fmt, "gemv", w, x), Yr, den, f"gemv {fmt} M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M", [1, 2])
+def test_gemv_one_hot_is_exact_one_two_tokens(fmt, M):
+    """The one-hot pin for one and two tokens: every position of the first
+    256-element group, and positions of the second chunk slot of each lane
+    (K = 4096: chunks 64..127) and the row's last element, must return the
+    dequantized weight bit for bit."""
+    N, K = 40, 4096
+    w = synth.weights_bf16(4200 + M, N, K, outliers=True)
+    blocks = ql.isq(fmt, to_dev_bf16(w))
+    Wref = oracle.dequant(fmt, oracle.quantize(fmt, w), N, K).astype(np.float32)
+    ks = list(range(0, 256)) + list(range(2048, 2304, 3)) + [3000, 4095]
+    for k in ks:
+        x = np.zeros((M, K), np.uint16)
+        x[0, k] = 0x3F80  # 1.0
+        if M == 2:
+            x[1, (k + 37) % K] = 0x3F80
+        Y = ql.qmatmul(fmt, blocks, to_dev_bf16(x), N, path="gemv").cpu().numpy()
+        assert np.array_equal(Y[0], Wref[:, k]), f"{fmt} M={M} k={k}"
+        if M == 2:
+            assert np.array_equal(Y[1], Wref[:, (k + 37) % K]), f"{fmt} M=2 k={(k + 37) % K}"
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 def test_mfma_bf16_one_hot(fmt):
     """Same pin for the bf16 MFMA path: one-hot rows give bf16(w) exactly."""
     N, K = 130, 512
