@@ -123,9 +123,15 @@ def graph_of(torch, launch, n):
     return g
 
 
-def time_graph(torch, g, reps, calls_per_replay):
+def time_graph(torch, g, reps, calls_per_replay, warm_s=0.1):
+    """Average time per call over `reps` replays, after replaying for at
+    least `warm_s` seconds (the GPU clocks settle under sustained load)."""
+    t0 = time.perf_counter()
     g.replay()
     torch.cuda.synchronize()
+    while time.perf_counter() - t0 < warm_s:
+        g.replay()
+        torch.cuda.synchronize()
     with Timer(torch) as t:
         for _ in range(reps):
             g.replay()

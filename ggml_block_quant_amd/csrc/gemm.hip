@@ -19,6 +19,8 @@
 // tiles alone cannot fill the 256 CUs.
 #include "qlinear_internal.h"
 
+#include <type_traits>
+
 namespace ql {
 namespace {
 
@@ -411,6 +413,295 @@ __global__ __launch_bounds__(512) void gemm_skinny_kernel(const uint8_t *__restr
 }
 
 // ---------------------------------------------------------------------------
+// Prefill dequant-to-bf16 path (large M): output tile 256 (m) x 256 (n) per
+// workgroup of four waves, each wave 128 x 128 = 4 x 4 tiles of
+// v_mfma_f32_32x32x16_bf16 (256 accumulator registers, one wave per SIMD).
+// K advances in slabs of 32 (one Q8_0 block / one K-quant sub-block per row).
+//
+//   * Every global read is a direct global->LDS load (no registers, no LDS
+//     store instruction): the X slab (bf16) into a ring of four stages and
+//     the raw block bytes of the 256 W rows into a ring of three.  The only
+//     waits on them are the explicit vmcnt waits below.
+//   * Thread t decodes row t of the W slab from its raw bytes to bf16 and
+//     stores it into a double-buffered W stage, one slab ahead, while the
+//     wave's first sixteen MFMAs of the current slab run.
+//   * Both bf16 operand stages use one layout: 16-byte chunk c (k = 8c..8c+7)
+//     of row r sits at slot 4r + (c ^ ((r >> 2) & 3)), so the sixteen rows a
+//     ds_read_b128 phase touches land on distinct banks.
+//   * One barrier per slab, between its two k-steps; after it the fragments
+//     of the next slab are read and the loads of slab s+4 are issued.
+//   * When the tiles alone cannot fill the chip, gridDim.y splits K: each
+//     workgroup takes a run of slabs and adds its partial tile into Y
+//     (zeroed beforehand) with fp32 atomics.
+// ---------------------------------------------------------------------------
+constexpr int PBM = 256, PBN = 256, PBK = 32;
+constexpr int PF_MIN_M = 128;                   // smallest M routed here (measured crossover)
+constexpr int PNX = 4, PNR = 3, PNW = 2;        // X, raw W and bf16 W stages
+constexpr int PSTAGE = 256 * PBK * 2;           // bytes per bf16 operand stage
+constexpr int PAHEAD = 4;                       // slabs between issue and use
+static_assert(PAHEAD == PNR + 1 && PAHEAD <= PNX, "stage counts");
+
+__device__ __forceinline__ int pslot(int row, int c) { return row * 4 + (c ^ ((row >> 2) & 3)); }
+
+// Raw bytes of one W slab (256 rows, 32 elements each) in LDS, and the
+// direct loads per wave that fill them (WD):
+//   Q8_0: codes 32 B/row at 32r; the scale dword holding d at 8192 + 4r
+//   Q4K:  codes 16 B/row at 16r; the 16-byte group header at 4096 + 16r
+//   Q6K:  low nibbles 16 B at 16r; the 16 high-bit bytes holding this chunk
+//         at 4096 + 16r; the sub-scale dword at 8192 + 4r; the d dword at
+//         9216 + 4r
+template <int FMT> struct PRaw;
+// (vpm: decode VALU instructions scheduled per MFMA)
+template <> struct PRaw<FMT_Q8_0> { static constexpr int bytes = 9216, wd = 3, vpm = 9; };
+template <> struct PRaw<FMT_Q4K> { static constexpr int bytes = 8192, wd = 2, vpm = 11; };
+template <> struct PRaw<FMT_Q6K> { static constexpr int bytes = 10240, wd = 4, vpm = 12; };
+
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+typedef __attribute__((address_space(1))) void *gbl_ptr_t;
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// Direct global->LDS loads: lane i's bytes land at l + 16*i (dma16) or
+// l + 4*i (dma4); l must be the same for the whole wave.  Issued from inline
+// assembly so that the compiler adds no waits of its own for them: they
+// write no register, and every read of the bytes they bring is preceded by
+// an explicit vmcnt wait and a barrier in the kernel.
+__device__ __forceinline__ void dma16(const void *g, uint8_t *l)
+{
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)l);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void *g, uint8_t *l)
+{
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)l);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_pf_kernel(
+    const uint8_t *__restrict__ B, int64_t sc_off, int64_t d_off, const uint16_t *__restrict__ X,
+    float *__restrict__ Y, int M, int N, int K, int slabs_per_split)
+{
+    constexpr int RAWB = PRaw<FMT>::bytes;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[PNX * PSTAGE + PNW * PSTAGE + PNR * RAWB];
+    uint8_t *const sx = smem;
+    uint8_t *const sw = smem + PNX * PSTAGE;
+    uint8_t *const sr = smem + (PNX + PNW) * PSTAGE;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
+
+    // Consecutive workgroup ids land on different XCDs (round robin over 8);
+    // give each XCD a contiguous run of tiles, which walks the m tiles of
+    // one n tile, so the W rows and X slabs it shares stay in its L2.
+    const int mt = (M + PBM - 1) / PBM, nt = (N + PBN - 1) / PBN, ntiles = mt * nt;
+    const int xcd = blockIdx.x % 8, q = ntiles / 8, rem = ntiles % 8;
+    const int t = xcd * q + min(xcd, rem) + (int)blockIdx.x / 8;
+    const int n_tile = t / mt, m_tile = t % mt;
+    const int m0 = m_tile * PBM, n0 = n_tile * PBN;
+    // this workgroup's slabs [sb, se)
+    const int sb = blockIdx.y * slabs_per_split;
+    const int se = min(K / PBK, sb + slabs_per_split);
+
+    // X: load j of this wave fills slots (4*wave + j)*64 + lane of a stage
+    const uint16_t *xsrc[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const int p = (4 * wave + j) * 64 + lane, row = p >> 2;
+        const int c = (p & 3) ^ ((row >> 2) & 3);
+        xsrc[j] = X + (int64_t)min(m0 + row, M - 1) * K + 8 * c;  // rows past M: results dropped
+    }
+    // W: the row this lane loads for (row 64*wave + lane; Q8_0 codes: two
+    // lanes per row), clamped to N-1 (results dropped)
+    const int64_t nl = min((int64_t)n0 + 64 * wave + lane, (int64_t)N - 1);
+    const int64_t nq = min((int64_t)n0 + 64 * wave + (lane >> 1), (int64_t)N - 1);       // Q8_0 codes, load 0
+    const int64_t nq1 = min((int64_t)n0 + 64 * wave + 32 + (lane >> 1), (int64_t)N - 1); // Q8_0 codes, load 1
+
+    auto issue = [&](int s) {
+        uint8_t *xs = sx + (s % PNX) * PSTAGE;
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            dma16(xsrc[j] + s * PBK, xs + (4 * wave + j) * 1024);
+        uint8_t *rs = sr + (s % PNR) * RAWB;
+        if constexpr (FMT == FMT_Q8_0) {
+            const int half = lane & 1;
+            dma16(B + nq * K + 32 * s + 16 * half, rs + (128 * wave) * 16);
+            dma16(B + nq1 * K + 32 * s + 16 * half, rs + (128 * wave + 64) * 16);
+            dma4(B + sc_off + 2 * nl * (K / 32) + 4 * (s >> 1), rs + 8192 + 256 * wave);
+        } else if constexpr (FMT == FMT_Q4K) {
+            dma16(B + 16 * (nl * (K / 32) + s), rs + 1024 * wave);
+            dma16(B + sc_off + 16 * (nl * (K / 256) + (s >> 3)), rs + 4096 + 1024 * wave);
+        } else {
+            const int64_t grp = nl * (K / 256) + (s >> 3);
+            const int cc = s & 7;
+            dma16(B + 192 * grp + 16 * cc, rs + 1024 * wave);
+            dma16(B + 192 * grp + 128 + 16 * (cc >> 1), rs + 4096 + 1024 * wave);
+            dma4(B + sc_off + 16 * grp + 4 * (cc >> 1), rs + 8192 + 256 * wave);
+            dma4(B + d_off + 4 * (grp >> 1), rs + 9216 + 256 * wave);
+        }
+    };
+    // row tid of slab s: raw bytes -> bf16 W stage, in two parts (the LDS
+    // reads, then the arithmetic and the stores) so the reads can be issued
+    // early
+    const int64_t nd = min((int64_t)n0 + tid, (int64_t)N - 1);
+    auto raw_of = [&](int s) {
+        const uint8_t *rs = sr + (s % PNR) * RAWB;
+        WBlk<FMT> w;
+        if constexpr (FMT == FMT_Q8_0) {
+            w.c0 = *reinterpret_cast<const uint4 *>(rs + 32 * tid);
+            w.c1 = *reinterpret_cast<const uint4 *>(rs + 32 * tid + 16);
+            w.d = *reinterpret_cast<const uint32_t *>(rs + 8192 + 4 * tid);
+        } else if constexpr (FMT == FMT_Q4K) {
+            w.c = *reinterpret_cast<const uint4 *>(rs + 16 * tid);
+            w.h = *reinterpret_cast<const uint4 *>(rs + 4096 + 16 * tid);
+        } else {
+            w.lo = *reinterpret_cast<const uint4 *>(rs + 16 * tid);
+            const uint4 h = *reinterpret_cast<const uint4 *>(rs + 4096 + 16 * tid);
+            w.hi = ((s & 7) & 1) ? make_uint2(h.z, h.w) : make_uint2(h.x, h.y);
+            w.sc2 = *reinterpret_cast<const uint32_t *>(rs + 8192 + 4 * tid);
+            w.d = *reinterpret_cast<const uint32_t *>(rs + 9216 + 4 * tid);
+        }
+        return w;
+    };
+    auto decode = [&](int s, WBlk<FMT> w) {
+        // pick the 16-bit halves out of the dwords the loads brought
+        if constexpr (FMT == FMT_Q8_0) {
+            w.d = (s & 1) ? w.d >> 16 : w.d & 0xffffu;
+        } else if constexpr (FMT == FMT_Q6K) {
+            w.sc2 = ((s & 7) & 1) ? w.sc2 >> 16 : w.sc2 & 0xffffu;
+            const int64_t grp = nd * (K / 256) + (s >> 3);
+            w.d = (grp & 1) ? w.d >> 16 : w.d & 0xffffu;
+        }
+        uint32_t v[16];
+        decode_wblk<FMT>(w, s, v);
+        uint8_t *ws = sw + (s % PNW) * PSTAGE;
+#pragma unroll
+        for (int c = 0; c < 4; c++)
+            *reinterpret_cast<uint4 *>(ws + 16 * pslot(tid, c)) = make_uint4(v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]);
+    };
+
+    const int r32 = lane & 31, kh = lane >> 5;
+    int offa[4][2], offb[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int kk = 0; kk < 2; kk++) {
+            offa[i][kk] = 16 * pslot(128 * wm + 32 * i + r32, 2 * kk + kh);
+            offb[i][kk] = 16 * pslot(128 * wn + 32 * i + r32, 2 * kk + kh);
+        }
+    auto frags = [&](int s, int kk, bf16x8_t (&af)[4], bf16x8_t (&bw)[4]) {
+        const uint8_t *xs = sx + (s % PNX) * PSTAGE, *ws = sw + (s % PNW) * PSTAGE;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            af[i] = *reinterpret_cast<const bf16x8_t *>(xs + offa[i][kk]);
+            bw[i] = *reinterpret_cast<const bf16x8_t *>(ws + offb[i][kk]);
+        }
+    };
+
+    f32x16_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            acc[i][j] = f32x16_t{};
+
+    // prologue: slabs sb..sb+2 landed and the W of slab sb decoded; slab
+    // sb+3 goes out only then, since its raw W takes the stage of slab sb
+    for (int s = sb; s < sb + PNR && s < se; s++)
+        issue(s);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt 0, lgkmcnt 0
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    decode(sb, raw_of(sb));
+    lds_barrier();
+    if (sb + PNR < se)
+        issue(sb + PNR);
+    bf16x8_t a0[4], b0[4], a1[4], b1[4];
+    frags(sb, 0, a0, b0);
+
+    // Slab s.  Steady state (s + 4 < se): the loads of slab s+4 go out
+    // after the barrier.  The barrier needs X of slab s+1 and the raw W of
+    // slab s+2 (decoded in the next slab): both came with the loads issued
+    // two slabs ago, so one slab's loads (4 + WD per wave) may remain.
+    constexpr int VM = 4 + PRaw<FMT>::wd;
+    static_assert(VM < 16, "vmcnt immediate");
+    auto body = [&](int s, auto steady) {
+        constexpr bool ST = decltype(steady)::value;
+        const bool dec = ST || s + 1 < se;
+        // the first MFMA ahead of all reads, so that its operand wait does
+        // not wait for them; then the raw W of the next slab and the second
+        // k-step's fragments
+        acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[0], b0[0], acc[0][0], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        WBlk<FMT> w{};
+        if (dec)
+            w = raw_of(s + 1);
+        frags(s, 1, a1, b1);
+        __builtin_amdgcn_sched_barrier(0);
+        // decode of the next slab's W spread over the remaining 15 MFMAs
+        if (dec)
+            decode(s + 1, w);
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+                if (i + j > 0)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], b0[j], acc[i][j], 0, 0, 0);
+        // three MFMAs cover the raw reads' latency, then the decode rides
+        // along the other twelve
+        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+#pragma unroll
+        for (int k = 0; k < 12; k++) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, PRaw<FMT>::vpm, 0);  // its share of the decode
+        }
+        __builtin_amdgcn_sched_group_barrier(0x200, 4, 0);               // the W stores
+        __builtin_amdgcn_sched_barrier(0);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if constexpr (ST)
+            __builtin_amdgcn_s_waitcnt(0x0070 | VM);  // vmcnt VM, lgkmcnt 0
+        else
+            __builtin_amdgcn_s_waitcnt(0x0070);       // vmcnt 0, lgkmcnt 0
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if constexpr (ST)
+            issue(s + PAHEAD);
+        // in the last slab these reads take a stale stage and are unused
+        frags(s + 1, 0, a0, b0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], b1[j], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    int s = sb;
+    for (; s + PAHEAD < se; s++)
+        body(s, std::true_type{});
+    for (; s < se; s++)
+        body(s, std::false_type{});
+
+    // lane holds D[m = 8*(r/4) + 4*(lane/32) + r%4][n = lane%32] of each tile
+    const bool split = gridDim.y > 1;
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int n = n0 + 128 * wn + 32 * j + r32;
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int m = m0 + 128 * wm + 32 * i + 8 * (r / 4) + 4 * kh + (r % 4);
+                if (m < M && n < N) {
+                    if (split)
+                        atomicAdd(Y + (int64_t)m * N + n, acc[i][j][r]);
+                    else
+                        Y[(int64_t)m * N + n] = acc[i][j][r];
+                }
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------
 // Q8_0 x Q8_0 int8 path
 // ---------------------------------------------------------------------------
 constexpr int BN = 128;     // n tile
@@ -597,6 +888,36 @@ hipError_t go_skinny(const uint8_t *blocks, const Planes &p, const uint16_t *X, 
     return hipGetLastError();
 }
 
+// split K while the tiles fill less than one round of the 256 CUs, keeping
+// at least 16 slabs per split
+int pf_splits(int64_t tiles, int nslab)
+{
+    int sp = 1;
+    while (sp < 8 && tiles * sp * 2 <= 256 && nslab / (sp * 2) >= 16)
+        sp *= 2;
+    return sp;
+}
+
+template <int FMT>
+hipError_t go_pf(const uint8_t *blocks, const Planes &p, const uint16_t *X, float *Y, int64_t M, int64_t N,
+                 int64_t K, hipStream_t s)
+{
+    const int64_t tiles = ((M + PBM - 1) / PBM) * ((N + PBN - 1) / PBN);
+    if (tiles > (int64_t)1 << 30)
+        return hipErrorInvalidValue;
+    const int nslab = (int)(K / PBK);
+    const int sp = pf_splits(tiles, nslab);
+    const int per = (nslab + sp - 1) / sp;
+    if (sp > 1) {
+        const hipError_t e = zero_y(Y, M * N, s);
+        if (e != hipSuccess)
+            return e;
+    }
+    hipLaunchKernelGGL((gemm_pf_kernel<FMT>), dim3((unsigned)tiles, (unsigned)sp), dim3(256), 0, s, blocks, p.scales,
+                       p.d, X, Y, (int)M, (int)N, (int)K, per);
+    return hipGetLastError();
+}
+
 template <int FMT>
 hipError_t bf16_by_m(const uint8_t *blocks, const Planes &p, const uint16_t *X, float *Y, int64_t M,
                      int64_t N, int64_t K, hipStream_t s)
@@ -610,6 +931,8 @@ hipError_t bf16_by_m(const uint8_t *blocks, const Planes &p, const uint16_t *X, 
         return go_skinny<FMT, 2, 1, 4>(blocks, p, X, Y, M, N, K, s);
     if (M <= 64)
         return go_bf16<FMT, 4, 4>(blocks, p, X, Y, M, N, K, s);
+    if (M >= PF_MIN_M)
+        return go_pf<FMT>(blocks, p, X, Y, M, N, K, s);
     return go_bf16<FMT, 8, 4>(blocks, p, X, Y, M, N, K, s);
 }
 

@@ -159,9 +159,13 @@ __global__ __launch_bounds__(256) void isq_q4k_kernel(const uint4 *__restrict__ 
 __global__ __launch_bounds__(256) void isq_q6k_kernel(const uint4 *__restrict__ W, int64_t tasks,
                                                       uint8_t *__restrict__ C,
                                                       int8_t *__restrict__ SC,
-                                                      uint16_t *__restrict__ D)
+                                                      uint16_t *__restrict__ D, uint8_t *__restrict__ pad,
+                                                      int npad)
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    // the tail padding of the buffer (to a multiple of 16 bytes) is zero
+    if (blockIdx.x == 0 && (int)threadIdx.x < npad)
+        pad[threadIdx.x] = 0;
     for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < tasks; t += stride) {
         float x[8];
         load8(W[t], x);
@@ -296,7 +300,8 @@ hipError_t launch_isq(int fmt, const uint16_t *W, int64_t N, int64_t K, uint8_t 
     else
         hipLaunchKernelGGL(isq_q6k_kernel, dim3(grid_for(tasks)), dim3(256), 0, s, w, tasks, out,
                            reinterpret_cast<int8_t *>(out + p.scales),
-                           reinterpret_cast<uint16_t *>(out + p.d));
+                           reinterpret_cast<uint16_t *>(out + p.d), out + 210 * (N * K / 256),
+                           (int)(p.total - 210 * (N * K / 256)));
     return hipGetLastError();
 }
 

@@ -31,10 +31,12 @@ inline Planes planes_of(int fmt, int64_t N, int64_t K)
         p.scales = 128 * G;
         p.total = 144 * G;
     } else {
+        // the buffer is padded to a multiple of 16 bytes, so that every
+        // aligned dword holding a d value lies inside it
         const int64_t G = E / 256;
         p.scales = 192 * G;
         p.d = 208 * G;
-        p.total = 210 * G;
+        p.total = (210 * G + 15) & ~(int64_t)15;
     }
     return p;
 }

@@ -96,8 +96,9 @@ enum {
 #define QLINEAR_MAX_K (1 << 20)
 
 /* Bytes of the block buffer of a [N][K] tensor in `fmt`: 34*N*K/32 (Q8_0),
- * 144*N*K/256 (Q4K), 210*N*K/256 (Q6K).  Returns 0 for an unsupported format
- * or an invalid shape.  The buffer is made of planes, each 16-byte aligned
+ * 144*N*K/256 (Q4K), 210*N*K/256 rounded up to a multiple of 16 (Q6K; the
+ * padding bytes are zero after isq_quantize).  Returns 0 for an unsupported
+ * format or an invalid shape.  The buffer is made of planes, each 16-byte aligned
  * (G = N*K/256 groups, group g = row n, columns 256*kb .. 256*kb+255 with
  * g = n*K/256 + kb):
  *   Q8_0: [codes int8 N*K, row-major][d fp16 N*K/32, row-major]

@@ -171,9 +171,12 @@ def quantize(fmt: str, w_bf16: np.ndarray) -> dict:
 
 
 def blocks_bytes(fmt: str, rows: int, cols: int) -> int:
-    """Bytes of the planar buffer: 34/32, 144/256, 210/256 bytes per element."""
+    """Bytes of the planar buffer: 34/32, 144/256, 210/256 bytes per element;
+    the Q6K buffer is zero-padded to a multiple of 16 bytes."""
     n = rows * cols
-    return {"q8_0": n * 34 // 32, "q4k": n * 144 // 256, "q6k": n * 210 // 256}[fmt]
+    if fmt == "q6k":
+        return (n * 210 // 256 + 15) // 16 * 16
+    return {"q8_0": n * 34 // 32, "q4k": n * 144 // 256}[fmt]
 
 
 def pack(fmt: str, f: dict, rows: int, cols: int) -> np.ndarray:

@@ -460,7 +460,9 @@ void oracle_matmul_a8(const uint16_t *dw16, const int8_t *qw, const uint16_t *dx
  *       stored code u = q + 32 in [0, 63].
  *       C: group g owns bytes 192g..192g+191 (layout at q6k_pack_group).
  *       S: 16 int8 sub-scales sc_j per group.  D: fp16 d per group (the
- *          plane starts at byte 208*G, a multiple of 16).
+ *          plane starts at byte 208*G, a multiple of 16).  The buffer is
+ *          zero-padded to a multiple of 16 bytes (the caller allocates it;
+ *          these routines touch only the 210*G bytes of the planes).
  */
 
 /* Q8_0 pack/unpack: the planes are the fields themselves. */

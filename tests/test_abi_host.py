@@ -39,7 +39,8 @@ def test_blocks_bytes():
     # bits per weight: 8.5, 4.5, 6.5625 (nominal 8, 4, 6 on the page's tables)
     assert ql.blocks_bytes("q8_0", 1, 256) * 8 / 256 == 8.5
     assert ql.blocks_bytes("q4k", 1, 256) * 8 / 256 == 4.5
-    assert ql.blocks_bytes("q6k", 1, 256) * 8 / 256 == 6.5625
+    assert ql.blocks_bytes("q6k", 8, 256) * 8 / 2048 == 6.5625
+    assert ql.blocks_bytes("q6k", 1, 256) == 224          # 210, zero-padded to 16
 
 
 def test_workspace_bytes():

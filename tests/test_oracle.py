@@ -358,6 +358,8 @@ def test_layout_bytes_by_hand():
     assert hi_h0 & 3 == 3 and (hi_h0 >> 16) & 3 == 0
     assert (hi_h1 >> 16) & 3 == 3
     assert bytes(b[192:208]) == bytes(range(16)) and bytes(b[208:210]) == bytes([0x00, 0x3C])
+    # one group: 210 bytes of planes, zero-padded to 224
+    assert b.size == 224 and not b[210:].any()
     # Q8_0: codes then scales
     fq8 = {"d16": np.array([[0x1234]], np.uint16), "q": np.arange(-16, 16, dtype=np.int8)[None, :]}
     b = oracle.pack("q8_0", fq8, 1, 32)

@@ -141,6 +141,17 @@ def test_mfma_bf16_shapes(fmt):
             check_outputs(run(fmt, "mfma_bf16", w, x), Yr, den, f"mfma_bf16 {fmt} M={M} N={N} K={K}")
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+def test_mfma_bf16_prefill_tiles(fmt):
+    """Large-M path (256 x 256 tiles, split over K when the tiles are few):
+    ragged M and N around the tile edges, K with one, two and eight splits."""
+    for M, N, K in ((128, 255, 256), (257, 513, 1024), (600, 300, 4096), (300, 1, 768), (129, 1000, 4096)):
+        w = synth.weights_bf16(5100 + N + K, N, K, outliers=True)
+        x = synth.activations_bf16(5101 + M, M, K)
+        Yr, den = a16_ref(fmt, w, x)
+        check_outputs(run(fmt, "mfma_bf16", w, x), Yr, den, f"prefill tiles {fmt} M={M} N={N} K={K}")
+
+
 def test_mfma_i8_shapes_and_activation_blocks():
     for M in (1, 9, 16, 64, 130, 256):
         for N, K in ((7, 256), (64, 1024), (300, 4096), (129, 512)):
