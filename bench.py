@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--quick", action="store_true", help="headline only (for profiling runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--parts", default=None,
+                    help="comma-separated parts measured after the headline: batched, prefill, isq "
+                         "(default: all of them, none with --quick)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only copy a buffer of BYTES bytes 10 times (the reference kernel that scales "
                          "the FETCH_SIZE / WRITE_SIZE counters), then exit")
@@ -235,7 +238,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(q4["alg_GBps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(q4["alg_GBps"] / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(),
                      "traffic_unit": "HBM bytes per launch (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0)",
-                     "kernel": "gemv_kernel<Q4K, M=1>", "alg_bytes_per_launch": q4["alg_bytes"]},
+                     "kernel": "gemv_lds_kernel<Q4K, M=1, CPT=2, R=2>", "alg_bytes_per_launch": q4["alg_bytes"]},
     })
     parts["gemv_q8_0_14336x4096_m1"] = {
         "us": round(head["q8_0"]["ms"] * 1e3, 3), "weight_GBps": round(head["q8_0"]["weight_GBps"], 1),
@@ -245,8 +248,9 @@ def main():
         "hbm_frac": round(q4["alg_GBps"] / HBM_PEAK_GBPS, 4), "parity_max_err": q4["parity_max_err"]}
     del W
 
-    if not args.quick:
-        parts.update(bench_parts(torch, ql, synth, dev, bf16_dev))
+    which = set(args.parts.split(",")) if args.parts else (set() if args.quick else {"batched", "prefill", "isq"})
+    if which:
+        parts.update(bench_parts(torch, ql, synth, dev, bf16_dev, which))
     result["parts"] = parts
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, x)
@@ -274,7 +278,7 @@ def check_gemv_parity(ql, fmt, w, x, blocks, Y, N):
     return float(e)
 
 
-def bench_parts(torch, ql, synth, dev, bf16_dev):
+def bench_parts(torch, ql, synth, dev, bf16_dev, which):
     parts = {}
 
     def timed_calls(launch, n_calls, reps=3):
@@ -283,130 +287,133 @@ def bench_parts(torch, ql, synth, dev, bf16_dev):
         g = graph_of(torch, launch, n_calls)
         return time_graph(torch, g, reps, n_calls)
 
-    # batched decode: K=14336, N=4096, Q4K with outliers, M = 4, 16, 64
-    log("batched decode 4096x14336 q4k")
-    N, K = 4096, 14336
-    w = synth.weights_bf16(synth.seed_for(3, 0), N, K, outliers=True)
-    xs = synth.activations_bf16(synth.seed_for(3, 1), 64, K)
-    blocks = ql.isq("q4k", bf16_dev(w))
-    R = copies_for(blocks.numel())
-    copies = [blocks] + [blocks.clone() for _ in range(R - 1)]
-    for M in (4, 16, 64):
-        X = bf16_dev(xs[:M])
+    if "batched" in which:
+        # batched decode: K=14336, N=4096, Q4K with outliers, M = 4, 16, 64
+        log("batched decode 4096x14336 q4k")
+        N, K = 4096, 14336
+        w = synth.weights_bf16(synth.seed_for(3, 0), N, K, outliers=True)
+        xs = synth.activations_bf16(synth.seed_for(3, 1), 64, K)
+        blocks = ql.isq("q4k", bf16_dev(w))
+        R = copies_for(blocks.numel())
+        copies = [blocks] + [blocks.clone() for _ in range(R - 1)]
+        for M in (4, 16, 64):
+            X = bf16_dev(xs[:M])
+            Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+            ms = timed_calls(lambda i: ql.qmatmul("q4k", copies[i % R], X, N, out=Y), 4 * R)
+            fl = 2.0 * M * N * K
+            parts[f"batched_q4k_m{M}"] = {
+                "us": round(ms * 1e3, 3), "path": "gemv" if M <= 2 else "mfma_bf16",
+                "weight_GBps": round(blocks.numel() / ms / 1e6, 1),
+                "hbm_frac": round((blocks.numel() + M * K * 2 + M * N * 4) / ms / 1e6 / HBM_PEAK_GBPS, 4),
+                "TFLOPs": round(fl / ms / 1e9, 2)}
+            log(f"  M={M}: {ms * 1e3:.2f} us")
+        # GEMV / MFMA crossover at this shape (sets the AUTO dispatch)
+        cross = {}
+        for M in range(1, 9):
+            X = bf16_dev(xs[:M])
+            Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+            row = {}
+            for path in ("gemv", "mfma_bf16"):
+                ms = timed_calls(lambda i: ql.qmatmul("q4k", copies[i % R], X, N, out=Y, path=path), 2 * R)
+                row[path] = round(ms * 1e3, 2)
+            cross[str(M)] = row
+        parts["crossover_q4k_4096x14336_us"] = cross
+        log(f"  crossover: {cross}")
+        del copies, blocks
+        torch.cuda.empty_cache()
+
+    if "prefill" in which:
+        # prefill: M=2048, K=4096, N=14336, Q8_0; bf16 MFMA path and int8 path
+        log("prefill 2048x4096x14336 q8_0")
+        M, N, K = 2048, 14336, 4096
+        w = synth.weights_bf16(synth.seed_for(4, 0), N, K)
+        X = bf16_dev(synth.activations_bf16(synth.seed_for(4, 1), M, K))
+        blocks = ql.isq("q8_0", bf16_dev(w))
+        copies = [blocks, blocks.clone()]
         Y = torch.empty((M, N), dtype=torch.float32, device=dev)
-        ms = timed_calls(lambda i: ql.qmatmul("q4k", copies[i % R], X, N, out=Y), 4 * R)
+        ws = torch.empty(ql.workspace_bytes("q8_0", "mfma_i8", M, K), dtype=torch.uint8, device=dev)
         fl = 2.0 * M * N * K
-        parts[f"batched_q4k_m{M}"] = {
-            "us": round(ms * 1e3, 3), "path": "gemv" if M <= 2 else "mfma_bf16",
-            "weight_GBps": round(blocks.numel() / ms / 1e6, 1),
-            "hbm_frac": round((blocks.numel() + M * K * 2 + M * N * 4) / ms / 1e6 / HBM_PEAK_GBPS, 4),
-            "TFLOPs": round(fl / ms / 1e9, 2)}
-        log(f"  M={M}: {ms * 1e3:.2f} us")
-    # GEMV / MFMA crossover at this shape (sets the AUTO dispatch)
-    cross = {}
-    for M in range(1, 9):
-        X = bf16_dev(xs[:M])
-        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
-        row = {}
-        for path in ("gemv", "mfma_bf16"):
-            ms = timed_calls(lambda i: ql.qmatmul("q4k", copies[i % R], X, N, out=Y, path=path), 2 * R)
-            row[path] = round(ms * 1e3, 2)
-        cross[str(M)] = row
-    parts["crossover_q4k_4096x14336_us"] = cross
-    log(f"  crossover: {cross}")
-    del copies, blocks
-    torch.cuda.empty_cache()
+        ms = timed_calls(lambda i: ql.qmatmul("q8_0", copies[i % 2], X, N, out=Y, path="mfma_bf16"), 10)
+        parts["prefill_q8_0_bf16_mfma"] = {"us": round(ms * 1e3, 2), "TFLOPs": round(fl / ms / 1e9, 1),
+                                           "mfma_frac": round(fl / ms / 1e9 / BF16_PEAK_TFLOPS, 4)}
+        log(f"  bf16 path: {ms * 1e3:.1f} us {fl / ms / 1e9:.0f} TFLOP/s")
+        ms = timed_calls(lambda i: ql.qmatmul("q8_0", copies[i % 2], X, N, out=Y, path="mfma_i8", workspace=ws), 10)
+        parts["prefill_q8_0_int8_mfma"] = {"us": round(ms * 1e3, 2), "TOPs": round(fl / ms / 1e9, 1),
+                                           "mfma_frac": round(fl / ms / 1e9 / INT8_PEAK_TOPS, 4),
+                                           "includes": "activation quantization"}
+        log(f"  int8 path: {ms * 1e3:.1f} us {fl / ms / 1e9:.0f} TOP/s")
+        del copies, blocks, ws, Y, X
+        torch.cuda.empty_cache()
 
-    # prefill: M=2048, K=4096, N=14336, Q8_0; bf16 MFMA path and int8 path
-    log("prefill 2048x4096x14336 q8_0")
-    M, N, K = 2048, 14336, 4096
-    w = synth.weights_bf16(synth.seed_for(4, 0), N, K)
-    X = bf16_dev(synth.activations_bf16(synth.seed_for(4, 1), M, K))
-    blocks = ql.isq("q8_0", bf16_dev(w))
-    copies = [blocks, blocks.clone()]
-    Y = torch.empty((M, N), dtype=torch.float32, device=dev)
-    ws = torch.empty(ql.workspace_bytes("q8_0", "mfma_i8", M, K), dtype=torch.uint8, device=dev)
-    fl = 2.0 * M * N * K
-    ms = timed_calls(lambda i: ql.qmatmul("q8_0", copies[i % 2], X, N, out=Y, path="mfma_bf16"), 10)
-    parts["prefill_q8_0_bf16_mfma"] = {"us": round(ms * 1e3, 2), "TFLOPs": round(fl / ms / 1e9, 1),
-                                       "mfma_frac": round(fl / ms / 1e9 / BF16_PEAK_TFLOPS, 4)}
-    log(f"  bf16 path: {ms * 1e3:.1f} us {fl / ms / 1e9:.0f} TFLOP/s")
-    ms = timed_calls(lambda i: ql.qmatmul("q8_0", copies[i % 2], X, N, out=Y, path="mfma_i8", workspace=ws), 10)
-    parts["prefill_q8_0_int8_mfma"] = {"us": round(ms * 1e3, 2), "TOPs": round(fl / ms / 1e9, 1),
-                                       "mfma_frac": round(fl / ms / 1e9 / INT8_PEAK_TOPS, 4),
-                                       "includes": "activation quantization"}
-    log(f"  int8 path: {ms * 1e3:.1f} us {fl / ms / 1e9:.0f} TOP/s")
-    del copies, blocks, ws, Y, X
-    torch.cuda.empty_cache()
-
-    # ISQ of the 32-layer decoder (Q4K) and the output head (Q6K)
-    log("decoder ISQ: 32 layers x 7 projections to q4k + 131072x5120 head to q6k")
-    shapes = [(4096, 4096), (1024, 4096), (1024, 4096), (4096, 4096), (14336, 4096), (14336, 4096),
-              (4096, 14336)]
-    Wl, Bl = [], []
-    read = write = 0
-    for layer in range(32):
-        for kind, (n, k) in enumerate(shapes):
-            Wt = synth.device_normal_bf16(synth.decoder_seed(layer, kind), (n, k), synth.W_SIGMA)
-            Wl.append(Wt)
-            Bl.append(torch.empty(ql.blocks_bytes("q4k", n, k), dtype=torch.uint8, device=dev))
-    Wh = synth.device_normal_bf16(synth.LM_HEAD_W_SEED, (131072, 5120), synth.W_SIGMA)
-    Bh = torch.empty(ql.blocks_bytes("q6k", 131072, 5120), dtype=torch.uint8, device=dev)
-    for Wt, Bt in zip(Wl, Bl):
-        read += Wt.numel() * 2
-        write += Bt.numel()
-    read += Wh.numel() * 2
-    write += Bh.numel()
-
-    def isq_all():
+    if "isq" in which:
+        # ISQ of the 32-layer decoder (Q4K) and the output head (Q6K)
+        log("decoder ISQ: 32 layers x 7 projections to q4k + 131072x5120 head to q6k")
+        shapes = [(4096, 4096), (1024, 4096), (1024, 4096), (4096, 4096), (14336, 4096), (14336, 4096),
+                  (4096, 14336)]
+        Wl, Bl = [], []
+        read = write = 0
+        for layer in range(32):
+            for kind, (n, k) in enumerate(shapes):
+                Wt = synth.device_normal_bf16(synth.decoder_seed(layer, kind), (n, k), synth.W_SIGMA)
+                Wl.append(Wt)
+                Bl.append(torch.empty(ql.blocks_bytes("q4k", n, k), dtype=torch.uint8, device=dev))
+        Wh = synth.device_normal_bf16(synth.LM_HEAD_W_SEED, (131072, 5120), synth.W_SIGMA)
+        Bh = torch.empty(ql.blocks_bytes("q6k", 131072, 5120), dtype=torch.uint8, device=dev)
         for Wt, Bt in zip(Wl, Bl):
-            ql.isq("q4k", Wt, out=Bt)
-        ql.isq("q6k", Wh, out=Bh)
+            read += Wt.numel() * 2
+            write += Bt.numel()
+        read += Wh.numel() * 2
+        write += Bh.numel()
 
-    isq_all()
-    torch.cuda.synchronize()
-    with Timer(torch) as t:
+        def isq_all():
+            for Wt, Bt in zip(Wl, Bl):
+                ql.isq("q4k", Wt, out=Bt)
+            ql.isq("q6k", Wh, out=Bh)
+
         isq_all()
-    parts["isq_decoder_32l_q4k_plus_head_q6k"] = {
-        "ms": round(t.ms, 3), "read_bytes": read, "write_bytes": write,
-        "GBps": round((read + write) / t.ms / 1e6, 1),
-        "hbm_frac": round((read + write) / t.ms / 1e6 / HBM_PEAK_GBPS, 4)}
-    log(f"  ISQ all: {t.ms:.2f} ms ({(read + write) / t.ms / 1e6:.0f} GB/s)")
-    del Wl, Wh
-    torch.cuda.empty_cache()
+        torch.cuda.synchronize()
+        with Timer(torch) as t:
+            isq_all()
+        parts["isq_decoder_32l_q4k_plus_head_q6k"] = {
+            "ms": round(t.ms, 3), "read_bytes": read, "write_bytes": write,
+            "GBps": round((read + write) / t.ms / 1e6, 1),
+            "hbm_frac": round((read + write) / t.ms / 1e6 / HBM_PEAK_GBPS, 4)}
+        log(f"  ISQ all: {t.ms:.2f} ms ({(read + write) / t.ms / 1e6:.0f} GB/s)")
+        del Wl, Wh
+        torch.cuda.empty_cache()
 
-    # output head GEMV, M = 1 and M = 8 (Q6K)
-    xh = synth.activations_bf16(synth.LM_HEAD_X_SEED, 8, 5120)
-    Bh2 = [Bh, Bh.clone()]
-    for M in (1, 8):
-        X = bf16_dev(xh[:M])
-        Y = torch.empty((M, 131072), dtype=torch.float32, device=dev)
-        ms = timed_calls(lambda i: ql.qmatmul("q6k", Bh2[i % 2], X, 131072, out=Y), 8)
-        parts[f"lm_head_q6k_m{M}"] = {"us": round(ms * 1e3, 2), "weight_GBps": round(Bh.numel() / ms / 1e6, 1),
-                                      "hbm_frac": round((Bh.numel() + M * 5120 * 2 + M * 131072 * 4) / ms / 1e6 / HBM_PEAK_GBPS, 4)}
-        log(f"  lm_head M={M}: {ms * 1e3:.1f} us")
-    del Bh2
+        # output head GEMV, M = 1 and M = 8 (Q6K)
+        xh = synth.activations_bf16(synth.LM_HEAD_X_SEED, 8, 5120)
+        Bh2 = [Bh, Bh.clone()]
+        for M in (1, 8):
+            X = bf16_dev(xh[:M])
+            Y = torch.empty((M, 131072), dtype=torch.float32, device=dev)
+            ms = timed_calls(lambda i: ql.qmatmul("q6k", Bh2[i % 2], X, 131072, out=Y), 8)
+            parts[f"lm_head_q6k_m{M}"] = {"us": round(ms * 1e3, 2), "weight_GBps": round(Bh.numel() / ms / 1e6, 1),
+                                          "hbm_frac": round((Bh.numel() + M * 5120 * 2 + M * 131072 * 4) / ms / 1e6 / HBM_PEAK_GBPS, 4)}
+            log(f"  lm_head M={M}: {ms * 1e3:.1f} us")
+        del Bh2
 
-    # equivalent decode tokens/s: every projection GEMV of the 32 layers + head
-    x1 = bf16_dev(synth.activations_bf16(9001, 1, 14336))
-    Ys = [torch.empty((1, n), dtype=torch.float32, device=dev) for (n, k) in shapes]
-    Yh = torch.empty((1, 131072), dtype=torch.float32, device=dev)
+        # equivalent decode tokens/s: every projection GEMV of the 32 layers + head
+        x1 = bf16_dev(synth.activations_bf16(9001, 1, 14336))
+        Ys = [torch.empty((1, n), dtype=torch.float32, device=dev) for (n, k) in shapes]
+        Yh = torch.empty((1, 131072), dtype=torch.float32, device=dev)
 
-    def token(_i):
-        for j, Bt in enumerate(Bl):
-            n, k = shapes[j % 7]
-            ql.qmatmul("q4k", Bt, x1[:, :k], n, out=Ys[j % 7])
-        ql.qmatmul("q6k", Bh, x1[:, :5120], 131072, out=Yh)
+        def token(_i):
+            for j, Bt in enumerate(Bl):
+                n, k = shapes[j % 7]
+                ql.qmatmul("q4k", Bt, x1[:, :k], n, out=Ys[j % 7])
+            ql.qmatmul("q6k", Bh, x1[:, :5120], 131072, out=Yh)
 
-    token(0)
-    g = graph_of(torch, token, 1)
-    ms = time_graph(torch, g, 10, 1)
-    total = sum(b.numel() for b in Bl) + Bh.numel()
-    parts["equiv_decode_tok_s"] = {"tok_s": round(1000.0 / ms, 1), "ms_per_token": round(ms, 4),
-                                   "weight_bytes_per_token": total,
-                                   "weight_GBps": round(total / ms / 1e6, 1),
-                                   "note": "225 quantized GEMVs per token (M=1); attention, norms, sampling excluded"}
-    log(f"  decode token: {ms:.3f} ms -> {1000 / ms:.0f} tok/s")
+        token(0)
+        g = graph_of(torch, token, 1)
+        ms = time_graph(torch, g, 10, 1)
+        total = sum(b.numel() for b in Bl) + Bh.numel()
+        parts["equiv_decode_tok_s"] = {"tok_s": round(1000.0 / ms, 1), "ms_per_token": round(ms, 4),
+                                       "weight_bytes_per_token": total,
+                                       "weight_GBps": round(total / ms / 1e6, 1),
+                                       "note": "225 quantized GEMVs per token (M=1); attention, norms, sampling excluded"}
+        log(f"  decode token: {ms:.3f} ms -> {1000 / ms:.0f} tok/s")
     return parts
 
 

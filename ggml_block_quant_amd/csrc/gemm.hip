@@ -460,21 +460,24 @@ typedef __attribute__((address_space(3))) void *lds_ptr_t;
 typedef __attribute__((address_space(1))) void *gbl_ptr_t;
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-// Direct global->LDS loads: lane i's bytes land at l + 16*i (dma16) or
-// l + 4*i (dma4); l must be the same for the whole wave.  Issued from inline
-// assembly so that the compiler adds no waits of its own for them: they
-// write no register, and every read of the bytes they bring is preceded by
-// an explicit vmcnt wait and a barrier in the kernel.
-__device__ __forceinline__ void dma16(const void *g, uint8_t *l)
+// Direct global->LDS loads in the scalar-base form: lane i reads base + off_i
+// (base the same for the whole wave, off_i a 32-bit byte offset) and its
+// bytes land at LDS address lds + 16*i (dma16) or lds + 4*i (dma4); lds is
+// the same for the whole wave.  Per-slab address updates are then scalar
+// adds.  Issued from inline assembly so that the compiler adds no waits of
+// its own for them: they write no register, and every read of the bytes
+// they bring is preceded by an explicit vmcnt wait and a barrier.
+__device__ __forceinline__ void dma16(const uint8_t *base, uint32_t off, uint32_t lds)
 {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)l);
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
+                 : "memory", "m0");
 }
-__device__ __forceinline__ void dma4(const void *g, uint8_t *l)
+__device__ __forceinline__ void dma4(const uint8_t *base, uint32_t off, uint32_t lds)
 {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)l);
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "s"(lds)
+                 : "memory", "m0");
 }
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t *p) { return (uint32_t)(uintptr_t)(lds_ptr_t)p; }
 
 template <int FMT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_pf_kernel(
@@ -501,41 +504,50 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int sb = blockIdx.y * slabs_per_split;
     const int se = min(K / PBK, sb + slabs_per_split);
 
-    // X: load j of this wave fills slots (4*wave + j)*64 + lane of a stage
-    const uint16_t *xsrc[4];
+    // X: load j of this wave fills slots (4*wave + j)*64 + lane of a stage;
+    // byte offsets from row m0 (rows past M re-read row M-1, results dropped)
+    const int wv = __builtin_amdgcn_readfirstlane(wave);  // known uniform
+    uint32_t ox[4];
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-        const int p = (4 * wave + j) * 64 + lane, row = p >> 2;
+        const int p = (4 * wv + j) * 64 + lane, row = p >> 2;
         const int c = (p & 3) ^ ((row >> 2) & 3);
-        xsrc[j] = X + (int64_t)min(m0 + row, M - 1) * K + 8 * c;  // rows past M: results dropped
+        ox[j] = (uint32_t)(((int64_t)(min(m0 + row, M - 1) - m0) * K + 8 * c) * 2);
     }
+    const uint8_t *const xbase = reinterpret_cast<const uint8_t *>(X + (int64_t)m0 * K);
     // W: the row this lane loads for (row 64*wave + lane; Q8_0 codes: two
-    // lanes per row), clamped to N-1 (results dropped)
-    const int64_t nl = min((int64_t)n0 + 64 * wave + lane, (int64_t)N - 1);
-    const int64_t nq = min((int64_t)n0 + 64 * wave + (lane >> 1), (int64_t)N - 1);       // Q8_0 codes, load 0
-    const int64_t nq1 = min((int64_t)n0 + 64 * wave + 32 + (lane >> 1), (int64_t)N - 1); // Q8_0 codes, load 1
+    // lanes per row), clamped to N-1 (results dropped), relative to row n0
+    const int rl = (int)(min((int64_t)n0 + 64 * wv + lane, (int64_t)N - 1) - n0);
+    const int rq = (int)(min((int64_t)n0 + 64 * wv + (lane >> 1), (int64_t)N - 1) - n0);
+    const int rq1 = (int)(min((int64_t)n0 + 64 * wv + 32 + (lane >> 1), (int64_t)N - 1) - n0);
+    const int64_t g0 = (int64_t)n0 * (K / 256);  // first group of row n0 (K-quants)
 
     auto issue = [&](int s) {
-        uint8_t *xs = sx + (s % PNX) * PSTAGE;
+        const uint32_t xs = lds_addr(sx + (s % PNX) * PSTAGE) + 4096 * wv;
 #pragma unroll
         for (int j = 0; j < 4; j++)
-            dma16(xsrc[j] + s * PBK, xs + (4 * wave + j) * 1024);
-        uint8_t *rs = sr + (s % PNR) * RAWB;
+            dma16(xbase + 2 * PBK * s, ox[j], xs + 1024 * j);
+        const uint32_t rs = lds_addr(sr + (s % PNR) * RAWB);
         if constexpr (FMT == FMT_Q8_0) {
-            const int half = lane & 1;
-            dma16(B + nq * K + 32 * s + 16 * half, rs + (128 * wave) * 16);
-            dma16(B + nq1 * K + 32 * s + 16 * half, rs + (128 * wave + 64) * 16);
-            dma4(B + sc_off + 2 * nl * (K / 32) + 4 * (s >> 1), rs + 8192 + 256 * wave);
+            const uint32_t half = lane & 1;
+            const uint8_t *cb = B + (int64_t)n0 * K + 32 * s;
+            dma16(cb, (uint32_t)rq * K + 16 * half, rs + 2048 * wv);
+            dma16(cb, (uint32_t)rq1 * K + 16 * half, rs + 2048 * wv + 1024);
+            dma4(B + sc_off + 2 * (int64_t)n0 * (K / 32) + 4 * (s >> 1), (uint32_t)rl * (K / 16), rs + 8192 + 256 * wv);
         } else if constexpr (FMT == FMT_Q4K) {
-            dma16(B + 16 * (nl * (K / 32) + s), rs + 1024 * wave);
-            dma16(B + sc_off + 16 * (nl * (K / 256) + (s >> 3)), rs + 4096 + 1024 * wave);
+            dma16(B + 16 * ((int64_t)n0 * (K / 32) + s), (uint32_t)rl * (K / 2), rs + 1024 * wv);
+            dma16(B + sc_off + 16 * (g0 + (s >> 3)), (uint32_t)rl * (K / 16), rs + 4096 + 1024 * wv);
         } else {
-            const int64_t grp = nl * (K / 256) + (s >> 3);
             const int cc = s & 7;
-            dma16(B + 192 * grp + 16 * cc, rs + 1024 * wave);
-            dma16(B + 192 * grp + 128 + 16 * (cc >> 1), rs + 4096 + 1024 * wave);
-            dma4(B + sc_off + 16 * grp + 4 * (cc >> 1), rs + 8192 + 256 * wave);
-            dma4(B + d_off + 4 * (grp >> 1), rs + 9216 + 256 * wave);
+            const uint8_t *gb = B + 192 * (g0 + (s >> 3));
+            const uint32_t og = (uint32_t)rl * (K / 256) * 192;
+            dma16(gb + 16 * cc, og, rs + 1024 * wv);
+            dma16(gb + 128 + 16 * (cc >> 1), og, rs + 4096 + 1024 * wv);
+            dma4(B + sc_off + 16 * (g0 + (s >> 3)) + 4 * (cc >> 1), (uint32_t)rl * (K / 16), rs + 8192 + 256 * wv);
+            // the d dword holding group grp: 4*(grp >> 1) from the d plane,
+            // counted from the dword holding group g0
+            const int64_t grp = g0 + (int64_t)rl * (K / 256) + (s >> 3);
+            dma4(B + d_off + 4 * (g0 >> 1), (uint32_t)(4 * ((grp >> 1) - (g0 >> 1))), rs + 9216 + 256 * wv);
         }
     };
     // row tid of slab s: raw bytes -> bf16 W stage, in two parts (the LDS
