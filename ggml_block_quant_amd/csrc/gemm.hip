@@ -714,6 +714,199 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 // ---------------------------------------------------------------------------
+// Batched-decode path (a few to 32 tokens): a weight stream.  A workgroup of
+// four waves owns 64 rows of W and one split of K; wave w owns rows
+// 16w..16w+15 and all 16*TM rows of X, so no weight is decoded twice.  K
+// advances in slabs of 128 (four blocks of 32 per row).
+//
+//   * X and the raw block bytes of the 64 rows reach LDS by direct
+//     global->LDS loads into a ring of four stages, three slabs ahead; the
+//     only waits on them are the explicit vmcnt waits.
+//   * Lane (g = lane/16, r = lane%16) decodes block g of the slab in row
+//     16w + r straight into the four B fragments of the slab's four
+//     v_mfma_f32_16x16x32_bf16 steps; step t pairs elements 8t..8t+7 of that
+//     block with X[m][32g + 8t + e] -- the k order inside the slab is
+//     permuted identically on both operands.
+//   * X stage: row m holds the slab's 16 chunks of 8 elements, chunk c at
+//     position c ^ (m & 15), so the 16 rows a ds_read_b128 phase touches
+//     land on distinct banks.
+//   * K splits add their partial tiles into Y (zeroed first) with fp32
+//     atomics.
+// ---------------------------------------------------------------------------
+constexpr int TBN = 64, TBK = 128, TNS = 4;
+
+// raw bytes of one slab of 64 rows in LDS, and the direct loads per wave (WD):
+//   Q8_0: codes [64][128] at 0; scales [64][8] at 8192
+//   Q4K:  codes [64][64] at 0; group headers [64][16] at 4096
+//   Q6K:  low nibbles [64][64] at 0; high bits [64][32] at 4096; sub-scales
+//         [64][8] at 6144; the dword holding d, [64][4] at 6656
+template <int FMT> struct TRaw;
+template <> struct TRaw<FMT_Q8_0> { static constexpr int bytes = 8704, wd = 3; };
+template <> struct TRaw<FMT_Q4K> { static constexpr int bytes = 5120, wd = 2; };
+template <> struct TRaw<FMT_Q6K> { static constexpr int bytes = 6912, wd = 4; };
+
+template <int FMT, int TM>
+__global__ __launch_bounds__(256) void gemm_bt_kernel(const uint8_t *__restrict__ B, int64_t sc_off, int64_t d_off,
+                                                      const uint16_t *__restrict__ X, float *__restrict__ Y, int M,
+                                                      int N, int K, int slabs_per_split)
+{
+    constexpr int XSTG = 16 * TM * TBK * 2;  // bytes of one X stage
+    constexpr int RAWB = TRaw<FMT>::bytes;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[TNS * (XSTG + RAWB)];
+    uint8_t *const sx = smem;
+    uint8_t *const sr = smem + TNS * XSTG;
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int g = lane >> 4, r16 = lane & 15;
+    const int n0 = blockIdx.x * TBN, m0 = blockIdx.y * 16 * TM;
+    const int sb = blockIdx.z * slabs_per_split;
+    const int se = min(K / TBK, sb + slabs_per_split);
+
+    // X: load j of wave w fills slots (4j + w)*64 + lane: row p/16, position
+    // p%16 holding chunk (p%16) ^ (row & 15); offsets from row m0
+    uint32_t ox[TM];
+#pragma unroll
+    for (int j = 0; j < TM; j++) {
+        const int p = (4 * j + wv) * 64 + lane, row = p >> 4;
+        const int c = (p & 15) ^ (row & 15);
+        ox[j] = (uint32_t)(((int64_t)(min(m0 + row, M - 1) - m0) * K + 8 * c) * 2);
+    }
+    const uint8_t *const xbase = reinterpret_cast<const uint8_t *>(X + (int64_t)m0 * K);
+    const int64_t g0 = (int64_t)n0 * (K / 256);
+    auto rn = [&](int row) { return (uint32_t)(min(n0 + row, N - 1) - n0); };  // rows past N: results dropped
+
+    auto issue = [&](int s) {
+        const uint32_t xs = lds_addr(sx + (s % TNS) * XSTG);
+#pragma unroll
+        for (int j = 0; j < TM; j++)
+            dma16(xbase + 2 * TBK * s, ox[j], xs + (4 * j + wv) * 1024);
+        const uint32_t rs = lds_addr(sr + (s % TNS) * RAWB);
+        if constexpr (FMT == FMT_Q8_0) {
+            const uint8_t *cb = B + (int64_t)n0 * K + TBK * s;
+#pragma unroll
+            for (int j = 0; j < 2; j++) {
+                const int p = (2 * wv + j) * 64 + lane;
+                dma16(cb, rn(p >> 3) * K + 16 * (p & 7), rs + (2 * wv + j) * 1024);
+            }
+            const int q = 32 * wv + lane;
+            if (lane < 32)
+                dma4(B + sc_off + (int64_t)n0 * (K / 16) + 8 * s, rn(q >> 1) * (K / 16) + 4 * (q & 1),
+                     rs + 8192 + 128 * wv);
+        } else if constexpr (FMT == FMT_Q4K) {
+            const int p = 64 * wv + lane;
+            dma16(B + (int64_t)n0 * (K / 2) + 64 * s, rn(p >> 2) * (K / 2) + 16 * (p & 3), rs + 1024 * wv);
+            if (lane < 16)
+                dma16(B + sc_off + 16 * (g0 + (s >> 1)), rn(16 * wv + lane) * (K / 16), rs + 4096 + 256 * wv);
+        } else {
+            const int cc0 = 4 * (s & 1);
+            const uint8_t *gb = B + 192 * (g0 + (s >> 1));
+            const int p = 64 * wv + lane;
+            dma16(gb + 16 * cc0, rn(p >> 2) * (K / 256) * 192 + 16 * (p & 3), rs + 1024 * wv);
+            const int q = 32 * wv + lane;
+            if (lane < 32) {
+                dma16(gb + 128 + 8 * cc0, rn(q >> 1) * (K / 256) * 192 + 16 * (q & 1), rs + 4096 + 512 * wv);
+                dma4(B + sc_off + 16 * (g0 + (s >> 1)) + 2 * cc0, rn(q >> 1) * (K / 16) + 4 * (q & 1),
+                     rs + 6144 + 128 * wv);
+            }
+            if (lane < 16) {
+                // the d dword of group grp, counted from the dword holding g
+                const int64_t gs = g0 + (s >> 1);
+                const int64_t grp = gs + (int64_t)rn(16 * wv + lane) * (K / 256);
+                dma4(B + d_off + 4 * (gs >> 1), (uint32_t)(4 * ((grp >> 1) - (gs >> 1))), rs + 6656 + 64 * wv);
+            }
+        }
+    };
+
+    const int row = 16 * wv + r16;  // the W row this lane decodes
+    const int64_t nd = min(n0 + row, N - 1);
+    auto decode = [&](int s, uint32_t (&v)[16]) {
+        const uint8_t *rs = sr + (s % TNS) * RAWB;
+        WBlk<FMT> w;
+        if constexpr (FMT == FMT_Q8_0) {
+            w.c0 = *reinterpret_cast<const uint4 *>(rs + 128 * row + 32 * g);
+            w.c1 = *reinterpret_cast<const uint4 *>(rs + 128 * row + 32 * g + 16);
+            w.d = *reinterpret_cast<const uint16_t *>(rs + 8192 + 8 * row + 2 * g);
+        } else if constexpr (FMT == FMT_Q4K) {
+            w.c = *reinterpret_cast<const uint4 *>(rs + 64 * row + 16 * g);
+            w.h = *reinterpret_cast<const uint4 *>(rs + 4096 + 16 * row);
+        } else {
+            w.lo = *reinterpret_cast<const uint4 *>(rs + 64 * row + 16 * g);
+            w.hi = *reinterpret_cast<const uint2 *>(rs + 4096 + 32 * row + 8 * g);
+            w.sc2 = *reinterpret_cast<const uint16_t *>(rs + 6144 + 8 * row + 2 * g);
+            const uint32_t dd = *reinterpret_cast<const uint32_t *>(rs + 6656 + 4 * row);
+            const int64_t grp = nd * (K / 256) + (s >> 1);
+            w.d = (grp & 1) ? dd >> 16 : dd & 0xffffu;
+        }
+        decode_wblk<FMT>(w, 4 * s + g, v);
+    };
+
+    f32x4_t acc[TM];
+#pragma unroll
+    for (int j = 0; j < TM; j++)
+        acc[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    for (int s = sb; s < sb + TNS - 1 && s < se; s++)
+        issue(s);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt 0, lgkmcnt 0
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+
+    // at the end of slab s the next slab must have landed: the loads of
+    // slab s+2 (TM + WD per wave) may remain in flight
+    constexpr int VM = TM + TRaw<FMT>::wd;
+    static_assert(VM < 16, "vmcnt immediate");
+    auto body = [&](int s, auto steady) {
+        constexpr bool ST = decltype(steady)::value;
+        uint32_t v[16];
+        decode(s, v);
+        const uint8_t *xs = sx + (s % TNS) * XSTG;
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+            const bf16x8_t bw = __builtin_bit_cast(bf16x8_t, make_uint4(v[4 * t], v[4 * t + 1], v[4 * t + 2], v[4 * t + 3]));
+#pragma unroll
+            for (int j = 0; j < TM; j++) {
+                const int xr = 16 * j + r16;
+                const bf16x8_t xa = *reinterpret_cast<const bf16x8_t *>(xs + 256 * xr + 16 * ((4 * g + t) ^ r16));
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bw, acc[j], 0, 0, 0);
+            }
+        }
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if constexpr (ST)
+            __builtin_amdgcn_s_waitcnt(0x0070 | VM);  // vmcnt VM, lgkmcnt 0
+        else
+            __builtin_amdgcn_s_waitcnt(0x0070);       // vmcnt 0, lgkmcnt 0
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if constexpr (ST)
+            issue(s + TNS - 1);
+    };
+    int s = sb;
+    for (; s + TNS - 1 < se; s++)
+        body(s, std::true_type{});
+    for (; s < se; s++)
+        body(s, std::false_type{});
+
+    // lane holds D[m = 4g + i][n = r16] of each 16 x 16 tile
+    const bool split = gridDim.z > 1;
+    const int n = n0 + row;
+    if (n < N) {
+#pragma unroll
+        for (int j = 0; j < TM; j++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int m = m0 + 16 * j + 4 * g + i;
+                if (m < M) {
+                    if (split)
+                        atomicAdd(Y + (int64_t)m * N + n, acc[j][i]);
+                    else
+                        Y[(int64_t)m * N + n] = acc[j][i];
+                }
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Q8_0 x Q8_0 int8 path
 // ---------------------------------------------------------------------------
 constexpr int BN = 128;     // n tile
@@ -863,14 +1056,17 @@ hipError_t zero_y(float *Y, int64_t count, hipStream_t s)
     return hipGetLastError();
 }
 
+// `fill`: workgroups (tiles x K splits) to aim for; more splits also mean
+// more fp32 atomics into Y, which measured slower past ~256 workgroups for
+// small M
 template <int FMT, int TM, int NT>
 hipError_t go_bf16(const uint8_t *blocks, const Planes &p, const uint16_t *X, float *Y, int64_t M,
-                   int64_t N, int64_t K, hipStream_t s)
+                   int64_t N, int64_t K, hipStream_t s, int fill = 512)
 {
     const int64_t gx = (N + 64 * NT - 1) / (64 * NT), gy = (M + 16 * TM - 1) / (16 * TM);
     const int nslab = (int)(K / SLAB);
     int splits = 1;
-    while (gx * gy * splits < 512 && splits < 32 && nslab / (2 * splits) >= 2)
+    while (gx * gy * splits < fill && splits < 32 && nslab / (2 * splits) >= 2)
         splits *= 2;
     const int per = (nslab + splits - 1) / splits;
     if (splits > 1) {
@@ -930,19 +1126,49 @@ hipError_t go_pf(const uint8_t *blocks, const Planes &p, const uint16_t *X, floa
     return hipGetLastError();
 }
 
+// Split K towards ~1024 workgroups (four per CU), at least four slabs each.
+template <int FMT, int TM>
+hipError_t go_bt(const uint8_t *blocks, const Planes &p, const uint16_t *X, float *Y, int64_t M, int64_t N,
+                 int64_t K, hipStream_t s)
+{
+    const int64_t gx = (N + TBN - 1) / TBN, gy = (M + 16 * TM - 1) / (16 * TM);
+    const int nslab = (int)(K / TBK);
+    int sp = 1;
+    while (sp < 32 && gx * gy * sp * 2 <= 1024 && nslab / (sp * 2) >= 4)
+        sp *= 2;
+    const int per = (nslab + sp - 1) / sp;
+    if (sp > 1) {
+        const hipError_t e = zero_y(Y, M * N, s);
+        if (e != hipSuccess)
+            return e;
+    }
+    hipLaunchKernelGGL((gemm_bt_kernel<FMT, TM>), dim3((unsigned)gx, (unsigned)gy, (unsigned)sp), dim3(256), 0, s,
+                       blocks, p.scales, p.d, X, Y, (int)M, (int)N, (int)K, per);
+    return hipGetLastError();
+}
+
 template <int FMT>
 hipError_t bf16_by_m(const uint8_t *blocks, const Planes &p, const uint16_t *X, float *Y, int64_t M,
                      int64_t N, int64_t K, hipStream_t s)
 {
     // tall matrices (many row tiles) stream two 16-row tiles per wave
+    // launch shapes from measured sweeps on MI355X (4096 x 14336,
+    // 14336 x 4096, 4096 x 4096 and 131072 x 5120 weights): the direct-load
+    // weight stream wins for up to 32 tokens once W has more than 2^24
+    // elements
+    if (M <= 32 && N * K > ((int64_t)1 << 24))
+        return M <= 16 ? go_bt<FMT, 1>(blocks, p, X, Y, M, N, K, s) : go_bt<FMT, 2>(blocks, p, X, Y, M, N, K, s);
     const bool tall = N >= 32768;
+    if (M <= 8)
+        return tall ? go_skinny<FMT, 1, 2, 4>(blocks, p, X, Y, M, N, K, s)
+                    : go_skinny<FMT, 1, 1, 2>(blocks, p, X, Y, M, N, K, s);
     if (M <= 16)
         return tall ? go_skinny<FMT, 1, 2, 4>(blocks, p, X, Y, M, N, K, s)
-                    : go_skinny<FMT, 1, 1, 4>(blocks, p, X, Y, M, N, K, s);
+                    : go_bf16<FMT, 1, 2>(blocks, p, X, Y, M, N, K, s, 256);
     if (M <= 32)
         return go_skinny<FMT, 2, 1, 4>(blocks, p, X, Y, M, N, K, s);
     if (M <= 64)
-        return go_bf16<FMT, 4, 4>(blocks, p, X, Y, M, N, K, s);
+        return go_bf16<FMT, 4, 2>(blocks, p, X, Y, M, N, K, s, 256);
     if (M >= PF_MIN_M)
         return go_pf<FMT>(blocks, p, X, Y, M, N, K, s);
     return go_bf16<FMT, 8, 4>(blocks, p, X, Y, M, N, K, s);

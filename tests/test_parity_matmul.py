@@ -152,6 +152,18 @@ def test_mfma_bf16_prefill_tiles(fmt):
         check_outputs(run(fmt, "mfma_bf16", w, x), Yr, den, f"prefill tiles {fmt} M={M} N={N} K={K}")
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+def test_mfma_bf16_batched_stream(fmt):
+    """Batched-decode path (3..32 tokens, more than 2^24 weights): ragged N
+    past the 64-row tiles, K split over workgroups, one and two m-tiles."""
+    N, K = 4100, 4352
+    w = synth.weights_bf16(5200, N, K, outliers=True)
+    for M in (3, 17, 32):
+        x = synth.activations_bf16(5201 + M, M, K)
+        Yr, den = a16_ref(fmt, w, x)
+        check_outputs(run(fmt, "mfma_bf16", w, x), Yr, den, f"batched stream {fmt} M={M}")
+
+
 def test_mfma_i8_shapes_and_activation_blocks():
     for M in (1, 9, 16, 64, 130, 256):
         for N, K in ((7, 256), (64, 1024), (300, 4096), (129, 512)):
