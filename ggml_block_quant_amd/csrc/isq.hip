@@ -51,6 +51,22 @@ __device__ __forceinline__ int code_of(float v, float lo, float hi)
     return (int)r;
 }
 
+// RHA of the correctly rounded quotient fl(u / S), for S > 0, given
+// r = fl(1 / S).  t = u*r rounds twice (r, the product), so it lies within
+// 3 * 2^-24 * |t| of fl(u / S); both round (half away from zero) to the same
+// integer unless a half-integer lies that close to t.  Only then is the
+// quotient computed by the correctly rounded division, so the code is the
+// one the definition gives, with one multiply in the common case.
+__device__ __forceinline__ float rha_quot(float u, float S, float r)
+{
+    const float t = u * r;
+    const float a = fabsf(t);
+    float q = roundf(t);
+    if (fabsf(a - floorf(a) - 0.5f) <= 2.5e-7f * a)
+        q = roundf(u / S);
+    return q;
+}
+
 // Even elements of an octet in the low half of a dword, odd ones in the high
 // half: nibble p holds element 2p (p < 4) or 2(p-4)+1 (p >= 4).
 __device__ __forceinline__ uint32_t pack_nibbles(const int q[8])
@@ -79,11 +95,12 @@ __global__ __launch_bounds__(256) void isq_q8_0_kernel(const uint4 *__restrict__
         a = fmaxf(a, __shfl_xor(a, 2));
         float df;
         const uint32_t d16 = scale_f16(a / 127.0f, &df);
+        const float rd = df > 0.0f ? 1.0f / df : 0.0f;  // d = 0: every code is 0
         uint32_t lo = 0, hi = 0;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            const int q0 = df == 0.0f ? 0 : code_of(x[i] / df, -127.0f, 127.0f);
-            const int q1 = df == 0.0f ? 0 : code_of(x[i + 4] / df, -127.0f, 127.0f);
+            const int q0 = (int)fminf(fmaxf(rha_quot(x[i], df, rd), -127.0f), 127.0f);
+            const int q1 = (int)fminf(fmaxf(rha_quot(x[i + 4], df, rd), -127.0f), 127.0f);
             lo |= ((uint32_t)q0 & 0xffu) << (8 * i);
             hi |= ((uint32_t)q1 & 0xffu) << (8 * i);
         }
@@ -129,11 +146,12 @@ __global__ __launch_bounds__(256) void isq_q4k_kernel(const uint4 *__restrict__ 
         const int mq = dmf > 0.0f ? code_of(m / dmf, 0.0f, 63.0f) : 0;
         const float S = df * (float)sc;
         const float M = dmf * (float)mq;
+        const float rS = S > 0.0f ? 1.0f / S : 0.0f;  // S = 0: every code is 0
         int q[8];
 #pragma unroll
         for (int i = 0; i < 8; i++) {
             const float u = x[i] + M;
-            q[i] = S > 0.0f ? code_of(u / S, 0.0f, 15.0f) : 0;
+            q[i] = (int)fminf(fmaxf(rha_quot(u, S, rS), 0.0f), 15.0f);
         }
         codes[t] = pack_nibbles(q);
 
@@ -183,10 +201,11 @@ __global__ __launch_bounds__(256) void isq_q6k_kernel(const uint4 *__restrict__ 
         const uint32_t d16 = scale_f16(smax / 127.0f, &df);
         const int sc = df > 0.0f ? code_of(s / df, 0.0f, 127.0f) : 0;
         const float S = df * (float)sc;
+        const float rS = S > 0.0f ? 1.0f / S : 0.0f;  // S = 0: every code is 0
         int u[8], lo4[8];
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-            u[i] = (S > 0.0f ? code_of(x[i] / S, -32.0f, 31.0f) : 0) + 32;
+            u[i] = (int)fminf(fmaxf(rha_quot(x[i], S, rS), -32.0f), 31.0f) + 32;
             lo4[i] = u[i] & 15;
         }
         const int64_t g = t >> 5;
