@@ -308,3 +308,59 @@ def test_workload_lm_head_q6k_m1_m8():
         y = ql.qmatmul("q6k", blocks, to_dev_bf16(x[:M]), N, path=path).cpu().numpy()
         Yr, den = oracle.matmul_a16(Wr, x[:M])
         check_outputs(y[:, rows], Yr, den, f"lm_head M={M} {path}")
+
+
+def test_graph_replays_match_eager():
+    """Every path captured once in a HIP graph (the split-K paths include the
+    fill kernel that zeroes Y) and replayed several times, with eager work
+    that overwrites the outputs between replays: every replay must give the
+    eager result (bit for bit where no atomics are involved, within 1e-6
+    where K splits add partial tiles in a run-dependent order)."""
+    cases = [("q4k", "gemv", 1, 4096, 4096, True),
+             ("q6k", "gemv", 2, 300, 1024, True),
+             ("q4k", "mfma_bf16", 16, 4100, 4352, False),   # batched stream, split K
+             ("q8_0", "mfma_bf16", 128, 255, 4096, False),  # prefill tiles, split K
+             ("q8_0", "mfma_bf16", 512, 1024, 512, True),   # prefill tiles, no split
+             ("q8_0", "mfma_i8", 64, 300, 1024, False)]
+    bufs = []
+    for i, (fmt, path, M, N, K, exact) in enumerate(cases):
+        w = synth.weights_bf16(5300 + i, N, K)
+        x = to_dev_bf16(synth.activations_bf16(5310 + i, M, K))
+        blocks = ql.isq(fmt, to_dev_bf16(w))
+        ws = None
+        if path == "mfma_i8":
+            ws = torch.empty(ql.workspace_bytes(fmt, path, M, K), dtype=torch.uint8, device=x.device)
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+        ref = ql.qmatmul(fmt, blocks, x, N, path=path, workspace=ws).clone()
+        bufs.append((fmt, path, blocks, x, N, y, ws, ref, exact))
+    torch.cuda.synchronize()
+
+    def launch_all():
+        for fmt, path, blocks, x, N, y, ws, _, _ in bufs:
+            ql.qmatmul(fmt, blocks, x, N, path=path, out=y, workspace=ws)
+
+    launch_all()  # warm before capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            launch_all()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for _, _, _, _, _, y, _, _, _ in bufs:
+            y.fill_(float("nan"))  # eager work between replays
+        other = bufs[rep % len(bufs)]
+        ql.qmatmul(other[0], other[2], other[3], other[4], path=other[1], workspace=other[6])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for fmt, path, _, _, N, y, _, ref, exact in bufs:
+            label = f"replay {rep} {fmt} {path} M={y.shape[0]} N={N}"
+            if exact:
+                assert torch.equal(y, ref), label
+            else:
+                err = ((y - ref).abs().max() / ref.abs().max()).item()
+                assert err < 1e-6, f"{label}: {err}"
