@@ -648,7 +648,9 @@ __global__ __launch_bounds__(64 * LW) void gemv_lds_kernel(Geo g, const uint16_t
 template <int FMT, int M, int CPT>
 hipError_t go_lds(const Geo &g, const uint16_t *X, float *Y, int64_t N, hipStream_t s)
 {
-    constexpr int R = (M == 1 && CPT <= 2) ? 2 : 1;
+    // rows per wave from sweeps on MI355X: two for K <= 4096, four for
+    // K = 5120 (the 131072 x 5120 head: 10 % faster than one), one above
+    constexpr int R = M != 1 ? 1 : CPT <= 2 ? 2 : CPT == 3 ? 4 : 1;
     const int64_t grid = (N + LW * R - 1) / (LW * R);
     hipLaunchKernelGGL((gemv_lds_kernel<FMT, M, CPT, R>), dim3((unsigned)grid), dim3(64 * LW), 0, s, g, X, Y, N);
     return hipGetLastError();
