@@ -43,6 +43,15 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
+// weight bytes are read once: a non-temporal load keeps them from displacing
+// X and the scale planes in the caches
+__device__ __forceinline__ uint4 ld_nt16(const uint8_t *p)
+{
+    typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // ---------------------------------------------------------------------------
 // Dequant-to-bf16 path.  Output tile BN (n) x BM (m) per workgroup of 4
 // wavefronts; wave w owns rows n0 + w*16*NT .. +16*NT of W and all BM rows
@@ -907,6 +916,151 @@ __global__ __launch_bounds__(256) void gemm_bt_kernel(const uint8_t *__restrict_
 }
 
 // ---------------------------------------------------------------------------
+// Q4K batched-decode kernel (up to 16 tokens).  Same operand layout and
+// decode as gemm_bt_kernel, with two changes measured to matter on MI355X:
+//
+//   * weight codes are loaded as 4 rows x 256 contiguous bytes per
+//     instruction (lane (a, b) of a wave reads chunk b of row a of a slab
+//     quad) instead of 16 rows x 64 bytes, which streams ~1.5 us faster per
+//     33 MB; each wave then transposes the quad through its own 4 KB of LDS
+//     (chunk c of row r at slot c ^ r, conflict-free both ways) into the
+//     MFMA layout -- no barrier, since no other wave touches that region;
+//   * a fifth wave stages X for the whole K range with direct
+//     global->LDS loads and waits for them alone, so the four weight waves
+//     issue nothing but register loads and their waits stay exact.
+//
+// FULL (M <= 4, X rows 0..3 only): a workgroup owns 16 rows and all of K,
+// wave w the K quarter w; the quarters are summed through LDS and Y is
+// written -- no zero-fill launch and no atomics.  Otherwise a workgroup owns
+// 64 rows (16 per wave) and SPW slabs of K; K splits add into a zeroed Y.
+// ---------------------------------------------------------------------------
+template <int SPW, bool FULL>
+__global__ __launch_bounds__(320) void gemm_bq_kernel(const uint8_t *__restrict__ B, int64_t sc_off,
+                                                      const uint16_t *__restrict__ X, float *__restrict__ Y, int M,
+                                                      int N, int K)
+{
+    static_assert(SPW % 4 == 0, "whole slab quads");
+    constexpr int NQ = SPW / 4;
+    constexpr int XR = FULL ? 4 : 16;          // X rows staged per slab
+    constexpr int NSX = FULL ? 4 * SPW : SPW;  // slabs of X in LDS
+    __shared__ __attribute__((aligned(1024))) uint8_t sx[NSX * XR * 256];
+    __shared__ __attribute__((aligned(1024))) uint8_t sw[4][4096];
+    __shared__ f32x4_t sred[FULL ? 3 : 1][64];
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int g = lane >> 4, r16 = lane & 15;
+    const int nw0 = FULL ? blockIdx.x * 16 : blockIdx.x * 64 + 16 * wv;  // first row of this wave
+    const int sb = FULL ? wv * SPW : blockIdx.y * SPW;                   // first slab of this wave
+    const int sx0 = FULL ? 0 : sb;                                       // first slab staged in LDS
+
+    if (wv == 4) {
+        // X: row m of slab s at sx + (s XR + m) 256, 16-byte chunk c at slot c ^ m
+        const uint8_t *xb = reinterpret_cast<const uint8_t *>(X) + (int64_t)sx0 * 256;
+        for (int q = 0; 4 * q < M && q < XR / 4; q++) {
+            const int row = 4 * q + (lane >> 4);
+            const int c = (lane & 15) ^ row;
+            const uint32_t ox = (uint32_t)((min(row, M - 1) * K + 8 * c) * 2);
+            const uint32_t xs = lds_addr(sx) + 1024 * q;
+#pragma unroll 4
+            for (int s = 0; s < NSX; s++)
+                dma16(xb + 256 * s, ox, xs + XR * 256 * s);
+        }
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt 0, lgkmcnt 0
+        __builtin_amdgcn_s_barrier();
+        if constexpr (FULL)
+            lds_barrier();  // the quarter-sum barrier of the weight waves
+        return;
+    }
+
+    const int64_t nrow = min(nw0 + r16, N - 1);  // the row this lane decodes (rows past N dropped)
+    uint4 cw[NQ][4];
+    uint4 hw[NQ][2];
+    auto issue = [&](int u) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int64_t rr = min(nw0 + 4 * i + g, N - 1);
+            cw[u][i] = ld_nt16(B + 16 * (rr * (K / 32) + 4 * (sb + 4 * u) + r16));
+        }
+#pragma unroll
+        for (int e = 0; e < 2; e++)
+            hw[u][e] = *reinterpret_cast<const uint4 *>(B + sc_off + 16 * (nrow * (K / 256) + (sb + 4 * u) / 2 + e));
+    };
+    issue(0);
+    // the decode must not be hoisted above the wait for X
+    __builtin_amdgcn_sched_barrier(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_sched_barrier(0);
+
+    uint8_t *const my = sw[wv];
+    const int xr = r16 & (XR - 1);  // FULL: X rows past 3 are not staged; their outputs are dropped
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int u = 0; u < NQ; u++) {
+        if (u + 1 < NQ)
+            issue(u + 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int rr = 4 * i + g;
+            *reinterpret_cast<uint4 *>(my + 256 * rr + 16 * (r16 ^ rr)) = cw[u][i];
+        }
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+            const int s = sb + 4 * u + t;  // slab of the row
+            WBlk<FMT_Q4K> w;
+            w.c = *reinterpret_cast<const uint4 *>(my + 256 * r16 + 16 * ((4 * t + g) ^ r16));
+            w.h = hw[u][t >> 1];
+            uint32_t v[16];
+            decode_wblk<FMT_Q4K>(w, 4 * s + g, v);
+            const uint8_t *xs = sx + XR * 256 * (s - sx0);
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const bf16x8_t bw = __builtin_bit_cast(bf16x8_t, make_uint4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]));
+                const bf16x8_t xa = *reinterpret_cast<const bf16x8_t *>(xs + 256 * xr + 16 * ((4 * g + q) ^ xr));
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bw, acc, 0, 0, 0);
+            }
+        }
+    }
+
+    // lane holds D[m = 4g + i][n = r16]
+    const int n = nw0 + r16;
+    if constexpr (FULL) {
+        if (wv > 0)
+            sred[wv - 1][lane] = acc;
+        lds_barrier();
+        if (wv == 0 && g == 0 && n < N) {
+#pragma unroll
+            for (int w = 0; w < 3; w++) {
+                const f32x4_t o = sred[w][lane];
+                acc[0] += o[0];
+                acc[1] += o[1];
+                acc[2] += o[2];
+                acc[3] += o[3];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                if (i < M)
+                    Y[(int64_t)i * N + n] = acc[i];
+        }
+    } else if (n < N) {
+        const bool split = gridDim.y > 1;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int m = 4 * g + i;
+            if (m < M) {
+                if (split)
+                    atomicAdd(Y + (int64_t)m * N + n, acc[i]);
+                else
+                    Y[(int64_t)m * N + n] = acc[i];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Q8_0 x Q8_0 int8 path
 // ---------------------------------------------------------------------------
 constexpr int BN = 128;     // n tile
@@ -1147,6 +1301,52 @@ hipError_t go_bt(const uint8_t *blocks, const Planes &p, const uint16_t *X, floa
     return hipGetLastError();
 }
 
+template <int SPW, bool FULL>
+hipError_t go_bq(const uint8_t *blocks, const Planes &p, const uint16_t *X, float *Y, int64_t M, int64_t N,
+                 int64_t K, hipStream_t s)
+{
+    const int ks = FULL ? 1 : (int)(K / TBK) / SPW;
+    if (ks > 1) {
+        const hipError_t e = zero_y(Y, M * N, s);
+        if (e != hipSuccess)
+            return e;
+    }
+    const dim3 grid = FULL ? dim3((unsigned)((N + 15) / 16)) : dim3((unsigned)((N + 63) / 64), (unsigned)ks);
+    hipLaunchKernelGGL((gemm_bq_kernel<SPW, FULL>), grid, dim3(320), 0, s, blocks, p.scales, X, Y, (int)M, (int)N,
+                       (int)K);
+    return hipGetLastError();
+}
+
+// Q4K, M <= 16: the instances measured faster than gemm_bt_kernel on MI355X
+// (whole-K workgroups for up to 4 tokens at K = 14336 / 16384; otherwise K
+// ranges of 28, 20 or 16 slabs); false when none fits the shape
+bool pick_bq(const uint8_t *blocks, const Planes &p, const uint16_t *X, float *Y, int64_t M, int64_t N, int64_t K,
+             hipStream_t s, hipError_t &e)
+{
+    const int nslab = (int)(K / TBK);
+    if (M <= 4 && nslab == 112) {
+        e = go_bq<28, true>(blocks, p, X, Y, M, N, K, s);
+        return true;
+    }
+    if (M <= 4 && nslab == 128) {
+        e = go_bq<32, true>(blocks, p, X, Y, M, N, K, s);
+        return true;
+    }
+    if (nslab % 28 == 0) {
+        e = go_bq<28, false>(blocks, p, X, Y, M, N, K, s);
+        return true;
+    }
+    if (nslab % 20 == 0) {
+        e = go_bq<20, false>(blocks, p, X, Y, M, N, K, s);
+        return true;
+    }
+    if (nslab % 16 == 0) {
+        e = go_bq<16, false>(blocks, p, X, Y, M, N, K, s);
+        return true;
+    }
+    return false;
+}
+
 template <int FMT>
 hipError_t bf16_by_m(const uint8_t *blocks, const Planes &p, const uint16_t *X, float *Y, int64_t M,
                      int64_t N, int64_t K, hipStream_t s)
@@ -1156,8 +1356,14 @@ hipError_t bf16_by_m(const uint8_t *blocks, const Planes &p, const uint16_t *X, 
     // 14336 x 4096, 4096 x 4096 and 131072 x 5120 weights): the direct-load
     // weight stream wins for up to 32 tokens once W has more than 2^24
     // elements
-    if (M <= 32 && N * K > ((int64_t)1 << 24))
+    if (M <= 32 && N * K > ((int64_t)1 << 24)) {
+        if constexpr (FMT == FMT_Q4K) {
+            hipError_t e;
+            if (M <= 16 && pick_bq(blocks, p, X, Y, M, N, K, s, e))
+                return e;
+        }
         return M <= 16 ? go_bt<FMT, 1>(blocks, p, X, Y, M, N, K, s) : go_bt<FMT, 2>(blocks, p, X, Y, M, N, K, s);
+    }
     const bool tall = N >= 32768;
     if (M <= 8)
         return tall ? go_skinny<FMT, 1, 2, 4>(blocks, p, X, Y, M, N, K, s)

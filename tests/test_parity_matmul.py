@@ -164,6 +164,29 @@ def test_mfma_bf16_batched_stream(fmt):
         check_outputs(run(fmt, "mfma_bf16", w, x), Yr, den, f"batched stream {fmt} M={M}")
 
 
+def test_mfma_bf16_q4k_quad_stream():
+    """Q4K batched decode through the quad-load kernel: whole-K workgroups for
+    up to 4 tokens (K = 14336 and 16384), and K ranges of 28, 20 and 16 slabs
+    split over workgroups (K = 14336, 5120, 4096); rows ragged past the 16-
+    and 64-row tiles.  One-hot rows pin the layout: bf16(w) bit for bit."""
+    for N, K, Ms in ((1300, 14336, (1, 3, 4, 7, 16)), (1100, 16384, (2, 4)), (3300, 5120, (4, 13)),
+                     (4150, 4096, (2, 9))):
+        w = synth.weights_bf16(5300 + K, N, K, outliers=True)
+        blocks = ql.isq("q4k", to_dev_bf16(w))
+        Wd = oracle.dequant("q4k", oracle.quantize("q4k", w), N, K)
+        for M in Ms:
+            x = synth.activations_bf16(5301 + M, M, K)
+            Yr, den = oracle.matmul_a16(Wd, x)
+            Y = ql.qmatmul("q4k", blocks, to_dev_bf16(x), N, path="mfma_bf16").cpu().numpy()
+            check_outputs(Y, Yr, den, f"quad stream q4k M={M} N={N} K={K}")
+        ks = np.array([0, 33, K // 2 + 7, K - 1])
+        x = np.zeros((4, K), np.uint16)
+        x[np.arange(4), ks] = 0x3F80
+        Y = ql.qmatmul("q4k", blocks, to_dev_bf16(x), N, path="mfma_bf16").cpu().numpy()
+        Wbf = synth.bf16_bits_to_f32(synth.bf16_bits_from_f32(Wd[:, ks].astype(np.float32)))
+        assert np.array_equal(Y, Wbf.T), f"quad stream one-hot N={N} K={K}"
+
+
 def test_mfma_i8_shapes_and_activation_blocks():
     for M in (1, 9, 16, 64, 130, 256):
         for N, K in ((7, 256), (64, 1024), (300, 4096), (129, 512)):
