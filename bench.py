@@ -394,6 +394,18 @@ def bench_parts(torch, ql, synth, dev, bf16_dev, which):
             log(f"  lm_head M={M}: {ms * 1e3:.1f} us")
         del Bh2
 
+        # embedding lookup from the same Q6K table (a tied head): 2048 random ids
+        ids = torch.randint(0, 131072, (2048,), generator=torch.Generator().manual_seed(9100),
+                            dtype=torch.int32).to(dev)
+        E = torch.empty((2048, 5120), dtype=torch.float32, device=dev)
+        ms = timed_calls(lambda i: ql.embed("q6k", Bh, 131072, 5120, ids, out=E), 20)
+        moved = 2048 * 5120 * 210 // 256 + E.numel() * 4
+        parts["embed_q6k_131072x5120_2048ids"] = {"us": round(ms * 1e3, 2), "GBps": round(moved / ms / 1e6, 1),
+                                                  "hbm_frac": round(moved / ms / 1e6 / HBM_PEAK_GBPS, 4),
+                                                  "bytes": moved, "note": "quantized rows read + fp32 rows written"}
+        log(f"  embed 2048 ids: {ms * 1e3:.1f} us ({moved / ms / 1e6:.0f} GB/s)")
+        del E
+
         # equivalent decode tokens/s: every projection GEMV of the 32 layers + head
         x1 = bf16_dev(synth.activations_bf16(9001, 1, 14336))
         Ys = [torch.empty((1, n), dtype=torch.float32, device=dev) for (n, k) in shapes]

@@ -38,6 +38,7 @@ SIGNATURES = {
     "qmatmul": (_INT, [_INT, _P, _P, _P, _I64, _I64, _I64, _P]),
     "qmatmul_workspace_bytes": (_SZ, [_INT, _INT, _I64, _I64]),
     "qmatmul_ex": (_INT, [_INT, _P, _P, _P, _I64, _I64, _I64, _INT, _P, _SZ, _P]),
+    "q_embed": (_INT, [_INT, _P, _I64, _I64, _P, _I64, _P, _P]),
     "q_dequantize": (_INT, [_INT, _P, _I64, _I64, _P, _P]),
     "isq_resolve_level": (_INT, [_INT, _IP]),
     "isq_sensitive_fmt": (_INT, [_INT, _IP]),
@@ -190,6 +191,24 @@ def qmatmul(fmt, blocks: torch.Tensor, X: torch.Tensor, N: int, path="auto",
     _check("qmatmul_ex", lib().qmatmul_ex(_fmt(fmt), _dev(blocks, "blocks", torch.uint8),
                                           _dev(X, "X", torch.bfloat16), _dev(out, "Y", torch.float32),
                                           M, N, K, p, ws_ptr, ws_bytes, _stream()))
+    return out
+
+
+def embed(fmt, blocks: torch.Tensor, N: int, K: int, ids: torch.Tensor,
+          out: torch.Tensor | None = None) -> torch.Tensor:
+    """Rows ``ids`` (int32, device) of the quantized [N][K] table, dequantized
+    exactly to fp32 [len(ids)][K]; ids outside [0, N) give zero rows.  The
+    same blocks serve ``qmatmul`` as a tied output head."""
+    if ids.dim() != 1:
+        raise ValueError("ids must be 1-D")
+    n = ids.numel()
+    if out is None:
+        out = torch.empty((n, K), dtype=torch.float32, device=blocks.device)
+    if n == 0:
+        return out
+    _check("q_embed", lib().q_embed(_fmt(fmt), _dev(blocks, "blocks", torch.uint8), N, K,
+                                    _dev(ids, "ids", torch.int32), n, _dev(out, "out", torch.float32),
+                                    _stream()))
     return out
 
 

@@ -172,6 +172,28 @@ int q_dequantize(int fmt, const void *blocks, int64_t N, int64_t K, float *W_fp3
                                         as_stream(stream)));
 }
 
+int q_embed(int fmt, const void *blocks, int64_t N, int64_t K, const int32_t *ids, int64_t n_ids, float *out_fp32,
+            void *stream)
+{
+    if (!known(fmt))
+        return Q_EINVAL;
+    if (!implemented(fmt))
+        return Q_ENOTSUP;
+    if (!blocks || !ids || !out_fp32)
+        return Q_EINVAL;
+    if (!aligned16(blocks) || !aligned16(out_fp32) || (reinterpret_cast<uintptr_t>(ids) & 3u) != 0)
+        return Q_EALIGN;
+    const int st = check_tensor(fmt, N, K, QLINEAR_MAX_N);
+    if (st != Q_OK)
+        return st;
+    if (n_ids < 0 || n_ids > QLINEAR_MAX_EMBED_IDS || n_ids * K > kMaxElems)
+        return Q_ESHAPE;
+    if (n_ids == 0)
+        return Q_OK;
+    return status_of(ql::launch_embed(fmt, static_cast<const uint8_t *>(blocks), N, K, ids, n_ids, out_fp32,
+                                      as_stream(stream)));
+}
+
 int isq_resolve_level(int level, int *out_fmt)
 {
     if (!out_fmt)

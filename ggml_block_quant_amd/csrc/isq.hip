@@ -242,6 +242,52 @@ __device__ __forceinline__ void unpack_nibbles(uint32_t d, int q[8])
     }
 }
 
+// the 8 elements of task t (elements 8t..8t+7 of the tensor), exactly
+__device__ __forceinline__ void dequant8(int fmt, const uint8_t *__restrict__ B, int64_t t, int64_t scales_off,
+                                         int64_t d_off, float v[8])
+{
+    if (fmt == FMT_Q8_0) {
+        const uint2 c = reinterpret_cast<const uint2 *>(B)[t];
+        const float d = h2f(reinterpret_cast<const uint16_t *>(B + scales_off)[t >> 2]);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            v[i] = d * (float)(int8_t)(c.x >> (8 * i));
+            v[i + 4] = d * (float)(int8_t)(c.y >> (8 * i));
+        }
+    } else if (fmt == FMT_Q4K) {
+        const uint32_t c = reinterpret_cast<const uint32_t *>(B)[t];
+        const uint4 h = reinterpret_cast<const uint4 *>(B + scales_off)[t >> 5];
+        const int j = (int)((t & 31) >> 2);
+        const uint32_t sc = ((h.y >> (4 * j)) & 15u) | ((h.w >> (2 * j)) & 3u) << 4;
+        const uint32_t mq = ((h.z >> (4 * j)) & 15u) | ((h.w >> (16 + 2 * j)) & 3u) << 4;
+        const float S = h2f(h.x & 0xffffu) * (float)sc;
+        const float M = h2f(h.x >> 16) * (float)mq;
+        int q[8];
+        unpack_nibbles(c, q);
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+            v[i] = fmaf(S, (float)q[i], -M);  // one rounding of the exact value
+    } else {
+        const int64_t g = t >> 5;
+        const int l = (int)(t & 31), c = l >> 2, w = l & 3, o = w & 1;
+        const uint8_t *Cg = B + 192 * g;
+        const uint32_t lo = *reinterpret_cast<const uint32_t *>(Cg + 4 * l);
+        const uint32_t hd = *reinterpret_cast<const uint32_t *>(Cg + 128 + 8 * c + 4 * (w >> 1));
+        const int sc = reinterpret_cast<const int8_t *>(B + scales_off)[16 * g + (l >> 1)];
+        const float S = h2f(reinterpret_cast<const uint16_t *>(B + d_off)[g]) * (float)sc;
+        int q[8];
+        unpack_nibbles(lo, q);
+#pragma unroll
+        for (int p = 0; p < 4; p++) {
+            q[2 * p] |= (int)((hd >> (8 * o + 2 * p)) & 3u) << 4;
+            q[2 * p + 1] |= (int)((hd >> (16 + 8 * o + 2 * p)) & 3u) << 4;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+            v[i] = S * (float)(q[i] - 32);
+    }
+}
+
 __global__ __launch_bounds__(256) void dequant_kernel(int fmt, const uint8_t *__restrict__ B,
                                                       int64_t tasks, int64_t scales_off,
                                                       int64_t d_off, float4 *__restrict__ out)
@@ -249,49 +295,37 @@ __global__ __launch_bounds__(256) void dequant_kernel(int fmt, const uint8_t *__
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < tasks; t += stride) {
         float v[8];
-        if (fmt == FMT_Q8_0) {
-            const uint2 c = reinterpret_cast<const uint2 *>(B)[t];
-            const float d = h2f(reinterpret_cast<const uint16_t *>(B + scales_off)[t >> 2]);
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                v[i] = d * (float)(int8_t)(c.x >> (8 * i));
-                v[i + 4] = d * (float)(int8_t)(c.y >> (8 * i));
-            }
-        } else if (fmt == FMT_Q4K) {
-            const uint32_t c = reinterpret_cast<const uint32_t *>(B)[t];
-            const uint4 h = reinterpret_cast<const uint4 *>(B + scales_off)[t >> 5];
-            const int j = (int)((t & 31) >> 2);
-            const uint32_t sc = ((h.y >> (4 * j)) & 15u) | ((h.w >> (2 * j)) & 3u) << 4;
-            const uint32_t mq = ((h.z >> (4 * j)) & 15u) | ((h.w >> (16 + 2 * j)) & 3u) << 4;
-            const float S = h2f(h.x & 0xffffu) * (float)sc;
-            const float M = h2f(h.x >> 16) * (float)mq;
-            int q[8];
-            unpack_nibbles(c, q);
-#pragma unroll
-            for (int i = 0; i < 8; i++)
-                v[i] = fmaf(S, (float)q[i], -M);  // one rounding of the exact value
-        } else {
-            const int64_t g = t >> 5;
-            const int l = (int)(t & 31), c = l >> 2, w = l & 3, o = w & 1;
-            const uint8_t *Cg = B + 192 * g;
-            const uint32_t lo = *reinterpret_cast<const uint32_t *>(Cg + 4 * l);
-            const uint32_t hd = *reinterpret_cast<const uint32_t *>(Cg + 128 + 8 * c + 4 * (w >> 1));
-            const int sc = reinterpret_cast<const int8_t *>(B + scales_off)[16 * g + (l >> 1)];
-            const float S = h2f(reinterpret_cast<const uint16_t *>(B + d_off)[g]) * (float)sc;
-            int q[8];
-            unpack_nibbles(lo, q);
-#pragma unroll
-            for (int p = 0; p < 4; p++) {
-                q[2 * p] |= (int)((hd >> (8 * o + 2 * p)) & 3u) << 4;
-                q[2 * p + 1] |= (int)((hd >> (16 + 8 * o + 2 * p)) & 3u) << 4;
-            }
-#pragma unroll
-            for (int i = 0; i < 8; i++)
-                v[i] = S * (float)(q[i] - 32);
-        }
+        dequant8(fmt, B, t, scales_off, d_off, v);
         out[2 * t] = make_float4(v[0], v[1], v[2], v[3]);
         out[2 * t + 1] = make_float4(v[4], v[5], v[6], v[7]);
     }
+}
+
+// ---------------------------------------------------------------------------
+// Quantized embedding lookup: row ids[i] of the [N][K] table, dequantized
+// exactly, becomes row i of the output.  Workgroup (x, y) writes 2048
+// elements of output row x; ids outside [0, N) give a row of zeros.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void embed_kernel(int fmt, const uint8_t *__restrict__ B, int64_t scales_off,
+                                                    int64_t d_off, const int32_t *__restrict__ ids, int64_t N,
+                                                    int64_t K, float4 *__restrict__ out)
+{
+    const int64_t row = blockIdx.x;
+    const int64_t k8 = (int64_t)blockIdx.y * 256 + threadIdx.x;  // task in the row
+    if (k8 >= K / 8)
+        return;
+    const int32_t id = ids[row];
+    float v[8];
+    if (id >= 0 && id < N) {
+        dequant8(fmt, B, (int64_t)id * (K / 8) + k8, scales_off, d_off, v);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+            v[i] = 0.0f;
+    }
+    float4 *o = out + 2 * (row * (K / 8) + k8);
+    o[0] = make_float4(v[0], v[1], v[2], v[3]);
+    o[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
 
 inline unsigned grid_for(int64_t tasks)
@@ -321,6 +355,16 @@ hipError_t launch_isq(int fmt, const uint16_t *W, int64_t N, int64_t K, uint8_t 
                            reinterpret_cast<int8_t *>(out + p.scales),
                            reinterpret_cast<uint16_t *>(out + p.d), out + 210 * (N * K / 256),
                            (int)(p.total - 210 * (N * K / 256)));
+    return hipGetLastError();
+}
+
+hipError_t launch_embed(int fmt, const uint8_t *blocks, int64_t N, int64_t K, const int32_t *ids, int64_t n_ids,
+                        float *out, hipStream_t s)
+{
+    const Planes p = planes_of(fmt, N, K);
+    const dim3 grid((unsigned)n_ids, (unsigned)((K / 8 + 255) / 256));
+    hipLaunchKernelGGL(embed_kernel, grid, dim3(256), 0, s, fmt, blocks, p.scales, p.d, ids, N, K,
+                       reinterpret_cast<float4 *>(out));
     return hipGetLastError();
 }
 

@@ -59,6 +59,8 @@ hipError_t launch_isq(int fmt, const uint16_t *W, int64_t N, int64_t K, uint8_t 
                       hipStream_t s);
 hipError_t launch_dequant(int fmt, const uint8_t *blocks, int64_t N, int64_t K, float *W,
                           hipStream_t s);
+hipError_t launch_embed(int fmt, const uint8_t *blocks, int64_t N, int64_t K, const int32_t *ids,
+                        int64_t n_ids, float *out, hipStream_t s);
 hipError_t launch_gemv(int fmt, const uint8_t *blocks, const uint16_t *X, float *Y, int M,
                        int64_t N, int64_t K, hipStream_t s);
 hipError_t launch_gemm_bf16(int fmt, const uint8_t *blocks, const uint16_t *X, float *Y,

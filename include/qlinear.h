@@ -143,6 +143,20 @@ int qmatmul_ex(int fmt, const void *blocks, const void *X_bf16, float *Y_fp32, i
                int64_t N, int64_t K, int path, void *workspace, size_t workspace_bytes,
                void *stream);
 
+/* Quantized embedding lookup (page "Quantization types", section
+ * "Sensitive tensor precision": token embeddings are stored quantized, and
+ * a tied output head reuses the embedding instead of a second copy -- the
+ * same block buffer serves this call and qmatmul).
+ * blocks: device, from isq_quantize(fmt, E, N, K) of the [N][K] table.
+ * ids: device int32 [n_ids], 4-byte aligned.  out_fp32: device [n_ids][K],
+ * row i = the exact dequantized row ids[i] (bit-exact: fp32 holds Q8_0 and
+ * Q6K weights exactly and Q4K's d*sc*q - dmin*m rounded once).  An id
+ * outside [0, N) gives a row of zeros.  n_ids == 0 launches nothing;
+ * 0 <= n_ids <= QLINEAR_MAX_EMBED_IDS. */
+#define QLINEAR_MAX_EMBED_IDS (1 << 24)
+int q_embed(int fmt, const void *blocks, int64_t N, int64_t K, const int32_t *ids, int64_t n_ids,
+            float *out_fp32, void *stream);
+
 /* Test aid: exact dequantization of a block buffer to fp32 [N][K] (device). */
 int q_dequantize(int fmt, const void *blocks, int64_t N, int64_t K, float *W_fp32,
                  void *stream);

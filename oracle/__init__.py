@@ -244,6 +244,20 @@ def dequant(fmt: str, f: dict, rows: int, cols: int) -> np.ndarray:
     return out
 
 
+def embed(W: np.ndarray, ids) -> np.ndarray:
+    """Quantized embedding lookup (page "Quantization types", section
+    "Sensitive tensor precision": token embeddings are stored quantized and a
+    tied output head reuses them): row i is row ids[i] of the exact
+    dequantized table W [N][K] (from ``dequant``), and an id outside [0, N)
+    gives a row of zeros.  Indexing only, no arithmetic."""
+    ids = np.asarray(ids, np.int64)
+    N, K = W.shape
+    out = np.zeros((ids.size, K), np.float64)
+    ok = (ids >= 0) & (ids < N)
+    out[ok] = W[ids[ok]]
+    return out
+
+
 def select_rows(fmt: str, f: dict, rows, cols: int) -> dict:
     """Fields of the selected weight rows only (for sampled parity checks)."""
     rows = np.asarray(rows, np.int64)

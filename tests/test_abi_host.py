@@ -136,3 +136,25 @@ def test_qmatmul_argument_errors():
     assert call(fmt=0, path=3, ws=MIS, wsb=1 << 20) == ql.Q_EALIGN
     assert L.qmatmul(1, A, A2, NULL, 4, 64, 256, NULL) == ql.Q_EINVAL
     assert ok
+
+
+def test_embed_argument_errors():
+    L = ql.lib()
+    IDS = ctypes.c_void_p(0x40004)   # int32 ids need only 4-byte alignment
+
+    def call(fmt=2, b=A, N=1000, K=512, ids=IDS, n=8, out=A3):
+        return L.q_embed(fmt, b, N, K, ids, n, out, NULL)
+
+    assert call(b=NULL) == ql.Q_EINVAL
+    assert call(ids=NULL) == ql.Q_EINVAL
+    assert call(out=NULL) == ql.Q_EINVAL
+    assert call(fmt=12) == ql.Q_EINVAL
+    assert call(fmt=4) == ql.Q_ENOTSUP                       # Q3K: named, not implemented
+    assert call(b=MIS) == ql.Q_EALIGN
+    assert call(out=MIS) == ql.Q_EALIGN
+    assert call(ids=ctypes.c_void_p(0x40002)) == ql.Q_EALIGN
+    assert call(K=100) == ql.Q_ESHAPE
+    assert call(N=0) == ql.Q_ESHAPE
+    assert call(n=-1) == ql.Q_ESHAPE
+    assert call(n=(1 << 24) + 1) == ql.Q_ESHAPE
+    assert call(n=0) == ql.Q_OK                              # nothing to launch

@@ -110,6 +110,25 @@ def test_q8_0_worked_blocks():
         assert np.array_equal(f["q"][0], want), (blk["name"], f["q"][0])
 
 
+def test_embed_rows_are_the_worked_blocks():
+    """Embedding lookup on a 3-row Q8_0 table built from the hand-derived
+    blocks: each looked-up row is d16 * q of its block, listed in
+    tests/golden/q8_0_blocks.json; ids outside the table give zero rows."""
+    blks = {b["name"]: b for b in _golden("q8_0_blocks.json")["blocks"]}
+    table = np.zeros((3, 32), np.uint16)
+    for r, name in enumerate(("A_basic", "C_zero_block", "B_ties")):
+        xs = _bf16(blks[name]["x"]) if blks[name]["x"] else np.zeros(0, np.uint16)
+        table[r, : len(xs)] = xs
+    W = oracle.dequant("q8_0", oracle.quantize("q8_0", table), 3, 32)
+    E = oracle.embed(W, [2, 0, -1, 3, 0, 1])
+    for i, name in ((0, "B_ties"), (1, "A_basic"), (4, "A_basic")):
+        d = float(np.frombuffer(np.uint16(_h(blks[name]["d16"])).tobytes(), np.float16)[0])
+        want = np.zeros(32)
+        want[: len(blks[name]["q"])] = np.array(blks[name]["q"], np.float64) * d
+        assert np.array_equal(E[i], want), name
+    assert not E[2].any() and not E[3].any() and not E[5].any()
+
+
 def _q8_blocks(seed, n_blocks, scale):
     w = synth.normal_bf16(seed, (n_blocks, 32), scale)
     return w, oracle.quantize("q8_0", w)
