@@ -51,7 +51,7 @@ def parse():
     ap.add_argument("--quick", action="store_true", help="headline only (for profiling runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--parts", default=None,
-                    help="comma-separated parts measured after the headline: batched, prefill, isq "
+                    help="comma-separated parts measured after the headline: batched, glu, prefill, isq "
                          "(default: all of them, none with --quick)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only copy a buffer of BYTES bytes 10 times (the reference kernel that scales "
@@ -248,7 +248,7 @@ def main():
         "hbm_frac": round(q4["alg_GBps"] / HBM_PEAK_GBPS, 4), "parity_max_err": q4["parity_max_err"]}
     del W
 
-    which = set(args.parts.split(",")) if args.parts else (set() if args.quick else {"batched", "prefill", "isq"})
+    which = set(args.parts.split(",")) if args.parts else (set() if args.quick else {"batched", "glu", "prefill", "isq"})
     if which:
         parts.update(bench_parts(torch, ql, synth, dev, bf16_dev, which))
     result["parts"] = parts
@@ -320,6 +320,37 @@ def bench_parts(torch, ql, synth, dev, bf16_dev, which):
         parts["crossover_q4k_4096x14336_us"] = cross
         log(f"  crossover: {cross}")
         del copies, blocks
+        torch.cuda.empty_cache()
+
+    if "glu" in which:
+        # gated FFN projection, 14336 x 4096 gate and up (Q4K): one fused launch
+        # against the two GEMVs it replaces (their outputs alone, no product)
+        log("gated FFN 14336x4096 q4k: fused gate/up + SiLU vs two GEMVs")
+        F, K = 14336, 4096
+        wg = bf16_dev(synth.weights_bf16(synth.seed_for(2, 0), F, K))
+        wu = synth.device_normal_bf16(9501, (F, K), synth.W_SIGMA)
+        bg, bu = ql.isq("q4k", wg), ql.isq("q4k", wu)
+        R = copies_for(2 * bg.numel())
+        cg = [bg] + [bg.clone() for _ in range(R - 1)]
+        cu = [bu] + [bu.clone() for _ in range(R - 1)]
+        xs = synth.activations_bf16(synth.seed_for(2, 1), 2, K)
+        for M in (1, 2):
+            X = bf16_dev(xs[:M])
+            H = torch.empty((M, F), dtype=torch.float32, device=dev)
+            Y2 = torch.empty((M, F), dtype=torch.float32, device=dev)
+            fused = timed_calls(lambda i: ql.qmatmul_glu("q4k", cg[i % R], cu[i % R], X, F, out=H), 2 * R)
+
+            def two(i):
+                ql.qmatmul("q4k", cg[i % R], X, F, out=Y2)
+                ql.qmatmul("q4k", cu[i % R], X, F, out=H)
+
+            sep = timed_calls(two, 2 * R)
+            parts[f"glu_q4k_14336x4096_m{M}"] = {
+                "fused_us": round(fused * 1e3, 2), "two_gemvs_us": round(sep * 1e3, 2),
+                "fused_weight_GBps": round(2 * bg.numel() / fused / 1e6, 1),
+                "hbm_frac": round(2 * bg.numel() / fused / 1e6 / HBM_PEAK_GBPS, 4)}
+            log(f"  M={M}: fused {fused * 1e3:.2f} us, two GEMVs {sep * 1e3:.2f} us")
+        del cg, cu, bg, bu, wg, wu
         torch.cuda.empty_cache()
 
     if "prefill" in which:
@@ -426,6 +457,26 @@ def bench_parts(torch, ql, synth, dev, bf16_dev, which):
                                        "weight_GBps": round(total / ms / 1e6, 1),
                                        "note": "225 quantized GEMVs per token (M=1); attention, norms, sampling excluded"}
         log(f"  decode token: {ms:.3f} ms -> {1000 / ms:.0f} tok/s")
+
+        # the same token with each layer's gate and up projections fused with
+        # SiLU * up into one launch (qmatmul_glu)
+        Hf = torch.empty((1, 14336), dtype=torch.float32, device=dev)
+
+        def token_fused(_i):
+            for layer in range(32):
+                for j in (0, 1, 2, 3, 6):
+                    n, k = shapes[j]
+                    ql.qmatmul("q4k", Bl[7 * layer + j], x1[:, :k], n, out=Ys[j])
+                ql.qmatmul_glu("q4k", Bl[7 * layer + 4], Bl[7 * layer + 5], x1[:, :4096], 14336, out=Hf)
+            ql.qmatmul("q6k", Bh, x1[:, :5120], 131072, out=Yh)
+
+        token_fused(0)
+        g = graph_of(torch, token_fused, 1)
+        ms = time_graph(torch, g, 10, 1)
+        parts["equiv_decode_tok_s_fused_ffn"] = {
+            "tok_s": round(1000.0 / ms, 1), "ms_per_token": round(ms, 4), "weight_GBps": round(total / ms / 1e6, 1),
+            "note": "per layer q, k, v, o, down GEMVs + one fused gate/up SiLU launch (193 launches per token)"}
+        log(f"  decode token, fused gate/up: {ms:.3f} ms -> {1000 / ms:.0f} tok/s")
     return parts
 
 

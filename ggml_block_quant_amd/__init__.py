@@ -25,6 +25,7 @@ FMT = {"q8_0": 0, "q4k": 1, "q6k": 2, "q2k": 3, "q3k": 4, "q5k": 5, "q8k": 6,
        "q4_0": 7, "q4_1": 8, "q5_0": 9, "q5_1": 10, "q8_1": 11}
 FMT_NAME = {v: k for k, v in FMT.items()}
 PATH = {"auto": 0, "gemv": 1, "mfma_bf16": 2, "mfma_i8": 3}
+ACT = {"silu": 0, "relu": 1, "sigmoid": 2}
 
 Q_OK, Q_EINVAL, Q_ESHAPE, Q_EALIGN, Q_ENOTSUP, Q_EHIP = 0, -1, -2, -3, -4, -5
 
@@ -39,6 +40,8 @@ SIGNATURES = {
     "qmatmul_workspace_bytes": (_SZ, [_INT, _INT, _I64, _I64]),
     "qmatmul_ex": (_INT, [_INT, _P, _P, _P, _I64, _I64, _I64, _INT, _P, _SZ, _P]),
     "q_embed": (_INT, [_INT, _P, _I64, _I64, _P, _I64, _P, _P]),
+    "qmatmul_glu_workspace_bytes": (_SZ, [_INT, _I64, _I64, _I64]),
+    "qmatmul_glu": (_INT, [_INT, _P, _P, _P, _P, _I64, _I64, _I64, _INT, _P, _SZ, _P]),
     "q_dequantize": (_INT, [_INT, _P, _I64, _I64, _P, _P]),
     "isq_resolve_level": (_INT, [_INT, _IP]),
     "isq_sensitive_fmt": (_INT, [_INT, _IP]),
@@ -191,6 +194,34 @@ def qmatmul(fmt, blocks: torch.Tensor, X: torch.Tensor, N: int, path="auto",
     _check("qmatmul_ex", lib().qmatmul_ex(_fmt(fmt), _dev(blocks, "blocks", torch.uint8),
                                           _dev(X, "X", torch.bfloat16), _dev(out, "Y", torch.float32),
                                           M, N, K, p, ws_ptr, ws_bytes, _stream()))
+    return out
+
+
+def glu_workspace_bytes(fmt, M: int, F: int, K: int) -> int:
+    return lib().qmatmul_glu_workspace_bytes(_fmt(fmt), M, F, K)
+
+
+def qmatmul_glu(fmt, gate_blocks: torch.Tensor, up_blocks: torch.Tensor, X: torch.Tensor, F: int,
+                act="silu", out: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """H = act(X . deq(Wg)^T) * (X . deq(Wu)^T) as fp32 [M][F] for the blocks
+    of the [F][K] gate and up weights; ``act``: silu | relu | sigmoid."""
+    if X.dim() != 2:
+        raise ValueError("X must be 2-D [M][K]")
+    M, K = X.shape
+    if out is None:
+        out = torch.empty((M, F), dtype=torch.float32, device=X.device)
+    ws_ptr, ws_bytes = None, 0
+    need = glu_workspace_bytes(fmt, M, F, K)
+    if need:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
+        ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    a = ACT[act] if isinstance(act, str) else int(act)
+    _check("qmatmul_glu", lib().qmatmul_glu(_fmt(fmt), _dev(gate_blocks, "gate_blocks", torch.uint8),
+                                            _dev(up_blocks, "up_blocks", torch.uint8),
+                                            _dev(X, "X", torch.bfloat16), _dev(out, "H", torch.float32),
+                                            M, F, K, a, ws_ptr, ws_bytes, _stream()))
     return out
 
 

@@ -155,6 +155,49 @@ int qmatmul(int fmt, const void *blocks, const void *X_bf16, float *Y_fp32, int6
     return qmatmul_ex(fmt, blocks, X_bf16, Y_fp32, M, N, K, QPATH_AUTO, nullptr, 0, stream);
 }
 
+size_t qmatmul_glu_workspace_bytes(int fmt, int64_t M, int64_t F, int64_t K)
+{
+    if (!implemented(fmt) || M < 1 || M > QLINEAR_MAX_M || check_tensor(fmt, F, K, QLINEAR_MAX_N) != Q_OK ||
+        K % 256 != 0 || M * F > kMaxElems)
+        return 0;
+    return ql::glu_fused_fits((int)M, K) ? 0 : (size_t)(4 * M * F);
+}
+
+int qmatmul_glu(int fmt, const void *gate_blocks, const void *up_blocks, const void *X_bf16, float *H_fp32,
+                int64_t M, int64_t F, int64_t K, int act, void *workspace, size_t workspace_bytes, void *stream)
+{
+    int st = matmul_args(fmt, gate_blocks, X_bf16, H_fp32, M, F, K);
+    if (st != Q_OK)
+        return st;
+    if (!up_blocks)
+        return Q_EINVAL;
+    if (!aligned16(up_blocks))
+        return Q_EALIGN;
+    if (act < QACT_SILU || act > QACT_SIGMOID)
+        return Q_EINVAL;
+    const auto *Bg = static_cast<const uint8_t *>(gate_blocks);
+    const auto *Bu = static_cast<const uint8_t *>(up_blocks);
+    const auto *X = static_cast<const uint16_t *>(X_bf16);
+    const hipStream_t s = as_stream(stream);
+    if (ql::glu_fused_fits((int)M, K))
+        return status_of(ql::launch_glu_fused(fmt, Bg, Bu, X, H_fp32, (int)M, F, K, act, s));
+    // two matmuls and the elementwise product: G in the workspace, U in H
+    if (!workspace)
+        return Q_EINVAL;
+    if (!aligned16(workspace))
+        return Q_EALIGN;
+    if (workspace_bytes < qmatmul_glu_workspace_bytes(fmt, M, F, K))
+        return Q_EINVAL;
+    float *G = static_cast<float *>(workspace);
+    st = qmatmul(fmt, gate_blocks, X_bf16, G, M, F, K, stream);
+    if (st != Q_OK)
+        return st;
+    st = qmatmul(fmt, up_blocks, X_bf16, H_fp32, M, F, K, stream);
+    if (st != Q_OK)
+        return st;
+    return status_of(ql::launch_glu_apply(G, H_fp32, M * F, act, s));
+}
+
 int q_dequantize(int fmt, const void *blocks, int64_t N, int64_t K, float *W_fp32, void *stream)
 {
     if (!known(fmt))

@@ -1393,6 +1393,24 @@ hipError_t launch_gemm_bf16(int fmt, const uint8_t *blocks, const uint16_t *X, f
     return bf16_by_m<FMT_Q8_0>(blocks, p, X, Y, M, N, K, s);
 }
 
+// Unfused gated projection, second step: H = act(G) * H, where H holds the
+// up projection (the fused kernel evaluates the same fp32 expression).
+__global__ __launch_bounds__(256) void glu_apply_kernel(const float *__restrict__ G, float *__restrict__ H, int64_t n,
+                                                        int act)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+        H[i] = act_f32(act, G[i]) * H[i];
+}
+
+hipError_t launch_glu_apply(const float *G, float *H, int64_t n, int act, hipStream_t s)
+{
+    int64_t g = (n + 255) / 256;
+    g = g < 1 ? 1 : (g > 65536 ? 65536 : g);
+    hipLaunchKernelGGL(glu_apply_kernel, dim3((unsigned)g), dim3(256), 0, s, G, H, n, act);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm_i8(const uint8_t *wblocks, const uint8_t *xblocks, float *Y, int64_t M, int64_t N,
                           int64_t K, hipStream_t s)
 {

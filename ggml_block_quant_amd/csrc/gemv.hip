@@ -288,6 +288,21 @@ __device__ __forceinline__ int butterfly_index(int lane)
     return idx;
 }
 
+// the lane that holds index idx after butterfly_sum (the inverse of
+// butterfly_index: a bit reversal over log2(V) bits)
+template <int V>
+__device__ __forceinline__ int butterfly_lane(int idx)
+{
+    int lane = 0, part = V;
+#pragma unroll
+    for (int b = 0; b < 6 && part > 1; b++) {
+        part >>= 1;
+        if (idx & part)
+            lane |= 1 << b;
+    }
+    return lane;
+}
+
 constexpr int pow2_at_least(int v)
 {
     int p = 1;
@@ -525,10 +540,15 @@ __device__ __forceinline__ Chunk<FMT> chunk_of(const WLoad<FMT> &w)
     }
 }
 
-template <int FMT, int M, int CPT, int R>
-__global__ __launch_bounds__(64 * LW) void gemv_lds_kernel(Geo g, const uint16_t *__restrict__ X,
-                                                           float *__restrict__ Y, int64_t N)
+// GLU: the fused gated projection -- wave w computes output f = row w of
+// the gate weights (g) and of the up weights (g2) as its two rows, and
+// writes act(gate) * up (same fp32 activation and product as the unfused
+// path); N is then the number of outputs F.
+template <int FMT, int M, int CPT, int R, bool GLU = false>
+__global__ __launch_bounds__(64 * LW) void gemv_lds_kernel(Geo g, Geo g2, const uint16_t *__restrict__ X,
+                                                           float *__restrict__ Y, int64_t N, int act)
 {
+    static_assert(!GLU || R == 2, "gate and up rows");
     constexpr int SLOTS = 64 * CPT;           // chunk slots per row
     constexpr bool SUMS = FMT != FMT_Q8_0;    // bias-correction sums (Q4K, Q6K)
     constexpr int XU = M * CPT;               // uint4 of X staged per thread
@@ -537,7 +557,7 @@ __global__ __launch_bounds__(64 * LW) void gemv_lds_kernel(Geo g, const uint16_t
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int S = g.K / 32;
-    const int64_t n0 = ((int64_t)blockIdx.x * LW + wv) * R;
+    const int64_t n0 = ((int64_t)blockIdx.x * LW + wv) * (GLU ? 1 : R);
 
     // X first, so that waiting for it never waits for the weights
     uint4 xs[XU];
@@ -553,11 +573,11 @@ __global__ __launch_bounds__(64 * LW) void gemv_lds_kernel(Geo g, const uint16_t
     WLoad<FMT> w[R][CPT];
 #pragma unroll
     for (int r = 0; r < R; r++) {
-        const int64_t n = n0 + r < N ? n0 + r : N - 1;
+        const int64_t n = GLU ? (n0 < N ? n0 : N - 1) : (n0 + r < N ? n0 + r : N - 1);
 #pragma unroll
         for (int i = 0; i < CPT; i++) {
             const int c = lane + 64 * i;
-            load_w<FMT>(g, n, c < S ? c : S - 1, lane, w[r][i]);
+            load_w<FMT>(GLU && r == 1 ? g2 : g, n, c < S ? c : S - 1, lane, w[r][i]);
         }
     }
     // stage X and the chunk sums (four consecutive lanes hold one chunk)
@@ -638,7 +658,12 @@ __global__ __launch_bounds__(64 * LW) void gemv_lds_kernel(Geo g, const uint16_t
     }
     const float tot = butterfly_sum<V>(v, lane);
     const int idx = butterfly_index<V>(lane);
-    if (lane < V && idx < R * M) {
+    if constexpr (GLU) {
+        // gate of token m sits at index m, up at index M + m
+        const float up = __shfl(tot, butterfly_lane<V>(idx + M < V ? idx + M : idx));
+        if (lane < V && idx < M && n0 < N)
+            Y[(int64_t)idx * N + n0] = act_f32(act, tot) * up;
+    } else if (lane < V && idx < R * M) {
         const int r = idx / M, m = idx % M;
         if (n0 + r < N)
             Y[(int64_t)m * N + n0 + r] = tot;
@@ -652,7 +677,18 @@ hipError_t go_lds(const Geo &g, const uint16_t *X, float *Y, int64_t N, hipStrea
     // K = 5120 (the 131072 x 5120 head: 10 % faster than one), one above
     constexpr int R = M != 1 ? 1 : CPT <= 2 ? 2 : CPT == 3 ? 4 : 1;
     const int64_t grid = (N + LW * R - 1) / (LW * R);
-    hipLaunchKernelGGL((gemv_lds_kernel<FMT, M, CPT, R>), dim3((unsigned)grid), dim3(64 * LW), 0, s, g, X, Y, N);
+    hipLaunchKernelGGL((gemv_lds_kernel<FMT, M, CPT, R>), dim3((unsigned)grid), dim3(64 * LW), 0, s, g, g, X, Y, N,
+                       0);
+    return hipGetLastError();
+}
+
+// fused gated projection: one output per wave, gate and up rows together
+template <int FMT, int M, int CPT>
+hipError_t go_glu(const Geo &gg, const Geo &gu, const uint16_t *X, float *H, int64_t F, int act, hipStream_t s)
+{
+    const int64_t grid = (F + LW - 1) / LW;
+    hipLaunchKernelGGL((gemv_lds_kernel<FMT, M, CPT, 2, true>), dim3((unsigned)grid), dim3(64 * LW), 0, s, gg, gu, X,
+                       H, F, act);
     return hipGetLastError();
 }
 
@@ -742,7 +778,44 @@ hipError_t by_m(const Geo &g, const uint16_t *X, float *Y, int M, int64_t N, hip
     }
 }
 
+template <int FMT, int M>
+hipError_t glu_by_cpt(const Geo &gg, const Geo &gu, const uint16_t *X, float *H, int64_t F, int act, hipStream_t s)
+{
+    switch ((gg.K / 32 + 63) / 64) {
+    case 1: return go_glu<FMT, M, 1>(gg, gu, X, H, F, act, s);
+    case 2: return go_glu<FMT, M, 2>(gg, gu, X, H, F, act, s);
+    case 3: return go_glu<FMT, M, 3>(gg, gu, X, H, F, act, s);
+    case 4: return go_glu<FMT, M, 4>(gg, gu, X, H, F, act, s);
+    default: return hipErrorNotSupported;
+    }
+}
+
+template <int FMT>
+hipError_t glu_by_m(const Geo &gg, const Geo &gu, const uint16_t *X, float *H, int M, int64_t F, int act,
+                    hipStream_t s)
+{
+    if (M == 1)
+        return glu_by_cpt<FMT, 1>(gg, gu, X, H, F, act, s);
+    return glu_by_cpt<FMT, 2>(gg, gu, X, H, F, act, s);
+}
+
 }  // namespace
+
+bool glu_fused_fits(int M, int64_t K) { return M >= 1 && M <= 2 && K / 32 <= 256; }
+
+hipError_t launch_glu_fused(int fmt, const uint8_t *gate, const uint8_t *up, const uint16_t *X, float *H, int M,
+                            int64_t F, int64_t K, int act, hipStream_t s)
+{
+    if (!glu_fused_fits(M, K))
+        return hipErrorNotSupported;
+    const Planes p = planes_of(fmt, F, K);
+    const Geo gg{gate, p.scales, p.d, (int)K}, gu{up, p.scales, p.d, (int)K};
+    if (fmt == FMT_Q4K)
+        return glu_by_m<FMT_Q4K>(gg, gu, X, H, M, F, act, s);
+    if (fmt == FMT_Q6K)
+        return glu_by_m<FMT_Q6K>(gg, gu, X, H, M, F, act, s);
+    return glu_by_m<FMT_Q8_0>(gg, gu, X, H, M, F, act, s);
+}
 
 hipError_t launch_gemv(int fmt, const uint8_t *blocks, const uint16_t *X, float *Y, int M,
                        int64_t N, int64_t K, hipStream_t s)

@@ -55,6 +55,17 @@ __device__ __forceinline__ void lds_barrier()
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Activations of the gated projection, evaluated in fp32 by the fused
+// kernel and by the unfused elementwise pass alike: 0 SiLU g / (1 + e^-g),
+// 1 ReLU max(g, 0), 2 sigmoid 1 / (1 + e^-g).
+__device__ __forceinline__ float act_f32(int act, float g)
+{
+    if (act == 1)
+        return g > 0.0f ? g : 0.0f;
+    const float e = 1.0f + expf(-g);
+    return act == 0 ? g / e : 1.0f / e;
+}
+
 hipError_t launch_isq(int fmt, const uint16_t *W, int64_t N, int64_t K, uint8_t *out,
                       hipStream_t s);
 hipError_t launch_dequant(int fmt, const uint8_t *blocks, int64_t N, int64_t K, float *W,
@@ -63,6 +74,10 @@ hipError_t launch_embed(int fmt, const uint8_t *blocks, int64_t N, int64_t K, co
                         int64_t n_ids, float *out, hipStream_t s);
 hipError_t launch_gemv(int fmt, const uint8_t *blocks, const uint16_t *X, float *Y, int M,
                        int64_t N, int64_t K, hipStream_t s);
+bool glu_fused_fits(int M, int64_t K);
+hipError_t launch_glu_fused(int fmt, const uint8_t *gate, const uint8_t *up, const uint16_t *X, float *H, int M,
+                            int64_t F, int64_t K, int act, hipStream_t s);
+hipError_t launch_glu_apply(const float *G, float *H, int64_t n, int act, hipStream_t s);
 hipError_t launch_gemm_bf16(int fmt, const uint8_t *blocks, const uint16_t *X, float *Y,
                             int64_t M, int64_t N, int64_t K, hipStream_t s);
 hipError_t launch_gemm_i8(const uint8_t *wblocks, const uint8_t *xblocks, float *Y, int64_t M,

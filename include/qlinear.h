@@ -143,6 +143,27 @@ int qmatmul_ex(int fmt, const void *blocks, const void *X_bf16, float *Y_fp32, i
                int64_t N, int64_t K, int path, void *workspace, size_t workspace_bytes,
                void *stream);
 
+/* Gated feed-forward projection (page "Quantization types", section
+ * "NVFP4": compatible gated feed-forward projections fuse the activation
+ * and the multiplication, keeping the activation and product rounding of
+ * the unfused path, for SiLU, ReLU and sigmoid):
+ *   H[m][f] = act(G[m][f]) * U[m][f],  G = X . deq(Wg)^T,  U = X . deq(Wu)^T,
+ * with G and U accumulated in fp32 and act(g) = g / (1 + e^-g) (SiLU),
+ * max(g, 0) (ReLU) or 1 / (1 + e^-g) (sigmoid) evaluated in fp32.
+ * gate_blocks / up_blocks: device, isq_quantize(fmt, W, F, K) of the [F][K]
+ * gate and up weights (a packed [2F][K] checkpoint tensor is quantized as
+ * its two halves).  X_bf16: device [M][K].  H_fp32: device [M][F],
+ * overwritten.  For M <= 2 and K <= 8192 one fused kernel computes the
+ * gate and up rows of each output together and needs no workspace;
+ * otherwise G goes through `workspace` (qmatmul_glu_workspace_bytes bytes,
+ * 16-byte aligned; Q_EINVAL without it) and U through H, followed by an
+ * elementwise pass with the same fp32 expression. */
+enum { QACT_SILU = 0, QACT_RELU = 1, QACT_SIGMOID = 2 };
+size_t qmatmul_glu_workspace_bytes(int fmt, int64_t M, int64_t F, int64_t K);
+int qmatmul_glu(int fmt, const void *gate_blocks, const void *up_blocks, const void *X_bf16, float *H_fp32,
+                int64_t M, int64_t F, int64_t K, int act, void *workspace, size_t workspace_bytes,
+                void *stream);
+
 /* Quantized embedding lookup (page "Quantization types", section
  * "Sensitive tensor precision": token embeddings are stored quantized, and
  * a tied output head reuses the embedding instead of a second copy -- the

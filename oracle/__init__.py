@@ -68,6 +68,7 @@ def _L():
             "oracle_matmul_a16": [P, P, I, I, I, P, P],
             "oracle_matmul_a16_pairs": [P, P, I, P, P, I, P, P],
             "oracle_matmul_a8": [P, P, P, P, I, I, I, P, P, I, P, P],
+            "oracle_glu": [P, P, P, P, I, I, P, P],
             "oracle_pack_q8_0": [P, P, I, I, P],
             "oracle_unpack_q8_0": [P, I, I, P, P],
             "oracle_pack_q4k": [P, P, P, P, P, I, I, P],
@@ -343,6 +344,33 @@ def matmul_a8(fw: dict, fx: dict, M: int, N: int, K: int, mi=None, ni=None):
     if full:
         return Y.reshape(M, N), den.reshape(M, N)
     return Y, den
+
+
+ACTS = {"silu": 0, "relu": 1, "sigmoid": 2}
+
+
+def glu_act(act: str, g, u, eg=None, eu=None):
+    """h = act(g) * u in fp64 (oracle.c: oracle_glu) and the bound on
+    |h' - h| for any g', u' within eg, eu of g, u (zeros when omitted)."""
+    g = _c(np.asarray(g, np.float64), np.float64)
+    u = _c(np.asarray(u, np.float64), np.float64)
+    eg = _c(np.zeros_like(g) if eg is None else np.asarray(eg, np.float64), np.float64)
+    eu = _c(np.zeros_like(u) if eu is None else np.asarray(eu, np.float64), np.float64)
+    h = np.empty_like(g)
+    bound = np.empty_like(g)
+    _L().oracle_glu(_p(g), _p(u), _p(eg), _p(eu), g.size, ACTS[act], _p(h), _p(bound))
+    return h, bound
+
+
+def glu(Wg: np.ndarray, Wu: np.ndarray, x_bf16: np.ndarray, act: str):
+    """Gated projection of bf16 x [M][K] with exact dequantized gate and up
+    weights [F][K]: returns h* = act(g*) u* and its normaliser, the bound
+    on |h - h*| when g and u each carry the matmul error bar (1 per unit of
+    sum_k |w||x|); a GPU result passes when |h - h*| <= 1e-3 * normaliser
+    (zero normaliser: h must be exactly 0)."""
+    g, dg = matmul_a16(Wg, x_bf16)
+    u, du = matmul_a16(Wu, x_bf16)
+    return glu_act(act, g, u, dg, du)
 
 
 def normalized_error(y_gpu, y_ref, den) -> np.ndarray:

@@ -403,6 +403,34 @@ void oracle_matmul_a16_pairs(const double *W, const uint16_t *x16, int64_t K,
     }
 }
 
+/* Gated feed-forward projection (page "Quantization types", section
+ * "NVFP4": gated feed-forward projections with SiLU, ReLU or sigmoid):
+ * h = act(g) * u in fp64 on the fp64 projections g and u, with
+ * act 0: SiLU g / (1 + exp(-g)); 1: ReLU max(g, 0); 2: sigmoid 1 / (1 + exp(-g)).
+ * Also a bound on |h' - h| when g' and u' are within eg and eu of g and u:
+ * |act(g') u' - act(g) u| <= |act(g') - act(g)| |u'| + |act(g)| |u' - u|
+ *                         <= L eg (|u| + eu) + |act(g)| eu,
+ * with L = 1.1, 1 and 1/4 bounding |act'| (SiLU's derivative lies in
+ * (-0.1, 1.1)). */
+static double act64(int act, double g)
+{
+    if (act == 1)
+        return g > 0.0 ? g : 0.0;
+    double e = 1.0 + exp(-g);
+    return act == 0 ? g / e : 1.0 / e;
+}
+
+void oracle_glu(const double *g, const double *u, const double *eg, const double *eu, int64_t n, int64_t act,
+                double *h, double *bound)
+{
+    const double L = act == 0 ? 1.1 : (act == 1 ? 1.0 : 0.25);
+    for (int64_t i = 0; i < n; i++) {
+        double a = act64((int)act, g[i]);
+        h[i] = a * u[i];
+        bound[i] = L * eg[i] * (fabs(u[i]) + eu[i]) + fabs(a) * eu[i];
+    }
+}
+
 /* A8 oracle (activations quantized to Q8_0 as well):
  *   Y[m][n] = sum_b dw[n][b] * dx[m][b] * (sum_{i in b} qw * qx)
  * with the integer block sums exact in int64 and the rest in fp64.

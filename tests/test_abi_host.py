@@ -158,3 +158,28 @@ def test_embed_argument_errors():
     assert call(n=-1) == ql.Q_ESHAPE
     assert call(n=(1 << 24) + 1) == ql.Q_ESHAPE
     assert call(n=0) == ql.Q_OK                              # nothing to launch
+
+
+def test_glu_argument_errors_and_workspace_sizes():
+    L = ql.lib()
+
+    def call(fmt=1, g=A, u=A2, x=A3, h=A, M=1, F=64, K=256, act=0, ws=NULL, wsb=0):
+        return L.qmatmul_glu(fmt, g, u, x, h, M, F, K, act, ws, wsb, NULL)
+
+    assert call(g=NULL) == ql.Q_EINVAL
+    assert call(u=NULL) == ql.Q_EINVAL
+    assert call(x=NULL) == ql.Q_EINVAL
+    assert call(h=NULL) == ql.Q_EINVAL
+    assert call(u=MIS) == ql.Q_EALIGN
+    assert call(fmt=5) == ql.Q_ENOTSUP
+    assert call(act=3) == ql.Q_EINVAL
+    assert call(act=-1) == ql.Q_EINVAL
+    assert call(K=100) == ql.Q_ESHAPE
+    assert call(M=0) == ql.Q_ESHAPE
+    assert call(M=3) == ql.Q_EINVAL                          # two-matmul path without a workspace
+    assert call(M=3, ws=A2, wsb=4 * 3 * 64 - 1) == ql.Q_EINVAL
+    assert call(M=3, ws=MIS, wsb=1 << 20) == ql.Q_EALIGN
+    assert ql.glu_workspace_bytes("q4k", 2, 64, 8192) == 0   # fused kernel
+    assert ql.glu_workspace_bytes("q4k", 3, 64, 256) == 4 * 3 * 64
+    assert ql.glu_workspace_bytes("q4k", 1, 64, 8448) == 4 * 64
+    assert ql.glu_workspace_bytes("q2k", 1, 64, 256) == 0

@@ -455,3 +455,44 @@ def test_matmul_a8_close_to_a16_on_random_activations():
 def test_normalized_error_zero_denominator():
     e = oracle.normalized_error([0.0, 1e-30, 2.0], [0.0, 0.0, 1.0], [0.0, 0.0, 4.0])
     assert e[0] == 0 and np.isinf(e[1]) and e[2] == 0.25
+
+
+@pytest.mark.parametrize("act", ["silu", "relu", "sigmoid"])
+def test_glu_activations_closed_forms(act):
+    """The gated projection's activations against forms written with tanh
+    (an independent library routine): sigmoid(x) = (1 + tanh(x/2)) / 2,
+    SiLU(x) = x sigmoid(x); ReLU by cases; h = act(g) * u."""
+    import math
+    g = np.array([0.0, 1e-8, -1e-8, 0.5, -0.5, 1.0, -1.0, 3.0, -3.0, 20.0, -20.0, 40.0, -40.0, 700.0, -700.0])
+    u = np.linspace(-2.0, 3.0, g.size)
+    h, bound = oracle.glu_act(act, g, u)
+    assert not bound.any()
+    for gi, ui, hi in zip(g, u, h):
+        sig = (1.0 + math.tanh(gi / 2.0)) / 2.0
+        a = {"silu": gi * sig, "relu": max(gi, 0.0), "sigmoid": sig}[act]
+        assert abs(hi - a * ui) <= 1e-15 * max(1.0, abs(a * ui)), (act, gi, ui, hi, a * ui)
+    if act == "silu":
+        hp, _ = oracle.glu_act(act, g, np.ones_like(g))
+        hm, _ = oracle.glu_act(act, -g, np.ones_like(g))
+        assert np.allclose(hp - hm, g, rtol=1e-15, atol=1e-300)   # SiLU(x) - SiLU(-x) = x
+    if act == "sigmoid":
+        assert oracle.glu_act(act, [0.0], [1.0])[0][0] == 0.5
+
+
+@pytest.mark.parametrize("act", ["silu", "relu", "sigmoid"])
+def test_glu_error_bound_holds(act):
+    """The stated bound holds for perturbations of g and u up to eg and eu
+    (random points, including kinks of ReLU at 0), and matches a hand value."""
+    rng = np.random.default_rng(11)
+    g = np.concatenate([rng.normal(0, 3, 2000), [0.0, 0.0, -1e-3]])
+    u = rng.normal(0, 2, g.size)
+    eg = np.abs(rng.normal(0, 0.05, g.size))
+    eu = np.abs(rng.normal(0, 0.05, g.size))
+    h, bound = oracle.glu_act(act, g, u, eg, eu)
+    for sg in (-1, 1):
+        for su in (-1, 1):
+            h2, _ = oracle.glu_act(act, g + sg * eg * rng.random(g.size), u + su * eu * rng.random(g.size))
+            assert np.all(np.abs(h2 - h) <= bound * (1 + 1e-12) + 1e-300), act
+    if act == "relu":
+        # g = 2, u = 3, eg = 0.1, eu = 0.2: 1 * 0.1 * (3 + 0.2) + 2 * 0.2 = 0.72
+        assert abs(oracle.glu_act(act, [2.0], [3.0], [0.1], [0.2])[1][0] - 0.72) < 1e-15
