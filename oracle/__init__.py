@@ -24,6 +24,11 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 FORMATS = ("q8_0", "q4k", "q6k")
+# further formats (oracle.c, "Further formats"): K-quants and the legacy
+# 32-element types, with the public header's format numbers
+KQ_FORMATS = {"q5k": 5, "q3k": 4, "q2k": 3}
+LEG_FORMATS = {"q4_0": 7, "q4_1": 8, "q5_0": 9, "q5_1": 10}
+MORE_FORMATS = tuple(KQ_FORMATS) + tuple(LEG_FORMATS)
 
 
 def build(force: bool = True) -> str:
@@ -69,6 +74,14 @@ def _L():
             "oracle_matmul_a16_pairs": [P, P, I, P, P, I, P, P],
             "oracle_matmul_a8": [P, P, P, P, I, I, I, P, P, I, P, P],
             "oracle_glu": [P, P, P, P, I, I, P, P],
+            "oracle_quantize_kq": [I, P, I, I, P, P, P, P, P],
+            "oracle_dequant_kq": [I, P, P, P, P, P, I, P],
+            "oracle_quantize_leg": [I, P, I, I, P, P, P],
+            "oracle_dequant_leg": [I, P, P, P, I, P],
+            "oracle_pack_kq": [I, P, P, P, P, P, I, I, P],
+            "oracle_unpack_kq": [I, P, I, I, P, P, P, P, P],
+            "oracle_pack_leg": [I, P, P, P, I, I, P],
+            "oracle_unpack_leg": [I, P, I, I, P, P, P],
             "oracle_pack_q8_0": [P, P, I, I, P],
             "oracle_unpack_q8_0": [P, I, I, P, P],
             "oracle_pack_q4k": [P, P, P, P, P, I, I, P],
@@ -80,6 +93,8 @@ def _L():
             fn = getattr(lib, name)
             fn.restype = None
             fn.argtypes = args
+        lib.oracle_more_layout.restype = ctypes.c_int64
+        lib.oracle_more_layout.argtypes = [I, I, I, P]
         _lib = lib
     return _lib
 
@@ -152,6 +167,13 @@ def quantize(fmt: str, w_bf16: np.ndarray) -> dict:
         q = np.empty((rows, cols), np.int8)
         L.oracle_quantize_q8_0(_p(w), rows, cols, _p(d16), _p(q))
         return {"d16": d16, "q": q}
+    if fmt in LEG_FORMATS:
+        assert cols % 32 == 0
+        d16 = np.empty((rows, cols // 32), np.uint16)
+        m16 = np.empty((rows, cols // 32), np.uint16)
+        q = np.empty((rows, cols), np.int8)
+        L.oracle_quantize_leg(LEG_FORMATS[fmt], _p(w), rows, cols, _p(d16), _p(m16), _p(q))
+        return {"d16": d16, "m16": m16, "q": q}
     assert cols % 256 == 0
     G = rows * cols // 256
     if fmt == "q4k":
@@ -168,13 +190,37 @@ def quantize(fmt: str, w_bf16: np.ndarray) -> dict:
         q = np.empty((rows, cols), np.int8)
         L.oracle_quantize_q6k(_p(w), rows, cols, _p(d16), _p(sc), _p(q))
         return {"d16": d16, "sc": sc, "q": q}
+    if fmt in KQ_FORMATS:
+        d16 = np.empty(G, np.uint16)
+        dmin16 = np.empty(G, np.uint16)
+        sc = np.empty((G, 16), np.uint8)
+        mq = np.empty((G, 16), np.uint8)
+        q = np.empty((rows, cols), np.int8)
+        L.oracle_quantize_kq(KQ_FORMATS[fmt], _p(w), rows, cols, _p(d16), _p(dmin16), _p(sc), _p(mq), _p(q))
+        return {"d16": d16, "dmin16": dmin16, "sc": sc, "mq": mq, "q": q}
+    if fmt in LEG_FORMATS:
+        d16 = np.empty((rows, cols // 32), np.uint16)
+        m16 = np.empty((rows, cols // 32), np.uint16)
+        q = np.empty((rows, cols), np.int8)
+        L.oracle_quantize_leg(LEG_FORMATS[fmt], _p(w), rows, cols, _p(d16), _p(m16), _p(q))
+        return {"d16": d16, "m16": m16, "q": q}
     raise ValueError(fmt)
+
+
+def more_layout(fmt: str, rows: int, cols: int):
+    """(plane offsets, total bytes) of a further format's planar buffer."""
+    o = np.zeros(4, np.int64)
+    fid = KQ_FORMATS.get(fmt, LEG_FORMATS.get(fmt))
+    total = _L().oracle_more_layout(fid, rows, cols, _p(o))
+    return [int(v) for v in o], int(total)
 
 
 def blocks_bytes(fmt: str, rows: int, cols: int) -> int:
     """Bytes of the planar buffer: 34/32, 144/256, 210/256 bytes per element;
     the Q6K buffer is zero-padded to a multiple of 16 bytes."""
     n = rows * cols
+    if fmt in MORE_FORMATS:
+        return more_layout(fmt, rows, cols)[1]
     if fmt == "q6k":
         return (n * 210 // 256 + 15) // 16 * 16
     return {"q8_0": n * 34 // 32, "q4k": n * 144 // 256}[fmt]
@@ -192,6 +238,13 @@ def pack(fmt: str, f: dict, rows: int, cols: int) -> np.ndarray:
                           _p(_c(f["q"], np.uint8)), rows, cols, _p(buf))
     elif fmt == "q6k":
         L.oracle_pack_q6k(_p(_c(f["d16"], np.uint16)), _p(_c(f["sc"], np.int8)),
+                          _p(_c(f["q"], np.int8)), rows, cols, _p(buf))
+    elif fmt in KQ_FORMATS:
+        L.oracle_pack_kq(KQ_FORMATS[fmt], _p(_c(f["d16"], np.uint16)), _p(_c(f["dmin16"], np.uint16)),
+                         _p(_c(f["sc"], np.uint8)), _p(_c(f["mq"], np.uint8)), _p(_c(f["q"], np.int8)),
+                         rows, cols, _p(buf))
+    elif fmt in LEG_FORMATS:
+        L.oracle_pack_leg(LEG_FORMATS[fmt], _p(_c(f["d16"], np.uint16)), _p(_c(f["m16"], np.uint16)),
                           _p(_c(f["q"], np.int8)), rows, cols, _p(buf))
     else:
         raise ValueError(fmt)
@@ -223,6 +276,20 @@ def unpack(fmt: str, buf: np.ndarray, rows: int, cols: int) -> dict:
         q = np.empty((rows, cols), np.int8)
         L.oracle_unpack_q6k(_p(b), rows, cols, _p(d16), _p(sc), _p(q))
         return {"d16": d16, "sc": sc, "q": q}
+    if fmt in KQ_FORMATS:
+        d16 = np.empty(G, np.uint16)
+        dmin16 = np.empty(G, np.uint16)
+        sc = np.empty((G, 16), np.uint8)
+        mq = np.empty((G, 16), np.uint8)
+        q = np.empty((rows, cols), np.int8)
+        L.oracle_unpack_kq(KQ_FORMATS[fmt], _p(b), rows, cols, _p(d16), _p(dmin16), _p(sc), _p(mq), _p(q))
+        return {"d16": d16, "dmin16": dmin16, "sc": sc, "mq": mq, "q": q}
+    if fmt in LEG_FORMATS:
+        d16 = np.empty((rows, cols // 32), np.uint16)
+        m16 = np.empty((rows, cols // 32), np.uint16)
+        q = np.empty((rows, cols), np.int8)
+        L.oracle_unpack_leg(LEG_FORMATS[fmt], _p(b), rows, cols, _p(d16), _p(m16), _p(q))
+        return {"d16": d16, "m16": m16, "q": q}
     raise ValueError(fmt)
 
 
@@ -239,6 +306,13 @@ def dequant(fmt: str, f: dict, rows: int, cols: int) -> np.ndarray:
                              _p(_c(f["q"], np.uint8)), n, _p(out))
     elif fmt == "q6k":
         L.oracle_dequant_q6k(_p(_c(f["d16"], np.uint16)), _p(_c(f["sc"], np.int8)),
+                             _p(_c(f["q"], np.int8)), n, _p(out))
+    elif fmt in KQ_FORMATS:
+        L.oracle_dequant_kq(KQ_FORMATS[fmt], _p(_c(f["d16"], np.uint16)), _p(_c(f["dmin16"], np.uint16)),
+                            _p(_c(f["sc"], np.uint8)), _p(_c(f["mq"], np.uint8)), _p(_c(f["q"], np.int8)),
+                            n, _p(out))
+    elif fmt in LEG_FORMATS:
+        L.oracle_dequant_leg(LEG_FORMATS[fmt], _p(_c(f["d16"], np.uint16)), _p(_c(f["m16"], np.uint16)),
                              _p(_c(f["q"], np.int8)), n, _p(out))
     else:
         raise ValueError(fmt)

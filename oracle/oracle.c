@@ -668,3 +668,413 @@ void oracle_unpack_q6k(const uint8_t *buf, int64_t rows, int64_t cols, uint16_t 
         d16[g] = (uint16_t)(D[2 * g] | D[2 * g + 1] << 8);
     }
 }
+
+/* ------------------------------------------------------------------ */
+/* Further formats: Q5K, Q3K, Q2K and Q4_0, Q4_1, Q5_0, Q5_1           */
+/* ------------------------------------------------------------------ */
+/*
+ * Page "Quantization types": section "Numeric shorthands" resolves ISQ
+ * levels 5, 3 and 2 to Q5K, Q3K and Q2K on CUDA / CPU; sections "Q*K
+ * family" (q2k 2, q3k 3, q5k 5 bits) and "Legacy GGML types" (q4_0/q4_1
+ * 4 bits, q5_0/q5_1 5 bits) name the formats.  The page gives bit widths
+ * only.  Readings, chosen to match the Q4K / Q6K / Q8_0 readings above and
+ * to keep the GGML byte counts (Q5K 176, Q3K 110, Q2K 84 bytes per 256
+ * elements; Q4_0 18, Q4_1 20, Q5_0 22, Q5_1 24 bytes per 32):
+ *   K-quants, groups of 256:
+ *     Q5K: 8 sub-blocks of 32, affine (the Q4K rule with 5-bit codes and
+ *          s_j = (hi - lo) / 31), 6-bit sc/m, fp16 d and dmin.
+ *     Q3K: 16 sub-blocks of 16, symmetric (the Q6K rule with 3-bit codes:
+ *          s_j = max|x| / 3, codes in [-4, 3]), 6-bit sc (d = max s / 63).
+ *     Q2K: 16 sub-blocks of 16, affine (s_j = (hi - lo) / 3, codes in
+ *          [0, 3]), 4-bit sc/m (d = max s / 15, dmin = max m / 15).
+ *   Legacy, blocks of 32:
+ *     Q4_0 / Q5_0: symmetric, d = F16(max|x| / 7 or / 15) (as Q8_0's
+ *          max|x| / 127), codes RHA(x / d) in [-8, 7] / [-16, 15].
+ *     Q4_1 / Q5_1: affine on the true min and max, d = F16((max - min) /
+ *          15 or 31), m = F16(min) (signed, clamped to +-65504), codes
+ *          RHA((x - m) / d) in [0, 15] / [0, 31]; decoded as d q + m.
+ * Every step is binary32, one operation at a time, as for the formats
+ * above; d = 0 (or S_j = 0) gives codes 0.
+ */
+
+#define FMT_Q2K 3
+#define FMT_Q3K 4
+#define FMT_Q5K 5
+#define FMT_Q4_0 7
+#define FMT_Q4_1 8
+#define FMT_Q5_0 9
+#define FMT_Q5_1 10
+
+/* K-quant parameters: sub-blocks, their length, code bits, affine?, scale bits */
+static void kq_params(int64_t fmt, int *ns, int *len, int *bits, int *affine, int *sbits)
+{
+    if (fmt == FMT_Q5K) {
+        *ns = 8; *len = 32; *bits = 5; *affine = 1; *sbits = 6;
+    } else if (fmt == FMT_Q3K) {
+        *ns = 16; *len = 16; *bits = 3; *affine = 0; *sbits = 6;
+    } else {
+        *ns = 16; *len = 16; *bits = 2; *affine = 1; *sbits = 4;
+    }
+}
+
+/* One K-quant group.  Affine: per sub-block lo = min(0, min x), hi = max x,
+ * s = (hi - lo) / (2^b - 1), m = 0 - lo; symmetric: s = max|x| /
+ * (2^(b-1) - 1).  Then d16 = F16(max s / (2^sb - 1)), dmin16 likewise from
+ * m, sc/mq = clamp(RHA(s / d), 0, 2^sb - 1), S = d sc, M = dmin mq (exact),
+ * codes clamp(RHA((x + M) / S), 0, 2^b - 1) or clamp(RHA(x / S),
+ * -2^(b-1), 2^(b-1) - 1). */
+static void kq_group(int64_t fmt, const uint16_t *x16, uint16_t *d16o, uint16_t *dm16o, uint8_t *sc,
+                     uint8_t *mq, int8_t *q)
+{
+    int ns, len, bits, affine, sbits;
+    kq_params(fmt, &ns, &len, &bits, &affine, &sbits);
+    const float qden = affine ? (float)((1 << bits) - 1) : (float)((1 << (bits - 1)) - 1);
+    const float sden = (float)((1 << sbits) - 1);
+    float x[256], s[16], m[16];
+    for (int i = 0; i < 256; i++)
+        x[i] = bf16_in(x16[i]);
+    float smax = 0.0f, mmax = 0.0f;
+    for (int j = 0; j < ns; j++) {
+        if (affine) {
+            float lo = 0.0f, hi = x[len * j];
+            for (int i = 0; i < len; i++) {
+                float v = x[len * j + i];
+                if (v < lo)
+                    lo = v;
+                if (v > hi)
+                    hi = v;
+            }
+            s[j] = (hi - lo) / qden;
+            m[j] = 0.0f - lo;
+        } else {
+            float a = 0.0f;
+            for (int i = 0; i < len; i++) {
+                float ax = fabsf(x[len * j + i]);
+                if (ax > a)
+                    a = ax;
+            }
+            s[j] = a / qden;
+            m[j] = 0.0f;
+        }
+        if (s[j] > smax)
+            smax = s[j];
+        if (m[j] > mmax)
+            mmax = m[j];
+    }
+    uint16_t d16 = scale_f16(smax / sden);
+    uint16_t dm16 = affine ? scale_f16(mmax / sden) : 0;
+    float df = oracle_f32_from_f16(d16), dmf = oracle_f32_from_f16(dm16);
+    const int smaxc = (1 << sbits) - 1;
+    for (int j = 0; j < ns; j++) {
+        sc[j] = (uint8_t)(df > 0.0f ? clamp_code(roundf(s[j] / df), 0, smaxc) : 0);
+        mq[j] = (uint8_t)(affine && dmf > 0.0f ? clamp_code(roundf(m[j] / dmf), 0, smaxc) : 0);
+        float S = df * (float)sc[j];
+        float M = dmf * (float)mq[j];
+        for (int i = 0; i < len; i++) {
+            float v = x[len * j + i];
+            int c;
+            if (!(S > 0.0f))
+                c = 0;
+            else if (affine)
+                c = clamp_code(roundf((v + M) / S), 0, (1 << bits) - 1);
+            else
+                c = clamp_code(roundf(v / S), -(1 << (bits - 1)), (1 << (bits - 1)) - 1);
+            q[len * j + i] = (int8_t)c;
+        }
+    }
+    *d16o = d16;
+    *dm16o = dm16;
+}
+
+/* rows*cols bf16 (cols % 256 == 0) -> K-quant fields per group g: d16[g],
+ * dmin16[g] (0 for Q3K), sc[g][16], mq[g][16] (the first 8 used by Q5K;
+ * mq 0 for Q3K), q[rows][cols]. */
+void oracle_quantize_kq(int64_t fmt, const uint16_t *w, int64_t rows, int64_t cols, uint16_t *d16,
+                        uint16_t *dmin16, uint8_t *sc, uint8_t *mq, int8_t *q)
+{
+    int64_t ng = rows * (cols / 256);
+#pragma omp parallel for schedule(static)
+    for (int64_t g = 0; g < ng; g++) {
+        memset(sc + 16 * g, 0, 16);
+        memset(mq + 16 * g, 0, 16);
+        kq_group(fmt, w + 256 * g, d16 + g, dmin16 + g, sc + 16 * g, mq + 16 * g, q + 256 * g);
+    }
+}
+
+/* Exact values: affine (d sc_j) q - (dmin mq_j); symmetric (d sc_j) q. */
+void oracle_dequant_kq(int64_t fmt, const uint16_t *d16, const uint16_t *dmin16, const uint8_t *sc,
+                       const uint8_t *mq, const int8_t *q, int64_t n_elems, double *out)
+{
+    int ns, len, bits, affine, sbits;
+    kq_params(fmt, &ns, &len, &bits, &affine, &sbits);
+#pragma omp parallel for schedule(static)
+    for (int64_t e = 0; e < n_elems; e++) {
+        int64_t g = e / 256;
+        int j = (int)((e % 256) / len);
+        double S = (double)oracle_f32_from_f16(d16[g]) * (double)sc[16 * g + j];
+        double M = affine ? (double)oracle_f32_from_f16(dmin16[g]) * (double)mq[16 * g + j] : 0.0;
+        out[e] = S * (double)q[e] - M;
+    }
+}
+
+/* One legacy block of 32 (rule in the section comment). */
+static void leg_block(int64_t fmt, const uint16_t *x16, uint16_t *d16o, uint16_t *m16o, int8_t *q)
+{
+    const int bits = (fmt == FMT_Q4_0 || fmt == FMT_Q4_1) ? 4 : 5;
+    const int affine = fmt == FMT_Q4_1 || fmt == FMT_Q5_1;
+    float x[32];
+    for (int i = 0; i < 32; i++)
+        x[i] = bf16_in(x16[i]);
+    if (!affine) {
+        float a = 0.0f;
+        for (int i = 0; i < 32; i++)
+            if (fabsf(x[i]) > a)
+                a = fabsf(x[i]);
+        uint16_t d16 = scale_f16(a / (float)((1 << (bits - 1)) - 1));
+        float df = oracle_f32_from_f16(d16);
+        for (int i = 0; i < 32; i++)
+            q[i] = (int8_t)(df == 0.0f ? 0 : clamp_code(roundf(x[i] / df), -(1 << (bits - 1)), (1 << (bits - 1)) - 1));
+        *d16o = d16;
+        *m16o = 0;
+        return;
+    }
+    float lo = x[0], hi = x[0];
+    for (int i = 1; i < 32; i++) {
+        if (x[i] < lo)
+            lo = x[i];
+        if (x[i] > hi)
+            hi = x[i];
+    }
+    uint16_t d16 = scale_f16((hi - lo) / (float)((1 << bits) - 1));
+    float mc = lo < -65504.0f ? -65504.0f : (lo > 65504.0f ? 65504.0f : lo);
+    uint16_t m16 = oracle_f16_from_f32(mc);
+    float df = oracle_f32_from_f16(d16), mf = oracle_f32_from_f16(m16);
+    for (int i = 0; i < 32; i++)
+        q[i] = (int8_t)(df == 0.0f ? 0 : clamp_code(roundf((x[i] - mf) / df), 0, (1 << bits) - 1));
+    *d16o = d16;
+    *m16o = m16;
+}
+
+/* rows*cols bf16 (cols % 32 == 0) -> legacy fields per block b: d16[b],
+ * m16[b] (0 for the symmetric types), q[rows][cols]. */
+void oracle_quantize_leg(int64_t fmt, const uint16_t *w, int64_t rows, int64_t cols, uint16_t *d16,
+                         uint16_t *m16, int8_t *q)
+{
+    int64_t nb = rows * (cols / 32);
+#pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < nb; b++)
+        leg_block(fmt, w + 32 * b, d16 + b, m16 + b, q + 32 * b);
+}
+
+/* Exact values: d q (+ m for the affine types). */
+void oracle_dequant_leg(int64_t fmt, const uint16_t *d16, const uint16_t *m16, const int8_t *q,
+                        int64_t n_elems, double *out)
+{
+    const int affine = fmt == FMT_Q4_1 || fmt == FMT_Q5_1;
+#pragma omp parallel for schedule(static)
+    for (int64_t e = 0; e < n_elems; e++) {
+        double d = (double)oracle_f32_from_f16(d16[e / 32]);
+        double m = affine ? (double)oracle_f32_from_f16(m16[e / 32]) : 0.0;
+        out[e] = d * (double)q[e] + m;
+    }
+}
+
+/*
+ * Planar layouts of the further formats (G = rows*cols/256 groups, B =
+ * rows*cols/32 blocks; every plane starts at a multiple of 16 bytes, the
+ * buffer is zero-padded to one; codes are stored in natural element order):
+ *   Q5K  [L: G*128, element e of a group at byte e/2, low nibble for even e]
+ *        [H: G*32, high bit of element e at bit e%8 of byte e/8]
+ *        [S: G*16, the Q4K header: d, dmin, sc/mq low-nibble dwords, high-pair dword]
+ *   Q3K  [L: G*64, low 2 bits of u = q+4 of element e at bits 2(e%4) of byte e/4]
+ *        [H: G*32, bit 2 of u at bit e%8 of byte e/8]
+ *        [S: G*12, dwords: nibble j of dword 0 / 1 = sc_j & 15 for j < 8 / j >= 8,
+ *                  bits 2j..2j+1 of dword 2 = sc_j >> 4]
+ *        [D: at round16(108 G), G*2 fp16 d]
+ *   Q2K  [C: G*64, code of element e at bits 2(e%4) of byte e/4]
+ *        [S: G*16, byte j = sc_j | mq_j << 4]  [D: G*4, d then dmin]
+ *   Q4_0 / Q4_1  [C: B*16, u (= q+8 for Q4_0) of element i of a block at byte i/2,
+ *                 low nibble for even i] [D: B*2 fp16 d] [M: B*2 fp16 m (Q4_1)]
+ *   Q5_0 / Q5_1  [C: B*16 low nibbles of u (= q+16 for Q5_0)] [H: B*4, bit 4 of u
+ *                 at bit i of the block's dword] [D: B*2] [M: B*2 (Q5_1)]
+ */
+static int64_t up16(int64_t v) { return (v + 15) / 16 * 16; }
+
+/* plane offsets o[0..3] and total bytes */
+int64_t oracle_more_layout(int64_t fmt, int64_t rows, int64_t cols, int64_t *o)
+{
+    int64_t n = rows * cols, G = n / 256, B = n / 32;
+    o[0] = o[1] = o[2] = o[3] = 0;
+    switch (fmt) {
+    case FMT_Q5K: o[1] = 128 * G; o[2] = 160 * G; return 176 * G;
+    case FMT_Q3K: o[1] = 64 * G; o[2] = 96 * G; o[3] = up16(108 * G); return up16(o[3] + 2 * G);
+    case FMT_Q2K: o[1] = 64 * G; o[2] = 80 * G; return up16(84 * G);
+    case FMT_Q4_0: o[1] = 16 * B; return up16(18 * B);
+    case FMT_Q4_1: o[1] = 16 * B; o[2] = up16(18 * B); return up16(o[2] + 2 * B);
+    case FMT_Q5_0: o[1] = 16 * B; o[2] = up16(20 * B); return up16(o[2] + 2 * B);
+    default: /* Q5_1 */ o[1] = 16 * B; o[2] = up16(20 * B); o[3] = up16(o[2] + 2 * B); return up16(o[3] + 2 * B);
+    }
+}
+
+static void put_u16(uint8_t *p, uint16_t v)
+{
+    p[0] = (uint8_t)v;
+    p[1] = (uint8_t)(v >> 8);
+}
+static uint16_t get_u16(const uint8_t *p) { return (uint16_t)(p[0] | p[1] << 8); }
+
+/* K-quant fields -> bytes (buf zeroed by the caller) */
+void oracle_pack_kq(int64_t fmt, const uint16_t *d16, const uint16_t *dmin16, const uint8_t *sc,
+                    const uint8_t *mq, const int8_t *q, int64_t rows, int64_t cols, uint8_t *buf)
+{
+    int64_t o[4];
+    oracle_more_layout(fmt, rows, cols, o);
+    int64_t G = rows * cols / 256;
+    for (int64_t g = 0; g < G; g++) {
+        const int8_t *qg = q + 256 * g;
+        const uint8_t *s = sc + 16 * g, *m = mq + 16 * g;
+        if (fmt == FMT_Q5K) {
+            for (int e = 0; e < 256; e++) {
+                uint32_t u = (uint32_t)qg[e];
+                buf[o[0] + 128 * g + e / 2] |= (uint8_t)((u & 15u) << (4 * (e % 2)));
+                buf[o[1] + 32 * g + e / 8] |= (uint8_t)((u >> 4) << (e % 8));
+            }
+            uint8_t *h = buf + o[2] + 16 * g;
+            put_u16(h, d16[g]);
+            put_u16(h + 2, dmin16[g]);
+            uint32_t a = 0, b = 0, c = 0;
+            for (int j = 0; j < 8; j++) {
+                a |= (uint32_t)(s[j] & 15u) << (4 * j);
+                b |= (uint32_t)(m[j] & 15u) << (4 * j);
+                c |= (uint32_t)(s[j] >> 4) << (2 * j) | (uint32_t)(m[j] >> 4) << (16 + 2 * j);
+            }
+            put_u32(h + 4, a);
+            put_u32(h + 8, b);
+            put_u32(h + 12, c);
+        } else if (fmt == FMT_Q3K) {
+            for (int e = 0; e < 256; e++) {
+                uint32_t u = (uint32_t)(qg[e] + 4);
+                buf[o[0] + 64 * g + e / 4] |= (uint8_t)((u & 3u) << (2 * (e % 4)));
+                buf[o[1] + 32 * g + e / 8] |= (uint8_t)((u >> 2) << (e % 8));
+            }
+            uint32_t a = 0, b = 0, c = 0;
+            for (int j = 0; j < 16; j++) {
+                if (j < 8)
+                    a |= (uint32_t)(s[j] & 15u) << (4 * j);
+                else
+                    b |= (uint32_t)(s[j] & 15u) << (4 * (j - 8));
+                c |= (uint32_t)(s[j] >> 4) << (2 * j);
+            }
+            put_u32(buf + o[2] + 12 * g, a);
+            put_u32(buf + o[2] + 12 * g + 4, b);
+            put_u32(buf + o[2] + 12 * g + 8, c);
+            put_u16(buf + o[3] + 2 * g, d16[g]);
+        } else {
+            for (int e = 0; e < 256; e++)
+                buf[o[0] + 64 * g + e / 4] |= (uint8_t)(((uint32_t)qg[e] & 3u) << (2 * (e % 4)));
+            for (int j = 0; j < 16; j++)
+                buf[o[1] + 16 * g + j] = (uint8_t)(s[j] | m[j] << 4);
+            put_u16(buf + o[2] + 4 * g, d16[g]);
+            put_u16(buf + o[2] + 4 * g + 2, dmin16[g]);
+        }
+    }
+}
+
+void oracle_unpack_kq(int64_t fmt, const uint8_t *buf, int64_t rows, int64_t cols, uint16_t *d16,
+                      uint16_t *dmin16, uint8_t *sc, uint8_t *mq, int8_t *q)
+{
+    int64_t o[4];
+    oracle_more_layout(fmt, rows, cols, o);
+    int64_t G = rows * cols / 256;
+    for (int64_t g = 0; g < G; g++) {
+        int8_t *qg = q + 256 * g;
+        uint8_t *s = sc + 16 * g, *m = mq + 16 * g;
+        memset(s, 0, 16);
+        memset(m, 0, 16);
+        if (fmt == FMT_Q5K) {
+            for (int e = 0; e < 256; e++) {
+                uint32_t lo = (buf[o[0] + 128 * g + e / 2] >> (4 * (e % 2))) & 15u;
+                uint32_t hi = (buf[o[1] + 32 * g + e / 8] >> (e % 8)) & 1u;
+                qg[e] = (int8_t)(lo | hi << 4);
+            }
+            const uint8_t *h = buf + o[2] + 16 * g;
+            d16[g] = get_u16(h);
+            dmin16[g] = get_u16(h + 2);
+            uint32_t a = get_u32(h + 4), b = get_u32(h + 8), c = get_u32(h + 12);
+            for (int j = 0; j < 8; j++) {
+                s[j] = (uint8_t)(((a >> (4 * j)) & 15u) | ((c >> (2 * j)) & 3u) << 4);
+                m[j] = (uint8_t)(((b >> (4 * j)) & 15u) | ((c >> (16 + 2 * j)) & 3u) << 4);
+            }
+        } else if (fmt == FMT_Q3K) {
+            for (int e = 0; e < 256; e++) {
+                uint32_t lo = (buf[o[0] + 64 * g + e / 4] >> (2 * (e % 4))) & 3u;
+                uint32_t hi = (buf[o[1] + 32 * g + e / 8] >> (e % 8)) & 1u;
+                qg[e] = (int8_t)((int)(lo | hi << 2) - 4);
+            }
+            uint32_t a = get_u32(buf + o[2] + 12 * g), b = get_u32(buf + o[2] + 12 * g + 4),
+                     c = get_u32(buf + o[2] + 12 * g + 8);
+            for (int j = 0; j < 16; j++)
+                s[j] = (uint8_t)((((j < 8 ? a : b) >> (4 * (j % 8))) & 15u) | ((c >> (2 * j)) & 3u) << 4);
+            d16[g] = get_u16(buf + o[3] + 2 * g);
+            dmin16[g] = 0;
+        } else {
+            for (int e = 0; e < 256; e++)
+                qg[e] = (int8_t)((buf[o[0] + 64 * g + e / 4] >> (2 * (e % 4))) & 3u);
+            for (int j = 0; j < 16; j++) {
+                s[j] = buf[o[1] + 16 * g + j] & 15u;
+                m[j] = buf[o[1] + 16 * g + j] >> 4;
+            }
+            d16[g] = get_u16(buf + o[2] + 4 * g);
+            dmin16[g] = get_u16(buf + o[2] + 4 * g + 2);
+        }
+    }
+}
+
+void oracle_pack_leg(int64_t fmt, const uint16_t *d16, const uint16_t *m16, const int8_t *q, int64_t rows,
+                     int64_t cols, uint8_t *buf)
+{
+    int64_t o[4];
+    oracle_more_layout(fmt, rows, cols, o);
+    int64_t B = rows * cols / 32;
+    const int five = fmt == FMT_Q5_0 || fmt == FMT_Q5_1;
+    const int bias = fmt == FMT_Q4_0 ? 8 : (fmt == FMT_Q5_0 ? 16 : 0);
+    const int affine = fmt == FMT_Q4_1 || fmt == FMT_Q5_1;
+    for (int64_t b = 0; b < B; b++) {
+        uint32_t hib = 0;
+        for (int i = 0; i < 32; i++) {
+            uint32_t u = (uint32_t)(q[32 * b + i] + bias);
+            buf[o[0] + 16 * b + i / 2] |= (uint8_t)((u & 15u) << (4 * (i % 2)));
+            hib |= (u >> 4) << i;
+        }
+        if (five) {
+            put_u32(buf + o[1] + 4 * b, hib);
+            put_u16(buf + o[2] + 2 * b, d16[b]);
+            if (affine)
+                put_u16(buf + o[3] + 2 * b, m16[b]);
+        } else {
+            put_u16(buf + o[1] + 2 * b, d16[b]);
+            if (affine)
+                put_u16(buf + o[2] + 2 * b, m16[b]);
+        }
+    }
+}
+
+void oracle_unpack_leg(int64_t fmt, const uint8_t *buf, int64_t rows, int64_t cols, uint16_t *d16,
+                       uint16_t *m16, int8_t *q)
+{
+    int64_t o[4];
+    oracle_more_layout(fmt, rows, cols, o);
+    int64_t B = rows * cols / 32;
+    const int five = fmt == FMT_Q5_0 || fmt == FMT_Q5_1;
+    const int bias = fmt == FMT_Q4_0 ? 8 : (fmt == FMT_Q5_0 ? 16 : 0);
+    const int affine = fmt == FMT_Q4_1 || fmt == FMT_Q5_1;
+    for (int64_t b = 0; b < B; b++) {
+        uint32_t hib = five ? get_u32(buf + o[1] + 4 * b) : 0u;
+        for (int i = 0; i < 32; i++) {
+            uint32_t u = ((buf[o[0] + 16 * b + i / 2] >> (4 * (i % 2))) & 15u) | ((hib >> i) & 1u) << 4;
+            q[32 * b + i] = (int8_t)((int)u - bias);
+        }
+        d16[b] = get_u16(buf + (five ? o[2] : o[1]) + 2 * b);
+        m16[b] = affine ? get_u16(buf + (five ? o[3] : o[2]) + 2 * b) : 0;
+    }
+}

@@ -496,3 +496,159 @@ def test_glu_error_bound_holds(act):
     if act == "relu":
         # g = 2, u = 3, eg = 0.1, eu = 0.2: 1 * 0.1 * (3 + 0.2) + 2 * 0.2 = 0.72
         assert abs(oracle.glu_act(act, [2.0], [3.0], [0.1], [0.2])[1][0] - 0.72) < 1e-15
+
+
+# ----------------------------------------------------------------------------
+# further formats (oracle.c, "Further formats")
+# ----------------------------------------------------------------------------
+
+KQ_PARAMS = {"q5k": (8, 32, 5, True, 6), "q3k": (16, 16, 3, False, 6), "q2k": (16, 16, 2, True, 4)}
+LEG_PARAMS = {"q4_0": (4, False), "q5_0": (5, False), "q4_1": (4, True), "q5_1": (5, True)}
+
+
+def _ramp(rule, n):
+    if rule.startswith("x[32j+i]"):
+        return [float((i - 8) * (j + 1) * 2.0 ** -10) for j in range(8) for i in range(32)]
+    return [float((i - 8) * (j + 1) * 2.0 ** -6) for j in range(16) for i in range(16)]
+
+
+def test_more_formats_worked_blocks():
+    """Worked blocks of the seven further formats (tests/golden/more_formats_worked.json,
+    derived with IEEE binary32/binary16 steps and exact half-away rounding,
+    independently of oracle.c)."""
+    for blk in _golden("more_formats_worked.json")["blocks"]:
+        fmt = blk["name"]
+        x = blk["x"] if "x" in blk else _ramp(blk["rule"], 256)
+        w = _bf16(x)[None, :]
+        assert np.array_equal(synth.bf16_bits_to_f32(w[0]), np.float32(x)), fmt
+        f = oracle.quantize(fmt, w)
+        assert int(f["d16"].ravel()[0]) == _h(blk["d16"]), (fmt, hex(int(f["d16"].ravel()[0])))
+        assert np.array_equal(f["q"][0], np.array(blk["q"], np.int8)), (fmt, f["q"][0][:16])
+        if fmt in KQ_PARAMS:
+            ns = KQ_PARAMS[fmt][0]
+            assert int(f["dmin16"][0]) == _h(blk["dmin16"]), fmt
+            assert list(f["sc"][0][:ns]) == blk["sc"] and list(f["mq"][0][:ns]) == blk["mq"], fmt
+        else:
+            assert int(f["m16"].ravel()[0]) == _h(blk["m16"]), fmt
+
+
+def _f16v(bits):
+    return np.asarray(bits, np.uint16).view(np.float16).astype(np.float64)
+
+
+@pytest.mark.parametrize("fmt", list(KQ_PARAMS) + list(LEG_PARAMS))
+@pytest.mark.parametrize("outliers", [False, True])
+def test_more_formats_ranges_and_nearest_grid(fmt, outliers):
+    """Codes lie in range; every unclamped code is the nearest grid point
+    (|w - x| <= step/2, by brute force over all codes of the element's
+    sub-block or block); the largest sub-scale is the top scale code."""
+    rows, cols = 64, 512
+    w = synth.weights_bf16(7700 + outliers, rows, cols, outliers=outliers)
+    x = synth.bf16_bits_to_f32(w).astype(np.float64)
+    f = oracle.quantize(fmt, w)
+    W = oracle.dequant(fmt, f, rows, cols)
+    q = f["q"].astype(np.int64)
+    if fmt in KQ_PARAMS:
+        ns, ln, bits, affine, sbits = KQ_PARAMS[fmt]
+        lo, hi = (0, 2 ** bits - 1) if affine else (-(2 ** (bits - 1)), 2 ** (bits - 1) - 1)
+        G = rows * cols // 256
+        d = _f16v(f["d16"])[:, None]
+        dm = _f16v(f["dmin16"])[:, None]
+        S = (d * f["sc"][:, :ns]).repeat(ln, axis=1).reshape(rows, cols)
+        M = (dm * f["mq"][:, :ns]).repeat(ln, axis=1).reshape(rows, cols) if affine else 0 * S
+        assert f["sc"][:, :ns].max() <= 2 ** sbits - 1 and f["sc"].max(axis=1).min() == 2 ** sbits - 1
+        assert not f["sc"][:, ns:].any() and (affine or not f["mq"].any())
+    else:
+        bits, affine = LEG_PARAMS[fmt]
+        lo, hi = (0, 2 ** bits - 1) if affine else (-(2 ** (bits - 1)), 2 ** (bits - 1) - 1)
+        S = _f16v(f["d16"]).repeat(32, axis=1)
+        M = -_f16v(f["m16"]).repeat(32, axis=1) if affine else 0 * S
+    assert q.min() >= lo and q.max() <= hi
+    assert np.array_equal(W, S * q - M)
+    grid = S[..., None] * np.arange(lo, hi + 1)[None, None, :] - M[..., None]
+    best = np.abs(grid - x[..., None]).min(axis=-1)
+    err = np.abs(W - x)
+    # unclamped elements: the chosen code is a nearest grid point (ties aside, within fp32 slack)
+    inside = (x + M > S * (lo - 0.5)) & (x + M < S * (hi + 0.5)) & (S > 0)
+    assert np.all(err[inside] <= best[inside] + 1e-6 * S[inside])
+    assert np.all(err[inside] <= S[inside] * (0.5 + 2 ** -17))
+
+
+@pytest.mark.parametrize("fmt", list(KQ_PARAMS) + list(LEG_PARAMS))
+def test_more_formats_pack_roundtrip_and_bytes(fmt):
+    """Pack -> unpack is the identity on random fields over their full
+    ranges; single codes and scales land on the bytes and bits the layout
+    states (written out here by hand)."""
+    rows, cols = 3, 512
+    rng = np.random.default_rng(3)
+    if fmt in KQ_PARAMS:
+        ns, ln, bits, affine, sbits = KQ_PARAMS[fmt]
+        G = rows * cols // 256
+        lo, hi = (0, 2 ** bits - 1) if affine else (-(2 ** (bits - 1)), 2 ** (bits - 1) - 1)
+        f = {"d16": rng.integers(0, 0x7c00, G).astype(np.uint16),
+             "dmin16": rng.integers(0, 0x7c00, G).astype(np.uint16) if affine else np.zeros(G, np.uint16),
+             "sc": np.zeros((G, 16), np.uint8), "mq": np.zeros((G, 16), np.uint8),
+             "q": rng.integers(lo, hi + 1, (rows, cols)).astype(np.int8)}
+        f["sc"][:, :ns] = rng.integers(0, 2 ** sbits, (G, ns))
+        if affine:
+            f["mq"][:, :ns] = rng.integers(0, 2 ** sbits, (G, ns))
+    else:
+        bits, affine = LEG_PARAMS[fmt]
+        lo, hi = (0, 2 ** bits - 1) if affine else (-(2 ** (bits - 1)), 2 ** (bits - 1) - 1)
+        f = {"d16": rng.integers(0, 0x7c00, (rows, cols // 32)).astype(np.uint16),
+             "m16": rng.integers(0, 0xfc00, (rows, cols // 32)).astype(np.uint16) if affine
+             else np.zeros((rows, cols // 32), np.uint16),
+             "q": rng.integers(lo, hi + 1, (rows, cols)).astype(np.int8)}
+    buf = oracle.pack(fmt, f, rows, cols)
+    g = oracle.unpack(fmt, buf, rows, cols)
+    for k in f:
+        assert np.array_equal(f[k], g[k]), (fmt, k)
+
+    # one element at the top code, everything else at the code whose stored value is 0
+    n, G, B = rows * cols, rows * cols // 256, rows * cols // 32
+    zero_code = {"q5k": 0, "q3k": -4, "q2k": 0, "q4_0": -8, "q5_0": -16, "q4_1": 0, "q5_1": 0}[fmt]
+    e = 256 + 37   # group 1, element 37 (block 9, element 5)
+    q = np.full((rows, cols), zero_code, np.int8)
+    q.ravel()[e] = hi
+    h = dict(f, q=q)
+    for k in h:
+        if k != "q":
+            h[k] = np.zeros_like(h[k])
+    b = oracle.pack(fmt, h, rows, cols)
+    nz = {int(i): int(b[i]) for i in np.flatnonzero(b)}
+    if fmt == "q5k":      # low nibble plane: byte 128*1 + 37/2, high nibble; high-bit plane at 128G: byte 32 + 4, bit 5
+        assert nz == {128 + 18: 0xF0, 128 * G + 32 + 4: 1 << 5}
+    elif fmt == "q3k":    # u = 7: low 2 bits at byte 64 + 9, bits 2..3; bit 2 at plane 64G, byte 32 + 4, bit 5
+        assert nz == {64 + 9: 3 << 2, 64 * G + 32 + 4: 1 << 5}
+    elif fmt == "q2k":    # code 3 at byte 64 + 9, bits 2..3
+        assert nz == {64 + 9: 3 << 2}
+    elif fmt in ("q4_0", "q4_1"):   # u = 15 at byte 16*9 + 2, high nibble
+        assert nz == {16 * 9 + 2: 0xF0}
+    else:                 # u = 31: low nibble 15 at byte 16*9 + 2 (high half), high bit at plane 16B, dword 9, bit 5
+        assert nz == {16 * 9 + 2: 0xF0, 16 * B + 4 * 9 + 0: 1 << 5}
+    # scales: a value in the second group / tenth block
+    if fmt in KQ_PARAMS:
+        s = dict(h, q=np.full((rows, cols), zero_code, np.int8))
+        s["d16"] = np.zeros(G, np.uint16)
+        s["d16"][1] = 0x1234
+        s["sc"] = np.zeros((G, 16), np.uint8)
+        s["sc"][1, 3] = 2 ** sbits - 1
+        b = oracle.pack(fmt, s, rows, cols)
+        nz = {int(i): int(b[i]) for i in np.flatnonzero(b)}
+        if fmt == "q5k":   # header of group 1 at 160G + 16: d, sc low nibble 3 of dword 1, high pair 3 of dword 3
+            h0 = 160 * G + 16
+            assert nz == {h0: 0x34, h0 + 1: 0x12, h0 + 4 + 1: 0xF0, h0 + 12 + 0: 3 << 6}
+        elif fmt == "q3k":  # scales of group 1 at 96G + 12: nibble 3 of dword 0, pair 3 of dword 2; d at up16(108G) + 2
+            s0 = 96 * G + 12
+            d0 = (108 * G + 15) // 16 * 16 + 2
+            assert nz == {s0 + 1: 0xF0, s0 + 8: 3 << 6, d0: 0x34, d0 + 1: 0x12}
+        else:              # Q2K: byte 64G + 16 + 3 = sc | mq << 4; d at 80G + 4
+            assert nz == {64 * G + 16 + 3: 15, 80 * G + 4: 0x34, 80 * G + 5: 0x12}
+    else:
+        s = dict(h, q=np.full((rows, cols), zero_code, np.int8))
+        s["d16"] = np.zeros((rows, cols // 32), np.uint16)
+        s["d16"].ravel()[9] = 0x1234
+        b = oracle.pack(fmt, s, rows, cols)
+        nz = {int(i): int(b[i]) for i in np.flatnonzero(b)}
+        dplane = 16 * B if fmt in ("q4_0", "q4_1") else 20 * B
+        assert nz == {dplane + 18: 0x34, dplane + 19: 0x12}
