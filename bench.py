@@ -51,7 +51,7 @@ def parse():
     ap.add_argument("--quick", action="store_true", help="headline only (for profiling runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--parts", default=None,
-                    help="comma-separated parts measured after the headline: batched, glu, prefill, isq "
+                    help="comma-separated parts measured after the headline: batched, glu, formats, prefill, isq "
                          "(default: all of them, none with --quick)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only copy a buffer of BYTES bytes 10 times (the reference kernel that scales "
@@ -248,7 +248,8 @@ def main():
         "hbm_frac": round(q4["alg_GBps"] / HBM_PEAK_GBPS, 4), "parity_max_err": q4["parity_max_err"]}
     del W
 
-    which = set(args.parts.split(",")) if args.parts else (set() if args.quick else {"batched", "glu", "prefill", "isq"})
+    which = set(args.parts.split(",")) if args.parts else (set() if args.quick else
+                                                           {"batched", "glu", "formats", "prefill", "isq"})
     if which:
         parts.update(bench_parts(torch, ql, synth, dev, bf16_dev, which))
     result["parts"] = parts
@@ -351,6 +352,36 @@ def bench_parts(torch, ql, synth, dev, bf16_dev, which):
                 "hbm_frac": round(2 * bg.numel() / fused / 1e6 / HBM_PEAK_GBPS, 4)}
             log(f"  M={M}: fused {fused * 1e3:.2f} us, two GEMVs {sep * 1e3:.2f} us")
         del cg, cu, bg, bu, wg, wu
+        torch.cuda.empty_cache()
+
+    if "formats" in which:
+        # the further formats on the generic kernels, at the 14336 x 4096 shape:
+        # ISQ, one-token GEMV and a 16-token batch
+        log("further formats 14336x4096: ISQ, GEMV M=1, MFMA M=16")
+        N, K = 14336, 4096
+        W = bf16_dev(synth.weights_bf16(synth.seed_for(2, 0), N, K))
+        xs = bf16_dev(synth.activations_bf16(synth.seed_for(2, 1), 16, K))
+        rows = {}
+        for fmt in ("q5k", "q3k", "q2k", "q4_0", "q4_1", "q5_0", "q5_1"):
+            blocks = ql.isq(fmt, W)
+            nb = blocks.numel()
+            R = copies_for(nb)
+            copies = [blocks] + [blocks.clone() for _ in range(R - 1)]
+            out = torch.empty_like(blocks)
+            isq_ms = timed_calls(lambda i: ql.isq(fmt, W, out=out), 10)
+            Y1 = torch.empty((1, N), dtype=torch.float32, device=dev)
+            g1 = timed_calls(lambda i: ql.qmatmul(fmt, copies[i % R], xs[:1], N, out=Y1), 2 * R)
+            Y16 = torch.empty((16, N), dtype=torch.float32, device=dev)
+            g16 = timed_calls(lambda i: ql.qmatmul(fmt, copies[i % R], xs, N, out=Y16), 2 * R)
+            rows[fmt] = {"bytes": nb, "isq_us": round(isq_ms * 1e3, 1),
+                         "isq_GBps": round((W.numel() * 2 + nb) / isq_ms / 1e6, 1),
+                         "gemv_m1_us": round(g1 * 1e3, 2), "gemv_m1_weight_GBps": round(nb / g1 / 1e6, 1),
+                         "m16_us": round(g16 * 1e3, 2), "m16_weight_GBps": round(nb / g16 / 1e6, 1)}
+            log(f"  {fmt}: ISQ {isq_ms * 1e3:.0f} us, GEMV M=1 {g1 * 1e3:.2f} us ({nb / g1 / 1e6:.0f} GB/s), "
+                f"M=16 {g16 * 1e3:.2f} us")
+            del copies, blocks, out
+        parts["further_formats_14336x4096"] = rows
+        del W, xs
         torch.cuda.empty_cache()
 
     if "prefill" in which:

@@ -8,7 +8,10 @@
 
 namespace {
 
-bool implemented(int fmt) { return fmt == QFMT_Q8_0 || fmt == QFMT_Q4K || fmt == QFMT_Q6K; }
+bool implemented(int fmt)
+{
+    return fmt == QFMT_Q8_0 || fmt == QFMT_Q4K || fmt == QFMT_Q6K || ql::generic_fmt(fmt);
+}
 bool known(int fmt) { return fmt >= QFMT_Q8_0 && fmt <= QFMT_Q8_1; }
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -160,7 +163,7 @@ size_t qmatmul_glu_workspace_bytes(int fmt, int64_t M, int64_t F, int64_t K)
     if (!implemented(fmt) || M < 1 || M > QLINEAR_MAX_M || check_tensor(fmt, F, K, QLINEAR_MAX_N) != Q_OK ||
         K % 256 != 0 || M * F > kMaxElems)
         return 0;
-    return ql::glu_fused_fits((int)M, K) ? 0 : (size_t)(4 * M * F);
+    return ql::glu_fused_fits(fmt, (int)M, K) ? 0 : (size_t)(4 * M * F);
 }
 
 int qmatmul_glu(int fmt, const void *gate_blocks, const void *up_blocks, const void *X_bf16, float *H_fp32,
@@ -179,7 +182,7 @@ int qmatmul_glu(int fmt, const void *gate_blocks, const void *up_blocks, const v
     const auto *Bu = static_cast<const uint8_t *>(up_blocks);
     const auto *X = static_cast<const uint16_t *>(X_bf16);
     const hipStream_t s = as_stream(stream);
-    if (ql::glu_fused_fits((int)M, K))
+    if (ql::glu_fused_fits(fmt, (int)M, K))
         return status_of(ql::launch_glu_fused(fmt, Bg, Bu, X, H_fp32, (int)M, F, K, act, s));
     // two matmuls and the elementwise product: G in the workspace, U in H
     if (!workspace)

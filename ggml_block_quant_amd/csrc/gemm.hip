@@ -18,6 +18,7 @@
 // split K over gridDim.z with fp32 atomics into a zeroed Y when the (n, m)
 // tiles alone cannot fill the 256 CUs.
 #include "qlinear_internal.h"
+#include "decode.h"
 
 #include <type_traits>
 
@@ -1061,6 +1062,63 @@ __global__ __launch_bounds__(320) void gemm_bq_kernel(const uint8_t *__restrict_
 }
 
 // ---------------------------------------------------------------------------
+// Generic MFMA GEMM for the formats without a tuned kernel: a workgroup of
+// four waves owns 64 rows of W (16 per wave) and 16*TM tokens; K advances in
+// steps of 32.  Lane (g = l/16, r = l%16) decodes elements 8g..8g+7 of the
+// step in row r of its wave exactly (dequant8), rounds them to bf16 and uses
+// them as its B operand of v_mfma_f32_16x16x32_bf16; the A operand is the
+// same 8 elements of X read straight from memory.  K splits over gridDim.z
+// add into a zeroed Y with fp32 atomics.
+// ---------------------------------------------------------------------------
+template <int FMT, int TM>
+__global__ __launch_bounds__(256) void gemm_gen_kernel(const uint8_t *__restrict__ B, Planes p,
+                                                       const uint16_t *__restrict__ X, float *__restrict__ Y, int M,
+                                                       int N, int K, int steps_per_split)
+{
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int g = lane >> 4, r16 = lane & 15;
+    const int n = blockIdx.x * 64 + 16 * wv + r16;
+    const int64_t nr = min(n, N - 1);  // rows past N are decoded but not stored
+    const int m0 = blockIdx.y * 16 * TM;
+    const int s0 = blockIdx.z * steps_per_split, s1 = min(K / 32, s0 + steps_per_split);
+    f32x4_t acc[TM];
+#pragma unroll
+    for (int j = 0; j < TM; j++)
+        acc[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    const uint16_t *xr[TM];
+#pragma unroll
+    for (int j = 0; j < TM; j++)
+        xr[j] = X + (int64_t)min(m0 + 16 * j + r16, M - 1) * K;
+    for (int s = s0; s < s1; s++) {
+        float w[8];
+        dequant8<FMT>(B, p, nr * (K / 8) + 4 * s + g, w);
+        const bf16x8_t bw = __builtin_bit_cast(
+            bf16x8_t, make_uint4(pack_bf16(w[0], w[1]), pack_bf16(w[2], w[3]), pack_bf16(w[4], w[5]),
+                                 pack_bf16(w[6], w[7])));
+#pragma unroll
+        for (int j = 0; j < TM; j++) {
+            const bf16x8_t xa = *reinterpret_cast<const bf16x8_t *>(xr[j] + 32 * s + 8 * g);
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bw, acc[j], 0, 0, 0);
+        }
+    }
+    if (n >= N)
+        return;
+    const bool split = gridDim.z > 1;
+#pragma unroll
+    for (int j = 0; j < TM; j++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int m = m0 + 16 * j + 4 * g + i;
+            if (m < M) {
+                if (split)
+                    atomicAdd(Y + (int64_t)m * N + n, acc[j][i]);
+                else
+                    Y[(int64_t)m * N + n] = acc[j][i];
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------
 // Q8_0 x Q8_0 int8 path
 // ---------------------------------------------------------------------------
 constexpr int BN = 128;     // n tile
@@ -1380,11 +1438,58 @@ hipError_t bf16_by_m(const uint8_t *blocks, const Planes &p, const uint16_t *X, 
     return go_bf16<FMT, 8, 4>(blocks, p, X, Y, M, N, K, s);
 }
 
+
+template <int FMT, int TM>
+hipError_t go_gen(const uint8_t *blocks, const uint16_t *X, float *Y, int64_t M, int64_t N, int64_t K, hipStream_t s)
+{
+    const Planes p = planes_of(FMT, N, K);
+    const int64_t gx = (N + 63) / 64, gy = (M + 16 * TM - 1) / (16 * TM);
+    const int steps = (int)(K / 32);
+    int sp = 1;
+    while (gx * gy * sp < 512 && sp < 32 && steps / (2 * sp) >= 8)
+        sp *= 2;
+    const int per = (steps + sp - 1) / sp;
+    if (sp > 1) {
+        const hipError_t e = zero_y(Y, M * N, s);
+        if (e != hipSuccess)
+            return e;
+    }
+    hipLaunchKernelGGL((gemm_gen_kernel<FMT, TM>), dim3((unsigned)gx, (unsigned)gy, (unsigned)sp), dim3(256), 0, s,
+                       blocks, p, X, Y, (int)M, (int)N, (int)K, per);
+    return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t gen_tm(const uint8_t *blocks, const uint16_t *X, float *Y, int64_t M, int64_t N, int64_t K, hipStream_t s)
+{
+    if (M <= 16)
+        return go_gen<FMT, 1>(blocks, X, Y, M, N, K, s);
+    if (M <= 32)
+        return go_gen<FMT, 2>(blocks, X, Y, M, N, K, s);
+    return go_gen<FMT, 4>(blocks, X, Y, M, N, K, s);
+}
+
+hipError_t launch_gemm_gen(int fmt, const uint8_t *blocks, const uint16_t *X, float *Y, int64_t M, int64_t N,
+                           int64_t K, hipStream_t s)
+{
+    switch (fmt) {
+    case FMT_Q5K: return gen_tm<FMT_Q5K>(blocks, X, Y, M, N, K, s);
+    case FMT_Q3K: return gen_tm<FMT_Q3K>(blocks, X, Y, M, N, K, s);
+    case FMT_Q2K: return gen_tm<FMT_Q2K>(blocks, X, Y, M, N, K, s);
+    case FMT_Q4_0: return gen_tm<FMT_Q4_0>(blocks, X, Y, M, N, K, s);
+    case FMT_Q4_1: return gen_tm<FMT_Q4_1>(blocks, X, Y, M, N, K, s);
+    case FMT_Q5_0: return gen_tm<FMT_Q5_0>(blocks, X, Y, M, N, K, s);
+    case FMT_Q5_1: return gen_tm<FMT_Q5_1>(blocks, X, Y, M, N, K, s);
+    default: return hipErrorInvalidValue;
+    }
+}
 }  // namespace
 
 hipError_t launch_gemm_bf16(int fmt, const uint8_t *blocks, const uint16_t *X, float *Y, int64_t M,
                             int64_t N, int64_t K, hipStream_t s)
 {
+    if (generic_fmt(fmt))
+        return launch_gemm_gen(fmt, blocks, X, Y, M, N, K, s);
     const Planes p = planes_of(fmt, N, K);
     if (fmt == FMT_Q4K)
         return bf16_by_m<FMT_Q4K>(blocks, p, X, Y, M, N, K, s);

@@ -31,6 +31,7 @@
 // sub-block:  sum x*(128+u) - 128*sum x.  Q8_0 codes are sign-extended
 // bytes converted to fp32 and FMA'd.  All accumulation is fp32.
 #include "qlinear_internal.h"
+#include "decode.h"
 
 namespace ql {
 namespace {
@@ -778,6 +779,85 @@ hipError_t by_m(const Geo &g, const uint16_t *X, float *Y, int M, int64_t N, hip
     }
 }
 
+// ---------------------------------------------------------------------------
+// Generic GEMV for the formats without a tuned kernel (Q5K, Q3K, Q2K and the
+// legacy 32-element types): wave w of a workgroup owns row n; lane l takes
+// the 8-element tasks l, l + 64, ... of the row, decodes each exactly
+// (dequant8) and accumulates w * x in fp32; a butterfly over the wave sums
+// the lanes.
+// ---------------------------------------------------------------------------
+template <int FMT, int M>
+__global__ __launch_bounds__(256) void gemv_gen_kernel(const uint8_t *__restrict__ B, Planes p,
+                                                       const uint16_t *__restrict__ X, float *__restrict__ Y,
+                                                       int64_t N, int K)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (n >= N)
+        return;  // the whole wave
+    const int T = K / 8;
+    float acc[M];
+#pragma unroll
+    for (int m = 0; m < M; m++)
+        acc[m] = 0.0f;
+    for (int i = lane; i < T; i += 64) {
+        float w[8];
+        dequant8<FMT>(B, p, n * T + i, w);
+#pragma unroll
+        for (int m = 0; m < M; m++) {
+            const uint4 xv = *reinterpret_cast<const uint4 *>(X + (int64_t)m * K + 8 * i);
+            const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                acc[m] = fmaf(w[2 * k], __uint_as_float(xw[k] << 16), acc[m]);
+                acc[m] = fmaf(w[2 * k + 1], __uint_as_float(xw[k] & 0xffff0000u), acc[m]);
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < M; m++) {
+#pragma unroll
+        for (int k = 32; k >= 1; k >>= 1)
+            acc[m] += __shfl_xor(acc[m], k);
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int m = 0; m < M; m++)
+            Y[(int64_t)m * N + n] = acc[m];
+    }
+}
+
+template <int FMT>
+hipError_t gen_by_m(const uint8_t *blocks, const Planes &p, const uint16_t *X, float *Y, int M, int64_t N,
+                    int64_t K, hipStream_t s)
+{
+    const dim3 grid((unsigned)((N + 3) / 4)), block(256);
+    switch (M) {
+#define C(MM) \
+    case MM: hipLaunchKernelGGL((gemv_gen_kernel<FMT, MM>), grid, block, 0, s, blocks, p, X, Y, N, (int)K); break;
+    C(1) C(2) C(3) C(4) C(5) C(6) C(7) C(8)
+#undef C
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv_gen(int fmt, const uint8_t *blocks, const uint16_t *X, float *Y, int M, int64_t N,
+                           int64_t K, hipStream_t s)
+{
+    const Planes p = planes_of(fmt, N, K);
+    switch (fmt) {
+    case FMT_Q5K: return gen_by_m<FMT_Q5K>(blocks, p, X, Y, M, N, K, s);
+    case FMT_Q3K: return gen_by_m<FMT_Q3K>(blocks, p, X, Y, M, N, K, s);
+    case FMT_Q2K: return gen_by_m<FMT_Q2K>(blocks, p, X, Y, M, N, K, s);
+    case FMT_Q4_0: return gen_by_m<FMT_Q4_0>(blocks, p, X, Y, M, N, K, s);
+    case FMT_Q4_1: return gen_by_m<FMT_Q4_1>(blocks, p, X, Y, M, N, K, s);
+    case FMT_Q5_0: return gen_by_m<FMT_Q5_0>(blocks, p, X, Y, M, N, K, s);
+    case FMT_Q5_1: return gen_by_m<FMT_Q5_1>(blocks, p, X, Y, M, N, K, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 template <int FMT, int M>
 hipError_t glu_by_cpt(const Geo &gg, const Geo &gu, const uint16_t *X, float *H, int64_t F, int act, hipStream_t s)
 {
@@ -801,12 +881,15 @@ hipError_t glu_by_m(const Geo &gg, const Geo &gu, const uint16_t *X, float *H, i
 
 }  // namespace
 
-bool glu_fused_fits(int M, int64_t K) { return M >= 1 && M <= 2 && K / 32 <= 256; }
+bool glu_fused_fits(int fmt, int M, int64_t K)
+{
+    return !generic_fmt(fmt) && M >= 1 && M <= 2 && K / 32 <= 256;
+}
 
 hipError_t launch_glu_fused(int fmt, const uint8_t *gate, const uint8_t *up, const uint16_t *X, float *H, int M,
                             int64_t F, int64_t K, int act, hipStream_t s)
 {
-    if (!glu_fused_fits(M, K))
+    if (!glu_fused_fits(fmt, M, K))
         return hipErrorNotSupported;
     const Planes p = planes_of(fmt, F, K);
     const Geo gg{gate, p.scales, p.d, (int)K}, gu{up, p.scales, p.d, (int)K};
@@ -820,6 +903,8 @@ hipError_t launch_glu_fused(int fmt, const uint8_t *gate, const uint8_t *up, con
 hipError_t launch_gemv(int fmt, const uint8_t *blocks, const uint16_t *X, float *Y, int M,
                        int64_t N, int64_t K, hipStream_t s)
 {
+    if (generic_fmt(fmt))
+        return launch_gemv_gen(fmt, blocks, X, Y, M, N, K, s);
     const Planes p = planes_of(fmt, N, K);
     Geo g{blocks, p.scales, p.d, (int)K};
     if (fmt == FMT_Q4K)

@@ -19,6 +19,7 @@
 // v_cvt_f16_f32 (round to nearest even, subnormals kept).  A -0.0 input is
 // read as +0.0 (x + 0.0f), so the sign of a zero never reaches a scale.
 #include "qlinear_internal.h"
+#include "decode.h"
 
 namespace ql {
 namespace {
@@ -229,73 +230,15 @@ __global__ __launch_bounds__(256) void isq_q6k_kernel(const uint4 *__restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// Exact dequantization to fp32 (test aid), same lane split
+// Exact dequantization to fp32 (test aid): one lane per 8 elements
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float h2f(uint32_t bits16) { return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16); }
-
-__device__ __forceinline__ void unpack_nibbles(uint32_t d, int q[8])
-{
-#pragma unroll
-    for (int p = 0; p < 4; p++) {
-        q[2 * p] = (d >> (4 * p)) & 15;
-        q[2 * p + 1] = (d >> (16 + 4 * p)) & 15;
-    }
-}
-
-// the 8 elements of task t (elements 8t..8t+7 of the tensor), exactly
-__device__ __forceinline__ void dequant8(int fmt, const uint8_t *__restrict__ B, int64_t t, int64_t scales_off,
-                                         int64_t d_off, float v[8])
-{
-    if (fmt == FMT_Q8_0) {
-        const uint2 c = reinterpret_cast<const uint2 *>(B)[t];
-        const float d = h2f(reinterpret_cast<const uint16_t *>(B + scales_off)[t >> 2]);
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            v[i] = d * (float)(int8_t)(c.x >> (8 * i));
-            v[i + 4] = d * (float)(int8_t)(c.y >> (8 * i));
-        }
-    } else if (fmt == FMT_Q4K) {
-        const uint32_t c = reinterpret_cast<const uint32_t *>(B)[t];
-        const uint4 h = reinterpret_cast<const uint4 *>(B + scales_off)[t >> 5];
-        const int j = (int)((t & 31) >> 2);
-        const uint32_t sc = ((h.y >> (4 * j)) & 15u) | ((h.w >> (2 * j)) & 3u) << 4;
-        const uint32_t mq = ((h.z >> (4 * j)) & 15u) | ((h.w >> (16 + 2 * j)) & 3u) << 4;
-        const float S = h2f(h.x & 0xffffu) * (float)sc;
-        const float M = h2f(h.x >> 16) * (float)mq;
-        int q[8];
-        unpack_nibbles(c, q);
-#pragma unroll
-        for (int i = 0; i < 8; i++)
-            v[i] = fmaf(S, (float)q[i], -M);  // one rounding of the exact value
-    } else {
-        const int64_t g = t >> 5;
-        const int l = (int)(t & 31), c = l >> 2, w = l & 3, o = w & 1;
-        const uint8_t *Cg = B + 192 * g;
-        const uint32_t lo = *reinterpret_cast<const uint32_t *>(Cg + 4 * l);
-        const uint32_t hd = *reinterpret_cast<const uint32_t *>(Cg + 128 + 8 * c + 4 * (w >> 1));
-        const int sc = reinterpret_cast<const int8_t *>(B + scales_off)[16 * g + (l >> 1)];
-        const float S = h2f(reinterpret_cast<const uint16_t *>(B + d_off)[g]) * (float)sc;
-        int q[8];
-        unpack_nibbles(lo, q);
-#pragma unroll
-        for (int p = 0; p < 4; p++) {
-            q[2 * p] |= (int)((hd >> (8 * o + 2 * p)) & 3u) << 4;
-            q[2 * p + 1] |= (int)((hd >> (16 + 8 * o + 2 * p)) & 3u) << 4;
-        }
-#pragma unroll
-        for (int i = 0; i < 8; i++)
-            v[i] = S * (float)(q[i] - 32);
-    }
-}
-
-__global__ __launch_bounds__(256) void dequant_kernel(int fmt, const uint8_t *__restrict__ B,
-                                                      int64_t tasks, int64_t scales_off,
-                                                      int64_t d_off, float4 *__restrict__ out)
+__global__ __launch_bounds__(256) void dequant_kernel(int fmt, const uint8_t *__restrict__ B, int64_t tasks, Planes p,
+                                                      float4 *__restrict__ out)
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < tasks; t += stride) {
         float v[8];
-        dequant8(fmt, B, t, scales_off, d_off, v);
+        dequant8_any(fmt, B, p, t, v);
         out[2 * t] = make_float4(v[0], v[1], v[2], v[3]);
         out[2 * t + 1] = make_float4(v[4], v[5], v[6], v[7]);
     }
@@ -306,9 +249,9 @@ __global__ __launch_bounds__(256) void dequant_kernel(int fmt, const uint8_t *__
 // exactly, becomes row i of the output.  Workgroup (x, y) writes 2048
 // elements of output row x; ids outside [0, N) give a row of zeros.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void embed_kernel(int fmt, const uint8_t *__restrict__ B, int64_t scales_off,
-                                                    int64_t d_off, const int32_t *__restrict__ ids, int64_t N,
-                                                    int64_t K, float4 *__restrict__ out)
+__global__ __launch_bounds__(256) void embed_kernel(int fmt, const uint8_t *__restrict__ B, Planes p,
+                                                    const int32_t *__restrict__ ids, int64_t N, int64_t K,
+                                                    float4 *__restrict__ out)
 {
     const int64_t row = blockIdx.x;
     const int64_t k8 = (int64_t)blockIdx.y * 256 + threadIdx.x;  // task in the row
@@ -317,7 +260,7 @@ __global__ __launch_bounds__(256) void embed_kernel(int fmt, const uint8_t *__re
     const int32_t id = ids[row];
     float v[8];
     if (id >= 0 && id < N) {
-        dequant8(fmt, B, (int64_t)id * (K / 8) + k8, scales_off, d_off, v);
+        dequant8_any(fmt, B, p, (int64_t)id * (K / 8) + k8, v);
     } else {
 #pragma unroll
         for (int i = 0; i < 8; i++)
@@ -326,6 +269,213 @@ __global__ __launch_bounds__(256) void embed_kernel(int fmt, const uint8_t *__re
     float4 *o = out + 2 * (row * (K / 8) + k8);
     o[0] = make_float4(v[0], v[1], v[2], v[3]);
     o[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+// ---------------------------------------------------------------------------
+// Further formats (Q5K, Q3K, Q2K; Q4_0, Q4_1, Q5_0, Q5_1): same lane split,
+// one lane per 8 elements; a K-quant group is 32 lanes (a sub-block 4 lanes
+// for Q5K, 2 for Q3K and Q2K), a legacy block 4 lanes.  Steps follow the
+// reference definitions one binary32 operation at a time:
+//   affine K-quants: lo = min(0, min x), hi = max x per sub-block,
+//     s = (hi - lo) / (2^b - 1), m = 0 - lo; d = F16(max s / (2^sb - 1)),
+//     dmin = F16(max m / (2^sb - 1)); sc, mq = clamp(RHA(s / d)), ...;
+//     codes clamp(RHA((x + dmin mq) / (d sc)), 0, 2^b - 1)
+//   Q3K: s = max|x| / 3, d = F16(max s / 63), codes clamp(RHA(x / (d sc)), -4, 3)
+//   Q4_0 / Q5_0: d = F16(max|x| / 7 or 15), codes clamp(RHA(x / d))
+//   Q4_1 / Q5_1: d = F16((max - min) / 15 or 31), m = F16(min) (signed,
+//     clamped to 65504), codes clamp(RHA((x - m) / d), 0, 2^b - 1)
+// Block 0 also zeroes the padding between planes and at the end (< 16 bytes each).
+// ---------------------------------------------------------------------------
+struct Gaps {
+    int64_t off[3];
+    int len[3];
+};
+
+template <int FMT>
+__global__ __launch_bounds__(256) void isq_more_kernel(const uint4 *__restrict__ W, int64_t tasks,
+                                                       uint8_t *__restrict__ out, Planes p, Gaps gaps)
+{
+    if (blockIdx.x == 0 && threadIdx.x < 48) {
+        const int r = threadIdx.x / 16, i = threadIdx.x % 16;
+        if (i < gaps.len[r])
+            out[gaps.off[r] + i] = 0;
+    }
+    constexpr bool KQ = FMT == FMT_Q5K || FMT == FMT_Q3K || FMT == FMT_Q2K;
+    constexpr bool AFF = FMT == FMT_Q5K || FMT == FMT_Q2K || FMT == FMT_Q4_1 || FMT == FMT_Q5_1;
+    constexpr int BITS = FMT == FMT_Q5K || FMT == FMT_Q5_0 || FMT == FMT_Q5_1 ? 5
+                         : FMT == FMT_Q3K                                     ? 3
+                         : FMT == FMT_Q2K                                     ? 2
+                                                                              : 4;
+    constexpr int SBITS = FMT == FMT_Q2K ? 4 : 6;
+    constexpr int QLO = AFF ? 0 : -(1 << (BITS - 1));
+    constexpr int QHI = AFF ? (1 << BITS) - 1 : (1 << (BITS - 1)) - 1;
+    const float qden = AFF ? (float)((1 << BITS) - 1) : (float)((1 << (BITS - 1)) - 1);
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < tasks; t += stride) {
+        float x[8];
+        load8(W[t], x);
+        // statistics of the lane's 8 elements, then of its sub-block / block
+        float lo = AFF && KQ ? 0.0f : x[0], hi = x[0], a = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            lo = fminf(lo, x[i]);
+            hi = fmaxf(hi, x[i]);
+            a = fmaxf(a, fabsf(x[i]));
+        }
+        constexpr int SUBL = FMT == FMT_Q5K || !KQ ? 4 : 2;  // lanes per sub-block / block
+#pragma unroll
+        for (int k = 1; k < SUBL; k <<= 1) {
+            lo = fminf(lo, __shfl_xor(lo, k));
+            hi = fmaxf(hi, __shfl_xor(hi, k));
+            a = fmaxf(a, __shfl_xor(a, k));
+        }
+        float S, M, rS;   // code step, subtracted min, 1 / step
+        uint32_t d16 = 0, m16 = 0, sc = 0, mq = 0;
+        if constexpr (KQ) {
+            const float sden = (float)((1 << SBITS) - 1);
+            const float s = AFF ? (hi - lo) / qden : a / qden;
+            const float m = AFF ? 0.0f - lo : 0.0f;
+            float smax = s, mmax = m;
+#pragma unroll
+            for (int k = SUBL; k < 32; k <<= 1) {
+                smax = fmaxf(smax, __shfl_xor(smax, k));
+                mmax = fmaxf(mmax, __shfl_xor(mmax, k));
+            }
+            float df, dmf = 0.0f;
+            d16 = scale_f16(smax / sden, &df);
+            if (AFF)
+                m16 = scale_f16(mmax / sden, &dmf);
+            sc = df > 0.0f ? (uint32_t)code_of(s / df, 0.0f, sden) : 0u;
+            mq = AFF && dmf > 0.0f ? (uint32_t)code_of(m / dmf, 0.0f, sden) : 0u;
+            S = df * (float)sc;
+            M = dmf * (float)mq;
+        } else if constexpr (AFF) {
+            float df;
+            d16 = scale_f16((hi - lo) / qden, &df);
+            const _Float16 mh = (_Float16)fmaxf(-65504.0f, fminf(lo, 65504.0f));
+            m16 = (uint32_t)__builtin_bit_cast(uint16_t, mh);
+            S = df;
+            M = -(float)mh;  // codes of (x - m) / d
+        } else {
+            float df;
+            d16 = scale_f16(a / qden, &df);
+            S = df;
+            M = 0.0f;
+        }
+        rS = S > 0.0f ? 1.0f / S : 0.0f;
+        int q[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const float u = AFF ? (KQ ? x[i] + M : x[i] - (-M)) : x[i];
+            q[i] = S > 0.0f ? (int)fminf(fmaxf(rha_quot(u, S, rS), (float)QLO), (float)QHI) : 0;
+        }
+        // stores
+        const int tl = (int)(t & 31);
+        const int64_t g = t >> 5;
+        if constexpr (FMT == FMT_Q5K) {
+            uint32_t lw = 0, hb = 0;
+#pragma unroll
+            for (int k = 0; k < 8; k++) {
+                lw |= (uint32_t)(q[k] & 15) << (4 * k);
+                hb |= (uint32_t)(q[k] >> 4) << k;
+            }
+            reinterpret_cast<uint32_t *>(out)[t] = lw;
+            out[p.hi + 32 * g + tl] = (uint8_t)hb;
+            const int j = tl >> 2;
+            const bool own = (tl & 3) == 0;
+            uint32_t w1 = own ? (sc & 15u) << (4 * j) : 0u, w2 = own ? (mq & 15u) << (4 * j) : 0u;
+            uint32_t w3 = own ? (sc >> 4) << (2 * j) | (mq >> 4) << (16 + 2 * j) : 0u;
+#pragma unroll
+            for (int k = 1; k < 32; k <<= 1) {
+                w1 |= (uint32_t)__shfl_xor((int)w1, k);
+                w2 |= (uint32_t)__shfl_xor((int)w2, k);
+                w3 |= (uint32_t)__shfl_xor((int)w3, k);
+            }
+            if (tl == 0)
+                reinterpret_cast<uint4 *>(out + p.scales)[g] = make_uint4(d16 | m16 << 16, w1, w2, w3);
+        } else if constexpr (FMT == FMT_Q3K) {
+            uint32_t lw = 0, hb = 0;
+#pragma unroll
+            for (int k = 0; k < 8; k++) {
+                const uint32_t u = (uint32_t)(q[k] + 4);
+                lw |= (u & 3u) << (2 * k);
+                hb |= (u >> 2) << k;
+            }
+            reinterpret_cast<uint16_t *>(out)[t] = (uint16_t)lw;
+            out[p.hi + 32 * g + tl] = (uint8_t)hb;
+            const int j = tl >> 1;
+            const bool own = (tl & 1) == 0;
+            uint32_t s0 = own && j < 8 ? (sc & 15u) << (4 * j) : 0u;
+            uint32_t s1 = own && j >= 8 ? (sc & 15u) << (4 * (j - 8)) : 0u;
+            uint32_t s2 = own ? (sc >> 4) << (2 * j) : 0u;
+#pragma unroll
+            for (int k = 1; k < 32; k <<= 1) {
+                s0 |= (uint32_t)__shfl_xor((int)s0, k);
+                s1 |= (uint32_t)__shfl_xor((int)s1, k);
+                s2 |= (uint32_t)__shfl_xor((int)s2, k);
+            }
+            if (tl == 0) {
+                uint32_t *o3 = reinterpret_cast<uint32_t *>(out + p.scales + 12 * g);
+                o3[0] = s0;
+                o3[1] = s1;
+                o3[2] = s2;
+                reinterpret_cast<uint16_t *>(out + p.d)[g] = (uint16_t)d16;
+            }
+        } else if constexpr (FMT == FMT_Q2K) {
+            uint32_t lw = 0;
+#pragma unroll
+            for (int k = 0; k < 8; k++)
+                lw |= (uint32_t)q[k] << (2 * k);
+            reinterpret_cast<uint16_t *>(out)[t] = (uint16_t)lw;
+            if ((tl & 1) == 0)
+                out[p.scales + 16 * g + (tl >> 1)] = (uint8_t)(sc | mq << 4);
+            if (tl == 0)
+                reinterpret_cast<uint32_t *>(out + p.d)[g] = d16 | m16 << 16;
+        } else {
+            constexpr int bias = FMT == FMT_Q4_0 ? 8 : (FMT == FMT_Q5_0 ? 16 : 0);
+            uint32_t lw = 0, hb = 0;
+#pragma unroll
+            for (int k = 0; k < 8; k++) {
+                const uint32_t u = (uint32_t)(q[k] + bias);
+                lw |= (u & 15u) << (4 * k);
+                hb |= (u >> 4) << k;
+            }
+            reinterpret_cast<uint32_t *>(out)[t] = lw;
+            if constexpr (FMT == FMT_Q5_0 || FMT == FMT_Q5_1)
+                out[p.hi + t] = (uint8_t)hb;
+            if ((t & 3) == 0) {
+                reinterpret_cast<uint16_t *>(out + p.d)[t >> 2] = (uint16_t)d16;
+                if constexpr (AFF)
+                    reinterpret_cast<uint16_t *>(out + p.m)[t >> 2] = (uint16_t)m16;
+            }
+        }
+    }
+}
+
+// padding bytes of a further format's buffer: after each plane up to the next
+// plane start, and up to the end
+Gaps gaps_of(int fmt, int64_t N, int64_t K, const Planes &p)
+{
+    const int64_t E = N * K, G = E / 256, B = E / 32;
+    Gaps z{{0, 0, 0}, {0, 0, 0}};
+    int n = 0;
+    auto gap = [&](int64_t from, int64_t to) {
+        if (to > from && n < 3) {
+            z.off[n] = from;
+            z.len[n] = (int)(to - from);
+            n++;
+        }
+    };
+    switch (fmt) {
+    case FMT_Q3K: gap(108 * G, p.d); gap(p.d + 2 * G, p.total); break;
+    case FMT_Q2K: gap(84 * G, p.total); break;
+    case FMT_Q4_0: gap(18 * B, p.total); break;
+    case FMT_Q4_1: gap(18 * B, p.m); gap(p.m + 2 * B, p.total); break;
+    case FMT_Q5_0: gap(20 * B, p.d); gap(p.d + 2 * B, p.total); break;
+    case FMT_Q5_1: gap(20 * B, p.d); gap(p.d + 2 * B, p.m); gap(p.m + 2 * B, p.total); break;
+    default: break;
+    }
+    return z;
 }
 
 inline unsigned grid_for(int64_t tasks)
@@ -350,11 +500,25 @@ hipError_t launch_isq(int fmt, const uint16_t *W, int64_t N, int64_t K, uint8_t 
         hipLaunchKernelGGL(isq_q4k_kernel, dim3(grid_for(tasks)), dim3(256), 0, s, w, tasks,
                            reinterpret_cast<uint32_t *>(out),
                            reinterpret_cast<uint4 *>(out + p.scales));
-    else
+    else if (fmt == FMT_Q6K)
         hipLaunchKernelGGL(isq_q6k_kernel, dim3(grid_for(tasks)), dim3(256), 0, s, w, tasks, out,
                            reinterpret_cast<int8_t *>(out + p.scales),
                            reinterpret_cast<uint16_t *>(out + p.d), out + 210 * (N * K / 256),
                            (int)(p.total - 210 * (N * K / 256)));
+    else {
+        const Gaps z = gaps_of(fmt, N, K, p);
+        const dim3 grid(grid_for(tasks)), block(256);
+        switch (fmt) {
+        case FMT_Q5K: hipLaunchKernelGGL(isq_more_kernel<FMT_Q5K>, grid, block, 0, s, w, tasks, out, p, z); break;
+        case FMT_Q3K: hipLaunchKernelGGL(isq_more_kernel<FMT_Q3K>, grid, block, 0, s, w, tasks, out, p, z); break;
+        case FMT_Q2K: hipLaunchKernelGGL(isq_more_kernel<FMT_Q2K>, grid, block, 0, s, w, tasks, out, p, z); break;
+        case FMT_Q4_0: hipLaunchKernelGGL(isq_more_kernel<FMT_Q4_0>, grid, block, 0, s, w, tasks, out, p, z); break;
+        case FMT_Q4_1: hipLaunchKernelGGL(isq_more_kernel<FMT_Q4_1>, grid, block, 0, s, w, tasks, out, p, z); break;
+        case FMT_Q5_0: hipLaunchKernelGGL(isq_more_kernel<FMT_Q5_0>, grid, block, 0, s, w, tasks, out, p, z); break;
+        case FMT_Q5_1: hipLaunchKernelGGL(isq_more_kernel<FMT_Q5_1>, grid, block, 0, s, w, tasks, out, p, z); break;
+        default: return hipErrorInvalidValue;
+        }
+    }
     return hipGetLastError();
 }
 
@@ -363,7 +527,7 @@ hipError_t launch_embed(int fmt, const uint8_t *blocks, int64_t N, int64_t K, co
 {
     const Planes p = planes_of(fmt, N, K);
     const dim3 grid((unsigned)n_ids, (unsigned)((K / 8 + 255) / 256));
-    hipLaunchKernelGGL(embed_kernel, grid, dim3(256), 0, s, fmt, blocks, p.scales, p.d, ids, N, K,
+    hipLaunchKernelGGL(embed_kernel, grid, dim3(256), 0, s, fmt, blocks, p, ids, N, K,
                        reinterpret_cast<float4 *>(out));
     return hipGetLastError();
 }
@@ -372,8 +536,8 @@ hipError_t launch_dequant(int fmt, const uint8_t *blocks, int64_t N, int64_t K, 
 {
     const int64_t tasks = N * K / 8;
     const Planes p = planes_of(fmt, N, K);
-    hipLaunchKernelGGL(dequant_kernel, dim3(grid_for(tasks)), dim3(256), 0, s, fmt, blocks, tasks,
-                       p.scales, p.d, reinterpret_cast<float4 *>(W));
+    hipLaunchKernelGGL(dequant_kernel, dim3(grid_for(tasks)), dim3(256), 0, s, fmt, blocks, tasks, p,
+                       reinterpret_cast<float4 *>(W));
     return hipGetLastError();
 }
 

@@ -34,7 +34,16 @@ def test_blocks_bytes():
     assert ql.blocks_bytes("q8_0", 3, 32) == 3 * 34
     assert ql.blocks_bytes("q4k", 3, 32) == 0          # K % 256
     assert ql.blocks_bytes("q4k", 0, 256) == 0
-    assert ql.blocks_bytes("q2k", 4, 256) == 0         # named but not implemented
+    assert ql.blocks_bytes("q8k", 4, 256) == 0         # named but not implemented
+    # further formats: GGML byte counts per 256 / 32 elements, planes padded to 16 bytes
+    assert ql.blocks_bytes("q5k", 4, 256) == 4 * 176
+    assert ql.blocks_bytes("q3k", 4, 256) == 448       # d plane at 108*4 = 432, + 8 bytes, rounded up to 16
+    assert ql.blocks_bytes("q2k", 4, 256) == 336
+    assert ql.blocks_bytes("q4_0", 4, 256) == 4 * 8 * 18
+    assert ql.blocks_bytes("q4_1", 4, 256) == 4 * 8 * 20
+    assert ql.blocks_bytes("q5_0", 4, 256) == 4 * 8 * 22
+    assert ql.blocks_bytes("q5_1", 4, 256) == 4 * 8 * 24
+    assert ql.blocks_bytes("q4_0", 4, 32) == 0         # the further formats need K % 256
     assert ql.blocks_bytes(99, 4, 256) == 0
     # bits per weight: 8.5, 4.5, 6.5625 (nominal 8, 4, 6 on the page's tables)
     assert ql.blocks_bytes("q8_0", 1, 256) * 8 / 256 == 8.5
@@ -76,7 +85,8 @@ def test_tensor_fmt_precedence():
 
 def test_supported_formats():
     assert [ql.fmt_supported(f) for f in ("q8_0", "q4k", "q6k")] == [True] * 3
-    assert not any(ql.fmt_supported(f) for f in ("q2k", "q3k", "q5k", "q8k", "q4_0", "q8_1"))
+    assert all(ql.fmt_supported(f) for f in ("q2k", "q3k", "q5k", "q4_0", "q4_1", "q5_0", "q5_1"))
+    assert not any(ql.fmt_supported(f) for f in ("q8k", "q8_1"))
     L = ql.lib()
     assert L.q_fmt_name(1) == b"q4k" and L.q_fmt_name(42) is None
     for s in range(-6, 1):
@@ -95,7 +105,9 @@ def test_isq_argument_errors():
     assert L.isq_quantize(0, NULL, 4, 256, A, NULL) == ql.Q_EINVAL
     assert L.isq_quantize(0, A, 4, 256, NULL, NULL) == ql.Q_EINVAL
     assert L.isq_quantize(17, A, 4, 256, A2, NULL) == ql.Q_EINVAL
-    assert L.isq_quantize(3, A, 4, 256, A2, NULL) == ql.Q_ENOTSUP   # Q2K
+    assert L.isq_quantize(6, A, 4, 256, A2, NULL) == ql.Q_ENOTSUP   # Q8K
+    assert L.isq_quantize(11, A, 4, 256, A2, NULL) == ql.Q_ENOTSUP  # Q8_1
+    assert L.isq_quantize(7, A, 4, 32, A2, NULL) == ql.Q_ESHAPE     # Q4_0 here needs K % 256
     assert L.isq_quantize(1, MIS, 4, 256, A2, NULL) == ql.Q_EALIGN
     assert L.isq_quantize(1, A, 4, 256, MIS, NULL) == ql.Q_EALIGN
     assert L.isq_quantize(1, A, 4, 250, A2, NULL) == ql.Q_ESHAPE
@@ -121,7 +133,7 @@ def test_qmatmul_argument_errors():
     assert call(x=NULL) == ql.Q_EINVAL
     assert call(y=NULL) == ql.Q_EINVAL
     assert call(fmt=12) == ql.Q_EINVAL
-    assert call(fmt=5) == ql.Q_ENOTSUP
+    assert call(fmt=6) == ql.Q_ENOTSUP                 # Q8K
     assert call(y=MIS) == ql.Q_EALIGN
     assert call(K=128) == ql.Q_ESHAPE
     assert call(K=384) == ql.Q_ESHAPE
@@ -149,7 +161,7 @@ def test_embed_argument_errors():
     assert call(ids=NULL) == ql.Q_EINVAL
     assert call(out=NULL) == ql.Q_EINVAL
     assert call(fmt=12) == ql.Q_EINVAL
-    assert call(fmt=4) == ql.Q_ENOTSUP                       # Q3K: named, not implemented
+    assert call(fmt=11) == ql.Q_ENOTSUP                      # Q8_1: named, not implemented
     assert call(b=MIS) == ql.Q_EALIGN
     assert call(out=MIS) == ql.Q_EALIGN
     assert call(ids=ctypes.c_void_p(0x40002)) == ql.Q_EALIGN
@@ -171,7 +183,7 @@ def test_glu_argument_errors_and_workspace_sizes():
     assert call(x=NULL) == ql.Q_EINVAL
     assert call(h=NULL) == ql.Q_EINVAL
     assert call(u=MIS) == ql.Q_EALIGN
-    assert call(fmt=5) == ql.Q_ENOTSUP
+    assert call(fmt=6) == ql.Q_ENOTSUP
     assert call(act=3) == ql.Q_EINVAL
     assert call(act=-1) == ql.Q_EINVAL
     assert call(K=100) == ql.Q_ESHAPE
@@ -182,4 +194,5 @@ def test_glu_argument_errors_and_workspace_sizes():
     assert ql.glu_workspace_bytes("q4k", 2, 64, 8192) == 0   # fused kernel
     assert ql.glu_workspace_bytes("q4k", 3, 64, 256) == 4 * 3 * 64
     assert ql.glu_workspace_bytes("q4k", 1, 64, 8448) == 4 * 64
-    assert ql.glu_workspace_bytes("q2k", 1, 64, 256) == 0
+    assert ql.glu_workspace_bytes("q8k", 1, 64, 256) == 0
+    assert ql.glu_workspace_bytes("q2k", 1, 64, 256) == 4 * 64   # generic formats: two-matmul path
