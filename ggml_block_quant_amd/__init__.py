@@ -2,7 +2,9 @@
 
 A thin Python binding over the C ABI of ``libqlinear.so`` (declared in
 ``include/qlinear.h``): in-situ quantization of bf16 weights into Q8_0, Q4K
-or Q6K blocks, and the fused dequantize-matmul that consumes them.  Every
+or Q6K blocks (and Q5K, Q3K, Q2K, Q4_0, Q4_1, Q5_0, Q5_1), the fused
+dequantize-matmul that consumes them, the gated feed-forward projection and
+the quantized embedding lookup.  Every
 step of the computation runs in the library's HIP kernels; this module only
 checks tensors and passes pointers, sizes and the current HIP stream.
 PyTorch provides device memory and streams.

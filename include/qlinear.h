@@ -41,6 +41,19 @@
  *         dmin*m, 144 bytes per 256 elements.
  *   Q6K:  super-blocks of 256 = 16 sub-blocks of 16, 8-bit sub-scales, one
  *         fp16 d, 6-bit symmetric codes, w = d*sc*q, 210 bytes per 256.
+ * Further formats (levels 5, 3, 2 of the shorthand table and the legacy
+ * 32-element types; same rules with other widths, GGML byte counts):
+ *   Q5K:  as Q4K with 5-bit codes, 176 bytes per 256.
+ *   Q3K:  16 sub-blocks of 16, 6-bit scales, one fp16 d, symmetric codes
+ *         in [-4, 3], w = d*sc*q, 110 bytes per 256.
+ *   Q2K:  16 sub-blocks of 16, 4-bit scales and mins, fp16 d and dmin,
+ *         2-bit codes, w = d*sc*q - dmin*m, 84 bytes per 256.
+ *   Q4_0 / Q5_0: blocks of 32, fp16 d = max|x| / 7 (/ 15), codes in
+ *         [-8, 7] ([-16, 15]), 18 (22) bytes per 32.
+ *   Q4_1 / Q5_1: blocks of 32, fp16 d = (max - min) / 15 (/ 31) and fp16
+ *         m = min, codes in [0, 15] ([0, 31]), w = d*q + m, 20 (24) bytes.
+ * These run on generic kernels (exact decode of 8 elements, then an fp32
+ * GEMV or a bf16 MFMA GEMM) and need K % 256 == 0 as well.
  */
 #ifndef QLINEAR_H
 #define QLINEAR_H
@@ -52,10 +65,9 @@
 extern "C" {
 #endif
 
-/* Quantization types.  The first three are implemented; the others are
- * named by the pages' tables (so that the level and promotion helpers can
- * answer for every row) and are rejected with Q_ENOTSUP by the compute
- * calls. */
+/* Quantization types.  All are implemented except Q8K and Q8_1, which the
+ * pages' tables name (so that the level and promotion helpers can answer
+ * for every row) and the compute calls reject with Q_ENOTSUP. */
 typedef enum {
     QFMT_Q8_0 = 0,
     QFMT_Q4K = 1,
@@ -104,7 +116,15 @@ enum {
  *   Q8_0: [codes int8 N*K, row-major][d fp16 N*K/32, row-major]
  *   Q4K:  [codes G*128][headers G*16: d, dmin, 12 bytes of 6-bit sc/m]
  *   Q6K:  [codes G*192: 128 bytes low 4 bits + 64 bytes high 2 bits of
- *          q+32][sub-scales G*16 int8][d G*2 fp16]                        */
+ *          q+32][sub-scales G*16 int8][d G*2 fp16]
+ * Further formats (natural element order; u = stored code; B = N*K/32;
+ * every plane start rounded up to 16 bytes, padding zero):
+ *   Q5K:  [low nibbles G*128][top bits G*32][Q4K-style headers G*16]
+ *   Q3K:  [low 2 bits of u = q+4, G*64][top bits G*32][6-bit scales G*12][d G*2]
+ *   Q2K:  [codes 2-bit G*64][sc | m << 4, G*16][d, dmin G*4]
+ *   Q4_0: [nibbles of q+8, B*16][d B*2]      Q4_1: [nibbles B*16][d B*2][m B*2]
+ *   Q5_0: [low nibbles of q+16, B*16][fifth bits B*4][d B*2]
+ *   Q5_1: [low nibbles B*16][fifth bits B*4][d B*2][m B*2]              */
 size_t q_blocks_bytes(int fmt, int64_t N, int64_t K);
 
 /* In-situ quantization (page "Quantization types": ISQ, --isq N).
@@ -112,7 +132,8 @@ size_t q_blocks_bytes(int fmt, int64_t N, int64_t K);
  * bytes, fully overwritten.  Codes and scales are bit-exact with the
  * library's reference definition (fp32 IEEE arithmetic, fp16 scales rounded
  * to nearest even after clamping to 65504, round-half-away-from-zero codes).
- * Requires K % 256 == 0 (Q8_0: K % 32 == 0), 1 <= N <= QLINEAR_MAX_N. */
+ * Requires K % 256 == 0 (Q8_0: K % 32 == 0), 1 <= N <= QLINEAR_MAX_N; the
+ * gaps between planes and the end padding are written as zeros. */
 int isq_quantize(int fmt, const void *W_bf16, int64_t N, int64_t K, void *out_blocks,
                  void *stream);
 
@@ -153,7 +174,7 @@ int qmatmul_ex(int fmt, const void *blocks, const void *X_bf16, float *Y_fp32, i
  * gate_blocks / up_blocks: device, isq_quantize(fmt, W, F, K) of the [F][K]
  * gate and up weights (a packed [2F][K] checkpoint tensor is quantized as
  * its two halves).  X_bf16: device [M][K].  H_fp32: device [M][F],
- * overwritten.  For M <= 2 and K <= 8192 one fused kernel computes the
+ * overwritten.  For M <= 2 and K <= 8192 (Q8_0, Q4K, Q6K) one fused kernel computes the
  * gate and up rows of each output together and needs no workspace;
  * otherwise G goes through `workspace` (qmatmul_glu_workspace_bytes bytes,
  * 16-byte aligned; Q_EINVAL without it) and U through H, followed by an
