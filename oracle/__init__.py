@@ -82,6 +82,10 @@ def _L():
             "oracle_unpack_kq": [I, P, I, I, P, P, P, P, P],
             "oracle_pack_leg": [I, P, P, P, I, I, P],
             "oracle_unpack_leg": [I, P, I, I, P, P, P],
+            "oracle_e4m3_from_f32_array": [P, I, P],
+            "oracle_quantize_fp8": [P, I, I, P, P],
+            "oracle_dequant_fp8": [P, P, I, I, P],
+            "oracle_matmul_fp8": [P, P, P, P, I, P, P, I, P, P],
             "oracle_pack_q8_0": [P, P, I, I, P],
             "oracle_unpack_q8_0": [P, I, I, P, P],
             "oracle_pack_q4k": [P, P, P, P, P, I, I, P],
@@ -93,6 +97,10 @@ def _L():
             fn = getattr(lib, name)
             fn.restype = None
             fn.argtypes = args
+        lib.oracle_e4m3_value.restype = ctypes.c_double
+        lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+        lib.oracle_e4m3_from_f32.restype = ctypes.c_uint8
+        lib.oracle_e4m3_from_f32.argtypes = [ctypes.c_float]
         lib.oracle_more_layout.restype = ctypes.c_int64
         lib.oracle_more_layout.argtypes = [I, I, I, P]
         _lib = lib
@@ -205,6 +213,80 @@ def quantize(fmt: str, w_bf16: np.ndarray) -> dict:
         L.oracle_quantize_leg(LEG_FORMATS[fmt], _p(w), rows, cols, _p(d16), _p(m16), _p(q))
         return {"d16": d16, "m16": m16, "q": q}
     raise ValueError(fmt)
+
+
+# ----------------------------------------------------------------------------
+# FP8 E4M3 with per-row scales (oracle.c, "FP8 E4M3 ...")
+# ----------------------------------------------------------------------------
+
+def e4m3_value(b: int) -> float:
+    return float(_L().oracle_e4m3_value(int(b)))
+
+
+def e4m3_from_f32_array(a) -> np.ndarray:
+    a = _c(np.asarray(a, np.float32), np.float32)
+    out = np.empty(a.shape, np.uint8)
+    _L().oracle_e4m3_from_f32_array(_p(a), a.size, _p(out))
+    return out
+
+
+def quantize_fp8(w_bf16: np.ndarray) -> dict:
+    """Rows of a bf16 tensor -> E4M3 codes [rows][cols] and binary32 scales
+    s [rows] = max|x| / 448."""
+    w = _c(w_bf16, np.uint16)
+    rows, cols = w.shape
+    q = np.empty((rows, cols), np.uint8)
+    s = np.empty(rows, np.float32)
+    _L().oracle_quantize_fp8(_p(w), rows, cols, _p(q), _p(s))
+    return {"q": q, "s": s}
+
+
+def dequant_fp8(f: dict) -> np.ndarray:
+    q = _c(f["q"], np.uint8)
+    rows, cols = q.shape
+    out = np.empty((rows, cols), np.float64)
+    _L().oracle_dequant_fp8(_p(q), _p(_c(f["s"], np.float32)), rows, cols, _p(out))
+    return out
+
+
+def pack_fp8(f: dict) -> np.ndarray:
+    """Planar bytes: codes [rows][cols], then the fp32 scales at the first
+    multiple of 16 bytes (zero padding)."""
+    q = _c(f["q"], np.uint8)
+    rows, cols = q.shape
+    off = (rows * cols + 15) // 16 * 16
+    buf = np.zeros((off + 4 * rows + 15) // 16 * 16, np.uint8)
+    buf[: rows * cols] = q.ravel()
+    buf[off: off + 4 * rows] = _c(f["s"], np.float32).view(np.uint8)
+    return buf
+
+
+def unpack_fp8(buf: np.ndarray, rows: int, cols: int) -> dict:
+    b = _c(buf, np.uint8)
+    off = (rows * cols + 15) // 16 * 16
+    return {"q": b[: rows * cols].reshape(rows, cols).copy(),
+            "s": b[off: off + 4 * rows].copy().view(np.float32)}
+
+
+def matmul_fp8(fx: dict, fw: dict, mi=None, ni=None):
+    """Dynamic per-token W8A8 oracle: Y = s_m s_n sum_k e4m3(qx) e4m3(qw)
+    (exact), with the normaliser s_m s_n sum |e4m3(qx) e4m3(qw)|; all
+    outputs or the pairs (mi, ni)."""
+    qx, qw = _c(fx["q"], np.uint8), _c(fw["q"], np.uint8)
+    M, K = qx.shape
+    N = qw.shape[0]
+    full = mi is None
+    if full:
+        mm, nn = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+        mi, ni = mm.ravel(), nn.ravel()
+    mi, ni = _c(mi, np.int64), _c(ni, np.int64)
+    Y = np.empty(mi.size, np.float64)
+    den = np.empty(mi.size, np.float64)
+    _L().oracle_matmul_fp8(_p(qx), _p(_c(fx["s"], np.float32)), _p(qw), _p(_c(fw["s"], np.float32)), K,
+                           _p(mi), _p(ni), mi.size, _p(Y), _p(den))
+    if full:
+        return Y.reshape(M, N), den.reshape(M, N)
+    return Y, den
 
 
 def more_layout(fmt: str, rows: int, cols: int):

@@ -1078,3 +1078,120 @@ void oracle_unpack_leg(int64_t fmt, const uint8_t *buf, int64_t rows, int64_t co
         m16[b] = affine ? get_u16(buf + (five ? o[3] : o[2]) + 2 * b) : 0;
     }
 }
+
+/* ------------------------------------------------------------------ */
+/* FP8 E4M3 with per-row (channel) scales; W8A16 and dynamic W8A8      */
+/* ------------------------------------------------------------------ */
+/*
+ * Page "Quantization types", section "FP8": E4M3 FP8 (4-bit exponent, 3-bit
+ * mantissa) produced by ISQ; symmetric E4M3 weights with tensor, channel or
+ * block scales; W8A16 converts each weight tile to BF16 inside the GEMM;
+ * dynamic per-token W8A8 quantizes the activations per token before an FP8
+ * GEMM.  Readings: channel (per output row) scales; the E4M3 variant
+ * without infinities (largest finite 448, exponent bias 7, subnormals of
+ * 2^-9); a scale is s = max|x| / 448 in binary32 and a code is E4M3(x / s),
+ * rounded to nearest even after the binary32 division and saturated to
+ * +-448; s = 0 gives codes 0.  Values: s * e4m3(q); the W8A8 product is
+ * s_m s_n sum_k e4m3(qx) e4m3(qw), exact in fp64.
+ */
+
+/* E4M3 bits -> value (exact).  0x7F / 0xFF are NaN (never produced here). */
+double oracle_e4m3_value(uint8_t b)
+{
+    int sgn = b >> 7, e = (b >> 3) & 15, m = b & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9); /* m/8 * 2^-6 */
+    else
+        v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sgn ? -v : v;
+}
+
+/* binary32 -> E4M3 bits: round to nearest, ties to even, saturate to 448. */
+uint8_t oracle_e4m3_from_f32(float v)
+{
+    uint8_t sgn = signbit(v) ? 0x80 : 0;
+    double a = fabs((double)v);
+    if (a >= 448.0)
+        return (uint8_t)(sgn | 0x7E); /* 448 = 1.75 * 2^8 */
+    /* the grid near a: spacing 2^(e-10) for normals (e = floor(log2 a) >= -6), 2^-9 below */
+    int e;
+    frexp(a, &e);          /* a = f * 2^e, f in [0.5, 1) */
+    e -= 1;                /* a in [2^e, 2^(e+1)) */
+    double ulp = e < -6 ? ldexp(1.0, -9) : ldexp(1.0, e - 3);
+    double k = a / ulp;    /* exact: a is binary32, ulp a power of two */
+    double r = floor(k);
+    double rest = k - r;
+    if (rest > 0.5 || (rest == 0.5 && fmod(r, 2.0) == 1.0))
+        r += 1.0;
+    double q = r * ulp;    /* the rounded magnitude, exact */
+    if (q >= 448.0)
+        return (uint8_t)(sgn | 0x7E);
+    if (q == 0.0)
+        return sgn;
+    int qe;
+    frexp(q, &qe);
+    qe -= 1;
+    uint8_t bits;
+    if (qe < -6)
+        bits = (uint8_t)(q / ldexp(1.0, -9)); /* subnormal: m = q / 2^-9 */
+    else
+        bits = (uint8_t)(((qe + 7) << 3) | (int)((q / ldexp(1.0, qe) - 1.0) * 8.0));
+    return (uint8_t)(sgn | bits);
+}
+
+void oracle_e4m3_from_f32_array(const float *in, int64_t n, uint8_t *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i++)
+        out[i] = oracle_e4m3_from_f32(in[i]);
+}
+
+/* rows*cols bf16 -> codes [rows][cols] and s [rows] (binary32 bits).
+ * Steps: a = max|x| (exact), s = a / 448, code = E4M3(x / s) (0 if s == 0). */
+void oracle_quantize_fp8(const uint16_t *w, int64_t rows, int64_t cols, uint8_t *q, float *s)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; r++) {
+        const uint16_t *x = w + r * cols;
+        float a = 0.0f;
+        for (int64_t i = 0; i < cols; i++) {
+            float ax = fabsf(bf16_in(x[i]));
+            if (ax > a)
+                a = ax;
+        }
+        float sc = a / 448.0f;
+        s[r] = sc;
+        for (int64_t i = 0; i < cols; i++)
+            q[r * cols + i] = sc == 0.0f ? 0 : oracle_e4m3_from_f32(bf16_in(x[i]) / sc);
+    }
+}
+
+/* W = s_row * e4m3(q), exact in fp64 */
+void oracle_dequant_fp8(const uint8_t *q, const float *s, int64_t rows, int64_t cols, double *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t e = 0; e < rows * cols; e++)
+        out[e] = (double)s[e / cols] * oracle_e4m3_value(q[e]);
+}
+
+/* W8A8: Y[m][n] = sx[m] sw[n] sum_k e4m3(qx[m][k]) e4m3(qw[n][k]) (exact
+ * sum in fp64), den = sx sw sum |..|, for a list of (m, n) pairs. */
+void oracle_matmul_fp8(const uint8_t *qx, const float *sx, const uint8_t *qw, const float *sw, int64_t K,
+                       const int64_t *mi, const int64_t *ni, int64_t npairs, double *Y, double *den)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < npairs; i++) {
+        double acc = 0.0, a = 0.0;
+        for (int64_t k = 0; k < K; k++) {
+            double p = oracle_e4m3_value(qx[mi[i] * K + k]) * oracle_e4m3_value(qw[ni[i] * K + k]);
+            acc += p;
+            a += fabs(p);
+        }
+        double sc = (double)sx[mi[i]] * (double)sw[ni[i]];
+        Y[i] = sc * acc;
+        den[i] = sc * a;
+    }
+}

@@ -652,3 +652,89 @@ def test_more_formats_pack_roundtrip_and_bytes(fmt):
         nz = {int(i): int(b[i]) for i in np.flatnonzero(b)}
         dplane = 16 * B if fmt in ("q4_0", "q4_1") else 20 * B
         assert nz == {dplane + 18: 0x34, dplane + 19: 0x12}
+
+
+# ----------------------------------------------------------------------------
+# FP8 E4M3 with per-row scales (oracle.c, "FP8 E4M3 ...")
+# ----------------------------------------------------------------------------
+
+def _e4m3_closed_form(b):
+    s, e, m = b >> 7, (b >> 3) & 15, b & 7
+    if e == 15 and m == 7:
+        return float("nan")
+    v = (m / 8.0) * 2.0 ** -6 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7)
+    return -v if s else v
+
+
+def test_e4m3_decode_every_code():
+    """All 256 codes against the closed form (bias 7, 3 mantissa bits,
+    subnormals m/8 * 2^-6, no infinities, NaN at 0x7F / 0xFF) and against
+    torch's float8_e4m3fn (a library routine)."""
+    import torch
+    t = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    for b in range(256):
+        v = oracle.e4m3_value(b)
+        want = _e4m3_closed_form(b)
+        assert (np.isnan(v) and np.isnan(want) and np.isnan(t[b])) or (v == want == t[b]), b
+    assert oracle.e4m3_value(0x7E) == 448.0 and oracle.e4m3_value(0x01) == 2.0 ** -9
+
+
+def test_e4m3_encode_ties_and_saturation():
+    """Round to nearest even on every exact midpoint between neighbouring
+    positive codes and on random values, against torch's cast (within
+    +-448); saturation to +-448 by hand above it."""
+    import torch
+    pos = np.array([oracle.e4m3_value(b) for b in range(0x7F)])
+    mids = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)
+    assert np.array_equal(mids.astype(np.float64), (pos[:-1] + pos[1:]) / 2)   # the midpoints are exact in fp32
+    rng = np.random.default_rng(5)
+    rnd = (rng.standard_normal(400_000) * np.exp(rng.uniform(-14, 7, 400_000))).astype(np.float32)
+    x = np.concatenate([mids, -mids, rnd[np.abs(rnd) <= 448], np.float32([0.0, 448.0, -448.0, 2 ** -10, 2 ** -11])])
+    got = oracle.e4m3_from_f32_array(x)
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, want)
+    # ties go to the even code: 1 + 1/16 lies between 1 (0x38) and 1.125 (0x39) -> 0x38
+    assert oracle.e4m3_from_f32_array([1.0625, 1.1875])[0] == 0x38
+    assert oracle.e4m3_from_f32_array([1.1875])[0] == 0x3A          # between 1.125 and 1.25 -> 1.25 (even)
+    sat = oracle.e4m3_from_f32_array([448.5, 464.0, 1e6, -500.0, 3e38])
+    assert sat.tolist() == [0x7E, 0x7E, 0x7E, 0xFE, 0x7E]
+
+
+def test_fp8_quantizer_worked_rows():
+    """Row with max 448: s = 1 and the codes are the values' own E4M3
+    patterns; row of zeros: s = 0, codes 0; row with max 2: s = 2/448 and
+    the max element maps to the top code 0x7E."""
+    x = np.zeros((3, 256), np.float32)
+    x[0, :6] = [448.0, -224.0, 1.0, 0.5, 2.0 ** -9, -0.09375]
+    x[2, :3] = [2.0, -1.0, 0.25]
+    f = oracle.quantize_fp8(synth.bf16_bits_from_f32(x))
+    assert f["s"].tolist() == [1.0, 0.0, np.float32(2.0) / np.float32(448.0)]
+    # 448 = 1.75 2^8: 0x7E; -224 = -1.75 2^7: 0xF6; 1: 0x38; 0.5: 0x30; 2^-9: subnormal 0x01;
+    # -0.09375 = -1.5 2^-4: exponent field 3, mantissa 4: 0x9C
+    assert f["q"][0, :6].tolist() == [0x7E, 0xF6, 0x38, 0x30, 0x01, 0x9C]
+    assert not f["q"][1].any()
+    assert f["q"][2, 0] == 0x7E
+    W = oracle.dequant_fp8(f)
+    assert W[0, 1] == -224.0 and W[2, 0] == 448.0 * float(f["s"][2])
+
+
+def test_fp8_round_trip_bound_and_matmul_bruteforce():
+    """|s e4m3(q) - x| <= s * half a code step (2^-4 relative for normals,
+    s 2^-10 absolute below); the W8A8 product equals a brute-force fp64 sum
+    over the decoded values."""
+    w = synth.weights_bf16(8800, 40, 512, outliers=True)
+    x = synth.bf16_bits_to_f32(w).astype(np.float64)
+    f = oracle.quantize_fp8(w)
+    W = oracle.dequant_fp8(f)
+    s = f["s"].astype(np.float64)[:, None]
+    a = np.abs(x / s)
+    bound = np.where(a >= 2.0 ** -6, 2.0 ** (np.floor(np.log2(np.maximum(a, 2.0 ** -6))) - 4), 2.0 ** -10) * s
+    assert np.all(np.abs(W - x) <= bound * (1 + 1e-6))
+    xa = synth.activations_bf16(8801, 3, 512)
+    fx = oracle.quantize_fp8(xa)
+    Y, den = oracle.matmul_fp8(fx, f)
+    vals = np.array([oracle.e4m3_value(b) for b in range(256)])
+    dx, dw = vals[fx["q"]], vals[f["q"]]
+    want = (fx["s"].astype(np.float64)[:, None] * f["s"].astype(np.float64)[None, :]) * (dx @ dw.T)
+    assert np.allclose(Y, want, rtol=1e-12, atol=0)
+    assert np.all(den >= np.abs(Y))
