@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0     # dense MFMA bf16, published
 INT8_PEAK_TOPS = 5000.0       # dense MFMA int8, published
+FP8_PEAK_TFLOPS = 5000.0      # dense MFMA fp8, published
 MALL_BYTES = 256 << 20        # Infinity Cache
 
 
@@ -51,7 +52,7 @@ def parse():
     ap.add_argument("--quick", action="store_true", help="headline only (for profiling runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--parts", default=None,
-                    help="comma-separated parts measured after the headline: batched, glu, formats, prefill, isq "
+                    help="comma-separated parts measured after the headline: batched, glu, formats, fp8, prefill, isq "
                          "(default: all of them, none with --quick)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only copy a buffer of BYTES bytes 10 times (the reference kernel that scales "
@@ -249,7 +250,7 @@ def main():
     del W
 
     which = set(args.parts.split(",")) if args.parts else (set() if args.quick else
-                                                           {"batched", "glu", "formats", "prefill", "isq"})
+                                                           {"batched", "glu", "formats", "fp8", "prefill", "isq"})
     if which:
         parts.update(bench_parts(torch, ql, synth, dev, bf16_dev, which))
     result["parts"] = parts
@@ -382,6 +383,37 @@ def bench_parts(torch, ql, synth, dev, bf16_dev, which):
             del copies, blocks, out
         parts["further_formats_14336x4096"] = rows
         del W, xs
+        torch.cuda.empty_cache()
+
+    if "fp8" in which:
+        # FP8 E4M3 with per-row scales: ISQ and W8A16 GEMV at 14336 x 4096, and
+        # dynamic per-token W8A8 at the prefill shape on the FP8 MFMA path
+        log("fp8: ISQ + W8A16 GEMV 14336x4096, W8A8 prefill 2048x4096x14336")
+        N, K = 14336, 4096
+        W = bf16_dev(synth.weights_bf16(synth.seed_for(4, 0), N, K))
+        b8 = ql.isq("fp8", W)
+        out = torch.empty_like(b8)
+        isq_ms = timed_calls(lambda i: ql.isq("fp8", W, out=out), 10)
+        R = copies_for(b8.numel())
+        copies = [b8] + [b8.clone() for _ in range(R - 1)]
+        x1 = bf16_dev(synth.activations_bf16(synth.seed_for(2, 1), 1, K))
+        Y1 = torch.empty((1, N), dtype=torch.float32, device=dev)
+        g1 = timed_calls(lambda i: ql.qmatmul("fp8", copies[i % R], x1, N, out=Y1), 2 * R)
+        M = 2048
+        X = bf16_dev(synth.activations_bf16(synth.seed_for(4, 1), M, K))
+        ws = torch.empty(ql.workspace_bytes("fp8", "mfma_fp8", M, K), dtype=torch.uint8, device=dev)
+        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        fl = 2.0 * M * N * K
+        pf = timed_calls(lambda i: ql.qmatmul("fp8", copies[i % 2], X, N, out=Y, path="mfma_fp8", workspace=ws), 10)
+        parts["fp8_e4m3_14336x4096"] = {
+            "isq_us": round(isq_ms * 1e3, 1), "isq_GBps": round((W.numel() * 2 + b8.numel()) / isq_ms / 1e6, 1),
+            "w8a16_gemv_m1_us": round(g1 * 1e3, 2), "w8a16_gemv_weight_GBps": round(b8.numel() / g1 / 1e6, 1),
+            "w8a8_prefill_m2048_us": round(pf * 1e3, 1), "w8a8_TOPs": round(fl / pf / 1e9, 1),
+            "w8a8_mfma_frac": round(fl / pf / 1e9 / FP8_PEAK_TFLOPS, 4),
+            "includes": "per-token activation quantization"}
+        log(f"  ISQ {isq_ms * 1e3:.0f} us, W8A16 GEMV M=1 {g1 * 1e3:.2f} us ({b8.numel() / g1 / 1e6:.0f} GB/s), "
+            f"W8A8 prefill {pf * 1e3:.0f} us {fl / pf / 1e9:.0f} TFLOP/s")
+        del copies, b8, out, W, X, ws, Y
         torch.cuda.empty_cache()
 
     if "prefill" in which:

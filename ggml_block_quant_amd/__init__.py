@@ -24,9 +24,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqlinear.so")
 
 FMT = {"q8_0": 0, "q4k": 1, "q6k": 2, "q2k": 3, "q3k": 4, "q5k": 5, "q8k": 6,
-       "q4_0": 7, "q4_1": 8, "q5_0": 9, "q5_1": 10, "q8_1": 11}
+       "q4_0": 7, "q4_1": 8, "q5_0": 9, "q5_1": 10, "q8_1": 11, "fp8": 12}
 FMT_NAME = {v: k for k, v in FMT.items()}
-PATH = {"auto": 0, "gemv": 1, "mfma_bf16": 2, "mfma_i8": 3}
+PATH = {"auto": 0, "gemv": 1, "mfma_bf16": 2, "mfma_i8": 3, "mfma_fp8": 4}
 ACT = {"silu": 0, "relu": 1, "sigmoid": 2}
 
 Q_OK, Q_EINVAL, Q_ESHAPE, Q_EALIGN, Q_ENOTSUP, Q_EHIP = 0, -1, -2, -3, -4, -5

@@ -12,7 +12,7 @@ bool implemented(int fmt)
 {
     return fmt == QFMT_Q8_0 || fmt == QFMT_Q4K || fmt == QFMT_Q6K || ql::generic_fmt(fmt);
 }
-bool known(int fmt) { return fmt >= QFMT_Q8_0 && fmt <= QFMT_Q8_1; }
+bool known(int fmt) { return fmt >= QFMT_Q8_0 && fmt <= QFMT_FP8; }
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 constexpr int64_t kMaxElems = int64_t(1) << 40;
@@ -100,11 +100,11 @@ int q_act_quantize(const void *X_bf16, int64_t M, int64_t K, void *out_blocks, v
 
 size_t qmatmul_workspace_bytes(int fmt, int path, int64_t M, int64_t K)
 {
-    if (path != QPATH_MFMA_I8 || fmt != QFMT_Q8_0)
-        return 0;
-    if (check_tensor(QFMT_Q8_0, M, K, QLINEAR_MAX_M) != Q_OK)
-        return 0;
-    return (size_t)ql::planes_of(ql::FMT_Q8_0, M, K).total;
+    if (path == QPATH_MFMA_I8 && fmt == QFMT_Q8_0 && check_tensor(QFMT_Q8_0, M, K, QLINEAR_MAX_M) == Q_OK)
+        return (size_t)ql::planes_of(ql::FMT_Q8_0, M, K).total;
+    if (path == QPATH_MFMA_FP8 && fmt == QFMT_FP8 && check_tensor(QFMT_FP8, M, K, QLINEAR_MAX_M) == Q_OK)
+        return (size_t)ql::planes_of(ql::FMT_FP8, M, K).total;
+    return 0;
 }
 
 int qmatmul_ex(int fmt, const void *blocks, const void *X_bf16, float *Y_fp32, int64_t M, int64_t N,
@@ -146,6 +146,21 @@ int qmatmul_ex(int fmt, const void *blocks, const void *X_bf16, float *Y_fp32, i
         if (st != Q_OK)
             return st;
         return status_of(ql::launch_gemm_i8(B, ws, Y_fp32, M, N, K, s));
+    }
+    case QPATH_MFMA_FP8: {
+        if (fmt != QFMT_FP8)
+            return Q_ENOTSUP;
+        if (!workspace)
+            return Q_EINVAL;
+        if (!aligned16(workspace))
+            return Q_EALIGN;
+        if (workspace_bytes < qmatmul_workspace_bytes(fmt, path, M, K))
+            return Q_EINVAL;
+        auto *ws = static_cast<uint8_t *>(workspace);
+        st = status_of(ql::launch_isq(ql::FMT_FP8, X, M, K, ws, s));
+        if (st != Q_OK)
+            return st;
+        return status_of(ql::launch_gemm_fp8(B, ws, Y_fp32, M, N, K, s));
     }
     default:
         return Q_EINVAL;
@@ -311,8 +326,8 @@ int q_fmt_supported(int fmt) { return implemented(fmt) ? 1 : 0; }
 
 const char *q_fmt_name(int fmt)
 {
-    static const char *names[] = {"q8_0", "q4k", "q6k", "q2k", "q3k", "q5k",
-                                  "q8k", "q4_0", "q4_1", "q5_0", "q5_1", "q8_1"};
+    static const char *names[] = {"q8_0", "q4k", "q6k", "q2k", "q3k", "q5k", "q8k",
+                                  "q4_0", "q4_1", "q5_0", "q5_1", "q8_1", "fp8"};
     return known(fmt) ? names[fmt] : nullptr;
 }
 

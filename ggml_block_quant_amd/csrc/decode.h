@@ -29,6 +29,14 @@ __device__ __forceinline__ void unpack_nibbles_eo(uint32_t d, int q[8])
     }
 }
 
+// E4M3 (no infinities, bias 7) code -> value, exact in fp32
+__device__ __forceinline__ float e4m3_value(uint32_t b)
+{
+    const int e = (int)((b >> 3) & 15u), m = (int)(b & 7u);
+    const float v = e ? __builtin_ldexpf(1.0f + (float)m * 0.125f, e - 7) : (float)m * 0x1p-9f;
+    return (b & 0x80u) ? -v : v;
+}
+
 template <int FMT>
 __device__ __forceinline__ void dequant8(const uint8_t *__restrict__ B, const Planes &p, int64_t t, float v[8])
 {
@@ -108,6 +116,15 @@ __device__ __forceinline__ void dequant8(const uint8_t *__restrict__ B, const Pl
 #pragma unroll
         for (int k = 0; k < 8; k++)
             v[k] = fmaf(S, (float)((c >> (2 * k)) & 3u), -M);
+    } else if constexpr (FMT == FMT_FP8) {
+        // codes of row t*8/K, each times the row's scale (rounded once)
+        const uint2 c = reinterpret_cast<const uint2 *>(B)[t];
+        const float sc = reinterpret_cast<const float *>(B + p.scales)[(8 * t) / p.K];
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            v[k] = sc * e4m3_value(c.x >> (8 * k));
+            v[k + 4] = sc * e4m3_value(c.y >> (8 * k));
+        }
     } else {
         // legacy blocks of 32: element 8 (t & 3) + k at nibble k of dword t,
         // the fifth bit (Q5_0, Q5_1) at bit k of byte t of the high-bit plane
@@ -141,6 +158,7 @@ __device__ __forceinline__ void dequant8_any(int fmt, const uint8_t *__restrict_
     case FMT_Q4_0: dequant8<FMT_Q4_0>(B, p, t, v); break;
     case FMT_Q4_1: dequant8<FMT_Q4_1>(B, p, t, v); break;
     case FMT_Q5_0: dequant8<FMT_Q5_0>(B, p, t, v); break;
+    case FMT_FP8: dequant8<FMT_FP8>(B, p, t, v); break;
     default: dequant8<FMT_Q5_1>(B, p, t, v); break;
     }
 }

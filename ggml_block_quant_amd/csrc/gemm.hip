@@ -1119,6 +1119,60 @@ __global__ __launch_bounds__(256) void gemm_gen_kernel(const uint8_t *__restrict
 }
 
 // ---------------------------------------------------------------------------
+// FP8 W8A8 (dynamic per-token activation scales, per-channel weight scales):
+// both operands are E4M3 codes (X quantized per row into the workspace by
+// the same quantizer as the weights); a workgroup of four waves owns 64 rows
+// of W and 16*TM tokens, and lane (g, r) feeds 8 codes of W row r and of X
+// row r (k = 8g..8g+7 of a 32-wide step) straight into
+// v_mfma_f32_16x16x32_fp8_fp8 -- exact products, fp32 sums; the scales
+// multiply the finished sums.  K splits add into a zeroed Y.
+// ---------------------------------------------------------------------------
+template <int TM>
+__global__ __launch_bounds__(256) void gemm_fp8_kernel(const uint8_t *__restrict__ Wq, const float *__restrict__ ws,
+                                                       const uint8_t *__restrict__ Xq, const float *__restrict__ xs,
+                                                       float *__restrict__ Y, int M, int N, int K, int steps_per_split)
+{
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int g = lane >> 4, r16 = lane & 15;
+    const int n = blockIdx.x * 64 + 16 * wv + r16;
+    const uint8_t *wr = Wq + (int64_t)min(n, N - 1) * K;
+    const int m0 = blockIdx.y * 16 * TM;
+    const int s0 = blockIdx.z * steps_per_split, s1 = min(K / 32, s0 + steps_per_split);
+    f32x4_t acc[TM];
+    const uint8_t *xr[TM];
+#pragma unroll
+    for (int j = 0; j < TM; j++) {
+        acc[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        xr[j] = Xq + (int64_t)min(m0 + 16 * j + r16, M - 1) * K;
+    }
+    for (int s = s0; s < s1; s++) {
+        const long b = *reinterpret_cast<const long *>(wr + 32 * s + 8 * g);
+#pragma unroll
+        for (int j = 0; j < TM; j++) {
+            const long a = *reinterpret_cast<const long *>(xr[j] + 32 * s + 8 * g);
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, acc[j], 0, 0, 0);
+        }
+    }
+    if (n >= N)
+        return;
+    const float sw = ws[n];
+    const bool split = gridDim.z > 1;
+#pragma unroll
+    for (int j = 0; j < TM; j++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int m = m0 + 16 * j + 4 * g + i;
+            if (m < M) {
+                const float v = acc[j][i] * (xs[m] * sw);
+                if (split)
+                    atomicAdd(Y + (int64_t)m * N + n, v);
+                else
+                    Y[(int64_t)m * N + n] = v;
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------
 // Q8_0 x Q8_0 int8 path
 // ---------------------------------------------------------------------------
 constexpr int BN = 128;     // n tile
@@ -1480,8 +1534,30 @@ hipError_t launch_gemm_gen(int fmt, const uint8_t *blocks, const uint16_t *X, fl
     case FMT_Q4_1: return gen_tm<FMT_Q4_1>(blocks, X, Y, M, N, K, s);
     case FMT_Q5_0: return gen_tm<FMT_Q5_0>(blocks, X, Y, M, N, K, s);
     case FMT_Q5_1: return gen_tm<FMT_Q5_1>(blocks, X, Y, M, N, K, s);
+    case FMT_FP8: return gen_tm<FMT_FP8>(blocks, X, Y, M, N, K, s);
     default: return hipErrorInvalidValue;
     }
+}
+
+template <int TM>
+hipError_t go_fp8(const uint8_t *wb, const uint8_t *xb, float *Y, int64_t M, int64_t N, int64_t K, hipStream_t s)
+{
+    const Planes pw = planes_of(FMT_FP8, N, K), px = planes_of(FMT_FP8, M, K);
+    const int64_t gx = (N + 63) / 64, gy = (M + 16 * TM - 1) / (16 * TM);
+    const int steps = (int)(K / 32);
+    int sp = 1;
+    while (gx * gy * sp < 512 && sp < 32 && steps / (2 * sp) >= 8)
+        sp *= 2;
+    const int per = (steps + sp - 1) / sp;
+    if (sp > 1) {
+        const hipError_t e = zero_y(Y, M * N, s);
+        if (e != hipSuccess)
+            return e;
+    }
+    hipLaunchKernelGGL((gemm_fp8_kernel<TM>), dim3((unsigned)gx, (unsigned)gy, (unsigned)sp), dim3(256), 0, s, wb,
+                       reinterpret_cast<const float *>(wb + pw.scales), xb,
+                       reinterpret_cast<const float *>(xb + px.scales), Y, (int)M, (int)N, (int)K, per);
+    return hipGetLastError();
 }
 }  // namespace
 
@@ -1514,6 +1590,16 @@ hipError_t launch_glu_apply(const float *G, float *H, int64_t n, int act, hipStr
     g = g < 1 ? 1 : (g > 65536 ? 65536 : g);
     hipLaunchKernelGGL(glu_apply_kernel, dim3((unsigned)g), dim3(256), 0, s, G, H, n, act);
     return hipGetLastError();
+}
+
+hipError_t launch_gemm_fp8(const uint8_t *wblocks, const uint8_t *xblocks, float *Y, int64_t M, int64_t N,
+                           int64_t K, hipStream_t s)
+{
+    if (M <= 16)
+        return go_fp8<1>(wblocks, xblocks, Y, M, N, K, s);
+    if (M <= 32)
+        return go_fp8<2>(wblocks, xblocks, Y, M, N, K, s);
+    return go_fp8<4>(wblocks, xblocks, Y, M, N, K, s);
 }
 
 hipError_t launch_gemm_i8(const uint8_t *wblocks, const uint8_t *xblocks, float *Y, int64_t M, int64_t N,

@@ -854,6 +854,7 @@ hipError_t launch_gemv_gen(int fmt, const uint8_t *blocks, const uint16_t *X, fl
     case FMT_Q4_1: return gen_by_m<FMT_Q4_1>(blocks, p, X, Y, M, N, K, s);
     case FMT_Q5_0: return gen_by_m<FMT_Q5_0>(blocks, p, X, Y, M, N, K, s);
     case FMT_Q5_1: return gen_by_m<FMT_Q5_1>(blocks, p, X, Y, M, N, K, s);
+    case FMT_FP8: return gen_by_m<FMT_FP8>(blocks, p, X, Y, M, N, K, s);
     default: return hipErrorInvalidValue;
     }
 }

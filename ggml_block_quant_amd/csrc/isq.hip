@@ -478,6 +478,74 @@ Gaps gaps_of(int fmt, int64_t N, int64_t K, const Planes &p)
     return z;
 }
 
+// ---------------------------------------------------------------------------
+// FP8 E4M3 with a scale per row (page "Quantization types", section "FP8"):
+// one wave per row; s = max|x| / 448, codes E4M3(x / s) -- the binary32
+// quotient rounded to the nearest even E4M3 value, saturated to +-448 (the
+// variant without infinities).  Also the dynamic per-token quantizer of the
+// activations on the W8A8 path.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t e4m3_from_f32(float v)
+{
+    const uint32_t sgn = (__float_as_uint(v) >> 31) << 7;
+    const float a = fabsf(v);
+    if (a >= 448.0f)
+        return sgn | 0x7Eu;
+    if (a < 0x1p-6f)  // subnormal range: units of 2^-9 (a code of 8 is the smallest normal, 0x08)
+        return sgn | (uint32_t)rintf(a * 512.0f);
+    int e = (int)((__float_as_uint(a) >> 23) & 0xffu) - 127;  // a in [2^e, 2^(e+1)), e in [-6, 8]
+    float r = rintf(__builtin_ldexpf(a, 3 - e));                // 8 .. 16 steps of 2^(e-3)
+    if (r == 16.0f) {
+        e += 1;
+        r = 8.0f;
+    }
+    if (e > 8 || (e == 8 && r > 14.0f))
+        return sgn | 0x7Eu;
+    return sgn | (uint32_t)((e + 7) << 3) | (uint32_t)(r - 8.0f);
+}
+
+__global__ __launch_bounds__(256) void isq_fp8_kernel(const uint4 *__restrict__ W, int64_t N, int K,
+                                                      uint8_t *__restrict__ out, int64_t scales_off, int64_t pad,
+                                                      int npad)
+{
+    if (blockIdx.x == 0 && (int)threadIdx.x < npad)
+        out[pad + threadIdx.x] = 0;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= N)
+        return;  // the whole wave
+    const int T = K / 8;
+    const uint4 *w = W + row * T;
+    float a = 0.0f;
+    for (int i = lane; i < T; i += 64) {
+        float x[8];
+        load8(w[i], x);
+#pragma unroll
+        for (int k = 0; k < 8; k++)
+            a = fmaxf(a, fabsf(x[k]));
+    }
+#pragma unroll
+    for (int k = 32; k >= 1; k >>= 1)
+        a = fmaxf(a, __shfl_xor(a, k));
+    const float sc = a / 448.0f;
+    if (lane == 0)
+        reinterpret_cast<float *>(out + scales_off)[row] = sc;
+    uint2 *o = reinterpret_cast<uint2 *>(out + row * K);
+    for (int i = lane; i < T; i += 64) {
+        float x[8];
+        load8(w[i], x);
+        uint32_t lo = 0, hi = 0;
+        if (sc > 0.0f) {
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                lo |= e4m3_from_f32(x[k] / sc) << (8 * k);
+                hi |= e4m3_from_f32(x[k + 4] / sc) << (8 * k);
+            }
+        }
+        o[i] = make_uint2(lo, hi);
+    }
+}
+
 inline unsigned grid_for(int64_t tasks)
 {
     int64_t b = (tasks + 255) / 256;
@@ -505,6 +573,9 @@ hipError_t launch_isq(int fmt, const uint16_t *W, int64_t N, int64_t K, uint8_t 
                            reinterpret_cast<int8_t *>(out + p.scales),
                            reinterpret_cast<uint16_t *>(out + p.d), out + 210 * (N * K / 256),
                            (int)(p.total - 210 * (N * K / 256)));
+    else if (fmt == FMT_FP8)
+        hipLaunchKernelGGL(isq_fp8_kernel, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, s, w, N, (int)K, out,
+                           p.scales, p.scales + 4 * N, (int)(p.total - p.scales - 4 * N));
     else {
         const Gaps z = gaps_of(fmt, N, K, p);
         const dim3 grid(grid_for(tasks)), block(256);

@@ -18,12 +18,13 @@ enum Fmt {
     FMT_Q4_0 = 7,
     FMT_Q4_1 = 8,
     FMT_Q5_0 = 9,
-    FMT_Q5_1 = 10
+    FMT_Q5_1 = 10,
+    FMT_FP8 = 12
 };
 
 // the formats served by the generic kernels (exact decode of 8 elements at
 // a time, then an fp32 GEMV or a bf16 MFMA GEMM)
-inline bool generic_fmt(int fmt) { return fmt >= FMT_Q2K && fmt != 6 && fmt <= FMT_Q5_1; }
+inline bool generic_fmt(int fmt) { return (fmt >= FMT_Q2K && fmt != 6 && fmt <= FMT_Q5_1) || fmt == FMT_FP8; }
 
 // Byte offsets of the planes of a [N][K] block buffer (see q_blocks_bytes in
 // the public header).  G = N*K/256 groups, B = N*K/32 blocks of 32.
@@ -35,6 +36,7 @@ struct Planes {
     int64_t total;
     int64_t hi = 0;  // Q5K, Q3K, Q5_0, Q5_1: the top bit of each code
     int64_t m = 0;   // Q4_1, Q5_1: fp16 min per block
+    int64_t K = 0;   // FP8: row length (its scales are per row)
 };
 
 inline int64_t up16(int64_t v) { return (v + 15) / 16 * 16; }
@@ -44,6 +46,11 @@ inline Planes planes_of(int fmt, int64_t N, int64_t K)
     const int64_t E = N * K, G = E / 256, B = E / 32;
     Planes p{0, 0, 0, 0};
     switch (fmt) {
+    case FMT_FP8:  // E4M3 codes [N][K], then fp32 scales [N]
+        p.scales = up16(E);
+        p.total = up16(p.scales + 4 * N);
+        p.K = K;
+        return p;
     case FMT_Q5K:
         p.hi = 128 * G;
         p.scales = 160 * G;
@@ -138,6 +145,8 @@ hipError_t launch_glu_fused(int fmt, const uint8_t *gate, const uint8_t *up, con
 hipError_t launch_glu_apply(const float *G, float *H, int64_t n, int act, hipStream_t s);
 hipError_t launch_gemm_bf16(int fmt, const uint8_t *blocks, const uint16_t *X, float *Y,
                             int64_t M, int64_t N, int64_t K, hipStream_t s);
+hipError_t launch_gemm_fp8(const uint8_t *wblocks, const uint8_t *xblocks, float *Y, int64_t M, int64_t N,
+                           int64_t K, hipStream_t s);
 hipError_t launch_gemm_i8(const uint8_t *wblocks, const uint8_t *xblocks, float *Y, int64_t M,
                           int64_t N, int64_t K, hipStream_t s);
 

@@ -54,6 +54,11 @@
  *         m = min, codes in [0, 15] ([0, 31]), w = d*q + m, 20 (24) bytes.
  * These run on generic kernels (exact decode of 8 elements, then an fp32
  * GEMV or a bf16 MFMA GEMM) and need K % 256 == 0 as well.
+ *   FP8:  E4M3 codes (no infinities: largest finite 448) with one fp32 scale
+ *         per row s = max|x| / 448, codes E4M3(x / s) rounded to nearest
+ *         even and saturated (page "Quantization types", section "FP8":
+ *         symmetric E4M3 with channel scales).  W8A16 on the generic
+ *         kernels; W8A8 with per-token activation scales on QPATH_MFMA_FP8.
  */
 #ifndef QLINEAR_H
 #define QLINEAR_H
@@ -80,7 +85,8 @@ typedef enum {
     QFMT_Q4_1 = 8,
     QFMT_Q5_0 = 9,
     QFMT_Q5_1 = 10,
-    QFMT_Q8_1 = 11
+    QFMT_Q8_1 = 11,
+    QFMT_FP8 = 12 /* E4M3 codes with one fp32 scale per row (page section "FP8") */
 } qfmt;
 
 /* Matmul path.  AUTO: GEMV for M <= 2, bf16 MFMA GEMM above (the crossover
@@ -89,7 +95,8 @@ typedef enum {
     QPATH_AUTO = 0,
     QPATH_GEMV = 1,      /* fused dequant-GEMV, M <= 8 only */
     QPATH_MFMA_BF16 = 2, /* weights dequantized to bf16 in LDS, MFMA bf16 */
-    QPATH_MFMA_I8 = 3    /* Q8_0 weights only: X quantized to Q8_0, int8 MFMA */
+    QPATH_MFMA_I8 = 3,   /* Q8_0 weights only: X quantized to Q8_0, int8 MFMA */
+    QPATH_MFMA_FP8 = 4   /* FP8 weights only: X quantized per token to E4M3, FP8 MFMA (W8A8) */
 } qpath;
 
 enum {
@@ -124,7 +131,8 @@ enum {
  *   Q2K:  [codes 2-bit G*64][sc | m << 4, G*16][d, dmin G*4]
  *   Q4_0: [nibbles of q+8, B*16][d B*2]      Q4_1: [nibbles B*16][d B*2][m B*2]
  *   Q5_0: [low nibbles of q+16, B*16][fifth bits B*4][d B*2]
- *   Q5_1: [low nibbles B*16][fifth bits B*4][d B*2][m B*2]              */
+ *   Q5_1: [low nibbles B*16][fifth bits B*4][d B*2][m B*2]
+ *   FP8:  [E4M3 codes N*K, row-major][fp32 scale per row N*4]           */
 size_t q_blocks_bytes(int fmt, int64_t N, int64_t K);
 
 /* In-situ quantization (page "Quantization types": ISQ, --isq N).
@@ -153,13 +161,18 @@ int qmatmul(int fmt, const void *blocks, const void *X_bf16, float *Y_fp32, int6
             int64_t N, int64_t K, void *stream);
 
 /* Workspace bytes `qmatmul_ex` needs for (fmt, path, M, K): the Q8_0 blocks
- * of X for QPATH_MFMA_I8 (q_blocks_bytes(QFMT_Q8_0, M, K)), 0 otherwise. */
+ * of X for QPATH_MFMA_I8 (q_blocks_bytes(QFMT_Q8_0, M, K)), its FP8 codes
+ * and scales for QPATH_MFMA_FP8 (q_blocks_bytes(QFMT_FP8, M, K)), 0 otherwise. */
 size_t qmatmul_workspace_bytes(int fmt, int path, int64_t M, int64_t K);
 
 /* Quantized matmul on an explicit path.  QPATH_GEMV needs M <= 8.
  * QPATH_MFMA_I8 needs fmt == QFMT_Q8_0 and a device workspace of at least
  * qmatmul_workspace_bytes() bytes (16-byte aligned); on return it holds
- * the Q8_0 blocks of X (codes then scales).  Other paths ignore it. */
+ * the Q8_0 blocks of X (codes then scales).  QPATH_MFMA_FP8 (page section
+ * "FP8": dynamic per-token W8A8) needs fmt == QFMT_FP8 and a workspace of
+ * qmatmul_workspace_bytes() bytes, which on return holds X quantized per
+ * token (E4M3 codes, then one fp32 scale per row); Y = s_x s_w * the exact
+ * E4M3 products summed in fp32.  Other paths ignore the workspace. */
 int qmatmul_ex(int fmt, const void *blocks, const void *X_bf16, float *Y_fp32, int64_t M,
                int64_t N, int64_t K, int path, void *workspace, size_t workspace_bytes,
                void *stream);

@@ -44,6 +44,7 @@ def test_blocks_bytes():
     assert ql.blocks_bytes("q5_0", 4, 256) == 4 * 8 * 22
     assert ql.blocks_bytes("q5_1", 4, 256) == 4 * 8 * 24
     assert ql.blocks_bytes("q4_0", 4, 32) == 0         # the further formats need K % 256
+    assert ql.blocks_bytes("fp8", 3, 256) == 3 * 256 + 16   # codes, then 3 fp32 scales rounded up to 16
     assert ql.blocks_bytes(99, 4, 256) == 0
     # bits per weight: 8.5, 4.5, 6.5625 (nominal 8, 4, 6 on the page's tables)
     assert ql.blocks_bytes("q8_0", 1, 256) * 8 / 256 == 8.5
@@ -56,6 +57,8 @@ def test_workspace_bytes():
     assert ql.workspace_bytes("q8_0", "mfma_i8", 2048, 4096) == ql.blocks_bytes("q8_0", 2048, 4096)
     assert ql.workspace_bytes("q8_0", "mfma_bf16", 2048, 4096) == 0
     assert ql.workspace_bytes("q4k", "mfma_i8", 16, 4096) == 0
+    assert ql.workspace_bytes("fp8", "mfma_fp8", 2048, 4096) == 2048 * 4096 + 2048 * 4
+    assert ql.workspace_bytes("q8_0", "mfma_fp8", 16, 4096) == 0
 
 
 def test_policy_tables_match_the_page():
@@ -88,7 +91,8 @@ def test_supported_formats():
     assert all(ql.fmt_supported(f) for f in ("q2k", "q3k", "q5k", "q4_0", "q4_1", "q5_0", "q5_1"))
     assert not any(ql.fmt_supported(f) for f in ("q8k", "q8_1"))
     L = ql.lib()
-    assert L.q_fmt_name(1) == b"q4k" and L.q_fmt_name(42) is None
+    assert L.q_fmt_name(1) == b"q4k" and L.q_fmt_name(12) == b"fp8" and L.q_fmt_name(42) is None
+    assert ql.fmt_supported("fp8")
     for s in range(-6, 1):
         assert L.q_strerror(s)
 
@@ -132,7 +136,7 @@ def test_qmatmul_argument_errors():
     assert call(b=NULL) == ql.Q_EINVAL
     assert call(x=NULL) == ql.Q_EINVAL
     assert call(y=NULL) == ql.Q_EINVAL
-    assert call(fmt=12) == ql.Q_EINVAL
+    assert call(fmt=13) == ql.Q_EINVAL
     assert call(fmt=6) == ql.Q_ENOTSUP                 # Q8K
     assert call(y=MIS) == ql.Q_EALIGN
     assert call(K=128) == ql.Q_ESHAPE
@@ -146,6 +150,10 @@ def test_qmatmul_argument_errors():
     assert call(fmt=0, path=3) == ql.Q_EINVAL          # ... and a workspace
     assert call(fmt=0, path=3, ws=A, wsb=10) == ql.Q_EINVAL
     assert call(fmt=0, path=3, ws=MIS, wsb=1 << 20) == ql.Q_EALIGN
+    assert call(path=4) == ql.Q_ENOTSUP                # the FP8 path needs FP8 weights
+    assert call(fmt=12, path=4) == ql.Q_EINVAL         # ... and a workspace
+    assert call(fmt=12, path=4, ws=A, wsb=100) == ql.Q_EINVAL
+    assert call(fmt=13) == ql.Q_EINVAL
     assert L.qmatmul(1, A, A2, NULL, 4, 64, 256, NULL) == ql.Q_EINVAL
     assert ok
 
@@ -160,7 +168,7 @@ def test_embed_argument_errors():
     assert call(b=NULL) == ql.Q_EINVAL
     assert call(ids=NULL) == ql.Q_EINVAL
     assert call(out=NULL) == ql.Q_EINVAL
-    assert call(fmt=12) == ql.Q_EINVAL
+    assert call(fmt=13) == ql.Q_EINVAL
     assert call(fmt=11) == ql.Q_ENOTSUP                      # Q8_1: named, not implemented
     assert call(b=MIS) == ql.Q_EALIGN
     assert call(out=MIS) == ql.Q_EALIGN

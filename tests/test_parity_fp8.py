@@ -1,0 +1,100 @@
+"""GPU parity of FP8 E4M3 with per-row scales (page "Quantization types",
+section "FP8"): ISQ codes and scales bit-exact, exact dequantization, W8A16
+on the generic kernels, and dynamic per-token W8A8 on the FP8 MFMA path (the
+activation codes and scales in the workspace bit-exact, outputs within 1e-3
+of the oracle's exact product, normalised by s_x s_w sum |e4m3 e4m3|)."""
+import numpy as np
+import pytest
+import torch
+
+import ggml_block_quant_amd as ql
+import oracle
+import synth
+from gpu_util import check_outputs, to_dev_bf16
+from test_parity_isq import _edge_tensor
+
+pytestmark = pytest.mark.gpu
+
+
+def _isq(w):
+    return ql.isq("fp8", to_dev_bf16(w))
+
+
+@pytest.mark.parametrize("N,K", [(1, 256), (7, 512), (300, 4096), (5, 14336)])
+def test_isq_fp8_bit_exact(N, K):
+    w = synth.weights_bf16(10000 + K + N, N, K, outliers=True)
+    got = _isq(w).cpu().numpy()
+    want = oracle.pack_fp8(oracle.quantize_fp8(w))
+    assert np.array_equal(got, want)
+
+
+def test_isq_fp8_edge_tensor():
+    """Zero rows (with -0.0), constants, one-signed rows, ties, 1e30 / 1e-6 /
+    1e-30 magnitudes, isolated outliers."""
+    w = _edge_tensor()
+    assert np.array_equal(_isq(w).cpu().numpy(), oracle.pack_fp8(oracle.quantize_fp8(w)))
+
+
+def test_fp8_dequant_and_embed_exact():
+    N, K = 64, 1024
+    w = synth.weights_bf16(10100, N, K, outliers=True)
+    b = _isq(w)
+    ref = oracle.dequant_fp8(oracle.quantize_fp8(w)).astype(np.float32)   # s * value, rounded once
+    assert np.array_equal(ql.dequantize("fp8", b, N, K).cpu().numpy(), ref)
+    ids = np.array([0, 63, 5, -3, 64], np.int32)
+    got = ql.embed("fp8", b, N, K, torch.from_numpy(ids).cuda()).cpu().numpy()
+    assert np.array_equal(got, oracle.embed(ref.astype(np.float64), ids).astype(np.float32))
+
+
+def test_fp8_w8a16_paths_and_one_hot():
+    for N, K in ((7, 256), (300, 1024), (129, 4096)):
+        w = synth.weights_bf16(10200 + N, N, K, outliers=True)
+        b = _isq(w)
+        Wd = oracle.dequant_fp8(oracle.quantize_fp8(w))
+        for M, path in ((1, "auto"), (2, "gemv"), (8, "gemv"), (3, "auto"), (16, "mfma_bf16"), (130, "auto")):
+            x = synth.activations_bf16(10201 + M, M, K)
+            Yr, den = oracle.matmul_a16(Wd, x)
+            Y = ql.qmatmul("fp8", b, to_dev_bf16(x), N, path=path).cpu().numpy()
+            check_outputs(Y, Yr, den, f"fp8 w8a16 {path} M={M} N={N} K={K}")
+        x = np.zeros((3, K), np.uint16)
+        x[[0, 1, 2], [0, 77, K - 1]] = 0x3F80
+        Y = ql.qmatmul("fp8", b, to_dev_bf16(x), N, path="gemv").cpu().numpy()
+        assert np.array_equal(Y, Wd[:, [0, 77, K - 1]].T.astype(np.float32))
+
+
+def test_fp8_w8a8_path():
+    """Dynamic per-token W8A8: the workspace holds X's E4M3 codes and
+    scales bit for bit; outputs within the bar of the exact product."""
+    for N, K in ((7, 256), (300, 1024), (129, 4096)):
+        w = synth.weights_bf16(10300 + N, N, K, outliers=True)
+        b = _isq(w)
+        fw = oracle.quantize_fp8(w)
+        for M in (1, 9, 16, 40, 130):
+            x = synth.activations_bf16(10301 + M, M, K)
+            ws = torch.empty(ql.workspace_bytes("fp8", "mfma_fp8", M, K), dtype=torch.uint8, device="cuda")
+            Y = ql.qmatmul("fp8", b, to_dev_bf16(x), N, path="mfma_fp8", workspace=ws).cpu().numpy()
+            fx = oracle.quantize_fp8(x)
+            assert np.array_equal(ws.cpu().numpy(), oracle.pack_fp8(fx)), f"activation codes M={M} K={K}"
+            Yr, den = oracle.matmul_fp8(fx, fw)
+            check_outputs(Y, Yr, den, f"fp8 w8a8 M={M} N={N} K={K}")
+
+
+def test_fp8_w8a8_prefill_shape_sampled():
+    """The prefill shape (2048 tokens, 14336 x 4096 weights) on the W8A8
+    path, checked on 2048 sampled outputs."""
+    M, N, K = 2048, 14336, 4096
+    w = synth.weights_bf16(10400, N, K)
+    x = synth.activations_bf16(10401, M, K)
+    b = _isq(w)
+    ws = torch.empty(ql.workspace_bytes("fp8", "mfma_fp8", M, K), dtype=torch.uint8, device="cuda")
+    Y = ql.qmatmul("fp8", b, to_dev_bf16(x), N, path="mfma_fp8", workspace=ws).cpu().numpy()
+    rng = np.random.default_rng(10402)
+    mi = rng.integers(0, M, 2048)
+    ni = rng.integers(0, N, 2048)
+    mi[:2], ni[:2] = [0, M - 1], [0, N - 1]
+    rows_w, inv_w = np.unique(ni, return_inverse=True)
+    rows_x, inv_x = np.unique(mi, return_inverse=True)
+    fw = oracle.quantize_fp8(w[rows_w])
+    fx = oracle.quantize_fp8(x[rows_x])
+    Yr, den = oracle.matmul_fp8(fx, fw, inv_x, inv_w)
+    check_outputs(Y[mi, ni], Yr, den, "fp8 w8a8 prefill sampled")
