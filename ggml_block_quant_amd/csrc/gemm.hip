@@ -1172,6 +1172,95 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(const uint8_t *__restrict
         }
 }
 
+// Large-M FP8 W8A8 (prefill): output tile 128 tokens x 128 rows of W per
+// workgroup of four waves (wave (wm, wn) owns 64 x 64 = 4 x 4 MFMA tiles of
+// 16 x 16); K advances in stages of 64 codes through a double-buffered LDS
+// copy of both tiles (rows padded to 72 bytes: the 16 rows a fragment read
+// touches land on distinct banks); the next stage's global loads are in
+// flight while the current one is multiplied.
+constexpr int F8T = 128, F8K = 64, F8P = 72;
+
+__global__ __launch_bounds__(256) void gemm_fp8_tile_kernel(const uint8_t *__restrict__ Wq,
+                                                            const float *__restrict__ ws,
+                                                            const uint8_t *__restrict__ Xq,
+                                                            const float *__restrict__ xs, float *__restrict__ Y,
+                                                            int M, int N, int K)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t sa[2][F8T * F8P];  // X tile: [token][k]
+    __shared__ __attribute__((aligned(16))) uint8_t sb[2][F8T * F8P];  // W tile: [row][k]
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int wm = wv >> 1, wn = wv & 1;
+    const int g = lane >> 4, r16 = lane & 15;
+    const int m0 = blockIdx.y * F8T, n0 = blockIdx.x * F8T;
+    // global -> LDS: thread t moves 16 bytes of rows t/4 and 64 + t/4, column 16 (t % 4)
+    const int lr = tid >> 2, lc = 16 * (tid & 3);
+    const uint8_t *xa0 = Xq + (int64_t)min(m0 + lr, M - 1) * K + lc;
+    const uint8_t *xa1 = Xq + (int64_t)min(m0 + 64 + lr, M - 1) * K + lc;
+    const uint8_t *wb0 = Wq + (int64_t)min(n0 + lr, N - 1) * K + lc;
+    const uint8_t *wb1 = Wq + (int64_t)min(n0 + 64 + lr, N - 1) * K + lc;
+    uint4 ra0, ra1, rb0, rb1;
+    auto fetch = [&](int k0) {
+        ra0 = *reinterpret_cast<const uint4 *>(xa0 + k0);
+        ra1 = *reinterpret_cast<const uint4 *>(xa1 + k0);
+        rb0 = *reinterpret_cast<const uint4 *>(wb0 + k0);
+        rb1 = *reinterpret_cast<const uint4 *>(wb1 + k0);
+    };
+    auto stash = [&](int b) {
+        *reinterpret_cast<uint4 *>(&sa[b][lr * F8P + lc]) = ra0;
+        *reinterpret_cast<uint4 *>(&sa[b][(64 + lr) * F8P + lc]) = ra1;
+        *reinterpret_cast<uint4 *>(&sb[b][lr * F8P + lc]) = rb0;
+        *reinterpret_cast<uint4 *>(&sb[b][(64 + lr) * F8P + lc]) = rb1;
+    };
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    const int nst = K / F8K;
+    fetch(0);
+    stash(0);
+    __syncthreads();
+    for (int st = 0; st < nst; st++) {
+        const int b = st & 1;
+        if (st + 1 < nst)
+            fetch(F8K * (st + 1));
+#pragma unroll
+        for (int ks = 0; ks < 2; ks++) {
+            long af[4], bf[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                af[i] = *reinterpret_cast<const long *>(&sa[b][(64 * wm + 16 * i + r16) * F8P + 32 * ks + 8 * g]);
+                bf[i] = *reinterpret_cast<const long *>(&sb[b][(64 * wn + 16 * i + r16) * F8P + 32 * ks + 8 * g]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(af[i], bf[j], acc[i][j], 0, 0, 0);
+        }
+        if (st + 1 < nst)
+            stash(b ^ 1);
+        __syncthreads();
+    }
+    // lane holds D[m = 4g + r][n = r16] of tile (i, j)
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const int n = n0 + 64 * wn + 16 * j + r16;
+        if (n >= N)
+            continue;
+        const float sw = ws[n];
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int m = m0 + 64 * wm + 16 * i + 4 * g + r;
+                if (m < M)
+                    Y[(int64_t)m * N + n] = acc[i][j][r] * (xs[m] * sw);
+            }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Q8_0 x Q8_0 int8 path
 // ---------------------------------------------------------------------------
@@ -1595,6 +1684,13 @@ hipError_t launch_glu_apply(const float *G, float *H, int64_t n, int act, hipStr
 hipError_t launch_gemm_fp8(const uint8_t *wblocks, const uint8_t *xblocks, float *Y, int64_t M, int64_t N,
                            int64_t K, hipStream_t s)
 {
+    if (M >= 128) {
+        const Planes pw = planes_of(FMT_FP8, N, K), px = planes_of(FMT_FP8, M, K);
+        hipLaunchKernelGGL(gemm_fp8_tile_kernel, dim3((unsigned)((N + F8T - 1) / F8T), (unsigned)((M + F8T - 1) / F8T)),
+                           dim3(256), 0, s, wblocks, reinterpret_cast<const float *>(wblocks + pw.scales), xblocks,
+                           reinterpret_cast<const float *>(xblocks + px.scales), Y, (int)M, (int)N, (int)K);
+        return hipGetLastError();
+    }
     if (M <= 16)
         return go_fp8<1>(wblocks, xblocks, Y, M, N, K, s);
     if (M <= 32)
