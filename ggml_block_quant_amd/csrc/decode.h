@@ -119,7 +119,9 @@ __device__ __forceinline__ void dequant8(const uint8_t *__restrict__ B, const Pl
     } else if constexpr (FMT == FMT_FP8) {
         // codes of row t*8/K, each times the row's scale (rounded once)
         const uint2 c = reinterpret_cast<const uint2 *>(B)[t];
-        const float sc = reinterpret_cast<const float *>(B + p.scales)[(8 * t) / p.K];
+        const int64_t tpr = p.K / 8;  // tasks per row
+        const int64_t row = t < 0x80000000ll ? (int64_t)((uint32_t)t / (uint32_t)tpr) : t / tpr;
+        const float sc = reinterpret_cast<const float *>(B + p.scales)[row];
 #pragma unroll
         for (int k = 0; k < 4; k++) {
             v[k] = sc * e4m3_value(c.x >> (8 * k));

@@ -1089,16 +1089,30 @@ __global__ __launch_bounds__(256) void gemm_gen_kernel(const uint8_t *__restrict
 #pragma unroll
     for (int j = 0; j < TM; j++)
         xr[j] = X + (int64_t)min(m0 + 16 * j + r16, M - 1) * K;
-    for (int s = s0; s < s1; s++) {
-        float w[8];
-        dequant8<FMT>(B, p, nr * (K / 8) + 4 * s + g, w);
-        const bf16x8_t bw = __builtin_bit_cast(
-            bf16x8_t, make_uint4(pack_bf16(w[0], w[1]), pack_bf16(w[2], w[3]), pack_bf16(w[4], w[5]),
-                                 pack_bf16(w[6], w[7])));
+    // U steps at a time (the last group re-reads step s1 - 1 and skips it),
+    // so that their loads are in flight together
+    constexpr int U = 4;
+    for (int s = s0; s < s1; s += U) {
+        float w[U][8];
+        bf16x8_t xa[U][TM];
 #pragma unroll
-        for (int j = 0; j < TM; j++) {
-            const bf16x8_t xa = *reinterpret_cast<const bf16x8_t *>(xr[j] + 32 * s + 8 * g);
-            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bw, acc[j], 0, 0, 0);
+        for (int u = 0; u < U; u++) {
+            const int su = min(s + u, s1 - 1);
+            dequant8<FMT>(B, p, nr * (K / 8) + 4 * su + g, w[u]);
+#pragma unroll
+            for (int j = 0; j < TM; j++)
+                xa[u][j] = *reinterpret_cast<const bf16x8_t *>(xr[j] + 32 * su + 8 * g);
+        }
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            if (s + u < s1) {
+                const bf16x8_t bw = __builtin_bit_cast(
+                    bf16x8_t, make_uint4(pack_bf16(w[u][0], w[u][1]), pack_bf16(w[u][2], w[u][3]),
+                                         pack_bf16(w[u][4], w[u][5]), pack_bf16(w[u][6], w[u][7])));
+#pragma unroll
+                for (int j = 0; j < TM; j++)
+                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[u][j], bw, acc[j], 0, 0, 0);
+            }
         }
     }
     if (n >= N)

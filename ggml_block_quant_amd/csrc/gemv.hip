@@ -780,11 +780,11 @@ hipError_t by_m(const Geo &g, const uint16_t *X, float *Y, int M, int64_t N, hip
 }
 
 // ---------------------------------------------------------------------------
-// Generic GEMV for the formats without a tuned kernel (Q5K, Q3K, Q2K and the
-// legacy 32-element types): wave w of a workgroup owns row n; lane l takes
-// the 8-element tasks l, l + 64, ... of the row, decodes each exactly
-// (dequant8) and accumulates w * x in fp32; a butterfly over the wave sums
-// the lanes.
+// Generic GEMV for the formats without a tuned kernel (Q5K, Q3K, Q2K, the
+// legacy 32-element types, FP8): one wave per output row; lane l takes the
+// 8-element tasks l, l + 64, ... of the row, decodes them exactly
+// (dequant8) and accumulates w * x in fp32, and a butterfly over the wave
+// sums the lanes.
 // ---------------------------------------------------------------------------
 template <int FMT, int M>
 __global__ __launch_bounds__(256) void gemv_gen_kernel(const uint8_t *__restrict__ B, Planes p,
@@ -800,31 +800,42 @@ __global__ __launch_bounds__(256) void gemv_gen_kernel(const uint8_t *__restrict
 #pragma unroll
     for (int m = 0; m < M; m++)
         acc[m] = 0.0f;
-    for (int i = lane; i < T; i += 64) {
-        float w[8];
-        dequant8<FMT>(B, p, n * T + i, w);
+    // U tasks per lane per step with a trip count the whole wave shares
+    // (tail lanes re-read the last task and add nothing), so the loads of
+    // all U tasks are in flight together
+    constexpr int U = 4;
+    for (int i0 = 0; i0 < T; i0 += 64 * U) {
+        float w[U][8];
+        int ic[U];
 #pragma unroll
-        for (int m = 0; m < M; m++) {
-            const uint4 xv = *reinterpret_cast<const uint4 *>(X + (int64_t)m * K + 8 * i);
-            const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+        for (int u = 0; u < U; u++) {
+            ic[u] = min(i0 + 64 * u + lane, T - 1);
+            dequant8<FMT>(B, p, n * T + ic[u], w[u]);
+        }
 #pragma unroll
-            for (int k = 0; k < 4; k++) {
-                acc[m] = fmaf(w[2 * k], __uint_as_float(xw[k] << 16), acc[m]);
-                acc[m] = fmaf(w[2 * k + 1], __uint_as_float(xw[k] & 0xffff0000u), acc[m]);
+        for (int u = 0; u < U; u++) {
+            const bool live = i0 + 64 * u + lane < T;
+#pragma unroll
+            for (int m = 0; m < M; m++) {
+                const uint4 xv = *reinterpret_cast<const uint4 *>(X + (int64_t)m * K + 8 * ic[u]);
+                const uint32_t xw[4] = {live ? xv.x : 0u, live ? xv.y : 0u, live ? xv.z : 0u, live ? xv.w : 0u};
+#pragma unroll
+                for (int k = 0; k < 4; k++) {
+                    acc[m] = fmaf(w[u][2 * k], __uint_as_float(xw[k] << 16), acc[m]);
+                    acc[m] = fmaf(w[u][2 * k + 1], __uint_as_float(xw[k] & 0xffff0000u), acc[m]);
+                }
             }
         }
     }
 #pragma unroll
-    for (int m = 0; m < M; m++) {
+    for (int m = 0; m < M; m++)
 #pragma unroll
         for (int k = 32; k >= 1; k >>= 1)
             acc[m] += __shfl_xor(acc[m], k);
-    }
-    if (lane == 0) {
+    if (lane == 0)
 #pragma unroll
         for (int m = 0; m < M; m++)
             Y[(int64_t)m * N + n] = acc[m];
-    }
 }
 
 template <int FMT>
