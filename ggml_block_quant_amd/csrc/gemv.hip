@@ -545,16 +545,28 @@ __device__ __forceinline__ Chunk<FMT> chunk_of(const WLoad<FMT> &w)
 // the gate weights (g) and of the up weights (g2) as its two rows, and
 // writes act(gate) * up (same fp32 activation and product as the unfused
 // path); N is then the number of outputs F.
-template <int FMT, int M, int CPT, int R, bool GLU = false>
+//
+// FS (rows of exactly FS chunks, FS not a multiple of 64): the R rows of a
+// wave are one run of R * FS chunks and lane l takes chunks l, l + 64, ...
+// of the run, so no lane decodes a padding chunk (K = 5120: 160 chunks a
+// row, ten per lane for four rows instead of twelve slots).  A lane item
+// may then fall in either of two rows, picked per lane.
+template <int FMT, int M, int CPT, int R, bool GLU = false, int FS = 0>
 __global__ __launch_bounds__(64 * LW) void gemv_lds_kernel(Geo g, Geo g2, const uint16_t *__restrict__ X,
                                                            float *__restrict__ Y, int64_t N, int act)
 {
     static_assert(!GLU || R == 2, "gate and up rows");
+    static_assert(FS == 0 || (!GLU && FS % 8 == 0 && FS >= 64 && FS < 64 * CPT), "whole groups, a zero X slot");
+    // the wave's items: (row, chunk) pairs, NI per lane
+    constexpr int NI = FS ? (R * FS + 63) / 64 : R * CPT;
     constexpr int SLOTS = 64 * CPT;           // chunk slots per row
     constexpr bool SUMS = FMT != FMT_Q8_0;    // bias-correction sums (Q4K, Q6K)
     constexpr int XU = M * CPT;               // uint4 of X staged per thread
     __shared__ uint4 sx[M][4][SLOTS];         // quarter t of chunk c at sx[m][t][c]
-    __shared__ float2 ss[SUMS ? M : 1][SUMS ? SLOTS : 1];
+    // chunk sums; the last slot takes the stores of the lanes that own no sum
+    // (stores without branches, so the compiler keeps every X load ahead
+    // of the weight loads instead of sinking them into the branches)
+    __shared__ float2 ss[SUMS ? M : 1][SUMS ? SLOTS + 1 : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int S = g.K / 32;
@@ -571,16 +583,26 @@ __global__ __launch_bounds__(64 * LW) void gemv_lds_kernel(Geo g, Geo g2, const 
     }
     // every weight load of the wave; rows past N re-read row N-1 and slots
     // past the row end re-read its last chunk (their X is zero)
-    WLoad<FMT> w[R][CPT];
-#pragma unroll
-    for (int r = 0; r < R; r++) {
-        const int64_t n = GLU ? (n0 < N ? n0 : N - 1) : (n0 + r < N ? n0 + r : N - 1);
-#pragma unroll
-        for (int i = 0; i < CPT; i++) {
-            const int c = lane + 64 * i;
-            load_w<FMT>(GLU && r == 1 ? g2 : g, n, c < S ? c : S - 1, lane, w[r][i]);
+    auto item = [&](int i, int &r, int &c) {
+        if constexpr (FS != 0) {
+            const int f = min(lane + 64 * i, R * FS - 1);
+            r = f / FS;
+            c = f - r * FS;
+        } else {
+            r = i / CPT;
+            c = lane + 64 * (i % CPT);
         }
+    };
+    WLoad<FMT> w[NI];
+#pragma unroll
+    for (int i = 0; i < NI; i++) {
+        int r, c;
+        item(i, r, c);
+        const int64_t n = GLU ? (n0 < N ? n0 : N - 1) : (n0 + r < N ? n0 + r : N - 1);
+        load_w<FMT>(GLU && r == 1 ? g2 : g, n, c < S ? c : S - 1, lane, w[i]);
     }
+    // keep the staging below (and its wait for X) after every weight load
+    __builtin_amdgcn_sched_barrier(0);
     // stage X and the chunk sums (four consecutive lanes hold one chunk)
 #pragma unroll
     for (int j = 0; j < XU; j++) {
@@ -597,13 +619,10 @@ __global__ __launch_bounds__(64 * LW) void gemv_lds_kernel(Geo g, Geo g2, const 
             p += dpp_f<0xB1>(p);  // quarters t, t^1: one 16-element half
             if constexpr (FMT == FMT_Q4K) {
                 p += dpp_f<0x4E>(p);  // both halves: the chunk
-                if (t == 0)
-                    ss[m][c].x = p;
+                ss[m][t == 0 ? c : SLOTS].x = p;
             } else {
-                if (t == 0)
-                    ss[m][c].x = p;
-                if (t == 2)
-                    ss[m][c].y = p;
+                // t = 0: the first half (.x), t = 2: the second (.y)
+                reinterpret_cast<float *>(&ss[m][(t & 1) ? SLOTS : c])[t >> 1] = p;
             }
         }
     }
@@ -615,48 +634,74 @@ __global__ __launch_bounds__(64 * LW) void gemv_lds_kernel(Geo g, Geo g2, const 
 #pragma unroll
     for (int t = 0; t < V; t++)
         v[t] = 0.0f;
+    float acc[R][M];
 #pragma unroll
-    for (int r = 0; r < R; r++) {
-        float acc[M];
+    for (int r = 0; r < R; r++)
 #pragma unroll
         for (int m = 0; m < M; m++)
-            acc[m] = 0.0f;
+            acc[r][m] = 0.0f;
 #pragma unroll
-        for (int i = 0; i < CPT; i++) {
-            const int c = lane + 64 * i;
-            XChunk<M> xc;
+    for (int i = 0; i < NI; i++) {
+        int r, c;
+        item(i, r, c);
+        // X slot: items past the run (FS) read the zero slot FS
+        const int cx = FS != 0 && lane + 64 * i >= R * FS ? FS : c;
+        XChunk<M> xc;
+#pragma unroll
+        for (int m = 0; m < M; m++) {
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                const uint4 q = sx[m][t][cx];
+                xc.p[m][4 * t + 0] = q.x;
+                xc.p[m][4 * t + 1] = q.y;
+                xc.p[m][4 * t + 2] = q.z;
+                xc.p[m][4 * t + 3] = q.w;
+            }
+            if constexpr (FMT == FMT_Q4K) {
+                const float tot = ss[m][cx].x;
+                xc.s0[m] = 128.0f * tot;
+                xc.s1[m] = tot;
+            } else if constexpr (FMT == FMT_Q6K) {
+                const float2 h = ss[m][cx];
+                xc.s0[m] = 160.0f * h.x;
+                xc.s1[m] = 160.0f * h.y;
+            }
+        }
+        auto dot = [&](float (&a)[M]) {
+            const Chunk<FMT> ck = chunk_of<FMT>(w[i]);
+            if constexpr (FMT == FMT_Q4K)
+                q4k_dot<M>(ck, xc, c & 7, a, k);
+            else if constexpr (FMT == FMT_Q6K)
+                q6k_dot<M>(ck, xc, a, k);
+            else
+                q8_0_dot<M>(ck, xc, a);
+        };
+        // the rows this item can fall in (constants once the loop is
+        // unrolled; with FS >= 64 at most two)
+        constexpr int FD = FS ? FS : 1;
+        const int RLO = FS ? 64 * i / FD : i / CPT;
+        const int RHI = FS ? min((64 * i + 63) / FD, R - 1) : RLO;
+        if (RLO == RHI) {
+            dot(acc[RLO]);
+        } else {
+            float t[M];
+#pragma unroll
+            for (int m = 0; m < M; m++)
+                t[m] = 0.0f;
+            dot(t);
+            const bool hi = r > RLO;
 #pragma unroll
             for (int m = 0; m < M; m++) {
-#pragma unroll
-                for (int t = 0; t < 4; t++) {
-                    const uint4 q = sx[m][t][c];
-                    xc.p[m][4 * t + 0] = q.x;
-                    xc.p[m][4 * t + 1] = q.y;
-                    xc.p[m][4 * t + 2] = q.z;
-                    xc.p[m][4 * t + 3] = q.w;
-                }
-                if constexpr (FMT == FMT_Q4K) {
-                    const float tot = ss[m][c].x;
-                    xc.s0[m] = 128.0f * tot;
-                    xc.s1[m] = tot;
-                } else if constexpr (FMT == FMT_Q6K) {
-                    const float2 h = ss[m][c];
-                    xc.s0[m] = 160.0f * h.x;
-                    xc.s1[m] = 160.0f * h.y;
-                }
+                acc[RLO][m] += hi ? 0.0f : t[m];
+                acc[RLO + 1][m] += hi ? t[m] : 0.0f;
             }
-            const Chunk<FMT> ck = chunk_of<FMT>(w[r][i]);
-            if constexpr (FMT == FMT_Q4K)
-                q4k_dot<M>(ck, xc, c & 7, acc, k);
-            else if constexpr (FMT == FMT_Q6K)
-                q6k_dot<M>(ck, xc, acc, k);
-            else
-                q8_0_dot<M>(ck, xc, acc);
         }
+    }
+#pragma unroll
+    for (int r = 0; r < R; r++)
 #pragma unroll
         for (int m = 0; m < M; m++)
-            v[r * M + m] = acc[m];
-    }
+            v[r * M + m] = acc[r][m];
     const float tot = butterfly_sum<V>(v, lane);
     const int idx = butterfly_index<V>(lane);
     if constexpr (GLU) {
@@ -678,8 +723,14 @@ hipError_t go_lds(const Geo &g, const uint16_t *X, float *Y, int64_t N, hipStrea
     // K = 5120 (the 131072 x 5120 head: 10 % faster than one), one above
     constexpr int R = M != 1 ? 1 : CPT <= 2 ? 2 : CPT == 3 ? 4 : 1;
     const int64_t grid = (N + LW * R - 1) / (LW * R);
-    hipLaunchKernelGGL((gemv_lds_kernel<FMT, M, CPT, R>), dim3((unsigned)grid), dim3(64 * LW), 0, s, g, g, X, Y, N,
-                       0);
+    // K-quant rows of 160 chunks as one run per wave (Q8_0 gains nothing)
+    constexpr bool RUN = FMT != FMT_Q8_0 && M == 1 && CPT == 3;
+    if (RUN && g.K == 5120)
+        hipLaunchKernelGGL((gemv_lds_kernel<FMT, M, CPT, R, false, RUN ? 160 : 0>),
+                           dim3((unsigned)grid), dim3(64 * LW), 0, s, g, g, X, Y, N, 0);
+    else
+        hipLaunchKernelGGL((gemv_lds_kernel<FMT, M, CPT, R>), dim3((unsigned)grid), dim3(64 * LW), 0, s, g, g, X, Y,
+                           N, 0);
     return hipGetLastError();
 }
 

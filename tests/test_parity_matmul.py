@@ -62,6 +62,25 @@ def test_gemv_long_rows(fmt):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_row_runs_one_hot(fmt):
+    """K = 5120 (160 chunks a row), M = 1: the four rows of a wave form one
+    run of 640 chunks, ten per lane, and the items at lanes 0..31 / 32..63
+    of the third and eighth step fall in different rows.  One-hot X at
+    chunk boundaries and inside those items returns every weight column
+    bit for bit, for rows at each position of the run (N = 9: two full
+    waves and a row past the end)."""
+    N, K = 9, 5120
+    w = synth.weights_bf16(4100, N, K, outliers=True)
+    blocks = ql.isq(fmt, to_dev_bf16(w))
+    Wref = oracle.dequant(fmt, oracle.quantize(fmt, w), N, K).astype(np.float32)
+    for k in (0, 31, 32, 1023, 1024, 2047, 4095, 4096, 4127, 4128, 5119):
+        x = np.zeros((1, K), np.uint16)
+        x[0, k] = 0x3F80
+        y = ql.qmatmul(fmt, blocks, to_dev_bf16(x), N, path="gemv").cpu().numpy()
+        assert np.array_equal(y[0], Wref[:, k]), f"{fmt} k={k}"
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 def test_gemv_one_hot_is_exact(fmt):
     """X = e_k: the GEMV must return the fp32 value of the dequantized weight
     bit for bit (products with 1 and sums of zeros are exact), for every
