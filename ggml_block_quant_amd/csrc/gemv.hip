@@ -123,6 +123,15 @@ __device__ __forceinline__ Masks make_masks()
     return k;
 }
 
+// (a & m) | b in one instruction; the compiler would otherwise fold
+// (x & m1) | (y & m2) | b into two ands and an or3
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t b)
+{
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(b));
+    return r;
+}
+
 template <int M>
 __device__ __forceinline__ void q4k_dot(const Chunk<FMT_Q4K> &ck, const XChunk<M> &x, int j, float acc[M],
                                         const Masks &k)
@@ -165,10 +174,10 @@ __device__ __forceinline__ void q6k_dot(const Chunk<FMT_Q6K> &ck, const XChunk<M
         const int o = q & 1;
 #pragma unroll
         for (int s = 0; s < 4; s++) {
-            const uint32_t lo = ((lw[q] >> (4 * s)) & k.nib) | 0x43004300u;
+            const uint32_t lo = and_or(lw[q] >> (4 * s), k.nib, 0x43004300u);
             const int sh = 8 * o + 2 * s;  // high bits of this pair start at bit sh (and 16+sh)
             const uint32_t h = sh >= 4 ? (hw[q >> 1] >> (sh - 4)) : (hw[q >> 1] << (4 - sh));
-            pr[4 * q + s] = (h & k.hi2) | lo;
+            pr[4 * q + s] = and_or(h, k.hi2, lo);
         }
     }
 #pragma unroll
@@ -524,6 +533,27 @@ __device__ __forceinline__ void load_w(const Geo &g, int64_t n, int c, int lane,
     }
 }
 
+// Loads of a row run (rows of 8G chunks, G = K / 256 groups, starting at
+// row n0 whose rows all exist): item i of lane l is chunk f = l + 64 i of
+// the run, i.e. chunk l % 8 of group n0 G + 8 i + l / 8 -- every address is
+// a wave-uniform base plus a lane constant.
+template <int FMT>
+__device__ __forceinline__ void load_run(const Geo &g, int64_t n0, int i, int lane, WLoad<FMT> &w)
+{
+    const int64_t grp0 = n0 * (g.K / 256) + 8 * i;  // uniform
+    const uint32_t lg = lane >> 3, lc = lane & 7;
+    if constexpr (FMT == FMT_Q4K) {
+        w.c = ld_stream16(g.B + 128 * grp0 + 16 * (uint32_t)lane);
+        w.h = *reinterpret_cast<const uint32_t *>(g.B + g.scales_off + 16 * grp0 + (16 * lg + 4 * (lane & 3)));
+    } else if constexpr (FMT == FMT_Q6K) {
+        const uint8_t *Cg = g.B + 192 * grp0;
+        w.ck.lo = ld_stream16(Cg + (192 * lg + 16 * lc));
+        w.ck.hi = ld_stream8(Cg + (192 * lg + 128 + 8 * lc));
+        w.ck.sc2 = *reinterpret_cast<const uint16_t *>(g.B + g.scales_off + 16 * grp0 + (16 * lg + 2 * lc));
+        w.ck.d = *reinterpret_cast<const uint16_t *>(g.B + g.d_off + 2 * grp0 + 2 * lg);
+    }
+}
+
 template <int FMT>
 __device__ __forceinline__ Chunk<FMT> chunk_of(const WLoad<FMT> &w)
 {
@@ -568,9 +598,13 @@ __global__ __launch_bounds__(64 * LW) void gemv_lds_kernel(Geo g, Geo g2, const 
     // of the weight loads instead of sinking them into the branches)
     __shared__ float2 ss[SUMS ? M : 1][SUMS ? SLOTS + 1 : 1];
 
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int S = g.K / 32;
     const int64_t n0 = ((int64_t)blockIdx.x * LW + wv) * (GLU ? 1 : R);
+    // FS: the run starts at row n0c <= n0 so that all its R rows exist
+    // (N >= R); the rows below n0 belong to the previous wave and are not
+    // written
+    const int64_t n0c = FS != 0 && n0 > N - R ? N - R : n0;
 
     // X first, so that waiting for it never waits for the weights
     uint4 xs[XU];
@@ -596,10 +630,14 @@ __global__ __launch_bounds__(64 * LW) void gemv_lds_kernel(Geo g, Geo g2, const 
     WLoad<FMT> w[NI];
 #pragma unroll
     for (int i = 0; i < NI; i++) {
-        int r, c;
-        item(i, r, c);
-        const int64_t n = GLU ? (n0 < N ? n0 : N - 1) : (n0 + r < N ? n0 + r : N - 1);
-        load_w<FMT>(GLU && r == 1 ? g2 : g, n, c < S ? c : S - 1, lane, w[i]);
+        if constexpr (FS != 0) {
+            load_run<FMT>(g, n0c, i, lane, w[i]);
+        } else {
+            int r, c;
+            item(i, r, c);
+            const int64_t n = GLU ? (n0 < N ? n0 : N - 1) : (n0 + r < N ? n0 + r : N - 1);
+            load_w<FMT>(GLU && r == 1 ? g2 : g, n, c < S ? c : S - 1, lane, w[i]);
+        }
     }
     // keep the staging below (and its wait for X) after every weight load
     __builtin_amdgcn_sched_barrier(0);
@@ -711,8 +749,8 @@ __global__ __launch_bounds__(64 * LW) void gemv_lds_kernel(Geo g, Geo g2, const 
             Y[(int64_t)idx * N + n0] = act_f32(act, tot) * up;
     } else if (lane < V && idx < R * M) {
         const int r = idx / M, m = idx % M;
-        if (n0 + r < N)
-            Y[(int64_t)m * N + n0 + r] = tot;
+        if (n0c + r >= n0 && n0c + r < N)
+            Y[(int64_t)m * N + n0c + r] = tot;
     }
 }
 
@@ -725,7 +763,7 @@ hipError_t go_lds(const Geo &g, const uint16_t *X, float *Y, int64_t N, hipStrea
     const int64_t grid = (N + LW * R - 1) / (LW * R);
     // K-quant rows of 160 chunks as one run per wave (Q8_0 gains nothing)
     constexpr bool RUN = FMT != FMT_Q8_0 && M == 1 && CPT == 3;
-    if (RUN && g.K == 5120)
+    if (RUN && g.K == 5120 && N >= R)
         hipLaunchKernelGGL((gemv_lds_kernel<FMT, M, CPT, R, false, RUN ? 160 : 0>),
                            dim3((unsigned)grid), dim3(64 * LW), 0, s, g, g, X, Y, N, 0);
     else
