@@ -535,8 +535,9 @@ __device__ __forceinline__ void load_w(const Geo &g, int64_t n, int c, int lane,
 
 // Loads of a row run (rows of 8G chunks, G = K / 256 groups, starting at
 // row n0 whose rows all exist): item i of lane l is chunk f = l + 64 i of
-// the run, i.e. chunk l % 8 of group n0 G + 8 i + l / 8 -- every address is
-// a wave-uniform base plus a lane constant.
+// the run, i.e. chunk l % 8 of group n0 G + 8 i + l / 8 (Q8_0: block
+// 8 (n0 G + 8 i) + l) -- every address is a wave-uniform base plus a lane
+// constant.
 template <int FMT>
 __device__ __forceinline__ void load_run(const Geo &g, int64_t n0, int i, int lane, WLoad<FMT> &w)
 {
@@ -551,6 +552,12 @@ __device__ __forceinline__ void load_run(const Geo &g, int64_t n0, int i, int la
         w.ck.hi = ld_stream8(Cg + (192 * lg + 128 + 8 * lc));
         w.ck.sc2 = *reinterpret_cast<const uint16_t *>(g.B + g.scales_off + 16 * grp0 + (16 * lg + 2 * lc));
         w.ck.d = *reinterpret_cast<const uint16_t *>(g.B + g.d_off + 2 * grp0 + 2 * lg);
+    } else {
+        // Q8_0: block n0 S + f, 32 code bytes and one fp16 d each
+        const int64_t blk0 = 8 * grp0;
+        w.ck.c0 = ld_stream16(g.B + 32 * blk0 + 32 * (uint32_t)lane);
+        w.ck.c1 = ld_stream16(g.B + 32 * blk0 + (32 * (uint32_t)lane + 16));
+        w.ck.d = *reinterpret_cast<const uint16_t *>(g.B + g.scales_off + 2 * blk0 + 2 * (uint32_t)lane);
     }
 }
 
@@ -586,7 +593,8 @@ __global__ __launch_bounds__(64 * LW) void gemv_lds_kernel(Geo g, Geo g2, const 
                                                            float *__restrict__ Y, int64_t N, int act)
 {
     static_assert(!GLU || R == 2, "gate and up rows");
-    static_assert(FS == 0 || (!GLU && FS % 8 == 0 && FS >= 64 && FS < 64 * CPT), "whole groups, a zero X slot");
+    static_assert(FS == 0 || (!GLU && FS % 8 == 0 && FS >= 32 && FS <= 64 * CPT && (FS < 64 * CPT || R * FS % 64 == 0)),
+                  "whole groups, items within two rows, a zero X slot where the run ends inside an item");
     // the wave's items: (row, chunk) pairs, NI per lane
     constexpr int NI = FS ? (R * FS + 63) / 64 : R * CPT;
     constexpr int SLOTS = 64 * CPT;           // chunk slots per row
@@ -715,7 +723,7 @@ __global__ __launch_bounds__(64 * LW) void gemv_lds_kernel(Geo g, Geo g2, const 
                 q8_0_dot<M>(ck, xc, a);
         };
         // the rows this item can fall in (constants once the loop is
-        // unrolled; with FS >= 64 at most two)
+        // unrolled; with FS >= 32 at most two)
         constexpr int FD = FS ? FS : 1;
         const int RLO = FS ? 64 * i / FD : i / CPT;
         const int RHI = FS ? min((64 * i + 63) / FD, R - 1) : RLO;
@@ -761,10 +769,18 @@ hipError_t go_lds(const Geo &g, const uint16_t *X, float *Y, int64_t N, hipStrea
     // K = 5120 (the 131072 x 5120 head: 10 % faster than one), one above
     constexpr int R = M != 1 ? 1 : CPT <= 2 ? 2 : CPT == 3 ? 4 : 1;
     const int64_t grid = (N + LW * R - 1) / (LW * R);
-    // K-quant rows of 160 chunks as one run per wave (Q8_0 gains nothing)
-    constexpr bool RUN = FMT != FMT_Q8_0 && M == 1 && CPT == 3;
-    if (RUN && g.K == 5120 && N >= R)
-        hipLaunchKernelGGL((gemv_lds_kernel<FMT, M, CPT, R, false, RUN ? 160 : 0>),
+    // one token, K = 1024, 4096, 5120, 14336: the wave's rows as one run
+    // (uniform-base loads; no padding slots where 64 does not divide K/32);
+    // Q8_0 only at K = 1024 (measured 1-2 % slower at the longer rows)
+    constexpr int FSV = M != 1                        ? 0
+                        : CPT == 1                    ? 32
+                        : FMT == FMT_Q8_0             ? 0
+                        : CPT == 2                    ? 128
+                        : CPT == 3                    ? 160
+                        : CPT == 7                    ? 448
+                                                      : 0;
+    if (FSV != 0 && g.K == 32 * FSV && N >= R)
+        hipLaunchKernelGGL((gemv_lds_kernel<FMT, M, CPT, R, false, FSV>),
                            dim3((unsigned)grid), dim3(64 * LW), 0, s, g, g, X, Y, N, 0);
     else
         hipLaunchKernelGGL((gemv_lds_kernel<FMT, M, CPT, R>), dim3((unsigned)grid), dim3(64 * LW), 0, s, g, g, X, Y,
