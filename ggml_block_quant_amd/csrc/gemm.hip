@@ -1276,93 +1276,174 @@ __global__ __launch_bounds__(256) void gemm_fp8_tile_kernel(const uint8_t *__res
 }
 
 // ---------------------------------------------------------------------------
-// Q8_0 x Q8_0 int8 path
+// Q8_0 x Q8_0 int8 path.  Output tile 128 (n) x 128 (m) per workgroup of
+// four waves (2 x 2, 64 x 64 each = 2 x 2 tiles of 32 x 32), two workgroups
+// per CU; K in steps of one Q8_0 block (32).
+//
+//   * Codes of W and X and the fp16 scales of both reach LDS by direct
+//     global->LDS loads into a ring of six stages, five steps ahead; the
+//     only waits on them are explicit vmcnt waits, one barrier per step.
+//     Codes: 16-byte chunk c of row r at slot 2r + (c ^ ((r >> 3) & 1)), so
+//     the 16 rows a ds_read_b128 phase touches land on distinct banks.
+//   * Per 32 x 32 tile: v_mfma_i32_32x32x32_i8 forms the exact integer dot
+//     products P[n][m] of the block; v_mfma_f32_32x32x8_f16 with d_w in
+//     k-slot 0 of A and d_x in k-slot 0 of B forms the outer product
+//     d_w[n] d_x[m] in the same output layout -- exact, since a product of
+//     two fp16 values fits binary32 -- and each output then costs one
+//     conversion and one fused multiply-add: acc += float(P) * (d_w d_x).
+//   * K splits add into a zeroed Y with fp32 atomics.
 // ---------------------------------------------------------------------------
 constexpr int BN = 128;     // n tile
-constexpr int BK = 64;      // k per step (two Q8_0 blocks)
+constexpr int BK = 32;      // k per step (one Q8_0 block)
 constexpr int IBM = 128;    // m tile
-constexpr int IPITCH = 80;  // bytes per LDS row of 64 codes (16-byte aligned, skewed banks)
+constexpr int INS = 6;      // stages
+constexpr int ISC = 8192;   // offset of the scales in a stage: d_w [128] dwords, then d_x [128]
+constexpr int ISTG = ISC + 1024;
 
-__global__ __launch_bounds__(256) void gemm_i8_kernel(const int8_t *__restrict__ Wq,
-                                                      const uint16_t *__restrict__ Wd,
-                                                      const int8_t *__restrict__ Xq,
-                                                      const uint16_t *__restrict__ Xd,
-                                                      float *__restrict__ Y, int M, int N, int K,
-                                                      int kt_per_split)
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int islot(int row, int c) { return 2 * row + (c ^ ((row >> 3) & 1)); }
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_i8_kernel(
+    const int8_t *__restrict__ Wq, const uint16_t *__restrict__ Wd, const int8_t *__restrict__ Xq,
+    const uint16_t *__restrict__ Xd, float *__restrict__ Y, int M, int N, int K, int kt_per_split)
 {
-    __shared__ __attribute__((aligned(16))) int8_t sW[BN * IPITCH];
-    __shared__ __attribute__((aligned(16))) int8_t sX[IBM * IPITCH];
-    __shared__ __attribute__((aligned(16))) float sDw[2][BN];
-    __shared__ __attribute__((aligned(16))) float sDx[2][IBM];
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wn = wave & 1, wm = wave >> 1;  // 2 x 2 waves, 64 x 64 each
-    const int64_t n0 = (int64_t)blockIdx.x * BN;
-    const int m0 = blockIdx.y * IBM;
-    const int nkt = K / BK;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[INS * ISTG];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wn = wv & 1, wm = wv >> 1;  // 2 x 2 waves, 64 x 64 each
+    const int n0 = blockIdx.x * BN, m0 = blockIdx.y * IBM;
     const int kt0 = blockIdx.z * kt_per_split;
-    const int kt1 = min(nkt, kt0 + kt_per_split);
+    const int kt1 = min(K / BK, kt0 + kt_per_split);
     const int KB = K / 32;
+    if (kt0 >= kt1)
+        return;  // an empty K split (the whole workgroup): adds nothing
 
-    float acc[2][2][16];
+    // direct loads: the load of wave w fills code slots 64w + lane of the
+    // W and the X region; rows past N / M re-read the last row (results
+    // dropped); byte offsets from row n0 / m0 of the step
+    const int p = 64 * wv + lane, pr = p >> 1, pc = (p & 1) ^ ((pr >> 3) & 1);
+    const uint32_t ow = (uint32_t)((min(n0 + pr, N - 1) - n0) * K + 16 * pc);
+    const uint32_t ox = (uint32_t)((min(m0 + pr, M - 1) - m0) * K + 16 * pc);
+    // scales: waves 0, 1 load the d_w dword holding the step's block of rows
+    // 64w + lane, waves 2, 3 the d_x dword of rows 64(w - 2) + lane
+    const bool sw = wv < 2;
+    const int srow = 64 * (wv & 1) + lane;
+    const uint32_t osc = (uint32_t)((sw ? min(n0 + srow, N - 1) - n0 : min(m0 + srow, M - 1) - m0) * KB * 2);
+    const uint8_t *const wbase = reinterpret_cast<const uint8_t *>(Wq) + (int64_t)n0 * K;
+    const uint8_t *const xbase = reinterpret_cast<const uint8_t *>(Xq) + (int64_t)m0 * K;
+    const uint8_t *const sbase = sw ? reinterpret_cast<const uint8_t *>(Wd + (int64_t)n0 * KB)
+                                    : reinterpret_cast<const uint8_t *>(Xd + (int64_t)m0 * KB);
+    auto issue = [&](int kt) {
+        const uint32_t st = lds_addr(smem + (kt % INS) * ISTG);
+        dma16(wbase + BK * kt, ow, st + 1024 * wv);
+        dma16(xbase + BK * kt, ox, st + 4096 + 1024 * wv);
+        dma4(sbase + 4 * (kt >> 1), osc, st + ISC + (sw ? 0 : 512) + 256 * (wv & 1));
+    };
+
+    const int r32 = lane & 31, kh = lane >> 5;
+    int oa[2], ob[2], sa[2], sb[2];
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        oa[i] = 16 * islot(64 * wn + 32 * i + r32, kh);
+        ob[i] = 4096 + 16 * islot(64 * wm + 32 * i + r32, kh);
+        sa[i] = ISC + 4 * (64 * wn + 32 * i + r32);
+        sb[i] = ISC + 512 + 4 * (64 * wm + 32 * i + r32);
+    }
+
+    f32x16_t acc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; i++)
 #pragma unroll
         for (int j = 0; j < 2; j++)
+            acc[i][j] = f32x16_t{};
+    const i32x16_t izero = {};
+    const f32x16_t fzero = {};
+
+    // the step's operands: codes, and d in k-slot 0 of lanes 0..31 (zeros
+    // elsewhere; read by every lane and masked, so that no branch serializes
+    // the reads); the scale operands of two steps are held
+    const uint32_t dmask = kh ? 0u : 0xffffu;
+    i32x4_t a[2], x[2];
+    f16x4_t as[2], xs[2], asn[2], xsn[2];  // this step's and the next step's
+    auto reads = [&](int kt) {
+        const uint8_t *st = smem + (kt % INS) * ISTG;
+        const int hs = 16 * (kt & 1);  // the step's fp16 half of the scale dwords
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            a[i] = *reinterpret_cast<const i32x4_t *>(st + oa[i]);
+            x[i] = *reinterpret_cast<const i32x4_t *>(st + ob[i]);
+            const uint32_t hw = (*reinterpret_cast<const uint32_t *>(st + sa[i]) >> hs) & dmask;
+            const uint32_t hx = (*reinterpret_cast<const uint32_t *>(st + sb[i]) >> hs) & dmask;
+            asn[i] = __builtin_bit_cast(f16x4_t, make_uint2(hw, 0u));
+            xsn[i] = __builtin_bit_cast(f16x4_t, make_uint2(hx, 0u));
+        }
+    };
+    i32x16_t P[4];  // tile t = 2i + j
+    auto products = [&]() {
+#pragma unroll
+        for (int t = 0; t < 4; t++)
+            P[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[t >> 1], x[t & 1], izero, 0, 0, 0);
+    };
+
+    for (int kt = kt0; kt < kt0 + INS - 1 && kt < kt1; kt++)
+        issue(kt);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt 0, lgkmcnt 0
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    reads(kt0);
+    products();
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        as[i] = asn[i];
+        xs[i] = xsn[i];
+    }
+
+    // Step kt: its integer products are in flight.  Wait until step kt + 1
+    // has landed (the loads of steps kt + 2 .. kt + 4, three per wave each,
+    // may remain) and every wave is past its reads of step kt - 1, whose
+    // stage the loads of step kt + 5 then take; read step kt + 1's operands
+    // (their latency hides behind the rescale); rescale step kt, each
+    // tile's d_w d_x product issued one tile ahead; then issue step kt + 1's
+    // integer products (their latency hides behind the next barrier).
+    auto step = [&](int kt, auto more_t) {
+        constexpr bool MORE = decltype(more_t)::value;  // a step kt + 1 follows
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (kt + INS - 2 < kt1)
+            __builtin_amdgcn_s_waitcnt(0x0070 | 3 * (INS - 3));  // vmcnt 9, lgkmcnt 0
+        else
+            __builtin_amdgcn_s_waitcnt(0x0070);                  // vmcnt 0, lgkmcnt 0
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (kt + INS - 1 < kt1)
+            issue(kt + INS - 1);
+        if constexpr (MORE)
+            reads(kt + 1);
+        f32x16_t S[2];
+        S[0] = __builtin_amdgcn_mfma_f32_32x32x8f16(as[0], xs[0], fzero, 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+            if (t + 1 < 4)
+                S[(t + 1) & 1] = __builtin_amdgcn_mfma_f32_32x32x8f16(as[(t + 1) >> 1], xs[(t + 1) & 1], fzero, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int r = 0; r < 16; r++)
-                acc[i][j][r] = 0.0f;
-    const i32x16_t zero = {};
-
-    for (int kt = kt0; kt < kt1; kt++) {
-        const int k0 = kt * BK;
-        {  // codes: 128 rows x 64 bytes per operand = 512 uint4; thread -> 2 of each
+                acc[t >> 1][t & 1][r] = fmaf((float)P[t][r], S[t & 1][r], acc[t >> 1][t & 1][r]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (MORE) {
+            products();
 #pragma unroll
-            for (int t = 0; t < 2; t++) {
-                const int i = tid + 256 * t, r = i >> 2, q = i & 3;
-                uint4 vw = make_uint4(0u, 0u, 0u, 0u), vx = make_uint4(0u, 0u, 0u, 0u);
-                if (n0 + r < N)
-                    vw = *reinterpret_cast<const uint4 *>(Wq + (n0 + r) * K + k0 + 16 * q);
-                if (m0 + r < M)
-                    vx = *reinterpret_cast<const uint4 *>(Xq + (int64_t)(m0 + r) * K + k0 + 16 * q);
-                *reinterpret_cast<uint4 *>(sW + r * IPITCH + 16 * q) = vw;
-                *reinterpret_cast<uint4 *>(sX + r * IPITCH + 16 * q) = vx;
+            for (int i = 0; i < 2; i++) {
+                as[i] = asn[i];
+                xs[i] = xsn[i];
             }
-            const int r = tid >> 1, b = tid & 1;
-            sDw[b][r] = n0 + r < N ? h2f(Wd[(n0 + r) * KB + 2 * kt + b]) : 0.0f;
-            sDx[b][r] = m0 + r < M ? h2f(Xd[(int64_t)(m0 + r) * KB + 2 * kt + b]) : 0.0f;
         }
-        __syncthreads();
-#pragma unroll
-        for (int blk = 0; blk < 2; blk++) {
-            i32x4_t a[2], bx[2];
-#pragma unroll
-            for (int i = 0; i < 2; i++)
-                a[i] = *reinterpret_cast<const i32x4_t *>(sW + (wn * 64 + 32 * i + (lane & 31)) * IPITCH +
-                                                          32 * blk + 16 * (lane >> 5));
-#pragma unroll
-            for (int j = 0; j < 2; j++)
-                bx[j] = *reinterpret_cast<const i32x4_t *>(sX + (wm * 64 + 32 * j + (lane & 31)) * IPITCH +
-                                                           32 * blk + 16 * (lane >> 5));
-#pragma unroll
-            for (int i = 0; i < 2; i++)
-#pragma unroll
-                for (int j = 0; j < 2; j++) {
-                    const i32x16_t d = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], bx[j], zero, 0, 0, 0);
-                    const float dx = sDx[blk][wm * 64 + 32 * j + (lane & 31)];
-#pragma unroll
-                    for (int g = 0; g < 4; g++) {
-                        // rows 8g + 4*(lane/32) + 0..3 of the 32 x 32 tile
-                        const f32x4_t dw = *reinterpret_cast<const f32x4_t *>(
-                            &sDw[blk][wn * 64 + 32 * i + 8 * g + 4 * (lane >> 5)]);
-#pragma unroll
-                        for (int e = 0; e < 4; e++)
-                            acc[i][j][4 * g + e] = fmaf((float)d[4 * g + e], dw[e] * dx, acc[i][j][4 * g + e]);
-                    }
-                }
-        }
-        __syncthreads();
-    }
+    };
+    for (int kt = kt0; kt < kt1 - 1; kt++)
+        step(kt, std::true_type{});
+    step(kt1 - 1, std::false_type{});
 
     // acc[i][j][4g+e] = D[n = 8g + 4*(lane/32) + e][m = lane%32] of its 32 x 32 tile
     const bool atomic = gridDim.z > 1;
@@ -1371,12 +1452,12 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(const int8_t *__restrict__
     for (int i = 0; i < 2; i++)
 #pragma unroll
         for (int j = 0; j < 2; j++) {
-            const int m = m0 + wm * 64 + 32 * j + (lane & 31);
+            const int m = m0 + wm * 64 + 32 * j + r32;
             if (m >= M)
                 continue;
 #pragma unroll
             for (int g = 0; g < 4; g++) {
-                const int64_t n = n0 + wn * 64 + 32 * i + 8 * g + 4 * (lane >> 5);
+                const int64_t n = n0 + wn * 64 + 32 * i + 8 * g + 4 * kh;
                 float *y = Y + (int64_t)m * N + n;
                 if (!atomic && vec4 && n + 3 < N) {
                     *reinterpret_cast<f32x4_t *>(y) =

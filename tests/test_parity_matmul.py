@@ -207,8 +207,10 @@ def test_mfma_bf16_q4k_quad_stream():
 
 
 def test_mfma_i8_shapes_and_activation_blocks():
+    """Ragged tiles and K splits; K = 1280 with one tile splits 40 steps of
+    one block into 16 runs of 3, the last two of them empty."""
     for M in (1, 9, 16, 64, 130, 256):
-        for N, K in ((7, 256), (64, 1024), (300, 4096), (129, 512)):
+        for N, K in ((7, 256), (64, 1024), (300, 4096), (129, 512), (7, 1280), (200, 768)):
             w = synth.weights_bf16(6000 + N, N, K)
             x = synth.activations_bf16(6001 + M, M, K)
             ws = torch.empty(ql.workspace_bytes("q8_0", "mfma_i8", M, K), dtype=torch.uint8, device="cuda")
