@@ -606,7 +606,9 @@ __global__ __launch_bounds__(64 * LW) void gemv_lds_kernel(Geo g, Geo g2, const 
     // of the weight loads instead of sinking them into the branches)
     __shared__ float2 ss[SUMS ? M : 1][SUMS ? SLOTS + 1 : 1];
 
-    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // (the row runs want a wave index the compiler knows to be uniform; the
+    // other instances measured faster with the plain one)
+    const int tid = threadIdx.x, lane = tid & 63, wv = FS != 0 ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
     const int S = g.K / 32;
     const int64_t n0 = ((int64_t)blockIdx.x * LW + wv) * (GLU ? 1 : R);
     // FS: the run starts at row n0c <= n0 so that all its R rows exist
@@ -769,16 +771,18 @@ hipError_t go_lds(const Geo &g, const uint16_t *X, float *Y, int64_t N, hipStrea
     // K = 5120 (the 131072 x 5120 head: 10 % faster than one), one above
     constexpr int R = M != 1 ? 1 : CPT <= 2 ? 2 : CPT == 3 ? 4 : 1;
     const int64_t grid = (N + LW * R - 1) / (LW * R);
-    // one token, K = 1024, 4096, 5120, 14336: the wave's rows as one run
-    // (uniform-base loads; no padding slots where 64 does not divide K/32);
-    // Q8_0 only at K = 1024 (measured 1-2 % slower at the longer rows)
-    constexpr int FSV = M != 1                        ? 0
-                        : CPT == 1                    ? 32
-                        : FMT == FMT_Q8_0             ? 0
-                        : CPT == 2                    ? 128
-                        : CPT == 3                    ? 160
-                        : CPT == 7                    ? 448
-                                                      : 0;
+    // one token: the wave's rows as one run (uniform-base loads; no padding
+    // slots where 64 does not divide K/32) where measured faster with weight
+    // copies rotated past the caches: K = 1024 and 5120, and Q6K also at
+    // K = 4096 and 14336 (Q4K and Q8_0 there: 1-4 % slower)
+    constexpr int FSV = M != 1                          ? 0
+                        : CPT == 1                      ? 32
+                        : FMT == FMT_Q8_0               ? 0
+                        : CPT == 3                      ? 160
+                        : FMT == FMT_Q4K                ? 0
+                        : CPT == 2                      ? 128
+                        : CPT == 7                      ? 448
+                                                        : 0;
     if (FSV != 0 && g.K == 32 * FSV && N >= R)
         hipLaunchKernelGGL((gemv_lds_kernel<FMT, M, CPT, R, false, FSV>),
                            dim3((unsigned)grid), dim3(64 * LW), 0, s, g, g, X, Y, N, 0);
