@@ -239,7 +239,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(q4["alg_GBps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(q4["alg_GBps"] / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(),
                      "traffic_unit": "HBM bytes per launch (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0)",
-                     "kernel": "gemv_lds_kernel<Q4K, M=1, CPT=2, R=2, run of 128 chunks>", "alg_bytes_per_launch": q4["alg_bytes"]},
+                     "kernel": "gemv_lds_kernel<Q4K, M=1, CPT=2, R=2>", "alg_bytes_per_launch": q4["alg_bytes"]},
     })
     parts["gemv_q8_0_14336x4096_m1"] = {
         "us": round(head["q8_0"]["ms"] * 1e3, 3), "weight_GBps": round(head["q8_0"]["weight_GBps"], 1),
