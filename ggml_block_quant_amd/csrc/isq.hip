@@ -77,66 +77,80 @@ __device__ __forceinline__ uint32_t pack_nibbles(const int q[8])
            (uint32_t)q[7] << 28;
 }
 
+// One lane per 32 consecutive elements (a Q8_0 block, a Q4K sub-block, a
+// Q6K chunk of two sub-blocks): 64 bytes of bf16 in flight per lane, and
+// the per-block scale arithmetic (IEEE divisions included) done once per
+// 32 elements.  Scales that span a 256-element group combine over the
+// group's 8 lanes with xor shuffles (groups never straddle a row, since
+// K % 256 == 0, so the 8 lanes are active together).
+__device__ __forceinline__ void load32(const uint4 *__restrict__ W, int64_t t, float x[32])
+{
+    const uint4 *p = W + 4 * t;
+    uint4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+        v[i] = p[i];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+        load8(v[i], x + 8 * i);
+}
+
 // ---------------------------------------------------------------------------
-// Q8_0: d = F16(max|x| / 127), q = clamp(RHA(x / d), -127, 127); 4 lanes/block
+// Q8_0: d = F16(max|x| / 127), q = clamp(RHA(x / d), -127, 127)
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void isq_q8_0_kernel(const uint4 *__restrict__ W, int64_t tasks,
-                                                       uint2 *__restrict__ codes,
+                                                       uint4 *__restrict__ codes,
                                                        uint16_t *__restrict__ scales)
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < tasks; t += stride) {
-        float x[8];
-        load8(W[t], x);
+        float x[32];
+        load32(W, t, x);
         float a = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 8; i++)
+        for (int i = 0; i < 32; i++)
             a = fmaxf(a, fabsf(x[i]));
-        a = fmaxf(a, __shfl_xor(a, 1));
-        a = fmaxf(a, __shfl_xor(a, 2));
         float df;
         const uint32_t d16 = scale_f16(a / 127.0f, &df);
         const float rd = df > 0.0f ? 1.0f / df : 0.0f;  // d = 0: every code is 0
-        uint32_t lo = 0, hi = 0;
+        uint32_t w[8];
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int q0 = (int)fminf(fmaxf(rha_quot(x[i], df, rd), -127.0f), 127.0f);
-            const int q1 = (int)fminf(fmaxf(rha_quot(x[i + 4], df, rd), -127.0f), 127.0f);
-            lo |= ((uint32_t)q0 & 0xffu) << (8 * i);
-            hi |= ((uint32_t)q1 & 0xffu) << (8 * i);
+        for (int k = 0; k < 8; k++) {
+            w[k] = 0;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int q = (int)fminf(fmaxf(rha_quot(x[4 * k + i], df, rd), -127.0f), 127.0f);
+                w[k] |= ((uint32_t)q & 0xffu) << (8 * i);
+            }
         }
-        codes[t] = make_uint2(lo, hi);
-        if ((t & 3) == 0)
-            scales[t >> 2] = (uint16_t)d16;
+        codes[2 * t] = make_uint4(w[0], w[1], w[2], w[3]);
+        codes[2 * t + 1] = make_uint4(w[4], w[5], w[6], w[7]);
+        scales[t] = (uint16_t)d16;
     }
 }
 
 // ---------------------------------------------------------------------------
-// Q4K: plain min/max affine rule per sub-block of 32; 32 lanes per group
+// Q4K: plain min/max affine rule per sub-block of 32; 8 lanes per group
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void isq_q4k_kernel(const uint4 *__restrict__ W, int64_t tasks,
-                                                      uint32_t *__restrict__ codes,
+                                                      uint4 *__restrict__ codes,
                                                       uint4 *__restrict__ headers)
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < tasks; t += stride) {
-        float x[8];
-        load8(W[t], x);
+        float x[32];
+        load32(W, t, x);
         float lo = 0.0f, hi = x[0];
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
+        for (int i = 0; i < 32; i++) {
             lo = fminf(lo, x[i]);
             hi = fmaxf(hi, x[i]);
         }
-        lo = fminf(lo, __shfl_xor(lo, 1));
-        lo = fminf(lo, __shfl_xor(lo, 2));
-        hi = fmaxf(hi, __shfl_xor(hi, 1));
-        hi = fmaxf(hi, __shfl_xor(hi, 2));
         const float s = (hi - lo) / 15.0f;
         const float m = 0.0f - lo;
         float smax = s, mmax = m;
 #pragma unroll
-        for (int k = 4; k <= 16; k <<= 1) {
+        for (int k = 1; k <= 4; k <<= 1) {
             smax = fmaxf(smax, __shfl_xor(smax, k));
             mmax = fmaxf(mmax, __shfl_xor(mmax, k));
         }
@@ -148,32 +162,37 @@ __global__ __launch_bounds__(256) void isq_q4k_kernel(const uint4 *__restrict__ 
         const float S = df * (float)sc;
         const float M = dmf * (float)mq;
         const float rS = S > 0.0f ? 1.0f / S : 0.0f;  // S = 0: every code is 0
-        int q[8];
+        uint32_t w[4];
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            const float u = x[i] + M;
-            q[i] = (int)fminf(fmaxf(rha_quot(u, S, rS), 0.0f), 15.0f);
+        for (int k = 0; k < 4; k++) {
+            int q[8];
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const float u = x[8 * k + i] + M;
+                q[i] = (int)fminf(fmaxf(rha_quot(u, S, rS), 0.0f), 15.0f);
+            }
+            w[k] = pack_nibbles(q);
         }
-        codes[t] = pack_nibbles(q);
+        codes[t] = make_uint4(w[0], w[1], w[2], w[3]);
 
-        const int l = (int)(t & 31), j = l >> 2, w = l & 3;
-        uint32_t h0 = w == 0 ? ((uint32_t)sc & 15u) << (4 * j) : 0u;
-        uint32_t h1 = w == 0 ? ((uint32_t)mq & 15u) << (4 * j) : 0u;
-        uint32_t h2 = w == 0 ? (((uint32_t)sc >> 4) << (2 * j)) | (((uint32_t)mq >> 4) << (16 + 2 * j))
-                             : 0u;
+        const int j = (int)(t & 7);  // sub-block of the group
+        uint32_t h0 = ((uint32_t)sc & 15u) << (4 * j);
+        uint32_t h1 = ((uint32_t)mq & 15u) << (4 * j);
+        uint32_t h2 = (((uint32_t)sc >> 4) << (2 * j)) | (((uint32_t)mq >> 4) << (16 + 2 * j));
 #pragma unroll
-        for (int k = 4; k <= 16; k <<= 1) {
+        for (int k = 1; k <= 4; k <<= 1) {
             h0 |= __shfl_xor(h0, k);
             h1 |= __shfl_xor(h1, k);
             h2 |= __shfl_xor(h2, k);
         }
-        if (l == 0)
-            headers[t >> 5] = make_uint4(d16 | (dm16 << 16), h0, h1, h2);
+        if (j == 0)
+            headers[t >> 3] = make_uint4(d16 | (dm16 << 16), h0, h1, h2);
     }
 }
 
 // ---------------------------------------------------------------------------
-// Q6K: symmetric 6-bit codes, 16 sub-blocks of 16, int8 sub-scales, fp16 d
+// Q6K: symmetric 6-bit codes, 16 sub-blocks of 16, int8 sub-scales, fp16 d;
+// lane c of a group's 8 takes chunk c (elements 32c..32c+31: two sub-blocks)
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void isq_q6k_kernel(const uint4 *__restrict__ W, int64_t tasks,
                                                       uint8_t *__restrict__ C,
@@ -186,45 +205,51 @@ __global__ __launch_bounds__(256) void isq_q6k_kernel(const uint4 *__restrict__ 
     if (blockIdx.x == 0 && (int)threadIdx.x < npad)
         pad[threadIdx.x] = 0;
     for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < tasks; t += stride) {
-        float x[8];
-        load8(W[t], x);
-        float a = 0.0f;
+        float x[32];
+        load32(W, t, x);
+        float a[2] = {0.0f, 0.0f};
 #pragma unroll
-        for (int i = 0; i < 8; i++)
-            a = fmaxf(a, fabsf(x[i]));
-        a = fmaxf(a, __shfl_xor(a, 1));  // sub-block of 16 = 2 lanes
-        const float s = a / 31.0f;
-        float smax = s;
+        for (int i = 0; i < 32; i++)
+            a[i >> 4] = fmaxf(a[i >> 4], fabsf(x[i]));
+        const float s[2] = {a[0] / 31.0f, a[1] / 31.0f};
+        float smax = fmaxf(s[0], s[1]);
 #pragma unroll
-        for (int k = 2; k <= 16; k <<= 1)
+        for (int k = 1; k <= 4; k <<= 1)
             smax = fmaxf(smax, __shfl_xor(smax, k));
         float df;
         const uint32_t d16 = scale_f16(smax / 127.0f, &df);
-        const int sc = df > 0.0f ? code_of(s / df, 0.0f, 127.0f) : 0;
-        const float S = df * (float)sc;
-        const float rS = S > 0.0f ? 1.0f / S : 0.0f;  // S = 0: every code is 0
-        int u[8], lo4[8];
+        int sc[2];
+        float S[2], rS[2];
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            u[i] = (int)fminf(fmaxf(rha_quot(x[i], S, rS), -32.0f), 31.0f) + 32;
-            lo4[i] = u[i] & 15;
+        for (int h = 0; h < 2; h++) {
+            sc[h] = df > 0.0f ? code_of(s[h] / df, 0.0f, 127.0f) : 0;
+            S[h] = df * (float)sc[h];
+            rS[h] = S[h] > 0.0f ? 1.0f / S[h] : 0.0f;  // S = 0: every code is 0
         }
-        const int64_t g = t >> 5;
-        const int l = (int)(t & 31), c = l >> 2, w = l & 3, o = w & 1;
+        uint32_t lw[4], hw[2] = {0u, 0u};
+#pragma unroll
+        for (int w = 0; w < 4; w++) {  // octet w of the chunk
+            int u[8], lo4[8];
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                u[i] = (int)fminf(fmaxf(rha_quot(x[8 * w + i], S[w >> 1], rS[w >> 1]), -32.0f), 31.0f) + 32;
+                lo4[i] = u[i] & 15;
+            }
+            lw[w] = pack_nibbles(lo4);
+            const int o = w & 1;
+#pragma unroll
+            for (int p = 0; p < 4; p++) {
+                hw[w >> 1] |= (uint32_t)(u[2 * p] >> 4) << (8 * o + 2 * p);
+                hw[w >> 1] |= (uint32_t)(u[2 * p + 1] >> 4) << (16 + 8 * o + 2 * p);
+            }
+        }
+        const int64_t g = t >> 3;
+        const int c = (int)(t & 7);
         uint8_t *Cg = C + 192 * g;
-        *reinterpret_cast<uint32_t *>(Cg + 4 * l) = pack_nibbles(lo4);
-        uint32_t hb = 0;
-#pragma unroll
-        for (int p = 0; p < 4; p++) {
-            hb |= (uint32_t)(u[2 * p] >> 4) << (8 * o + 2 * p);
-            hb |= (uint32_t)(u[2 * p + 1] >> 4) << (16 + 8 * o + 2 * p);
-        }
-        hb |= __shfl_xor(hb, 1);
-        if (o == 0)
-            *reinterpret_cast<uint32_t *>(Cg + 128 + 8 * c + 4 * (w >> 1)) = hb;
-        if ((l & 1) == 0)
-            SC[16 * g + (l >> 1)] = (int8_t)sc;
-        if (l == 0)
+        *reinterpret_cast<uint4 *>(Cg + 16 * c) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        *reinterpret_cast<uint2 *>(Cg + 128 + 8 * c) = make_uint2(hw[0], hw[1]);
+        *reinterpret_cast<uint16_t *>(SC + 16 * g + 2 * c) = (uint16_t)(((uint32_t)sc[0] & 0xffu) | ((uint32_t)sc[1] & 0xffu) << 8);
+        if (c == 0)
             D[g] = (uint16_t)d16;
     }
 }
@@ -560,16 +585,17 @@ hipError_t launch_isq(int fmt, const uint16_t *W, int64_t N, int64_t K, uint8_t 
     const int64_t tasks = N * K / 8;
     const Planes p = planes_of(fmt, N, K);
     const uint4 *w = reinterpret_cast<const uint4 *>(W);
+    const int64_t blocks32 = N * K / 32;  // lanes of the Q8_0 / Q4K / Q6K quantizers
     if (fmt == FMT_Q8_0)
-        hipLaunchKernelGGL(isq_q8_0_kernel, dim3(grid_for(tasks)), dim3(256), 0, s, w, tasks,
-                           reinterpret_cast<uint2 *>(out),
+        hipLaunchKernelGGL(isq_q8_0_kernel, dim3(grid_for(blocks32)), dim3(256), 0, s, w, blocks32,
+                           reinterpret_cast<uint4 *>(out),
                            reinterpret_cast<uint16_t *>(out + p.scales));
     else if (fmt == FMT_Q4K)
-        hipLaunchKernelGGL(isq_q4k_kernel, dim3(grid_for(tasks)), dim3(256), 0, s, w, tasks,
-                           reinterpret_cast<uint32_t *>(out),
+        hipLaunchKernelGGL(isq_q4k_kernel, dim3(grid_for(blocks32)), dim3(256), 0, s, w, blocks32,
+                           reinterpret_cast<uint4 *>(out),
                            reinterpret_cast<uint4 *>(out + p.scales));
     else if (fmt == FMT_Q6K)
-        hipLaunchKernelGGL(isq_q6k_kernel, dim3(grid_for(tasks)), dim3(256), 0, s, w, tasks, out,
+        hipLaunchKernelGGL(isq_q6k_kernel, dim3(grid_for(blocks32)), dim3(256), 0, s, w, blocks32, out,
                            reinterpret_cast<int8_t *>(out + p.scales),
                            reinterpret_cast<uint16_t *>(out + p.d), out + 210 * (N * K / 256),
                            (int)(p.total - 210 * (N * K / 256)));
