@@ -57,13 +57,16 @@ __device__ __forceinline__ int code_of(float v, float lo, float hi)
 // 3 * 2^-24 * |t| of fl(u / S); both round (half away from zero) to the same
 // integer unless a half-integer lies that close to t.  Only then is the
 // quotient computed by the correctly rounded division, so the code is the
-// one the definition gives, with one multiply in the common case.
+// one the definition gives, with one multiply in the common case.  Away
+// from those cases RHA(t) = sign(t) floor(|t| + 1/2) exactly: the sum's
+// rounding error (at most 2^-24 (|t| + 1/2) <= 2^-23 |t| for |t| >= 1/2,
+// 2^-25 below) is smaller than the distance of |t| + 1/2 from an integer.
 __device__ __forceinline__ float rha_quot(float u, float S, float r)
 {
     const float t = u * r;
     const float a = fabsf(t);
-    float q = roundf(t);
-    if (fabsf(a - floorf(a) - 0.5f) <= 2.5e-7f * a)
+    float q = copysignf(floorf(a + 0.5f), t);
+    if (fabsf(__builtin_amdgcn_fractf(a) - 0.5f) <= 2.5e-7f * a)
         q = roundf(u / S);
     return q;
 }
