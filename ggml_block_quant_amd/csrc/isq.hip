@@ -122,7 +122,7 @@ __global__ __launch_bounds__(256) void isq_q8_0_kernel(const uint4 *__restrict__
             w[k] = 0;
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                const int q = (int)fminf(fmaxf(rha_quot(x[4 * k + i], df, rd), -127.0f), 127.0f);
+                const int q = (int)__builtin_amdgcn_fmed3f(rha_quot(x[4 * k + i], df, rd), -127.0f, 127.0f);
                 w[k] |= ((uint32_t)q & 0xffu) << (8 * i);
             }
         }
@@ -172,7 +172,7 @@ __global__ __launch_bounds__(256) void isq_q4k_kernel(const uint4 *__restrict__ 
 #pragma unroll
             for (int i = 0; i < 8; i++) {
                 const float u = x[8 * k + i] + M;
-                q[i] = (int)fminf(fmaxf(rha_quot(u, S, rS), 0.0f), 15.0f);
+                q[i] = (int)__builtin_amdgcn_fmed3f(rha_quot(u, S, rS), 0.0f, 15.0f);
             }
             w[k] = pack_nibbles(q);
         }
@@ -235,7 +235,7 @@ __global__ __launch_bounds__(256) void isq_q6k_kernel(const uint4 *__restrict__ 
             int u[8], lo4[8];
 #pragma unroll
             for (int i = 0; i < 8; i++) {
-                u[i] = (int)fminf(fmaxf(rha_quot(x[8 * w + i], S[w >> 1], rS[w >> 1]), -32.0f), 31.0f) + 32;
+                u[i] = (int)__builtin_amdgcn_fmed3f(rha_quot(x[8 * w + i], S[w >> 1], rS[w >> 1]), -32.0f, 31.0f) + 32;
                 lo4[i] = u[i] & 15;
             }
             lw[w] = pack_nibbles(lo4);
@@ -395,7 +395,7 @@ __global__ __launch_bounds__(256) void isq_more_kernel(const uint4 *__restrict__
 #pragma unroll
         for (int i = 0; i < 8; i++) {
             const float u = AFF ? (KQ ? x[i] + M : x[i] - (-M)) : x[i];
-            q[i] = S > 0.0f ? (int)fminf(fmaxf(rha_quot(u, S, rS), (float)QLO), (float)QHI) : 0;
+            q[i] = S > 0.0f ? (int)__builtin_amdgcn_fmed3f(rha_quot(u, S, rS), (float)QLO, (float)QHI) : 0;
         }
         // stores
         const int tl = (int)(t & 31);
