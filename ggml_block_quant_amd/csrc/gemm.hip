@@ -128,7 +128,11 @@ __device__ __forceinline__ void decode_wblk(const WBlk<FMT> &w, int c, uint32_t 
             // nibble p holds element 2p (p < 4) or 2(p-4)+1, so the bytes of
             // lo = v & 0x0F0F0F0F are elements 0,4,1,5 and those of
             // hi = (v >> 4) & 0x0F0F0F0F are elements 2,6,3,7
-            const uint32_t lo = v[q] & 0x0F0F0F0Fu, hi = (v[q] >> 4) & 0x0F0F0F0Fu;
+            uint32_t lo = v[q] & 0x0F0F0F0Fu, hi = (v[q] >> 4) & 0x0F0F0F0Fu;
+            // opaque to the optimizer, so that each element converts with one
+            // byte-selecting v_cvt_f32_ubyteN instead of a bfe and a convert
+            asm("" : "+v"(lo));
+            asm("" : "+v"(hi));
             const float e0 = (float)(lo & 0xffu), e4 = (float)((lo >> 8) & 0xffu);
             const float e1 = (float)((lo >> 16) & 0xffu), e5 = (float)(lo >> 24);
             const float e2 = (float)(hi & 0xffu), e6 = (float)((hi >> 8) & 0xffu);
@@ -146,14 +150,24 @@ __device__ __forceinline__ void decode_wblk(const WBlk<FMT> &w, int c, uint32_t 
 #pragma unroll
         for (int q = 0; q < 4; q++) {
             const int o = q & 1;
-            const float S = Sab[q >> 1];
-#pragma unroll
-            for (int p = 0; p < 4; p++) {
-                const int sh = 8 * o + 2 * p;
-                const int u0 = (int)(((l4[q] >> (4 * p)) & 15u) | ((h2[q >> 1] >> sh) & 3u) << 4);
-                const int u1 = (int)(((l4[q] >> (16 + 4 * p)) & 15u) | ((h2[q >> 1] >> (16 + sh)) & 3u) << 4);
-                out[4 * q + p] = pack_bf16(S * (float)(u0 - 32), S * (float)(u1 - 32));
-            }
+            const float S = Sab[q >> 1], B = -32.0f * S;  // S (u - 32) = fma(S, u, -32 S), one rounding
+            // the four codes u = q + 32 of bytes (e0, e4, e1, e5) and (e2, e6, e3, e7) of the octet:
+            // low nibbles masked out of the dword, the two high bits of each moved to bits 4-5 of
+            // its byte (element 2p's pair at bit 8o + 2p of the high-bit dword, 2p + 1's at 16 + 8o + 2p)
+            const uint32_t x = h2[q >> 1] >> (8 * o);
+            uint32_t ua = (l4[q] & 0x0F0F0F0Fu) | ((x << 4) & 0x00300030u) | ((x << 8) & 0x30003000u);
+            uint32_t ub = ((l4[q] >> 4) & 0x0F0F0F0Fu) | ((x << 2) & 0x00300030u) | ((x << 6) & 0x30003000u);
+            // opaque, so that each element converts with one byte-selecting v_cvt_f32_ubyteN
+            asm("" : "+v"(ua));
+            asm("" : "+v"(ub));
+            const float e0 = (float)(ua & 0xffu), e4 = (float)((ua >> 8) & 0xffu);
+            const float e1 = (float)((ua >> 16) & 0xffu), e5 = (float)(ua >> 24);
+            const float e2 = (float)(ub & 0xffu), e6 = (float)((ub >> 8) & 0xffu);
+            const float e3 = (float)((ub >> 16) & 0xffu), e7 = (float)(ub >> 24);
+            out[4 * q + 0] = pack_bf16(fmaf(S, e0, B), fmaf(S, e1, B));
+            out[4 * q + 1] = pack_bf16(fmaf(S, e2, B), fmaf(S, e3, B));
+            out[4 * q + 2] = pack_bf16(fmaf(S, e4, B), fmaf(S, e5, B));
+            out[4 * q + 3] = pack_bf16(fmaf(S, e6, B), fmaf(S, e7, B));
         }
     }
 }
