@@ -543,9 +543,9 @@ def bench_parts(torch, ql, synth, dev, bf16_dev, which):
     return parts
 
 
-def cpu_baseline(w, x):
-    """The oracle's quantized GEMV (unpack + exact dequant + fp64 matmul) on
-    the host cores, over whole 14336x4096 Q4K matrices, repeated for ~12 s."""
+def _oracle_gemv_rate(w, x, seconds):
+    """GB/s of quantized weights through the oracle's GEMV (unpack + exact
+    dequant + fp64 matmul) over whole matrices, repeated for `seconds`."""
     import oracle
 
     N, K = w.shape
@@ -558,13 +558,49 @@ def cpu_baseline(w, x):
         oracle.matmul_a16(Wd, x)
         reps += 1
         el = time.perf_counter() - t0
-        if el > 12.0 or reps >= 1000:
+        if el > seconds or reps >= 1000:
             break
+    return buf.size * reps / el / 1e9, reps, el
+
+
+_ONE_CORE = """
+import sys, json, numpy as np
+sys.path.insert(0, {root!r})
+import bench
+d = np.load({path!r})
+r, reps, el = bench._oracle_gemv_rate(d["w"], d["x"], 8.0)
+print(json.dumps({{"value": round(r, 3), "reps": reps, "el": el}}))
+"""
+
+
+def cpu_baseline(w, x):
+    """The oracle's quantized GEMV on the host cores, over whole 14336x4096
+    Q4K matrices, repeated for ~12 s; then the same on one core in a child
+    process whose thread counts are pinned to 1 (the child never touches the
+    GPU)."""
+    import subprocess
+    import tempfile
+
+    rate, reps, el = _oracle_gemv_rate(w, x, 12.0)
     cores = len(os.sched_getaffinity(0))
     threads = int(os.environ.get("OMP_NUM_THREADS", cores))
-    return {"value": round(buf.size * reps / el / 1e9, 3), "unit": "GB/s", "cores": min(cores, threads),
-            "kind": "oracle",
-            "sample": f"{reps} full 14336x4096 Q4K GEMVs (M=1): unpack + fp64 dequant + fp64 matmul, {el:.1f} s"}
+    out = {"value": round(rate, 3), "unit": "GB/s", "cores": min(cores, threads), "kind": "oracle",
+           "sample": f"{reps} full {w.shape[0]}x{w.shape[1]} Q4K GEMVs (M=1): unpack + fp64 dequant + fp64 matmul, "
+                     f"{el:.1f} s"}
+    with tempfile.TemporaryDirectory() as tmp:
+        path = os.path.join(tmp, "wx.npz")
+        np.savez(path, w=w, x=x)
+        env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1",
+                   HIP_VISIBLE_DEVICES="")
+        res = subprocess.run([sys.executable, "-c", _ONE_CORE.format(root=ROOT, path=path)], env=env,
+                             capture_output=True, text=True, timeout=300)
+    if res.returncode == 0 and res.stdout.strip():
+        one = json.loads(res.stdout.strip().splitlines()[-1])
+        out["one_core"] = {"value": one["value"], "unit": "GB/s", "cores": 1,
+                           "sample": f"{one['reps']} full {w.shape[0]}x{w.shape[1]} Q4K GEMVs (M=1), {one['el']:.1f} s"}
+    else:
+        out["one_core"] = {"value": None, "error": (res.stderr or "no output")[-300:]}
+    return out
 
 
 if __name__ == "__main__":
