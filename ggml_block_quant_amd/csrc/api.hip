@@ -2,6 +2,7 @@
 // selection and launches.  Every check happens before any HIP call, so an
 // argument error never launches anything.
 #include "../../include/qlinear.h"
+#include "gemv_fp8.h"
 #include "qlinear_internal.h"
 
 #include <stdint.h>
@@ -55,6 +56,18 @@ int matmul_args(int fmt, const void *blocks, const void *X, const float *Y, int6
         K % 256 != 0 || N * K > kMaxElems || M * K > kMaxElems || M * N > kMaxElems)
         return Q_ESHAPE;
     return Q_OK;
+}
+
+// the GEMV of a format: FP8 one- and two-token shapes on their own one-shot
+// kernel, everything else on the GEMV kernels of the format
+int gemv(int fmt, const uint8_t *B, const uint16_t *X, float *Y, int64_t M, int64_t N, int64_t K, hipStream_t s)
+{
+    if (fmt == QFMT_FP8) {
+        hipError_t e = hipSuccess;
+        if (ql::launch_gemv_fp8(B, X, Y, (int)M, N, K, s, e))
+            return status_of(e);
+    }
+    return status_of(ql::launch_gemv(fmt, B, X, Y, (int)M, N, K, s));
 }
 
 }  // namespace
@@ -121,7 +134,7 @@ int qmatmul_ex(int fmt, const void *blocks, const void *X_bf16, float *Y_fp32, i
         // measured crossover on MI355X: the fused GEMV wins for one or two
         // tokens; from three tokens the MFMA weight stream is faster
         if (M <= 2) {
-            st = status_of(ql::launch_gemv(fmt, B, X, Y_fp32, (int)M, N, K, s));
+            st = gemv(fmt, B, X, Y_fp32, M, N, K, s);
             if (st != Q_ENOTSUP)
                 return st;
         }
@@ -129,7 +142,7 @@ int qmatmul_ex(int fmt, const void *blocks, const void *X_bf16, float *Y_fp32, i
     case QPATH_GEMV:
         if (M > 8)
             return Q_ESHAPE;
-        return status_of(ql::launch_gemv(fmt, B, X, Y_fp32, (int)M, N, K, s));
+        return gemv(fmt, B, X, Y_fp32, M, N, K, s);
     case QPATH_MFMA_BF16:
         return status_of(ql::launch_gemm_bf16(fmt, B, X, Y_fp32, M, N, K, s));
     case QPATH_MFMA_I8: {

@@ -62,6 +62,25 @@ def test_fp8_w8a16_paths_and_one_hot():
         assert np.array_equal(Y, Wd[:, [0, 77, K - 1]].T.astype(np.float32))
 
 
+def test_fp8_gemv_long_rows():
+    """The one-shot FP8 GEMV at 5 .. 16 pieces of 1024 codes per lane and
+    row (K = 5120 .. 16384, ragged N), two tokens up to K = 8192 and the
+    generic kernel beyond; a one-hot X returns s * e4m3 of every column."""
+    for N, K, Ms in ((129, 5120, (1, 2)), (70, 8192, (1, 2)), (33, 14336, (1, 2)), (17, 16384, (1,))):
+        w = synth.weights_bf16(10250 + K, N, K, outliers=True)
+        b = _isq(w)
+        Wd = oracle.dequant_fp8(oracle.quantize_fp8(w))
+        for M in Ms:
+            x = synth.activations_bf16(10251 + M, M, K)
+            Yr, den = oracle.matmul_a16(Wd, x)
+            Y = ql.qmatmul("fp8", b, to_dev_bf16(x), N, path="gemv").cpu().numpy()
+            check_outputs(Y, Yr, den, f"fp8 gemv M={M} N={N} K={K}")
+        x = np.zeros((1, K), np.uint16)
+        x[0, K - 17] = 0x3F80
+        Y = ql.qmatmul("fp8", b, to_dev_bf16(x), N, path="gemv").cpu().numpy()
+        assert np.array_equal(Y[0], Wd[:, K - 17].astype(np.float32))
+
+
 def test_fp8_w8a8_path():
     """Dynamic per-token W8A8: the workspace holds X's E4M3 codes and
     scales bit for bit; outputs within the bar of the exact product."""
