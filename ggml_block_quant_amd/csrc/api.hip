@@ -52,8 +52,10 @@ int matmul_args(int fmt, const void *blocks, const void *X, const float *Y, int6
         return Q_EINVAL;
     if (!aligned16(blocks) || !aligned16(X) || !aligned16(Y))
         return Q_EALIGN;
-    if (M < 1 || M > QLINEAR_MAX_M || N < 1 || N > QLINEAR_MAX_N || K < 256 || K > QLINEAR_MAX_K ||
-        K % 256 != 0 || N * K > kMaxElems || M * K > kMaxElems || M * N > kMaxElems)
+    // K % 256 (Q8_0: K % 32, the tail of whole blocks)
+    const int kq = fmt == QFMT_Q8_0 ? 32 : 256;
+    if (M < 1 || M > QLINEAR_MAX_M || N < 1 || N > QLINEAR_MAX_N || K < kq || K > QLINEAR_MAX_K || K % kq != 0 ||
+        N * K > kMaxElems || M * K > kMaxElems || M * N > kMaxElems)
         return Q_ESHAPE;
     return Q_OK;
 }
@@ -113,7 +115,7 @@ int q_act_quantize(const void *X_bf16, int64_t M, int64_t K, void *out_blocks, v
 
 size_t qmatmul_workspace_bytes(int fmt, int path, int64_t M, int64_t K)
 {
-    if (path == QPATH_MFMA_I8 && fmt == QFMT_Q8_0 && check_tensor(QFMT_Q8_0, M, K, QLINEAR_MAX_M) == Q_OK)
+    if (path == QPATH_MFMA_I8 && fmt == QFMT_Q8_0 && K % 256 == 0 && check_tensor(QFMT_Q8_0, M, K, QLINEAR_MAX_M) == Q_OK)
         return (size_t)ql::planes_of(ql::FMT_Q8_0, M, K).total;
     if (path == QPATH_MFMA_FP8 && fmt == QFMT_FP8 && check_tensor(QFMT_FP8, M, K, QLINEAR_MAX_M) == Q_OK)
         return (size_t)ql::planes_of(ql::FMT_FP8, M, K).total;
@@ -148,6 +150,8 @@ int qmatmul_ex(int fmt, const void *blocks, const void *X_bf16, float *Y_fp32, i
     case QPATH_MFMA_I8: {
         if (fmt != QFMT_Q8_0)
             return Q_ENOTSUP;
+        if (K % 256 != 0)
+            return Q_ESHAPE;  // the int8 kernels take the scales of two blocks per dword
         if (!workspace)
             return Q_EINVAL;
         if (!aligned16(workspace))

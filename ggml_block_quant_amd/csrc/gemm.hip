@@ -1120,12 +1120,30 @@ __global__ __launch_bounds__(256) void gemm_gen_kernel(const uint8_t *__restrict
 #pragma unroll
         for (int u = 0; u < U; u++) {
             if (s + u < s1) {
-                const bf16x8_t bw = __builtin_bit_cast(
-                    bf16x8_t, make_uint4(pack_bf16(w[u][0], w[u][1]), pack_bf16(w[u][2], w[u][3]),
-                                         pack_bf16(w[u][4], w[u][5]), pack_bf16(w[u][6], w[u][7])));
+                uint32_t h[4];
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    h[e] = pack_bf16(w[u][2 * e], w[u][2 * e + 1]);
+                const bf16x8_t bw = __builtin_bit_cast(bf16x8_t, make_uint4(h[0], h[1], h[2], h[3]));
 #pragma unroll
                 for (int j = 0; j < TM; j++)
                     acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[u][j], bw, acc[j], 0, 0, 0);
+                if constexpr (FMT == FMT_Q8_0) {
+                    // Q8_0 here serves rows that end in a tail of blocks, down to
+                    // a single block, where the bf16 rounding of each weight
+                    // (up to 2^-9) would not average out: add the remainder
+                    // w - bf16(w) (exact in fp32: d q has at most 18 significant
+                    // bits) as a second bf16 operand, leaving at most 2^-18 |w|
+                    uint32_t l[4];
+#pragma unroll
+                    for (int e = 0; e < 4; e++)
+                        l[e] = pack_bf16(w[u][2 * e] - __uint_as_float(h[e] << 16),
+                                         w[u][2 * e + 1] - __uint_as_float(h[e] & 0xffff0000u));
+                    const bf16x8_t bl = __builtin_bit_cast(bf16x8_t, make_uint4(l[0], l[1], l[2], l[3]));
+#pragma unroll
+                    for (int j = 0; j < TM; j++)
+                        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[u][j], bl, acc[j], 0, 0, 0);
+                }
             }
         }
     }
@@ -1764,6 +1782,11 @@ hipError_t launch_gemm_bf16(int fmt, const uint8_t *blocks, const uint16_t *X, f
 {
     if (generic_fmt(fmt))
         return launch_gemm_gen(fmt, blocks, X, Y, M, N, K, s);
+    // Q8_0 rows that end in a tail of blocks (K % 256 != 0): the generic
+    // kernel, which steps K by one block (the tuned ones take 128-element
+    // slabs and two blocks' scales per dword)
+    if (fmt == FMT_Q8_0 && K % 256 != 0)
+        return gen_tm<FMT_Q8_0>(blocks, X, Y, M, N, K, s);
     const Planes p = planes_of(fmt, N, K);
     if (fmt == FMT_Q4K)
         return bf16_by_m<FMT_Q4K>(blocks, p, X, Y, M, N, K, s);

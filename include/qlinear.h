@@ -102,7 +102,7 @@ typedef enum {
 enum {
     Q_OK = 0,
     Q_EINVAL = -1,  /* NULL pointer, unknown format/path, bad workspace */
-    Q_ESHAPE = -2,  /* M, N, K out of range or K not a multiple of 256 */
+    Q_ESHAPE = -2,  /* M, N, K out of range or K not a multiple of 256 (Q8_0: 32) */
     Q_EALIGN = -3,  /* a pointer is not 16-byte aligned */
     Q_ENOTSUP = -4, /* format or path not implemented for these arguments */
     Q_EHIP = -5     /* the HIP runtime refused a launch or a query */
@@ -156,7 +156,9 @@ int q_act_quantize(const void *X_bf16, int64_t M, int64_t K, void *out_blocks, v
 /* Quantized matmul Y = X . deq(W)^T on the AUTO path (no workspace).
  * blocks: device, from isq_quantize(fmt, W, N, K).  X_bf16: device [M][K].
  * Y_fp32: device [M][N], overwritten (not accumulated).
- * 1 <= M <= QLINEAR_MAX_M, K % 256 == 0. */
+ * 1 <= M <= QLINEAR_MAX_M, K % 256 == 0; Q8_0 weights also take rows that end
+ * in a tail of whole blocks (K % 32 == 0, K >= 32: the GEMV kernels, and for
+ * the MFMA path the generic exact-decode kernel). */
 int qmatmul(int fmt, const void *blocks, const void *X_bf16, float *Y_fp32, int64_t M,
             int64_t N, int64_t K, void *stream);
 
@@ -166,7 +168,7 @@ int qmatmul(int fmt, const void *blocks, const void *X_bf16, float *Y_fp32, int6
 size_t qmatmul_workspace_bytes(int fmt, int path, int64_t M, int64_t K);
 
 /* Quantized matmul on an explicit path.  QPATH_GEMV needs M <= 8.
- * QPATH_MFMA_I8 needs fmt == QFMT_Q8_0 and a device workspace of at least
+ * QPATH_MFMA_I8 needs fmt == QFMT_Q8_0, K % 256 == 0 and a device workspace of at least
  * qmatmul_workspace_bytes() bytes (16-byte aligned); on return it holds
  * the Q8_0 blocks of X (codes then scales).  QPATH_MFMA_FP8 (page section
  * "FP8": dynamic per-token W8A8) needs fmt == QFMT_FP8 and a workspace of

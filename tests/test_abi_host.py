@@ -154,6 +154,15 @@ def test_qmatmul_argument_errors():
     assert call(fmt=12, path=4) == ql.Q_EINVAL         # ... and a workspace
     assert call(fmt=12, path=4, ws=A, wsb=100) == ql.Q_EINVAL
     assert call(fmt=13) == ql.Q_EINVAL
+    # Q8_0 rows may end in a tail of whole blocks (K % 32); other formats and
+    # the int8 path need K % 256 (no launch happens for these errors)
+    assert call(fmt=0, K=100) == ql.Q_ESHAPE
+    assert call(fmt=0, K=16) == ql.Q_ESHAPE
+    assert call(fmt=7, K=96) == ql.Q_ESHAPE
+    assert call(fmt=12, K=96) == ql.Q_ESHAPE
+    assert call(fmt=0, K=96, path=3, ws=A, wsb=1 << 20) == ql.Q_ESHAPE
+    assert L.qmatmul_workspace_bytes(0, 3, 4, 96) == 0
+    assert L.qmatmul_workspace_bytes(0, 3, 4, 256) > 0
     assert L.qmatmul(1, A, A2, NULL, 4, 64, 256, NULL) == ql.Q_EINVAL
     assert ok
 

@@ -206,6 +206,29 @@ def test_mfma_bf16_q4k_quad_stream():
         assert np.array_equal(Y, Wbf.T), f"quad stream one-hot N={N} K={K}"
 
 
+def test_q8_0_block_tails():
+    """Q8_0 rows of K % 32 == 0 that are not whole 256-element groups: ISQ
+    and dequantization exact, GEMV (M = 1, 2 on the one-shot kernel, 3 and 8
+    on the persistent one) and the MFMA path (the generic kernel) within the
+    bar, one-hot columns exact on the GEMV."""
+    for N, K in ((7, 32), (300, 96), (129, 992), (65, 4128)):
+        w = synth.weights_bf16(5200 + K, N, K, outliers=True)
+        blocks = ql.isq("q8_0", to_dev_bf16(w))
+        assert_blocks_equal("q8_0", blocks.cpu().numpy(), w, f"isq K={K}")
+        Wd = oracle.dequant("q8_0", oracle.quantize("q8_0", w), N, K)
+        assert np.array_equal(ql.dequantize("q8_0", blocks, N, K).cpu().numpy(), Wd.astype(np.float32))
+        for M, path in ((1, "gemv"), (2, "auto"), (3, "gemv"), (8, "gemv"), (3, "auto"), (16, "mfma_bf16"),
+                        (130, "auto")):
+            x = synth.activations_bf16(5201 + M, M, K)
+            Yr, den = oracle.matmul_a16(Wd, x)
+            Y = ql.qmatmul("q8_0", blocks, to_dev_bf16(x), N, path=path).cpu().numpy()
+            check_outputs(Y, Yr, den, f"q8_0 tail {path} M={M} N={N} K={K}")
+        x = np.zeros((2, K), np.uint16)
+        x[0, 0], x[1, K - 1] = 0x3F80, 0x3F80
+        Y = ql.qmatmul("q8_0", blocks, to_dev_bf16(x), N, path="gemv").cpu().numpy()
+        assert np.array_equal(Y, Wd[:, [0, K - 1]].T.astype(np.float32))
+
+
 def test_mfma_i8_shapes_and_activation_blocks():
     """Ragged tiles and K splits; K = 1280 with one tile splits 40 steps of
     one block into 16 runs of 3, the last two of them empty."""
