@@ -30,6 +30,7 @@ typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef int i32x16_t __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ float h2f(uint32_t bits16)
@@ -1218,93 +1219,205 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(const uint8_t *__restrict
         }
 }
 
-// Large-M FP8 W8A8 (prefill): output tile 128 tokens x 128 rows of W per
-// workgroup of four waves (wave (wm, wn) owns 64 x 64 = 4 x 4 MFMA tiles of
-// 16 x 16); K advances in stages of 64 codes through a double-buffered LDS
-// copy of both tiles (rows padded to 72 bytes: the 16 rows a fragment read
-// touches land on distinct banks); the next stage's global loads are in
-// flight while the current one is multiplied.
-constexpr int F8T = 128, F8K = 64, F8P = 72;
+// Large-M FP8 W8A8 (prefill): a workgroup of WMW x WNW waves owns an output
+// tile of TM = 32 TI WMW tokens by TN = 32 TJ WNW rows of W; wave (wm, wn)
+// owns TI x TJ tiles of 32 x 32.  K advances in steps of 64 codes, one
+// v_mfma_f32_32x32x64_f8f6f4 per tile and step (E4M3 operands, unit block
+// scales).  Lane (h, r) of a fragment holds the 32 codes k = 32h .. 32h + 31
+// of row r for both operands: the instruction pairs A and B elements by the
+// same lane and byte, so any such common placement of k gives the same dot
+// products.
+//
+// X and W codes reach LDS by direct global->LDS loads into a ring of four
+// stages (TM X rows then TN W rows of 64 bytes each), issued four steps
+// ahead; the only waits on them are explicit vmcnt waits, one barrier per
+// step.  16-byte chunk c of row r sits at slot 4r + (c ^ ((r>>1 ^ r>>2) &
+// 3)), so the 16 (or 8) rows one ds_read_b128 phase touches land on distinct
+// banks.  Step kt + 1's operands are read while step kt's products run.
+constexpr int F8K = 64;  // k per step
+constexpr int F8S = 4;   // ring stages
 
-__global__ __launch_bounds__(256) void gemm_fp8_tile_kernel(const uint8_t *__restrict__ Wq,
-                                                            const float *__restrict__ ws,
-                                                            const uint8_t *__restrict__ Xq,
-                                                            const float *__restrict__ xs, float *__restrict__ Y,
-                                                            int M, int N, int K)
+// s_waitcnt immediate: vmcnt n (bits 3:0 and 15:14), lgkmcnt 0, expcnt any
+constexpr int vm_wait(int n) { return 0x0070 | (n & 15) | ((n >> 4) << 14); }
+
+__device__ __forceinline__ int f8slot(int r, int c) { return 4 * r + (c ^ (((r >> 1) ^ (r >> 2)) & 3)); }
+
+template <int WMW, int WNW, int TI, int TJ>
+struct F8Tile {
+    static constexpr int W = WMW * WNW;              // waves
+    static constexpr int TM = 32 * TI * WMW, TN = 32 * TJ * WNW;
+    static constexpr int STG = (TM + TN) * F8K;      // bytes per stage
+    static constexpr int LX = TM / 16 / W, LW = TN / 16 / W;  // loads per wave and stage
+    static_assert(LX * 16 * W == TM && LW * 16 * W == TN, "whole load instructions per wave");
+    static_assert(4 * (LX + LW) * (F8S - 1) < 64, "vmcnt range");
+};
+
+template <int WMW, int WNW, int TI, int TJ>
+__global__ __launch_bounds__(64 * WMW * WNW) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_fp8_tile_kernel(
+    const uint8_t *__restrict__ Wq, const float *__restrict__ ws, const uint8_t *__restrict__ Xq,
+    const float *__restrict__ xs, float *__restrict__ Y, int M, int N, int K)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t sa[2][F8T * F8P];  // X tile: [token][k]
-    __shared__ __attribute__((aligned(16))) uint8_t sb[2][F8T * F8P];  // W tile: [row][k]
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int wm = wv >> 1, wn = wv & 1;
-    const int g = lane >> 4, r16 = lane & 15;
-    const int m0 = blockIdx.y * F8T, n0 = blockIdx.x * F8T;
-    // global -> LDS: thread t moves 16 bytes of rows t/4 and 64 + t/4, column 16 (t % 4)
-    const int lr = tid >> 2, lc = 16 * (tid & 3);
-    const uint8_t *xa0 = Xq + (int64_t)min(m0 + lr, M - 1) * K + lc;
-    const uint8_t *xa1 = Xq + (int64_t)min(m0 + 64 + lr, M - 1) * K + lc;
-    const uint8_t *wb0 = Wq + (int64_t)min(n0 + lr, N - 1) * K + lc;
-    const uint8_t *wb1 = Wq + (int64_t)min(n0 + 64 + lr, N - 1) * K + lc;
-    uint4 ra0, ra1, rb0, rb1;
-    auto fetch = [&](int k0) {
-        ra0 = *reinterpret_cast<const uint4 *>(xa0 + k0);
-        ra1 = *reinterpret_cast<const uint4 *>(xa1 + k0);
-        rb0 = *reinterpret_cast<const uint4 *>(wb0 + k0);
-        rb1 = *reinterpret_cast<const uint4 *>(wb1 + k0);
+    using T = F8Tile<WMW, WNW, TI, TJ>;
+    constexpr int LX = T::LX, LW = T::LW, NL = LX + LW;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[F8S * T::STG];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wv / WNW, wn = wv % WNW;
+    const int m0 = blockIdx.y * T::TM, n0 = blockIdx.x * T::TN;
+    const int nk = K / F8K;
+
+    // direct loads: instruction j of wave w fills slots 64 (L w + j) + lane
+    // of the X (L = LX) or the W (L = LW) region; rows past M / N re-read the
+    // last row (results dropped); byte offsets from row m0 / n0 of the step
+    uint32_t ox[LX], ow[LW];
+#pragma unroll
+    for (int j = 0; j < LX; j++) {
+        const int sl = 64 * (LX * wv + j) + lane, r = sl >> 2;
+        const int c = (sl & 3) ^ (((r >> 1) ^ (r >> 2)) & 3);
+        ox[j] = (uint32_t)((min(m0 + r, M - 1) - m0) * K + 16 * c);
+    }
+#pragma unroll
+    for (int j = 0; j < LW; j++) {
+        const int sl = 64 * (LW * wv + j) + lane, r = sl >> 2;
+        const int c = (sl & 3) ^ (((r >> 1) ^ (r >> 2)) & 3);
+        ow[j] = (uint32_t)((min(n0 + r, N - 1) - n0) * K + 16 * c);
+    }
+    const uint8_t *const xbase = Xq + (int64_t)m0 * K;
+    const uint8_t *const wbase = Wq + (int64_t)n0 * K;
+    auto issue = [&](int kt) {
+        const uint32_t st = lds_addr(smem + (kt % F8S) * T::STG);
+#pragma unroll
+        for (int j = 0; j < LX; j++)
+            dma16(xbase + F8K * kt, ox[j], st + 1024 * (LX * wv + j));
+#pragma unroll
+        for (int j = 0; j < LW; j++)
+            dma16(wbase + F8K * kt, ow[j], st + T::TM * F8K + 1024 * (LW * wv + j));
     };
-    auto stash = [&](int b) {
-        *reinterpret_cast<uint4 *>(&sa[b][lr * F8P + lc]) = ra0;
-        *reinterpret_cast<uint4 *>(&sa[b][(64 + lr) * F8P + lc]) = ra1;
-        *reinterpret_cast<uint4 *>(&sb[b][lr * F8P + lc]) = rb0;
-        *reinterpret_cast<uint4 *>(&sb[b][(64 + lr) * F8P + lc]) = rb1;
+
+    // fragment offsets in a stage: A = X rows 32 (TI wm + i) + r, B = W rows
+    // 32 (TJ wn + j) + r; chunks 2h and 2h + 1
+    const int r32 = lane & 31, h = lane >> 5;
+    int oa[TI][2], ob[TJ][2];
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+#pragma unroll
+        for (int i = 0; i < TI; i++)
+            oa[i][q] = 16 * f8slot(32 * (TI * wm + i) + r32, 2 * h + q);
+#pragma unroll
+        for (int j = 0; j < TJ; j++)
+            ob[j][q] = T::TM * F8K + 16 * f8slot(32 * (TJ * wn + j) + r32, 2 * h + q);
+    }
+    auto frag = [&](const uint8_t *p0, const uint8_t *p1) {
+        const i32x4_t u = *reinterpret_cast<const i32x4_t *>(p0), v = *reinterpret_cast<const i32x4_t *>(p1);
+        return i32x8_t{u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
     };
-    f32x4_t acc[4][4];
+    i32x8_t a[TI], b[TJ], an[TI], bn[TJ];
+    auto reads = [&](int kt) {
+        const uint8_t *st = smem + (kt % F8S) * T::STG;
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+        for (int i = 0; i < TI; i++)
+            an[i] = frag(st + oa[i][0], st + oa[i][1]);
 #pragma unroll
-        for (int j = 0; j < 4; j++)
-            acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    const int nst = K / F8K;
-    fetch(0);
-    stash(0);
-    __syncthreads();
-    for (int st = 0; st < nst; st++) {
-        const int b = st & 1;
-        if (st + 1 < nst)
-            fetch(F8K * (st + 1));
+        for (int j = 0; j < TJ; j++)
+            bn[j] = frag(st + ob[j][0], st + ob[j][1]);
+    };
+    auto take = [&]() {
 #pragma unroll
-        for (int ks = 0; ks < 2; ks++) {
-            long af[4], bf[4];
+        for (int i = 0; i < TI; i++)
+            a[i] = an[i];
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                af[i] = *reinterpret_cast<const long *>(&sa[b][(64 * wm + 16 * i + r16) * F8P + 32 * ks + 8 * g]);
-                bf[i] = *reinterpret_cast<const long *>(&sb[b][(64 * wn + 16 * i + r16) * F8P + 32 * ks + 8 * g]);
-            }
+        for (int j = 0; j < TJ; j++)
+            b[j] = bn[j];
+    };
+    f32x16_t acc[TI][TJ];
 #pragma unroll
-            for (int i = 0; i < 4; i++)
+    for (int i = 0; i < TI; i++)
 #pragma unroll
-                for (int j = 0; j < 4; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(af[i], bf[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < TJ; j++)
+            acc[i][j] = f32x16_t{};
+    auto products = [&]() {
+#pragma unroll
+        for (int i = 0; i < TI; i++)
+#pragma unroll
+            for (int j = 0; j < TJ; j++)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], 0, 0, 0, 127, 0,
+                                                                           127);
+    };
+
+    for (int kt = 0; kt < F8S && kt < nk; kt++)
+        issue(kt);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (nk >= F8S)
+        __builtin_amdgcn_s_waitcnt(vm_wait(NL * (F8S - 1)));  // step 0 landed
+    else
+        __builtin_amdgcn_s_waitcnt(vm_wait(0));
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    reads(0);
+    // Step kt: wait until step kt + 1 has landed (the loads of steps kt + 2
+    // and kt + 3 may remain) and every wave's reads of step kt are done, so
+    // that the loads of step kt + 4 can take its stage; read step kt + 1's
+    // operands, then multiply step kt's.
+    for (int kt = 0; kt + 1 < nk; kt++) {
+        take();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (kt + F8S - 1 < nk)
+            __builtin_amdgcn_s_waitcnt(vm_wait(NL * (F8S - 2)));
+        else
+            __builtin_amdgcn_s_waitcnt(vm_wait(0));
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (kt + F8S < nk)
+            issue(kt + F8S);
+        reads(kt + 1);
+        products();
+    }
+    take();
+    products();
+
+    // lane holds D[m = 8 (r / 4) + 4 h + r % 4][n = r32] of tile (i, j).  The
+    // scales load unconditionally (clamped rows), and whole tiles store
+    // without guards: a scale used inside a guarded store makes the compiler
+    // wait for every earlier memory operation before each store.
+    float sx[TI][16], swn[TJ];
+#pragma unroll
+    for (int i = 0; i < TI; i++)
+#pragma unroll
+        for (int r = 0; r < 16; r++)
+            sx[i][r] = xs[min(m0 + 32 * (TI * wm + i) + 8 * (r >> 2) + 4 * h + (r & 3), M - 1)];
+#pragma unroll
+    for (int j = 0; j < TJ; j++)
+        swn[j] = ws[min(n0 + 32 * (TJ * wn + j) + r32, N - 1)];
+    auto store = [&](auto guard_t) {
+        constexpr bool GUARD = decltype(guard_t)::value;
+#pragma unroll
+        for (int j = 0; j < TJ; j++) {
+            const int n = n0 + 32 * (TJ * wn + j) + r32;
+#pragma unroll
+            for (int i = 0; i < TI; i++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const int m = m0 + 32 * (TI * wm + i) + 8 * (r >> 2) + 4 * h + (r & 3);
+                    if (!GUARD || (m < M && n < N))
+                        Y[(int64_t)m * N + n] = acc[i][j][r] * (sx[i][r] * swn[j]);
+                }
         }
-        if (st + 1 < nst)
-            stash(b ^ 1);
-        __syncthreads();
-    }
-    // lane holds D[m = 4g + r][n = r16] of tile (i, j)
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const int n = n0 + 64 * wn + 16 * j + r16;
-        if (n >= N)
-            continue;
-        const float sw = ws[n];
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const int m = m0 + 64 * wm + 16 * i + 4 * g + r;
-                if (m < M)
-                    Y[(int64_t)m * N + n] = acc[i][j][r] * (xs[m] * sw);
-            }
-    }
+    };
+    if (m0 + T::TM <= M && n0 + T::TN <= N)
+        store(std::false_type{});
+    else
+        store(std::true_type{});
+}
+
+template <int WMW, int WNW, int TI, int TJ>
+hipError_t go_fp8_tile(const uint8_t *wblocks, const float *ws, const uint8_t *xblocks, const float *xs, float *Y,
+                       int64_t M, int64_t N, int64_t K, hipStream_t s)
+{
+    using T = F8Tile<WMW, WNW, TI, TJ>;
+    hipLaunchKernelGGL((gemm_fp8_tile_kernel<WMW, WNW, TI, TJ>),
+                       dim3((unsigned)((N + T::TN - 1) / T::TN), (unsigned)((M + T::TM - 1) / T::TM)),
+                       dim3(64 * T::W), 0, s, wblocks, ws, xblocks, xs, Y, (int)M, (int)N, (int)K);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -1818,10 +1931,13 @@ hipError_t launch_gemm_fp8(const uint8_t *wblocks, const uint8_t *xblocks, float
 {
     if (M >= 128) {
         const Planes pw = planes_of(FMT_FP8, N, K), px = planes_of(FMT_FP8, M, K);
-        hipLaunchKernelGGL(gemm_fp8_tile_kernel, dim3((unsigned)((N + F8T - 1) / F8T), (unsigned)((M + F8T - 1) / F8T)),
-                           dim3(256), 0, s, wblocks, reinterpret_cast<const float *>(wblocks + pw.scales), xblocks,
-                           reinterpret_cast<const float *>(xblocks + px.scales), Y, (int)M, (int)N, (int)K);
-        return hipGetLastError();
+        const float *ws = reinterpret_cast<const float *>(wblocks + pw.scales);
+        const float *xs = reinterpret_cast<const float *>(xblocks + px.scales);
+        // 256 x 256 tiles (eight waves) move half the bytes per product of the
+        // 128 x 128 ones, where there are enough of them for every CU
+        if (((M + 255) / 256) * ((N + 255) / 256) >= 256)
+            return go_fp8_tile<4, 2, 2, 4>(wblocks, ws, xblocks, xs, Y, M, N, K, s);
+        return go_fp8_tile<2, 2, 2, 2>(wblocks, ws, xblocks, xs, Y, M, N, K, s);
     }
     if (M <= 16)
         return go_fp8<1>(wblocks, xblocks, Y, M, N, K, s);

@@ -513,25 +513,140 @@ Gaps gaps_of(int fmt, int64_t N, int64_t K, const Planes &p)
 // variant without infinities).  Also the dynamic per-token quantizer of the
 // activations on the W8A8 path.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t e4m3_from_f32(float v)
+// E4M3 code of v, rounded to nearest even, saturated to +-448: with e the
+// binade of |v| (at least -6, the subnormal grid) and u = |v| 2^(3 - e) in
+// [0, 16), r = rint(u) and the code is 8 (e + 7) + r - 8 -- one formula for
+// subnormals (e = -6, u < 8), normals and the carry r = 16 into the next
+// binade; codes above 0x7E saturate (the variant without infinities).  near
+// is set where u lies within 2^-19 u of a rounding midpoint, which flags
+// every value within three ulps of a change of code.
+__device__ __forceinline__ uint32_t e4m3_rne(float v, bool &near)
 {
-    const uint32_t sgn = (__float_as_uint(v) >> 31) << 7;
+    const uint32_t sgn = (__float_as_uint(v) >> 24) & 0x80u;
     const float a = fabsf(v);
-    if (a >= 448.0f)
-        return sgn | 0x7Eu;
-    if (a < 0x1p-6f)  // subnormal range: units of 2^-9 (a code of 8 is the smallest normal, 0x08)
-        return sgn | (uint32_t)rintf(a * 512.0f);
-    int e = (int)((__float_as_uint(a) >> 23) & 0xffu) - 127;  // a in [2^e, 2^(e+1)), e in [-6, 8]
-    float r = rintf(__builtin_ldexpf(a, 3 - e));                // 8 .. 16 steps of 2^(e-3)
-    if (r == 16.0f) {
-        e += 1;
-        r = 8.0f;
-    }
-    if (e > 8 || (e == 8 && r > 14.0f))
-        return sgn | 0x7Eu;
-    return sgn | (uint32_t)((e + 7) << 3) | (uint32_t)(r - 8.0f);
+    const int e = max((int)(__float_as_uint(a) >> 23) - 127, -6);
+    const float u = __builtin_ldexpf(a, 3 - e);
+    const float r = rintf(u);
+    near |= fabsf(u - r) >= fmaf(-0x1p-19f, u, 0.5f);
+    return sgn | (uint32_t)min(8 * (e + 7) + (int)r - 8, 0x7E);
 }
 
+// Codes of 16-byte pieces (8 elements) of a row: the E4M3 code of each
+// product t = x * rs; bit j of *redo is set where one of them is near a tie
+// (or where fast is false).
+__device__ __forceinline__ uint2 fp8_piece(uint4 v, float rs, bool fast, uint32_t &redo, int j)
+{
+    float x[8];
+    load8(v, x);
+    uint32_t lo = 0, hi = 0;
+    bool near = !fast;
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        lo |= e4m3_rne(x[k] * rs, near) << (8 * k);
+        hi |= e4m3_rne(x[k + 4] * rs, near) << (8 * k);
+    }
+    redo |= (near ? 1u : 0u) << j;
+    return make_uint2(lo, hi);
+}
+
+// the same piece from the binary32 quotients x / sc
+__device__ __forceinline__ uint2 fp8_piece_exact(uint4 v, float sc)
+{
+    float x[8];
+    load8(v, x);
+    uint32_t lo = 0, hi = 0;
+    bool unused = false;
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        lo |= e4m3_rne(x[k] / sc, unused) << (8 * k);
+        hi |= e4m3_rne(x[k + 4] / sc, unused) << (8 * k);
+    }
+    return make_uint2(lo, hi);
+}
+
+// max of the bf16 magnitudes of a piece into two 15-bit lanes of mx
+__device__ __forceinline__ void absmax_piece(uint4 v, uint32_t &mx)
+{
+    const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        const uint32_t m = q[k] & 0x7fff7fffu;
+        mx = max(mx & 0xffffu, m & 0xffffu) | (max(mx >> 16, m >> 16) << 16);
+    }
+}
+
+// One workgroup per row of up to 2048 CPT elements: thread t holds pieces
+// t + 256 j (j < CPT) in registers; max|x| over the row (exact, on the bf16
+// magnitude bits) by shuffles and LDS, then the codes.  A code is the
+// E4M3 rounding of the binary32 quotient q = x / sc; the kernel rounds
+// t = x * (1 / sc) instead, which differs from q by at most 1.5 * 2^-23 |q|
+// and so rounds the same way unless t is near a rounding midpoint: the
+// 16-byte pieces holding such a t (rare) are recomputed from q afterwards.
+template <int CPT>
+__global__ __launch_bounds__(256) void isq_fp8_row_kernel(const uint4 *__restrict__ W, int K, uint8_t *__restrict__ out,
+                                                          int64_t scales_off, int64_t pad, int npad)
+{
+    __shared__ uint32_t red[4];
+    const int tid = threadIdx.x, lane = tid & 63;
+    if (blockIdx.x == 0 && tid < npad)
+        out[pad + tid] = 0;
+    const int64_t row = blockIdx.x;
+    const int T = K / 8;
+    const uint4 *w = W + row * T;
+    uint4 v[CPT];
+    uint32_t mx = 0;
+#pragma unroll
+    for (int j = 0; j < CPT; j++) {
+        const int i = tid + 256 * j;
+        v[j] = i < T ? w[i] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < CPT; j++)
+        absmax_piece(v[j], mx);
+    uint32_t m16 = max(mx & 0xffffu, mx >> 16);
+#pragma unroll
+    for (int k = 32; k >= 1; k >>= 1)
+        m16 = max(m16, (uint32_t)__shfl_xor((int)m16, k));
+    if (lane == 0)
+        red[tid >> 6] = m16;
+    __syncthreads();
+    m16 = max(max(red[0], red[1]), max(red[2], red[3]));
+    const float sc = __uint_as_float(m16 << 16) / 448.0f;
+    if (tid == 0)
+        reinterpret_cast<float *>(out + scales_off)[row] = sc;
+    uint2 *o = reinterpret_cast<uint2 *>(out + row * K);
+    if (!(sc > 0.0f)) {  // a zero row: zero codes
+#pragma unroll
+        for (int j = 0; j < CPT; j++)
+            if (tid + 256 * j < T)
+                o[tid + 256 * j] = make_uint2(0, 0);
+        return;
+    }
+    // 1 / sc is finite and the bound above holds where sc is normal;
+    // otherwise every piece takes the quotient
+    const bool fast = sc >= 0x1p-120f;
+    const float rs = 1.0f / sc;
+    uint32_t redo = 0;
+#pragma unroll
+    for (int j = 0; j < CPT; j++) {
+        const uint2 c = fp8_piece(v[j], rs, fast, redo, j);
+        if (tid + 256 * j < T)
+            o[tid + 256 * j] = c;
+    }
+    // the rare pieces, from the quotients (same thread, same address: the
+    // later store wins)
+    while (redo) {
+        const int j = __builtin_ctz(redo);
+        redo &= redo - 1;
+        const int i = tid + 256 * j;
+        if (i < T)
+            o[i] = fp8_piece_exact(w[i], sc);
+    }
+}
+
+// Rows longer than 16384 elements: one wave per row, max|x| over segments
+// of 4096 elements (eight 16-byte loads per lane in flight), then the codes
+// segment by segment, re-read.
 __global__ __launch_bounds__(256) void isq_fp8_kernel(const uint4 *__restrict__ W, int64_t N, int K,
                                                       uint8_t *__restrict__ out, int64_t scales_off, int64_t pad,
                                                       int npad)
@@ -542,35 +657,61 @@ __global__ __launch_bounds__(256) void isq_fp8_kernel(const uint4 *__restrict__ 
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= N)
         return;  // the whole wave
+    constexpr int S = 8;  // 16-byte loads per lane and segment
     const int T = K / 8;
     const uint4 *w = W + row * T;
-    float a = 0.0f;
-    for (int i = lane; i < T; i += 64) {
-        float x[8];
-        load8(w[i], x);
+    uint4 v[S];
+    uint32_t mx = 0;  // two 15-bit magnitudes
+    for (int s0 = 0; s0 < T; s0 += 64 * S) {
 #pragma unroll
-        for (int k = 0; k < 8; k++)
-            a = fmaxf(a, fabsf(x[k]));
+        for (int j = 0; j < S; j++) {
+            const int i = s0 + lane + 64 * j;
+            v[j] = i < T ? w[i] : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < S; j++)
+            absmax_piece(v[j], mx);
     }
+    uint32_t m16 = max(mx & 0xffffu, mx >> 16);
 #pragma unroll
     for (int k = 32; k >= 1; k >>= 1)
-        a = fmaxf(a, __shfl_xor(a, k));
-    const float sc = a / 448.0f;
+        m16 = max(m16, (uint32_t)__shfl_xor((int)m16, k));
+    const float sc = __uint_as_float(m16 << 16) / 448.0f;
     if (lane == 0)
         reinterpret_cast<float *>(out + scales_off)[row] = sc;
+    if (!(sc > 0.0f)) {  // a zero row: zero codes
+        for (int i = lane; i < T; i += 64)
+            reinterpret_cast<uint2 *>(out + row * K)[i] = make_uint2(0, 0);
+        return;
+    }
+    // 1 / sc is finite and the bound above holds where sc is normal;
+    // otherwise every piece takes the quotient
+    const bool fast = sc >= 0x1p-120f;
+    const float rs = 1.0f / sc;
     uint2 *o = reinterpret_cast<uint2 *>(out + row * K);
-    for (int i = lane; i < T; i += 64) {
-        float x[8];
-        load8(w[i], x);
-        uint32_t lo = 0, hi = 0;
-        if (sc > 0.0f) {
+    for (int s0 = 0; s0 < T; s0 += 64 * S) {
 #pragma unroll
-            for (int k = 0; k < 4; k++) {
-                lo |= e4m3_from_f32(x[k] / sc) << (8 * k);
-                hi |= e4m3_from_f32(x[k + 4] / sc) << (8 * k);
-            }
+        for (int j = 0; j < S; j++) {
+            const int i = s0 + lane + 64 * j;
+            v[j] = i < T ? w[i] : make_uint4(0, 0, 0, 0);
         }
-        o[i] = make_uint2(lo, hi);
+        uint32_t redo = 0;
+#pragma unroll
+        for (int j = 0; j < S; j++) {
+            const int i = s0 + lane + 64 * j;
+            const uint2 c = fp8_piece(v[j], rs, fast, redo, j);
+            if (i < T)
+                o[i] = c;
+        }
+        // the rare pieces, from the quotients (same lane, same address: the
+        // later store wins)
+        while (redo) {
+            const int j = __builtin_ctz(redo);
+            redo &= redo - 1;
+            const int i = s0 + lane + 64 * j;
+            if (i < T)
+                o[i] = fp8_piece_exact(w[i], sc);
+        }
     }
 }
 
@@ -602,10 +743,22 @@ hipError_t launch_isq(int fmt, const uint16_t *W, int64_t N, int64_t K, uint8_t 
                            reinterpret_cast<int8_t *>(out + p.scales),
                            reinterpret_cast<uint16_t *>(out + p.d), out + 210 * (N * K / 256),
                            (int)(p.total - 210 * (N * K / 256)));
-    else if (fmt == FMT_FP8)
-        hipLaunchKernelGGL(isq_fp8_kernel, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, s, w, N, (int)K, out,
-                           p.scales, p.scales + 4 * N, (int)(p.total - p.scales - 4 * N));
-    else {
+    else if (fmt == FMT_FP8) {
+        const int64_t pad = p.scales + 4 * N;
+        const int npad = (int)(p.total - pad);
+        switch ((K + 2047) / 2048) {
+#define C(CPT)                                                                                                      \
+    case CPT:                                                                                                       \
+        hipLaunchKernelGGL(isq_fp8_row_kernel<CPT>, dim3((unsigned)N), dim3(256), 0, s, w, (int)K, out, p.scales, pad, \
+                           npad);                                                                                   \
+        break;
+            C(1) C(2) C(3) C(4) C(5) C(6) C(7) C(8)
+#undef C
+        default:
+            hipLaunchKernelGGL(isq_fp8_kernel, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, s, w, N, (int)K, out,
+                               p.scales, pad, npad);
+        }
+    } else {
         const Gaps z = gaps_of(fmt, N, K, p);
         const dim3 grid(grid_for(tasks)), block(256);
         switch (fmt) {

@@ -20,9 +20,41 @@ def _isq(w):
     return ql.isq("fp8", to_dev_bf16(w))
 
 
-@pytest.mark.parametrize("N,K", [(1, 256), (7, 512), (300, 4096), (5, 14336)])
+@pytest.mark.parametrize("N,K", [(1, 256), (7, 512), (300, 4096), (5, 14336), (3, 5120), (2, 16384), (3, 16640),
+                                 (2, 24576)])
 def test_isq_fp8_bit_exact(N, K):
+    """Row lengths on every register-tile size of the workgroup-per-row
+    kernel (K <= 16384) and on the long-row kernel beyond."""
     w = synth.weights_bf16(10000 + K + N, N, K, outliers=True)
+    got = _isq(w).cpu().numpy()
+    want = oracle.pack_fp8(oracle.quantize_fp8(w))
+    assert np.array_equal(got, want)
+
+
+def _e4m3_midpoints():
+    vals = np.array(sorted({oracle.e4m3_value(c) for c in range(0x7F)}), np.float64)
+    return (vals[:-1] + vals[1:]) / 2
+
+
+@pytest.mark.parametrize("s", [1.0, 3.0, 7.0, 0.75])
+def test_isq_fp8_ties_and_near_ties(s):
+    """Rows whose quotients x / s fall exactly on E4M3 rounding midpoints
+    (ties to even) or one bf16 step beside them, with s = max|x| / 448 exact:
+    the kernel rounds x * (1/s) and must take the quotient wherever the two
+    could round differently (for s = 3, x * (1/s) lands just above many
+    midpoints that x / s hits exactly)."""
+    mids = _e4m3_midpoints() * s
+    x = mids.astype(np.float32)
+    x = x[synth.bf16_bits_to_f32(synth.bf16_bits_from_f32(x)) == x]   # exactly representable in bf16
+    b = synth.bf16_bits_from_f32(x)
+    near = np.concatenate([b, b + 1, b - 1]).astype(np.uint16)        # the bf16 neighbours too
+    vals = np.concatenate([near, near ^ 0x8000])                      # both signs
+    K = (vals.size + 1 + 255) // 256 * 256
+    row = np.zeros(K, np.uint16)
+    row[: vals.size] = vals
+    row[vals.size] = synth.bf16_bits_from_f32(np.array([448.0 * s], np.float32))[0]  # the row maximum: s exact
+    assert synth.bf16_bits_to_f32(row[vals.size]) == np.float32(448.0 * s)
+    w = np.stack([row, np.roll(row, 7)])
     got = _isq(w).cpu().numpy()
     want = oracle.pack_fp8(oracle.quantize_fp8(w))
     assert np.array_equal(got, want)
@@ -117,3 +149,27 @@ def test_fp8_w8a8_prefill_shape_sampled():
     fx = oracle.quantize_fp8(x[rows_x])
     Yr, den = oracle.matmul_fp8(fx, fw, inv_x, inv_w)
     check_outputs(Y[mi, ni], Yr, den, "fp8 w8a8 prefill sampled")
+
+
+@pytest.mark.parametrize("M,N,K", [(2125, 7300, 512), (2304, 7169, 256)])
+def test_fp8_w8a8_large_tiles_ragged(M, N, K):
+    """Shapes with at least 256 tiles of 256 x 256 take the eight-wave
+    kernel: ragged M and N (partial last tiles), K of 8 and 4 steps (the
+    latter exactly the ring depth); sampled outputs cover every edge."""
+    w = synth.weights_bf16(10500 + K, N, K, outliers=True)
+    x = synth.activations_bf16(10501 + K, M, K)
+    b = _isq(w)
+    ws = torch.empty(ql.workspace_bytes("fp8", "mfma_fp8", M, K), dtype=torch.uint8, device="cuda")
+    Y = ql.qmatmul("fp8", b, to_dev_bf16(x), N, path="mfma_fp8", workspace=ws).cpu().numpy()
+    rng = np.random.default_rng(10502 + K)
+    edge_m = [0, 255, 256, M - 1, M - 2, min((M // 256) * 256, M - 1)]
+    edge_n = [0, 255, 256, N - 1, N - 2, min((N // 256) * 256, N - 1)]
+    mi = np.concatenate([rng.integers(0, M, 3000), np.repeat(edge_m, len(edge_n))])
+    ni = np.concatenate([rng.integers(0, N, 3000), np.tile(edge_n, len(edge_m))])
+    rows_w, inv_w = np.unique(ni, return_inverse=True)
+    rows_x, inv_x = np.unique(mi, return_inverse=True)
+    fw = oracle.quantize_fp8(w[rows_w])
+    fx = oracle.quantize_fp8(x[rows_x])
+    Yr, den = oracle.matmul_fp8(fx, fw, inv_x, inv_w)
+    check_outputs(Y[mi, ni], Yr, den, f"fp8 w8a8 large tiles M={M} N={N} K={K}")
+    assert np.isfinite(Y).all()
