@@ -1202,19 +1202,29 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(const uint8_t *__restrict
     }
     if (n >= N)
         return;
+    // every output formed before the first store (the scales load
+    // unconditionally, clamped; the empty asm keeps the products out of the
+    // guarded stores, where each would wait for all earlier memory traffic)
     const float sw = ws[n];
     const bool split = gridDim.z > 1;
+    float v[TM][4];
+#pragma unroll
+    for (int j = 0; j < TM; j++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            v[j][i] = acc[j][i] * (xs[min(m0 + 16 * j + 4 * g + i, M - 1)] * sw);
+            asm volatile("" ::"v"(v[j][i]));
+        }
 #pragma unroll
     for (int j = 0; j < TM; j++)
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int m = m0 + 16 * j + 4 * g + i;
             if (m < M) {
-                const float v = acc[j][i] * (xs[m] * sw);
                 if (split)
-                    atomicAdd(Y + (int64_t)m * N + n, v);
+                    atomicAdd(Y + (int64_t)m * N + n, v[j][i]);
                 else
-                    Y[(int64_t)m * N + n] = v;
+                    Y[(int64_t)m * N + n] = v[j][i];
             }
         }
 }
