@@ -1441,11 +1441,13 @@ hipError_t go_fp8_tile(const uint8_t *wblocks, const float *ws, const uint8_t *x
 //     Codes: 16-byte chunk c of row r at slot 2r + (c ^ ((r >> 3) & 1)), so
 //     the 16 rows a ds_read_b128 phase touches land on distinct banks.
 //   * Per 32 x 32 tile: v_mfma_i32_32x32x32_i8 forms the exact integer dot
-//     products P[n][m] of the block; v_mfma_f32_32x32x8_f16 with d_w in
-//     k-slot 0 of A and d_x in k-slot 0 of B forms the outer product
-//     d_w[n] d_x[m] in the same output layout -- exact, since a product of
-//     two fp16 values fits binary32 -- and each output then costs one
-//     conversion and one fused multiply-add: acc += float(P) * (d_w d_x).
+//     products P[m][n] of the block (X codes the A operand, W codes the B
+//     operand); v_mfma_f32_32x32x8_f16 with d_x in k-slot 0 of A and d_w in
+//     k-slot 0 of B forms the outer product d_x[m] d_w[n] in the same output
+//     layout -- exact, since a product of two fp16 values fits binary32 --
+//     and each output then costs one conversion and one fused multiply-add:
+//     acc += float(P) * (d_x d_w).  The 32 lanes of an output row hold 32
+//     consecutive n, so stores and atomics are 128-byte rows.
 //   * K splits add into a zeroed Y with fp32 atomics.
 // ---------------------------------------------------------------------------
 constexpr int BN = 128;     // n tile
@@ -1538,7 +1540,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     auto products = [&]() {
 #pragma unroll
         for (int t = 0; t < 4; t++)
-            P[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[t >> 1], x[t & 1], izero, 0, 0, 0);
+            P[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(x[t & 1], a[t >> 1], izero, 0, 0, 0);
     };
 
     for (int kt = kt0; kt < kt0 + INS - 1 && kt < kt1; kt++)
@@ -1576,11 +1578,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if constexpr (MORE)
             reads(kt + 1);
         f32x16_t S[2];
-        S[0] = __builtin_amdgcn_mfma_f32_32x32x8f16(as[0], xs[0], fzero, 0, 0, 0);
+        S[0] = __builtin_amdgcn_mfma_f32_32x32x8f16(xs[0], as[0], fzero, 0, 0, 0);
 #pragma unroll
         for (int t = 0; t < 4; t++) {
             if (t + 1 < 4)
-                S[(t + 1) & 1] = __builtin_amdgcn_mfma_f32_32x32x8f16(as[(t + 1) >> 1], xs[(t + 1) & 1], fzero, 0, 0, 0);
+                S[(t + 1) & 1] = __builtin_amdgcn_mfma_f32_32x32x8f16(xs[(t + 1) & 1], as[(t + 1) >> 1], fzero, 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int r = 0; r < 16; r++)
@@ -1600,35 +1602,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         step(kt, std::true_type{});
     step(kt1 - 1, std::false_type{});
 
-    // acc[i][j][4g+e] = D[n = 8g + 4*(lane/32) + e][m = lane%32] of its 32 x 32 tile
+    // X is the A operand and W the B operand of both products, so
+    // acc[i][j][r] = D[m = 8 (r / 4) + 4 (lane / 32) + r % 4][n = lane % 32]
+    // of tile (W part i, X part j): the 32 lanes of a row write 128
+    // consecutive bytes (plain stores, or fp32 atomics for K splits)
     const bool atomic = gridDim.z > 1;
-    const bool vec4 = (N & 3) == 0;
 #pragma unroll
-    for (int i = 0; i < 2; i++)
+    for (int i = 0; i < 2; i++) {
+        const int n = n0 + wn * 64 + 32 * i + r32;
+        if (n >= N)
+            continue;
 #pragma unroll
-        for (int j = 0; j < 2; j++) {
-            const int m = m0 + wm * 64 + 32 * j + r32;
-            if (m >= M)
-                continue;
+        for (int j = 0; j < 2; j++)
 #pragma unroll
-            for (int g = 0; g < 4; g++) {
-                const int64_t n = n0 + wn * 64 + 32 * i + 8 * g + 4 * kh;
-                float *y = Y + (int64_t)m * N + n;
-                if (!atomic && vec4 && n + 3 < N) {
-                    *reinterpret_cast<f32x4_t *>(y) =
-                        f32x4_t{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; e++)
-                        if (n + e < N) {
-                            if (atomic)
-                                atomicAdd(y + e, acc[i][j][4 * g + e]);
-                            else
-                                y[e] = acc[i][j][4 * g + e];
-                        }
+            for (int r = 0; r < 16; r++) {
+                const int m = m0 + wm * 64 + 32 * j + 8 * (r >> 2) + 4 * kh + (r & 3);
+                if (m < M) {
+                    if (atomic)
+                        atomicAdd(Y + (int64_t)m * N + n, acc[i][j][r]);
+                    else
+                        Y[(int64_t)m * N + n] = acc[i][j][r];
                 }
             }
-        }
+    }
 }
 
 // Zero-fill of Y before a split-K accumulation (a kernel, not a memset, so
@@ -1962,7 +1958,11 @@ hipError_t launch_gemm_i8(const uint8_t *wblocks, const uint8_t *xblocks, float 
     const Planes pw = planes_of(FMT_Q8_0, N, K), px = planes_of(FMT_Q8_0, M, K);
     const int64_t gx = (N + BN - 1) / BN, gy = (M + IBM - 1) / IBM;
     const int nkt = (int)(K / BK);
-    const int splits = splits_for(gx * gy, nkt);
+    // K splits only while the workgroups still fit one round (two per CU):
+    // 448 tiles at 512 x 14336 ran 158 us split in two, 138 us whole
+    int splits = 1;
+    while (gx * gy * 2 * splits <= 512 && splits < 16 && nkt / (2 * splits) >= 2)
+        splits *= 2;
     const int per = (nkt + splits - 1) / splits;
     if (splits > 1) {
         const hipError_t e = zero_y(Y, M * N, s);
