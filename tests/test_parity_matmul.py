@@ -162,9 +162,12 @@ def test_mfma_bf16_shapes(fmt):
 
 @pytest.mark.parametrize("fmt", FMTS)
 def test_mfma_bf16_prefill_tiles(fmt):
-    """Large-M path (256 x 256 tiles, split over K when the tiles are few):
-    ragged M and N around the tile edges, K with one, two and eight splits."""
-    for M, N, K in ((128, 255, 256), (257, 513, 1024), (600, 300, 4096), (300, 1, 768), (129, 1000, 4096)):
+    """Large-M paths: 65..512 tokens on 128 x 256 tiles and from 513 tokens
+    on 256 x 256 tiles, each split over K when the tiles are few; ragged M
+    and N around the tile edges, K with one, two and eight splits."""
+    for M, N, K in ((128, 255, 256), (257, 513, 1024), (600, 300, 4096), (300, 1, 768), (129, 1000, 4096),
+                    (65, 257, 512), (512, 300, 1024), (513, 255, 256), (777, 513, 1024), (1100, 1, 768),
+                    (2049, 130, 512)):
         w = synth.weights_bf16(5100 + N + K, N, K, outliers=True)
         x = synth.activations_bf16(5101 + M, M, K)
         Yr, den = a16_ref(fmt, w, x)
@@ -386,8 +389,9 @@ def test_graph_replays_match_eager():
     cases = [("q4k", "gemv", 1, 4096, 4096, True),
              ("q6k", "gemv", 2, 300, 1024, True),
              ("q4k", "mfma_bf16", 16, 4100, 4352, False),   # batched stream, split K
-             ("q8_0", "mfma_bf16", 128, 255, 4096, False),  # prefill tiles, split K
-             ("q8_0", "mfma_bf16", 512, 1024, 512, True),   # prefill tiles, no split
+             ("q8_0", "mfma_bf16", 128, 255, 4096, False),  # 128 x 256 tiles, split K
+             ("q8_0", "mfma_bf16", 640, 255, 4096, False),  # prefill tiles, split K
+             ("q8_0", "mfma_bf16", 1024, 1024, 512, True),  # prefill tiles, no split
              ("q8_0", "mfma_i8", 64, 300, 1024, False)]
     bufs = []
     for i, (fmt, path, M, N, K, exact) in enumerate(cases):
