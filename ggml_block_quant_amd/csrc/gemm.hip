@@ -1165,71 +1165,9 @@ __global__ __launch_bounds__(256) void gemm_gen_kernel(const uint8_t *__restrict
         }
 }
 
-// ---------------------------------------------------------------------------
-// FP8 W8A8 (dynamic per-token activation scales, per-channel weight scales):
-// both operands are E4M3 codes (X quantized per row into the workspace by
-// the same quantizer as the weights); a workgroup of four waves owns 64 rows
-// of W and 16*TM tokens, and lane (g, r) feeds 8 codes of W row r and of X
-// row r (k = 8g..8g+7 of a 32-wide step) straight into
-// v_mfma_f32_16x16x32_fp8_fp8 -- exact products, fp32 sums; the scales
-// multiply the finished sums.  K splits add into a zeroed Y.
-// ---------------------------------------------------------------------------
-template <int TM>
-__global__ __launch_bounds__(256) void gemm_fp8_kernel(const uint8_t *__restrict__ Wq, const float *__restrict__ ws,
-                                                       const uint8_t *__restrict__ Xq, const float *__restrict__ xs,
-                                                       float *__restrict__ Y, int M, int N, int K, int steps_per_split)
-{
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int g = lane >> 4, r16 = lane & 15;
-    const int n = blockIdx.x * 64 + 16 * wv + r16;
-    const uint8_t *wr = Wq + (int64_t)min(n, N - 1) * K;
-    const int m0 = blockIdx.y * 16 * TM;
-    const int s0 = blockIdx.z * steps_per_split, s1 = min(K / 32, s0 + steps_per_split);
-    f32x4_t acc[TM];
-    const uint8_t *xr[TM];
-#pragma unroll
-    for (int j = 0; j < TM; j++) {
-        acc[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        xr[j] = Xq + (int64_t)min(m0 + 16 * j + r16, M - 1) * K;
-    }
-    for (int s = s0; s < s1; s++) {
-        const long b = *reinterpret_cast<const long *>(wr + 32 * s + 8 * g);
-#pragma unroll
-        for (int j = 0; j < TM; j++) {
-            const long a = *reinterpret_cast<const long *>(xr[j] + 32 * s + 8 * g);
-            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, acc[j], 0, 0, 0);
-        }
-    }
-    if (n >= N)
-        return;
-    // every output formed before the first store (the scales load
-    // unconditionally, clamped; the empty asm keeps the products out of the
-    // guarded stores, where each would wait for all earlier memory traffic)
-    const float sw = ws[n];
-    const bool split = gridDim.z > 1;
-    float v[TM][4];
-#pragma unroll
-    for (int j = 0; j < TM; j++)
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            v[j][i] = acc[j][i] * (xs[min(m0 + 16 * j + 4 * g + i, M - 1)] * sw);
-            asm volatile("" ::"v"(v[j][i]));
-        }
-#pragma unroll
-    for (int j = 0; j < TM; j++)
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int m = m0 + 16 * j + 4 * g + i;
-            if (m < M) {
-                if (split)
-                    atomicAdd(Y + (int64_t)m * N + n, v[j][i]);
-                else
-                    Y[(int64_t)m * N + n] = v[j][i];
-            }
-        }
-}
-
-// Large-M FP8 W8A8 (prefill): a workgroup of WMW x WNW waves owns an output
+// FP8 W8A8 (dynamic per-token activation scales, per-channel weight scales;
+// X quantized per row into the workspace by the same quantizer as the
+// weights): a workgroup of WMW x WNW waves owns an output
 // tile of TM = 32 TI WMW tokens by TN = 32 TJ WNW rows of W; wave (wm, wn)
 // owns TI x TJ tiles of 32 x 32.  K advances in steps of 64 codes, one
 // v_mfma_f32_32x32x64_f8f6f4 per tile and step (E4M3 operands, unit block
@@ -1246,6 +1184,7 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(const uint8_t *__restrict
 // banks.  Step kt + 1's operands are read while step kt's products run.
 constexpr int F8K = 64;  // k per step
 constexpr int F8S = 4;   // ring stages
+constexpr int F8MINSPLIT = 16;  // fewest K steps (of 64 codes) per split
 
 // s_waitcnt immediate: vmcnt n (bits 3:0 and 15:14), lgkmcnt 0, expcnt any
 constexpr int vm_wait(int n) { return 0x0070 | (n & 15) | ((n >> 4) << 14); }
@@ -1265,7 +1204,7 @@ struct F8Tile {
 template <int WMW, int WNW, int TI, int TJ>
 __global__ __launch_bounds__(64 * WMW * WNW) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_fp8_tile_kernel(
     const uint8_t *__restrict__ Wq, const float *__restrict__ ws, const uint8_t *__restrict__ Xq,
-    const float *__restrict__ xs, float *__restrict__ Y, int M, int N, int K)
+    const float *__restrict__ xs, float *__restrict__ Y, int M, int N, int K, int steps_per_split)
 {
     using T = F8Tile<WMW, WNW, TI, TJ>;
     constexpr int LX = T::LX, LW = T::LW, NL = LX + LW;
@@ -1274,7 +1213,11 @@ __global__ __launch_bounds__(64 * WMW * WNW) __attribute__((amdgpu_waves_per_eu(
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wv / WNW, wn = wv % WNW;
     const int m0 = blockIdx.y * T::TM, n0 = blockIdx.x * T::TN;
-    const int nk = K / F8K;
+    // this workgroup's K steps: [kb, kb + nk) of K / F8K (gridDim.z splits)
+    const int kb = blockIdx.z * steps_per_split;
+    const int nk = min(K / F8K - kb, steps_per_split);
+    if (nk <= 0)
+        return;  // an empty split (the whole workgroup): adds nothing
 
     // direct loads: instruction j of wave w fills slots 64 (L w + j) + lane
     // of the X (L = LX) or the W (L = LW) region; rows past M / N re-read the
@@ -1292,8 +1235,8 @@ __global__ __launch_bounds__(64 * WMW * WNW) __attribute__((amdgpu_waves_per_eu(
         const int c = (sl & 3) ^ (((r >> 1) ^ (r >> 2)) & 3);
         ow[j] = (uint32_t)((min(n0 + r, N - 1) - n0) * K + 16 * c);
     }
-    const uint8_t *const xbase = Xq + (int64_t)m0 * K;
-    const uint8_t *const wbase = Wq + (int64_t)n0 * K;
+    const uint8_t *const xbase = Xq + (int64_t)m0 * K + F8K * kb;
+    const uint8_t *const wbase = Wq + (int64_t)n0 * K + F8K * kb;
     auto issue = [&](int kt) {
         const uint32_t st = lds_addr(smem + (kt % F8S) * T::STG);
 #pragma unroll
@@ -1398,8 +1341,8 @@ __global__ __launch_bounds__(64 * WMW * WNW) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
     for (int j = 0; j < TJ; j++)
         swn[j] = ws[min(n0 + 32 * (TJ * wn + j) + r32, N - 1)];
-    auto store = [&](auto guard_t) {
-        constexpr bool GUARD = decltype(guard_t)::value;
+    auto store = [&](auto guard_t, auto atomic_t) {
+        constexpr bool GUARD = decltype(guard_t)::value, ATOMIC = decltype(atomic_t)::value;
 #pragma unroll
         for (int j = 0; j < TJ; j++) {
             const int n = n0 + 32 * (TJ * wn + j) + r32;
@@ -1408,25 +1351,54 @@ __global__ __launch_bounds__(64 * WMW * WNW) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
                 for (int r = 0; r < 16; r++) {
                     const int m = m0 + 32 * (TI * wm + i) + 8 * (r >> 2) + 4 * h + (r & 3);
-                    if (!GUARD || (m < M && n < N))
-                        Y[(int64_t)m * N + n] = acc[i][j][r] * (sx[i][r] * swn[j]);
+                    if (!GUARD || (m < M && n < N)) {
+                        const float v = acc[i][j][r] * (sx[i][r] * swn[j]);
+                        if constexpr (ATOMIC)
+                            atomicAdd(Y + (int64_t)m * N + n, v);
+                        else
+                            Y[(int64_t)m * N + n] = v;
+                    }
                 }
         }
     };
-    if (m0 + T::TM <= M && n0 + T::TN <= N)
-        store(std::false_type{});
-    else
-        store(std::true_type{});
+    // K splits add their partial tiles into a zeroed Y: each product of the
+    // scales is formed the same way in every split, so the result differs
+    // from the unsplit one only in the order of the fp32 additions
+    const bool whole = m0 + T::TM <= M && n0 + T::TN <= N;
+    if (gridDim.z > 1) {
+        if (whole)
+            store(std::false_type{}, std::true_type{});
+        else
+            store(std::true_type{}, std::true_type{});
+    } else if (whole) {
+        store(std::false_type{}, std::false_type{});
+    } else {
+        store(std::true_type{}, std::false_type{});
+    }
 }
 
+hipError_t zero_y(float *Y, int64_t count, hipStream_t s);
+
+// `slots`: workgroups that run at once (CUs x workgroups per CU); K splits
+// (fp32 atomics into a zeroed Y) while the split tiles still fit them
 template <int WMW, int WNW, int TI, int TJ>
 hipError_t go_fp8_tile(const uint8_t *wblocks, const float *ws, const uint8_t *xblocks, const float *xs, float *Y,
-                       int64_t M, int64_t N, int64_t K, hipStream_t s)
+                       int64_t M, int64_t N, int64_t K, hipStream_t s, int64_t slots)
 {
     using T = F8Tile<WMW, WNW, TI, TJ>;
-    hipLaunchKernelGGL((gemm_fp8_tile_kernel<WMW, WNW, TI, TJ>),
-                       dim3((unsigned)((N + T::TN - 1) / T::TN), (unsigned)((M + T::TM - 1) / T::TM)),
-                       dim3(64 * T::W), 0, s, wblocks, ws, xblocks, xs, Y, (int)M, (int)N, (int)K);
+    const int64_t gx = (N + T::TN - 1) / T::TN, gy = (M + T::TM - 1) / T::TM;
+    const int steps = (int)(K / F8K);
+    int splits = 1;
+    while (gx * gy * splits * 2 <= slots && splits < 16 && steps / (2 * splits) >= F8MINSPLIT)
+        splits *= 2;
+    const int per = (steps + splits - 1) / splits;
+    if (splits > 1) {
+        const hipError_t e = zero_y(Y, M * N, s);
+        if (e != hipSuccess)
+            return e;
+    }
+    hipLaunchKernelGGL((gemm_fp8_tile_kernel<WMW, WNW, TI, TJ>), dim3((unsigned)gx, (unsigned)gy, (unsigned)splits),
+                       dim3(64 * T::W), 0, s, wblocks, ws, xblocks, xs, Y, (int)M, (int)N, (int)K, per);
     return hipGetLastError();
 }
 
@@ -1880,26 +1852,6 @@ hipError_t launch_gemm_gen(int fmt, const uint8_t *blocks, const uint16_t *X, fl
     }
 }
 
-template <int TM>
-hipError_t go_fp8(const uint8_t *wb, const uint8_t *xb, float *Y, int64_t M, int64_t N, int64_t K, hipStream_t s)
-{
-    const Planes pw = planes_of(FMT_FP8, N, K), px = planes_of(FMT_FP8, M, K);
-    const int64_t gx = (N + 63) / 64, gy = (M + 16 * TM - 1) / (16 * TM);
-    const int steps = (int)(K / 32);
-    int sp = 1;
-    while (gx * gy * sp < 512 && sp < 32 && steps / (2 * sp) >= 8)
-        sp *= 2;
-    const int per = (steps + sp - 1) / sp;
-    if (sp > 1) {
-        const hipError_t e = zero_y(Y, M * N, s);
-        if (e != hipSuccess)
-            return e;
-    }
-    hipLaunchKernelGGL((gemm_fp8_kernel<TM>), dim3((unsigned)gx, (unsigned)gy, (unsigned)sp), dim3(256), 0, s, wb,
-                       reinterpret_cast<const float *>(wb + pw.scales), xb,
-                       reinterpret_cast<const float *>(xb + px.scales), Y, (int)M, (int)N, (int)K, per);
-    return hipGetLastError();
-}
 }  // namespace
 
 hipError_t launch_gemm_bf16(int fmt, const uint8_t *blocks, const uint16_t *X, float *Y, int64_t M,
@@ -1941,21 +1893,19 @@ hipError_t launch_glu_apply(const float *G, float *H, int64_t n, int act, hipStr
 hipError_t launch_gemm_fp8(const uint8_t *wblocks, const uint8_t *xblocks, float *Y, int64_t M, int64_t N,
                            int64_t K, hipStream_t s)
 {
-    if (M >= 128) {
-        const Planes pw = planes_of(FMT_FP8, N, K), px = planes_of(FMT_FP8, M, K);
-        const float *ws = reinterpret_cast<const float *>(wblocks + pw.scales);
-        const float *xs = reinterpret_cast<const float *>(xblocks + px.scales);
-        // 256 x 256 tiles (eight waves) move half the bytes per product of the
-        // 128 x 128 ones, where there are enough of them for every CU
-        if (((M + 255) / 256) * ((N + 255) / 256) >= 256)
-            return go_fp8_tile<4, 2, 2, 4>(wblocks, ws, xblocks, xs, Y, M, N, K, s);
-        return go_fp8_tile<2, 2, 2, 2>(wblocks, ws, xblocks, xs, Y, M, N, K, s);
-    }
-    if (M <= 16)
-        return go_fp8<1>(wblocks, xblocks, Y, M, N, K, s);
-    if (M <= 32)
-        return go_fp8<2>(wblocks, xblocks, Y, M, N, K, s);
-    return go_fp8<4>(wblocks, xblocks, Y, M, N, K, s);
+    const Planes pw = planes_of(FMT_FP8, N, K), px = planes_of(FMT_FP8, M, K);
+    const float *ws = reinterpret_cast<const float *>(wblocks + pw.scales);
+    const float *xs = reinterpret_cast<const float *>(xblocks + px.scales);
+    // 256 x 256 tiles (eight waves) move half the bytes per product of the
+    // 128 x 128 ones, where there are enough of them for every CU; fewer
+    // tiles split K up to one workgroup per CU with at least 16 steps each
+    // (measured over 1..512 tokens at 14336 x 4096, 4096 x 14336 and
+    // 4096 x 4096: 448 split workgroups of 256 tokens ran 50 us against 35
+    // whole, while one token over 32 tiles ran 21 us split eight ways and 43
+    // split two ways)
+    if (((M + 255) / 256) * ((N + 255) / 256) >= 256)
+        return go_fp8_tile<4, 2, 2, 4>(wblocks, ws, xblocks, xs, Y, M, N, K, s, 256);
+    return go_fp8_tile<2, 2, 2, 2>(wblocks, ws, xblocks, xs, Y, M, N, K, s, 256);
 }
 
 hipError_t launch_gemm_i8(const uint8_t *wblocks, const uint8_t *xblocks, float *Y, int64_t M, int64_t N,
