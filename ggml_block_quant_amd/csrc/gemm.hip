@@ -1077,6 +1077,122 @@ __global__ __launch_bounds__(320) void gemm_bq_kernel(const uint8_t *__restrict_
 }
 
 // ---------------------------------------------------------------------------
+// Generic MFMA GEMM for many tokens (the formats without a tuned kernel): the
+// structure of gemm_bf16_kernel -- X slabs of 128 staged in LDS once per
+// workgroup and shared by its four waves, 16 TM tokens and 64 NT rows of W
+// per workgroup -- with the weights decoded by the shared exact decoder
+// (dequant8) straight from the blocks: lane (g, r) decodes block 4s + g of
+// its rows in slab s, rounds it to bf16 and feeds four
+// v_mfma_f32_16x16x32_bf16 steps.  Each weight is decoded once per 16 TM
+// tokens instead of once per 64.
+// ---------------------------------------------------------------------------
+template <int FMT, int TM, int NT>
+__global__ __launch_bounds__(256) void gemm_gen_lds_kernel(const uint8_t *__restrict__ B, Planes p,
+                                                           const uint16_t *__restrict__ X, float *__restrict__ Y,
+                                                           int M, int N, int K, int slabs_per_split)
+{
+    constexpr int BM = 16 * TM;
+    constexpr int XPER = BM * SLAB * 2 / 16;  // uint4 of X per slab
+    constexpr int XU4 = XPER / 256;           // per thread
+    static_assert(XU4 * 256 == XPER, "X staging");
+    __shared__ __attribute__((aligned(16))) uint8_t sX[2][BM * XPITCH];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, r16 = lane & 15;
+    const int64_t n_wave = (int64_t)blockIdx.x * (64 * NT) + wave * 16 * NT;
+    const int m0 = blockIdx.y * BM;
+    const int nslab = K / SLAB;
+    const int s0 = blockIdx.z * slabs_per_split;
+    const int s1 = min(nslab, s0 + slabs_per_split);
+    if (s0 >= s1)
+        return;
+    int64_t wpiece[NT];  // first 8-element piece of this lane's rows (clamped: rows past N are not stored)
+#pragma unroll
+    for (int i = 0; i < NT; i++)
+        wpiece[i] = min(n_wave + 16 * i + r16, (int64_t)N - 1) * (K / 8);
+
+    auto load_x = [&](int s, uint4 (&xr)[XU4]) {
+#pragma unroll
+        for (int t = 0; t < XU4; t++) {
+            const int i = tid + 256 * t;
+            const int row = i / (SLAB / 8), q = i % (SLAB / 8);
+            xr[t] = m0 + row < M ? *reinterpret_cast<const uint4 *>(X + (int64_t)(m0 + row) * K + s * SLAB + 8 * q)
+                                 : make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
+    auto store_x = [&](int buf, const uint4 (&xr)[XU4]) {
+#pragma unroll
+        for (int t = 0; t < XU4; t++) {
+            const int i = tid + 256 * t;
+            const int row = i / (SLAB / 8), q = i % (SLAB / 8);
+            *reinterpret_cast<uint4 *>(&sX[buf][row * XPITCH + 16 * q]) = xr[t];
+        }
+    };
+
+    f32x4_t acc[NT][TM];
+#pragma unroll
+    for (int i = 0; i < NT; i++)
+#pragma unroll
+        for (int j = 0; j < TM; j++)
+            acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    uint4 x1[XU4];
+    load_x(s0, x1);
+    store_x(0, x1);
+    if (s0 + 1 < s1)
+        load_x(s0 + 1, x1);
+    lds_barrier();
+    for (int s = s0; s < s1; s++) {
+        const int buf = (s - s0) & 1;
+#pragma unroll
+        for (int i = 0; i < NT; i++) {
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                float w[8];
+                dequant8<FMT>(B, p, wpiece[i] + 16 * s + 4 * g + t, w);
+                const bf16x8_t bw = __builtin_bit_cast(
+                    bf16x8_t, make_uint4(pack_bf16(w[0], w[1]), pack_bf16(w[2], w[3]), pack_bf16(w[4], w[5]),
+                                         pack_bf16(w[6], w[7])));
+#pragma unroll
+                for (int j = 0; j < TM; j++) {
+                    const bf16x8_t xa = *reinterpret_cast<const bf16x8_t *>(
+                        &sX[buf][(16 * j + r16) * XPITCH + 64 * g + 16 * t]);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bw, acc[i][j], 0, 0, 0);
+                }
+            }
+        }
+        if (s + 1 < s1) {
+            store_x(buf ^ 1, x1);
+            if (s + 2 < s1)
+                load_x(s + 2, x1);
+        }
+        lds_barrier();
+    }
+
+    // lane holds D[m = 4*g + r][n = r16] of each 16 x 16 tile
+    const bool atomic = gridDim.z > 1;
+#pragma unroll
+    for (int i = 0; i < NT; i++) {
+        const int64_t n = n_wave + 16 * i + r16;
+        if (n >= N)
+            continue;
+#pragma unroll
+        for (int j = 0; j < TM; j++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int m = m0 + 16 * j + 4 * g + r;
+                if (m < M) {
+                    float *y = Y + (int64_t)m * N + n;
+                    if (atomic)
+                        atomicAdd(y, acc[i][j][r]);
+                    else
+                        *y = acc[i][j][r];
+                }
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Generic MFMA GEMM for the formats without a tuned kernel: a workgroup of
 // four waves owns 64 rows of W (16 per wave) and 16*TM tokens; K advances in
 // steps of 32.  Lane (g = l/16, r = l%16) decodes elements 8g..8g+7 of the
@@ -1826,9 +1942,37 @@ hipError_t go_gen(const uint8_t *blocks, const uint16_t *X, float *Y, int64_t M,
     return hipGetLastError();
 }
 
+// tokens above which the generic formats take the LDS-staged kernel, and its tile
+constexpr int GEN_LDS_MIN_M = 64, GTM = 8, GNT = 2;
+
+template <int FMT>
+hipError_t go_gen_lds(const uint8_t *blocks, const uint16_t *X, float *Y, int64_t M, int64_t N, int64_t K,
+                      hipStream_t s)
+{
+    const Planes p = planes_of(FMT, N, K);
+    const int64_t gx = (N + 64 * GNT - 1) / (64 * GNT), gy = (M + 16 * GTM - 1) / (16 * GTM);
+    const int nslab = (int)(K / SLAB);
+    int splits = 1;
+    while (gx * gy * splits * 2 <= 256 && splits < 32 && nslab / (2 * splits) >= 2)
+        splits *= 2;
+    const int per = (nslab + splits - 1) / splits;
+    if (splits > 1) {
+        const hipError_t e = zero_y(Y, M * N, s);
+        if (e != hipSuccess)
+            return e;
+    }
+    hipLaunchKernelGGL((gemm_gen_lds_kernel<FMT, GTM, GNT>), dim3((unsigned)gx, (unsigned)gy, (unsigned)splits),
+                       dim3(256), 0, s, blocks, p, X, Y, (int)M, (int)N, (int)K, per);
+    return hipGetLastError();
+}
+
 template <int FMT>
 hipError_t gen_tm(const uint8_t *blocks, const uint16_t *X, float *Y, int64_t M, int64_t N, int64_t K, hipStream_t s)
 {
+    // (Q8_0 here serves block tails, whose remainder operand only the
+    // per-step kernel carries)
+    if (FMT != FMT_Q8_0 && M > GEN_LDS_MIN_M && K % SLAB == 0)
+        return go_gen_lds<FMT>(blocks, X, Y, M, N, K, s);
     if (M <= 16)
         return go_gen<FMT, 1>(blocks, X, Y, M, N, K, s);
     if (M <= 32)
