@@ -134,8 +134,10 @@ int qmatmul_ex(int fmt, const void *blocks, const void *X_bf16, float *Y_fp32, i
     switch (path) {
     case QPATH_AUTO:
         // measured crossover on MI355X: the fused GEMV wins for one or two
-        // tokens; from three tokens the MFMA weight stream is faster
-        if (M <= 2) {
+        // tokens; from three tokens the MFMA weight stream is faster -- for
+        // the generic formats, whose MFMA kernel streams the weights less
+        // well, from five (Q5K 14336 x 4096, 3 tokens: 33.6 vs 54.3 us)
+        if (M <= (ql::generic_fmt(fmt) && fmt != QFMT_FP8 ? 4 : 2)) {
             st = gemv(fmt, B, X, Y_fp32, M, N, K, s);
             if (st != Q_ENOTSUP)
                 return st;

@@ -1077,14 +1077,14 @@ __global__ __launch_bounds__(320) void gemm_bq_kernel(const uint8_t *__restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Generic MFMA GEMM for many tokens (the formats without a tuned kernel): the
-// structure of gemm_bf16_kernel -- X slabs of 128 staged in LDS once per
+// Generic MFMA GEMM (the formats without a tuned kernel): the structure of
+// gemm_bf16_kernel -- X slabs of 128 staged in LDS once per
 // workgroup and shared by its four waves, 16 TM tokens and 64 NT rows of W
 // per workgroup -- with the weights decoded by the shared exact decoder
 // (dequant8) straight from the blocks: lane (g, r) decodes block 4s + g of
 // its rows in slab s, rounds it to bf16 and feeds four
 // v_mfma_f32_16x16x32_bf16 steps.  Each weight is decoded once per 16 TM
-// tokens instead of once per 64.
+// tokens, and X is read once per workgroup rather than once per wave.
 // ---------------------------------------------------------------------------
 template <int FMT, int TM, int NT>
 __global__ __launch_bounds__(256) void gemm_gen_lds_kernel(const uint8_t *__restrict__ B, Planes p,
@@ -1193,9 +1193,10 @@ __global__ __launch_bounds__(256) void gemm_gen_lds_kernel(const uint8_t *__rest
 }
 
 // ---------------------------------------------------------------------------
-// Generic MFMA GEMM for the formats without a tuned kernel: a workgroup of
-// four waves owns 64 rows of W (16 per wave) and 16*TM tokens; K advances in
-// steps of 32.  Lane (g = l/16, r = l%16) decodes elements 8g..8g+7 of the
+// Per-step generic MFMA GEMM (Q8_0 rows that end in a tail of blocks, and
+// any row length that is not a whole number of 128-element slabs): a
+// workgroup of four waves owns 64 rows of W (16 per wave) and 16*TM tokens;
+// K advances in steps of 32.  Lane (g = l/16, r = l%16) decodes elements 8g..8g+7 of the
 // step in row r of its wave exactly (dequant8), rounds them to bf16 and uses
 // them as its B operand of v_mfma_f32_16x16x32_bf16; the A operand is the
 // same 8 elements of X read straight from memory.  K splits over gridDim.z
@@ -1942,10 +1943,7 @@ hipError_t go_gen(const uint8_t *blocks, const uint16_t *X, float *Y, int64_t M,
     return hipGetLastError();
 }
 
-// tokens above which the generic formats take the LDS-staged kernel, and its tile
-constexpr int GEN_LDS_MIN_M = 64, GTM = 8, GNT = 2;
-
-template <int FMT>
+template <int FMT, int GTM, int GNT>
 hipError_t go_gen_lds(const uint8_t *blocks, const uint16_t *X, float *Y, int64_t M, int64_t N, int64_t K,
                       hipStream_t s)
 {
@@ -1969,10 +1967,18 @@ hipError_t go_gen_lds(const uint8_t *blocks, const uint16_t *X, float *Y, int64_
 template <int FMT>
 hipError_t gen_tm(const uint8_t *blocks, const uint16_t *X, float *Y, int64_t M, int64_t N, int64_t K, hipStream_t s)
 {
-    // (Q8_0 here serves block tails, whose remainder operand only the
-    // per-step kernel carries)
-    if (FMT != FMT_Q8_0 && M > GEN_LDS_MIN_M && K % SLAB == 0)
-        return go_gen_lds<FMT>(blocks, X, Y, M, N, K, s);
+    // the LDS-staged kernel, tiles of 16..128 tokens by 128..256 rows (Q8_0
+    // here serves block tails, whose remainder operand only the per-step
+    // kernel carries)
+    if (FMT != FMT_Q8_0 && K % SLAB == 0) {
+        if (M <= 16)
+            return go_gen_lds<FMT, 1, 4>(blocks, X, Y, M, N, K, s);
+        if (M <= 32)
+            return go_gen_lds<FMT, 2, 4>(blocks, X, Y, M, N, K, s);
+        if (M <= 64)
+            return go_gen_lds<FMT, 4, 2>(blocks, X, Y, M, N, K, s);
+        return go_gen_lds<FMT, 8, 2>(blocks, X, Y, M, N, K, s);
+    }
     if (M <= 16)
         return go_gen<FMT, 1>(blocks, X, Y, M, N, K, s);
     if (M <= 32)
