@@ -1913,12 +1913,15 @@ hipError_t bf16_by_m(const uint8_t *blocks, const Planes &p, const uint16_t *X, 
         return go_skinny<FMT, 2, 1, 4>(blocks, p, X, Y, M, N, K, s);
     if (M <= 64)
         return go_bf16<FMT, 4, 2>(blocks, p, X, Y, M, N, K, s, 256);
-    if (M >= PF_MIN_M)
+    // the prefill kernel from 513 tokens, and from 256 where its 256 x 256
+    // tiles number at least 200 (wide weights: the 131072 x 5120 head at 256
+    // tokens ran 510 us there against 692 us on the tiles below)
+    if (M >= PF_MIN_M || (M >= 256 && ((M + 255) / 256) * ((N + 255) / 256) >= 200))
         return go_pf<FMT>(blocks, p, X, Y, M, N, K, s);
-    // 65..512 tokens: 128 x 256 tiles, K split only as far as the workgroups
-    // stay within one per CU (measured: at 96 tokens 14336 x 4096 ran 94 us
-    // with 16 splits, 44 us with 4; up to 512 tokens this beats the prefill
-    // kernel, e.g. 97.7 vs 115.4 us at 512 x 14336 x 4096)
+    // otherwise 65..512 tokens: 128 x 256 tiles, K split only as far as the
+    // workgroups stay within one per CU (measured: at 96 tokens 14336 x 4096
+    // ran 94 us with 16 splits, 44 us with 4; up to 512 tokens this beats the
+    // prefill kernel there, e.g. 97.7 vs 115.4 us at 512 x 14336 x 4096)
     return go_bf16<FMT, 8, 4>(blocks, p, X, Y, M, N, K, s, 256, true);
 }
 
