@@ -339,6 +339,25 @@ def _sampled(N, M, count, seed):
     return rng.integers(0, M, count), rng.integers(0, N, count)
 
 
+@pytest.mark.parametrize("fmt,M,N,K", [("q4k", 100, 8300, 4096), ("q6k", 300, 8200, 4352), ("q8_0", 257, 9000, 4096)])
+def test_mid_token_counts_wide_weights(fmt, M, N, K):
+    """65..512 tokens on weights above 2^25 elements (128 x 256 tiles, K split
+    as far as one workgroup per CU): ragged M and N, 3000 sampled outputs
+    plus every edge row and column pair."""
+    w = synth.weights_bf16(5600 + M, N, K, outliers=True)
+    x = synth.activations_bf16(5601 + M, M, K)
+    blocks = ql.isq(fmt, to_dev_bf16(w))
+    y = ql.qmatmul(fmt, blocks, to_dev_bf16(x), N).cpu().numpy()
+    mi, ni = _sampled(N, M, 3000, 5602 + M)
+    em, en = [0, min(127, M - 1), min(128, M - 1), M - 1], [0, 255, 256, N - 1]
+    mi = np.concatenate([mi, np.repeat(em, len(en))])
+    ni = np.concatenate([ni, np.tile(en, len(em))])
+    rows, inv = np.unique(ni, return_inverse=True)
+    Wr = oracle.dequant(fmt, oracle.quantize(fmt, w[rows]), len(rows), K)
+    Yr, den = oracle.matmul_a16_pairs(Wr, x, mi, inv)
+    check_outputs(y[mi, ni], Yr, den, f"mid tokens {fmt} M={M} N={N} K={K}")
+
+
 def test_workload_prefill_2048_both_paths():
     """M = 2048 x K = 4096 x N = 14336, Q8_0 weights; the bf16 MFMA path and
     the int8 path, checked on 4096 sampled outputs (rows of W quantized by
