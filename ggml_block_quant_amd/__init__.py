@@ -180,7 +180,7 @@ def act_quantize(X: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tens
 def qmatmul(fmt, blocks: torch.Tensor, X: torch.Tensor, N: int, path="auto",
             out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """Y = X . deq(W)^T as fp32 [M][N] for X bf16 [M][K] and the blocks of a
-    [N][K] weight.  ``path``: auto | gemv | mfma_bf16 | mfma_i8."""
+    [N][K] weight.  ``path``: auto | gemv | mfma_bf16 | mfma_i8 | mfma_fp8."""
     if X.dim() != 2:
         raise ValueError("X must be 2-D [M][K]")
     M, K = X.shape
