@@ -764,25 +764,29 @@ __global__ __launch_bounds__(64 * LW) void gemv_lds_kernel(Geo g, Geo g2, const 
     }
 }
 
+constexpr int64_t GEMV_WIDE_N = 2048;
+
 template <int FMT, int M, int CPT>
 hipError_t go_lds(const Geo &g, const uint16_t *X, float *Y, int64_t N, hipStream_t s)
 {
     // rows per wave from sweeps on MI355X: two for K <= 4096, four for
-    // K = 5120 (the 131072 x 5120 head: 10 % faster than one), one above
-    constexpr int R = M != 1 ? 1 : CPT <= 2 ? 2 : CPT == 3 ? 4 : 1;
+    // K = 5120 (the 131072 x 5120 head: 10 % faster than one), one above;
+    // one for narrow weights (N below GEMV_WIDE_N), whose grid would
+    // otherwise leave CUs idle
+    constexpr int R = CPT <= 2 ? 2 : CPT == 3 ? 4 : 1;
+    if (R > 1 && N < GEMV_WIDE_N) {
+        hipLaunchKernelGGL((gemv_lds_kernel<FMT, M, CPT, 1>), dim3((unsigned)((N + LW - 1) / LW)), dim3(64 * LW), 0, s,
+                           g, g, X, Y, N, 0);
+        return hipGetLastError();
+    }
     const int64_t grid = (N + LW * R - 1) / (LW * R);
-    // one token: the wave's rows as one run (uniform-base loads; no padding
-    // slots where 64 does not divide K/32) where measured faster with weight
-    // copies rotated past the caches: K = 1024 and 5120, and Q6K also at
-    // K = 4096 and 14336 (Q4K and Q8_0 there: 1-4 % slower)
-    constexpr int FSV = M != 1                          ? 0
-                        : CPT == 1                      ? 32
-                        : FMT == FMT_Q8_0               ? 0
-                        : CPT == 3                      ? 160
-                        : FMT == FMT_Q4K                ? 0
-                        : CPT == 2                      ? 128
-                        : CPT == 7                      ? 448
-                                                        : 0;
+    // the wave's rows as one run (uniform-base loads; no padding slots where
+    // 64 does not divide K/32) where measured faster with weight copies
+    // rotated past the caches: K = 1024 and 5120, and Q6K also at K = 4096
+    // and 14336 (Q4K and Q8_0 there: 1-4 % slower); for two tokens too (the
+    // head at two tokens: 149 -> 110 us with four rows per wave as a run)
+    constexpr int FSV = CPT == 1 ? 32 : FMT == FMT_Q8_0 ? 0 : CPT == 3 ? 160 : FMT == FMT_Q4K ? 0 : CPT == 2 ? 128
+                        : CPT == 7 ? 448 : 0;
     if (FSV != 0 && g.K == 32 * FSV && N >= R)
         hipLaunchKernelGGL((gemv_lds_kernel<FMT, M, CPT, R, false, FSV>),
                            dim3((unsigned)grid), dim3(64 * LW), 0, s, g, g, X, Y, N, 0);

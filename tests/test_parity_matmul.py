@@ -81,6 +81,34 @@ def test_gemv_row_runs_one_hot(fmt):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("K", [1024, 4096, 5120, 14336])
+def test_gemv_wide_weights(fmt, K):
+    """From 2048 rows a wave takes two or four rows (as one run of chunks at
+    the widths where that measured faster), for one and two tokens: N =
+    2051 leaves a partial last workgroup; random X within the bar, and
+    one-hot X at the first, a middle and the last element exact."""
+    N = 2051
+    w = synth.weights_bf16(4300 + K, N, K, outliers=True)
+    blocks = ql.isq(fmt, to_dev_bf16(w))
+    Wd = oracle.dequant(fmt, oracle.quantize(fmt, w), N, K)
+    Wf = Wd.astype(np.float32)
+    for M in (1, 2):
+        x = synth.activations_bf16(4301 + M, M, K)
+        Yr, den = oracle.matmul_a16(Wd, x)
+        y = ql.qmatmul(fmt, blocks, to_dev_bf16(x), N, path="gemv").cpu().numpy()
+        check_outputs(y, Yr, den, f"gemv wide {fmt} M={M} K={K}")
+        for k in (0, K // 2 + 5, K - 1):
+            x = np.zeros((M, K), np.uint16)
+            x[0, k] = 0x3F80
+            if M == 2:
+                x[1, (k + 33) % K] = 0x3F80
+            y = ql.qmatmul(fmt, blocks, to_dev_bf16(x), N, path="gemv").cpu().numpy()
+            assert np.array_equal(y[0], Wf[:, k]), f"{fmt} M={M} K={K} k={k}"
+            if M == 2:
+                assert np.array_equal(y[1], Wf[:, (k + 33) % K]), f"{fmt} M=2 K={K} k={k}"
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 def test_gemv_one_hot_is_exact(fmt):
     """X = e_k: the GEMV must return the fp32 value of the dequantized weight
     bit for bit (products with 1 and sums of zeros are exact), for every
