@@ -439,17 +439,20 @@ __global__ __launch_bounds__(512) void gemm_skinny_kernel(const uint8_t *__restr
 
 // ---------------------------------------------------------------------------
 // Prefill dequant-to-bf16 path (large M): output tile 256 (m) x 256 (n) per
-// workgroup of four waves, each wave 128 x 128 = 4 x 4 tiles of
-// v_mfma_f32_32x32x16_bf16 (256 accumulator registers, one wave per SIMD).
-// K advances in slabs of 32 (one Q8_0 block / one K-quant sub-block per row).
+// workgroup of eight waves (two per SIMD), each wave 128 x 64 = 4 x 2 tiles
+// of v_mfma_f32_32x32x16_bf16 (128 accumulator registers).  K advances in
+// slabs of 32 (one Q8_0 block / one K-quant sub-block per row).
 //
 //   * Every global read is a direct global->LDS load (no registers, no LDS
-//     store instruction): the X slab (bf16) into a ring of four stages and
-//     the raw block bytes of the 256 W rows into a ring of three.  The only
-//     waits on them are the explicit vmcnt waits below.
-//   * Thread t decodes row t of the W slab from its raw bytes to bf16 and
-//     stores it into a double-buffered W stage, one slab ahead, while the
-//     wave's first sixteen MFMAs of the current slab run.
+//     store instruction): the X slab (bf16) into a ring of four stages (two
+//     loads per wave) and the raw block bytes of the 256 W rows into a ring
+//     of three (waves 0..3).  The only waits on them are the explicit vmcnt
+//     waits below, each wave counting its own loads.
+//   * Thread t < 256 (waves 0..3) decodes row t of the W slab from its raw
+//     bytes to bf16 and stores it into a double-buffered W stage, one slab
+//     ahead, while its wave's first eight MFMAs of the current slab run;
+//     waves 4..7 decode nothing, so each SIMD pairs a decoding wave with one
+//     whose MFMAs fill the decode's issue slots.
 //   * Both bf16 operand stages use one layout: 16-byte chunk c (k = 8c..8c+7)
 //     of row r sits at slot 4r + (c ^ ((r >> 2) & 3)), so the sixteen rows a
 //     ds_read_b128 phase touches land on distinct banks.
@@ -505,7 +508,7 @@ __device__ __forceinline__ void dma4(const uint8_t *base, uint32_t off, uint32_t
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t *p) { return (uint32_t)(uintptr_t)(lds_ptr_t)p; }
 
 template <int FMT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_pf_kernel(
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_pf_kernel(
     const uint8_t *__restrict__ B, int64_t sc_off, int64_t d_off, const uint16_t *__restrict__ X,
     float *__restrict__ Y, int M, int N, int K, int slabs_per_split)
 {
@@ -515,7 +518,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     uint8_t *const sw = smem + PNX * PSTAGE;
     uint8_t *const sr = smem + (PNX + PNW) * PSTAGE;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wm = wave & 1, wn = wave >> 1;  // 2 x 4 waves of 128 x 64
 
     // Consecutive workgroup ids land on different XCDs (round robin over 8);
     // give each XCD a contiguous run of tiles, which walks the m tiles of
@@ -532,10 +535,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // X: load j of this wave fills slots (4*wave + j)*64 + lane of a stage;
     // byte offsets from row m0 (rows past M re-read row M-1, results dropped)
     const int wv = __builtin_amdgcn_readfirstlane(wave);  // known uniform
-    uint32_t ox[4];
+    uint32_t ox[2];
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const int p = (4 * wv + j) * 64 + lane, row = p >> 2;
+    for (int j = 0; j < 2; j++) {
+        const int p = (2 * wv + j) * 64 + lane, row = p >> 2;
         const int c = (p & 3) ^ ((row >> 2) & 3);
         ox[j] = (uint32_t)(((int64_t)(min(m0 + row, M - 1) - m0) * K + 8 * c) * 2);
     }
@@ -548,10 +551,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int64_t g0 = (int64_t)n0 * (K / 256);  // first group of row n0 (K-quants)
 
     auto issue = [&](int s) {
-        const uint32_t xs = lds_addr(sx + (s % PNX) * PSTAGE) + 4096 * wv;
+        const uint32_t xs = lds_addr(sx + (s % PNX) * PSTAGE) + 2048 * wv;
 #pragma unroll
-        for (int j = 0; j < 4; j++)
+        for (int j = 0; j < 2; j++)
             dma16(xbase + 2 * PBK * s, ox[j], xs + 1024 * j);
+        if (wv >= 4)
+            return;  // the raw W bytes: waves 0..3
         const uint32_t rs = lds_addr(sr + (s % PNR) * RAWB);
         if constexpr (FMT == FMT_Q8_0) {
             const uint32_t half = lane & 1;
@@ -616,28 +621,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     };
 
     const int r32 = lane & 31, kh = lane >> 5;
-    int offa[4][2], offb[4][2];
+    int offa[4][2], offb[2][2];
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int kk = 0; kk < 2; kk++) {
 #pragma unroll
-        for (int kk = 0; kk < 2; kk++) {
+        for (int i = 0; i < 4; i++)
             offa[i][kk] = 16 * pslot(128 * wm + 32 * i + r32, 2 * kk + kh);
-            offb[i][kk] = 16 * pslot(128 * wn + 32 * i + r32, 2 * kk + kh);
-        }
-    auto frags = [&](int s, int kk, bf16x8_t (&af)[4], bf16x8_t (&bw)[4]) {
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+            offb[j][kk] = 16 * pslot(64 * wn + 32 * j + r32, 2 * kk + kh);
+    }
+    auto frags = [&](int s, int kk, bf16x8_t (&af)[4], bf16x8_t (&bw)[2]) {
         const uint8_t *xs = sx + (s % PNX) * PSTAGE, *ws = sw + (s % PNW) * PSTAGE;
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
+        for (int i = 0; i < 4; i++)
             af[i] = *reinterpret_cast<const bf16x8_t *>(xs + offa[i][kk]);
-            bw[i] = *reinterpret_cast<const bf16x8_t *>(ws + offb[i][kk]);
-        }
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+            bw[j] = *reinterpret_cast<const bf16x8_t *>(ws + offb[j][kk]);
     };
 
-    f32x16_t acc[4][4];
+    f32x16_t acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++)
+        for (int j = 0; j < 2; j++)
             acc[i][j] = f32x16_t{};
 
     // prologue: slabs sb..sb+2 landed and the W of slab sb decoded; slab
@@ -648,83 +656,85 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt 0, lgkmcnt 0
     __builtin_amdgcn_s_barrier();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    decode(sb, raw_of(sb));
+    if (wv < 4)
+        decode(sb, raw_of(sb));
     lds_barrier();
     if (sb + PNR < se)
         issue(sb + PNR);
-    bf16x8_t a0[4], b0[4], a1[4], b1[4];
+    bf16x8_t a0[4], b0[2], a1[4], b1[2];
     frags(sb, 0, a0, b0);
 
     // Slab s.  Steady state (s + 4 < se): the loads of slab s+4 go out
     // after the barrier.  The barrier needs X of slab s+1 and the raw W of
-    // slab s+2 (decoded in the next slab): both came with the loads issued
-    // two slabs ago, so one slab's loads (4 + WD per wave) may remain.
-    constexpr int VM = 4 + PRaw<FMT>::wd;
-    static_assert(VM < 16, "vmcnt immediate");
-    auto body = [&](int s, auto steady) {
-        constexpr bool ST = decltype(steady)::value;
+    // slab s+2: both came with the loads issued two slabs ago, so one slab's
+    // loads may remain (waves 0..3: 2 of X + WD of raw W; waves 4..7: 2).
+    constexpr int VMD = 2 + PRaw<FMT>::wd, VMX = 2;
+    static_assert(VMD < 16, "vmcnt immediate");
+    auto body = [&](int s, auto steady, auto decoder) {
+        constexpr bool ST = decltype(steady)::value, DEC = decltype(decoder)::value;
         const bool dec = ST || s + 1 < se;
-        // the first MFMA ahead of all reads, so that its operand wait does
-        // not wait for them; then the raw W of the next slab and the second
-        // k-step's fragments
         acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[0], b0[0], acc[0][0], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
         WBlk<FMT> w{};
-        if (dec)
+        if (DEC && dec)
             w = raw_of(s + 1);
         frags(s, 1, a1, b1);
         __builtin_amdgcn_sched_barrier(0);
-        // decode of the next slab's W spread over the remaining 15 MFMAs
-        if (dec)
+        if (DEC && dec)
             decode(s + 1, w);
 #pragma unroll
         for (int i = 0; i < 4; i++)
 #pragma unroll
-            for (int j = 0; j < 4; j++)
+            for (int j = 0; j < 2; j++)
                 if (i + j > 0)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], b0[j], acc[i][j], 0, 0, 0);
-        // three MFMAs cover the raw reads' latency, then the decode rides
-        // along the other twelve
-        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+        if constexpr (DEC) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 #pragma unroll
-        for (int k = 0; k < 12; k++) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, PRaw<FMT>::vpm, 0);  // its share of the decode
+            for (int q = 0; q < 6; q++) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 2 * PRaw<FMT>::vpm, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x200, 4, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x200, 4, 0);               // the W stores
         __builtin_amdgcn_sched_barrier(0);
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         if constexpr (ST)
-            __builtin_amdgcn_s_waitcnt(0x0070 | VM);  // vmcnt VM, lgkmcnt 0
+            __builtin_amdgcn_s_waitcnt(0x0070 | (DEC ? VMD : VMX));
         else
-            __builtin_amdgcn_s_waitcnt(0x0070);       // vmcnt 0, lgkmcnt 0
+            __builtin_amdgcn_s_waitcnt(0x0070);
         __builtin_amdgcn_s_barrier();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         if constexpr (ST)
             issue(s + PAHEAD);
-        // in the last slab these reads take a stale stage and are unused
         frags(s + 1, 0, a0, b0);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < 4; i++)
 #pragma unroll
-            for (int j = 0; j < 4; j++)
+            for (int j = 0; j < 2; j++)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], b1[j], acc[i][j], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
-    int s = sb;
-    for (; s + PAHEAD < se; s++)
-        body(s, std::true_type{});
-    for (; s < se; s++)
-        body(s, std::false_type{});
+    auto run = [&](auto decoder) {
+        int s = sb;
+        for (; s + PAHEAD < se; s++)
+            body(s, std::true_type{}, decoder);
+        for (; s < se; s++)
+            body(s, std::false_type{}, decoder);
+    };
+    if (wv < 4)
+        run(std::true_type{});
+    else
+        run(std::false_type{});
 
     // lane holds D[m = 8*(r/4) + 4*(lane/32) + r%4][n = lane%32] of each tile
     const bool split = gridDim.y > 1;
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const int n = n0 + 128 * wn + 32 * j + r32;
+        for (int j = 0; j < 2; j++) {
+            const int n = n0 + 64 * wn + 32 * j + r32;
 #pragma unroll
             for (int r = 0; r < 16; r++) {
                 const int m = m0 + 128 * wm + 32 * i + 8 * (r / 4) + 4 * kh + (r % 4);
@@ -1813,7 +1823,7 @@ hipError_t go_pf(const uint8_t *blocks, const Planes &p, const uint16_t *X, floa
         if (e != hipSuccess)
             return e;
     }
-    hipLaunchKernelGGL((gemm_pf_kernel<FMT>), dim3((unsigned)tiles, (unsigned)sp), dim3(256), 0, s, blocks, p.scales,
+    hipLaunchKernelGGL((gemm_pf_kernel<FMT>), dim3((unsigned)tiles, (unsigned)sp), dim3(512), 0, s, blocks, p.scales,
                        p.d, X, Y, (int)M, (int)N, (int)K, per);
     return hipGetLastError();
 }
