@@ -133,11 +133,13 @@ int qmatmul_ex(int fmt, const void *blocks, const void *X_bf16, float *Y_fp32, i
     const hipStream_t s = as_stream(stream);
     switch (path) {
     case QPATH_AUTO:
-        // measured crossover on MI355X: the fused GEMV wins for one or two
-        // tokens; from three tokens the MFMA weight stream is faster -- for
-        // the generic formats, whose MFMA kernel streams the weights less
-        // well, from five (Q5K 14336 x 4096, 3 tokens: 33.6 vs 54.3 us)
-        if (M <= (ql::generic_fmt(fmt) && fmt != QFMT_FP8 ? 4 : 2)) {
+        // measured crossovers on MI355X: the fused GEMV wins for one or two
+        // tokens, and for three or four where its one-shot kernel takes the
+        // shape (Q6K 14336 x 4096, 3 tokens: 13.2 vs 21.7 us on the MFMA
+        // stream); for the generic formats, whose MFMA kernel streams the
+        // weights less well, up to four (Q5K 14336 x 4096, 3 tokens: 33.6 vs
+        // 54.3 us); beyond, the MFMA weight stream
+        if (M <= 2 || (M <= 4 && ((ql::generic_fmt(fmt) && fmt != QFMT_FP8) || ql::gemv_one_shot_fits(fmt, (int)M, K)))) {
             st = gemv(fmt, B, X, Y_fp32, M, N, K, s);
             if (st != Q_ENOTSUP)
                 return st;

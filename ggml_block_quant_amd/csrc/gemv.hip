@@ -806,15 +806,22 @@ hipError_t go_glu(const Geo &gg, const Geo &gu, const uint16_t *X, float *H, int
     return hipGetLastError();
 }
 
-// one-shot kernel for M <= 2 while X fits the workgroup's LDS budget
-// (M * CPT <= 14: at most 63 KiB); false when the shape needs the
-// persistent kernel
+// one-shot kernel for M <= 4 while X fits the workgroup's LDS budget
+// (M * CPT <= 14: at most 63 KiB), except four Q8_0 tokens (measured slower
+// than the persistent kernel: 27.9 vs 21.9 us at 14336 x 4096); false when
+// the shape needs the persistent kernel
+bool one_shot_fits(int fmt, int M, int64_t K)
+{
+    const int64_t cpt = (K / 32 + 63) / 64;
+    return !generic_fmt(fmt) && M >= 1 && M <= 4 && !(fmt == FMT_Q8_0 && M == 4) && cpt <= 8 && M * cpt <= 14;
+}
+
 template <int FMT, int M>
 bool pick_lds(const Geo &g, const uint16_t *X, float *Y, int64_t N, hipStream_t s, hipError_t &e)
 {
     const int S = g.K / 32;
     const int cpt = (S + 63) / 64;
-    if (M > 2 || cpt > 8 || M * cpt > 14)
+    if (!one_shot_fits(FMT, M, g.K))
         return false;
     switch (cpt) {
     case 1: e = go_lds<FMT, M, 1>(g, X, Y, N, s); return true;
@@ -849,7 +856,7 @@ template <int FMT, int M>
 hipError_t pick(const Geo &g, const uint16_t *X, float *Y, int64_t N, hipStream_t s)
 {
     const int S = g.K / 32;  // chunks per row
-    if constexpr (M <= 2) {
+    if constexpr (M <= 4) {
         hipError_t e;
         if (pick_lds<FMT, M>(g, X, Y, N, s, e))
             return e;
@@ -1005,6 +1012,8 @@ hipError_t glu_by_m(const Geo &gg, const Geo &gu, const uint16_t *X, float *H, i
 }
 
 }  // namespace
+
+bool gemv_one_shot_fits(int fmt, int M, int64_t K) { return one_shot_fits(fmt, M, K); }
 
 bool glu_fused_fits(int fmt, int M, int64_t K)
 {

@@ -139,6 +139,8 @@ hipError_t launch_embed(int fmt, const uint8_t *blocks, int64_t N, int64_t K, co
                         int64_t n_ids, float *out, hipStream_t s);
 hipError_t launch_gemv(int fmt, const uint8_t *blocks, const uint16_t *X, float *Y, int M,
                        int64_t N, int64_t K, hipStream_t s);
+// whether the one-shot GEMV (X staged in LDS) takes M tokens of row length K
+bool gemv_one_shot_fits(int fmt, int M, int64_t K);
 bool glu_fused_fits(int fmt, int M, int64_t K);
 hipError_t launch_glu_fused(int fmt, const uint8_t *gate, const uint8_t *up, const uint16_t *X, float *H, int M,
                             int64_t F, int64_t K, int act, hipStream_t s);

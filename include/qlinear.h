@@ -89,9 +89,10 @@ typedef enum {
     QFMT_FP8 = 12 /* E4M3 codes with one fp32 scale per row (page section "FP8") */
 } qfmt;
 
-/* Matmul path.  AUTO: GEMV for M <= 2 (M <= 4 for Q5K, Q3K, Q2K and the
- * legacy 32-element formats), bf16 MFMA GEMM above (crossovers measured on
- * MI355X at decode shapes). */
+/* Matmul path.  AUTO: GEMV for M <= 2, and for M <= 4 where the one-shot
+ * GEMV takes the row length (and for Q5K, Q3K, Q2K and the legacy
+ * 32-element formats); bf16 MFMA GEMM above (crossovers measured on MI355X
+ * at decode shapes). */
 typedef enum {
     QPATH_AUTO = 0,
     QPATH_GEMV = 1,      /* fused dequant-GEMV, M <= 8 only */

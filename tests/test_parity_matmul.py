@@ -84,28 +84,27 @@ def test_gemv_row_runs_one_hot(fmt):
 @pytest.mark.parametrize("K", [1024, 4096, 5120, 14336])
 def test_gemv_wide_weights(fmt, K):
     """From 2048 rows a wave takes two or four rows (as one run of chunks at
-    the widths where that measured faster), for one and two tokens: N =
-    2051 leaves a partial last workgroup; random X within the bar, and
-    one-hot X at the first, a middle and the last element exact."""
+    the widths where that measured faster), for one to four tokens where the
+    one-shot kernel takes them: N = 2051 leaves a partial last workgroup;
+    random X within the bar, and one-hot X at the first, a middle and the
+    last element exact in every token row."""
     N = 2051
     w = synth.weights_bf16(4300 + K, N, K, outliers=True)
     blocks = ql.isq(fmt, to_dev_bf16(w))
     Wd = oracle.dequant(fmt, oracle.quantize(fmt, w), N, K)
     Wf = Wd.astype(np.float32)
-    for M in (1, 2):
+    for M in ((1, 2, 3, 4) if K <= 5120 else (1, 2)):
         x = synth.activations_bf16(4301 + M, M, K)
         Yr, den = oracle.matmul_a16(Wd, x)
         y = ql.qmatmul(fmt, blocks, to_dev_bf16(x), N, path="gemv").cpu().numpy()
         check_outputs(y, Yr, den, f"gemv wide {fmt} M={M} K={K}")
         for k in (0, K // 2 + 5, K - 1):
             x = np.zeros((M, K), np.uint16)
-            x[0, k] = 0x3F80
-            if M == 2:
-                x[1, (k + 33) % K] = 0x3F80
+            for m in range(M):
+                x[m, (k + 33 * m) % K] = 0x3F80
             y = ql.qmatmul(fmt, blocks, to_dev_bf16(x), N, path="gemv").cpu().numpy()
-            assert np.array_equal(y[0], Wf[:, k]), f"{fmt} M={M} K={K} k={k}"
-            if M == 2:
-                assert np.array_equal(y[1], Wf[:, (k + 33) % K]), f"{fmt} M=2 K={K} k={k}"
+            for m in range(M):
+                assert np.array_equal(y[m], Wf[:, (k + 33 * m) % K]), f"{fmt} M={M} m={m} K={K} k={k}"
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -142,12 +141,13 @@ def test_gemv_one_and_two_tokens_all_widths(fmt):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("M", [1, 2])
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
 def test_gemv_one_hot_is_exact_one_two_tokens(fmt, M):
-    """The one-hot pin for one and two tokens: every position of the first
+    """The one-hot pin for the one-shot kernel (one to four tokens; four
+    Q8_0 tokens take the persistent kernel): every position of the first
     256-element group, and positions of the second chunk slot of each lane
     (K = 4096: chunks 64..127) and the row's last element, must return the
-    dequantized weight bit for bit."""
+    dequantized weight bit for bit, in every token row."""
     N, K = 40, 4096
     w = synth.weights_bf16(4200 + M, N, K, outliers=True)
     blocks = ql.isq(fmt, to_dev_bf16(w))
@@ -155,13 +155,12 @@ def test_gemv_one_hot_is_exact_one_two_tokens(fmt, M):
     ks = list(range(0, 256)) + list(range(2048, 2304, 3)) + [3000, 4095]
     for k in ks:
         x = np.zeros((M, K), np.uint16)
-        x[0, k] = 0x3F80  # 1.0
-        if M == 2:
-            x[1, (k + 37) % K] = 0x3F80
+        for m in range(M):
+            x[m, (k + 37 * m) % K] = 0x3F80  # 1.0
         Y = ql.qmatmul(fmt, blocks, to_dev_bf16(x), N, path="gemv").cpu().numpy()
-        assert np.array_equal(Y[0], Wref[:, k]), f"{fmt} M={M} k={k}"
-        if M == 2:
-            assert np.array_equal(Y[1], Wref[:, (k + 37) % K]), f"{fmt} M=2 k={(k + 37) % K}"
+        for m in range(M):
+            km = (k + 37 * m) % K
+            assert np.array_equal(Y[m], Wref[:, km]), f"{fmt} M={M} m={m} k={km}"
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -283,14 +282,15 @@ def test_act_quantize_entry_point():
 
 @pytest.mark.parametrize("fmt", FMTS)
 def test_auto_path_dispatch(fmt):
-    """AUTO = GEMV for M <= 2 (bit for bit: the GEMV is deterministic) and
-    the bf16 MFMA GEMM above (equal up to the order of fp32 sums, so
-    compared to 1e-6 of sum |w||x|)."""
+    """AUTO = GEMV for M <= 2, and for 3 or 4 tokens where the one-shot GEMV
+    takes the shape (K = 1024 here; four Q8_0 tokens excepted) -- bit for
+    bit, the GEMV is deterministic -- and the bf16 MFMA GEMM above (equal up
+    to the order of fp32 sums, so compared to 1e-6 of sum |w||x|)."""
     N, K = 200, 1024
     w = synth.weights_bf16(7000, N, K)
     blocks = ql.isq(fmt, to_dev_bf16(w))
-    for M, path in ((1, "gemv"), (2, "gemv"), (3, "mfma_bf16"), (8, "mfma_bf16"), (9, "mfma_bf16"),
-                    (100, "mfma_bf16")):
+    for M, path in ((1, "gemv"), (2, "gemv"), (3, "gemv"), (4, "mfma_bf16" if fmt == "q8_0" else "gemv"),
+                    (5, "mfma_bf16"), (8, "mfma_bf16"), (9, "mfma_bf16"), (100, "mfma_bf16")):
         x = synth.activations_bf16(7001, M, K)
         X = to_dev_bf16(x)
         a = ql.qmatmul(fmt, blocks, X, N, path="auto")
