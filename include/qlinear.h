@@ -191,7 +191,8 @@ int qmatmul_ex(int fmt, const void *blocks, const void *X_bf16, float *Y_fp32, i
  * gate_blocks / up_blocks: device, isq_quantize(fmt, W, F, K) of the [F][K]
  * gate and up weights (a packed [2F][K] checkpoint tensor is quantized as
  * its two halves).  X_bf16: device [M][K].  H_fp32: device [M][F],
- * overwritten.  For M <= 2 and K <= 8192 (Q8_0, Q4K, Q6K) one fused kernel computes the
+ * overwritten.  For Q8_0, Q4K and Q6K with M <= 2 and K <= 8192, M = 3 and
+ * K <= 8192, or M = 4 and K <= 6144 (not Q8_0), one fused kernel computes the
  * gate and up rows of each output together and needs no workspace;
  * otherwise G goes through `workspace` (qmatmul_glu_workspace_bytes bytes,
  * 16-byte aligned; Q_EINVAL without it) and U through H, followed by an

@@ -209,7 +209,9 @@ def test_glu_argument_errors_and_workspace_sizes():
     assert call(M=3, ws=A2, wsb=4 * 3 * 64 - 1) == ql.Q_EINVAL
     assert call(M=3, ws=MIS, wsb=1 << 20) == ql.Q_EALIGN
     assert ql.glu_workspace_bytes("q4k", 2, 64, 8192) == 0   # fused kernel
-    assert ql.glu_workspace_bytes("q4k", 3, 64, 256) == 4 * 3 * 64
+    assert ql.glu_workspace_bytes("q4k", 3, 64, 256) == 0   # fused up to four tokens where X fits
+    assert ql.glu_workspace_bytes("q8_0", 4, 64, 256) == 4 * 4 * 64   # four Q8_0 tokens: two-matmul path
+    assert ql.glu_workspace_bytes("q4k", 5, 64, 256) == 4 * 5 * 64
     assert ql.glu_workspace_bytes("q4k", 1, 64, 8448) == 4 * 64
     assert ql.glu_workspace_bytes("q8k", 1, 64, 256) == 0
     assert ql.glu_workspace_bytes("q2k", 1, 64, 256) == 4 * 64   # generic formats: two-matmul path

@@ -49,20 +49,27 @@ def _case(fmt, F, K, M, seed, act):
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("act", ACTS)
 def test_glu_fused_kernel(fmt, act):
+    """One to four tokens where X fits the one-shot kernel (three tokens up
+    to K = 8192, four up to 6144; four Q8_0 tokens take the two-matmul
+    path): no workspace."""
     assert ql.glu_workspace_bytes(fmt, 2, 300, 8192) == 0   # fused: no workspace
+    assert ql.glu_workspace_bytes(fmt, 3, 300, 8192) == 0
     for F, K in ((300, 256), (1000, 1024), (129, 4096), (64, 8192)):
-        for M in (1, 2):
+        for M in (1, 2, 3, 4):
+            if M == 4 and K > 6144:
+                continue
             _case(fmt, F, K, M, 9000 + K + M, act)
 
 
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("act", ACTS)
 def test_glu_two_matmul_path(fmt, act):
-    """M > 2 or K > 8192: G through the workspace, U through H, then the
-    elementwise pass."""
-    assert ql.glu_workspace_bytes(fmt, 3, 1000, 1024) == 4 * 3 * 1000
+    """M > 4, K > 8192 or beyond the one-shot kernel's X budget: G through
+    the workspace, U through H, then the elementwise pass."""
+    assert ql.glu_workspace_bytes(fmt, 5, 1000, 1024) == 4 * 5 * 1000
+    assert ql.glu_workspace_bytes(fmt, 4, 1000, 8192) == 4 * 4 * 1000
     assert ql.glu_workspace_bytes(fmt, 1, 64, 14336) == 4 * 64
-    for F, K, M in ((1000, 1024, 3), (300, 4096, 9), (130, 512, 40), (64, 14336, 1)):
+    for F, K, M in ((1000, 1024, 5), (300, 4096, 9), (130, 512, 40), (64, 14336, 1), (200, 8192, 4)):
         _case(fmt, F, K, M, 9100 + K + M, act)
 
 
@@ -122,9 +129,9 @@ def test_glu_zero_input_and_argument_errors():
         assert not ql.qmatmul_glu("q4k", b, b, x, F, act=act).any()
     with pytest.raises(ql.QLinearError):
         ql.qmatmul_glu("q4k", b, b, x, F, act=7)
-    # no workspace where the two-matmul path needs one
+    # no workspace where the two-matmul path needs one (five tokens)
     L = ql.lib()
-    x3 = torch.zeros((3, K), dtype=torch.bfloat16, device="cuda")
-    H = torch.empty((3, F), dtype=torch.float32, device="cuda")
-    st = L.qmatmul_glu(1, b.data_ptr(), b.data_ptr(), x3.data_ptr(), H.data_ptr(), 3, F, K, 0, None, 0, None)
+    x5 = torch.zeros((5, K), dtype=torch.bfloat16, device="cuda")
+    H = torch.empty((5, F), dtype=torch.float32, device="cuda")
+    st = L.qmatmul_glu(1, b.data_ptr(), b.data_ptr(), x5.data_ptr(), H.data_ptr(), 5, F, K, 0, None, 0, None)
     assert st == ql.Q_EINVAL
