@@ -205,9 +205,9 @@ def test_glu_argument_errors_and_workspace_sizes():
     assert call(act=-1) == ql.Q_EINVAL
     assert call(K=100) == ql.Q_ESHAPE
     assert call(M=0) == ql.Q_ESHAPE
-    assert call(M=3) == ql.Q_EINVAL                          # two-matmul path without a workspace
-    assert call(M=3, ws=A2, wsb=4 * 3 * 64 - 1) == ql.Q_EINVAL
-    assert call(M=3, ws=MIS, wsb=1 << 20) == ql.Q_EALIGN
+    assert call(M=5) == ql.Q_EINVAL                          # two-matmul path without a workspace
+    assert call(M=5, ws=A2, wsb=4 * 5 * 64 - 1) == ql.Q_EINVAL
+    assert call(M=5, ws=MIS, wsb=1 << 20) == ql.Q_EALIGN
     assert ql.glu_workspace_bytes("q4k", 2, 64, 8192) == 0   # fused kernel
     assert ql.glu_workspace_bytes("q4k", 3, 64, 256) == 0   # fused up to four tokens where X fits
     assert ql.glu_workspace_bytes("q8_0", 4, 64, 256) == 4 * 4 * 64   # four Q8_0 tokens: two-matmul path
