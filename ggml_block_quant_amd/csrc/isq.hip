@@ -71,6 +71,18 @@ __device__ __forceinline__ float rha_quot(float u, float S, float r)
     return q;
 }
 
+// rha_quot where the code is clamped at 0 from below (Q4K): for t < 0 both
+// RHA(t) and floor(t + 0.5) are at most 0, so the sign restore is dropped;
+// for t >= 0 they are the same value
+__device__ __forceinline__ float rha_quot_nonneg(float u, float S, float r)
+{
+    const float t = u * r;
+    float q = floorf(t + 0.5f);
+    if (fabsf(__builtin_amdgcn_fractf(t) - 0.5f) <= 2.5e-7f * fabsf(t))
+        q = roundf(u / S);
+    return q;
+}
+
 // Even elements of an octet in the low half of a dword, odd ones in the high
 // half: nibble p holds element 2p (p < 4) or 2(p-4)+1 (p >= 4).
 __device__ __forceinline__ uint32_t pack_nibbles(const int q[8])
@@ -172,7 +184,7 @@ __global__ __launch_bounds__(256) void isq_q4k_kernel(const uint4 *__restrict__ 
 #pragma unroll
             for (int i = 0; i < 8; i++) {
                 const float u = x[8 * k + i] + M;
-                q[i] = (int)__builtin_amdgcn_fmed3f(rha_quot(u, S, rS), 0.0f, 15.0f);
+                q[i] = (int)__builtin_amdgcn_fmed3f(rha_quot_nonneg(u, S, rS), 0.0f, 15.0f);
             }
             w[k] = pack_nibbles(q);
         }
