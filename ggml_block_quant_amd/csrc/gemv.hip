@@ -600,6 +600,7 @@ __global__ __launch_bounds__(64 * LW) void gemv_lds_kernel(Geo g, Geo g2, const 
     constexpr int SLOTS = 64 * CPT;           // chunk slots per row
     constexpr bool SUMS = FMT != FMT_Q8_0;    // bias-correction sums (Q4K, Q6K)
     constexpr int XU = M * CPT;               // uint4 of X staged per thread
+    static_assert(64 * LW * XU == M * 4 * SLOTS, "the workgroup stages every quarter of X exactly once");
     __shared__ uint4 sx[M][4][SLOTS];         // quarter t of chunk c at sx[m][t][c]
     // chunk sums; the last slot takes the stores of the lanes that own no sum
     // (stores without branches, so the compiler keeps every X load ahead
