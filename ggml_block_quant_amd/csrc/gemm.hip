@@ -105,17 +105,29 @@ __device__ __forceinline__ void load_wblk(const uint8_t *__restrict__ B, int64_t
     }
 }
 
-// 32 dequantized weights -> 16 dwords of bf16 pairs (element 2e, 2e+1 in dword e)
+// Each weight w (fp32) reaches the MFMA as two bf16 operands, hi = bf16(w)
+// (round to nearest even) and lo = bf16(w - hi): w - hi is exact in fp32
+// and at most 2^-8 |w|, so |hi + lo - w| <= 2^-17 |w|.  A single bf16 per
+// weight would leave up to 2^-8 |w| per product, and those errors add up
+// when they share a sign (a constant row against positive activations).
+__device__ __forceinline__ void split_bf16(float a, float b, uint32_t &hi, uint32_t &lo)
+{
+    hi = pack_bf16(a, b);
+    lo = pack_bf16(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+}
+
+// 32 dequantized weights of one block -> 16 dwords of hi bf16 pairs and 16
+// of lo pairs (element 2e, 2e+1 in dword e)
 template <int FMT>
-__device__ __forceinline__ void decode_wblk(const WBlk<FMT> &w, int c, uint32_t out[16])
+__device__ __forceinline__ void decode_wblk(const WBlk<FMT> &w, int c, uint32_t hi[16], uint32_t lo[16])
 {
     if constexpr (FMT == FMT_Q8_0) {
         const float d = h2f(w.d);
         const uint32_t v[8] = {w.c0.x, w.c0.y, w.c0.z, w.c0.w, w.c1.x, w.c1.y, w.c1.z, w.c1.w};
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-            out[2 * i] = pack_bf16(d * (float)(int8_t)(v[i]), d * (float)(int8_t)(v[i] >> 8));
-            out[2 * i + 1] = pack_bf16(d * (float)(int8_t)(v[i] >> 16), d * (float)(int8_t)(v[i] >> 24));
+            split_bf16(d * (float)(int8_t)(v[i]), d * (float)(int8_t)(v[i] >> 8), hi[2 * i], lo[2 * i]);
+            split_bf16(d * (float)(int8_t)(v[i] >> 16), d * (float)(int8_t)(v[i] >> 24), hi[2 * i + 1], lo[2 * i + 1]);
         }
     } else if constexpr (FMT == FMT_Q4K) {
         const int j = c & 7;
@@ -129,19 +141,19 @@ __device__ __forceinline__ void decode_wblk(const WBlk<FMT> &w, int c, uint32_t 
             // nibble p holds element 2p (p < 4) or 2(p-4)+1, so the bytes of
             // lo = v & 0x0F0F0F0F are elements 0,4,1,5 and those of
             // hi = (v >> 4) & 0x0F0F0F0F are elements 2,6,3,7
-            uint32_t lo = v[q] & 0x0F0F0F0Fu, hi = (v[q] >> 4) & 0x0F0F0F0Fu;
+            uint32_t nl = v[q] & 0x0F0F0F0Fu, nh = (v[q] >> 4) & 0x0F0F0F0Fu;
             // opaque to the optimizer, so that each element converts with one
             // byte-selecting v_cvt_f32_ubyteN instead of a bfe and a convert
-            asm("" : "+v"(lo));
-            asm("" : "+v"(hi));
-            const float e0 = (float)(lo & 0xffu), e4 = (float)((lo >> 8) & 0xffu);
-            const float e1 = (float)((lo >> 16) & 0xffu), e5 = (float)(lo >> 24);
-            const float e2 = (float)(hi & 0xffu), e6 = (float)((hi >> 8) & 0xffu);
-            const float e3 = (float)((hi >> 16) & 0xffu), e7 = (float)(hi >> 24);
-            out[4 * q + 0] = pack_bf16(fmaf(S, e0, -Mn), fmaf(S, e1, -Mn));
-            out[4 * q + 1] = pack_bf16(fmaf(S, e2, -Mn), fmaf(S, e3, -Mn));
-            out[4 * q + 2] = pack_bf16(fmaf(S, e4, -Mn), fmaf(S, e5, -Mn));
-            out[4 * q + 3] = pack_bf16(fmaf(S, e6, -Mn), fmaf(S, e7, -Mn));
+            asm("" : "+v"(nl));
+            asm("" : "+v"(nh));
+            const float e0 = (float)(nl & 0xffu), e4 = (float)((nl >> 8) & 0xffu);
+            const float e1 = (float)((nl >> 16) & 0xffu), e5 = (float)(nl >> 24);
+            const float e2 = (float)(nh & 0xffu), e6 = (float)((nh >> 8) & 0xffu);
+            const float e3 = (float)((nh >> 16) & 0xffu), e7 = (float)(nh >> 24);
+            split_bf16(fmaf(S, e0, -Mn), fmaf(S, e1, -Mn), hi[4 * q + 0], lo[4 * q + 0]);
+            split_bf16(fmaf(S, e2, -Mn), fmaf(S, e3, -Mn), hi[4 * q + 1], lo[4 * q + 1]);
+            split_bf16(fmaf(S, e4, -Mn), fmaf(S, e5, -Mn), hi[4 * q + 2], lo[4 * q + 2]);
+            split_bf16(fmaf(S, e6, -Mn), fmaf(S, e7, -Mn), hi[4 * q + 3], lo[4 * q + 3]);
         }
     } else {
         const float d = h2f(w.d);
@@ -151,7 +163,7 @@ __device__ __forceinline__ void decode_wblk(const WBlk<FMT> &w, int c, uint32_t 
 #pragma unroll
         for (int q = 0; q < 4; q++) {
             const int o = q & 1;
-            const float S = Sab[q >> 1], B = -32.0f * S;  // S (u - 32) = fma(S, u, -32 S), one rounding
+            const float S = Sab[q >> 1], B = -32.0f * S;  // S (u - 32) = fma(S, u, -32 S), exact
             // the four codes u = q + 32 of bytes (e0, e4, e1, e5) and (e2, e6, e3, e7) of the octet:
             // low nibbles masked out of the dword, the two high bits of each moved to bits 4-5 of
             // its byte (element 2p's pair at bit 8o + 2p of the high-bit dword, 2p + 1's at 16 + 8o + 2p)
@@ -165,10 +177,10 @@ __device__ __forceinline__ void decode_wblk(const WBlk<FMT> &w, int c, uint32_t 
             const float e1 = (float)((ua >> 16) & 0xffu), e5 = (float)(ua >> 24);
             const float e2 = (float)(ub & 0xffu), e6 = (float)((ub >> 8) & 0xffu);
             const float e3 = (float)((ub >> 16) & 0xffu), e7 = (float)(ub >> 24);
-            out[4 * q + 0] = pack_bf16(fmaf(S, e0, B), fmaf(S, e1, B));
-            out[4 * q + 1] = pack_bf16(fmaf(S, e2, B), fmaf(S, e3, B));
-            out[4 * q + 2] = pack_bf16(fmaf(S, e4, B), fmaf(S, e5, B));
-            out[4 * q + 3] = pack_bf16(fmaf(S, e6, B), fmaf(S, e7, B));
+            split_bf16(fmaf(S, e0, B), fmaf(S, e1, B), hi[4 * q + 0], lo[4 * q + 0]);
+            split_bf16(fmaf(S, e2, B), fmaf(S, e3, B), hi[4 * q + 1], lo[4 * q + 1]);
+            split_bf16(fmaf(S, e4, B), fmaf(S, e5, B), hi[4 * q + 2], lo[4 * q + 2]);
+            split_bf16(fmaf(S, e6, B), fmaf(S, e7, B), hi[4 * q + 3], lo[4 * q + 3]);
         }
     }
 }
@@ -258,16 +270,18 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint8_t *__restric
         }
 #pragma unroll
         for (int i = 0; i < NT; i++) {
-            uint32_t wv[16];
-            decode_wblk<FMT>(wa[i], 4 * s + g, wv);
+            uint32_t wh[16], wl[16];
+            decode_wblk<FMT>(wa[i], 4 * s + g, wh, wl);
 #pragma unroll
             for (int t = 0; t < 4; t++) {
-                const bf16x8_t bw = __builtin_bit_cast(bf16x8_t, make_uint4(wv[4 * t], wv[4 * t + 1], wv[4 * t + 2], wv[4 * t + 3]));
+                const bf16x8_t bh = __builtin_bit_cast(bf16x8_t, make_uint4(wh[4 * t], wh[4 * t + 1], wh[4 * t + 2], wh[4 * t + 3]));
+                const bf16x8_t bl = __builtin_bit_cast(bf16x8_t, make_uint4(wl[4 * t], wl[4 * t + 1], wl[4 * t + 2], wl[4 * t + 3]));
 #pragma unroll
                 for (int j = 0; j < TM; j++) {
                     const bf16x8_t xa = *reinterpret_cast<const bf16x8_t *>(
                         &sX[buf][(16 * j + r16) * XPITCH + 64 * g + 16 * t]);
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bw, acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bh, acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bl, acc[i][j], 0, 0, 0);
                 }
             }
         }
@@ -393,18 +407,21 @@ __global__ __launch_bounds__(512) void gemm_skinny_kernel(const uint8_t *__restr
             if (su < se) {
 #pragma unroll
                 for (int i = 0; i < NT; i++) {
-                    uint32_t wv16[16];
-                    decode_wblk<FMT>(ring[u][i], 4 * su + g, wv16);
+                    uint32_t wh[16], wl[16];
+                    decode_wblk<FMT>(ring[u][i], 4 * su + g, wh, wl);
 #pragma unroll
                     for (int t = 0; t < 4; t++) {
-                        const bf16x8_t bw = __builtin_bit_cast(
-                            bf16x8_t, make_uint4(wv16[4 * t], wv16[4 * t + 1], wv16[4 * t + 2], wv16[4 * t + 3]));
+                        const bf16x8_t bh = __builtin_bit_cast(
+                            bf16x8_t, make_uint4(wh[4 * t], wh[4 * t + 1], wh[4 * t + 2], wh[4 * t + 3]));
+                        const bf16x8_t bl = __builtin_bit_cast(
+                            bf16x8_t, make_uint4(wl[4 * t], wl[4 * t + 1], wl[4 * t + 2], wl[4 * t + 3]));
 #pragma unroll
                         for (int j = 0; j < TM; j++) {
                             // rows of X past M read row 0 and are zeroed here
-                            const uint4 xv = xlive[j] ? xq[u][j][t] : make_uint4(0u, 0u, 0u, 0u);
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                __builtin_bit_cast(bf16x8_t, xv), bw, acc[i][j], 0, 0, 0);
+                            const bf16x8_t xa = __builtin_bit_cast(
+                                bf16x8_t, xlive[j] ? xq[u][j][t] : make_uint4(0u, 0u, 0u, 0u));
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bh, acc[i][j], 0, 0, 0);
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bl, acc[i][j], 0, 0, 0);
                         }
                     }
                 }
@@ -480,9 +497,9 @@ __device__ __forceinline__ int pslot(int row, int c) { return row * 4 + (c ^ ((r
 //         9216 + 4r
 template <int FMT> struct PRaw;
 // (vpm: decode VALU instructions scheduled per MFMA)
-template <> struct PRaw<FMT_Q8_0> { static constexpr int bytes = 9216, wd = 3, vpm = 9; };
-template <> struct PRaw<FMT_Q4K> { static constexpr int bytes = 8192, wd = 2, vpm = 11; };
-template <> struct PRaw<FMT_Q6K> { static constexpr int bytes = 10240, wd = 4, vpm = 12; };
+template <> struct PRaw<FMT_Q8_0> { static constexpr int bytes = 9216, wd = 3, vpm = 12; };
+template <> struct PRaw<FMT_Q4K> { static constexpr int bytes = 8192, wd = 2, vpm = 12; };
+template <> struct PRaw<FMT_Q6K> { static constexpr int bytes = 10240, wd = 4, vpm = 13; };
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 typedef __attribute__((address_space(1))) void *gbl_ptr_t;
@@ -513,10 +530,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     float *__restrict__ Y, int M, int N, int K, int slabs_per_split)
 {
     constexpr int RAWB = PRaw<FMT>::bytes;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[PNX * PSTAGE + PNW * PSTAGE + PNR * RAWB];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[PNX * PSTAGE + 2 * PNW * PSTAGE + PNR * RAWB];
     uint8_t *const sx = smem;
-    uint8_t *const sw = smem + PNX * PSTAGE;
-    uint8_t *const sr = smem + (PNX + PNW) * PSTAGE;
+    uint8_t *const sw = smem + PNX * PSTAGE;               // hi parts of the decoded W
+    uint8_t *const swl = smem + (PNX + PNW) * PSTAGE;      // lo parts
+    uint8_t *const sr = smem + (PNX + 2 * PNW) * PSTAGE;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave & 1, wn = wave >> 1;  // 2 x 4 waves of 128 x 64
 
@@ -612,12 +630,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const int64_t grp = nd * (K / 256) + (s >> 3);
             w.d = (grp & 1) ? w.d >> 16 : w.d & 0xffffu;
         }
-        uint32_t v[16];
-        decode_wblk<FMT>(w, s, v);
-        uint8_t *ws = sw + (s % PNW) * PSTAGE;
+        uint32_t vh[16], vl[16];
+        decode_wblk<FMT>(w, s, vh, vl);
+        uint8_t *wh = sw + (s % PNW) * PSTAGE, *wl = swl + (s % PNW) * PSTAGE;
 #pragma unroll
-        for (int c = 0; c < 4; c++)
-            *reinterpret_cast<uint4 *>(ws + 16 * pslot(tid, c)) = make_uint4(v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]);
+        for (int c = 0; c < 4; c++) {
+            *reinterpret_cast<uint4 *>(wh + 16 * pslot(tid, c)) = make_uint4(vh[4 * c], vh[4 * c + 1], vh[4 * c + 2], vh[4 * c + 3]);
+            *reinterpret_cast<uint4 *>(wl + 16 * pslot(tid, c)) = make_uint4(vl[4 * c], vl[4 * c + 1], vl[4 * c + 2], vl[4 * c + 3]);
+        }
     };
 
     const int r32 = lane & 31, kh = lane >> 5;
@@ -631,14 +651,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int j = 0; j < 2; j++)
             offb[j][kk] = 16 * pslot(64 * wn + 32 * j + r32, 2 * kk + kh);
     }
-    auto frags = [&](int s, int kk, bf16x8_t (&af)[4], bf16x8_t (&bw)[2]) {
-        const uint8_t *xs = sx + (s % PNX) * PSTAGE, *ws = sw + (s % PNW) * PSTAGE;
+    auto frags = [&](int s, int kk, bf16x8_t (&af)[4], bf16x8_t (&bw)[4]) {
+        const uint8_t *xs = sx + (s % PNX) * PSTAGE, *ws = sw + (s % PNW) * PSTAGE, *wl = swl + (s % PNW) * PSTAGE;
 #pragma unroll
         for (int i = 0; i < 4; i++)
             af[i] = *reinterpret_cast<const bf16x8_t *>(xs + offa[i][kk]);
 #pragma unroll
-        for (int j = 0; j < 2; j++)
+        for (int j = 0; j < 2; j++) {
             bw[j] = *reinterpret_cast<const bf16x8_t *>(ws + offb[j][kk]);
+            bw[2 + j] = *reinterpret_cast<const bf16x8_t *>(wl + offb[j][kk]);
+        }
     };
 
     f32x16_t acc[4][2];
@@ -661,7 +683,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     lds_barrier();
     if (sb + PNR < se)
         issue(sb + PNR);
-    bf16x8_t a0[4], b0[2], a1[4], b1[2];
+    bf16x8_t a0[4], b0[4], a1[4], b1[4];  // b: hi parts of the two n tiles, then lo parts
     frags(sb, 0, a0, b0);
 
     // Slab s.  Steady state (s + 4 < se): the loads of slab s+4 go out
@@ -674,6 +696,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         constexpr bool ST = decltype(steady)::value, DEC = decltype(decoder)::value;
         const bool dec = ST || s + 1 < se;
         acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[0], b0[0], acc[0][0], 0, 0, 0);
+        acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[0], b0[2], acc[0][0], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
         WBlk<FMT> w{};
         if (DEC && dec)
@@ -686,16 +709,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int i = 0; i < 4; i++)
 #pragma unroll
             for (int j = 0; j < 2; j++)
-                if (i + j > 0)
+                if (i + j > 0) {
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], b0[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], b0[2 + j], acc[i][j], 0, 0, 0);
+                }
         if constexpr (DEC) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 #pragma unroll
-            for (int q = 0; q < 6; q++) {
+            for (int q = 0; q < 13; q++) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 2 * PRaw<FMT>::vpm, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, PRaw<FMT>::vpm, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x200, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x200, 8, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -712,8 +737,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int i = 0; i < 4; i++)
 #pragma unroll
-            for (int j = 0; j < 2; j++)
+            for (int j = 0; j < 2; j++) {
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], b1[j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], b1[2 + j], acc[i][j], 0, 0, 0);
+            }
         __builtin_amdgcn_sched_barrier(0);
     };
     auto run = [&](auto decoder) {
@@ -854,7 +881,7 @@ __global__ __launch_bounds__(256) void gemm_bt_kernel(const uint8_t *__restrict_
 
     const int row = 16 * wv + r16;  // the W row this lane decodes
     const int64_t nd = min(n0 + row, N - 1);
-    auto decode = [&](int s, uint32_t (&v)[16]) {
+    auto decode = [&](int s, uint32_t (&vh)[16], uint32_t (&vl)[16]) {
         const uint8_t *rs = sr + (s % TNS) * RAWB;
         WBlk<FMT> w;
         if constexpr (FMT == FMT_Q8_0) {
@@ -872,7 +899,7 @@ __global__ __launch_bounds__(256) void gemm_bt_kernel(const uint8_t *__restrict_
             const int64_t grp = nd * (K / 256) + (s >> 1);
             w.d = (grp & 1) ? dd >> 16 : dd & 0xffffu;
         }
-        decode_wblk<FMT>(w, 4 * s + g, v);
+        decode_wblk<FMT>(w, 4 * s + g, vh, vl);
     };
 
     f32x4_t acc[TM];
@@ -893,17 +920,19 @@ __global__ __launch_bounds__(256) void gemm_bt_kernel(const uint8_t *__restrict_
     static_assert(VM < 16, "vmcnt immediate");
     auto body = [&](int s, auto steady) {
         constexpr bool ST = decltype(steady)::value;
-        uint32_t v[16];
-        decode(s, v);
+        uint32_t vh[16], vl[16];
+        decode(s, vh, vl);
         const uint8_t *xs = sx + (s % TNS) * XSTG;
 #pragma unroll
         for (int t = 0; t < 4; t++) {
-            const bf16x8_t bw = __builtin_bit_cast(bf16x8_t, make_uint4(v[4 * t], v[4 * t + 1], v[4 * t + 2], v[4 * t + 3]));
+            const bf16x8_t bh = __builtin_bit_cast(bf16x8_t, make_uint4(vh[4 * t], vh[4 * t + 1], vh[4 * t + 2], vh[4 * t + 3]));
+            const bf16x8_t bl = __builtin_bit_cast(bf16x8_t, make_uint4(vl[4 * t], vl[4 * t + 1], vl[4 * t + 2], vl[4 * t + 3]));
 #pragma unroll
             for (int j = 0; j < TM; j++) {
                 const int xr = 16 * j + r16;
                 const bf16x8_t xa = *reinterpret_cast<const bf16x8_t *>(xs + 256 * xr + 16 * ((4 * g + t) ^ r16));
-                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bw, acc[j], 0, 0, 0);
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bh, acc[j], 0, 0, 0);
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bl, acc[j], 0, 0, 0);
             }
         }
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -1039,14 +1068,16 @@ __global__ __launch_bounds__(320) void gemm_bq_kernel(const uint8_t *__restrict_
             WBlk<FMT_Q4K> w;
             w.c = *reinterpret_cast<const uint4 *>(my + 256 * r16 + 16 * ((4 * t + g) ^ r16));
             w.h = hw[u][t >> 1];
-            uint32_t v[16];
-            decode_wblk<FMT_Q4K>(w, 4 * s + g, v);
+            uint32_t vh[16], vl[16];
+            decode_wblk<FMT_Q4K>(w, 4 * s + g, vh, vl);
             const uint8_t *xs = sx + XR * 256 * (s - sx0);
 #pragma unroll
             for (int q = 0; q < 4; q++) {
-                const bf16x8_t bw = __builtin_bit_cast(bf16x8_t, make_uint4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]));
+                const bf16x8_t bh = __builtin_bit_cast(bf16x8_t, make_uint4(vh[4 * q], vh[4 * q + 1], vh[4 * q + 2], vh[4 * q + 3]));
+                const bf16x8_t bl = __builtin_bit_cast(bf16x8_t, make_uint4(vl[4 * q], vl[4 * q + 1], vl[4 * q + 2], vl[4 * q + 3]));
                 const bf16x8_t xa = *reinterpret_cast<const bf16x8_t *>(xs + 256 * xr + 16 * ((4 * g + q) ^ xr));
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bw, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bh, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bl, acc, 0, 0, 0);
             }
         }
     }
@@ -1160,14 +1191,18 @@ __global__ __launch_bounds__(256) void gemm_gen_lds_kernel(const uint8_t *__rest
             for (int t = 0; t < 4; t++) {
                 float w[8];
                 dequant8<FMT>(B, p, wpiece[i] + 16 * s + 4 * g + t, w);
-                const bf16x8_t bw = __builtin_bit_cast(
-                    bf16x8_t, make_uint4(pack_bf16(w[0], w[1]), pack_bf16(w[2], w[3]), pack_bf16(w[4], w[5]),
-                                         pack_bf16(w[6], w[7])));
+                uint32_t h[4], l[4];
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    split_bf16(w[2 * e], w[2 * e + 1], h[e], l[e]);
+                const bf16x8_t bh = __builtin_bit_cast(bf16x8_t, make_uint4(h[0], h[1], h[2], h[3]));
+                const bf16x8_t bl = __builtin_bit_cast(bf16x8_t, make_uint4(l[0], l[1], l[2], l[3]));
 #pragma unroll
                 for (int j = 0; j < TM; j++) {
                     const bf16x8_t xa = *reinterpret_cast<const bf16x8_t *>(
                         &sX[buf][(16 * j + r16) * XPITCH + 64 * g + 16 * t]);
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bw, acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bh, acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bl, acc[i][j], 0, 0, 0);
                 }
             }
         }
@@ -1248,29 +1283,16 @@ __global__ __launch_bounds__(256) void gemm_gen_kernel(const uint8_t *__restrict
 #pragma unroll
         for (int u = 0; u < U; u++) {
             if (s + u < s1) {
-                uint32_t h[4];
+                uint32_t h[4], l[4];
 #pragma unroll
                 for (int e = 0; e < 4; e++)
-                    h[e] = pack_bf16(w[u][2 * e], w[u][2 * e + 1]);
-                const bf16x8_t bw = __builtin_bit_cast(bf16x8_t, make_uint4(h[0], h[1], h[2], h[3]));
+                    split_bf16(w[u][2 * e], w[u][2 * e + 1], h[e], l[e]);
+                const bf16x8_t bh = __builtin_bit_cast(bf16x8_t, make_uint4(h[0], h[1], h[2], h[3]));
+                const bf16x8_t bl = __builtin_bit_cast(bf16x8_t, make_uint4(l[0], l[1], l[2], l[3]));
 #pragma unroll
-                for (int j = 0; j < TM; j++)
-                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[u][j], bw, acc[j], 0, 0, 0);
-                if constexpr (FMT == FMT_Q8_0) {
-                    // Q8_0 here serves rows that end in a tail of blocks, down to
-                    // a single block, where the bf16 rounding of each weight
-                    // (up to 2^-9) would not average out: add the remainder
-                    // w - bf16(w) (exact in fp32: d q has at most 18 significant
-                    // bits) as a second bf16 operand, leaving at most 2^-18 |w|
-                    uint32_t l[4];
-#pragma unroll
-                    for (int e = 0; e < 4; e++)
-                        l[e] = pack_bf16(w[u][2 * e] - __uint_as_float(h[e] << 16),
-                                         w[u][2 * e + 1] - __uint_as_float(h[e] & 0xffff0000u));
-                    const bf16x8_t bl = __builtin_bit_cast(bf16x8_t, make_uint4(l[0], l[1], l[2], l[3]));
-#pragma unroll
-                    for (int j = 0; j < TM; j++)
-                        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[u][j], bl, acc[j], 0, 0, 0);
+                for (int j = 0; j < TM; j++) {
+                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[u][j], bh, acc[j], 0, 0, 0);
+                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[u][j], bl, acc[j], 0, 0, 0);
                 }
             }
         }

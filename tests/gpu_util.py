@@ -40,3 +40,18 @@ def check_outputs(y_gpu: np.ndarray, y_ref: np.ndarray, den: np.ndarray, label="
     worst = float(e.max()) if e.size else 0.0
     assert worst <= TOL, f"{label}: max normalised error {worst:.3e} > {TOL}"
     return worst
+
+
+# The bf16 MFMA kernels give each weight w to the matrix cores as two bf16
+# values, hi = bf16(w) and lo = bf16(w - hi); with one-hot activations an
+# output is hi + lo, within 2^-17 |w| of the fp32 weight.
+SPLIT_REL = 2.0 ** -17
+
+
+def assert_split_exact(y: np.ndarray, w32: np.ndarray, label=""):
+    """One-hot outputs of a bf16 MFMA kernel against the fp32 weights they
+    select: |y - w| <= 2^-17 |w| element by element (w = 0 gives y = 0)."""
+    y = np.asarray(y, np.float64)
+    w = np.asarray(w32, np.float32).astype(np.float64)
+    bad = np.abs(y - w) > SPLIT_REL * np.abs(w)
+    assert not bad.any(), f"{label}: {int(bad.sum())} one-hot outputs off, first at {np.argwhere(bad)[0]}"
