@@ -23,13 +23,26 @@
 // their contribution is dropped or multiplied by a zero X), so the load
 // path has no branches.
 //
-// Arithmetic.  Q4K / Q6K codes u (4 or 6 bits) become bf16 pairs with one
-// v_and_or_b32: bits 0x4300 | u are exactly the bf16 value 128 + u, and the
-// nibble order of the layout puts two consecutive elements in the two
-// halves of a dword.  v_dot2_f32_bf16 multiplies them by the bf16 pair of
-// X directly (products exact in fp32), and the bias is removed once per
-// sub-block:  sum x*(128+u) - 128*sum x.  Q8_0 codes are sign-extended
-// bytes converted to fp32 and FMA'd.  All accumulation is fp32.
+// Arithmetic: every product of a code and an activation is exact and only
+// the fp32 sums round, so an output's error is relative to sum |w||x|.
+//   * Q4K: the 4-bit codes u are taken as E4M3 bytes -- a byte 0..15 is the
+//     E4M3 value u * 2^-9 (subnormal up to 7, the first binade from 8) --
+//     and v_cvt_scalef32_pk_bf16_fp8 with scale 2^9 turns two of them into
+//     the bf16 pair (u, u') exactly.  The layout's nibble order gives the
+//     pairs (0,4), (1,5), (2,6), (3,7) of each group of eight elements, so X
+//     is staged in that pairing.  v_dot2_f32_bf16 forms sum u*x; the chunk
+//     adds S * sum u*x - Mn * sum x.
+//   * Q6K: the codes q = u - 32 (-32 .. 31) are exact in fp16: the bits
+//     0x6400 | u are 1024 + u, and one v_pk_add_f16 of -1056 leaves q for
+//     two elements.  X is staged in fp16 after scaling each chunk of 32 by a
+//     power of two that puts its largest magnitude in [2^14, 2^15), where
+//     every bf16 value down to 2^-32 of that maximum is exact; the scale is
+//     undone on the chunk's sum.  v_dot2_f32_f16 forms sum q*x.
+//   * Q8_0: signed codes converted with v_cvt_f32_i32 on a sign-extended
+//     byte (SDWA), fused multiply-adds with X.
+// (Adding a bias to the codes instead, sum x*(128+u) - 128 sum x, rounds at
+// the scale of the bias and fails the bar on blocks whose codes are mostly
+// zero where X is large.)
 #include "qlinear_internal.h"
 #include "decode.h"
 
@@ -99,13 +112,57 @@ __device__ __forceinline__ void load_chunk<FMT_Q8_0>(const Geo &g, int64_t n, in
     ck.d = *reinterpret_cast<const uint16_t *>(g.B + g.scales_off + 2 * blk);
 }
 
-// X of one chunk for M rows: 16 bf16 pairs per row, plus the terms of the
-// bias correction (Q4K: s0 = 128 * sum, s1 = sum over the chunk; Q6K:
-// s0, s1 = 160 * sum over each 16-element half).
+// X of one chunk for M rows: 16 pairs per row (Q4K: bf16 in the pairing of
+// the codes; Q6K: scaled fp16; Q8_0: bf16), plus Q4K's sum over the chunk
+// (sum) or Q6K's scale exponent (e: X was multiplied by 2^e).
 template <int M> struct XChunk {
     uint32_t p[M][16];
-    float s0[M], s1[M];
+    float sum[M];
+    int e[M];
 };
+
+typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2_t;
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2h(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c, false);
+}
+
+// bytes 2H, 2H+1 of w, each 0..15, as the bf16 pair of those integers
+template <bool H>
+__device__ __forceinline__ uint32_t nib_pair(uint32_t w)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 512.0f, H));
+}
+
+// the bf16 dwords of eight consecutive activations (elements 0-1, 2-3, 4-5,
+// 6-7) -> the pairs (0,4), (1,5), (2,6), (3,7) the Q4K codes come in
+__device__ __forceinline__ uint4 octet_pairs(uint4 v)
+{
+    return make_uint4(__builtin_amdgcn_perm(v.z, v.x, 0x05040100u), __builtin_amdgcn_perm(v.z, v.x, 0x07060302u),
+                      __builtin_amdgcn_perm(v.w, v.y, 0x05040100u), __builtin_amdgcn_perm(v.w, v.y, 0x07060302u));
+}
+
+// the exponent e that puts max|x| (> 0) of a chunk in [2^14, 2^15)
+__device__ __forceinline__ int chunk_exp(float amax)
+{
+    return amax > 0.0f ? 15 - __builtin_amdgcn_frexp_expf(amax) : 0;
+}
+
+// a bf16 pair scaled by 2^e -> fp16 pair (exact for every value down to
+// 2^-32 of the chunk maximum; below, rounded toward zero)
+__device__ __forceinline__ uint32_t bf16_pair_to_f16(uint32_t p, int e)
+{
+    const float a = __builtin_amdgcn_ldexpf(__uint_as_float(p << 16), e);
+    const float b = __builtin_amdgcn_ldexpf(__uint_as_float(p & 0xffff0000u), e);
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+
+__device__ __forceinline__ float bf16_pair_absmax(uint32_t p, float m)
+{
+    return fmaxf(m, fmaxf(fabsf(__uint_as_float(p << 16)), fabsf(__uint_as_float(p & 0xffff0000u))));
+}
 
 // Loop-invariant constants held in VGPRs: a VOP3 and-or on gfx950 takes at
 // most one SGPR/constant operand, so the masks live in registers and the
@@ -133,8 +190,7 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t b)
 }
 
 template <int M>
-__device__ __forceinline__ void q4k_dot(const Chunk<FMT_Q4K> &ck, const XChunk<M> &x, int j, float acc[M],
-                                        const Masks &k)
+__device__ __forceinline__ void q4k_dot(const Chunk<FMT_Q4K> &ck, const XChunk<M> &x, int j, float acc[M])
 {
     const uint32_t sc = __builtin_amdgcn_ubfe(ck.h.y, 4 * j, 4) | (__builtin_amdgcn_ubfe(ck.h.w, 2 * j, 2) << 4);
     const uint32_t mq = __builtin_amdgcn_ubfe(ck.h.z, 4 * j, 4) | (__builtin_amdgcn_ubfe(ck.h.w, 16 + 2 * j, 2) << 4);
@@ -143,19 +199,23 @@ __device__ __forceinline__ void q4k_dot(const Chunk<FMT_Q4K> &ck, const XChunk<M
     const uint32_t w[4] = {ck.c.x, ck.c.y, ck.c.z, ck.c.w};
     uint32_t pr[16];
 #pragma unroll
-    for (int q = 0; q < 4; q++)
-#pragma unroll
-        for (int s = 0; s < 4; s++)
-            pr[4 * q + s] = ((w[q] >> (4 * s)) & k.nib) | 0x43004300u;
+    for (int q = 0; q < 4; q++) {
+        // nibble p of dword q is element 2p (p < 4) or 2(p-4)+1 of its octet:
+        // the bytes of lo are elements 0, 4, 1, 5, those of hi 2, 6, 3, 7
+        const uint32_t lo = w[q] & 0x0F0F0F0Fu, hi = (w[q] >> 4) & 0x0F0F0F0Fu;
+        pr[4 * q + 0] = nib_pair<false>(lo);
+        pr[4 * q + 1] = nib_pair<true>(lo);
+        pr[4 * q + 2] = nib_pair<false>(hi);
+        pr[4 * q + 3] = nib_pair<true>(hi);
+    }
 #pragma unroll
     for (int m = 0; m < M; m++) {
         float d = 0.0f;
 #pragma unroll
         for (int e = 0; e < 16; e++)
             d = dot2(pr[e], x.p[m][e], d);
-        // S*(d - 128*sum x) - Mn*sum x
-        acc[m] = fmaf(S, d - x.s0[m], acc[m]);
-        acc[m] = fmaf(-Mn, x.s1[m], acc[m]);
+        acc[m] = fmaf(S, d, acc[m]);
+        acc[m] = fmaf(-Mn, x.sum[m], acc[m]);
     }
 }
 
@@ -168,16 +228,19 @@ __device__ __forceinline__ void q6k_dot(const Chunk<FMT_Q6K> &ck, const XChunk<M
     const float Sb = d * (float)(int8_t)(ck.sc2 >> 8);
     const uint32_t lw[4] = {ck.lo.x, ck.lo.y, ck.lo.z, ck.lo.w};
     const uint32_t hw[2] = {ck.hi.x, ck.hi.y};
+    const f16x2_t off = {(_Float16)-1056.0f, (_Float16)-1056.0f};
     uint32_t pr[16];
 #pragma unroll
     for (int q = 0; q < 4; q++) {
         const int o = q & 1;
 #pragma unroll
         for (int s = 0; s < 4; s++) {
-            const uint32_t lo = and_or(lw[q] >> (4 * s), k.nib, 0x43004300u);
+            const uint32_t lo = and_or(lw[q] >> (4 * s), k.nib, 0x64006400u);
             const int sh = 8 * o + 2 * s;  // high bits of this pair start at bit sh (and 16+sh)
             const uint32_t h = sh >= 4 ? (hw[q >> 1] >> (sh - 4)) : (hw[q >> 1] << (4 - sh));
-            pr[4 * q + s] = and_or(h, k.hi2, lo);
+            // fp16 1024 + u, then q = u - 32 exactly
+            const uint32_t u = and_or(h, k.hi2, lo);
+            pr[4 * q + s] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, u) + off);
         }
     }
 #pragma unroll
@@ -185,12 +248,11 @@ __device__ __forceinline__ void q6k_dot(const Chunk<FMT_Q6K> &ck, const XChunk<M
         float da = 0.0f, db = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; e++) {
-            da = dot2(pr[e], x.p[m][e], da);
-            db = dot2(pr[8 + e], x.p[m][8 + e], db);
+            da = dot2h(pr[e], x.p[m][e], da);
+            db = dot2h(pr[8 + e], x.p[m][8 + e], db);
         }
-        // stored u = q + 32, so 128 + u = 160 + q
-        acc[m] = fmaf(Sa, da - x.s0[m], acc[m]);
-        acc[m] = fmaf(Sb, db - x.s1[m], acc[m]);
+        // X of this chunk was scaled by 2^e
+        acc[m] += __builtin_amdgcn_ldexpf(fmaf(Sa, da, Sb * db), -x.e[m]);
     }
 }
 
@@ -362,7 +424,7 @@ __device__ __forceinline__ void process_batch(const Batch<FMT, M, CPT, R> &bt, c
 #pragma unroll
         for (int i = 0; i < CPT; i++) {
             if constexpr (FMT == FMT_Q4K)
-                q4k_dot<M>(bt.ck[r][i], xr[i], cj[i], acc, k);
+                q4k_dot<M>(bt.ck[r][i], xr[i], cj[i], acc);
             else if constexpr (FMT == FMT_Q6K)
                 q6k_dot<M>(bt.ck[r][i], xr[i], acc, k);
             else
@@ -431,27 +493,29 @@ __global__ __launch_bounds__(512) void gemv_kernel(Geo g, const uint16_t *__rest
                 if (!live)
                     q[t] = make_uint4(0u, 0u, 0u, 0u);
             }
+            // Q4K: pairs (i, i+4) of each octet and the chunk sum; Q6K: the
+            // chunk scaled by 2^e in fp16; Q8_0: as loaded
+            float amax = 0.0f, sum = 0.0f;
 #pragma unroll
             for (int t = 0; t < 4; t++) {
-                xr[i].p[m][4 * t + 0] = q[t].x;
-                xr[i].p[m][4 * t + 1] = q[t].y;
-                xr[i].p[m][4 * t + 2] = q[t].z;
-                xr[i].p[m][4 * t + 3] = q[t].w;
-            }
-            float s0 = 0.0f, s1 = 0.0f;
+                const uint32_t v[4] = {q[t].x, q[t].y, q[t].z, q[t].w};
 #pragma unroll
-            for (int e = 0; e < 8; e++) {
-                s0 = dot2(xr[i].p[m][e], 0x3F803F80u, s0);
-                s1 = dot2(xr[i].p[m][8 + e], 0x3F803F80u, s1);
+                for (int c = 0; c < 4; c++) {
+                    sum = dot2(v[c], 0x3F803F80u, sum);
+                    amax = bf16_pair_absmax(v[c], amax);
+                }
+                const uint4 o = FMT == FMT_Q4K ? octet_pairs(q[t]) : q[t];
+                xr[i].p[m][4 * t + 0] = o.x;
+                xr[i].p[m][4 * t + 1] = o.y;
+                xr[i].p[m][4 * t + 2] = o.z;
+                xr[i].p[m][4 * t + 3] = o.w;
             }
-            // bias corrections: Q4K s0 = 128*sum, s1 = sum (whole chunk);
-            // Q6K s0/s1 = 160*sum of each half; Q8_0 needs none
+            xr[i].sum[m] = sum;
+            xr[i].e[m] = chunk_exp(amax);
             if constexpr (FMT == FMT_Q6K) {
-                xr[i].s0[m] = 160.0f * s0;
-                xr[i].s1[m] = 160.0f * s1;
-            } else {
-                xr[i].s0[m] = 128.0f * (s0 + s1);
-                xr[i].s1[m] = s0 + s1;
+#pragma unroll
+                for (int e = 0; e < 16; e++)
+                    xr[i].p[m][e] = bf16_pair_to_f16(xr[i].p[m][e], xr[i].e[m]);
             }
         }
     }
@@ -598,14 +662,14 @@ __global__ __launch_bounds__(64 * LW) void gemv_lds_kernel(Geo g, Geo g2, const 
     // the wave's items: (row, chunk) pairs, NI per lane
     constexpr int NI = FS ? (R * FS + 63) / 64 : R * CPT;
     constexpr int SLOTS = 64 * CPT;           // chunk slots per row
-    constexpr bool SUMS = FMT != FMT_Q8_0;    // bias-correction sums (Q4K, Q6K)
+    constexpr bool SUMS = FMT != FMT_Q8_0;    // per-chunk terms: Q4K sum of X, Q6K scale exponent
     constexpr int XU = M * CPT;               // uint4 of X staged per thread
     static_assert(64 * LW * XU == M * 4 * SLOTS, "the workgroup stages every quarter of X exactly once");
     __shared__ uint4 sx[M][4][SLOTS];         // quarter t of chunk c at sx[m][t][c]
-    // chunk sums; the last slot takes the stores of the lanes that own no sum
-    // (stores without branches, so the compiler keeps every X load ahead
-    // of the weight loads instead of sinking them into the branches)
-    __shared__ float2 ss[SUMS ? M : 1][SUMS ? SLOTS + 1 : 1];
+    // per-chunk terms; the last slot takes the stores of the lanes that own
+    // none (stores without branches, so the compiler keeps every X load
+    // ahead of the weight loads instead of sinking them into the branches)
+    __shared__ float ss[SUMS ? M : 1][SUMS ? SLOTS + 1 : 1];
 
     // (the row runs want a wave index the compiler knows to be uniform; the
     // other instances measured faster with the plain one)
@@ -652,27 +716,33 @@ __global__ __launch_bounds__(64 * LW) void gemv_lds_kernel(Geo g, Geo g2, const 
     }
     // keep the staging below (and its wait for X) after every weight load
     __builtin_amdgcn_sched_barrier(0);
-    // stage X and the chunk sums (four consecutive lanes hold one chunk)
+    // stage X and the per-chunk terms (four consecutive lanes hold the four
+    // octets of one chunk)
 #pragma unroll
     for (int j = 0; j < XU; j++) {
         const int u = tid + 64 * LW * j;
         const int m = u / (4 * SLOTS), c = (u >> 2) % SLOTS, t = u & 3;
         const uint32_t keep = c < S ? ~0u : 0u;
         const uint4 v = make_uint4(xs[j].x & keep, xs[j].y & keep, xs[j].z & keep, xs[j].w & keep);
-        sx[m][t][c] = v;
-        if constexpr (SUMS) {
+        if constexpr (FMT == FMT_Q4K) {
+            sx[m][t][c] = octet_pairs(v);
             float p = dot2(v.x, 0x3F803F80u, 0.0f);
             p = dot2(v.y, 0x3F803F80u, p);
             p = dot2(v.z, 0x3F803F80u, p);
             p = dot2(v.w, 0x3F803F80u, p);
-            p += dpp_f<0xB1>(p);  // quarters t, t^1: one 16-element half
-            if constexpr (FMT == FMT_Q4K) {
-                p += dpp_f<0x4E>(p);  // both halves: the chunk
-                ss[m][t == 0 ? c : SLOTS].x = p;
-            } else {
-                // t = 0: the first half (.x), t = 2: the second (.y)
-                reinterpret_cast<float *>(&ss[m][(t & 1) ? SLOTS : c])[t >> 1] = p;
-            }
+            p += dpp_f<0xB1>(p);  // quarters t, t^1
+            p += dpp_f<0x4E>(p);  // all four: the chunk
+            ss[m][t == 0 ? c : SLOTS] = p;
+        } else if constexpr (FMT == FMT_Q6K) {
+            float a = bf16_pair_absmax(v.x, bf16_pair_absmax(v.y, bf16_pair_absmax(v.z, bf16_pair_absmax(v.w, 0.0f))));
+            a = fmaxf(a, dpp_f<0xB1>(a));
+            a = fmaxf(a, dpp_f<0x4E>(a));
+            const int e = chunk_exp(a);
+            sx[m][t][c] = make_uint4(bf16_pair_to_f16(v.x, e), bf16_pair_to_f16(v.y, e), bf16_pair_to_f16(v.z, e),
+                                     bf16_pair_to_f16(v.w, e));
+            ss[m][t == 0 ? c : SLOTS] = __int_as_float(e);
+        } else {
+            sx[m][t][c] = v;
         }
     }
     lds_barrier();
@@ -706,20 +776,15 @@ __global__ __launch_bounds__(64 * LW) void gemv_lds_kernel(Geo g, Geo g2, const 
                 xc.p[m][4 * t + 2] = q.z;
                 xc.p[m][4 * t + 3] = q.w;
             }
-            if constexpr (FMT == FMT_Q4K) {
-                const float tot = ss[m][cx].x;
-                xc.s0[m] = 128.0f * tot;
-                xc.s1[m] = tot;
-            } else if constexpr (FMT == FMT_Q6K) {
-                const float2 h = ss[m][cx];
-                xc.s0[m] = 160.0f * h.x;
-                xc.s1[m] = 160.0f * h.y;
-            }
+            if constexpr (FMT == FMT_Q4K)
+                xc.sum[m] = ss[m][cx];
+            else if constexpr (FMT == FMT_Q6K)
+                xc.e[m] = __float_as_int(ss[m][cx]);
         }
         auto dot = [&](float (&a)[M]) {
             const Chunk<FMT> ck = chunk_of<FMT>(w[i]);
             if constexpr (FMT == FMT_Q4K)
-                q4k_dot<M>(ck, xc, c & 7, a, k);
+                q4k_dot<M>(ck, xc, c & 7, a);
             else if constexpr (FMT == FMT_Q6K)
                 q6k_dot<M>(ck, xc, a, k);
             else

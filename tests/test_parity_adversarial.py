@@ -190,8 +190,6 @@ def test_mfma_i8_adversarial():
         check_outputs(y, Yr, den, f"mfma_i8 X={kind}")
 
 
-@pytest.mark.xfail(strict=False, reason="the GEMV's bias correction sum x*(128+u) - 128*sum x rounds at the "
-                   "scale of the bias; exact codes replace it")
 @pytest.mark.parametrize("fmt", KQ)
 def test_gemv_sparse_rows(fmt):
     """The GEMV on rows whose blocks hold one large weight among tiny ones,
