@@ -196,8 +196,10 @@ int qmatmul(int fmt, const void *blocks, const void *X_bf16, float *Y_fp32, int6
 
 size_t qmatmul_glu_workspace_bytes(int fmt, int64_t M, int64_t F, int64_t K)
 {
+    // every valid shape (check_tensor: K % 256, Q8_0 K % 32) that the fused
+    // kernel does not take needs G in the workspace
     if (!implemented(fmt) || M < 1 || M > QLINEAR_MAX_M || check_tensor(fmt, F, K, QLINEAR_MAX_N) != Q_OK ||
-        K % 256 != 0 || M * F > kMaxElems)
+        M * F > kMaxElems)
         return 0;
     return ql::glu_fused_fits(fmt, (int)M, K) ? 0 : (size_t)(4 * M * F);
 }
@@ -357,7 +359,7 @@ const char *q_strerror(int status)
     switch (status) {
     case Q_OK: return "ok";
     case Q_EINVAL: return "invalid argument (null pointer, unknown format or path, bad workspace)";
-    case Q_ESHAPE: return "shape out of range (M, N, K limits; K must be a multiple of 256)";
+    case Q_ESHAPE: return "shape out of range (M, N, K limits; K a multiple of 256, or of 32 for Q8_0)";
     case Q_EALIGN: return "pointer not 16-byte aligned";
     case Q_ENOTSUP: return "format or path not implemented for these arguments";
     case Q_EHIP: return "HIP runtime error at launch";

@@ -215,3 +215,9 @@ def test_glu_argument_errors_and_workspace_sizes():
     assert ql.glu_workspace_bytes("q4k", 1, 64, 8448) == 4 * 64
     assert ql.glu_workspace_bytes("q8k", 1, 64, 256) == 0
     assert ql.glu_workspace_bytes("q2k", 1, 64, 256) == 4 * 64   # generic formats: two-matmul path
+    # Q8_0 rows ending in a block tail (K % 32) take both paths as well: the
+    # two-matmul path needs its workspace, and an undersized one is refused
+    assert ql.glu_workspace_bytes("q8_0", 5, 64, 4128) == 4 * 5 * 64
+    assert ql.glu_workspace_bytes("q8_0", 2, 64, 4128) == 0      # fused kernel
+    assert call(fmt=0, M=5, K=4128) == ql.Q_EINVAL
+    assert call(fmt=0, M=5, K=4128, ws=A2, wsb=4 * 5 * 64 - 16) == ql.Q_EINVAL
