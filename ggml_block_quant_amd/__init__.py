@@ -29,7 +29,8 @@ FMT_NAME = {v: k for k, v in FMT.items()}
 PATH = {"auto": 0, "gemv": 1, "mfma_bf16": 2, "mfma_i8": 3, "mfma_fp8": 4}
 ACT = {"silu": 0, "relu": 1, "sigmoid": 2}
 
-Q_OK, Q_EINVAL, Q_ESHAPE, Q_EALIGN, Q_ENOTSUP, Q_EHIP = 0, -1, -2, -3, -4, -5
+Q_OK, Q_EINVAL, Q_ESHAPE, Q_EALIGN, Q_ENOTSUP, Q_EHIP, Q_ESCRATCH = 0, -1, -2, -3, -4, -5, -6
+STATIC_SCRATCH_BYTES = 32 << 20  # QLINEAR_STATIC_SCRATCH_BYTES
 
 # every symbol include/qlinear.h declares, with its ctypes signature
 _P, _I64, _INT, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
@@ -41,6 +42,7 @@ SIGNATURES = {
     "qmatmul": (_INT, [_INT, _P, _P, _P, _I64, _I64, _I64, _P]),
     "qmatmul_workspace_bytes": (_SZ, [_INT, _INT, _I64, _I64]),
     "qmatmul_ex": (_INT, [_INT, _P, _P, _P, _I64, _I64, _I64, _INT, _P, _SZ, _P]),
+    "qmatmul_static": (_INT, [_INT, _P, _P, _P, _I64, _I64, _I64, _INT, _P]),
     "q_embed": (_INT, [_INT, _P, _I64, _I64, _P, _I64, _P, _P]),
     "qmatmul_glu_workspace_bytes": (_SZ, [_INT, _I64, _I64, _I64]),
     "qmatmul_glu": (_INT, [_INT, _P, _P, _P, _P, _I64, _I64, _I64, _INT, _P, _SZ, _P]),
@@ -196,6 +198,24 @@ def qmatmul(fmt, blocks: torch.Tensor, X: torch.Tensor, N: int, path="auto",
     _check("qmatmul_ex", lib().qmatmul_ex(_fmt(fmt), _dev(blocks, "blocks", torch.uint8),
                                           _dev(X, "X", torch.bfloat16), _dev(out, "Y", torch.float32),
                                           M, N, K, p, ws_ptr, ws_bytes, _stream()))
+    return out
+
+
+def qmatmul_static(fmt, blocks: torch.Tensor, X: torch.Tensor, N: int, path="auto",
+                   out: torch.Tensor | None = None) -> torch.Tensor:
+    """As ``qmatmul``, with no workspace: the int8 and FP8 paths keep X's
+    activation blocks in the library's fixed per-GPU buffer (calls that
+    overlap in time on one GPU race on it).  With ``out`` given, the call
+    itself allocates nothing."""
+    if X.dim() != 2:
+        raise ValueError("X must be 2-D [M][K]")
+    M, K = X.shape
+    p = PATH[path] if isinstance(path, str) else int(path)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    _check("qmatmul_static", lib().qmatmul_static(_fmt(fmt), _dev(blocks, "blocks", torch.uint8),
+                                                  _dev(X, "X", torch.bfloat16), _dev(out, "Y", torch.float32),
+                                                  M, N, K, p, _stream()))
     return out
 
 

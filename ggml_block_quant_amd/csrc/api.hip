@@ -7,6 +7,9 @@
 
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 namespace {
 
 bool implemented(int fmt)
@@ -70,6 +73,37 @@ int gemv(int fmt, const uint8_t *B, const uint16_t *X, float *Y, int64_t M, int6
             return status_of(e);
     }
     return status_of(ql::launch_gemv(fmt, B, X, Y, (int)M, N, K, s));
+}
+
+// The fixed device buffer of qmatmul_static: one copy per GPU, held until the
+// process ends.  Host code never uses the array's name as an address: the
+// device address of each GPU's copy comes from hipGetSymbolAddress, taken
+// once per device with that device current.
+__device__ __align__(256) uint8_t scratch[QLINEAR_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> scratch_addr[kMaxDevices];
+std::mutex scratch_mu;
+
+int scratch_of_current_device(void **out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return Q_EHIP;
+    if (dev < 0 || dev >= kMaxDevices)
+        return Q_ENOTSUP;
+    void *p = scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(scratch_mu);
+        p = scratch_addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+                return Q_EHIP;
+            scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return Q_OK;
 }
 
 }  // namespace
@@ -192,6 +226,24 @@ int qmatmul(int fmt, const void *blocks, const void *X_bf16, float *Y_fp32, int6
             void *stream)
 {
     return qmatmul_ex(fmt, blocks, X_bf16, Y_fp32, M, N, K, QPATH_AUTO, nullptr, 0, stream);
+}
+
+int qmatmul_static(int fmt, const void *blocks, const void *X_bf16, float *Y_fp32, int64_t M, int64_t N, int64_t K,
+                   int path, void *stream)
+{
+    const int st = matmul_args(fmt, blocks, X_bf16, Y_fp32, M, N, K);
+    if (st != Q_OK)
+        return st;
+    const size_t need = qmatmul_workspace_bytes(fmt, path, M, K);
+    if (need == 0)  // no workspace on this path (or invalid arguments, which qmatmul_ex reports)
+        return qmatmul_ex(fmt, blocks, X_bf16, Y_fp32, M, N, K, path, nullptr, 0, stream);
+    if (need > QLINEAR_STATIC_SCRATCH_BYTES)
+        return Q_ESCRATCH;
+    void *ws = nullptr;
+    const int sst = scratch_of_current_device(&ws);
+    if (sst != Q_OK)
+        return sst;
+    return qmatmul_ex(fmt, blocks, X_bf16, Y_fp32, M, N, K, path, ws, need, stream);
 }
 
 size_t qmatmul_glu_workspace_bytes(int fmt, int64_t M, int64_t F, int64_t K)
@@ -363,6 +415,7 @@ const char *q_strerror(int status)
     case Q_EALIGN: return "pointer not 16-byte aligned";
     case Q_ENOTSUP: return "format or path not implemented for these arguments";
     case Q_EHIP: return "HIP runtime error at launch";
+    case Q_ESCRATCH: return "activation blocks larger than the library's fixed scratch buffer (QLINEAR_STATIC_SCRATCH_BYTES)";
     default: return "unknown status";
     }
 }

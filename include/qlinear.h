@@ -107,7 +107,8 @@ enum {
     Q_ESHAPE = -2,  /* M, N, K out of range or K not a multiple of 256 (Q8_0: 32) */
     Q_EALIGN = -3,  /* a pointer is not 16-byte aligned */
     Q_ENOTSUP = -4, /* format or path not implemented for these arguments */
-    Q_EHIP = -5     /* the HIP runtime refused a launch or a query */
+    Q_EHIP = -5,    /* the HIP runtime refused a launch or a query */
+    Q_ESCRATCH = -6 /* qmatmul_static: the activation blocks exceed the fixed buffer */
 };
 
 /* Largest accepted dimension values (element counts N*K and M*K must also
@@ -180,6 +181,24 @@ size_t qmatmul_workspace_bytes(int fmt, int path, int64_t M, int64_t K);
 int qmatmul_ex(int fmt, const void *blocks, const void *X_bf16, float *Y_fp32, int64_t M,
                int64_t N, int64_t K, int path, void *workspace, size_t workspace_bytes,
                void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): qmatmul_ex
+ * without a caller workspace.  QPATH_MFMA_I8 and QPATH_MFMA_FP8 keep X's
+ * activation blocks in a buffer of QLINEAR_STATIC_SCRATCH_BYTES that the
+ * library holds in device memory, one per GPU, from the first such call on
+ * that GPU (with that GPU current, hipGetDevice) until the process ends;
+ * a call whose qmatmul_workspace_bytes exceeds it returns Q_ESCRATCH before
+ * anything is launched.  The buffer is fully rewritten by each call that
+ * uses it (nothing in it needs to start at zero), and every call on one
+ * GPU shares it: calls whose work overlaps in time on one GPU (different
+ * streams, or no ordering between host threads) race; calls on one stream
+ * are ordered.  The other paths need no workspace and run as in qmatmul_ex.
+ * Nothing is allocated by the call itself; the stream must belong to the
+ * current device. */
+#define QLINEAR_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+int qmatmul_static(int fmt, const void *blocks, const void *X_bf16, float *Y_fp32, int64_t M,
+                   int64_t N, int64_t K, int path, void *stream);
 
 /* Gated feed-forward projection (page "Quantization types", section
  * "NVFP4": compatible gated feed-forward projections fuse the activation

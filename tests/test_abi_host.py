@@ -95,6 +95,7 @@ def test_supported_formats():
     assert ql.fmt_supported("fp8")
     for s in range(-6, 1):
         assert L.q_strerror(s)
+    assert b"scratch" in L.q_strerror(ql.Q_ESCRATCH)
 
 
 A = ctypes.c_void_p(0x10000)     # 16-byte aligned, never dereferenced
@@ -165,6 +166,32 @@ def test_qmatmul_argument_errors():
     assert L.qmatmul_workspace_bytes(0, 3, 4, 256) > 0
     assert L.qmatmul(1, A, A2, NULL, 4, 64, 256, NULL) == ql.Q_EINVAL
     assert ok
+
+
+def test_qmatmul_static_argument_errors():
+    """The no-allocation entry point checks its arguments like qmatmul_ex and
+    refuses activation blocks larger than its fixed buffer, all before any
+    HIP call (the pointers are never dereferenced)."""
+    L = ql.lib()
+
+    def call(fmt=0, b=A, x=A2, y=A3, M=4, N=64, K=256, path=3):
+        return L.qmatmul_static(fmt, b, x, y, M, N, K, path, NULL)
+
+    assert call(b=NULL) == ql.Q_EINVAL
+    assert call(x=NULL) == ql.Q_EINVAL
+    assert call(y=MIS) == ql.Q_EALIGN
+    assert call(fmt=13) == ql.Q_EINVAL
+    assert call(K=100) == ql.Q_ESHAPE
+    assert call(M=0) == ql.Q_ESHAPE
+    assert call(fmt=1, path=3) == ql.Q_ENOTSUP          # int8 path: Q8_0 weights only
+    assert call(K=96) == ql.Q_ESHAPE                     # int8 path: K % 256
+    assert call(path=9) == ql.Q_EINVAL
+    assert call(fmt=0, path=1, M=9) == ql.Q_ESHAPE      # GEMV: M <= 8
+    # the activation blocks of 8192 x 4096 (35.7 MB) exceed the 32 MiB buffer
+    assert ql.workspace_bytes("q8_0", "mfma_i8", 8192, 4096) > ql.STATIC_SCRATCH_BYTES
+    assert call(M=8192, K=4096) == ql.Q_ESCRATCH
+    assert call(fmt=12, path=4, M=8192, K=4096) == ql.Q_ESCRATCH
+    assert ql.workspace_bytes("q8_0", "mfma_i8", 7680, 4096) <= ql.STATIC_SCRATCH_BYTES
 
 
 def test_embed_argument_errors():
