@@ -497,7 +497,7 @@ __device__ __forceinline__ int pslot(int row, int c) { return row * 4 + (c ^ ((r
 //         9216 + 4r
 template <int FMT> struct PRaw;
 // (vpm: decode VALU instructions scheduled per MFMA)
-template <> struct PRaw<FMT_Q8_0> { static constexpr int bytes = 9216, wd = 3, vpm = 12; };
+template <> struct PRaw<FMT_Q8_0> { static constexpr int bytes = 9216, wd = 3, vpm = 8; };
 template <> struct PRaw<FMT_Q4K> { static constexpr int bytes = 8192, wd = 2, vpm = 12; };
 template <> struct PRaw<FMT_Q6K> { static constexpr int bytes = 10240, wd = 4, vpm = 13; };
 
@@ -529,12 +529,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const uint8_t *__restrict__ B, int64_t sc_off, int64_t d_off, const uint16_t *__restrict__ X,
     float *__restrict__ Y, int M, int N, int K, int slabs_per_split)
 {
+    // Q8_0: the W stage holds the codes (exact in bf16) and the block scale
+    // enters through a running rescale of the accumulators; the K-quants:
+    // each weight as a bf16 hi + lo pair (two W stages)
+    constexpr bool CODE = FMT == FMT_Q8_0;
+    constexpr int NWS = CODE ? 1 : 2;                      // bf16 W planes per stage
     constexpr int RAWB = PRaw<FMT>::bytes;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[PNX * PSTAGE + 2 * PNW * PSTAGE + PNR * RAWB];
+    constexpr int RHO = CODE ? (PNW + 1) * 256 * 4 : 0;   // rescale factors per stage, final scales
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[PNX * PSTAGE + NWS * PNW * PSTAGE + PNR * RAWB + RHO];
     uint8_t *const sx = smem;
-    uint8_t *const sw = smem + PNX * PSTAGE;               // hi parts of the decoded W
-    uint8_t *const swl = smem + (PNX + PNW) * PSTAGE;      // lo parts
-    uint8_t *const sr = smem + (PNX + 2 * PNW) * PSTAGE;
+    uint8_t *const sw = smem + PNX * PSTAGE;               // hi parts of the decoded W (Q8_0: codes)
+    uint8_t *const swl = smem + (PNX + PNW) * PSTAGE;      // lo parts (K-quants)
+    uint8_t *const sr = smem + (PNX + NWS * PNW) * PSTAGE;
+    float *const srho = reinterpret_cast<float *>(sr + PNR * RAWB);  // [PNW + 1][256]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave & 1, wn = wave >> 1;  // 2 x 4 waves of 128 x 64
 
@@ -621,6 +628,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
         return w;
     };
+    // Q8_0 running scale of row tid: the block scale of the latest slab that
+    // has one (a block of zeros, d = 0, keeps the previous scale)
+    float e_run = 1.0f;
     auto decode = [&](int s, WBlk<FMT> w) {
         // pick the 16-bit halves out of the dwords the loads brought
         if constexpr (FMT == FMT_Q8_0) {
@@ -630,13 +640,32 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const int64_t grp = nd * (K / 256) + (s >> 3);
             w.d = (grp & 1) ? w.d >> 16 : w.d & 0xffffu;
         }
-        uint32_t vh[16], vl[16];
-        decode_wblk<FMT>(w, s, vh, vl);
         uint8_t *wh = sw + (s % PNW) * PSTAGE, *wl = swl + (s % PNW) * PSTAGE;
+        if constexpr (CODE) {
+            // the 32 codes as bf16 (exact), and the factor that takes the
+            // accumulators from the previous slab's scale to this one's
+            const uint32_t v[8] = {w.c0.x, w.c0.y, w.c0.z, w.c0.w, w.c1.x, w.c1.y, w.c1.z, w.c1.w};
+            uint32_t vh[16];
 #pragma unroll
-        for (int c = 0; c < 4; c++) {
-            *reinterpret_cast<uint4 *>(wh + 16 * pslot(tid, c)) = make_uint4(vh[4 * c], vh[4 * c + 1], vh[4 * c + 2], vh[4 * c + 3]);
-            *reinterpret_cast<uint4 *>(wl + 16 * pslot(tid, c)) = make_uint4(vl[4 * c], vl[4 * c + 1], vl[4 * c + 2], vl[4 * c + 3]);
+            for (int i = 0; i < 8; i++) {
+                vh[2 * i] = pack_bf16((float)(int8_t)(v[i]), (float)(int8_t)(v[i] >> 8));
+                vh[2 * i + 1] = pack_bf16((float)(int8_t)(v[i] >> 16), (float)(int8_t)(v[i] >> 24));
+            }
+#pragma unroll
+            for (int c = 0; c < 4; c++)
+                *reinterpret_cast<uint4 *>(wh + 16 * pslot(tid, c)) = make_uint4(vh[4 * c], vh[4 * c + 1], vh[4 * c + 2], vh[4 * c + 3]);
+            const float dn = h2f(w.d);
+            const float en = dn != 0.0f ? dn : e_run;
+            srho[(s % PNW) * 256 + tid] = e_run / en;  // IEEE division
+            e_run = en;
+        } else {
+            uint32_t vh[16], vl[16];
+            decode_wblk<FMT>(w, s, vh, vl);
+#pragma unroll
+            for (int c = 0; c < 4; c++) {
+                *reinterpret_cast<uint4 *>(wh + 16 * pslot(tid, c)) = make_uint4(vh[4 * c], vh[4 * c + 1], vh[4 * c + 2], vh[4 * c + 3]);
+                *reinterpret_cast<uint4 *>(wl + 16 * pslot(tid, c)) = make_uint4(vl[4 * c], vl[4 * c + 1], vl[4 * c + 2], vl[4 * c + 3]);
+            }
         }
     };
 
@@ -651,6 +680,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int j = 0; j < 2; j++)
             offb[j][kk] = 16 * pslot(64 * wn + 32 * j + r32, 2 * kk + kh);
     }
+    // Q8_0: rescale factors of the lane's two columns for the next slab
+    float rho[2] = {1.0f, 1.0f};
     auto frags = [&](int s, int kk, bf16x8_t (&af)[4], bf16x8_t (&bw)[4]) {
         const uint8_t *xs = sx + (s % PNX) * PSTAGE, *ws = sw + (s % PNW) * PSTAGE, *wl = swl + (s % PNW) * PSTAGE;
 #pragma unroll
@@ -659,7 +690,30 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int j = 0; j < 2; j++) {
             bw[j] = *reinterpret_cast<const bf16x8_t *>(ws + offb[j][kk]);
-            bw[2 + j] = *reinterpret_cast<const bf16x8_t *>(wl + offb[j][kk]);
+            if constexpr (!CODE)
+                bw[2 + j] = *reinterpret_cast<const bf16x8_t *>(wl + offb[j][kk]);
+        }
+        if constexpr (CODE) {
+            if (kk == 0) {
+#pragma unroll
+                for (int j = 0; j < 2; j++)
+                    rho[j] = srho[(s % PNW) * 256 + 64 * wn + 32 * j + r32];
+            }
+        }
+    };
+    // one output tile's k-step: Q8_0 one MFMA on the codes, the K-quants two
+    // (hi and lo parts of the weights)
+    auto mfma = [&](f32x16_t &c, const bf16x8_t &a, const bf16x8_t (&bw)[4], int j) {
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bw[j], c, 0, 0, 0);
+        if constexpr (!CODE)
+            c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bw[2 + j], c, 0, 0, 0);
+    };
+    // Q8_0: the accumulators of a tile, from the previous slab's scale to this slab's
+    auto rescale = [&](f32x16_t &c, int j) {
+        if constexpr (CODE) {
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+                c[r] *= rho[j];
         }
     };
 
@@ -695,8 +749,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     auto body = [&](int s, auto steady, auto decoder) {
         constexpr bool ST = decltype(steady)::value, DEC = decltype(decoder)::value;
         const bool dec = ST || s + 1 < se;
-        acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[0], b0[0], acc[0][0], 0, 0, 0);
-        acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[0], b0[2], acc[0][0], 0, 0, 0);
+        rescale(acc[0][0], 0);
+        mfma(acc[0][0], a0[0], b0, 0);
         __builtin_amdgcn_sched_barrier(0);
         WBlk<FMT> w{};
         if (DEC && dec)
@@ -710,13 +764,27 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
             for (int j = 0; j < 2; j++)
                 if (i + j > 0) {
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], b0[j], acc[i][j], 0, 0, 0);
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], b0[2 + j], acc[i][j], 0, 0, 0);
+                    rescale(acc[i][j], j);
+                    mfma(acc[i][j], a0[i], b0, j);
                 }
-        if constexpr (DEC) {
+        if constexpr (CODE) {
+            // Q8_0: each MFMA of this k-step follows the 16 multiplies that
+            // rescale its tile, so that one tile's MFMA runs while the next
+            // tile is rescaled; the decoding waves add a share of the next
+            // slab's decode to each group
+#pragma unroll
+            for (int q = 0; q < 7; q++) {
+                __builtin_amdgcn_sched_group_barrier(0x002, 16 + (DEC ? PRaw<FMT>::vpm : 0), 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            }
+            if constexpr (DEC)
+                __builtin_amdgcn_sched_group_barrier(0x200, 4, 0);
+        } else if constexpr (DEC) {
+            // MFMAs of this k-step after the first, each followed by a share
+            // of the next slab's decode
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 #pragma unroll
-            for (int q = 0; q < 13; q++) {
+            for (int q = 0; q < 14; q++) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x002, PRaw<FMT>::vpm, 0);
             }
@@ -737,10 +805,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int i = 0; i < 4; i++)
 #pragma unroll
-            for (int j = 0; j < 2; j++) {
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], b1[j], acc[i][j], 0, 0, 0);
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], b1[2 + j], acc[i][j], 0, 0, 0);
-            }
+            for (int j = 0; j < 2; j++)
+                mfma(acc[i][j], a1[i], b1, j);
         __builtin_amdgcn_sched_barrier(0);
     };
     auto run = [&](auto decoder) {
@@ -755,6 +821,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     else
         run(std::false_type{});
 
+    // Q8_0: the accumulators hold the sums in units of the last slab's
+    // scale of each row; multiply it back
+    float eout[2] = {1.0f, 1.0f};
+    if constexpr (CODE) {
+        if (wv < 4)
+            srho[PNW * 256 + tid] = e_run;
+        lds_barrier();
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+            eout[j] = srho[PNW * 256 + 64 * wn + 32 * j + r32];
+    }
+
     // lane holds D[m = 8*(r/4) + 4*(lane/32) + r%4][n = lane%32] of each tile
     const bool split = gridDim.y > 1;
 #pragma unroll
@@ -765,11 +843,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
             for (int r = 0; r < 16; r++) {
                 const int m = m0 + 128 * wm + 32 * i + 8 * (r / 4) + 4 * kh + (r % 4);
+                const float v = CODE ? acc[i][j][r] * eout[j] : acc[i][j][r];
                 if (m < M && n < N) {
                     if (split)
-                        atomicAdd(Y + (int64_t)m * N + n, acc[i][j][r]);
+                        atomicAdd(Y + (int64_t)m * N + n, v);
                     else
-                        Y[(int64_t)m * N + n] = acc[i][j][r];
+                        Y[(int64_t)m * N + n] = v;
                 }
             }
         }

@@ -168,8 +168,10 @@ __device__ __forceinline__ float bf16_pair_absmax(uint32_t p, float m)
 // most one SGPR/constant operand, so the masks live in registers and the
 // bias in an SGPR, which gives one v_and_or_b32 per bf16 pair.
 struct Masks {
-    uint32_t nib;  // 0x000F000F
-    uint32_t hi2;  // 0x00300030
+    uint32_t nib;     // 0x000F000F
+    uint32_t hi2;     // 0x00300030
+    uint32_t nibx16;  // 0x00F000F0
+    uint32_t hi2x16;  // 0x03000300
 };
 
 __device__ __forceinline__ Masks make_masks()
@@ -177,6 +179,8 @@ __device__ __forceinline__ Masks make_masks()
     Masks k;
     asm volatile("v_mov_b32 %0, 0x000f000f" : "=v"(k.nib));
     asm volatile("v_mov_b32 %0, 0x00300030" : "=v"(k.hi2));
+    asm volatile("v_mov_b32 %0, 0x00f000f0" : "=v"(k.nibx16));
+    asm volatile("v_mov_b32 %0, 0x03000300" : "=v"(k.hi2x16));
     return k;
 }
 
@@ -219,6 +223,13 @@ __device__ __forceinline__ void q4k_dot(const Chunk<FMT_Q4K> &ck, const XChunk<M
     }
 }
 
+// Q6K codes of one chunk: dword q of the low nibbles holds octet q (nibble
+// s: element 2s, nibble s + 4: element 2s + 1); the two high bits of the
+// pair s of octet q sit at bit 8(q & 1) + 2s (and 16 + that) of high-bit
+// dword q / 2.  Pairs s = 0, 2 take the nibble at bits 0-3 of lw (s = 2:
+// lw >> 8) and the high bits at 4-5 -- fp16 1024 + u; pairs s = 1, 3 take it
+// at bits 4-7 and the high bits at 8-9 -- fp16 1024 + 16 u -- which saves
+// a shift of lw per pair.  v_pk_add_f16 then leaves q or 16 q exactly.
 template <int M>
 __device__ __forceinline__ void q6k_dot(const Chunk<FMT_Q6K> &ck, const XChunk<M> &x, float acc[M],
                                         const Masks &k)
@@ -228,29 +239,39 @@ __device__ __forceinline__ void q6k_dot(const Chunk<FMT_Q6K> &ck, const XChunk<M
     const float Sb = d * (float)(int8_t)(ck.sc2 >> 8);
     const uint32_t lw[4] = {ck.lo.x, ck.lo.y, ck.lo.z, ck.lo.w};
     const uint32_t hw[2] = {ck.hi.x, ck.hi.y};
-    const f16x2_t off = {(_Float16)-1056.0f, (_Float16)-1056.0f};
+    const f16x2_t off1 = {(_Float16)-1056.0f, (_Float16)-1056.0f};   // 1024 + u   -> q
+    const f16x2_t off16 = {(_Float16)-1536.0f, (_Float16)-1536.0f};  // 1024 + 16u -> 16 q
+    auto shl = [](uint32_t v, int n) { return n >= 0 ? v << n : v >> -n; };
     uint32_t pr[16];
 #pragma unroll
     for (int q = 0; q < 4; q++) {
-        const int o = q & 1;
-#pragma unroll
-        for (int s = 0; s < 4; s++) {
-            const uint32_t lo = and_or(lw[q] >> (4 * s), k.nib, 0x64006400u);
-            const int sh = 8 * o + 2 * s;  // high bits of this pair start at bit sh (and 16+sh)
-            const uint32_t h = sh >= 4 ? (hw[q >> 1] >> (sh - 4)) : (hw[q >> 1] << (4 - sh));
-            // fp16 1024 + u, then q = u - 32 exactly
-            const uint32_t u = and_or(h, k.hi2, lo);
-            pr[4 * q + s] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, u) + off);
-        }
+        const int o = 8 * (q & 1);
+        const uint32_t l01 = lw[q], l23 = lw[q] >> 8, H = hw[q >> 1];
+        const uint32_t u0 = and_or(shl(H, 4 - o), k.hi2, and_or(l01, k.nib, 0x64006400u));
+        const uint32_t u1 = and_or(shl(H, 6 - o), k.hi2x16, and_or(l01, k.nibx16, 0x64006400u));
+        const uint32_t u2 = and_or(shl(H, 0 - o), k.hi2, and_or(l23, k.nib, 0x64006400u));
+        const uint32_t u3 = and_or(shl(H, 2 - o), k.hi2x16, and_or(l23, k.nibx16, 0x64006400u));
+        pr[4 * q + 0] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, u0) + off1);
+        pr[4 * q + 1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, u1) + off16);
+        pr[4 * q + 2] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, u2) + off1);
+        pr[4 * q + 3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, u3) + off16);
     }
 #pragma unroll
     for (int m = 0; m < M; m++) {
-        float da = 0.0f, db = 0.0f;
+        // sub-block a (octets 0, 1) and b (octets 2, 3); the pairs holding
+        // 16 q in their own sums
+        float a1 = 0.0f, a16 = 0.0f, b1 = 0.0f, b16 = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 8; e++) {
-            da = dot2h(pr[e], x.p[m][e], da);
-            db = dot2h(pr[8 + e], x.p[m][8 + e], db);
+        for (int q = 0; q < 2; q++) {
+#pragma unroll
+            for (int s = 0; s < 4; s += 2) {
+                a1 = dot2h(pr[4 * q + s], x.p[m][4 * q + s], a1);
+                a16 = dot2h(pr[4 * q + s + 1], x.p[m][4 * q + s + 1], a16);
+                b1 = dot2h(pr[8 + 4 * q + s], x.p[m][8 + 4 * q + s], b1);
+                b16 = dot2h(pr[8 + 4 * q + s + 1], x.p[m][8 + 4 * q + s + 1], b16);
+            }
         }
+        const float da = fmaf(a16, 0.0625f, a1), db = fmaf(b16, 0.0625f, b1);
         // X of this chunk was scaled by 2^e
         acc[m] += __builtin_amdgcn_ldexpf(fmaf(Sa, da, Sb * db), -x.e[m]);
     }
