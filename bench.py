@@ -1,27 +1,42 @@
 """Benchmark of the block-quantized linear layer on one MI355X.
 
-Headline step: one decode step of a quantized projection -- the fused
-dequant-GEMV of a Q4K weight at the FFN up-projection shape (N = 14336,
-K = 4096, M = 1 token), weights already quantized (ISQ) and resident in HBM.
-`value` is quantized-weight GB/s: weight bytes per step / time per step.
-Each step reads a different copy of the weights (enough copies to exceed
-twice the 256 MiB Infinity Cache), so the bytes come from HBM.  Launches are
-captured in a HIP graph (kernels are warmed before capture) so that host
-launch cost does not enter a 4-microsecond kernel's time.
+Headline (the largest configuration): the quantized GEMV of the output head of
+a 32-layer decoder -- a 131072 x 5120 weight, promoted from the model's Q4K to
+Q6K by the sensitive-tensor policy (page "Quantization types", section
+"Sensitive tensor precision") -- for one token, after ISQ of the whole
+decoder to Q4K and of the head to Q6K.  One step is one launch of that GEMV
+with its blocks resident in HBM; two copies alternate, and at 550 MB each is
+larger than the 256 MiB Infinity Cache, so every step streams its weights
+from HBM.  value = weight bytes per step / time per step (GB/s).
 
-The same run also measures, as "parts": the Q8_0 variant of the headline
-GEMV, batched decode (M = 4/16/64, K = 14336, N = 4096, Q4K with outliers),
-prefill (M = 2048, K = 4096, N = 14336, Q8_0 weights) on the bf16 MFMA and
-the int8 MFMA paths, ISQ of a 32-layer decoder to Q4K plus its 131072 x 5120
-output head to Q6K, the output head GEMV at M = 1 and 8, and the equivalent
-decode tokens/s of that decoder (all 224 projection GEMVs plus the head).
-Parity with the CPU oracle is checked in the same run before timing.
+The same run measures, each with its own roofline block:
+  * the Q8_0 GEMV 1024 x 1024 (latency; cache-resident), the Q4K and Q8_0
+    GEMVs at 14336 x 4096 (one token);
+  * batched decode, Q4K 4096 x 14336 with 1 % outliers, 4 / 16 / 64 tokens;
+  * prefill 2048 x 4096 x 14336 with Q8_0 weights on the bf16 MFMA path and
+    on the int8 path (activation quantization included), and FP8 W8A8 at the
+    same shape;
+  * ISQ of the whole decoder and head; the head GEMV for eight tokens;
+  * equivalent decode tokens/s of the decoder (every projection GEMV of the
+    32 layers plus the head, with q/k/v as one concatenated launch and
+    gate/up as one fused SiLU launch);
+  * two ceilings: a streaming read of a buffer read once per launch, and an
+    MFMA-only loop.
+Timing (page "Quantization types", section "NVFP4": kernels warmed up before
+graph capture, outputs checked, median latency reported): parity with the
+CPU oracle first (codes bit-exact, outputs within 1e-3 of sum |w||x| on
+sampled outputs); W untimed launches; then a HIP graph of the launches,
+replayed at least 10 times, each replay timed with HIP events on the stream
+the launches go to; median, p10 and p90 per launch.  The oracle is also
+timed on the host cores (cpu_baseline).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--reps R]
+                       [--parts list] [--quick] [--no-cpu]
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -39,6 +54,14 @@ INT8_PEAK_TOPS = 5000.0       # dense MFMA int8, published
 FP8_PEAK_TFLOPS = 5000.0      # dense MFMA fp8, published
 MALL_BYTES = 256 << 20        # Infinity Cache
 
+HEAD_N, HEAD_K = 131072, 5120
+DECODER_SHAPES = [(4096, 4096), (1024, 4096), (1024, 4096), (4096, 4096), (14336, 4096), (14336, 4096),
+                  (4096, 14336)]  # q, k, v, o, gate, up, down: [out][in]
+ALL_PARTS = ("gemv", "batched", "prefill", "model", "ceilings", "crossover", "glu")
+
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gemv_q6k_131072x5120_m1_traffic.md")
+TRAFFIC_SOURCES = [os.path.join(ROOT, "ggml_block_quant_amd", "csrc", f) for f in ("gemv.hip", "qlinear_internal.h")]
+
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
@@ -47,29 +70,24 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=20, help="launches per timed graph replay (headline)")
+    ap.add_argument("--warmup", type=int, default=5, help="untimed launches before capture")
+    ap.add_argument("--reps", type=int, default=10, help="timed replays (at least 10)")
+    ap.add_argument("--parts", default=None, help="comma-separated: " + ",".join(ALL_PARTS) + " (default: all)")
     ap.add_argument("--quick", action="store_true", help="headline only (for profiling runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--parts", default=None,
-                    help="comma-separated parts measured after the headline: batched, glu, formats, fp8, prefill, isq "
-                         "(default: all of them, none with --quick)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only copy a buffer of BYTES bytes 10 times (the reference kernel that scales "
                          "the FETCH_SIZE / WRITE_SIZE counters), then exit")
-    return ap.parse_args()
-
-
-TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gemv_q4k_14336x4096_m1_traffic.md")
-TRAFFIC_SOURCES = [os.path.join(ROOT, "ggml_block_quant_amd", "csrc", f) for f in ("gemv.hip", "qlinear_internal.h")]
+    a = ap.parse_args()
+    a.reps = max(10, a.reps)
+    return a
 
 
 def measured_traffic():
     """HBM bytes per launch of the headline GEMV from the committed FETCH_SIZE /
     WRITE_SIZE counter record, scaled by the copy-probe factors it states; None
     when there is no record or the kernel's sources changed since it was taken."""
-    import hashlib
-
     try:
         rec = {}
         for line in open(TRAFFIC_RECORD):
@@ -89,65 +107,103 @@ def measured_traffic():
 
 
 def copies_for(nbytes: int) -> int:
+    """Distinct weight copies rotated so that each launch reads HBM, not the
+    Infinity Cache (twice its size in total)."""
     return max(2, math.ceil(2 * MALL_BYTES / nbytes))
 
 
-class Timer:
-    """HIP events on the current stream (the stream every launch uses)."""
+def stats(per_launch_ms):
+    a = np.sort(np.asarray(per_launch_ms, np.float64))
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)), "p90": float(np.percentile(a, 90)),
+            "n": int(a.size)}
 
-    def __init__(self, torch):
+
+class Runner:
+    """Graph capture and timed replays on the current stream."""
+
+    def __init__(self, torch, reps):
         self.t = torch
-        self.a = torch.cuda.Event(enable_timing=True)
-        self.b = torch.cuda.Event(enable_timing=True)
+        self.reps = reps
 
-    def __enter__(self):
-        self.t.cuda.synchronize()
-        self.a.record()
-        return self
-
-    def __exit__(self, *exc):
-        self.b.record()
-        self.t.cuda.synchronize()
-        self.ms = self.a.elapsed_time(self.b)
-
-
-def graph_of(torch, launch, n):
-    """Capture n calls launch(i) in one HIP graph (after eager warm-up)."""
-    launch(0)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        with torch.cuda.graph(g, stream=s):
-            for i in range(n):
-                launch(i)
-    torch.cuda.current_stream().wait_stream(s)
-    torch.cuda.synchronize()
-    return g
-
-
-def time_graph(torch, g, reps, calls_per_replay, warm_s=0.1):
-    """Average time per call over `reps` replays, after replaying for at
-    least `warm_s` seconds (the GPU clocks settle under sustained load)."""
-    t0 = time.perf_counter()
-    g.replay()
-    torch.cuda.synchronize()
-    while time.perf_counter() - t0 < warm_s:
-        g.replay()
+    def graph(self, launch, n):
+        torch = self.t
         torch.cuda.synchronize()
-    with Timer(torch) as t:
-        for _ in range(reps):
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for i in range(n):
+                    launch(i)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        return g
+
+    def time(self, launch, n, warmup=3, settle_s=0.1):
+        """Per-launch times (ms) of `reps` replays of a graph of n launches,
+        after `warmup` eager launches and replays for `settle_s` seconds."""
+        torch = self.t
+        for i in range(warmup):
+            launch(i)
+        g = self.graph(launch, n)
+        t0 = time.perf_counter()
+        while True:
             g.replay()
-    return t.ms / (reps * calls_per_replay)
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 > settle_s:
+                break
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(self.reps)]
+        s = torch.cuda.current_stream()
+        torch.cuda.synchronize()
+        for a, b in evs:
+            a.record(s)
+            g.replay()
+            b.record(s)
+        torch.cuda.synchronize()
+        return stats([a.elapsed_time(b) / n for a, b in evs])
+
+
+def roof(bound, units, t, peak, unit, kernel, traffic=None, note=None):
+    """Roofline block: `units` algorithmic bytes (GB/s) or FLOP/OP (TFLOP/s)
+    per launch over the median launch time (ms)."""
+    scale = 1e6 if unit == "GB/s" else 1e9
+    ach = units / t["median"] / scale
+    d = {"bound": bound, "achieved": round(ach, 1), "peak": peak, "unit": unit, "frac": round(ach / peak, 4),
+         "traffic": traffic, "kernel": kernel,
+         ("alg_bytes_per_launch" if unit == "GB/s" else "alg_ops_per_launch"): int(units),
+         "us_median": round(t["median"] * 1e3, 3), "us_p10": round(t["p10"] * 1e3, 3),
+         "us_p90": round(t["p90"] * 1e3, 3), "replays": t["n"]}
+    if note:
+        d["note"] = note
+    return d
+
+
+def sample_rows(N, count, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return np.unique(np.concatenate([[0, N - 1], rng.choice(N, min(N, count), replace=False)]))
+
+
+def check_gemv_rows(ql, fmt, w_rows, rows, blocks, N, K, x, y, label, isq_exact=True):
+    """ISQ bytes of the sampled rows bit-exact and outputs within the bar."""
+    import oracle
+
+    f = oracle.quantize(fmt, w_rows)
+    if isq_exact:
+        got = oracle.rows_of_buffer(fmt, blocks.cpu().numpy(), N, K, rows)
+        if not np.array_equal(got, oracle.pack(fmt, f, len(rows), K)):
+            raise SystemExit(f"parity failure: {label}: ISQ bytes differ from the oracle")
+    Yr, den = oracle.matmul_a16(oracle.dequant(fmt, f, len(rows), K), x)
+    e = float(oracle.normalized_error(y[:, rows], Yr, den).max())
+    if e > 1e-3:
+        raise SystemExit(f"parity failure: {label}: error {e:.3e}")
+    return e
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this library has no multi-GPU path "
-              "(sharding is described in the design notes, not built). Use --gpus 1.",
-              file=sys.stderr)
+        print("bench.py measures one GPU: this library has no multi-GPU path (how it would shard is "
+              "described in the design notes, not built).  Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -169,437 +225,555 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": args.copy_probe, "launches": 10}))
         return
-    result = {}
+    run = Runner(torch, args.reps)
 
     def bf16_dev(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    # ------------------------------------------------------------------
-    # headline: Q4K GEMV, N=14336, K=4096, M=1, cold weights
-    # ------------------------------------------------------------------
-    N, K, M = 14336, 4096, 1
-    log("headline: generating 14336x4096 weights and quantizing")
-    w = synth.weights_bf16(synth.seed_for(2, 0), N, K)
-    x = synth.activations_bf16(synth.seed_for(2, 1), M, K)
-    W = bf16_dev(w)
-    X = bf16_dev(x)
-    parts = {}
-    head = {}
-    for fmt in ("q4k", "q8_0"):
-        blocks = ql.isq(fmt, W)
-        nb = blocks.numel()
-        R = copies_for(nb)
-        copies = [blocks] + [blocks.clone() for _ in range(R - 1)]
-        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
-        # parity on the live buffers (oracle on 256 sampled rows)
-        parity = check_gemv_parity(ql, fmt, w, x, blocks, Y, N)
+    def host_rows(W, rows):
+        return W[torch.from_numpy(rows).to(dev)].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
-        def launch(i, fmt=fmt, copies=copies, Y=Y):
-            ql.qmatmul(fmt, copies[i % len(copies)], X, N, out=Y)
+    # ------------------------------------------------------------------
+    # headline: the Q6K head GEMV, M = 1
+    # ------------------------------------------------------------------
+    log(f"headline: head {HEAD_N}x{HEAD_K} to q6k, GEMV M=1")
+    Wh = synth.device_normal_bf16(synth.LM_HEAD_W_SEED, (HEAD_N, HEAD_K), synth.W_SIGMA)
+    Bh = ql.isq("q6k", Wh)
+    xh = synth.activations_bf16(synth.LM_HEAD_X_SEED, 8, HEAD_K)
+    Xh = bf16_dev(xh)
+    rows = sample_rows(HEAD_N, 256, 12)
+    wrows = host_rows(Wh, rows)
+    Y1 = torch.empty((1, HEAD_N), dtype=torch.float32, device=dev)
+    ql.qmatmul("q6k", Bh, Xh[:1], HEAD_N, out=Y1)
+    err_head = check_gemv_rows(ql, "q6k", wrows, rows, Bh, HEAD_N, HEAD_K, xh[:1], Y1.cpu().numpy(), "head M=1")
+    Bh2 = [Bh, Bh.clone()]
+    nb_head = Bh.numel()
 
-        steps = args.steps
-        for i in range(args.warmup):
-            launch(i)
-        g = graph_of(torch, launch, steps)
-        torch.cuda.synchronize()
-        # the replay must reproduce the eager result (checked before timing)
-        y_eager = Y.clone()
+    def head_launch(i):
+        ql.qmatmul("q6k", Bh2[i % 2], Xh[:1], HEAD_N, out=Y1)
+
+    for i in range(args.warmup):
+        head_launch(i)
+    g = run.graph(head_launch, args.steps)
+    y_eager = Y1.clone()
+    g.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(Y1, y_eager):
+        raise SystemExit("parity failure: graph replay of the head GEMV differs from its eager launch")
+    # replays until the clocks settle, then the timed region: `reps`
+    # replays of exactly `steps` launches each
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.3:
         g.replay()
         torch.cuda.synchronize()
-        assert torch.equal(Y, y_eager), "graph replay differs from eager launch"
-        ms = time_graph(torch, g, 1, steps)   # exactly `steps` launches timed
-        ms_rep = time_graph(torch, g, 5, steps)
-        wbytes = nb
-        alg = nb + M * K * 2 + M * N * 4
-        head[fmt] = dict(ms=ms, ms_5reps=ms_rep, weight_bytes=wbytes, alg_bytes=alg, copies=R,
-                         weight_GBps=wbytes / (ms * 1e-3) / 1e9, alg_GBps=alg / (ms * 1e-3) / 1e9,
-                         parity_max_err=parity)
-        log(f"  {fmt} GEMV: {ms * 1e3:.2f} us/launch  {head[fmt]['weight_GBps']:.0f} GB/s weights  "
-            f"(max err {parity:.1e}, {R} copies)")
-        del copies, g, blocks
-        torch.cuda.empty_cache()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.reps)]
+    s = torch.cuda.current_stream()
+    for a, b in evs:
+        a.record(s)
+        g.replay()
+        b.record(s)
+    torch.cuda.synchronize()
+    th = stats([a.elapsed_time(b) / args.steps for a, b in evs])
+    alg_head = nb_head + HEAD_K * 2 + HEAD_N * 4
+    log(f"  head GEMV M=1: median {th['median'] * 1e3:.1f} us (p10 {th['p10'] * 1e3:.1f}, p90 {th['p90'] * 1e3:.1f}); "
+        f"{nb_head / th['median'] / 1e6:.0f} GB/s of weights; max err {err_head:.1e}")
+    del g
 
-    q4 = head["q4k"]
-    result.update({
+    result = {
         "metric": "quantized GEMV weight GB/s (% HBM peak) + prefill qGEMM TOPS (% MFMA peak)",
-        "value": round(q4["weight_GBps"], 1),
+        "value": round(nb_head / th["median"] / 1e6, 1),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": q4["ms"],
+        "ms_per_step": th["median"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "q4k_decode_gemv", "N": N, "K": K, "M": M, "weights": "N(0,0.02) bf16 -> Q4K",
-                   "activations": "N(0,1) bf16", "weight_copies_rotated": q4["copies"],
-                   "launch": "HIP graph of `steps` launches"},
-        "roofline": {"bound": "hbm", "achieved": round(q4["alg_GBps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(q4["alg_GBps"] / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(),
-                     "traffic_unit": "HBM bytes per launch (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0)",
-                     "kernel": "gemv_lds_kernel<Q4K, M=1, CPT=2, R=2>", "alg_bytes_per_launch": q4["alg_bytes"]},
-    })
-    parts["gemv_q8_0_14336x4096_m1"] = {
-        "us": round(head["q8_0"]["ms"] * 1e3, 3), "weight_GBps": round(head["q8_0"]["weight_GBps"], 1),
-        "hbm_frac": round(head["q8_0"]["alg_GBps"] / HBM_PEAK_GBPS, 4), "parity_max_err": head["q8_0"]["parity_max_err"]}
-    parts["gemv_q4k_14336x4096_m1"] = {
-        "us": round(q4["ms"] * 1e3, 3), "weight_GBps": round(q4["weight_GBps"], 1),
-        "hbm_frac": round(q4["alg_GBps"] / HBM_PEAK_GBPS, 4), "parity_max_err": q4["parity_max_err"]}
-    del W
+        "config": {"workload": "output head GEMV of the 32-layer decoder (ISQ: layers Q4K, head promoted to Q6K)",
+                   "N": HEAD_N, "K": HEAD_K, "M": 1, "format": "q6k", "weight_bytes": nb_head,
+                   "weights": "N(0,0.02) bf16 (device generator, seed 5999)", "activations": "N(0,1) bf16",
+                   "weight_copies_rotated": 2, "timing": f"{args.reps} replays of a HIP graph of {args.steps} "
+                   "launches, HIP events on the launch stream, median per launch",
+                   "arithmetic": "exact Q6K codes x fp16-scaled activations, fp32 sums"},
+        "roofline": roof("hbm", alg_head, th, HBM_PEAK_GBPS, "GB/s",
+                         "gemv_lds_kernel<Q6K, M=1, CPT=3, R=4, FS=160>", traffic=measured_traffic(),
+                         note="achieved = (weight bytes + X + Y) per launch / median launch time; traffic = "
+                              "FETCH_SIZE + WRITE_SIZE per dispatch scaled by a copy kernel of known size"),
+    }
+    parts = {"head_q6k_gemv_m1": {"parity_max_err": err_head, **result["roofline"]}}
 
-    which = set(args.parts.split(",")) if args.parts else (set() if args.quick else
-                                                           {"batched", "glu", "formats", "fp8", "prefill", "isq"})
-    if which:
-        parts.update(bench_parts(torch, ql, synth, dev, bf16_dev, which))
+    which = set() if args.quick else (set(args.parts.split(",")) if args.parts else set(ALL_PARTS))
+    if "model" in which:
+        parts.update(part_model(torch, ql, synth, run, dev, bf16_dev, host_rows, Wh, Bh2, Xh, xh))
+    del Wh
+    torch.cuda.empty_cache()
+    if "gemv" in which:
+        parts.update(part_gemv(torch, ql, synth, run, dev, bf16_dev))
+    if "batched" in which:
+        parts.update(part_batched(torch, ql, synth, run, dev, bf16_dev))
+    if "crossover" in which:
+        parts.update(part_crossover(torch, ql, synth, run, dev, bf16_dev))
+    if "glu" in which:
+        parts.update(part_glu(torch, ql, synth, run, dev, bf16_dev))
+    if "prefill" in which:
+        parts.update(part_prefill(torch, ql, synth, run, dev, bf16_dev))
+    if "ceilings" in which:
+        parts.update(part_ceilings(torch, ql, run, dev))
     result["parts"] = parts
     if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(w, x)
+        result["cpu_baseline"] = cpu_baseline()
     print(json.dumps(result), flush=True)
 
 
-def check_gemv_parity(ql, fmt, w, x, blocks, Y, N):
-    import torch
+# ----------------------------------------------------------------------
+# parts
+# ----------------------------------------------------------------------
 
+def part_model(torch, ql, synth, run, dev, bf16_dev, host_rows, Wh, Bh2, Xh, xh):
+    """ISQ of the 32-layer decoder (Q4K) and the head (Q6K); the head GEMV for
+    eight tokens; equivalent decode tokens/s."""
     import oracle
 
-    ql.qmatmul(fmt, blocks, torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(blocks.device), N, out=Y)
-    y = Y.cpu().numpy()
-    rng = np.random.Generator(np.random.PCG64(1))
-    rows = np.sort(rng.choice(N, 256, replace=False))
-    K = w.shape[1]
-    got = oracle.rows_of_buffer(fmt, blocks.cpu().numpy(), N, K, rows)
-    f = oracle.quantize(fmt, w[rows])
-    if not np.array_equal(got, oracle.pack(fmt, f, len(rows), K)):
-        raise SystemExit(f"parity failure: {fmt} ISQ bytes differ from the oracle")
-    Yr, den = oracle.matmul_a16(oracle.dequant(fmt, f, len(rows), K), x)
-    e = oracle.normalized_error(y[:, rows], Yr, den).max()
-    if e > 1e-3:
-        raise SystemExit(f"parity failure: {fmt} GEMV error {e:.3e}")
-    return float(e)
-
-
-def bench_parts(torch, ql, synth, dev, bf16_dev, which):
     parts = {}
+    log("model: ISQ of 32 layers x 7 projections (q4k) + head (q6k)")
+    Wl, Bl = [], []
+    for layer in range(32):
+        for kind, (n, k) in enumerate(DECODER_SHAPES):
+            Wl.append(synth.device_normal_bf16(synth.decoder_seed(layer, kind), (n, k), synth.W_SIGMA))
+            Bl.append(torch.empty(ql.blocks_bytes("q4k", n, k), dtype=torch.uint8, device=dev))
+    Bh_out = torch.empty_like(Bh2[0])
+    read = sum(w.numel() * 2 for w in Wl) + Wh.numel() * 2
+    write = sum(b.numel() for b in Bl) + Bh_out.numel()
 
-    def timed_calls(launch, n_calls, reps=3):
-        for i in range(3):
-            launch(i)
-        g = graph_of(torch, launch, n_calls)
-        return time_graph(torch, g, reps, n_calls)
-
-    if "batched" in which:
-        # batched decode: K=14336, N=4096, Q4K with outliers, M = 4, 16, 64
-        log("batched decode 4096x14336 q4k")
-        N, K = 4096, 14336
-        w = synth.weights_bf16(synth.seed_for(3, 0), N, K, outliers=True)
-        xs = synth.activations_bf16(synth.seed_for(3, 1), 64, K)
-        blocks = ql.isq("q4k", bf16_dev(w))
-        R = copies_for(blocks.numel())
-        copies = [blocks] + [blocks.clone() for _ in range(R - 1)]
-        for M in (4, 16, 64):
-            X = bf16_dev(xs[:M])
-            Y = torch.empty((M, N), dtype=torch.float32, device=dev)
-            ms = timed_calls(lambda i: ql.qmatmul("q4k", copies[i % R], X, N, out=Y), 4 * R)
-            fl = 2.0 * M * N * K
-            parts[f"batched_q4k_m{M}"] = {
-                "us": round(ms * 1e3, 3), "path": "gemv" if M <= 2 else "mfma_bf16",
-                "weight_GBps": round(blocks.numel() / ms / 1e6, 1),
-                "hbm_frac": round((blocks.numel() + M * K * 2 + M * N * 4) / ms / 1e6 / HBM_PEAK_GBPS, 4),
-                "TFLOPs": round(fl / ms / 1e9, 2)}
-            log(f"  M={M}: {ms * 1e3:.2f} us")
-        # GEMV / MFMA crossover at this shape (sets the AUTO dispatch)
-        cross = {}
-        for M in range(1, 9):
-            X = bf16_dev(xs[:M])
-            Y = torch.empty((M, N), dtype=torch.float32, device=dev)
-            row = {}
-            for path in ("gemv", "mfma_bf16"):
-                ms = timed_calls(lambda i: ql.qmatmul("q4k", copies[i % R], X, N, out=Y, path=path), 2 * R)
-                row[path] = round(ms * 1e3, 2)
-            cross[str(M)] = row
-        parts["crossover_q4k_4096x14336_us"] = cross
-        log(f"  crossover: {cross}")
-        del copies, blocks
-        torch.cuda.empty_cache()
-
-    if "glu" in which:
-        # gated FFN projection, 14336 x 4096 gate and up (Q4K): one fused launch
-        # against the two GEMVs it replaces (their outputs alone, no product)
-        log("gated FFN 14336x4096 q4k: fused gate/up + SiLU vs two GEMVs")
-        F, K = 14336, 4096
-        wg = bf16_dev(synth.weights_bf16(synth.seed_for(2, 0), F, K))
-        wu = synth.device_normal_bf16(9501, (F, K), synth.W_SIGMA)
-        bg, bu = ql.isq("q4k", wg), ql.isq("q4k", wu)
-        R = copies_for(2 * bg.numel())
-        cg = [bg] + [bg.clone() for _ in range(R - 1)]
-        cu = [bu] + [bu.clone() for _ in range(R - 1)]
-        xs = synth.activations_bf16(synth.seed_for(2, 1), 2, K)
-        for M in (1, 2):
-            X = bf16_dev(xs[:M])
-            H = torch.empty((M, F), dtype=torch.float32, device=dev)
-            Y2 = torch.empty((M, F), dtype=torch.float32, device=dev)
-            fused = timed_calls(lambda i: ql.qmatmul_glu("q4k", cg[i % R], cu[i % R], X, F, out=H), 2 * R)
-
-            def two(i):
-                ql.qmatmul("q4k", cg[i % R], X, F, out=Y2)
-                ql.qmatmul("q4k", cu[i % R], X, F, out=H)
-
-            sep = timed_calls(two, 2 * R)
-            parts[f"glu_q4k_14336x4096_m{M}"] = {
-                "fused_us": round(fused * 1e3, 2), "two_gemvs_us": round(sep * 1e3, 2),
-                "fused_weight_GBps": round(2 * bg.numel() / fused / 1e6, 1),
-                "hbm_frac": round(2 * bg.numel() / fused / 1e6 / HBM_PEAK_GBPS, 4)}
-            log(f"  M={M}: fused {fused * 1e3:.2f} us, two GEMVs {sep * 1e3:.2f} us")
-        del cg, cu, bg, bu, wg, wu
-        torch.cuda.empty_cache()
-
-    if "formats" in which:
-        # the further formats on the generic kernels, at the 14336 x 4096 shape:
-        # ISQ, one-token GEMV and a 16-token batch
-        log("further formats 14336x4096: ISQ, GEMV M=1, MFMA M=16")
-        N, K = 14336, 4096
-        W = bf16_dev(synth.weights_bf16(synth.seed_for(2, 0), N, K))
-        xs = bf16_dev(synth.activations_bf16(synth.seed_for(2, 1), 16, K))
-        rows = {}
-        for fmt in ("q5k", "q3k", "q2k", "q4_0", "q4_1", "q5_0", "q5_1"):
-            blocks = ql.isq(fmt, W)
-            nb = blocks.numel()
-            R = copies_for(nb)
-            copies = [blocks] + [blocks.clone() for _ in range(R - 1)]
-            out = torch.empty_like(blocks)
-            isq_ms = timed_calls(lambda i: ql.isq(fmt, W, out=out), 10)
-            Y1 = torch.empty((1, N), dtype=torch.float32, device=dev)
-            g1 = timed_calls(lambda i: ql.qmatmul(fmt, copies[i % R], xs[:1], N, out=Y1), 2 * R)
-            Y16 = torch.empty((16, N), dtype=torch.float32, device=dev)
-            g16 = timed_calls(lambda i: ql.qmatmul(fmt, copies[i % R], xs, N, out=Y16), 2 * R)
-            rows[fmt] = {"bytes": nb, "isq_us": round(isq_ms * 1e3, 1),
-                         "isq_GBps": round((W.numel() * 2 + nb) / isq_ms / 1e6, 1),
-                         "gemv_m1_us": round(g1 * 1e3, 2), "gemv_m1_weight_GBps": round(nb / g1 / 1e6, 1),
-                         "m16_us": round(g16 * 1e3, 2), "m16_weight_GBps": round(nb / g16 / 1e6, 1)}
-            log(f"  {fmt}: ISQ {isq_ms * 1e3:.0f} us, GEMV M=1 {g1 * 1e3:.2f} us ({nb / g1 / 1e6:.0f} GB/s), "
-                f"M=16 {g16 * 1e3:.2f} us")
-            del copies, blocks, out
-        parts["further_formats_14336x4096"] = rows
-        del W, xs
-        torch.cuda.empty_cache()
-
-    if "fp8" in which:
-        # FP8 E4M3 with per-row scales: ISQ and W8A16 GEMV at 14336 x 4096, and
-        # dynamic per-token W8A8 at the prefill shape on the FP8 MFMA path
-        log("fp8: ISQ + W8A16 GEMV 14336x4096, W8A8 prefill 2048x4096x14336")
-        N, K = 14336, 4096
-        W = bf16_dev(synth.weights_bf16(synth.seed_for(4, 0), N, K))
-        b8 = ql.isq("fp8", W)
-        out = torch.empty_like(b8)
-        isq_ms = timed_calls(lambda i: ql.isq("fp8", W, out=out), 10)
-        R = copies_for(b8.numel())
-        copies = [b8] + [b8.clone() for _ in range(R - 1)]
-        x1 = bf16_dev(synth.activations_bf16(synth.seed_for(2, 1), 1, K))
-        Y1 = torch.empty((1, N), dtype=torch.float32, device=dev)
-        g1 = timed_calls(lambda i: ql.qmatmul("fp8", copies[i % R], x1, N, out=Y1), 2 * R)
-        M = 2048
-        X = bf16_dev(synth.activations_bf16(synth.seed_for(4, 1), M, K))
-        ws = torch.empty(ql.workspace_bytes("fp8", "mfma_fp8", M, K), dtype=torch.uint8, device=dev)
-        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
-        fl = 2.0 * M * N * K
-        pf = timed_calls(lambda i: ql.qmatmul("fp8", copies[i % 2], X, N, out=Y, path="mfma_fp8", workspace=ws), 10)
-        parts["fp8_e4m3_14336x4096"] = {
-            "isq_us": round(isq_ms * 1e3, 1), "isq_GBps": round((W.numel() * 2 + b8.numel()) / isq_ms / 1e6, 1),
-            "w8a16_gemv_m1_us": round(g1 * 1e3, 2), "w8a16_gemv_weight_GBps": round(b8.numel() / g1 / 1e6, 1),
-            "w8a8_prefill_m2048_us": round(pf * 1e3, 1), "w8a8_TOPs": round(fl / pf / 1e9, 1),
-            "w8a8_mfma_frac": round(fl / pf / 1e9 / FP8_PEAK_TFLOPS, 4),
-            "includes": "per-token activation quantization"}
-        log(f"  ISQ {isq_ms * 1e3:.0f} us, W8A16 GEMV M=1 {g1 * 1e3:.2f} us ({b8.numel() / g1 / 1e6:.0f} GB/s), "
-            f"W8A8 prefill {pf * 1e3:.0f} us {fl / pf / 1e9:.0f} TFLOP/s")
-        del copies, b8, out, W, X, ws, Y
-        torch.cuda.empty_cache()
-
-    if "prefill" in which:
-        # prefill: M=2048, K=4096, N=14336, Q8_0; bf16 MFMA path and int8 path
-        log("prefill 2048x4096x14336 q8_0")
-        M, N, K = 2048, 14336, 4096
-        w = synth.weights_bf16(synth.seed_for(4, 0), N, K)
-        X = bf16_dev(synth.activations_bf16(synth.seed_for(4, 1), M, K))
-        blocks = ql.isq("q8_0", bf16_dev(w))
-        copies = [blocks, blocks.clone()]
-        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
-        ws = torch.empty(ql.workspace_bytes("q8_0", "mfma_i8", M, K), dtype=torch.uint8, device=dev)
-        fl = 2.0 * M * N * K
-        ms = timed_calls(lambda i: ql.qmatmul("q8_0", copies[i % 2], X, N, out=Y, path="mfma_bf16"), 10)
-        parts["prefill_q8_0_bf16_mfma"] = {"us": round(ms * 1e3, 2), "TFLOPs": round(fl / ms / 1e9, 1),
-                                           "mfma_frac": round(fl / ms / 1e9 / BF16_PEAK_TFLOPS, 4)}
-        log(f"  bf16 path: {ms * 1e3:.1f} us {fl / ms / 1e9:.0f} TFLOP/s")
-        ms = timed_calls(lambda i: ql.qmatmul("q8_0", copies[i % 2], X, N, out=Y, path="mfma_i8", workspace=ws), 10)
-        parts["prefill_q8_0_int8_mfma"] = {"us": round(ms * 1e3, 2), "TOPs": round(fl / ms / 1e9, 1),
-                                           "mfma_frac": round(fl / ms / 1e9 / INT8_PEAK_TOPS, 4),
-                                           "includes": "activation quantization"}
-        log(f"  int8 path: {ms * 1e3:.1f} us {fl / ms / 1e9:.0f} TOP/s")
-        del copies, blocks, ws, Y, X
-        torch.cuda.empty_cache()
-
-    if "isq" in which:
-        # ISQ of the 32-layer decoder (Q4K) and the output head (Q6K)
-        log("decoder ISQ: 32 layers x 7 projections to q4k + 131072x5120 head to q6k")
-        shapes = [(4096, 4096), (1024, 4096), (1024, 4096), (4096, 4096), (14336, 4096), (14336, 4096),
-                  (4096, 14336)]
-        Wl, Bl = [], []
-        read = write = 0
-        for layer in range(32):
-            for kind, (n, k) in enumerate(shapes):
-                Wt = synth.device_normal_bf16(synth.decoder_seed(layer, kind), (n, k), synth.W_SIGMA)
-                Wl.append(Wt)
-                Bl.append(torch.empty(ql.blocks_bytes("q4k", n, k), dtype=torch.uint8, device=dev))
-        Wh = synth.device_normal_bf16(synth.LM_HEAD_W_SEED, (131072, 5120), synth.W_SIGMA)
-        Bh = torch.empty(ql.blocks_bytes("q6k", 131072, 5120), dtype=torch.uint8, device=dev)
+    def isq_all(_i):
         for Wt, Bt in zip(Wl, Bl):
-            read += Wt.numel() * 2
-            write += Bt.numel()
-        read += Wh.numel() * 2
-        write += Bh.numel()
+            ql.isq("q4k", Wt, out=Bt)
+        ql.isq("q6k", Wh, out=Bh_out)
 
-        def isq_all():
-            for Wt, Bt in zip(Wl, Bl):
-                ql.isq("q4k", Wt, out=Bt)
-            ql.isq("q6k", Wh, out=Bh)
+    isq_all(0)
+    torch.cuda.synchronize()
+    # codes bit-exact: 8 sampled rows of every layer's tensors, 64 rows of the head
+    for j in range(len(Wl)):
+        n, k = DECODER_SHAPES[j % 7]
+        rows = sample_rows(n, 8, 100 + j)
+        w_rows = host_rows(Wl[j], rows)
+        got = oracle.rows_of_buffer("q4k", Bl[j].cpu().numpy(), n, k, rows)
+        if not np.array_equal(got, oracle.pack("q4k", oracle.quantize("q4k", w_rows), len(rows), k)):
+            raise SystemExit(f"parity failure: decoder tensor {j} ISQ bytes")
+    if not torch.equal(Bh_out, Bh2[0]):
+        raise SystemExit("parity failure: head ISQ is not deterministic")
+    t = run.time(isq_all, 1, warmup=1)
+    parts["isq_decoder_32l_q4k_head_q6k"] = {
+        **roof("hbm", read + write, t, HBM_PEAK_GBPS, "GB/s", "isq_q4k_kernel x224 + isq_q6k_kernel",
+               note="bf16 read + blocks written, 225 launches per step"),
+        "read_bytes": read, "write_bytes": write, "parity": "224 tensors x 8 sampled rows + the head: bit-exact"}
+    log(f"  ISQ: {t['median']:.2f} ms ({(read + write) / t['median'] / 1e6:.0f} GB/s)")
 
-        isq_all()
-        torch.cuda.synchronize()
-        with Timer(torch) as t:
-            isq_all()
-        parts["isq_decoder_32l_q4k_plus_head_q6k"] = {
-            "ms": round(t.ms, 3), "read_bytes": read, "write_bytes": write,
-            "GBps": round((read + write) / t.ms / 1e6, 1),
-            "hbm_frac": round((read + write) / t.ms / 1e6 / HBM_PEAK_GBPS, 4)}
-        log(f"  ISQ all: {t.ms:.2f} ms ({(read + write) / t.ms / 1e6:.0f} GB/s)")
-        del Wl, Wh
-        torch.cuda.empty_cache()
+    # head GEMV, eight tokens
+    Y8 = torch.empty((8, HEAD_N), dtype=torch.float32, device=dev)
+    ql.qmatmul("q6k", Bh2[0], Xh, HEAD_N, out=Y8)
+    rows = sample_rows(HEAD_N, 128, 13)
+    e8 = check_gemv_rows(ql, "q6k", host_rows(Wh, rows), rows, Bh2[0], HEAD_N, HEAD_K, xh, Y8.cpu().numpy(),
+                         "head M=8", isq_exact=False)
+    t = run.time(lambda i: ql.qmatmul("q6k", Bh2[i % 2], Xh, HEAD_N, out=Y8), 8)
+    nb = Bh2[0].numel()
+    parts["head_q6k_gemv_m8"] = {**roof("hbm", nb + 8 * HEAD_K * 2 + 8 * HEAD_N * 4, t, HBM_PEAK_GBPS, "GB/s",
+                                        "AUTO (8 tokens)"), "parity_max_err": e8}
+    log(f"  head GEMV M=8: {t['median'] * 1e3:.1f} us")
 
-        # output head GEMV, M = 1 and M = 8 (Q6K)
-        xh = synth.activations_bf16(synth.LM_HEAD_X_SEED, 8, 5120)
-        Bh2 = [Bh, Bh.clone()]
-        for M in (1, 8):
-            X = bf16_dev(xh[:M])
-            Y = torch.empty((M, 131072), dtype=torch.float32, device=dev)
-            ms = timed_calls(lambda i: ql.qmatmul("q6k", Bh2[i % 2], X, 131072, out=Y), 8)
-            parts[f"lm_head_q6k_m{M}"] = {"us": round(ms * 1e3, 2), "weight_GBps": round(Bh.numel() / ms / 1e6, 1),
-                                          "hbm_frac": round((Bh.numel() + M * 5120 * 2 + M * 131072 * 4) / ms / 1e6 / HBM_PEAK_GBPS, 4)}
-            log(f"  lm_head M={M}: {ms * 1e3:.1f} us")
-        del Bh2
+    # equivalent decode tokens/s: q/k/v concatenated into one [6144][4096]
+    # weight per layer (rows are quantized independently, so its blocks are
+    # those of the three tensors), gate/up fused with SiLU, o and down, head
+    log("  equivalent decode: building the concatenated q/k/v weights")
+    Bqkv = []
+    for layer in range(32):
+        Wc = torch.cat([Wl[7 * layer], Wl[7 * layer + 1], Wl[7 * layer + 2]], 0)
+        Bqkv.append(ql.isq("q4k", Wc))
+    del Wc
+    x1 = bf16_dev(synth.activations_bf16(9001, 1, 14336))
+    Yqkv = torch.empty((1, 6144), dtype=torch.float32, device=dev)
+    Yo = torch.empty((1, 4096), dtype=torch.float32, device=dev)
+    Hf = torch.empty((1, 14336), dtype=torch.float32, device=dev)
+    Yh = torch.empty((1, HEAD_N), dtype=torch.float32, device=dev)
+    # parity of the concatenated launch against the oracle (sampled rows over q, k and v)
+    ql.qmatmul("q4k", Bqkv[0], x1[:, :4096], 6144, out=Yqkv)
+    rows = np.unique(np.concatenate([sample_rows(6144, 64, 14), [4095, 4096, 5119, 5120]]))
+    Wc_rows = torch.cat([Wl[0], Wl[1], Wl[2]], 0)
+    eq = check_gemv_rows(ql, "q4k", host_rows(Wc_rows, rows), rows, Bqkv[0], 6144, 4096,
+                         synth.activations_bf16(9001, 1, 14336)[:, :4096], Yqkv.cpu().numpy(), "qkv concatenated")
+    del Wc_rows
 
-        # embedding lookup from the same Q6K table (a tied head): 2048 random ids
-        ids = torch.randint(0, 131072, (2048,), generator=torch.Generator().manual_seed(9100),
-                            dtype=torch.int32).to(dev)
-        E = torch.empty((2048, 5120), dtype=torch.float32, device=dev)
-        ms = timed_calls(lambda i: ql.embed("q6k", Bh, 131072, 5120, ids, out=E), 20)
-        moved = 2048 * 5120 * 210 // 256 + E.numel() * 4
-        parts["embed_q6k_131072x5120_2048ids"] = {"us": round(ms * 1e3, 2), "GBps": round(moved / ms / 1e6, 1),
-                                                  "hbm_frac": round(moved / ms / 1e6 / HBM_PEAK_GBPS, 4),
-                                                  "bytes": moved, "note": "quantized rows read + fp32 rows written"}
-        log(f"  embed 2048 ids: {ms * 1e3:.1f} us ({moved / ms / 1e6:.0f} GB/s)")
-        del E
+    def token(_i):
+        for layer in range(32):
+            ql.qmatmul("q4k", Bqkv[layer], x1[:, :4096], 6144, out=Yqkv)
+            ql.qmatmul("q4k", Bl[7 * layer + 3], x1[:, :4096], 4096, out=Yo)
+            ql.qmatmul_glu("q4k", Bl[7 * layer + 4], Bl[7 * layer + 5], x1[:, :4096], 14336, out=Hf)
+            ql.qmatmul("q4k", Bl[7 * layer + 6], x1[:, :14336], 4096, out=Yo)
+        ql.qmatmul("q6k", Bh2[0], x1[:, :HEAD_K], HEAD_N, out=Yh)
 
-        # equivalent decode tokens/s: every projection GEMV of the 32 layers + head
-        x1 = bf16_dev(synth.activations_bf16(9001, 1, 14336))
-        Ys = [torch.empty((1, n), dtype=torch.float32, device=dev) for (n, k) in shapes]
-        Yh = torch.empty((1, 131072), dtype=torch.float32, device=dev)
+    total = sum(b.numel() for b in Bl) + nb
+    t = run.time(token, 1, warmup=1)
+    parts["equiv_decode_tok_s"] = {
+        "tok_s": round(1.0 / (t["median"] * 1e-3), 1), **roof("hbm", total, t, HBM_PEAK_GBPS, "GB/s",
+                                                              "129 launches per token"),
+        "qkv_parity_max_err": eq,
+        "note": "per layer: q/k/v as one concatenated GEMV, o, gate/up fused with SiLU, down; then the Q6K head; "
+                "attention, norms and sampling excluded; bound 1,787 tok/s at 8 TB/s"}
+    log(f"  decode token: {t['median']:.3f} ms -> {1.0 / (t['median'] * 1e-3):.0f} tok/s")
 
-        def token(_i):
-            for j, Bt in enumerate(Bl):
-                n, k = shapes[j % 7]
-                ql.qmatmul("q4k", Bt, x1[:, :k], n, out=Ys[j % 7])
-            ql.qmatmul("q6k", Bh, x1[:, :5120], 131072, out=Yh)
+    def token_plain(_i):
+        for j, Bt in enumerate(Bl):
+            n, k = DECODER_SHAPES[j % 7]
+            ql.qmatmul("q4k", Bt, x1[:, :k], n, out=Yo if n == 4096 else Hf if n == 14336 else Yqkv[:, :n])
+        ql.qmatmul("q6k", Bh2[0], x1[:, :HEAD_K], HEAD_N, out=Yh)
 
-        token(0)
-        g = graph_of(torch, token, 1)
-        ms = time_graph(torch, g, 10, 1)
-        total = sum(b.numel() for b in Bl) + Bh.numel()
-        parts["equiv_decode_tok_s"] = {"tok_s": round(1000.0 / ms, 1), "ms_per_token": round(ms, 4),
-                                       "weight_bytes_per_token": total,
-                                       "weight_GBps": round(total / ms / 1e6, 1),
-                                       "note": "225 quantized GEMVs per token (M=1); attention, norms, sampling excluded"}
-        log(f"  decode token: {ms:.3f} ms -> {1000 / ms:.0f} tok/s")
-
-        # the same token with each layer's gate and up projections fused with
-        # SiLU * up into one launch (qmatmul_glu)
-        Hf = torch.empty((1, 14336), dtype=torch.float32, device=dev)
-
-        def token_fused(_i):
-            for layer in range(32):
-                for j in (0, 1, 2, 3, 6):
-                    n, k = shapes[j]
-                    ql.qmatmul("q4k", Bl[7 * layer + j], x1[:, :k], n, out=Ys[j])
-                ql.qmatmul_glu("q4k", Bl[7 * layer + 4], Bl[7 * layer + 5], x1[:, :4096], 14336, out=Hf)
-            ql.qmatmul("q6k", Bh, x1[:, :5120], 131072, out=Yh)
-
-        token_fused(0)
-        g = graph_of(torch, token_fused, 1)
-        ms = time_graph(torch, g, 10, 1)
-        parts["equiv_decode_tok_s_fused_ffn"] = {
-            "tok_s": round(1000.0 / ms, 1), "ms_per_token": round(ms, 4), "weight_GBps": round(total / ms / 1e6, 1),
-            "note": "per layer q, k, v, o, down GEMVs + one fused gate/up SiLU launch (193 launches per token)"}
-        log(f"  decode token, fused gate/up: {ms:.3f} ms -> {1000 / ms:.0f} tok/s")
+    t = run.time(token_plain, 1, warmup=1)
+    parts["equiv_decode_tok_s_unfused"] = {
+        "tok_s": round(1.0 / (t["median"] * 1e-3), 1), "ms_per_token": round(t["median"], 4),
+        "note": "225 separate GEMV launches per token"}
+    log(f"  decode token, 225 launches: {t['median']:.3f} ms")
+    del Wl, Bl, Bqkv
+    torch.cuda.empty_cache()
     return parts
 
 
-def _oracle_gemv_rate(w, x, seconds):
+def part_gemv(torch, ql, synth, run, dev, bf16_dev):
+    """One-token GEMVs: Q8_0 1024 x 1024 (latency) and 14336 x 4096 Q4K / Q8_0."""
+    parts = {}
+    N, K = 1024, 1024
+    w = synth.weights_bf16(synth.seed_for(1, 0), N, K)
+    x = synth.activations_bf16(synth.seed_for(1, 1), 1, K)
+    B = ql.isq("q8_0", bf16_dev(w))
+    X = bf16_dev(x)
+    Y = torch.empty((1, N), dtype=torch.float32, device=dev)
+    ql.qmatmul("q8_0", B, X, N, out=Y)
+    rows = np.arange(N)
+    e = check_gemv_rows(ql, "q8_0", w, rows, B, N, K, x, Y.cpu().numpy(), "q8_0 1024")
+    hot = run.time(lambda i: ql.qmatmul("q8_0", B, X, N, out=Y), 100)
+    R = copies_for(B.numel())
+    cp = [B] + [B.clone() for _ in range(R - 1)]
+    cold = run.time(lambda i: ql.qmatmul("q8_0", cp[i % R], X, N, out=Y), R)
+    alg = B.numel() + K * 2 + N * 4
+    parts["gemv_q8_0_1024x1024_m1"] = {
+        **roof("latency", alg, hot, HBM_PEAK_GBPS, "GB/s", "gemv_lds_kernel<Q8_0, M=1, CPT=1, R=1>",
+               note="cache-resident (1.1 MB): a latency figure, no roofline claim"),
+        "cold_us_median": round(cold["median"] * 1e3, 3), "cold_copies": R, "parity_max_err": e}
+    log(f"gemv 1024x1024 q8_0: hot {hot['median'] * 1e3:.2f} us, cold {cold['median'] * 1e3:.2f} us")
+    del cp, B
+
+    N, K = 14336, 4096
+    w = synth.weights_bf16(synth.seed_for(2, 0), N, K)
+    x = synth.activations_bf16(synth.seed_for(2, 1), 1, K)
+    W = bf16_dev(w)
+    X = bf16_dev(x)
+    rows = sample_rows(N, 256, 1)
+    for fmt, kern in (("q4k", "gemv_lds_kernel<Q4K, M=1, CPT=2, R=2>"), ("q8_0", "gemv_lds_kernel<Q8_0, M=1, CPT=2, R=2>")):
+        B = ql.isq(fmt, W)
+        Y = torch.empty((1, N), dtype=torch.float32, device=dev)
+        ql.qmatmul(fmt, B, X, N, out=Y)
+        e = check_gemv_rows(ql, fmt, w[rows], rows, B, N, K, x, Y.cpu().numpy(), f"{fmt} 14336x4096")
+        R = copies_for(B.numel())
+        cp = [B] + [B.clone() for _ in range(R - 1)]
+        t = run.time(lambda i: ql.qmatmul(fmt, cp[i % R], X, N, out=Y), R)
+        parts[f"gemv_{fmt}_14336x4096_m1"] = {**roof("hbm", B.numel() + K * 2 + N * 4, t, HBM_PEAK_GBPS, "GB/s", kern),
+                                             "weight_GBps": round(B.numel() / t["median"] / 1e6, 1),
+                                             "copies": R, "parity_max_err": e}
+        log(f"gemv 14336x4096 {fmt}: {t['median'] * 1e3:.2f} us")
+        del cp, B
+    torch.cuda.empty_cache()
+    return parts
+
+
+def part_batched(torch, ql, synth, run, dev, bf16_dev):
+    """Batched decode: Q4K 4096 x 14336 (1 % outliers), 4 / 16 / 64 tokens on AUTO."""
+    import oracle
+
+    parts = {}
+    N, K = 4096, 14336
+    w = synth.weights_bf16(synth.seed_for(3, 0), N, K, outliers=True)
+    xs = synth.activations_bf16(synth.seed_for(3, 1), 64, K)
+    B = ql.isq("q4k", bf16_dev(w))
+    rows = sample_rows(N, 128, 3)
+    Wd = oracle.dequant("q4k", oracle.quantize("q4k", w[rows]), len(rows), K)
+    R = copies_for(B.numel())
+    cp = [B] + [B.clone() for _ in range(R - 1)]
+    for M in (4, 16, 64):
+        X = bf16_dev(xs[:M])
+        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        ql.qmatmul("q4k", B, X, N, out=Y)
+        Yr, den = oracle.matmul_a16(Wd, xs[:M])
+        e = float(oracle.normalized_error(Y.cpu().numpy()[:, rows], Yr, den).max())
+        if e > 1e-3:
+            raise SystemExit(f"parity failure: batched M={M}: {e:.3e}")
+        t = run.time(lambda i: ql.qmatmul("q4k", cp[i % R], X, N, out=Y), R)
+        parts[f"batched_q4k_4096x14336_m{M}"] = {
+            **roof("hbm", B.numel() + M * K * 2 + M * N * 4, t, HBM_PEAK_GBPS, "GB/s", "AUTO (bf16 MFMA)"),
+            "TFLOPs": round(2.0 * M * N * K / t["median"] / 1e9, 2), "parity_max_err": e}
+        log(f"batched M={M}: {t['median'] * 1e3:.2f} us")
+    del cp, B
+    torch.cuda.empty_cache()
+    return parts
+
+
+def part_crossover(torch, ql, synth, run, dev, bf16_dev):
+    """GEMV against the MFMA path for 1..8 tokens at 4096 x 14336 (sets AUTO)."""
+    N, K = 4096, 14336
+    B = ql.isq("q4k", bf16_dev(synth.weights_bf16(synth.seed_for(3, 0), N, K, outliers=True)))
+    xs = bf16_dev(synth.activations_bf16(synth.seed_for(3, 1), 8, K))
+    R = copies_for(B.numel())
+    cp = [B] + [B.clone() for _ in range(R - 1)]
+    cross = {}
+    for M in range(1, 9):
+        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        row = {}
+        for path in ("gemv", "mfma_bf16", "auto"):
+            t = run.time(lambda i: ql.qmatmul("q4k", cp[i % R], xs[:M], N, out=Y, path=path), R)
+            row[path] = round(t["median"] * 1e3, 2)
+        cross[str(M)] = row
+    log(f"crossover 4096x14336 q4k (us): {cross}")
+    del cp, B
+    torch.cuda.empty_cache()
+    return {"crossover_q4k_4096x14336_us": cross}
+
+
+def part_glu(torch, ql, synth, run, dev, bf16_dev):
+    """Gated FFN projection 14336 x 4096 Q4K: one fused launch against two GEMVs."""
+    parts = {}
+    F, K = 14336, 4096
+    bg = ql.isq("q4k", bf16_dev(synth.weights_bf16(synth.seed_for(2, 0), F, K)))
+    bu = ql.isq("q4k", synth.device_normal_bf16(9501, (F, K), synth.W_SIGMA))
+    R = copies_for(2 * bg.numel())
+    cg = [bg] + [bg.clone() for _ in range(R - 1)]
+    cu = [bu] + [bu.clone() for _ in range(R - 1)]
+    xs = bf16_dev(synth.activations_bf16(synth.seed_for(2, 1), 2, K))
+    for M in (1, 2):
+        H = torch.empty((M, F), dtype=torch.float32, device=dev)
+        Y2 = torch.empty((M, F), dtype=torch.float32, device=dev)
+        fused = run.time(lambda i: ql.qmatmul_glu("q4k", cg[i % R], cu[i % R], xs[:M], F, out=H), R)
+
+        def two(i):
+            ql.qmatmul("q4k", cg[i % R], xs[:M], F, out=Y2)
+            ql.qmatmul("q4k", cu[i % R], xs[:M], F, out=H)
+
+        sep = run.time(two, R)
+        parts[f"glu_q4k_14336x4096_m{M}"] = {
+            **roof("hbm", 2 * bg.numel() + M * K * 2 + M * F * 4, fused, HBM_PEAK_GBPS, "GB/s",
+                   f"gemv_lds_kernel<Q4K, M={M}, GLU>"), "two_gemvs_us": round(sep["median"] * 1e3, 2)}
+        log(f"glu M={M}: fused {fused['median'] * 1e3:.2f} us, two GEMVs {sep['median'] * 1e3:.2f} us")
+    del cg, cu, bg, bu
+    torch.cuda.empty_cache()
+    return parts
+
+
+def part_prefill(torch, ql, synth, run, dev, bf16_dev):
+    """Prefill 2048 x 4096 x 14336: Q8_0 on the bf16 MFMA and int8 paths, FP8 W8A8."""
+    import oracle
+
+    parts = {}
+    M, N, K = 2048, 14336, 4096
+    w = synth.weights_bf16(synth.seed_for(4, 0), N, K)
+    x = synth.activations_bf16(synth.seed_for(4, 1), M, K)
+    X = bf16_dev(x)
+    W = bf16_dev(w)
+    fl = 2.0 * M * N * K
+    rng = np.random.Generator(np.random.PCG64(11))
+    mi, ni = rng.integers(0, M, 1024), rng.integers(0, N, 1024)
+    rows, inv = np.unique(ni, return_inverse=True)
+    Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+
+    B = ql.isq("q8_0", W)
+    cp = [B, B.clone()]
+    fw = oracle.quantize("q8_0", w[rows])
+    ql.qmatmul("q8_0", B, X, N, out=Y, path="mfma_bf16")
+    Yr, den = oracle.matmul_a16_pairs(oracle.dequant("q8_0", fw, len(rows), K), x, mi, inv)
+    e = float(oracle.normalized_error(Y.cpu().numpy()[mi, ni], Yr, den).max())
+    if e > 1e-3:
+        raise SystemExit(f"parity failure: prefill bf16 {e:.3e}")
+    t = run.time(lambda i: ql.qmatmul("q8_0", cp[i % 2], X, N, out=Y, path="mfma_bf16"), 4)
+    parts["prefill_q8_0_2048x4096x14336_bf16_mfma"] = {
+        **roof("mfma", fl, t, BF16_PEAK_TFLOPS, "TFLOP/s", "gemm_pf_kernel<Q8_0> (exact codes, running rescale)"),
+        "parity_max_err": e}
+    log(f"prefill q8_0 bf16 path: {t['median'] * 1e3:.1f} us")
+
+    ws = torch.empty(ql.workspace_bytes("q8_0", "mfma_i8", M, K), dtype=torch.uint8, device=dev)
+    ql.qmatmul("q8_0", B, X, N, out=Y, path="mfma_i8", workspace=ws)
+    Y8, den8 = oracle.matmul_a8(fw, oracle.quantize("q8_0", x), M, len(rows), K, mi=mi, ni=inv)
+    e = float(oracle.normalized_error(Y.cpu().numpy()[mi, ni], Y8, den8).max())
+    if e > 1e-3:
+        raise SystemExit(f"parity failure: prefill int8 {e:.3e}")
+    t = run.time(lambda i: ql.qmatmul("q8_0", cp[i % 2], X, N, out=Y, path="mfma_i8", workspace=ws), 4)
+    parts["prefill_q8_0_2048x4096x14336_int8_mfma"] = {
+        **roof("mfma", fl, t, INT8_PEAK_TOPS, "TFLOP/s", "isq (activations) + gemm_i8_kernel",
+               note="TOPS against the int8 peak; activation quantization included"), "parity_max_err": e}
+    log(f"prefill q8_0 int8 path: {t['median'] * 1e3:.1f} us")
+    del cp, B, ws
+
+    B = ql.isq("fp8", W)
+    cp = [B, B.clone()]
+    ws = torch.empty(ql.workspace_bytes("fp8", "mfma_fp8", M, K), dtype=torch.uint8, device=dev)
+    ql.qmatmul("fp8", B, X, N, out=Y, path="mfma_fp8", workspace=ws)
+    Yf, denf = oracle.matmul_fp8(oracle.quantize_fp8(x), oracle.quantize_fp8(w[rows]), mi=mi, ni=inv)
+    e = float(oracle.normalized_error(Y.cpu().numpy()[mi, ni], Yf, denf).max())
+    if e > 1e-3:
+        raise SystemExit(f"parity failure: prefill fp8 {e:.3e}")
+    t = run.time(lambda i: ql.qmatmul("fp8", cp[i % 2], X, N, out=Y, path="mfma_fp8", workspace=ws), 4)
+    parts["prefill_fp8_2048x4096x14336_w8a8"] = {
+        **roof("mfma", fl, t, FP8_PEAK_TFLOPS, "TFLOP/s", "isq_fp8 (activations) + gemm_fp8_tile_kernel",
+               note="FP8 E4M3 weights (per-row scales), dynamic per-token activations; quantization included"),
+        "parity_max_err": e}
+    log(f"prefill fp8 w8a8: {t['median'] * 1e3:.1f} us")
+    del cp, B, ws, W, X, Y
+    torch.cuda.empty_cache()
+    return parts
+
+
+def part_ceilings(torch, ql, run, dev):
+    """Measured ceilings: a streaming read of buffers read once per launch
+    (550 MB, the head's size; 33 MB slices rotated past the Infinity Cache,
+    the Q4K 14336 x 4096 size), and an MFMA-only bf16 loop."""
+    parts = {}
+    sink = torch.zeros(1, dtype=torch.float32, device=dev)
+    big = torch.empty(2 * 550_502_400 // 16 * 16, dtype=torch.uint8, device=dev).fill_(1)
+    half = big.numel() // 2
+    views = [big[:half], big[half:]]
+    t = run.time(lambda i: ql.probe_read(views[i % 2], sink), 4)
+    parts["ceiling_read_550MB"] = roof("hbm", half, t, HBM_PEAK_GBPS, "GB/s", "read_probe_kernel",
+                                       note="measured HBM read ceiling at the head's size")
+    n33 = 33_030_144
+    R = copies_for(n33)
+    sl = [big[i * n33:(i + 1) * n33] for i in range(R)]
+    t = run.time(lambda i: ql.probe_read(sl[i % R], sink), R)
+    parts["ceiling_read_33MB"] = roof("hbm", n33, t, HBM_PEAK_GBPS, "GB/s", "read_probe_kernel",
+                                      note="measured ceiling for one launch reading 33 MB (launch, ramp, drain)")
+    log(f"ceilings: read 550 MB {parts['ceiling_read_550MB']['achieved']:.0f} GB/s, "
+        f"33 MB {parts['ceiling_read_33MB']['achieved']:.0f} GB/s")
+    del big, views, sl
+    iters = 2000
+    flops = ql.probe_mfma(iters, sink)
+    t = run.time(lambda i: ql.probe_mfma(iters, sink), 2)
+    parts["ceiling_mfma_bf16"] = roof("mfma", flops, t, BF16_PEAK_TFLOPS, "TFLOP/s", "mfma_probe_kernel",
+                                      note="v_mfma_f32_32x32x16_bf16 chains, two waves per SIMD, no memory")
+    log(f"ceilings: MFMA bf16 {parts['ceiling_mfma_bf16']['achieved']:.0f} TFLOP/s")
+    torch.cuda.empty_cache()
+    return parts
+
+
+# ----------------------------------------------------------------------
+# the oracle on the host cores
+# ----------------------------------------------------------------------
+
+def _oracle_gemv_rate(fmt, w, x, seconds):
     """GB/s of quantized weights through the oracle's GEMV (unpack + exact
-    dequant + fp64 matmul) over whole matrices, repeated for `seconds`."""
+    dequant + fp64 matmul), repeated for `seconds`."""
     import oracle
 
     N, K = w.shape
-    f = oracle.quantize("q4k", w)
-    buf = oracle.pack("q4k", f, N, K)
+    buf = oracle.pack(fmt, oracle.quantize(fmt, w), N, K)
     reps, t0 = 0, time.perf_counter()
     while True:
-        g = oracle.unpack("q4k", buf, N, K)
-        Wd = oracle.dequant("q4k", g, N, K)
+        Wd = oracle.dequant(fmt, oracle.unpack(fmt, buf, N, K), N, K)
         oracle.matmul_a16(Wd, x)
         reps += 1
         el = time.perf_counter() - t0
-        if el > seconds or reps >= 1000:
+        if el > seconds or reps >= 10000:
             break
     return buf.size * reps / el / 1e9, reps, el
 
 
+def _oracle_isq_rate(fmt, w, seconds):
+    import oracle
+
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.quantize(fmt, w)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el > seconds:
+            break
+    return w.size * reps / el, reps, el
+
+
+def _oracle_gemm_rate(w, x, seconds):
+    import oracle
+
+    Wd = oracle.dequant("q8_0", oracle.quantize("q8_0", w), *w.shape)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.matmul_a16(Wd, x)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el > seconds:
+            break
+    return 2.0 * x.shape[0] * w.shape[0] * w.shape[1] * reps / el / 1e9, reps, el
+
+
+def _samples():
+    import synth
+
+    return {
+        "head": (synth.weights_bf16(7001, 512, HEAD_K), synth.activations_bf16(7002, 1, HEAD_K)),
+        "cfg1": (synth.weights_bf16(synth.seed_for(1, 0), 1024, 1024), synth.activations_bf16(synth.seed_for(1, 1), 1, 1024)),
+        "cfg2": (synth.weights_bf16(synth.seed_for(2, 0), 2048, 4096), synth.activations_bf16(synth.seed_for(2, 1), 1, 4096)),
+    }
+
+
 _ONE_CORE = """
-import sys, json, numpy as np
+import sys, json
 sys.path.insert(0, {root!r})
 import bench
-d = np.load({path!r})
-r, reps, el = bench._oracle_gemv_rate(d["w"], d["x"], 8.0)
-print(json.dumps({{"value": round(r, 3), "reps": reps, "el": el}}))
+s = bench._samples()
+out = {{}}
+for name, fmt, sec in (("head", "q6k", 4.0), ("cfg1", "q8_0", 2.0), ("cfg2", "q4k", 3.0)):
+    r, reps, el = bench._oracle_gemv_rate(fmt, s[name][0], s[name][1], sec)
+    out[name] = {{"value": round(r, 4), "reps": reps, "el": round(el, 2)}}
+print(json.dumps(out))
 """
 
 
-def cpu_baseline(w, x):
-    """The oracle's quantized GEMV on the host cores, over whole 14336x4096
-    Q4K matrices, repeated for ~12 s; then the same on one core in a child
-    process whose thread counts are pinned to 1 (the child never touches the
-    GPU)."""
+def cpu_baseline():
+    """The oracle on the host cores, on bounded samples of the workloads:
+    headline unit (GB/s of Q6K head weights through the oracle's GEMV), ISQ
+    per format, the fp64 GEMM at the prefill shape's inner dimensions; then
+    one core (child process, thread counts 1, no GPU) for cfg1, cfg2 and the
+    head."""
     import subprocess
-    import tempfile
 
-    rate, reps, el = _oracle_gemv_rate(w, x, 12.0)
+    import synth
+
     cores = len(os.sched_getaffinity(0))
-    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
-    out = {"value": round(rate, 3), "unit": "GB/s", "cores": min(cores, threads), "kind": "oracle",
-           "sample": f"{reps} full {w.shape[0]}x{w.shape[1]} Q4K GEMVs (M=1): unpack + fp64 dequant + fp64 matmul, "
-                     f"{el:.1f} s"}
-    with tempfile.TemporaryDirectory() as tmp:
-        path = os.path.join(tmp, "wx.npz")
-        np.savez(path, w=w, x=x)
-        env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1",
-                   HIP_VISIBLE_DEVICES="")
-        res = subprocess.run([sys.executable, "-c", _ONE_CORE.format(root=ROOT, path=path)], env=env,
-                             capture_output=True, text=True, timeout=300)
+    threads = min(cores, int(os.environ.get("OMP_NUM_THREADS", cores)))
+    s = _samples()
+    rate, reps, el = _oracle_gemv_rate("q6k", s["head"][0], s["head"][1], 8.0)
+    out = {"value": round(rate, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "sample": f"{reps} one-token GEMVs over 512 rows x {HEAD_K} of a Q6K head (1/256 of the 131072 rows): "
+                     f"unpack + exact fp64 dequant + fp64 matmul, {el:.1f} s; GB/s of quantized weights"}
+    try:
+        with open("/proc/cpuinfo") as f:
+            out["cpu_model"] = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
+    w = synth.weights_bf16(7003, 1024, 4096)
+    isq = {}
+    for fmt in ("q8_0", "q4k", "q6k"):
+        r, reps, el = _oracle_isq_rate(fmt, w, 2.0)
+        isq[fmt] = {"elements_per_s": round(r, 1), "bf16_GBps": round(2 * r / 1e9, 4), "reps": reps}
+    out["isq_1024x4096"] = isq
+    xg = synth.activations_bf16(7004, 64, 4096)
+    r, reps, el = _oracle_gemm_rate(synth.weights_bf16(7005, 512, 4096), xg, 4.0)
+    out["gemm_fp64_64x512x4096"] = {"GFLOPs": round(r, 3), "reps": reps,
+                                    "note": "the prefill GEMM's arithmetic on a 64-token x 512-row sample"}
+    env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1",
+               HIP_VISIBLE_DEVICES="", ROCR_VISIBLE_DEVICES="")
+    res = subprocess.run([sys.executable, "-c", _ONE_CORE.format(root=ROOT)], env=env, capture_output=True,
+                         text=True, timeout=300)
     if res.returncode == 0 and res.stdout.strip():
         one = json.loads(res.stdout.strip().splitlines()[-1])
-        out["one_core"] = {"value": one["value"], "unit": "GB/s", "cores": 1,
-                           "sample": f"{one['reps']} full {w.shape[0]}x{w.shape[1]} Q4K GEMVs (M=1), {one['el']:.1f} s"}
+        out["one_core"] = {k: {"value": v["value"], "unit": "GB/s", "cores": 1, "reps": v["reps"]} for k, v in one.items()}
     else:
-        out["one_core"] = {"value": None, "error": (res.stderr or "no output")[-300:]}
+        out["one_core"] = {"error": (res.stderr or "no output")[-300:]}
     return out
 
 

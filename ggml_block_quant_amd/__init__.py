@@ -53,6 +53,9 @@ SIGNATURES = {
     "q_fmt_supported": (_INT, [_INT]),
     "q_fmt_name": (ctypes.c_char_p, [_INT]),
     "q_strerror": (ctypes.c_char_p, [_INT]),
+    "q_probe_read": (_INT, [_P, _I64, _P, _P]),
+    "q_probe_mfma": (_INT, [_P, _I64, _P]),
+    "q_probe_mfma_flops": (_I64, [_I64]),
 }
 
 
@@ -271,3 +274,19 @@ def dequantize(fmt, blocks: torch.Tensor, N: int, K: int) -> torch.Tensor:
     _check("q_dequantize", lib().q_dequantize(_fmt(fmt), _dev(blocks, "blocks", torch.uint8), N, K,
                                               _dev(out, "W"), _stream()))
     return out
+
+
+# ----------------------------------------------------------------------------
+# measurement aids (the benchmark's ceilings; not part of the computation)
+# ----------------------------------------------------------------------------
+
+def probe_read(buf: torch.Tensor, sink: torch.Tensor):
+    """Read every byte of device tensor ``buf`` once (streaming-read ceiling)."""
+    n = buf.numel() * buf.element_size()
+    _check("q_probe_read", lib().q_probe_read(_dev(buf, "buf"), n, _dev(sink, "sink", torch.float32), _stream()))
+
+
+def probe_mfma(iters: int, sink: torch.Tensor) -> int:
+    """A loop of bf16 MFMAs with no memory traffic; returns its FLOP count."""
+    _check("q_probe_mfma", lib().q_probe_mfma(_dev(sink, "sink", torch.float32), iters, _stream()))
+    return int(lib().q_probe_mfma_flops(iters))

@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqlinear.so")
 OBJDIR = os.path.join(HERE, "_build")
-SOURCES = ["api.hip", "isq.hip", "gemv.hip", "gemv_fp8.hip", "gemm.hip"]
+SOURCES = ["api.hip", "isq.hip", "gemv.hip", "gemv_fp8.hip", "gemm.hip", "probe.hip"]
 ARCH = os.environ.get("QLINEAR_ARCH", "gfx950")
 
 FLAGS = [

@@ -330,6 +330,30 @@ int q_embed(int fmt, const void *blocks, int64_t N, int64_t K, const int32_t *id
                                       as_stream(stream)));
 }
 
+int q_probe_read(const void *buf, int64_t bytes, float *out, void *stream)
+{
+    if (!buf || !out)
+        return Q_EINVAL;
+    if (!aligned16(buf))
+        return Q_EALIGN;
+    if (bytes < 16 || bytes % 16 != 0 || bytes > kMaxElems)
+        return Q_ESHAPE;
+    return status_of(ql::launch_read_probe(buf, bytes, out, as_stream(stream)));
+}
+
+int q_probe_mfma(float *out, int64_t iters, void *stream)
+{
+    if (!out)
+        return Q_EINVAL;
+    if (iters < 0 || iters > (int64_t(1) << 24))
+        return Q_ESHAPE;
+    if (iters == 0)
+        return Q_OK;
+    return status_of(ql::launch_mfma_probe(out, iters, as_stream(stream)));
+}
+
+int64_t q_probe_mfma_flops(int64_t iters) { return iters < 0 ? 0 : ql::mfma_probe_flops(iters); }
+
 int isq_resolve_level(int level, int *out_fmt)
 {
     if (!out_fmt)

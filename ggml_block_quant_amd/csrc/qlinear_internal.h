@@ -151,5 +151,8 @@ hipError_t launch_gemm_fp8(const uint8_t *wblocks, const uint8_t *xblocks, float
                            int64_t K, hipStream_t s);
 hipError_t launch_gemm_i8(const uint8_t *wblocks, const uint8_t *xblocks, float *Y, int64_t M,
                           int64_t N, int64_t K, hipStream_t s);
+hipError_t launch_read_probe(const void *buf, int64_t bytes, float *out, hipStream_t s);
+hipError_t launch_mfma_probe(float *out, int64_t iters, hipStream_t s);
+int64_t mfma_probe_flops(int64_t iters);
 
 }  // namespace ql

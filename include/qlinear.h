@@ -240,6 +240,23 @@ int q_embed(int fmt, const void *blocks, int64_t N, int64_t K, const int32_t *id
 int q_dequantize(int fmt, const void *blocks, int64_t N, int64_t K, float *W_fp32,
                  void *stream);
 
+/* Measurement aids, not part of the computation: the two ceilings the
+ * benchmark reports beside the published peaks (page "Quantization types",
+ * section "NVFP4": measured latencies, with the caveat that repeated
+ * projections benefit from the cache -- so the read ceiling is taken on a
+ * buffer read once per launch).
+ * q_probe_read: every byte of device buffer `buf` read once with 16-byte
+ * non-temporal loads; `bytes` a positive multiple of 16, `buf` 16-byte
+ * aligned; `out` a device float that is written only if the XOR of all
+ * words read equals 0x9E3779B9 (it keeps the loads from being removed).
+ * q_probe_mfma: `iters` rounds of four dependent v_mfma_f32_32x32x16_bf16
+ * chains in each of 8192 waves (two per SIMD), no memory traffic; `out`
+ * as above (never written for iters >= 0).  q_probe_mfma_flops: the FLOP
+ * count of one q_probe_mfma call (0 for iters < 0). */
+int q_probe_read(const void *buf, int64_t bytes, float *out, void *stream);
+int q_probe_mfma(float *out, int64_t iters, void *stream);
+int64_t q_probe_mfma_flops(int64_t iters);
+
 /* ISQ level -> format, page "Quantization types", section "Numeric
  * shorthands", column "CUDA / CPU resolves to": 2 Q2K, 3 Q3K, 4 Q4K, 5 Q5K,
  * 6 Q6K, 8 Q8_0.  Other levels: Q_EINVAL.  *out_fmt may name a format this

@@ -194,6 +194,22 @@ def test_qmatmul_static_argument_errors():
     assert ql.workspace_bytes("q8_0", "mfma_i8", 7680, 4096) <= ql.STATIC_SCRATCH_BYTES
 
 
+def test_probe_argument_errors():
+    """The measurement aids check their arguments before any HIP call."""
+    L = ql.lib()
+    assert L.q_probe_read(NULL, 1024, A2, NULL) == ql.Q_EINVAL
+    assert L.q_probe_read(A, 1024, NULL, NULL) == ql.Q_EINVAL
+    assert L.q_probe_read(MIS, 1024, A2, NULL) == ql.Q_EALIGN
+    assert L.q_probe_read(A, 1000, A2, NULL) == ql.Q_ESHAPE
+    assert L.q_probe_read(A, 0, A2, NULL) == ql.Q_ESHAPE
+    assert L.q_probe_mfma(NULL, 10, NULL) == ql.Q_EINVAL
+    assert L.q_probe_mfma(A, -1, NULL) == ql.Q_ESHAPE
+    assert L.q_probe_mfma(A, 0, NULL) == ql.Q_OK          # nothing to launch
+    # 1024 workgroups x 8 waves x 4 chains x 32*32*16 multiply-adds x 2
+    assert L.q_probe_mfma_flops(1) == 1024 * 8 * 4 * 32 * 32 * 16 * 2
+    assert L.q_probe_mfma_flops(-3) == 0
+
+
 def test_embed_argument_errors():
     L = ql.lib()
     IDS = ctypes.c_void_p(0x40004)   # int32 ids need only 4-byte alignment
