@@ -1050,149 +1050,155 @@ __global__ __launch_bounds__(256) void gemm_bt_kernel(const uint8_t *__restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Q4K batched-decode kernel (up to 16 tokens).  Same operand layout and
-// decode as gemm_bt_kernel, with two changes measured to matter on MI355X:
-//
-//   * weight codes are loaded as 4 rows x 256 contiguous bytes per
-//     instruction (lane (a, b) of a wave reads chunk b of row a of a slab
-//     quad) instead of 16 rows x 64 bytes, which streams ~1.5 us faster per
-//     33 MB; each wave then transposes the quad through its own 4 KB of LDS
-//     (chunk c of row r at slot c ^ r, conflict-free both ways) into the
-//     MFMA layout -- no barrier, since no other wave touches that region;
-//   * a fifth wave stages X for the whole K range with direct
-//     global->LDS loads and waits for them alone, so the four weight waves
-//     issue nothing but register loads and their waits stay exact.
-//
-// FULL (M <= 4, X rows 0..3 only): a workgroup owns 16 rows and all of K,
-// wave w the K quarter w; the quarters are summed through LDS and Y is
-// written -- no zero-fill launch and no atomics.  Otherwise a workgroup owns
-// 64 rows (16 per wave) and SPW slabs of K; K splits add into a zeroed Y.
+// Q4K batched decode with exact codes (a few to 32 tokens).  The structure of
+// gemm_bt_kernel -- four waves of 16 rows of W, X and the raw blocks staged
+// by direct loads in a ring of four slabs of 128 -- but the matrix cores see
+// the 4-bit codes u themselves, which bf16 holds exactly, and each 32-element
+// sub-block's scale and min are applied to its partial sums:
+//   y += S sum_k x u - Mn sum_k x,   S = d sc, Mn = dmin m (exact in fp32),
+// one v_mfma_f32_16x16x32_bf16 on the codes and one on ones (the sums of X)
+// per sub-block and 16-token tile.  Products are exact and only fp32 sums
+// round.  MFMA t of a slab covers sub-block t: lane (g, r) gives elements
+// 8g..8g+7 of it for row r.
+//   * Codes: a nibble 0..15 read as an E4M3 byte is the value u 2^-9, so
+//     v_cvt_scalef32_pk_bf16_fp8 with scale 2^9 turns two of them into a
+//     bf16 pair exactly; a byte permute first puts the nibbles of elements
+//     (0, 1, 4, 5) and (2, 3, 6, 7) in the bytes of two dwords.
+//   * Raw codes in LDS: sub-block c of row r at slot 4r + (c ^ ((r >> 2) & 3))
+//     (16-byte slots), so the dword reads of one sub-block by 64 lanes fall
+//     in distinct banks.
 // ---------------------------------------------------------------------------
-template <int SPW, bool FULL>
-__global__ __launch_bounds__(320) void gemm_bq_kernel(const uint8_t *__restrict__ B, int64_t sc_off,
+template <int TM>
+__global__ __launch_bounds__(256) void gemm_bx_kernel(const uint8_t *__restrict__ B, int64_t sc_off,
                                                       const uint16_t *__restrict__ X, float *__restrict__ Y, int M,
-                                                      int N, int K)
+                                                      int N, int K, int slabs_per_split)
 {
-    static_assert(SPW % 4 == 0, "whole slab quads");
-    constexpr int NQ = SPW / 4;
-    constexpr int XR = FULL ? 4 : 16;          // X rows staged per slab
-    constexpr int NSX = FULL ? 4 * SPW : SPW;  // slabs of X in LDS
-    __shared__ __attribute__((aligned(1024))) uint8_t sx[NSX * XR * 256];
-    __shared__ __attribute__((aligned(1024))) uint8_t sw[4][4096];
-    __shared__ f32x4_t sred[FULL ? 3 : 1][64];
+    constexpr int XSTG = 16 * TM * TBK * 2;  // bytes of one X stage
+    constexpr int RAWB = TRaw<FMT_Q4K>::bytes;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[TNS * (XSTG + RAWB)];
+    uint8_t *const sx = smem;
+    uint8_t *const sr = smem + TNS * XSTG;
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int g = lane >> 4, r16 = lane & 15;
-    const int nw0 = FULL ? blockIdx.x * 16 : blockIdx.x * 64 + 16 * wv;  // first row of this wave
-    const int sb = FULL ? wv * SPW : blockIdx.y * SPW;                   // first slab of this wave
-    const int sx0 = FULL ? 0 : sb;                                       // first slab staged in LDS
+    const int n0 = blockIdx.x * TBN, m0 = blockIdx.y * 16 * TM;
+    const int sb = blockIdx.z * slabs_per_split;
+    const int se = min(K / TBK, sb + slabs_per_split);
 
-    if (wv == 4) {
-        // X: row m of slab s at sx + (s XR + m) 256, 16-byte chunk c at slot c ^ m
-        const uint8_t *xb = reinterpret_cast<const uint8_t *>(X) + (int64_t)sx0 * 256;
-        for (int q = 0; 4 * q < M && q < XR / 4; q++) {
-            const int row = 4 * q + (lane >> 4);
-            const int c = (lane & 15) ^ row;
-            const uint32_t ox = (uint32_t)((min(row, M - 1) * K + 8 * c) * 2);
-            const uint32_t xs = lds_addr(sx) + 1024 * q;
-#pragma unroll 4
-            for (int s = 0; s < NSX; s++)
-                dma16(xb + 256 * s, ox, xs + XR * 256 * s);
-        }
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt 0, lgkmcnt 0
-        __builtin_amdgcn_s_barrier();
-        if constexpr (FULL)
-            lds_barrier();  // the quarter-sum barrier of the weight waves
-        return;
+    // X: as in gemm_bt_kernel (row m of a stage: chunk c of 8 elements at c ^ (m & 15))
+    uint32_t ox[TM];
+#pragma unroll
+    for (int j = 0; j < TM; j++) {
+        const int p = (4 * j + wv) * 64 + lane, row = p >> 4;
+        const int c = (p & 15) ^ (row & 15);
+        ox[j] = (uint32_t)(((int64_t)(min(m0 + row, M - 1) - m0) * K + 8 * c) * 2);
     }
+    const uint8_t *const xbase = reinterpret_cast<const uint8_t *>(X + (int64_t)m0 * K);
+    const int64_t g0 = (int64_t)n0 * (K / 256);
+    auto rn = [&](int row) { return (uint32_t)(min(n0 + row, N - 1) - n0); };  // rows past N: results dropped
+    // W codes: lane p of wave wv fills slot 64 wv + p of the codes region with
+    // sub-block c of row r, where slot = 4r + (c ^ ((r >> 2) & 3))
+    const int wslot = 64 * wv + lane, wrow = wslot >> 2, wsub = (wslot & 3) ^ ((wrow >> 2) & 3);
+    const uint32_t ocode = rn(wrow) * (uint32_t)(K / 2) + 16 * wsub;
 
-    const int64_t nrow = min(nw0 + r16, N - 1);  // the row this lane decodes (rows past N dropped)
-    uint4 cw[NQ][4];
-    uint4 hw[NQ][2];
-    auto issue = [&](int u) {
+    auto issue = [&](int s) {
+        const uint32_t xs = lds_addr(sx + (s % TNS) * XSTG);
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int64_t rr = min(nw0 + 4 * i + g, N - 1);
-            cw[u][i] = ld_nt16(B + 16 * (rr * (K / 32) + 4 * (sb + 4 * u) + r16));
-        }
-#pragma unroll
-        for (int e = 0; e < 2; e++)
-            hw[u][e] = *reinterpret_cast<const uint4 *>(B + sc_off + 16 * (nrow * (K / 256) + (sb + 4 * u) / 2 + e));
+        for (int j = 0; j < TM; j++)
+            dma16(xbase + 2 * TBK * s, ox[j], xs + (4 * j + wv) * 1024);
+        const uint32_t rs = lds_addr(sr + (s % TNS) * RAWB);
+        dma16(B + (int64_t)n0 * (K / 2) + 64 * s, ocode, rs + 1024 * wv);
+        if (lane < 16)
+            dma16(B + sc_off + 16 * (g0 + (s >> 1)), rn(16 * wv + lane) * (K / 16), rs + 4096 + 256 * wv);
     };
-    issue(0);
-    // the decode must not be hoisted above the wait for X
-    __builtin_amdgcn_sched_barrier(0);
+
+    const int row = 16 * wv + r16;  // the W row this lane decodes
+    typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+    auto pair = [](uint32_t w, bool h) {
+        return h ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 512.0f, true))
+                 : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 512.0f, false));
+    };
+    const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+
+    f32x4_t acc[TM];
+#pragma unroll
+    for (int j = 0; j < TM; j++)
+        acc[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    for (int s = sb; s < sb + TNS - 1 && s < se; s++)
+        issue(s);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt 0, lgkmcnt 0
     __builtin_amdgcn_s_barrier();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_sched_barrier(0);
 
-    uint8_t *const my = sw[wv];
-    const int xr = r16 & (XR - 1);  // FULL: X rows past 3 are not staged; their outputs are dropped
-    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    constexpr int VM = TM + TRaw<FMT_Q4K>::wd;
+    static_assert(VM < 16, "vmcnt immediate");
+    auto body = [&](int s, auto steady) {
+        constexpr bool ST = decltype(steady)::value;
+        const uint8_t *rs = sr + (s % TNS) * RAWB;
+        const uint8_t *xs = sx + (s % TNS) * XSTG;
+        const uint4 h = *reinterpret_cast<const uint4 *>(rs + 4096 + 16 * row);
+        const float d = h2f(h.x), dmin = h2f(h.x >> 16);
+        uint32_t w[4];
 #pragma unroll
-    for (int u = 0; u < NQ; u++) {
-        if (u + 1 < NQ)
-            issue(u + 1);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int rr = 4 * i + g;
-            *reinterpret_cast<uint4 *>(my + 256 * rr + 16 * (r16 ^ rr)) = cw[u][i];
-        }
+        for (int t = 0; t < 4; t++)
+            w[t] = *reinterpret_cast<const uint32_t *>(rs + 16 * (4 * row + (t ^ ((row >> 2) & 3))) + 4 * g);
 #pragma unroll
         for (int t = 0; t < 4; t++) {
-            const int s = sb + 4 * u + t;  // slab of the row
-            WBlk<FMT_Q4K> w;
-            w.c = *reinterpret_cast<const uint4 *>(my + 256 * r16 + 16 * ((4 * t + g) ^ r16));
-            w.h = hw[u][t >> 1];
-            uint32_t vh[16], vl[16];
-            decode_wblk<FMT_Q4K>(w, 4 * s + g, vh, vl);
-            const uint8_t *xs = sx + XR * 256 * (s - sx0);
+            // sub-block j of the group: its 6-bit scale and min
+            const int j = 4 * (s & 1) + t;
+            const uint32_t sc = __builtin_amdgcn_ubfe(h.y, 4 * j, 4) | (__builtin_amdgcn_ubfe(h.w, 2 * j, 2) << 4);
+            const uint32_t mq = __builtin_amdgcn_ubfe(h.z, 4 * j, 4) | (__builtin_amdgcn_ubfe(h.w, 16 + 2 * j, 2) << 4);
+            const float S = d * (float)sc, Mn = dmin * (float)mq;
+            // nibbles of elements (0,1,4,5) and (2,3,6,7): bytes 0, 2, 1, 3 of the dword
+            const uint32_t P = __builtin_amdgcn_perm(w[t], w[t], 0x03010200u);
+            const uint32_t lo = P & 0x0F0F0F0Fu, hi = (P >> 4) & 0x0F0F0F0Fu;
+            const bf16x8_t bw = __builtin_bit_cast(bf16x8_t, make_uint4(pair(lo, false), pair(hi, false),
+                                                                        pair(lo, true), pair(hi, true)));
 #pragma unroll
-            for (int q = 0; q < 4; q++) {
-                const bf16x8_t bh = __builtin_bit_cast(bf16x8_t, make_uint4(vh[4 * q], vh[4 * q + 1], vh[4 * q + 2], vh[4 * q + 3]));
-                const bf16x8_t bl = __builtin_bit_cast(bf16x8_t, make_uint4(vl[4 * q], vl[4 * q + 1], vl[4 * q + 2], vl[4 * q + 3]));
-                const bf16x8_t xa = *reinterpret_cast<const bf16x8_t *>(xs + 256 * xr + 16 * ((4 * g + q) ^ xr));
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bh, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bl, acc, 0, 0, 0);
+            for (int m = 0; m < TM; m++) {
+                const int xr = 16 * m + r16;
+                const bf16x8_t xa = *reinterpret_cast<const bf16x8_t *>(xs + 256 * xr + 16 * ((4 * t + g) ^ r16));
+                const f32x4_t D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bw, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+                const f32x4_t T = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, ones, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+                    acc[m][i] = fmaf(-Mn, T[i], fmaf(S, D[i], acc[m][i]));
             }
         }
-    }
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if constexpr (ST)
+            __builtin_amdgcn_s_waitcnt(0x0070 | VM);  // vmcnt VM, lgkmcnt 0
+        else
+            __builtin_amdgcn_s_waitcnt(0x0070);       // vmcnt 0, lgkmcnt 0
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if constexpr (ST)
+            issue(s + TNS - 1);
+    };
+    int s = sb;
+    for (; s + TNS - 1 < se; s++)
+        body(s, std::true_type{});
+    for (; s < se; s++)
+        body(s, std::false_type{});
 
-    // lane holds D[m = 4g + i][n = r16]
-    const int n = nw0 + r16;
-    if constexpr (FULL) {
-        if (wv > 0)
-            sred[wv - 1][lane] = acc;
-        lds_barrier();
-        if (wv == 0 && g == 0 && n < N) {
+    // lane holds D[m = 4g + i][n = r16] of each 16 x 16 tile
+    const bool split = gridDim.z > 1;
+    const int n = n0 + row;
+    if (n < N) {
 #pragma unroll
-            for (int w = 0; w < 3; w++) {
-                const f32x4_t o = sred[w][lane];
-                acc[0] += o[0];
-                acc[1] += o[1];
-                acc[2] += o[2];
-                acc[3] += o[3];
+        for (int j = 0; j < TM; j++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int m = m0 + 16 * j + 4 * g + i;
+                if (m < M) {
+                    if (split)
+                        atomicAdd(Y + (int64_t)m * N + n, acc[j][i]);
+                    else
+                        Y[(int64_t)m * N + n] = acc[j][i];
+                }
             }
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-                if (i < M)
-                    Y[(int64_t)i * N + n] = acc[i];
-        }
-    } else if (n < N) {
-        const bool split = gridDim.y > 1;
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int m = 4 * g + i;
-            if (m < M) {
-                if (split)
-                    atomicAdd(Y + (int64_t)m * N + n, acc[i]);
-                else
-                    Y[(int64_t)m * N + n] = acc[i];
-            }
-        }
     }
 }
 
@@ -1950,50 +1956,25 @@ hipError_t go_bt(const uint8_t *blocks, const Planes &p, const uint16_t *X, floa
     return hipGetLastError();
 }
 
-template <int SPW, bool FULL>
-hipError_t go_bq(const uint8_t *blocks, const Planes &p, const uint16_t *X, float *Y, int64_t M, int64_t N,
-                 int64_t K, hipStream_t s)
+// Split K towards ~1024 workgroups (four per CU), at least four slabs each.
+template <int TM>
+hipError_t go_bx(const uint8_t *blocks, const Planes &p, const uint16_t *X, float *Y, int64_t M, int64_t N, int64_t K,
+                 hipStream_t s)
 {
-    const int ks = FULL ? 1 : (int)(K / TBK) / SPW;
-    if (ks > 1) {
+    const int64_t gx = (N + TBN - 1) / TBN, gy = (M + 16 * TM - 1) / (16 * TM);
+    const int nslab = (int)(K / TBK);
+    int sp = 1;
+    while (sp < 32 && gx * gy * sp * 2 <= 1024 && nslab / (sp * 2) >= 4)
+        sp *= 2;
+    const int per = (nslab + sp - 1) / sp;
+    if (sp > 1) {
         const hipError_t e = zero_y(Y, M * N, s);
         if (e != hipSuccess)
             return e;
     }
-    const dim3 grid = FULL ? dim3((unsigned)((N + 15) / 16)) : dim3((unsigned)((N + 63) / 64), (unsigned)ks);
-    hipLaunchKernelGGL((gemm_bq_kernel<SPW, FULL>), grid, dim3(320), 0, s, blocks, p.scales, X, Y, (int)M, (int)N,
-                       (int)K);
+    hipLaunchKernelGGL((gemm_bx_kernel<TM>), dim3((unsigned)gx, (unsigned)gy, (unsigned)sp), dim3(256), 0, s, blocks,
+                       p.scales, X, Y, (int)M, (int)N, (int)K, per);
     return hipGetLastError();
-}
-
-// Q4K, M <= 16: the instances measured faster than gemm_bt_kernel on MI355X
-// (whole-K workgroups for up to 4 tokens at K = 14336 / 16384; otherwise K
-// ranges of 28, 20 or 16 slabs); false when none fits the shape
-bool pick_bq(const uint8_t *blocks, const Planes &p, const uint16_t *X, float *Y, int64_t M, int64_t N, int64_t K,
-             hipStream_t s, hipError_t &e)
-{
-    const int nslab = (int)(K / TBK);
-    if (M <= 4 && nslab == 112) {
-        e = go_bq<28, true>(blocks, p, X, Y, M, N, K, s);
-        return true;
-    }
-    if (M <= 4 && nslab == 128) {
-        e = go_bq<32, true>(blocks, p, X, Y, M, N, K, s);
-        return true;
-    }
-    if (nslab % 28 == 0) {
-        e = go_bq<28, false>(blocks, p, X, Y, M, N, K, s);
-        return true;
-    }
-    if (nslab % 20 == 0) {
-        e = go_bq<20, false>(blocks, p, X, Y, M, N, K, s);
-        return true;
-    }
-    if (nslab % 16 == 0) {
-        e = go_bq<16, false>(blocks, p, X, Y, M, N, K, s);
-        return true;
-    }
-    return false;
 }
 
 template <int FMT>
@@ -2006,11 +1987,8 @@ hipError_t bf16_by_m(const uint8_t *blocks, const Planes &p, const uint16_t *X, 
     // weight stream wins for up to 32 tokens once W has more than 2^24
     // elements
     if (M <= 32 && N * K > ((int64_t)1 << 24)) {
-        if constexpr (FMT == FMT_Q4K) {
-            hipError_t e;
-            if (M <= 16 && pick_bq(blocks, p, X, Y, M, N, K, s, e))
-                return e;
-        }
+        if constexpr (FMT == FMT_Q4K)
+            return M <= 16 ? go_bx<1>(blocks, p, X, Y, M, N, K, s) : go_bx<2>(blocks, p, X, Y, M, N, K, s);
         return M <= 16 ? go_bt<FMT, 1>(blocks, p, X, Y, M, N, K, s) : go_bt<FMT, 2>(blocks, p, X, Y, M, N, K, s);
     }
     const bool tall = N >= 32768;

@@ -117,14 +117,14 @@ MFMA_CASES = [
     ("bf16 64-token tiles", 40, 64, 1024),      # gemm_bf16_kernel<_, 4, 2>
     ("bf16 128-token tiles", 200, 8192, 4352),  # gemm_bf16_kernel<_, 8, 4>
     ("prefill tiles", 520, 256, 1024),          # gemm_pf_kernel (K split in two)
-    ("batched stream", 8, 4096, 4352),          # gemm_bt_kernel<_, 1>
-    ("batched stream 2 tiles", 24, 4096, 4352),  # gemm_bt_kernel<_, 2>
+    ("batched stream", 8, 4096, 4352),          # gemm_bt_kernel<_, 1> (Q4K: gemm_bx_kernel<1>)
+    ("batched stream 2 tiles", 24, 4096, 4352),  # gemm_bt_kernel<_, 2> (Q4K: gemm_bx_kernel<2>)
 ]
 Q4K_QUAD_CASES = [
-    ("quad whole K", 4, 1200, 14336),   # gemm_bq_kernel<28, true>
-    ("quad 28 slabs", 12, 1200, 14336),  # gemm_bq_kernel<28, false>
-    ("quad 20 slabs", 12, 1700, 10240),  # gemm_bq_kernel<20, false>
-    ("quad 16 slabs", 12, 2100, 8192),   # gemm_bq_kernel<16, false>
+    ("exact codes 4 tokens", 4, 1200, 14336),    # gemm_bx_kernel<1>, K split in 8
+    ("exact codes 12 tokens", 12, 1200, 14336),  # gemm_bx_kernel<1>
+    ("exact codes 20 slabs", 12, 1700, 10240),   # gemm_bx_kernel<1>
+    ("exact codes 2 tiles", 24, 2100, 8192),     # gemm_bx_kernel<2>
 ]
 
 

@@ -214,11 +214,11 @@ def test_mfma_bf16_batched_stream(fmt):
 
 
 def test_mfma_bf16_q4k_quad_stream():
-    """Q4K batched decode through the quad-load kernel: whole-K workgroups for
-    up to 4 tokens (K = 14336 and 16384), and K ranges of 28, 20 and 16 slabs
-    split over workgroups (K = 14336, 5120, 4096); rows ragged past the 16-
-    and 64-row tiles.  One-hot rows pin the layout: every weight to within
-    2^-17 of its value."""
+    """Q4K batched decode through the exact-code kernel (up to 32 tokens,
+    more than 2^24 weights): K = 14336, 16384, 5120 and 4096 split over
+    workgroups, rows ragged past the 16- and 64-row tiles.  One-hot rows pin
+    the layout: every weight to within 2^-17 of its value (the kernel gives
+    the fp32 weight itself: exact products, one rounding of S u - Mn)."""
     for N, K, Ms in ((1300, 14336, (1, 3, 4, 7, 16)), (1100, 16384, (2, 4)), (3300, 5120, (4, 13)),
                      (4150, 4096, (2, 9))):
         w = synth.weights_bf16(5300 + K, N, K, outliers=True)
