@@ -137,26 +137,57 @@ DECODER = [("q", 4096, 4096), ("k", 1024, 4096), ("v", 1024, 4096), ("o", 4096, 
            ("gate", 14336, 4096), ("up", 14336, 4096), ("down", 4096, 14336)]
 
 
-def test_isq_decoder_32_layers_sampled_rows():
-    """The 32-layer decoder's projections to Q4K (level 4) and the
-    131072x5120 output head to Q6K (promoted), drawn on the GPU; 16 random
-    rows of every tensor are checked byte for byte against the oracle."""
-    rng = np.random.Generator(np.random.PCG64(77))
-    for layer in range(32):
-        for kind, (name, N, K) in enumerate(DECODER):
-            fmt = ql.tensor_fmt(4, False)
-            W = synth.device_normal_bf16(synth.decoder_seed(layer, kind), (N, K), synth.W_SIGMA)
-            blocks = ql.isq(fmt, W)
-            sel = np.sort(rng.choice(N, 16, replace=False))
-            w_rows = from_dev_bf16(W[torch.from_numpy(sel).cuda()])
-            got = oracle.rows_of_buffer(fmt, blocks.cpu().numpy(), N, K, sel)
-            assert_blocks_equal(fmt, got, w_rows, f"layer {layer} {name}")
-            del W, blocks
-    N, K = 131072, 5120
+def _row_range_planes(fmt, buf, N, K, r0, r1):
+    """The planar buffer of rows [r0, r1) of a [N][K] buffer, made of the
+    contiguous slice of each plane (layout in oracle.c), zero-padded to the
+    16-byte multiple that a buffer of that many rows has."""
+    E = N * K
+    if fmt == "q6k":
+        G = E // 256
+        planes = [(0, K * 192 // 256), (192 * G, K // 16), (208 * G, K // 128)]
+    elif fmt == "q4k":
+        G = E // 256
+        planes = [(0, K // 2), (128 * G, K // 16)]
+    else:
+        raise ValueError(fmt)
+    out = np.concatenate([buf[off + r0 * per:off + r1 * per] for off, per in planes])
+    return np.concatenate([out, np.zeros(-out.size % 16, np.uint8)])  # buffer ends 16-aligned
+
+
+def _every_byte(fmt, W, label, chunk):
+    """Every byte of the GPU blocks of device tensor W against the oracle's
+    packing of its own quantization, row ranges of `chunk` rows at a time."""
+    N, K = W.shape
+    blocks = ql.isq(fmt, W).cpu().numpy()
+    nb = ql.blocks_bytes(fmt, N, K)
+    assert blocks.size == nb
+    if fmt == "q6k":
+        tail = blocks[210 * N * K // 256:]
+        assert not tail.any(), f"{label}: padding bytes not zero"
+    for r0 in range(0, N, chunk):
+        r1 = min(N, r0 + chunk)
+        w = from_dev_bf16(W[r0:r1])
+        got = _row_range_planes(fmt, blocks, N, K, r0, r1)
+        assert_blocks_equal(fmt, got, w, f"{label} rows {r0}..{r1}")
+        print(f"  {label}: rows {r0}..{r1} bit-exact", flush=True)
+
+
+def test_isq_head_q6k_every_byte():
+    """The 131072 x 5120 output head, promoted to Q6K: every byte of its 550 MB
+    of blocks equals the oracle's (page "Quantization types", section
+    "Sensitive tensor precision", promotes the head from Q4K to Q6K)."""
     fmt = ql.tensor_fmt(4, True)
     assert fmt == "q6k"
-    W = synth.device_normal_bf16(synth.LM_HEAD_W_SEED, (N, K), synth.W_SIGMA)
-    blocks = ql.isq(fmt, W)
-    sel = np.sort(rng.choice(N, 64, replace=False))
-    got = oracle.rows_of_buffer(fmt, blocks.cpu().numpy(), N, K, sel)
-    assert_blocks_equal(fmt, got, from_dev_bf16(W[torch.from_numpy(sel).cuda()]), "lm_head")
+    W = synth.device_normal_bf16(synth.LM_HEAD_W_SEED, (131072, 5120), synth.W_SIGMA)
+    _every_byte(fmt, W, "head", 16384)
+
+
+@pytest.mark.parametrize("layer", range(32))
+def test_isq_decoder_layer_every_byte(layer):
+    """Every byte of the Q4K blocks (level 4) of each of the 32 decoder
+    layers: q, k, v, o, gate, up and down, drawn on the GPU."""
+    fmt = ql.tensor_fmt(4, False)
+    for kind, (name, N, K) in enumerate(DECODER):
+        W = synth.device_normal_bf16(synth.decoder_seed(layer, kind), (N, K), synth.W_SIGMA)
+        _every_byte(fmt, W, f"layer {layer} {name}", 4096)
+        del W
