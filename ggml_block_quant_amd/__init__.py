@@ -21,7 +21,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libqlinear.so")
+# QLINEAR_LIB names another build of the same library (the host-sanitizer
+# build of tests/sanitize_host.py); there is no other implementation
+LIB_PATH = os.environ.get("QLINEAR_LIB") or os.path.join(_HERE, "libqlinear.so")
 
 FMT = {"q8_0": 0, "q4k": 1, "q6k": 2, "q2k": 3, "q3k": 4, "q5k": 5, "q8k": 6,
        "q4_0": 7, "q4_1": 8, "q5_0": 9, "q5_1": 10, "q8_1": 11, "fp8": 12}

@@ -21,7 +21,10 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIB names another build of oracle.c (the host-sanitizer build of
+# tests/sanitize_host.py), used as is
+_BUILT = os.path.join(_HERE, "liboracle.so")
+_LIB = os.environ.get("ORACLE_LIB") or _BUILT
 
 FORMATS = ("q8_0", "q4k", "q6k")
 # further formats (oracle.c, "Further formats"): K-quants and the legacy
@@ -34,13 +37,13 @@ MORE_FORMATS = tuple(KQ_FORMATS) + tuple(LEG_FORMATS)
 def build(force: bool = True) -> str:
     """Compile oracle.c into liboracle.so with gcc (plain C, OpenMP over
     independent rows/blocks only)."""
-    if force or not os.path.exists(_LIB):
+    if force or not os.path.exists(_BUILT):
         cmd = ["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp",
                "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC", _SRC,
-               "-o", _LIB + ".tmp", "-lm"]
+               "-o", _BUILT + ".tmp", "-lm"]
         subprocess.run(cmd, check=True)
-        os.replace(_LIB + ".tmp", _LIB)
-    return _LIB
+        os.replace(_BUILT + ".tmp", _BUILT)
+    return _BUILT
 
 
 _lib = None
