@@ -562,12 +562,13 @@ __global__ __launch_bounds__(512) void gemv_kernel(Geo g, const uint16_t *__rest
 }
 
 // ----------------------------------------------------------------------------
-// One-shot GEMV for one or two tokens.  Each wave owns R whole rows and
-// issues every weight load for them at once; the four waves of a workgroup
-// share one copy of X, staged in LDS (zero-padded to CPT*64 chunks) by the
-// workgroup before any weight is consumed.  The threads that stage X also
-// produce the per-chunk sums of the bias correction, so no wave recomputes
-// them.  There is no loop over rows: the grid covers N, and the weight bytes
+// One-shot GEMV for one to four tokens (while M times the chunks per lane
+// stays within 14, so that X fits the workgroup's LDS).  Each wave owns R
+// whole rows and issues every weight load for them at once; the four waves
+// of a workgroup share one copy of X, staged in LDS (zero-padded to CPT*64
+// chunks) by the workgroup before any weight is consumed.  The threads that
+// stage X also produce the per-chunk terms (Q4K: the sum of X over the
+// chunk; Q6K: its power-of-two scale), so no wave recomputes them.  There is no loop over rows: the grid covers N, and the weight bytes
 // of a wave are in flight from its first instructions.
 // ----------------------------------------------------------------------------
 constexpr int LW = 4;  // waves per workgroup of the one-shot kernel

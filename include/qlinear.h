@@ -117,7 +117,10 @@ enum {
 #define QLINEAR_MAX_N (1 << 24)
 #define QLINEAR_MAX_K (1 << 20)
 
-/* Bytes of the block buffer of a [N][K] tensor in `fmt`: 34*N*K/32 (Q8_0),
+/* Bytes of the block buffer of a [N][K] tensor in `fmt` (page "Quantization
+ * types", sections "Q*K family" and "Legacy GGML types": the formats and
+ * their bit widths; the byte counts per block are the formats' own):
+ * 34*N*K/32 (Q8_0),
  * 144*N*K/256 (Q4K), 210*N*K/256 rounded up to a multiple of 16 (Q6K; the
  * padding bytes are zero after isq_quantize).  Returns 0 for an unsupported
  * format or an invalid shape.  The buffer is made of planes, each 16-byte aligned
@@ -156,7 +159,11 @@ int isq_quantize(int fmt, const void *W_bf16, int64_t N, int64_t K, void *out_bl
  * layout as isq_quantize(QFMT_Q8_0, ...). */
 int q_act_quantize(const void *X_bf16, int64_t M, int64_t K, void *out_blocks, void *stream);
 
-/* Quantized matmul Y = X . deq(W)^T on the AUTO path (no workspace).
+/* Quantized matmul Y = X . deq(W)^T on the AUTO path (no workspace): the
+ * matrix-vector kernel for small decode batches and tiled MFMA kernels for
+ * larger ones (page "Quantization types", section "NVFP4", which splits a
+ * quantized linear layer's kernels that way; section "FP8": the weight tile
+ * is dequantized inside the GEMM).
  * blocks: device, from isq_quantize(fmt, W, N, K).  X_bf16: device [M][K].
  * Y_fp32: device [M][N], overwritten (not accumulated).
  * 1 <= M <= QLINEAR_MAX_M, K % 256 == 0; Q8_0 weights also take rows that end
@@ -165,7 +172,10 @@ int q_act_quantize(const void *X_bf16, int64_t M, int64_t K, void *out_blocks, v
 int qmatmul(int fmt, const void *blocks, const void *X_bf16, float *Y_fp32, int64_t M,
             int64_t N, int64_t K, void *stream);
 
-/* Workspace bytes `qmatmul_ex` needs for (fmt, path, M, K): the Q8_0 blocks
+/* Workspace bytes `qmatmul_ex` needs for (fmt, path, M, K) -- room for the
+ * activations quantized once per call and reused by every output tile (page
+ * "Quantization types", section "NVFP4"; section "FP8": dynamic per-token
+ * activation quantizers): the Q8_0 blocks
  * of X for QPATH_MFMA_I8 (q_blocks_bytes(QFMT_Q8_0, M, K)), its FP8 codes
  * and scales for QPATH_MFMA_FP8 (q_blocks_bytes(QFMT_FP8, M, K)), 0 otherwise. */
 size_t qmatmul_workspace_bytes(int fmt, int path, int64_t M, int64_t K);

@@ -1,5 +1,5 @@
 """GPU parity of the gated feed-forward projection (qmatmul_glu): the fused
-one-shot kernel (M <= 2, K <= 8192) and the two-matmul path with a
+one-shot kernel (M <= 4 where X fits its LDS budget, K <= 8192) and the two-matmul path with a
 workspace, against the oracle's h* = act(g*) u*.
 
 Bar: g and u each carry the matmul bar (1e-3 of sum_k |w||x|), so

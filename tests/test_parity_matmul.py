@@ -141,6 +141,23 @@ def test_gemv_one_and_two_tokens_all_widths(fmt):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_three_four_tokens_wide(fmt):
+    """Three and four tokens around the one-shot kernel's LDS budget (M times
+    chunks per lane at most 14): K = 6144 (three chunks per lane, both M
+    one-shot), K = 6400 (200 chunks in four slots per lane, ragged: three
+    tokens one-shot, four on the persistent kernel) and K = 8192 (likewise),
+    ragged N, on the GEMV path and on AUTO."""
+    for K, Ms in ((6144, (3, 4)), (6400, (3, 4)), (8192, (3, 4))):
+        for M in Ms:
+            for N in (5, 300):
+                w = synth.weights_bf16(5100 + K + N, N, K, outliers=True)
+                x = synth.activations_bf16(5101 + M, M, K)
+                Yr, den = a16_ref(fmt, w, x)
+                for path in ("gemv", "auto"):
+                    check_outputs(run(fmt, path, w, x), Yr, den, f"{path} {fmt} M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("M", [1, 2, 3, 4])
 def test_gemv_one_hot_is_exact_one_two_tokens(fmt, M):
     """The one-hot pin for the one-shot kernel (one to four tokens; four
