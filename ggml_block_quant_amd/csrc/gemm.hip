@@ -1203,6 +1203,145 @@ __global__ __launch_bounds__(256) void gemm_bx_kernel(const uint8_t *__restrict_
 }
 
 // ---------------------------------------------------------------------------
+// Q4K batched decode in one pass (up to 16 tokens).  A workgroup owns 16 rows
+// of W and all of K; its KW waves split K by 256-element groups (wave w:
+// groups [w G / KW, (w + 1) G / KW)) and add their partial results through
+// LDS at the end -- no K split across workgroups, hence no atomics and no
+// zero-fill launch.  Nothing is staged in LDS and the loop has no barrier:
+// each wave loads its weight blocks and its X straight into registers, DG
+// groups ahead, already in the layout of the v_mfma_f32_16x16x32_bf16
+// operands (all loads of a wave are register loads, so the compiler's
+// in-order vmcnt waits are exact).  DG = 1 measured fastest: 1 / 4 / 16
+// tokens at 4096 x 14336 ran 13.2 / 14.5 / 20.9 us with one group in
+// flight per wave, 13.5 / 15.2 / 20.9 with two, 15.4 / 17.6 / 22.3 with
+// four -- the kernel is bound by its VALU work and by the L2 reads of X
+// (every workgroup reads all of X), not by load latency.
+//   * B (W): lane (g, r) loads sub-block 4h + g of row r (its four octets)
+//     for each half h of a group; a 4 x 4 transpose across the four 16-lane
+//     rows (v_permlane32_swap, then v_permlane16_swap) leaves in dword t
+//     octet g of sub-block 4h + t: the lane's 8 elements of MFMA t.
+//   * A (X): lane (g, r) loads elements 8g..8g+7 of each sub-block for
+//     token r (tokens past M re-read token M - 1; their outputs are not
+//     stored).
+// The codes enter the MFMA exactly (as in gemm_bx_kernel); per sub-block j,
+// D = MFMA(x, u) is added as acc += S_j D, while MFMA(x, m_j), whose B holds
+// the 6-bit min code m_j at every k, accumulates sum_j m_j sum_k x over the
+// group, subtracted once per group as acc -= dmin * that.  Products are
+// exact and only fp32 sums round.
+// ---------------------------------------------------------------------------
+template <int KW, int DG>
+__global__ __launch_bounds__(64 * KW) void gemm_bs_kernel(const uint8_t *__restrict__ B, int64_t sc_off,
+                                                           const uint16_t *__restrict__ X, float *__restrict__ Y,
+                                                           int M, int N, int K)
+{
+    __shared__ f32x4_t red[KW - 1][64];
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int g = lane >> 4, r = lane & 15;
+    const int n0 = blockIdx.x * 16;
+    const int G = K / 256, S = K / 32;
+    const int gb = wv * G / KW, ng = (wv + 1) * G / KW - gb;
+    const int64_t row = min(n0 + r, N - 1);  // rows past N: results dropped
+    const int tok = min(r, M - 1);
+    const uint8_t *const wp = B + 16 * (row * S + 8 * gb + g);
+    const uint8_t *const hp = B + sc_off + 16 * (row * G + gb);
+    const uint16_t *const xp = X + (int64_t)tok * K + 256 * gb + 8 * g;
+
+    struct Stage {
+        uint4 w[2];  // sub-blocks g and 4 + g of the group
+        uint4 h;     // the group header of row r
+        uint4 x[8];  // elements 8g..8g+7 of each sub-block, token r
+    };
+    Stage st[DG];
+    auto issue = [&](Stage &q, int i) {
+        q.w[0] = ld_nt16(wp + 128 * i);
+        q.w[1] = ld_nt16(wp + 128 * i + 64);
+        q.h = *reinterpret_cast<const uint4 *>(hp + 16 * i);
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+            q.x[j] = *reinterpret_cast<const uint4 *>(xp + 256 * i + 32 * j);
+    };
+    auto pair = [](uint32_t w, bool h) {
+        return h ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 512.0f, true))
+                 : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 512.0f, false));
+    };
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    auto compute = [&](const Stage &q) {
+        const float d = h2f(q.h.x), dmin = h2f(q.h.x >> 16);
+        f32x4_t dm = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            uint32_t a0 = q.w[h].x, a1 = q.w[h].y, a2 = q.w[h].z, a3 = q.w[h].w;
+            const auto p02 = __builtin_amdgcn_permlane32_swap(a0, a2, false, false);
+            const auto p13 = __builtin_amdgcn_permlane32_swap(a1, a3, false, false);
+            const auto q01 = __builtin_amdgcn_permlane16_swap(p02[0], p13[0], false, false);
+            const auto q23 = __builtin_amdgcn_permlane16_swap(p02[1], p13[1], false, false);
+            const uint32_t wt[4] = {q01[0], q01[1], q23[0], q23[1]};
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                const int j = 4 * h + t;
+                const uint32_t sc = __builtin_amdgcn_ubfe(q.h.y, 4 * j, 4) | (__builtin_amdgcn_ubfe(q.h.w, 2 * j, 2) << 4);
+                const uint32_t mq = __builtin_amdgcn_ubfe(q.h.z, 4 * j, 4) | (__builtin_amdgcn_ubfe(q.h.w, 16 + 2 * j, 2) << 4);
+                const float Sj = d * (float)sc;
+                const uint32_t mb = __float_as_uint((float)mq) >> 16;  // bf16 of the integer m_j (exact)
+                const uint32_t mm = mb | (mb << 16);
+                const bf16x8_t bm = __builtin_bit_cast(bf16x8_t, make_uint4(mm, mm, mm, mm));
+                // nibbles of elements (0,1,4,5) and (2,3,6,7): bytes 0, 2, 1, 3 of the dword
+                const uint32_t P = __builtin_amdgcn_perm(wt[t], wt[t], 0x03010200u);
+                const uint32_t lo = P & 0x0F0F0F0Fu, hi = (P >> 4) & 0x0F0F0F0Fu;
+                const bf16x8_t bw = __builtin_bit_cast(bf16x8_t, make_uint4(pair(lo, false), pair(hi, false),
+                                                                            pair(lo, true), pair(hi, true)));
+                const bf16x8_t xa = __builtin_bit_cast(bf16x8_t, q.x[j]);
+                const f32x4_t D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bw, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+                dm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bm, dm, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+                    acc[i] = fmaf(Sj, D[i], acc[i]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            acc[i] = fmaf(-dmin, dm[i], acc[i]);
+    };
+
+#pragma unroll
+    for (int j = 0; j < DG; j++)
+        if (j < ng)
+            issue(st[j], j);
+    for (int i0 = 0; i0 < ng; i0 += DG) {
+#pragma unroll
+        for (int j = 0; j < DG; j++) {
+            const int i = i0 + j;
+            if (i < ng) {
+                compute(st[j]);
+                if (i + DG < ng)
+                    issue(st[j], i + DG);
+            }
+        }
+    }
+
+    // lane (g, r) holds tokens 4g..4g+3 of row r; wave 0 adds the others'
+    if (wv > 0)
+        red[wv - 1][lane] = acc;
+    __syncthreads();
+    if (wv == 0) {
+#pragma unroll
+        for (int w = 0; w < KW - 1; w++) {
+            const f32x4_t o = red[w][lane];
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                acc[i] += o[i];
+        }
+        const int n = n0 + r;
+        if (n < N)
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                if (4 * g + i < M)
+                    Y[(int64_t)(4 * g + i) * N + n] = acc[i];
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Generic MFMA GEMM (the formats without a tuned kernel): the structure of
 // gemm_bf16_kernel -- X slabs of 128 staged in LDS once per
 // workgroup and shared by its four waves, 16 TM tokens and 64 NT rows of W
@@ -1956,6 +2095,16 @@ hipError_t go_bt(const uint8_t *blocks, const Planes &p, const uint16_t *X, floa
     return hipGetLastError();
 }
 
+// one workgroup per 16 rows, K split over its KW waves
+template <int KW, int DG>
+hipError_t go_bs(const uint8_t *blocks, const Planes &p, const uint16_t *X, float *Y, int64_t M, int64_t N, int64_t K,
+                 hipStream_t s)
+{
+    hipLaunchKernelGGL((gemm_bs_kernel<KW, DG>), dim3((unsigned)((N + 15) / 16)), dim3(64 * KW), 0, s, blocks,
+                       p.scales, X, Y, (int)M, (int)N, (int)K);
+    return hipGetLastError();
+}
+
 // Split K towards ~1024 workgroups (four per CU), at least four slabs each.
 template <int TM>
 hipError_t go_bx(const uint8_t *blocks, const Planes &p, const uint16_t *X, float *Y, int64_t M, int64_t N, int64_t K,
@@ -1985,10 +2134,15 @@ hipError_t bf16_by_m(const uint8_t *blocks, const Planes &p, const uint16_t *X, 
     // launch shapes from measured sweeps on MI355X (4096 x 14336,
     // 14336 x 4096, 4096 x 4096 and 131072 x 5120 weights): the direct-load
     // weight stream wins for up to 32 tokens once W has more than 2^24
-    // elements
+    // elements; for Q4K the one-pass kernel up to five tokens (4096 x 14336,
+    // eager launches: 1 / 4 / 8 / 16 tokens 13.4 / 14.8 / 17.1 / 21.0 us
+    // against 16.9 / 17.3 / 17.3 / 17.2 us for the ring kernel and its
+    // zero-fill launch; 14336 x 4096: 14.3 / 16.5 / 18.1 / 22.8 against
+    // 17.5 / 18.1 / 17.6 / 17.9 us)
     if (M <= 32 && N * K > ((int64_t)1 << 24)) {
         if constexpr (FMT == FMT_Q4K)
-            return M <= 16 ? go_bx<1>(blocks, p, X, Y, M, N, K, s) : go_bx<2>(blocks, p, X, Y, M, N, K, s);
+            return M <= 5 ? go_bs<8, 1>(blocks, p, X, Y, M, N, K, s)
+                   : M <= 16 ? go_bx<1>(blocks, p, X, Y, M, N, K, s) : go_bx<2>(blocks, p, X, Y, M, N, K, s);
         return M <= 16 ? go_bt<FMT, 1>(blocks, p, X, Y, M, N, K, s) : go_bt<FMT, 2>(blocks, p, X, Y, M, N, K, s);
     }
     const bool tall = N >= 32768;

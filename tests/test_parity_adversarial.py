@@ -121,7 +121,10 @@ MFMA_CASES = [
     ("batched stream 2 tiles", 24, 4096, 4352),  # gemm_bt_kernel<_, 2> (Q4K: gemm_bx_kernel<2>)
 ]
 Q4K_QUAD_CASES = [
-    ("exact codes 4 tokens", 4, 1200, 14336),    # gemm_bx_kernel<1>, K split in 8
+    ("one pass 1 token", 1, 1201, 14336),        # gemm_bs_kernel (rows past N in the last workgroup)
+    ("one pass 5 tokens", 5, 1200, 14336),       # gemm_bs_kernel
+    ("one pass 17 groups", 3, 4100, 4352),       # gemm_bs_kernel: 2 or 3 groups per wave
+    ("exact codes 6 tokens", 6, 1200, 14336),    # gemm_bx_kernel<1>, K split in 8
     ("exact codes 12 tokens", 12, 1200, 14336),  # gemm_bx_kernel<1>
     ("exact codes 20 slabs", 12, 1700, 10240),   # gemm_bx_kernel<1>
     ("exact codes 2 tiles", 24, 2100, 8192),     # gemm_bx_kernel<2>
