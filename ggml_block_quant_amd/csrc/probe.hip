@@ -5,13 +5,16 @@
 //
 //   * read_probe_kernel: every byte of a buffer read once with 16-byte
 //     non-temporal loads (the weight stream of the GEMV kernels), each
-//     workgroup a contiguous span, eight loads in flight per thread;
+//     workgroup a contiguous span, eight loads in flight per thread (the
+//     grid shrinks for small buffers so that each thread has eight);
 //     nothing is written unless the XOR of all
 //     loaded words equals a value that the caller's buffer contents make
 //     impossible in practice, so the loads stay live.
 //   * mfma_probe_kernel: dependent chains of v_mfma_f32_32x32x16_bf16 on
 //     four accumulators per wave, eight waves per workgroup (two per SIMD),
 //     no memory traffic inside the loop.
+#include <algorithm>
+
 #include "qlinear_internal.h"
 
 namespace ql {
@@ -79,8 +82,14 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_probe_kernel(float *__restr
 
 hipError_t launch_read_probe(const void *buf, int64_t bytes, float *out, hipStream_t s)
 {
-    hipLaunchKernelGGL(read_probe_kernel, dim3(kReadBlocks), dim3(kReadThreads), 0, s,
-                       static_cast<const u32x4_t *>(buf), bytes / 16, out);
+    // at most kReadBlocks workgroups, fewer for small buffers so that every
+    // thread still has a full batch of kInFlight loads (a 33 MB buffer: 1008
+    // workgroups, one batch each)
+    const int64_t n16 = bytes / 16;
+    const int64_t per_wg = (int64_t)kReadThreads * 8;
+    const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>(kReadBlocks, n16 / per_wg));
+    hipLaunchKernelGGL(read_probe_kernel, dim3((unsigned)blocks), dim3(kReadThreads), 0, s,
+                       static_cast<const u32x4_t *>(buf), n16, out);
     return hipGetLastError();
 }
 

@@ -379,6 +379,30 @@ def test_workload_batched_decode_down_proj():
             check_outputs(y, Yr, den, "down-proj M=4 gemv")
 
 
+def test_qkv_concatenated_launch():
+    """The q, k and v projections of a layer quantized as one [6144][4096]
+    Q4K tensor: its blocks are the three tensors' blocks row after row (ISQ
+    works per row), and one launch gives every output within the bar, for
+    one to four tokens on AUTO and on the GEMV path."""
+    parts = [synth.weights_bf16(synth.seed_for(2, 10 + t), n, 4096) for t, n in enumerate((4096, 1024, 1024))]
+    w = np.concatenate(parts)
+    blocks = ql.isq("q4k", to_dev_bf16(w)).cpu().numpy()
+    r0 = 0
+    for t, wt in enumerate(parts):
+        rows = np.arange(r0, r0 + wt.shape[0])
+        sep = ql.isq("q4k", to_dev_bf16(wt)).cpu().numpy()
+        assert np.array_equal(oracle.rows_of_buffer("q4k", blocks, 6144, 4096, rows), sep), f"part {t}"
+        r0 += wt.shape[0]
+    W = oracle.dequant("q4k", oracle.quantize("q4k", w), 6144, 4096)
+    x = synth.activations_bf16(synth.seed_for(2, 13), 4, 4096)
+    dev = torch.from_numpy(blocks).cuda()
+    for M in (1, 2, 3, 4):
+        Yr, den = oracle.matmul_a16(W, x[:M])
+        for path in ("auto", "gemv"):
+            y = ql.qmatmul("q4k", dev, to_dev_bf16(x[:M]), 6144, path=path).cpu().numpy()
+            check_outputs(y, Yr, den, f"qkv 6144x4096 M={M} {path}")
+
+
 def _sampled(N, M, count, seed):
     rng = np.random.Generator(np.random.PCG64(seed))
     return rng.integers(0, M, count), rng.integers(0, N, count)
