@@ -1046,11 +1046,97 @@ __global__ __launch_bounds__(256) void gemv_gen_kernel(const uint8_t *__restrict
             Y[(int64_t)m * N + n] = acc[m];
 }
 
+// The same arithmetic with X staged once per workgroup in LDS and R rows per
+// wave (while M * K * 2 bytes of X fit 64 KiB): the kernel above reads X
+// from the caches once per row, so for one token its X traffic (K * 2 bytes
+// per row) is larger than the weights it streams; here each 16-byte slice of
+// X is read from LDS once per wave and applied to R rows.
+template <int FMT, int M, int R>
+__global__ __launch_bounds__(256) void gemv_genx_kernel(const uint8_t *__restrict__ B, Planes p,
+                                                        const uint16_t *__restrict__ X, float *__restrict__ Y,
+                                                        int64_t N, int K)
+{
+    extern __shared__ uint4 sxs[];  // X as [M][K / 8] 16-byte slices
+    const int T = K / 8;
+    for (int i = threadIdx.x; i < M * T; i += 256)
+        sxs[i] = *reinterpret_cast<const uint4 *>(X + 8 * (int64_t)i);
+    __syncthreads();
+    const int lane = threadIdx.x & 63;
+    const int64_t n0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * R;
+    float acc[R][M];
+#pragma unroll
+    for (int r = 0; r < R; r++)
+#pragma unroll
+        for (int m = 0; m < M; m++)
+            acc[r][m] = 0.0f;
+    constexpr int U = 4;  // tasks per lane per step, all loads of a step in flight together
+    for (int i0 = 0; i0 < T; i0 += 64 * U) {
+        float w[R][U][8];
+        int ic[U];
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            ic[u] = min(i0 + 64 * u + lane, T - 1);
+#pragma unroll
+            for (int r = 0; r < R; r++)
+                dequant8<FMT>(B, p, min(n0 + r, N - 1) * T + ic[u], w[r][u]);  // rows past N: not stored
+        }
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const bool live = i0 + 64 * u + lane < T;
+#pragma unroll
+            for (int m = 0; m < M; m++) {
+                const uint4 xv = sxs[m * T + ic[u]];
+                const uint32_t xw[4] = {live ? xv.x : 0u, live ? xv.y : 0u, live ? xv.z : 0u, live ? xv.w : 0u};
+#pragma unroll
+                for (int r = 0; r < R; r++)
+#pragma unroll
+                    for (int k = 0; k < 4; k++) {
+                        acc[r][m] = fmaf(w[r][u][2 * k], __uint_as_float(xw[k] << 16), acc[r][m]);
+                        acc[r][m] = fmaf(w[r][u][2 * k + 1], __uint_as_float(xw[k] & 0xffff0000u), acc[r][m]);
+                    }
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < R; r++)
+#pragma unroll
+        for (int m = 0; m < M; m++)
+#pragma unroll
+            for (int k = 32; k >= 1; k >>= 1)
+                acc[r][m] += __shfl_xor(acc[r][m], k);
+    if (lane == 0)
+#pragma unroll
+        for (int r = 0; r < R; r++)
+            if (n0 + r < N)
+#pragma unroll
+                for (int m = 0; m < M; m++)
+                    Y[(int64_t)m * N + n0 + r] = acc[r][m];
+}
+
 template <int FMT>
 hipError_t gen_by_m(const uint8_t *blocks, const Planes &p, const uint16_t *X, float *Y, int M, int64_t N,
                     int64_t K, hipStream_t s)
 {
-    const dim3 grid((unsigned)((N + 3) / 4)), block(256);
+    const dim3 block(256);
+    // X in LDS, two rows per wave (14336 x 4096, microseconds before -> after:
+    // one token Q5K 22.8 -> 21.2, Q2K 13.7 -> 11.9, Q4_0 13.6 -> 11.8, Q5_1
+    // 16.3 -> 14.2; three tokens Q3K 41.5 -> 25.1, Q4_0 29.8 -> 17.6, Q5_0
+    // 32.5 -> 20.6); four FP8 tokens measured slower (37.2 -> 41.0)
+    if (M * K * 2 <= 65536 && !(FMT == FMT_FP8 && M >= 4)) {
+        const dim3 grid2((unsigned)((N + 7) / 8));
+        const size_t lds = (size_t)M * K * 2;
+        switch (M) {
+#define C(MM)                                                                                                   \
+    case MM:                                                                                                    \
+        hipLaunchKernelGGL((gemv_genx_kernel<FMT, MM, 2>), grid2, block, lds, s, blocks, p, X, Y, N, (int)K); \
+        break;
+            C(1) C(2) C(3) C(4) C(5) C(6) C(7) C(8)
+#undef C
+        default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
+    const dim3 grid((unsigned)((N + 3) / 4));
     switch (M) {
 #define C(MM) \
     case MM: hipLaunchKernelGGL((gemv_gen_kernel<FMT, MM>), grid, block, 0, s, blocks, p, X, Y, N, (int)K); break;
