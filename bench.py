@@ -17,6 +17,8 @@ The same run measures, each with its own roofline block:
     on the int8 path (activation quantization included), and FP8 W8A8 at the
     same shape;
   * ISQ of the whole decoder and head; the head GEMV for eight tokens;
+  * the further formats and FP8 at 14336 x 4096 (ISQ, one-token GEMV,
+    16-token MFMA path);
   * equivalent decode tokens/s of the decoder (every projection GEMV of the
     32 layers plus the head, with q/k/v as one concatenated launch and
     gate/up as one fused SiLU launch);
@@ -57,7 +59,7 @@ MALL_BYTES = 256 << 20        # Infinity Cache
 HEAD_N, HEAD_K = 131072, 5120
 DECODER_SHAPES = [(4096, 4096), (1024, 4096), (1024, 4096), (4096, 4096), (14336, 4096), (14336, 4096),
                   (4096, 14336)]  # q, k, v, o, gate, up, down: [out][in]
-ALL_PARTS = ("gemv", "batched", "prefill", "model", "ceilings", "crossover", "glu")
+ALL_PARTS = ("gemv", "batched", "prefill", "model", "ceilings", "crossover", "glu", "formats")
 
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gemv_q6k_131072x5120_m1_traffic.md")
 TRAFFIC_SOURCES = [os.path.join(ROOT, "ggml_block_quant_amd", "csrc", f) for f in ("gemv.hip", "qlinear_internal.h")]
@@ -320,6 +322,8 @@ def main():
         parts.update(part_glu(torch, ql, synth, run, dev, bf16_dev))
     if "prefill" in which:
         parts.update(part_prefill(torch, ql, synth, run, dev, bf16_dev))
+    if "formats" in which:
+        parts.update(part_formats(torch, ql, synth, run, dev, bf16_dev))
     if "ceilings" in which:
         parts.update(part_ceilings(torch, ql, run, dev))
     result["parts"] = parts
@@ -564,6 +568,51 @@ def part_glu(torch, ql, synth, run, dev, bf16_dev):
                    f"gemv_lds_kernel<Q4K, M={M}, GLU>"), "two_gemvs_us": round(sep["median"] * 1e3, 2)}
         log(f"glu M={M}: fused {fused['median'] * 1e3:.2f} us, two GEMVs {sep['median'] * 1e3:.2f} us")
     del cg, cu, bg, bu
+    torch.cuda.empty_cache()
+    return parts
+
+
+def part_formats(torch, ql, synth, run, dev, bf16_dev):
+    """The further formats (Q5K, Q3K, Q2K, Q4_0, Q4_1, Q5_0, Q5_1) and FP8
+    (W8A16) at 14336 x 4096: ISQ, the one-token GEMV and the 16-token MFMA
+    path, each output checked against the oracle on sampled rows."""
+    import oracle
+
+    parts = {}
+    N, K = 14336, 4096
+    w = synth.weights_bf16(synth.seed_for(2, 0), N, K)
+    x = synth.activations_bf16(synth.seed_for(2, 2), 16, K)
+    W = bf16_dev(w)
+    X = bf16_dev(x)
+    rows = sample_rows(N, 128, 3)
+    for fmt in oracle.MORE_FORMATS + ("fp8",):
+        B = ql.isq(fmt, W)
+        out = torch.empty_like(B)
+        t_isq = run.time(lambda i: ql.isq(fmt, W, out=out), 4)
+        if fmt == "fp8":
+            Wd = oracle.dequant_fp8(oracle.quantize_fp8(w[rows]))
+        else:
+            Wd = oracle.dequant(fmt, oracle.quantize(fmt, w[rows]), len(rows), K)
+        R = copies_for(B.numel())
+        cp = [B] + [B.clone() for _ in range(R - 1)]
+        entry = {"isq_us": round(t_isq["median"] * 1e3, 2),
+                 "isq_GBps": round((2 * N * K + B.numel()) / t_isq["median"] / 1e6, 1), "weight_bytes": B.numel()}
+        for M, path in ((1, "gemv"), (16, "mfma_bf16")):
+            Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+            ql.qmatmul(fmt, B, X[:M], N, out=Y, path=path)
+            Yr, den = oracle.matmul_a16(Wd, x[:M])
+            e = float(oracle.normalized_error(Y.cpu().numpy()[:, rows], Yr, den).max())
+            if e > 1e-3:
+                raise SystemExit(f"parity failure: {fmt} {path} M={M}: {e:.3e}")
+            t = run.time(lambda i: ql.qmatmul(fmt, cp[i % R], X[:M], N, out=Y, path=path), R)
+            entry[f"m{M}"] = {**roof("hbm", B.numel() + M * K * 2 + M * N * 4, t, HBM_PEAK_GBPS, "GB/s",
+                                     "gemv_fp8_kernel" if (fmt == "fp8" and M <= 2) else
+                                     ("gemv_genx_kernel" if M == 1 else "gemm_gen_lds_kernel")),
+                              "parity_max_err": e}
+        parts[f"format_{fmt}_14336x4096"] = entry
+        log(f"format {fmt}: ISQ {entry['isq_us']} us, GEMV M=1 {entry['m1']['us_median']} us, "
+            f"MFMA M=16 {entry['m16']['us_median']} us")
+        del cp, B, out
     torch.cuda.empty_cache()
     return parts
 
