@@ -1347,9 +1347,11 @@ __global__ __launch_bounds__(64 * KW) void gemm_bs_kernel(const uint8_t *__restr
 // workgroup and shared by its four waves, 16 TM tokens and 64 NT rows of W
 // per workgroup -- with the weights decoded by the shared exact decoder
 // (dequant8) straight from the blocks: lane (g, r) decodes block 4s + g of
-// its rows in slab s, rounds it to bf16 and feeds four
-// v_mfma_f32_16x16x32_bf16 steps.  Each weight is decoded once per 16 TM
-// tokens, and X is read once per workgroup rather than once per wave.
+// its rows in slab s into bf16 hi + lo pairs and feeds four pairs of
+// v_mfma_f32_16x16x32_bf16 steps.  FP8 (W8A16) takes its E4M3 codes, exact
+// in bf16, as one operand and multiplies the sums by the row scale at the
+// end.  Each weight is decoded once per 16 TM tokens, and X is read once
+// per workgroup rather than once per wave.
 // ---------------------------------------------------------------------------
 template <int FMT, int TM, int NT>
 __global__ __launch_bounds__(256) void gemm_gen_lds_kernel(const uint8_t *__restrict__ B, Planes p,
@@ -1413,20 +1415,37 @@ __global__ __launch_bounds__(256) void gemm_gen_lds_kernel(const uint8_t *__rest
         for (int i = 0; i < NT; i++) {
 #pragma unroll
             for (int t = 0; t < 4; t++) {
-                float w[8];
-                dequant8<FMT>(B, p, wpiece[i] + 16 * s + 4 * g + t, w);
-                uint32_t h[4], l[4];
+                if constexpr (FMT == FMT_FP8) {
+                    // E4M3 codes are exact in bf16: one MFMA on the codes, the
+                    // row scale applied to the sums at the end
+                    const uint2 c = reinterpret_cast<const uint2 *>(B)[wpiece[i] + 16 * s + 4 * g + t];
+                    const bf16x8_t bc = __builtin_bit_cast(
+                        bf16x8_t, make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.0f, false)),
+                                             __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.0f, true)),
+                                             __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.0f, false)),
+                                             __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.0f, true))));
 #pragma unroll
-                for (int e = 0; e < 4; e++)
-                    split_bf16(w[2 * e], w[2 * e + 1], h[e], l[e]);
-                const bf16x8_t bh = __builtin_bit_cast(bf16x8_t, make_uint4(h[0], h[1], h[2], h[3]));
-                const bf16x8_t bl = __builtin_bit_cast(bf16x8_t, make_uint4(l[0], l[1], l[2], l[3]));
+                    for (int j = 0; j < TM; j++) {
+                        const bf16x8_t xa = *reinterpret_cast<const bf16x8_t *>(
+                            &sX[buf][(16 * j + r16) * XPITCH + 64 * g + 16 * t]);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bc, acc[i][j], 0, 0, 0);
+                    }
+                } else {
+                    float w[8];
+                    dequant8<FMT>(B, p, wpiece[i] + 16 * s + 4 * g + t, w);
+                    uint32_t h[4], l[4];
 #pragma unroll
-                for (int j = 0; j < TM; j++) {
-                    const bf16x8_t xa = *reinterpret_cast<const bf16x8_t *>(
-                        &sX[buf][(16 * j + r16) * XPITCH + 64 * g + 16 * t]);
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bh, acc[i][j], 0, 0, 0);
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bl, acc[i][j], 0, 0, 0);
+                    for (int e = 0; e < 4; e++)
+                        split_bf16(w[2 * e], w[2 * e + 1], h[e], l[e]);
+                    const bf16x8_t bh = __builtin_bit_cast(bf16x8_t, make_uint4(h[0], h[1], h[2], h[3]));
+                    const bf16x8_t bl = __builtin_bit_cast(bf16x8_t, make_uint4(l[0], l[1], l[2], l[3]));
+#pragma unroll
+                    for (int j = 0; j < TM; j++) {
+                        const bf16x8_t xa = *reinterpret_cast<const bf16x8_t *>(
+                            &sX[buf][(16 * j + r16) * XPITCH + 64 * g + 16 * t]);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bh, acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bl, acc[i][j], 0, 0, 0);
+                    }
                 }
             }
         }
@@ -1443,6 +1462,14 @@ __global__ __launch_bounds__(256) void gemm_gen_lds_kernel(const uint8_t *__rest
 #pragma unroll
     for (int i = 0; i < NT; i++) {
         const int64_t n = n_wave + 16 * i + r16;
+        if constexpr (FMT == FMT_FP8) {
+            const float sc = reinterpret_cast<const float *>(B + p.scales)[min(n, (int64_t)N - 1)];
+#pragma unroll
+            for (int j = 0; j < TM; j++)
+#pragma unroll
+                for (int r = 0; r < 4; r++)
+                    acc[i][j][r] *= sc;
+        }
         if (n >= N)
             continue;
 #pragma unroll
