@@ -477,6 +477,10 @@ def test_graph_replays_match_eager():
     cases = [("q4k", "gemv", 1, 4096, 4096, True),
              ("q6k", "gemv", 2, 300, 1024, True),
              ("q4k", "mfma_bf16", 16, 4100, 4352, False),   # batched stream, split K
+             ("q4k", "mfma_bf16", 4, 4100, 4352, True),     # one-pass batched kernel (LDS reduction)
+             ("q5k", "mfma_bf16", 16, 300, 1024, False),    # generic LDS-staged MFMA
+             ("fp8", "mfma_bf16", 16, 300, 1024, False),    # FP8 W8A16 on exact codes
+             ("q3k", "gemv", 3, 300, 1024, True),           # generic GEMV, X in LDS
              ("q8_0", "mfma_bf16", 128, 255, 4096, False),  # 128 x 256 tiles, split K
              ("q8_0", "mfma_bf16", 640, 255, 4096, False),  # prefill tiles, split K
              ("q8_0", "mfma_bf16", 1024, 1024, 512, True),  # prefill tiles, no split
