@@ -164,6 +164,28 @@ __device__ __forceinline__ float bf16_pair_absmax(uint32_t p, float m)
     return fmaxf(m, fmaxf(fabsf(__uint_as_float(p << 16)), fabsf(__uint_as_float(p & 0xffff0000u))));
 }
 
+// Smallest nonzero magnitude of two bf16 values, as (magnitude bits - 1) in
+// 16 bits: a zero wraps to 0xFFFF and never wins; min with m (same form).
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u16x2_t bf16_pair_minnz(uint32_t p, u16x2_t m)
+{
+    const u16x2_t a = __builtin_bit_cast(u16x2_t, p & 0x7FFF7FFFu) - u16x2_t{1, 1};
+    return __builtin_elementwise_min(a, m);
+}
+
+// A Q6K chunk's activations are staged in fp16 after scaling the largest
+// magnitude into [2^14, 2^15); every nonzero bf16 value of at least 2^-28 of
+// that maximum is then exact in fp16 (at least 2^-14, a normal).  A chunk
+// holding a smaller nonzero value is flagged: the dot product takes the exact
+// fp32 path for it.  Flagged exponents carry +1024.
+constexpr int Q6K_EXACT_FLAG = 1024;
+__device__ __forceinline__ int chunk_exp_flagged(float amax, uint32_t minnz1)
+{
+    const int e = chunk_exp(amax);
+    const bool tiny = minnz1 != 0xFFFFu && __uint_as_float((minnz1 + 1u) << 16) < __builtin_amdgcn_ldexpf(amax, -28);
+    return tiny ? e + Q6K_EXACT_FLAG : e;
+}
+
 // Loop-invariant constants held in VGPRs: a VOP3 and-or on gfx950 takes at
 // most one SGPR/constant operand, so the masks live in registers and the
 // bias in an SGPR, which gives one v_and_or_b32 per bf16 pair.
@@ -232,7 +254,7 @@ __device__ __forceinline__ void q4k_dot(const Chunk<FMT_Q4K> &ck, const XChunk<M
 // a shift of lw per pair.  v_pk_add_f16 then leaves q or 16 q exactly.
 template <int M>
 __device__ __forceinline__ void q6k_dot(const Chunk<FMT_Q6K> &ck, const XChunk<M> &x, float acc[M],
-                                        const Masks &k)
+                                        const Masks &k, const uint16_t *__restrict__ xg, int64_t K)
 {
     const float d = h2f(ck.d);
     const float Sa = d * (float)(int8_t)(ck.sc2 & 0xffu);
@@ -258,6 +280,32 @@ __device__ __forceinline__ void q6k_dot(const Chunk<FMT_Q6K> &ck, const XChunk<M
     }
 #pragma unroll
     for (int m = 0; m < M; m++) {
+        if (x.e[m] >= Q6K_EXACT_FLAG / 2) {
+            // exact path: the chunk's bf16 activations from memory (xg: chunk
+            // of token 0, rows K apart) times the codes, fp32 products (exact)
+            // and sums; pair j of the codes holds elements 2j, 2j+1 (q, or 16 q
+            // for odd j % 4), as does dword j of X
+            const uint4 *xq = reinterpret_cast<const uint4 *>(xg + (int64_t)m * K);
+            float a1 = 0.0f, a16 = 0.0f, b1 = 0.0f, b16 = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const uint4 v = xq[q];
+                const uint32_t xd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int t = 0; t < 4; t++) {
+                    const uint32_t pv = pr[4 * q + t];
+                    float r = (float)__builtin_bit_cast(_Float16, (uint16_t)(pv & 0xffffu)) * __uint_as_float(xd[t] << 16);
+                    r = fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)(pv >> 16)), __uint_as_float(xd[t] & 0xffff0000u), r);
+                    if (q < 2)
+                        (t & 1 ? a16 : a1) += r;
+                    else
+                        (t & 1 ? b16 : b1) += r;
+                }
+            }
+            const float da = fmaf(a16, 0.0625f, a1), db = fmaf(b16, 0.0625f, b1);
+            acc[m] += fmaf(Sa, da, Sb * db);
+            continue;
+        }
         // sub-block a (octets 0, 1) and b (octets 2, 3); the pairs holding
         // 16 q in their own sums
         float a1 = 0.0f, a16 = 0.0f, b1 = 0.0f, b16 = 0.0f;
@@ -427,7 +475,8 @@ __device__ __forceinline__ void load_batch(const Geo &g, int64_t b, int64_t N, c
 
 template <int FMT, int M, int CPT, int R>
 __device__ __forceinline__ void process_batch(const Batch<FMT, M, CPT, R> &bt, const XChunk<M> (&xr)[CPT],
-                                              const int (&cj)[CPT], const Masks &k, int64_t b, int64_t N,
+                                              const int (&cj)[CPT], const int (&cl)[CPT],
+                                              const uint16_t *__restrict__ X, int K, const Masks &k, int64_t b, int64_t N,
                                               float *__restrict__ Y, int lane, int wv, int KS,
                                               float (*part)[pow2_at_least(R * M)])
 {
@@ -447,7 +496,7 @@ __device__ __forceinline__ void process_batch(const Batch<FMT, M, CPT, R> &bt, c
             if constexpr (FMT == FMT_Q4K)
                 q4k_dot<M>(bt.ck[r][i], xr[i], cj[i], acc);
             else if constexpr (FMT == FMT_Q6K)
-                q6k_dot<M>(bt.ck[r][i], xr[i], acc, k);
+                q6k_dot<M>(bt.ck[r][i], xr[i], acc, k, X + 32 * (int64_t)cl[i], K);
             else
                 q8_0_dot<M>(bt.ck[r][i], xr[i], acc);
         }
@@ -517,13 +566,18 @@ __global__ __launch_bounds__(512) void gemv_kernel(Geo g, const uint16_t *__rest
             // Q4K: pairs (i, i+4) of each octet and the chunk sum; Q6K: the
             // chunk scaled by 2^e in fp16; Q8_0: as loaded
             float amax = 0.0f, sum = 0.0f;
+            u16x2_t mnz = {0xFFFF, 0xFFFF};
 #pragma unroll
             for (int t = 0; t < 4; t++) {
                 const uint32_t v[4] = {q[t].x, q[t].y, q[t].z, q[t].w};
 #pragma unroll
                 for (int c = 0; c < 4; c++) {
-                    sum = dot2(v[c], 0x3F803F80u, sum);
-                    amax = bf16_pair_absmax(v[c], amax);
+                    if constexpr (FMT == FMT_Q4K)
+                        sum = dot2(v[c], 0x3F803F80u, sum);
+                    if constexpr (FMT == FMT_Q6K) {
+                        amax = bf16_pair_absmax(v[c], amax);
+                        mnz = bf16_pair_minnz(v[c], mnz);
+                    }
                 }
                 const uint4 o = FMT == FMT_Q4K ? octet_pairs(q[t]) : q[t];
                 xr[i].p[m][4 * t + 0] = o.x;
@@ -532,11 +586,13 @@ __global__ __launch_bounds__(512) void gemv_kernel(Geo g, const uint16_t *__rest
                 xr[i].p[m][4 * t + 3] = o.w;
             }
             xr[i].sum[m] = sum;
-            xr[i].e[m] = chunk_exp(amax);
+            xr[i].e[m] = 0;
             if constexpr (FMT == FMT_Q6K) {
+                xr[i].e[m] = chunk_exp_flagged(amax, min((uint32_t)mnz.x, (uint32_t)mnz.y));
+                const int es = xr[i].e[m] >= Q6K_EXACT_FLAG / 2 ? xr[i].e[m] - Q6K_EXACT_FLAG : xr[i].e[m];
 #pragma unroll
                 for (int e = 0; e < 16; e++)
-                    xr[i].p[m][e] = bf16_pair_to_f16(xr[i].p[m][e], xr[i].e[m]);
+                    xr[i].p[m][e] = bf16_pair_to_f16(xr[i].p[m][e], es);
             }
         }
     }
@@ -553,11 +609,11 @@ __global__ __launch_bounds__(512) void gemv_kernel(Geo g, const uint16_t *__rest
         const bool hasB = b + G < nbatch;
         if (hasB)
             load_batch<FMT, M, CPT, R>(g, b + G, N, cl, B);
-        process_batch<FMT, M, CPT, R>(A, xr, cj, k, b, N, Y, lane, wv, KS, part);
+        process_batch<FMT, M, CPT, R>(A, xr, cj, cl, X, g.K, k, b, N, Y, lane, wv, KS, part);
         if (b + 2 * G < nbatch)
             load_batch<FMT, M, CPT, R>(g, b + 2 * G, N, cl, A);
         if (hasB)
-            process_batch<FMT, M, CPT, R>(B, xr, cj, k, b + G, N, Y, lane, wv, KS, part);
+            process_batch<FMT, M, CPT, R>(B, xr, cj, cl, X, g.K, k, b + G, N, Y, lane, wv, KS, part);
     }
 }
 
@@ -759,10 +815,15 @@ __global__ __launch_bounds__(64 * LW) void gemv_lds_kernel(Geo g, Geo g2, const 
             float a = bf16_pair_absmax(v.x, bf16_pair_absmax(v.y, bf16_pair_absmax(v.z, bf16_pair_absmax(v.w, 0.0f))));
             a = fmaxf(a, dpp_f<0xB1>(a));
             a = fmaxf(a, dpp_f<0x4E>(a));
-            const int e = chunk_exp(a);
+            const u16x2_t mz = bf16_pair_minnz(v.x, bf16_pair_minnz(v.y, bf16_pair_minnz(v.z, bf16_pair_minnz(v.w, u16x2_t{0xFFFF, 0xFFFF}))));
+            uint32_t mn = min((uint32_t)mz.x, (uint32_t)mz.y);
+            mn = min(mn, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mn, 0xB1, 0xF, 0xF, false));  // quarters t, t^1
+            mn = min(mn, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mn, 0x4E, 0xF, 0xF, false));  // the chunk
+            const int ef = chunk_exp_flagged(a, mn);
+            const int e = ef >= Q6K_EXACT_FLAG / 2 ? ef - Q6K_EXACT_FLAG : ef;
             sx[m][t][c] = make_uint4(bf16_pair_to_f16(v.x, e), bf16_pair_to_f16(v.y, e), bf16_pair_to_f16(v.z, e),
                                      bf16_pair_to_f16(v.w, e));
-            ss[m][t == 0 ? c : SLOTS] = __int_as_float(e);
+            ss[m][t == 0 ? c : SLOTS] = __int_as_float(ef);
         } else {
             sx[m][t][c] = v;
         }
@@ -808,7 +869,7 @@ __global__ __launch_bounds__(64 * LW) void gemv_lds_kernel(Geo g, Geo g2, const 
             if constexpr (FMT == FMT_Q4K)
                 q4k_dot<M>(ck, xc, c & 7, a);
             else if constexpr (FMT == FMT_Q6K)
-                q6k_dot<M>(ck, xc, a, k);
+                q6k_dot<M>(ck, xc, a, k, X + 32 * (int64_t)c, g.K);
             else
                 q8_0_dot<M>(ck, xc, a);
         };

@@ -201,3 +201,25 @@ def test_gemv_sparse_rows(fmt):
         w = tile_rows(sparse_patterns(), N, K)
         xs = [("small_lead", activations("small_lead", M, K, 61 + M)) for M in Ms]
         check_case(fmt, w, xs, "gemv", "gemv sparse")
+
+
+def test_gemv_q6k_activation_range():
+    """Q6K activations are staged in fp16 after a power of two per 32-element
+    chunk; a chunk holding a nonzero value below 2^-28 of its largest takes
+    the exact fp32 path.  Here each chunk has one value of 1e10 where the
+    weight is zero and values near 1e-3 elsewhere (13 orders of magnitude
+    below), so the whole result comes from the small ones; chunks of other
+    tokens are ordinary, so flagged and unflagged chunks share waves."""
+    rng = np.random.Generator(np.random.PCG64(91))
+    for N, K, Ms in ((300, 1024, (1, 2, 3, 4, 8)), (130, 5120, (1, 2, 3)), (70, 14336, (1, 5))):
+        w32 = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+        w32[:, ::32] = 0.0
+        w = synth.bf16_bits_from_f32(w32)
+        xs = []
+        for M in Ms:
+            x32 = (np.abs(rng.standard_normal((M, K))) * 1e-3 + 1e-4).astype(np.float32)
+            x32[:, ::32] = 1e10
+            x32[1::2] = rng.standard_normal((M // 2, K)).astype(np.float32)  # ordinary tokens
+            xs.append(("range", synth.bf16_bits_from_f32(x32)))
+        check_case("q6k", w, xs, "gemv", "gemv q6k range")
+        check_case("q6k", w, xs, "auto", "auto q6k range")
