@@ -706,6 +706,27 @@ def part_ceilings(torch, ql, run, dev):
     parts["ceiling_mfma_bf16"] = roof("mfma", flops, t, BF16_PEAK_TFLOPS, "TFLOP/s", "mfma_probe_kernel",
                                       note="v_mfma_f32_32x32x16_bf16 chains, two waves per SIMD, no memory")
     log(f"ceilings: MFMA bf16 {parts['ceiling_mfma_bf16']['achieved']:.0f} TFLOP/s")
+    # the same loop with 16 fp32 fmas per MFMA: MFMAs only, fmas only, and
+    # both in one instruction stream, at 1, 2 and 8 waves per SIMD -- how far
+    # VALU work hides behind MFMAs at a kernel's occupancy
+    mixes = {}
+    for wps in (1, 2, 8):
+        mix, counts = {}, {}
+        for mode, name in ((0, "mfma_only"), (1, "valu_only"), (2, "interleaved")):
+            counts[name] = ql.probe_mix(iters // wps, mode, wps, sink)
+            t = run.time(lambda i, mode=mode, wps=wps: ql.probe_mix(iters // wps, mode, wps, sink), 2)
+            mix[name] = round(t["median"] * 1e3, 1)
+        hidden = mix["mfma_only"] + mix["valu_only"] - mix["interleaved"]
+        mixes[f"waves_per_simd_{wps}"] = {
+            "us_median": mix, "mfma_flops": counts["mfma_only"][0], "valu_fma_insts": counts["valu_only"][1],
+            "hidden_frac": round(hidden / min(mix["mfma_only"], mix["valu_only"]), 3)}
+    parts["ceiling_mfma_valu_mix"] = {
+        **mixes,
+        "note": "mix_probe_kernel: v_mfma_f32_32x32x16_bf16 chains with 16 fp32 fmas per MFMA (the fmas take "
+                "twice the MFMAs' time alone); hidden_frac = (t_mfma + t_valu - t_both) / min(t_mfma, t_valu), "
+                "1 = full overlap, 0 = the two add"}
+    log("ceilings: MFMA + VALU mix, hidden fraction at 1 / 2 / 8 waves per SIMD: "
+        + " / ".join(str(v["hidden_frac"]) for v in mixes.values()))
     torch.cuda.empty_cache()
     return parts
 

@@ -58,6 +58,8 @@ SIGNATURES = {
     "q_probe_read": (_INT, [_P, _I64, _P, _P]),
     "q_probe_mfma": (_INT, [_P, _I64, _P]),
     "q_probe_mfma_flops": (_I64, [_I64]),
+    "q_probe_mix": (_INT, [_P, _I64, _INT, _INT, _P]),
+    "q_probe_mix_valu": (_I64, [_I64, _INT]),
 }
 
 
@@ -292,3 +294,14 @@ def probe_mfma(iters: int, sink: torch.Tensor) -> int:
     """A loop of bf16 MFMAs with no memory traffic; returns its FLOP count."""
     _check("q_probe_mfma", lib().q_probe_mfma(_dev(sink, "sink", torch.float32), iters, _stream()))
     return int(lib().q_probe_mfma_flops(iters))
+
+
+def probe_mix(iters: int, mode: int, waves_per_simd: int, sink: torch.Tensor):
+    """The MFMA loop with 16 fp32 fmas per MFMA, waves_per_simd waves on
+    each SIMD: mode 0 MFMAs only, 1 fmas only, 2 both interleaved; returns
+    (MFMA FLOP, wave-level fma instructions) of the call."""
+    _check("q_probe_mix", lib().q_probe_mix(_dev(sink, "sink", torch.float32), iters, mode, waves_per_simd,
+                                            _stream()))
+    fmas = int(lib().q_probe_mix_valu(iters, waves_per_simd))
+    flops = fmas // 16 * 32 * 32 * 16 * 2 if mode != 1 else 0
+    return flops, (fmas if mode != 0 else 0)

@@ -354,6 +354,22 @@ int q_probe_mfma(float *out, int64_t iters, void *stream)
 
 int64_t q_probe_mfma_flops(int64_t iters) { return iters < 0 ? 0 : ql::mfma_probe_flops(iters); }
 
+int q_probe_mix(float *out, int64_t iters, int mode, int waves_per_simd, void *stream)
+{
+    if (!out)
+        return Q_EINVAL;
+    if (iters < 0 || iters > (int64_t(1) << 24) || mode < 0 || mode > 2 || waves_per_simd < 1 || waves_per_simd > 8)
+        return Q_ESHAPE;
+    if (iters == 0)
+        return Q_OK;
+    return status_of(ql::launch_mix_probe(out, iters, mode, waves_per_simd, as_stream(stream)));
+}
+
+int64_t q_probe_mix_valu(int64_t iters, int waves_per_simd)
+{
+    return iters < 0 || waves_per_simd < 1 || waves_per_simd > 8 ? 0 : ql::mix_probe_valu_insts(iters, waves_per_simd);
+}
+
 int isq_resolve_level(int level, int *out_fmt)
 {
     if (!out_fmt)

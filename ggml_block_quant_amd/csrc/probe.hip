@@ -13,6 +13,12 @@
 //   * mfma_probe_kernel: dependent chains of v_mfma_f32_32x32x16_bf16 on
 //     four accumulators per wave, eight waves per workgroup (two per SIMD),
 //     no memory traffic inside the loop.
+//   * mix_probe_kernel: the same loop with sixteen independent fp32 fmas
+//     (eight chains) after each MFMA -- the MFMAs only, the fmas only, or
+//     both interleaved in one instruction stream -- with one to eight waves
+//     per SIMD (workgroups of four waves, 256 per wave-per-SIMD), which
+//     measures how far the VALU work of a kernel can hide behind its MFMAs
+//     at a given occupancy.
 #include <algorithm>
 
 #include "qlinear_internal.h"
@@ -26,6 +32,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kReadBlocks = 2048, kReadThreads = 256;
 constexpr int kMfmaBlocks = 1024, kMfmaThreads = 512, kMfmaChains = 4;
+constexpr int kMixFmas = 16;  // fp32 fmas per MFMA in the mixed probe
 
 __global__ __launch_bounds__(kReadThreads) void read_probe_kernel(const u32x4_t *__restrict__ p, int64_t n16,
                                                                   float *__restrict__ out)
@@ -78,6 +85,51 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_probe_kernel(float *__restr
         out[0] = s;
 }
 
+// MODE 0: the MFMAs only; 1: the fmas only; 2: both, interleaved
+constexpr int kMixThreads = 256;  // one wave per SIMD per workgroup
+template <int MODE>
+__global__ __launch_bounds__(kMixThreads) void mix_probe_kernel(float *__restrict__ out, int64_t iters, float s)
+{
+    f32x16_t acc[kMfmaChains] = {};
+    bf16x8_t a, b;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        a[i] = (__bf16)(float)((threadIdx.x + i) & 7);
+        b[i] = (__bf16)(0.0009765625f * (float)i);
+    }
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+        v[i] = (float)(threadIdx.x & 7) + (float)i;
+    for (int64_t it = 0; it < iters; it++) {
+#pragma unroll
+        for (int t = 0; t < kMfmaChains; t++) {
+            if constexpr (MODE != 1)
+                acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[t], 0, 0, 0);
+            if constexpr (MODE != 0) {
+#pragma unroll
+                for (int u = 0; u < kMixFmas / 8; u++)
+#pragma unroll
+                    for (int i = 0; i < 8; i++)
+                        v[i] = fmaf(v[i], s, 1.0f);
+            }
+        }
+    }
+    // every term is non-negative (s = 0.5: the chains stay in [0, 8]), so
+    // the store is never taken; it keeps both kinds of work live
+    float r = 0.0f;
+#pragma unroll
+    for (int t = 0; t < kMfmaChains; t++)
+#pragma unroll
+        for (int q = 0; q < 16; q++)
+            r += acc[t][q];
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+        r += v[i];
+    if (r == -1.0f)
+        out[0] = r;
+}
+
 }  // namespace
 
 hipError_t launch_read_probe(const void *buf, int64_t bytes, float *out, hipStream_t s)
@@ -103,6 +155,24 @@ int64_t mfma_probe_flops(int64_t iters)
 {
     // waves x iterations x chains x (32 x 32 x 16 multiply-adds x 2)
     return (int64_t)kMfmaBlocks * (kMfmaThreads / 64) * iters * kMfmaChains * 32 * 32 * 16 * 2;
+}
+
+hipError_t launch_mix_probe(float *out, int64_t iters, int mode, int waves_per_simd, hipStream_t s)
+{
+    const dim3 grid(256u * (unsigned)waves_per_simd), block(kMixThreads);
+    if (mode == 0)
+        hipLaunchKernelGGL(mix_probe_kernel<0>, grid, block, 0, s, out, iters, 0.5f);
+    else if (mode == 1)
+        hipLaunchKernelGGL(mix_probe_kernel<1>, grid, block, 0, s, out, iters, 0.5f);
+    else
+        hipLaunchKernelGGL(mix_probe_kernel<2>, grid, block, 0, s, out, iters, 0.5f);
+    return hipGetLastError();
+}
+
+int64_t mix_probe_valu_insts(int64_t iters, int waves_per_simd)
+{
+    // wave-level fp32 fma instructions of one mode-1 or mode-2 launch
+    return (int64_t)256 * waves_per_simd * (kMixThreads / 64) * iters * kMfmaChains * kMixFmas;
 }
 
 }  // namespace ql

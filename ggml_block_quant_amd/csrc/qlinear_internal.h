@@ -154,5 +154,7 @@ hipError_t launch_gemm_i8(const uint8_t *wblocks, const uint8_t *xblocks, float 
 hipError_t launch_read_probe(const void *buf, int64_t bytes, float *out, hipStream_t s);
 hipError_t launch_mfma_probe(float *out, int64_t iters, hipStream_t s);
 int64_t mfma_probe_flops(int64_t iters);
+hipError_t launch_mix_probe(float *out, int64_t iters, int mode, int waves_per_simd, hipStream_t s);
+int64_t mix_probe_valu_insts(int64_t iters, int waves_per_simd);
 
 }  // namespace ql

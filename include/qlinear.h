@@ -262,10 +262,21 @@ int q_dequantize(int fmt, const void *blocks, int64_t N, int64_t K, float *W_fp3
  * q_probe_mfma: `iters` rounds of four dependent v_mfma_f32_32x32x16_bf16
  * chains in each of 8192 waves (two per SIMD), no memory traffic; `out`
  * as above (never written for iters >= 0).  q_probe_mfma_flops: the FLOP
- * count of one q_probe_mfma call (0 for iters < 0). */
+ * count of one q_probe_mfma call (0 for iters < 0).
+ * q_probe_mix: the q_probe_mfma loop with sixteen independent fp32 fmas
+ * after each MFMA, in 1024 * waves_per_simd waves (waves_per_simd per SIMD
+ * of the 256 CUs); `mode` 0 runs the MFMAs only, 1 the fmas only, 2 both
+ * interleaved in one instruction stream (how far a kernel's VALU work can
+ * hide behind its MFMAs at that occupancy); `out` as above; Q_ESHAPE for
+ * iters < 0, a mode outside 0..2 or waves_per_simd outside 1..8.
+ * q_probe_mix_valu: the wave-level fma instructions of one call in mode 1
+ * or 2 (each MFMA of mode 0 or 2 stands for 16 of them; 0 for invalid
+ * arguments). */
 int q_probe_read(const void *buf, int64_t bytes, float *out, void *stream);
 int q_probe_mfma(float *out, int64_t iters, void *stream);
 int64_t q_probe_mfma_flops(int64_t iters);
+int q_probe_mix(float *out, int64_t iters, int mode, int waves_per_simd, void *stream);
+int64_t q_probe_mix_valu(int64_t iters, int waves_per_simd);
 
 /* ISQ level -> format, page "Quantization types", section "Numeric
  * shorthands", column "CUDA / CPU resolves to": 2 Q2K, 3 Q3K, 4 Q4K, 5 Q5K,

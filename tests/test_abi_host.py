@@ -205,6 +205,16 @@ def test_probe_argument_errors():
     assert L.q_probe_mfma(NULL, 10, NULL) == ql.Q_EINVAL
     assert L.q_probe_mfma(A, -1, NULL) == ql.Q_ESHAPE
     assert L.q_probe_mfma(A, 0, NULL) == ql.Q_OK          # nothing to launch
+    assert L.q_probe_mix(NULL, 10, 2, 1, NULL) == ql.Q_EINVAL
+    assert L.q_probe_mix(A, -1, 2, 1, NULL) == ql.Q_ESHAPE
+    assert L.q_probe_mix(A, 10, 3, 1, NULL) == ql.Q_ESHAPE
+    assert L.q_probe_mix(A, 10, -1, 1, NULL) == ql.Q_ESHAPE
+    assert L.q_probe_mix(A, 10, 2, 0, NULL) == ql.Q_ESHAPE
+    assert L.q_probe_mix(A, 10, 2, 9, NULL) == ql.Q_ESHAPE
+    assert L.q_probe_mix(A, 0, 2, 1, NULL) == ql.Q_OK     # nothing to launch
+    assert L.q_probe_mix_valu(1, 2) == 256 * 2 * 4 * 4 * 16
+    assert L.q_probe_mix_valu(-1, 2) == 0
+    assert L.q_probe_mix_valu(1, 0) == 0
     # 1024 workgroups x 8 waves x 4 chains x 32*32*16 multiply-adds x 2
     assert L.q_probe_mfma_flops(1) == 1024 * 8 * 4 * 32 * 32 * 16 * 2
     assert L.q_probe_mfma_flops(-3) == 0
