@@ -223,3 +223,24 @@ def test_gemv_q6k_activation_range():
             xs.append(("range", synth.bf16_bits_from_f32(x32)))
         check_case("q6k", w, xs, "gemv", "gemv q6k range")
         check_case("q6k", w, xs, "auto", "auto q6k range")
+
+
+def test_gemv_q6k_activation_range_row_runs():
+    """The same activations on weights wide enough (N >= 2048) for the
+    one-shot kernel's row-run instances -- four rows per wave as one run of
+    chunks at K = 5120 (the output head's width), two at K = 4096 and one at
+    K = 14336 -- with N not a multiple of a workgroup's rows, so that the
+    last run is shifted back to stay inside the weights."""
+    rng = np.random.Generator(np.random.PCG64(93))
+    for N, K, Ms in ((2100, 5120, (1, 2)), (2052, 4096, (1, 2, 3)), (2049, 14336, (1,))):
+        w32 = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+        w32[:, ::32] = 0.0
+        w = synth.bf16_bits_from_f32(w32)
+        xs = []
+        for M in Ms:
+            x32 = (np.abs(rng.standard_normal((M, K))) * 1e-3 + 1e-4).astype(np.float32)
+            x32[:, ::32] = 1e10
+            x32[1::2] = rng.standard_normal((M // 2, K)).astype(np.float32)  # ordinary tokens
+            xs.append(("range", synth.bf16_bits_from_f32(x32)))
+        check_case("q6k", w, xs, "gemv", "gemv q6k range row runs")
+
