@@ -619,7 +619,8 @@ __global__ __launch_bounds__(512) void gemv_kernel(Geo g, const uint16_t *__rest
 
 // ----------------------------------------------------------------------------
 // One-shot GEMV for one to four tokens (while M times the chunks per lane
-// stays within 14, so that X fits the workgroup's LDS).  Each wave owns R
+// stays within 14, so that X fits the workgroup's LDS), and for five to
+// eight Q4K / Q6K tokens at up to two chunks per lane.  Each wave owns R
 // whole rows and issues every weight load for them at once; the four waves
 // of a workgroup share one copy of X, staged in LDS (zero-padded to CPT*64
 // chunks) by the workgroup before any weight is consumed.  The threads that
@@ -957,11 +958,18 @@ hipError_t go_glu(const Geo &gg, const Geo &gu, const uint16_t *X, float *H, int
 
 // one-shot kernel for M <= 4 while X fits the workgroup's LDS budget
 // (M * CPT <= 14: at most 63 KiB), except four Q8_0 tokens (measured slower
-// than the persistent kernel: 27.9 vs 21.9 us at 14336 x 4096); false when
-// the shape needs the persistent kernel
+// than the persistent kernel: 27.9 vs 21.9 us at 14336 x 4096); for five to
+// eight Q4K and Q6K tokens up to two chunks per lane (K <= 4096: at most
+// 64 KiB of X), where it measured 1.3-1.9x faster than the persistent
+// kernel (Q4K 4096 x 4096, five tokens: 11.7 -> 6.5 us; 14336 x 4096:
+// 25.3 -> 16.7 us; eight tokens 35.4 -> 32.8 us; Q6K 41.9 -> 27.7 us at five
+// tokens), while five and six Q8_0 tokens ran 1-7 % slower; false when the
+// shape needs the persistent kernel
 bool one_shot_fits(int fmt, int M, int64_t K)
 {
     const int64_t cpt = (K / 32 + 63) / 64;
+    if (M >= 5 && M <= 8)
+        return (fmt == FMT_Q4K || fmt == FMT_Q6K) && cpt <= 2;
     return !generic_fmt(fmt) && M >= 1 && M <= 4 && !(fmt == FMT_Q8_0 && M == 4) && cpt <= 8 && M * cpt <= 14;
 }
 
@@ -972,20 +980,28 @@ bool pick_lds(const Geo &g, const uint16_t *X, float *Y, int64_t N, hipStream_t 
     const int cpt = (S + 63) / 64;
     if (!one_shot_fits(FMT, M, g.K))
         return false;
-    switch (cpt) {
-    case 1: e = go_lds<FMT, M, 1>(g, X, Y, N, s); return true;
-    case 2: e = go_lds<FMT, M, 2>(g, X, Y, N, s); return true;
-    case 3: e = go_lds<FMT, M, 3>(g, X, Y, N, s); return true;
-    case 4: e = go_lds<FMT, M, 4>(g, X, Y, N, s); return true;
-    case 5: e = go_lds<FMT, M, 5>(g, X, Y, N, s); return true;
-    case 6: e = go_lds<FMT, M, 6>(g, X, Y, N, s); return true;
-    case 7: e = go_lds<FMT, M, 7>(g, X, Y, N, s); return true;
-    default:
-        if constexpr (M == 1) {
-            e = go_lds<FMT, M, 8>(g, X, Y, N, s);
-            return true;
+    if constexpr (M > 4) {
+        switch (cpt) {
+        case 1: e = go_lds<FMT, M, 1>(g, X, Y, N, s); return true;
+        case 2: e = go_lds<FMT, M, 2>(g, X, Y, N, s); return true;
+        default: return false;
         }
-        return false;
+    } else {
+        switch (cpt) {
+        case 1: e = go_lds<FMT, M, 1>(g, X, Y, N, s); return true;
+        case 2: e = go_lds<FMT, M, 2>(g, X, Y, N, s); return true;
+        case 3: e = go_lds<FMT, M, 3>(g, X, Y, N, s); return true;
+        case 4: e = go_lds<FMT, M, 4>(g, X, Y, N, s); return true;
+        case 5: e = go_lds<FMT, M, 5>(g, X, Y, N, s); return true;
+        case 6: e = go_lds<FMT, M, 6>(g, X, Y, N, s); return true;
+        case 7: e = go_lds<FMT, M, 7>(g, X, Y, N, s); return true;
+        default:
+            if constexpr (M == 1) {
+                e = go_lds<FMT, M, 8>(g, X, Y, N, s);
+                return true;
+            }
+            return false;
+        }
     }
 }
 
@@ -1005,7 +1021,7 @@ template <int FMT, int M>
 hipError_t pick(const Geo &g, const uint16_t *X, float *Y, int64_t N, hipStream_t s)
 {
     const int S = g.K / 32;  // chunks per row
-    if constexpr (M <= 4) {
+    {
         hipError_t e;
         if (pick_lds<FMT, M>(g, X, Y, N, s, e))
             return e;
@@ -1258,7 +1274,7 @@ bool gemv_one_shot_fits(int fmt, int M, int64_t K) { return one_shot_fits(fmt, M
 // for two GEMVs and the elementwise pass) up to four chunks of X per lane
 bool glu_fused_fits(int fmt, int M, int64_t K)
 {
-    return one_shot_fits(fmt, M, K) && (K / 32 + 63) / 64 <= 4;
+    return M <= 4 && one_shot_fits(fmt, M, K) && (K / 32 + 63) / 64 <= 4;
 }
 
 hipError_t launch_glu_fused(int fmt, const uint8_t *gate, const uint8_t *up, const uint16_t *X, float *H, int M,

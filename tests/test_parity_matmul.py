@@ -158,6 +158,40 @@ def test_gemv_three_four_tokens_wide(fmt):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_five_to_eight_tokens(fmt):
+    """Five to eight tokens at up to two chunks per lane (K = 2048, 4096):
+    Q4K and Q6K on the one-shot kernel (X staged in LDS, one row per wave
+    below 2048 rows, two as one run of chunks from 2048), Q8_0 on the
+    persistent kernel; ragged N, on the GEMV path and on AUTO."""
+    for K in (2048, 4096):
+        for M in (5, 6, 7, 8):
+            for N in (300, 2100):
+                w = synth.weights_bf16(5300 + K + N, N, K, outliers=True)
+                x = synth.activations_bf16(5301 + M, M, K)
+                Yr, den = a16_ref(fmt, w, x)
+                for path in ("gemv", "auto"):
+                    check_outputs(run(fmt, path, w, x), Yr, den, f"{path} {fmt} M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q6k"])
+@pytest.mark.parametrize("M", [5, 8])
+def test_gemv_one_hot_is_exact_five_eight_tokens(fmt, M):
+    """The one-hot pin for the one-shot kernel at five and eight tokens."""
+    N, K = 40, 4096
+    w = synth.weights_bf16(4300 + M, N, K, outliers=True)
+    blocks = ql.isq(fmt, to_dev_bf16(w))
+    Wref = oracle.dequant(fmt, oracle.quantize(fmt, w), N, K).astype(np.float32)
+    for k in list(range(0, 256, 5)) + list(range(2048, 2304, 7)) + [3000, 4095]:
+        x = np.zeros((M, K), np.uint16)
+        for m in range(M):
+            x[m, (k + 37 * m) % K] = 0x3F80  # 1.0
+        Y = ql.qmatmul(fmt, blocks, to_dev_bf16(x), N, path="gemv").cpu().numpy()
+        for m in range(M):
+            km = (k + 37 * m) % K
+            assert np.array_equal(Y[m], Wref[:, km]), f"{fmt} M={M} m={m} k={km}"
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("M", [1, 2, 3, 4])
 def test_gemv_one_hot_is_exact_one_two_tokens(fmt, M):
     """The one-hot pin for the one-shot kernel (one to four tokens; four
