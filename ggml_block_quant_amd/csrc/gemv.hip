@@ -914,15 +914,17 @@ __global__ __launch_bounds__(64 * LW) void gemv_lds_kernel(Geo g, Geo g2, const 
     }
 }
 
-constexpr int64_t GEMV_WIDE_N = 2048;
+constexpr int64_t GEMV_WIDE_N = 8192;
 
 template <int FMT, int M, int CPT>
 hipError_t go_lds(const Geo &g, const uint16_t *X, float *Y, int64_t N, hipStream_t s)
 {
     // rows per wave from sweeps on MI355X: two for K <= 4096, four for
     // K = 5120 (the 131072 x 5120 head: 10 % faster than one), one above;
-    // one for narrow weights (N below GEMV_WIDE_N), whose grid would
-    // otherwise leave CUs idle
+    // one for weights below GEMV_WIDE_N rows, whose grid would otherwise
+    // leave CUs idle or run few workgroups per CU (one token, same process:
+    // Q4K 4096 x 4096 4.22 -> 4.15 us, 6144 x 4096 5.01 -> 4.97 us, Q6K
+    // 4096 x 4096 6.04 -> 5.62 us against two rows per wave)
     constexpr int R = CPT <= 2 ? 2 : CPT == 3 ? 4 : 1;
     if (R > 1 && N < GEMV_WIDE_N) {
         hipLaunchKernelGGL((gemv_lds_kernel<FMT, M, CPT, 1>), dim3((unsigned)((N + LW - 1) / LW)), dim3(64 * LW), 0, s,

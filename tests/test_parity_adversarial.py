@@ -226,13 +226,13 @@ def test_gemv_q6k_activation_range():
 
 
 def test_gemv_q6k_activation_range_row_runs():
-    """The same activations on weights wide enough (N >= 2048) for the
+    """The same activations on weights wide enough (N >= 8192) for the
     one-shot kernel's row-run instances -- four rows per wave as one run of
     chunks at K = 5120 (the output head's width), two at K = 4096 and one at
-    K = 14336 -- with N not a multiple of a workgroup's rows, so that the
-    last run is shifted back to stay inside the weights."""
+    K = 14336 (at any N) -- with N not a multiple of a workgroup's rows, so
+    that the last run is shifted back to stay inside the weights."""
     rng = np.random.Generator(np.random.PCG64(93))
-    for N, K, Ms in ((2100, 5120, (1, 2)), (2052, 4096, (1, 2, 3)), (2049, 14336, (1,))):
+    for N, K, Ms in ((8196, 5120, (1, 2)), (8196, 4096, (1, 2, 3)), (2049, 14336, (1,))):
         w32 = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
         w32[:, ::32] = 0.0
         w = synth.bf16_bits_from_f32(w32)

@@ -67,9 +67,9 @@ def test_gemv_row_runs_one_hot(fmt):
     run of 640 chunks, ten per lane, and the items at lanes 0..31 / 32..63
     of the third and eighth step fall in different rows.  One-hot X at
     chunk boundaries and inside those items returns every weight column
-    bit for bit, for rows at each position of the run (N = 9: two full
-    waves and a row past the end)."""
-    N, K = 9, 5120
+    bit for bit, for rows at each position of the run (N = 8201: row runs
+    from 8192 rows, and a last run shifted back to end at the last row)."""
+    N, K = 8201, 5120
     w = synth.weights_bf16(4100, N, K, outliers=True)
     blocks = ql.isq(fmt, to_dev_bf16(w))
     Wref = oracle.dequant(fmt, oracle.quantize(fmt, w), N, K).astype(np.float32)
@@ -83,12 +83,13 @@ def test_gemv_row_runs_one_hot(fmt):
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("K", [1024, 4096, 5120, 14336])
 def test_gemv_wide_weights(fmt, K):
-    """From 2048 rows a wave takes two or four rows (as one run of chunks at
+    """From 8192 rows a wave takes two or four rows (as one run of chunks at
     the widths where that measured faster), for one to four tokens where the
-    one-shot kernel takes them: N = 2051 leaves a partial last workgroup;
-    random X within the bar, and one-hot X at the first, a middle and the
-    last element exact in every token row."""
-    N = 2051
+    one-shot kernel takes them: N = 8195 leaves a partial last workgroup
+    (K = 14336 keeps one row per wave at any N: 2051 rows); random X within
+    the bar, and one-hot X at the first, a middle and the last element exact
+    in every token row."""
+    N = 8195 if K <= 5120 else 2051
     w = synth.weights_bf16(4300 + K, N, K, outliers=True)
     blocks = ql.isq(fmt, to_dev_bf16(w))
     Wd = oracle.dequant(fmt, oracle.quantize(fmt, w), N, K)
@@ -161,11 +162,11 @@ def test_gemv_three_four_tokens_wide(fmt):
 def test_gemv_five_to_eight_tokens(fmt):
     """Five to eight tokens at up to two chunks per lane (K = 2048, 4096):
     Q4K and Q6K on the one-shot kernel (X staged in LDS, one row per wave
-    below 2048 rows, two as one run of chunks from 2048), Q8_0 on the
-    persistent kernel; ragged N, on the GEMV path and on AUTO."""
+    below 8192 rows, two from 8192), Q8_0 on the persistent kernel; ragged
+    N, on the GEMV path and on AUTO."""
     for K in (2048, 4096):
         for M in (5, 6, 7, 8):
-            for N in (300, 2100):
+            for N in (300, 8196):
                 w = synth.weights_bf16(5300 + K + N, N, K, outliers=True)
                 x = synth.activations_bf16(5301 + M, M, K)
                 Yr, den = a16_ref(fmt, w, x)
