@@ -91,8 +91,9 @@ typedef enum {
 
 /* Matmul path.  AUTO: GEMV for M <= 2, and for M <= 4 where the one-shot
  * GEMV takes the row length (and for Q5K, Q3K, Q2K and the legacy
- * 32-element formats); bf16 MFMA GEMM above (crossovers measured on MI355X
- * at decode shapes). */
+ * 32-element formats), and for five or six Q4K tokens on weights of at most
+ * 2^25 elements with K <= 4096; bf16 MFMA GEMM above (crossovers measured
+ * on MI355X at decode shapes). */
 typedef enum {
     QPATH_AUTO = 0,
     QPATH_GEMV = 1,      /* fused dequant-GEMV, M <= 8 only */
