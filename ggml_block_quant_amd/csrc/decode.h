@@ -146,6 +146,52 @@ __device__ __forceinline__ void dequant8(const uint8_t *__restrict__ B, const Pl
     }
 }
 
+// The formats whose weights are a scale times a signed code, w = S * q, with
+// one S per 8-element task: Q4_0 (d (u - 8)), Q5_0 (d (u - 16)) and Q3K
+// (d sc (u - 4)).  S * q is exact in fp32 (at most 11 + 6 + 5 bits), so a
+// dot product can form sum q * x with exact products and scale the task's
+// sum once.
+template <int FMT>
+constexpr bool signed_code_fmt = FMT == FMT_Q4_0 || FMT == FMT_Q5_0 || FMT == FMT_Q3K;
+
+// The codes q of task t as fp32 integers; returns their scale S.  The same
+// fields as dequant8, with the bias subtracted in the integer domain: a
+// field u of width n and bias 2^(n-1) gives q = u - 2^(n-1), which is u with
+// its top bit flipped read as a signed n-bit field.  For the split codes
+// (Q5_0, Q3K) the flipped top bit comes from the high-bit plane as 0 or -1
+// (a signed 1-bit field of the complemented byte) and is shifted above the
+// low bits.
+template <int FMT>
+__device__ __forceinline__ float codes8(const uint8_t *__restrict__ B, const Planes &p, int64_t t, float q[8])
+{
+    static_assert(signed_code_fmt<FMT>, "scale-times-signed-code formats only");
+    if constexpr (FMT == FMT_Q4_0) {
+        const uint32_t c = reinterpret_cast<const uint32_t *>(B)[t] ^ 0x88888888u;
+#pragma unroll
+        for (int k = 0; k < 8; k++)
+            q[k] = (float)(int)__builtin_amdgcn_sbfe((int)c, 4 * k, 4);  // the builtin returns unsigned
+        return f16_bits_to_f32(reinterpret_cast<const uint16_t *>(B + p.d)[t >> 2]);
+    } else if constexpr (FMT == FMT_Q5_0) {
+        const uint32_t c = reinterpret_cast<const uint32_t *>(B)[t];
+        const int nh = ~(int)B[p.hi + t];
+#pragma unroll
+        for (int k = 0; k < 8; k++)
+            q[k] = (float)(int)(((uint32_t)__builtin_amdgcn_sbfe(nh, k, 1) << 4) | __builtin_amdgcn_ubfe(c, 4 * k, 4));
+        return f16_bits_to_f32(reinterpret_cast<const uint16_t *>(B + p.d)[t >> 2]);
+    } else {
+        const int64_t g = t >> 5;
+        const int tl = (int)(t & 31), j = tl >> 1;
+        const uint32_t lo = reinterpret_cast<const uint16_t *>(B)[t];
+        const int nh = ~(int)B[p.hi + 32 * g + tl];
+        const uint32_t *s3 = reinterpret_cast<const uint32_t *>(B + p.scales + 12 * g);
+        const uint32_t sc = (((j < 8 ? s3[0] : s3[1]) >> (4 * (j & 7))) & 15u) | ((s3[2] >> (2 * j)) & 3u) << 4;
+#pragma unroll
+        for (int k = 0; k < 8; k++)
+            q[k] = (float)(int)(((uint32_t)__builtin_amdgcn_sbfe(nh, k, 1) << 2) | __builtin_amdgcn_ubfe(lo, 2 * k, 2));
+        return f16_bits_to_f32(reinterpret_cast<const uint16_t *>(B + p.d)[g]) * (float)sc;
+    }
+}
+
 // runtime dispatch of dequant8 (the dequantizer and the embedding lookup)
 __device__ __forceinline__ void dequant8_any(int fmt, const uint8_t *__restrict__ B, const Planes &p, int64_t t,
                                              float v[8])

@@ -1129,13 +1129,32 @@ __global__ __launch_bounds__(256) void gemv_gen_kernel(const uint8_t *__restrict
 // wave (while M * K * 2 bytes of X fit 64 KiB): the kernel above reads X
 // from the caches once per row, so for one token its X traffic (K * 2 bytes
 // per row) is larger than the weights it streams; here each 16-byte slice of
-// X is read from LDS once per wave and applied to R rows.
+// X is read from LDS once per wave and applied to R rows.  Q4_0, Q5_0 and
+// Q3K take their signed codes and the task's scale (codes8): sum q * x over
+// the task with exact products, then one fused multiply-add of the scale
+// into the row's sum.
+//
+// Where the weight loads of a step are fenced off from the products by a
+// scheduling barrier (measured on MI355X, 14336 x 4096, one / two / four
+// tokens, microseconds without -> with it): without one the compiler
+// interleaves each task's loads, a wait for them and its products for some
+// formats (Q4_1 26.4 -> 16.7 at two tokens, 33.6 -> 22.5 at four; Q3K 53.2
+// -> 27.7 at four; Q2K 33.2 -> 22.8 at four); with one the decode of the
+// signed-code formats loses its overlap with the products (Q4_0 10.9 ->
+// 12.5 at one token, 21.0 -> 21.7 at four).
+template <int FMT>
+constexpr int gen_fence_from_m = FMT == FMT_Q5K ? 1
+                                 : (FMT == FMT_Q3K || FMT == FMT_Q4_1 || FMT == FMT_Q5_1) ? 2
+                                 : FMT == FMT_Q2K ? 4
+                                                  : 1 << 20;
+
 template <int FMT, int M, int R>
 __global__ __launch_bounds__(256) void gemv_genx_kernel(const uint8_t *__restrict__ B, Planes p,
                                                         const uint16_t *__restrict__ X, float *__restrict__ Y,
                                                         int64_t N, int K)
 {
     extern __shared__ uint4 sxs[];  // X as [M][K / 8] 16-byte slices
+    constexpr bool SC = signed_code_fmt<FMT>;
     const int T = K / 8;
     for (int i = threadIdx.x; i < M * T; i += 256)
         sxs[i] = *reinterpret_cast<const uint4 *>(X + 8 * (int64_t)i);
@@ -1150,15 +1169,22 @@ __global__ __launch_bounds__(256) void gemv_genx_kernel(const uint8_t *__restric
             acc[r][m] = 0.0f;
     constexpr int U = 4;  // tasks per lane per step, all loads of a step in flight together
     for (int i0 = 0; i0 < T; i0 += 64 * U) {
-        float w[R][U][8];
+        float w[R][U][8], S[R][U];
         int ic[U];
 #pragma unroll
         for (int u = 0; u < U; u++) {
             ic[u] = min(i0 + 64 * u + lane, T - 1);
 #pragma unroll
-            for (int r = 0; r < R; r++)
-                dequant8<FMT>(B, p, min(n0 + r, N - 1) * T + ic[u], w[r][u]);  // rows past N: not stored
+            for (int r = 0; r < R; r++) {
+                const int64_t t = min(n0 + r, N - 1) * T + ic[u];  // rows past N: not stored
+                if constexpr (SC)
+                    S[r][u] = codes8<FMT>(B, p, t, w[r][u]);
+                else
+                    dequant8<FMT>(B, p, t, w[r][u]);
+            }
         }
+        if constexpr (M >= gen_fence_from_m<FMT>)
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < U; u++) {
             const bool live = i0 + 64 * u + lane < T;
@@ -1166,13 +1192,26 @@ __global__ __launch_bounds__(256) void gemv_genx_kernel(const uint8_t *__restric
             for (int m = 0; m < M; m++) {
                 const uint4 xv = sxs[m * T + ic[u]];
                 const uint32_t xw[4] = {live ? xv.x : 0u, live ? xv.y : 0u, live ? xv.z : 0u, live ? xv.w : 0u};
+                float xf[8];
 #pragma unroll
-                for (int r = 0; r < R; r++)
+                for (int k = 0; k < 4; k++) {
+                    xf[2 * k] = __uint_as_float(xw[k] << 16);
+                    xf[2 * k + 1] = __uint_as_float(xw[k] & 0xffff0000u);
+                }
 #pragma unroll
-                    for (int k = 0; k < 4; k++) {
-                        acc[r][m] = fmaf(w[r][u][2 * k], __uint_as_float(xw[k] << 16), acc[r][m]);
-                        acc[r][m] = fmaf(w[r][u][2 * k + 1], __uint_as_float(xw[k] & 0xffff0000u), acc[r][m]);
+                for (int r = 0; r < R; r++) {
+                    if constexpr (SC) {
+                        float d = 0.0f;
+#pragma unroll
+                        for (int k = 0; k < 8; k++)
+                            d = fmaf(w[r][u][k], xf[k], d);
+                        acc[r][m] = fmaf(S[r][u], d, acc[r][m]);
+                    } else {
+#pragma unroll
+                        for (int k = 0; k < 8; k++)
+                            acc[r][m] = fmaf(w[r][u][k], xf[k], acc[r][m]);
                     }
+                }
             }
         }
     }
