@@ -1134,14 +1134,15 @@ __global__ __launch_bounds__(256) void gemv_gen_kernel(const uint8_t *__restrict
 // the task with exact products, then one fused multiply-add of the scale
 // into the row's sum.
 //
-// Where the weight loads of a step are fenced off from the products by a
-// scheduling barrier (measured on MI355X, 14336 x 4096, one / two / four
-// tokens, microseconds without -> with it): without one the compiler
-// interleaves each task's loads, a wait for them and its products for some
-// formats (Q4_1 26.4 -> 16.7 at two tokens, 33.6 -> 22.5 at four; Q3K 53.2
-// -> 27.7 at four; Q2K 33.2 -> 22.8 at four); with one the decode of the
-// signed-code formats loses its overlap with the products (Q4_0 10.9 ->
-// 12.5 at one token, 21.0 -> 21.7 at four).
+// A scheduling barrier between a step's weight loads (with their decode)
+// and its products, for the formats and token counts where it measured
+// faster.  Without it the compiler interleaves, for some formats, each
+// task's loads, a wait for them and its products, so that a step's loads
+// are not in flight together (MI355X, 14336 x 4096, microseconds without ->
+// with the barrier: Q4_1 26.4 -> 16.7 at two tokens, 33.6 -> 22.5 at four;
+// Q3K 53.2 -> 27.7 at four; Q2K 33.2 -> 22.8 at four).  The signed-code
+// formats go without: the barrier takes away the overlap of their decode
+// with the products (Q4_0 10.9 -> 12.5 at one token, 21.0 -> 21.7 at four).
 template <int FMT>
 constexpr int gen_fence_from_m = FMT == FMT_Q5K ? 1
                                  : (FMT == FMT_Q3K || FMT == FMT_Q4_1 || FMT == FMT_Q5_1) ? 2
