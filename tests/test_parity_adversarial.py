@@ -193,10 +193,12 @@ def test_mfma_i8_adversarial():
         check_outputs(y, Yr, den, f"mfma_i8 X={kind}")
 
 
-@pytest.mark.parametrize("fmt", KQ)
+@pytest.mark.parametrize("fmt", KQ + MORE)
 def test_gemv_sparse_rows(fmt):
     """The GEMV on rows whose blocks hold one large weight among tiny ones,
-    with small activations at the large weights."""
+    with small activations at the large weights (the generic formats: most
+    codes at the zero point, where a sum that took the zero point apart from
+    the codes would cancel)."""
     for N, K, Ms in ((300, 1024, (1, 2, 3, 4, 8)), (130, 5120, (1, 2)), (70, 14336, (1, 5))):
         w = tile_rows(sparse_patterns(), N, K)
         xs = [("small_lead", activations("small_lead", M, K, 61 + M)) for M in Ms]
