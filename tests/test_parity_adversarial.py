@@ -75,6 +75,16 @@ def sparse_patterns(n=8, seed=77):
     return synth.bf16_bits_from_f32(w)
 
 
+def negative_lead_patterns(n=8, seed=5):
+    """Rows of zeros with one negative weight (-0.06 .. -0.01) per 16
+    elements: the affine formats put the zeros at a code near the top of the
+    range, so S * sum(u x) and M * sum(x) nearly cancel where X is large."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    w = np.zeros((n, 256), np.float32)
+    w[:, ::16] = -rng.uniform(0.01, 0.06, (n, 16)).astype(np.float32)
+    return synth.bf16_bits_from_f32(w)
+
+
 def tile_rows(pat, N, K):
     reps = -(-K // 256)
     return np.ascontiguousarray(np.tile(pat, (1, reps))[:, :K][np.arange(N) % len(pat)])
@@ -87,6 +97,8 @@ def activations(kind, M, K, seed):
     if kind == "small_lead":
         # small activations where the sparse rows hold their large weight
         x[:, ::32] = synth.bf16_bits_from_f32(np.full((M, (K + 31) // 32), 1e-3, np.float32))
+    if kind == "small_lead16":
+        x[:, ::16] = synth.bf16_bits_from_f32(np.full((M, (K + 15) // 16), 1e-3, np.float32))
     return x
 
 
@@ -246,3 +258,17 @@ def test_gemv_q6k_activation_range_row_runs():
             xs.append(("range", synth.bf16_bits_from_f32(x32)))
         check_case("q6k", w, xs, "gemv", "gemv q6k range row runs")
 
+
+@pytest.mark.parametrize("fmt", KQ + MORE)
+def test_negative_lead_rows(fmt):
+    """Zeros with one negative weight per 16 elements and small activations
+    at those weights, on the GEMV and the bf16 MFMA paths: the sums that
+    take the affine offset apart from the codes (Q4K and the further affine
+    formats) cancel most here (measured worst 1.7e-4 of the bar's
+    normaliser, Q4K)."""
+    for path, shapes in (("gemv", ((300, 1024, (1, 2, 3, 4, 8)), (130, 5120, (1, 2)), (70, 14336, (1, 5)))),
+                         ("mfma_bf16", ((64, 1024, (5, 12, 40, 520)), (4096, 4352, (8, 24))))):
+        for N, K, Ms in shapes:
+            w = tile_rows(negative_lead_patterns(), N, K)
+            xs = [("small_lead16", activations("small_lead16", M, K, 70 + M)) for M in Ms]
+            check_case(fmt, w, xs, path, "negative lead")
