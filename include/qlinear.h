@@ -169,7 +169,13 @@ int q_act_quantize(const void *X_bf16, int64_t M, int64_t K, void *out_blocks, v
  * Y_fp32: device [M][N], overwritten (not accumulated).
  * 1 <= M <= QLINEAR_MAX_M, K % 256 == 0; Q8_0 weights also take rows that end
  * in a tail of whole blocks (K % 32 == 0, K >= 32: the GEMV kernels, and for
- * the MFMA path the generic exact-decode kernel). */
+ * the MFMA path the generic exact-decode kernel).
+ * Accuracy: each output is within 1e-3 of sum_k |w||x| of the exact product,
+ * with one known exception: the Q4K kernels that take the codes exactly
+ * (decode GEMV, batched decode up to 32 tokens) form a sub-block's sum as
+ * S * sum(u x) - M * sum(x), whose error is bounded by ~2^-23 (S * 15 + M)
+ * sum |x| instead; on sub-blocks whose other weights dequantize to exactly 0
+ * while X is (near) 0 at the nonzero ones, that exceeds the bar. */
 int qmatmul(int fmt, const void *blocks, const void *X_bf16, float *Y_fp32, int64_t M,
             int64_t N, int64_t K, void *stream);
 

@@ -272,3 +272,50 @@ def test_negative_lead_rows(fmt):
             w = tile_rows(negative_lead_patterns(), N, K)
             xs = [("small_lead16", activations("small_lead16", M, K, 70 + M)) for M in Ms]
             check_case(fmt, w, xs, path, "negative lead")
+
+
+def exact_zero_rows(fmt, step=32):
+    """Rows of zeros with one negative weight per sub-block, for the lead
+    values (bf16 over 0.004 .. 0.2) at which the format's quantizer puts the
+    zeros on a code that dequantizes to exactly 0."""
+    bits = np.arange(0x3B80, 0x3E50, dtype=np.uint16)
+    vals = synth.bf16_bits_to_f32(bits)
+    vals = vals[(vals >= 0.004) & (vals <= 0.2)]
+    w = np.zeros((len(vals), 256), np.float32)
+    w[:, ::step] = -vals[:, None]
+    wb = synth.bf16_bits_from_f32(w)
+    Wd = _quantize_dequant(fmt, wb)
+    off = np.ones(256, bool)
+    off[::step] = False
+    return wb[np.all(Wd[:, off] == 0, axis=1)]
+
+
+@pytest.mark.xfail(strict=True, reason=(
+    "known limitation: the exact-code Q4K kernels (every GEMV instance, gemm_bs, gemm_bx) form a "
+    "sub-block's sum as S*sum(u x) - M*sum(x); where the other weights dequantize to exactly 0 and X "
+    "is 0 at the nonzero one, the true output is 0 but the two terms round apart (error ~2^-23 M sum|x|)"))
+@pytest.mark.parametrize("path, N, K, M", [("gemv", 300, 1024, 1), ("mfma_bf16", 4096, 4352, 8)])
+def test_q4k_exact_zero_rows(path, N, K, M):
+    pat = exact_zero_rows("q4k")
+    assert len(pat) > 0
+    w = tile_rows(pat, N, K)
+    x = synth.activations_bf16(80 + M, M, K) & np.uint16(0x7FFF)
+    x[:, ::32] = 0
+    check_case("q4k", w, [("zero_lead", x)], path, "exact-zero rows")
+
+
+@pytest.mark.parametrize("fmt, step", [("q5k", 32), ("q2k", 16), ("q4_1", 32), ("q5_1", 32)])
+def test_affine_exact_zero_rows(fmt, step):
+    """The same rows on the other affine formats, whose kernels form each
+    weight before its product: within the bar (and exact zeros where X is 0
+    at the nonzero weights)."""
+    pat = exact_zero_rows(fmt, step)
+    assert len(pat) > 0
+    for path, N, K, Ms in (("gemv", 300, 1024, (1, 2, 4)), ("mfma_bf16", 4096, 4352, (8, 24))):
+        w = tile_rows(pat, N, K)
+        xs = []
+        for M in Ms:
+            x = synth.activations_bf16(90 + M, M, K) & np.uint16(0x7FFF)
+            x[:, ::step] = 0
+            xs.append(("zero_lead", x))
+        check_case(fmt, w, xs, path, "exact-zero rows")
